@@ -1,0 +1,156 @@
+"""MI355X (gfx950) streaming semi-Markov CRF: Python binding of the C ABI.
+
+The functions below only marshal arguments: they check devices, dtypes and
+shapes, allocate the outputs and the workspace with PyTorch (which supplies
+device memory and the current stream) and call ``libsemicrf.so``.  Every step of
+the computation runs in the library's HIP kernels.
+
+    logz(em, lengths, trans, dur)            -> log Z  [B]
+    backward(em, lengths, trans, dur, ...)   -> gradients, marginals, log Z
+    viterbi(em, lengths, trans, dur)         -> best score, labels, segment starts
+    log_partition(em, lengths, trans, dur)   -> log Z with autograd support
+
+Shapes: em [B, T, C] float32, lengths [B] int32, trans [C, C] float32 (row =
+previous label), dur [K, C] float32 (row k-1 scores length k).
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import _native
+from ._native import OP_BACKWARD, OP_LOGZ, OP_VITERBI, SemiCRFError
+
+__all__ = ["logz", "backward", "viterbi", "log_partition", "workspace_bytes",
+           "checkpoint_interval", "read_status", "SemiCRFError",
+           "OP_LOGZ", "OP_BACKWARD", "OP_VITERBI"]
+
+
+def checkpoint_interval(T: int, K: int, delta: int = 0) -> int:
+    return int(_native.load().semicrf_checkpoint_interval(T, K, delta))
+
+
+def workspace_bytes(op: int, B: int, T: int, C: int, K: int, delta: int = 0) -> int:
+    return int(_native.load().semicrf_workspace_bytes(op, B, T, C, K, delta))
+
+
+def _check_inputs(em, lengths, trans, dur):
+    for name, t, dt in (("emissions", em, torch.float32), ("lengths", lengths, torch.int32),
+                        ("trans", trans, torch.float32), ("dur", dur, torch.float32)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.device != em.device:
+            raise ValueError(f"{name} is on {t.device}, emissions on {em.device}")
+    if em.dim() != 3:
+        raise ValueError("emissions must be [B, T, C]")
+    B, T, C = em.shape
+    if lengths.shape != (B,) or trans.shape != (C, C) or dur.dim() != 2 or dur.shape[1] != C:
+        raise ValueError("shape mismatch: lengths [B], trans [C, C], dur [K, C] required")
+    return int(B), int(T), int(C), int(dur.shape[0])
+
+
+def _workspace(op, B, T, C, K, delta, device, workspace):
+    n = workspace_bytes(op, B, T, C, K, delta)
+    if n == 0:
+        raise SemiCRFError("semicrf_workspace_bytes", 3)
+    if workspace is None:
+        workspace = torch.empty(n, dtype=torch.uint8, device=device)
+    if workspace.numel() < n or workspace.data_ptr() % 256:
+        raise ValueError(f"workspace must hold {n} bytes, 256-byte aligned")
+    return workspace, n
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def read_status(workspace: torch.Tensor) -> int:
+    """Device status flag of the last call that used ``workspace`` (synchronises)."""
+    return int(_native.load().semicrf_read_status(workspace.data_ptr(),
+                                                  _stream(workspace.device)))
+
+
+def _maybe_check(workspace, check_status, fn):
+    if check_status:
+        _native.check(fn, read_status(workspace))
+
+
+def logz(em, lengths, trans, dur, *, workspace=None, check_status=False) -> torch.Tensor:
+    B, T, C, K = _check_inputs(em, lengths, trans, dur)
+    ws, n = _workspace(OP_LOGZ, B, T, C, K, 0, em.device, workspace)
+    out = torch.empty(B, dtype=torch.float32, device=em.device)
+    rc = _native.load().semicrf_logz(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
+                                     dur.data_ptr(), B, T, C, K, _stream(em.device),
+                                     ws.data_ptr(), n, out.data_ptr())
+    _native.check("semicrf_logz", rc)
+    _maybe_check(ws, check_status, "semicrf_logz")
+    return out
+
+
+def backward(em, lengths, trans, dur, *, grad_log_z=None, delta=0, want_marginals=True,
+             workspace=None, check_status=False) -> dict:
+    """Gradients of sum_b grad_log_z[b] * log Z_b (all ones when None).  Returns a dict
+    with grad_em [B,T,C], grad_trans [C,C], grad_dur [K,C], marginals [B,T,C] (or
+    None) and log_z [B]."""
+    B, T, C, K = _check_inputs(em, lengths, trans, dur)
+    dev = em.device
+    if grad_log_z is not None:
+        if grad_log_z.shape != (B,) or grad_log_z.dtype != torch.float32 or grad_log_z.device != dev:
+            raise ValueError("grad_log_z must be a float32 [B] tensor on the emissions' device")
+        grad_log_z = grad_log_z.contiguous()
+    ws, n = _workspace(OP_BACKWARD, B, T, C, K, delta, dev, workspace)
+    grad_em = torch.empty_like(em)
+    grad_trans = torch.empty_like(trans)
+    grad_dur = torch.empty_like(dur)
+    mu = torch.empty_like(em) if want_marginals else None
+    lz = torch.empty(B, dtype=torch.float32, device=dev)
+    rc = _native.load().semicrf_backward(
+        em.data_ptr(), lengths.data_ptr(), trans.data_ptr(), dur.data_ptr(), B, T, C, K, delta,
+        _stream(dev), ws.data_ptr(), n,
+        None if grad_log_z is None else grad_log_z.data_ptr(),
+        grad_em.data_ptr(), grad_trans.data_ptr(), grad_dur.data_ptr(),
+        None if mu is None else mu.data_ptr(), lz.data_ptr())
+    _native.check("semicrf_backward", rc)
+    _maybe_check(ws, check_status, "semicrf_backward")
+    return {"grad_em": grad_em, "grad_trans": grad_trans, "grad_dur": grad_dur,
+            "marginals": mu, "log_z": lz}
+
+
+def viterbi(em, lengths, trans, dur, *, workspace=None, check_status=False):
+    """Returns (best_score [B] float32, labels [B,T] int32, seg_start [B,T] uint8)."""
+    B, T, C, K = _check_inputs(em, lengths, trans, dur)
+    dev = em.device
+    ws, n = _workspace(OP_VITERBI, B, T, C, K, 0, dev, workspace)
+    score = torch.empty(B, dtype=torch.float32, device=dev)
+    labels = torch.empty((B, T), dtype=torch.int32, device=dev)
+    seg = torch.empty((B, T), dtype=torch.uint8, device=dev)
+    rc = _native.load().semicrf_viterbi(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
+                                        dur.data_ptr(), B, T, C, K, _stream(dev), ws.data_ptr(), n,
+                                        score.data_ptr(), labels.data_ptr(), seg.data_ptr())
+    _native.check("semicrf_viterbi", rc)
+    _maybe_check(ws, check_status, "semicrf_viterbi")
+    return score, labels, seg
+
+
+class _LogPartition(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, em, lengths, trans, dur, delta):
+        ctx.save_for_backward(em, lengths, trans, dur)
+        ctx.delta = delta
+        return logz(em, lengths, trans, dur)
+
+    @staticmethod
+    def backward(ctx, g):
+        em, lengths, trans, dur = ctx.saved_tensors
+        out = backward(em, lengths, trans, dur, grad_log_z=g.contiguous().float(),
+                       delta=ctx.delta, want_marginals=False)
+        return out["grad_em"], None, out["grad_trans"], out["grad_dur"], None
+
+
+def log_partition(em, lengths, trans, dur, delta: int = 0) -> torch.Tensor:
+    """log Z [B] as a differentiable op (a drop-in CRF-layer loss term)."""
+    return _LogPartition.apply(em, lengths, trans, dur, delta)

@@ -1,0 +1,69 @@
+"""ctypes loader for ``libsemicrf.so`` (the C ABI declared in include/semicrf.h).
+
+torch is imported before the library is opened so that both bind to the same
+HIP runtime (they share the ``libamdhip64.so.7`` soname).  Loading fails loudly
+when the library has not been built: there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (must precede the dlopen below, see module docstring)
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsemicrf.so")
+
+OP_LOGZ, OP_BACKWARD, OP_VITERBI = 0, 1, 2
+STATUS_NAMES = {0: "SEMICRF_OK", 1: "SEMICRF_ERR_INVALID", 2: "SEMICRF_ERR_WORKSPACE",
+                3: "SEMICRF_ERR_UNSUPPORTED", 4: "SEMICRF_ERR_DEVICE"}
+
+_c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> (restype, argtypes); every pointer is passed as an integer address
+SIGNATURES = {
+    "semicrf_status_string": (ctypes.c_char_p, [_c_int]),
+    "semicrf_checkpoint_interval": (_c_int, [_c_int, _c_int, _c_int]),
+    "semicrf_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "semicrf_logz": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
+                              _c_size, _vp]),
+    "semicrf_backward": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                  _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "semicrf_viterbi": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
+                                 _c_size, _vp, _vp, _vp]),
+    "semicrf_read_status": (_c_int, [_vp, _vp]),
+}
+
+
+class SemiCRFError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS_NAMES.get(status, status)} "
+                         f"({status_string(status)})")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m "
+                              f"semi_markov_crf_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().semicrf_status_string(status).decode()
+
+
+def check(fn: str, status: int) -> None:
+    if status != 0:
+        raise SemiCRFError(fn, status)

@@ -1,0 +1,119 @@
+// Internal interfaces between the C ABI (api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace semicrf {
+
+// ------------------------------------------------------------------ problem shape
+struct Shape {
+    int B, T, C, K;
+};
+
+// Positions per tile of the emission reduction / prefix-scan kernels.
+int scan_tile(int C);
+// Positions per tile of the marginal and node-marginal kernels.
+int marg_tile(int C, int K);
+
+// ------------------------------------------------------------------ sweep configuration
+// Lanes are grouped G per label; each lane covers KPL durations and CPL previous labels.
+struct SweepCfg {
+    int G, KPL, CPL;     // instantiated kernel shape
+    int NT;              // threads per workgroup (multiple of 64)
+    int RS, RSP;         // ring slots (power of two >= K+1) and padded row pitch
+    int CH;              // positions per prefetch chunk of S
+    size_t lds_bytes;    // dynamic LDS
+    bool ok;
+};
+SweepCfg choose_sweep(int C, int K);
+
+enum SweepMode { MODE_FULL = 0, MODE_SPAN = 1 };
+
+struct SweepArgs {
+    const double* S;        // [B][T+1][C] centred prefix sums
+    const int* Leff;        // [B] clamped length, negated when the input length was invalid
+    const float* trans;     // [C][C]
+    const float* dur;       // [K][C]
+    int B, T, C, K;
+    int mode;               // MODE_FULL: grid (B, ndir); MODE_SPAN: grid (nspans, B, ndir)
+    int delta;              // checkpoint interval
+    int nspans;             // max spans per sequence (ceil(T / delta))
+    int write_ckpt;         // FULL mode: write checkpoints at multiples of delta
+    int write_xa;           // write per-position X / A (SPAN mode, or FULL with one span)
+    // checkpoints [2 dirs][B][nspans][...]; index 0 of the span axis is unused
+    float* ck_ring;         // [..][K][C]
+    double* ck_base;        // [..][C]
+    float* ck_mprev;        // [..][C]
+    double* ck_href;        // [..]
+    // per-position outputs, natural-log units, [B][T+1][C]
+    double* XF;             // forward: alpha[t, c]
+    double* AF;             // forward: alpha_bar[t, c] - S[t, c]
+    double* XB;             // backward: beta_bar[s, c]
+    double* AB;             // backward: beta[u, c] + S[u, c] - S[L, c]
+    double* logz;           // [B] forward log Z
+    double* logz_b;         // [B] log Z from the backward sweep (consistency check)
+    // Viterbi
+    uint32_t* bp;           // [B][T+1][C]: (k) | (previous label << 16)
+    double* vscore;         // [B]
+    int* vcstar;            // [B] final label
+};
+
+hipError_t launch_sweep(const SweepCfg& cfg, bool viterbi, const SweepArgs& a, int ndir,
+                        hipStream_t stream);
+
+// ------------------------------------------------------------------ scans
+// Per-tile column sums of the valid emissions; also writes the clamped lengths Leff
+// (negated where the input length was outside [1, T]).
+hipError_t launch_em_tile_sums(const float* em, const int32_t* lengths, int B, int T, int C,
+                               double* tile_sums, int* Leff, hipStream_t stream);
+// For each b: exclusive prefix (or suffix when reverse) over tiles of [B][n][C] doubles,
+// written to `offsets`, and the totals to `totals` [B][C] (either may be NULL).
+hipError_t launch_tile_scan(const double* tile_sums, int B, int n, int C, bool reverse,
+                            double* offsets, double* totals, hipStream_t stream);
+// Centred prefix sums S [B][T+1][C] from the emissions and the tile offsets / totals;
+// status[0] = 1 if any length was invalid, else 0.
+hipError_t launch_prefix(const float* em, const int* Leff, int B, int T, int C,
+                         const double* tile_offsets, const double* totals, double* S, int* status,
+                         hipStream_t stream);
+
+// ------------------------------------------------------------------ marginals / gradients
+struct MargArgs {
+    const double* S;
+    const int* Leff;
+    const float* trans;
+    const float* dur;
+    int B, T, C, K;
+    int tile;               // positions per tile
+    int ntiles;             // ceil((T+1) / tile)
+    const double* XF; const double* AF; const double* XB; const double* AB;
+    const double* logz;
+    double* Dn;             // [B][T+1][C]: start mass - end mass of segments at each position
+    double* dn_tile;        // [B][ntiles][C]: tile sums of Dn
+    double* part_dur;       // [B][ntiles][K][C]
+    double* part_trans;     // [B][ntiles][C][C]
+};
+hipError_t launch_marginals(const MargArgs& a, hipStream_t stream);
+
+// mu = prefix sum of Dn, normalised per position; writes marginals, per-tile sums of
+// mu and the per-tile mean normaliser.
+hipError_t launch_node_marginals(const double* Dn, const double* dn_off, const int* Leff,
+                                 int B, int T, int C, int tile, int ntiles, float* mu,
+                                 double* mu_tile, double* z_tile, hipStream_t stream);
+hipError_t launch_grad_em(const float* mu, const double* mu_tot, const int* Leff,
+                          const float* grad_log_z, int B, int T, int C, float* grad_em,
+                          hipStream_t stream);
+hipError_t launch_reduce_partials(const double* part_dur, const double* part_trans,
+                                  const double* z_tile, const int* Leff, const float* grad_log_z,
+                                  int B, int T, int C, int K, int tile, int ntiles,
+                                  float* grad_dur, float* grad_trans, hipStream_t stream);
+hipError_t launch_write_logz(const double* logz, int B, float* out, hipStream_t stream);
+
+// ------------------------------------------------------------------ Viterbi
+hipError_t launch_backtrace(const uint32_t* bp, const double* vscore, const int* vcstar,
+                            const int* Leff, int B, int T, int C, int32_t* seg_ws,
+                            float* best_score, int32_t* labels, uint8_t* seg_start,
+                            hipStream_t stream);
+
+}  // namespace semicrf

@@ -1,0 +1,309 @@
+// Posterior marginals and gradients of log Z on gfx950.
+//
+// From the per-position forward / backward quantities written by the span recompute
+//   XF[s,c] = alpha[s,c]        AF[s,c] = abar[s,c] - S[s,c]
+//   XB[s,c] = beta_bar[s,c]     AB[u,c] = beta[u,c] + S[u,c] - S[L,c]
+// the posterior of one segment [s, s+k) of label c is
+//   p(s,k,c) = exp(AF[s,c] + AB[s+k,c] + S[L,c] + dur[k-1,c] - logZ)
+// and that of a transition c' -> c at s is exp(XF[s,c'] + trans[c',c] + XB[s,c] - logZ).
+// Their sums are the gradients of log Z with respect to dur and trans, and the
+// position marginal mu[t,c] (the probability that t lies in a segment of label c) is the
+// mass of the segments covering t.  The pages validate exactly these quantities
+// ("Streaming Structured Inference with Flash-SemiCRF", gist.science EN explainer,
+// "4. Results and Benchmarks": marginals sum to 1, exact gradients).
+//
+// mu is formed as a prefix sum over positions of (start mass - end mass), where both
+// masses are sums of the same per-segment values, so each segment's contribution
+// cancels exactly once it has ended.  mu is then divided by its sum over labels at each
+// position (1 in exact arithmetic).  This per-position normalisation removes the slow
+// drift between the forward and backward sweeps' rounding over 10^5..10^6 positions;
+// the dur / trans partial sums of a tile are divided by the tile's mean normaliser.
+#include "common.h"
+#include "internal.h"
+
+namespace semicrf {
+
+int marg_tile(int C, int K) {
+    // LDS (bytes) = 8*C*(2*(TM+K) + 1 + 3*TM) + 4*(K*C + C*C); keep it near 100 KB
+    int tm = 512;
+    auto lds = [&](int t) {
+        return (size_t)8 * C * (2 * (t + K) + 1 + 3 * t) + (size_t)4 * (K * C + C * C);
+    };
+    while (tm > 8 && lds(tm) > 100 * 1024) tm >>= 1;
+    return tm;
+}
+
+constexpr double DNEG = -1.0e300;
+
+// grid (ntiles, B), block 256
+__global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
+    extern __shared__ double lds[];
+    const int C = a.C, K = a.K, T = a.T, TM = a.tile;
+    const int tile = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int L = abs(a.Leff[b]);
+    const int p0 = tile * TM;
+    const size_t rowC = (size_t)(T + 1) * C;
+
+    double* AFs = lds;                               // [TM + K][C]: starts p0-K .. p0+TM-1
+    double* ABs = AFs + (size_t)(TM + K) * C;        // [TM + K + 1][C]: ends p0 .. p0+TM+K
+    double* XFs = ABs + (size_t)(TM + K + 1) * C;    // [TM][C]
+    double* XBs = XFs + (size_t)TM * C;              // [TM][C]
+    double* Dsh = XBs + (size_t)TM * C;              // [TM][C]
+    float* dur2 = (float*)(Dsh + (size_t)TM * C);    // [K][C]
+    float* tr2 = dur2 + (size_t)K * C;               // [C][C]
+
+    double* part_dur = a.part_dur + ((size_t)b * a.ntiles + tile) * K * C;
+    double* part_trans = a.part_trans + ((size_t)b * a.ntiles + tile) * C * C;
+    double* dn_tile = a.dn_tile + ((size_t)b * a.ntiles + tile) * C;
+    double* Dn = a.Dn + (size_t)b * rowC;
+
+    if (p0 > L) {   // nothing of this sequence here
+        for (int q = tid; q < K * C; q += 256) part_dur[q] = 0.0;
+        for (int q = tid; q < C * C; q += 256) part_trans[q] = 0.0;
+        for (int q = tid; q < C; q += 256) dn_tile[q] = 0.0;
+        for (int q = tid; q < TM * C; q += 256)
+            if (p0 + q / C <= T) Dn[(size_t)p0 * C + q] = 0.0;
+        return;
+    }
+    const double logZ = a.logz[b];
+    const double* Sb = a.S + (size_t)b * rowC;
+    const double* XF = a.XF + (size_t)b * rowC;
+    const double* AF = a.AF + (size_t)b * rowC;
+    const double* XB = a.XB + (size_t)b * rowC;
+    const double* AB = a.AB + (size_t)b * rowC;
+
+    // stage (invalid positions get DNEG so that their exponentials vanish)
+    for (int q = tid; q < (TM + K) * C; q += 256) {
+        const int r = q / C, c = q - r * C;
+        const int s = p0 - K + r;            // segment start
+        AFs[q] = (s >= 0 && s <= L - 1) ? AF[(size_t)s * C + c] + Sb[(size_t)L * C + c] - logZ : DNEG;
+    }
+    for (int q = tid; q < (TM + K + 1) * C; q += 256) {
+        const int r = q / C, c = q - r * C;
+        const int u = p0 + r;                // segment end
+        ABs[q] = (u >= 1 && u <= L) ? AB[(size_t)u * C + c] : DNEG;
+    }
+    for (int q = tid; q < TM * C; q += 256) {
+        const int r = q / C, c = q - r * C;
+        const int s = p0 + r;
+        XFs[q] = (s >= 1 && s <= L - 1) ? XF[(size_t)s * C + c] : DNEG;
+        XBs[q] = (s >= 1 && s <= L - 1) ? XB[(size_t)s * C + c] - logZ : DNEG;
+    }
+    for (int q = tid; q < K * C; q += 256) dur2[q] = fmaxf((float)((double)a.dur[q] * LOG2E), NEG);
+    for (int q = tid; q < C * C; q += 256) tr2[q] = fmaxf((float)((double)a.trans[q] * LOG2E), NEG);
+    __syncthreads();
+
+    // segment posterior from staged values: start s (AF row s - p0 + K), end e (AB row e - p0)
+    auto seg = [&](int ra, int rb, int k, int c) -> float {
+        const double v = AFs[(size_t)ra * C + c] + ABs[(size_t)rb * C + c];
+        return fast_exp2((float)(v * LOG2E) + dur2[(k - 1) * C + c]);
+    };
+
+    // ---- phase 1: per position, start mass - end mass (lanes over (t, c))
+    for (int q = tid; q < TM * C; q += 256) {
+        const int r = q / C, c = q - r * C;
+        const int t = p0 + r;
+        double st = 0.0, en = 0.0;
+        if (t <= L) {
+            for (int k = 1; k <= K; ++k) {
+                st += (double)seg(r + K, r + k, k, c);       // segment [t, t+k)
+                en += (double)seg(r + K - k, r, k, c);       // segment [t-k, t)
+            }
+        }
+        const double d = st - en;
+        Dsh[q] = d;
+        if (t <= T) Dn[(size_t)t * C + c] = d;
+    }
+    __syncthreads();
+    for (int c = tid; c < C; c += 256) {
+        double s = 0.0;
+        for (int r = 0; r < TM; ++r) s += Dsh[(size_t)r * C + c];
+        dn_tile[c] = s;
+    }
+
+    // ---- phase 2: duration partials, lanes over (k, c), segments starting in the tile
+    for (int q = tid; q < K * C; q += 256) {
+        const int k = q / C + 1, c = q - (k - 1) * C;
+        double acc = 0.0;
+        for (int r = 0; r < TM; ++r) acc += (double)seg(r + K, r + k, k, c);
+        part_dur[(size_t)(k - 1) * C + c] = acc;
+    }
+
+    // ---- phase 3: transition partials, lanes over (c', c)
+    for (int q = tid; q < C * C; q += 256) {
+        const int cp = q / C, c = q - cp * C;
+        const float tv = tr2[q];
+        double acc = 0.0;
+        for (int r = 0; r < TM; ++r) {
+            const double v = XFs[(size_t)r * C + cp] + XBs[(size_t)r * C + c];
+            acc += (double)fast_exp2((float)(v * LOG2E) + tv);
+        }
+        part_trans[q] = acc;
+    }
+}
+
+hipError_t launch_marginals(const MargArgs& a, hipStream_t stream) {
+    const int TM = a.tile, K = a.K, C = a.C;
+    const size_t lds = (size_t)8 * C * (2 * (TM + K) + 1 + 3 * TM) + (size_t)4 * (K * C + C * C);
+    hipLaunchKernelGGL(k_marginals, dim3(a.ntiles, a.B), dim3(256), lds, stream, a);
+    return hipGetLastError();
+}
+
+// grid (ntiles, B), block 256: mu over positions [p0, p0+TM) of the prefix sum of Dn,
+// normalised per position; tile sums of mu and the tile's mean normaliser.
+__global__ __launch_bounds__(256) void k_node_marginals(const double* __restrict__ Dn,
+                                                        const double* __restrict__ dn_off,
+                                                        const int* __restrict__ Leff, int T, int C,
+                                                        int TM, float* __restrict__ mu,
+                                                        double* __restrict__ mu_tile,
+                                                        double* __restrict__ z_tile) {
+    extern __shared__ double lds[];
+    const int tile = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, ntiles = gridDim.x;
+    const int L = abs(Leff[b]);
+    const int p0 = tile * TM;
+    double* v = lds;                       // [TM][C]
+    double* csum = v + (size_t)TM * C;     // [256]
+    double* zrow = csum + 256;             // [TM]
+    const double* D = Dn + (size_t)b * (T + 1) * C;
+    const int rows = max(0, min(TM, L - p0));   // positions p0 .. p0+rows-1 are < L
+    for (int q = tid; q < rows * C; q += 256) v[q] = D[(size_t)p0 * C + q];
+    __syncthreads();
+    const double* off = dn_off + ((size_t)b * ntiles + tile) * C;
+    for (int c0 = 0; c0 < C; c0 += 256) {
+        const int CW = min(256, C - c0);
+        const int R = 256 / CW;
+        const int chunk = (rows + R - 1) / R;
+        const int cw = tid % CW, r = tid / CW, c = c0 + cw;
+        const bool act = r < R;
+        double acc = 0.0;
+        if (act)
+            for (int i = r * chunk; i < min(rows, (r + 1) * chunk); ++i) acc += v[(size_t)i * C + c];
+        csum[tid] = acc;
+        __syncthreads();
+        if (act) {
+            double run = off[c];
+            for (int qq = 0; qq < r; ++qq) run += csum[qq * CW + cw];
+            for (int i = r * chunk; i < min(rows, (r + 1) * chunk); ++i) {
+                run += v[(size_t)i * C + c];
+                v[(size_t)i * C + c] = run;
+            }
+        }
+        __syncthreads();
+    }
+    for (int r = tid; r < rows; r += 256) {
+        double z = 0.0;
+        for (int c = 0; c < C; ++c) z += v[(size_t)r * C + c];
+        zrow[r] = z;
+    }
+    __syncthreads();
+    float* mub = mu + (size_t)b * T * C;
+    for (int q = tid; q < TM * C; q += 256) {
+        const int r = q / C;
+        const int t = p0 + r;
+        if (t >= T) continue;
+        float val = 0.0f;
+        if (r < rows) {
+            const double w = v[q] / zrow[r];
+            v[q] = w;
+            val = (float)w;
+        }
+        mub[(size_t)t * C + (q - r * C)] = val;
+    }
+    __syncthreads();
+    for (int c = tid; c < C; c += 256) {
+        double s = 0.0;
+        for (int r = 0; r < rows; ++r) s += v[(size_t)r * C + c];
+        mu_tile[((size_t)b * ntiles + tile) * C + c] = s;
+    }
+    if (tid == 0) {
+        double z = 0.0;
+        for (int r = 0; r < rows; ++r) z += zrow[r];
+        z_tile[(size_t)b * ntiles + tile] = rows > 0 ? z / rows : 1.0;
+    }
+}
+
+hipError_t launch_node_marginals(const double* Dn, const double* dn_off, const int* Leff, int B,
+                                 int T, int C, int tile, int ntiles, float* mu, double* mu_tile,
+                                 double* z_tile, hipStream_t stream) {
+    const size_t lds = (size_t)8 * ((size_t)tile * C + 256 + tile);
+    hipLaunchKernelGGL(k_node_marginals, dim3(ntiles, B), dim3(256), lds, stream, Dn, dn_off, Leff,
+                       T, C, tile, mu, mu_tile, z_tile);
+    return hipGetLastError();
+}
+
+// grid (ceil(T*C/256), B): grad_em = g * (mu - mean over the valid positions of mu)
+__global__ __launch_bounds__(256) void k_grad_em(const float* __restrict__ mu,
+                                                 const double* __restrict__ mu_tot,
+                                                 const int* __restrict__ Leff,
+                                                 const float* __restrict__ grad_log_z, int T,
+                                                 int C, float* __restrict__ grad_em) {
+    const int b = blockIdx.y;
+    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (size_t)T * C) return;
+    const int L = abs(Leff[b]);
+    const int t = (int)(q / C), c = (int)(q - (size_t)t * C);
+    const size_t idx = (size_t)b * T * C + q;
+    float out = 0.0f;
+    if (t < L) {
+        const double g = grad_log_z ? (double)grad_log_z[b] : 1.0;
+        out = (float)(g * ((double)mu[idx] - mu_tot[(size_t)b * C + c] / (double)L));
+    }
+    grad_em[idx] = out;
+}
+
+hipError_t launch_grad_em(const float* mu, const double* mu_tot, const int* Leff,
+                          const float* grad_log_z, int B, int T, int C, float* grad_em,
+                          hipStream_t stream) {
+    const size_t n = (size_t)T * C;
+    hipLaunchKernelGGL(k_grad_em, dim3((unsigned)((n + 255) / 256), B), dim3(256), 0, stream, mu,
+                       mu_tot, Leff, grad_log_z, T, C, grad_em);
+    return hipGetLastError();
+}
+
+// one thread per output element of grad_dur [K*C] followed by grad_trans [C*C]
+__global__ __launch_bounds__(256) void k_reduce_partials(const double* __restrict__ part_dur,
+                                                         const double* __restrict__ part_trans,
+                                                         const double* __restrict__ z_tile,
+                                                         const float* __restrict__ grad_log_z,
+                                                         int B, int C, int K, int ntiles,
+                                                         float* __restrict__ grad_dur,
+                                                         float* __restrict__ grad_trans) {
+    const int q = blockIdx.x * 256 + threadIdx.x;
+    const int nd = K * C, nt = C * C;
+    if (q >= nd + nt) return;
+    const bool isd = q < nd;
+    const int e = isd ? q : q - nd;
+    const int stride = isd ? nd : nt;
+    const double* src = isd ? part_dur : part_trans;
+    double total = 0.0;
+    for (int b = 0; b < B; ++b) {
+        double s = 0.0;
+        for (int j = 0; j < ntiles; ++j)
+            s += src[((size_t)b * ntiles + j) * stride + e] / z_tile[(size_t)b * ntiles + j];
+        total += (grad_log_z ? (double)grad_log_z[b] : 1.0) * s;
+    }
+    (isd ? grad_dur : grad_trans)[e] = (float)total;
+}
+
+hipError_t launch_reduce_partials(const double* part_dur, const double* part_trans,
+                                  const double* z_tile, const int* Leff, const float* grad_log_z,
+                                  int B, int T, int C, int K, int tile, int ntiles,
+                                  float* grad_dur, float* grad_trans, hipStream_t stream) {
+    (void)Leff; (void)T; (void)tile;
+    const int n = K * C + C * C;
+    hipLaunchKernelGGL(k_reduce_partials, dim3((n + 255) / 256), dim3(256), 0, stream, part_dur,
+                       part_trans, z_tile, grad_log_z, B, C, K, ntiles, grad_dur, grad_trans);
+    return hipGetLastError();
+}
+
+__global__ void k_write_logz(const double* __restrict__ logz, int B, float* __restrict__ out) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) out[b] = (float)logz[b];
+}
+
+hipError_t launch_write_logz(const double* logz, int B, float* out, hipStream_t stream) {
+    hipLaunchKernelGGL(k_write_logz, dim3((B + 255) / 256), dim3(256), 0, stream, logz, B, out);
+    return hipGetLastError();
+}
+
+}  // namespace semicrf

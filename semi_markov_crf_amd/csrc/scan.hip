@@ -1,0 +1,184 @@
+// Centring and prefix-sum kernels (gfx950).
+//
+// S[b, 0, c] = 0 and S[b, t, c] = sum_{u < t} (em[b, u, c] - nu[b, c]) for t <= L_b, with
+// nu[b, c] the mean of em[b, :L_b, c] ("Streaming Structured Inference with Flash-SemiCRF",
+// gist.science EN explainer, "2. Methodology": "Emission Baseline Centering" and
+// "On-the-Fly Edge Computation via Prefix Sums").  Positions t > L_b repeat S[b, L_b].
+//
+// Three streaming passes, all HBM bound, with fp64 accumulation:
+//   1. per-tile column sums of the valid emissions (coalesced rows of C floats),
+//   2. an exclusive scan of the tile sums per sequence (also gives nu),
+//   3. the in-tile centred prefix sum, staged through LDS so that both the fp32 reads
+//      and the fp64 writes of the tile are contiguous.
+#include "common.h"
+#include "internal.h"
+
+namespace semicrf {
+
+int scan_tile(int C) {
+    int ts = 1024;
+    while (ts > 32 && ts * C > 8192) ts >>= 1;
+    return ts;
+}
+
+// grid (ntiles, B), block 256
+__global__ __launch_bounds__(256) void k_em_tile_sums(const float* __restrict__ em,
+                                                      const int32_t* __restrict__ lengths,
+                                                      int T, int C, int TS,
+                                                      double* __restrict__ tile_sums,
+                                                      int* __restrict__ Leff) {
+    __shared__ double part[256];
+    const int tile = blockIdx.x, b = blockIdx.y, ntiles = gridDim.x;
+    const int Lraw = lengths[b];
+    const bool bad = Lraw < 1 || Lraw > T;
+    const int L = min(max(Lraw, 1), T);
+    if (tile == 0 && threadIdx.x == 0) Leff[b] = bad ? -L : L;   // negated: length was invalid
+    const int t0 = tile * TS;
+    const int t1 = min(t0 + TS, L);
+    const float* e = em + (size_t)b * T * C;
+    for (int c0 = 0; c0 < C; c0 += 256) {
+        const int CW = min(256, C - c0);
+        const int R = 256 / CW;
+        const int tid = threadIdx.x;
+        const int cw = tid % CW, r = tid / CW;
+        double acc = 0.0;
+        if (r < R)
+            for (int t = t0 + r; t < t1; t += R) acc += (double)e[(size_t)t * C + c0 + cw];
+        part[tid] = acc;
+        __syncthreads();
+        if (tid < CW) {
+            double s = 0.0;
+            for (int i = 0; i < R; ++i) s += part[i * CW + tid];
+            tile_sums[((size_t)b * ntiles + tile) * C + c0 + tid] = s;
+        }
+        __syncthreads();
+    }
+}
+
+// grid (B), block 256.  Exclusive prefix (or suffix) over the n tiles, per column.
+__global__ __launch_bounds__(256) void k_tile_scan(const double* __restrict__ tile_sums, int n,
+                                                   int C, int reverse,
+                                                   double* __restrict__ offsets,
+                                                   double* __restrict__ totals) {
+    __shared__ double part[257];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int per = (n + 255) / 256;
+    const double* in = tile_sums + (size_t)b * n * C;
+    for (int c = 0; c < C; ++c) {
+        // thread tid owns the tiles at ordinal positions [tid*per, (tid+1)*per) of the
+        // scan order (ascending tile index, or descending when reverse)
+        double s = 0.0;
+        for (int i = 0; i < per; ++i) {
+            const int o = tid * per + i;
+            if (o < n) s += in[(size_t)(reverse ? n - 1 - o : o) * C + c];
+        }
+        part[tid] = s;
+        __syncthreads();
+        if (tid == 0) {
+            double run = 0.0;
+            for (int i = 0; i < 256; ++i) {
+                const double v = part[i];
+                part[i] = run;
+                run += v;
+            }
+            part[256] = run;
+        }
+        __syncthreads();
+        double run = part[tid];
+        if (offsets)
+            for (int i = 0; i < per; ++i) {
+                const int o = tid * per + i;
+                if (o < n) {
+                    const size_t idx = (size_t)(reverse ? n - 1 - o : o) * C + c;
+                    offsets[(size_t)b * n * C + idx] = run;
+                    run += in[idx];
+                }
+            }
+        if (totals && tid == 0) totals[(size_t)b * C + c] = part[256];
+        __syncthreads();
+    }
+}
+
+// grid (ntiles, B), block 256, dynamic LDS = TS*C*4 + TS*C*8 + 256*8 bytes.
+__global__ __launch_bounds__(256) void k_prefix(const float* __restrict__ em,
+                                                const int* __restrict__ Leff, int B, int T, int C,
+                                                int TS, const double* __restrict__ tile_off,
+                                                const double* __restrict__ totals,
+                                                double* __restrict__ S, int* __restrict__ status) {
+    extern __shared__ double lds[];
+    const int tile = blockIdx.x, b = blockIdx.y, ntiles = gridDim.x;
+    const int L = abs(Leff[b]);
+    const int t0 = tile * TS;
+    const int rows = min(TS, T - t0);           // emission rows of this tile
+    if (tile == 0 && b == 0 && threadIdx.x == 0) {
+        int flag = 0;
+        for (int i = 0; i < B; ++i) flag |= Leff[i] < 0;
+        status[0] = flag;
+    }
+    double* out = lds;                          // [TS][C] doubles
+    double* csum = out + (size_t)TS * C;        // [256]
+    float* in = (float*)(csum + 256);           // [TS][C] floats
+    const float* e = em + ((size_t)b * T + t0) * C;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < rows * C; i += 256) in[i] = e[i];
+    __syncthreads();
+    const double* off = tile_off + ((size_t)b * ntiles + tile) * C;
+    const double* tot = totals + (size_t)b * C;
+    const int nvalid_before = min(t0, L);
+    for (int c0 = 0; c0 < C; c0 += 256) {
+        const int CW = min(256, C - c0);
+        const int R = 256 / CW;
+        const int chunk = (rows + R - 1) / R;
+        const int cw = tid % CW, r = tid / CW, c = c0 + cw;
+        const bool act = r < R;
+        const double nu = tot[c] / (double)L;
+        double acc = 0.0;
+        if (act)
+            for (int i = r * chunk; i < min(rows, (r + 1) * chunk); ++i)
+                if (t0 + i < L) acc += (double)in[i * C + c] - nu;
+        csum[tid] = acc;
+        __syncthreads();
+        if (act) {
+            double run = off[c] - nu * (double)nvalid_before;
+            for (int q = 0; q < r; ++q) run += csum[q * CW + cw];
+            for (int i = r * chunk; i < min(rows, (r + 1) * chunk); ++i) {
+                if (t0 + i < L) run += (double)in[i * C + c] - nu;
+                out[i * C + c] = run;
+            }
+        }
+        __syncthreads();
+    }
+    double* Sb = S + (size_t)b * (T + 1) * C;
+    for (int i = tid; i < rows * C; i += 256) Sb[(size_t)(t0 + 1) * C + i] = out[i];
+    if (tile == 0)
+        for (int c = tid; c < C; c += 256) Sb[c] = 0.0;
+}
+
+hipError_t launch_em_tile_sums(const float* em, const int32_t* lengths, int B, int T, int C,
+                               double* tile_sums, int* Leff, hipStream_t stream) {
+    const int TS = scan_tile(C);
+    const int nt = (T + TS - 1) / TS;
+    hipLaunchKernelGGL(k_em_tile_sums, dim3(nt, B), dim3(256), 0, stream, em, lengths, T, C, TS,
+                       tile_sums, Leff);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_scan(const double* tile_sums, int B, int n, int C, bool reverse,
+                            double* offsets, double* totals, hipStream_t stream) {
+    hipLaunchKernelGGL(k_tile_scan, dim3(B), dim3(256), 0, stream, tile_sums, n, C,
+                       reverse ? 1 : 0, offsets, totals);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefix(const float* em, const int* Leff, int B, int T, int C,
+                         const double* tile_offsets, const double* totals, double* S, int* status,
+                         hipStream_t stream) {
+    const int TS = scan_tile(C);
+    const int nt = (T + TS - 1) / TS;
+    const size_t lds = (size_t)TS * C * 8 + 256 * 8 + (size_t)TS * C * 4;
+    hipLaunchKernelGGL(k_prefix, dim3(nt, B), dim3(256), lds, stream, em, Leff, B, T, C, TS,
+                       tile_offsets, totals, S, status);
+    return hipGetLastError();
+}
+
+}  // namespace semicrf

@@ -1,0 +1,226 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances (fixed here, derived in the design doc):
+  log Z, Viterbi score     |gpu - ref| <= 1e-5 * max(1, |ref|)
+  marginals, grad_em       |gpu - ref| <= 1e-4
+  grad_trans, grad_dur     |gpu - ref| <= 1e-4 * max(1, |ref|)   (sums over up to B*T positions)
+  Viterbi segmentation     identical wherever the oracle's margin exceeds 1e-4; otherwise the
+                           GPU segmentation must be valid and score (rescored in fp64 by the
+                           oracle) within the score tolerance of the best.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+LOGZ_RTOL = 1e-5
+MARG_ATOL = 1e-4
+GRAD_RTOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def crf():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import semi_markov_crf_amd
+    semi_markov_crf_amd._native.load()
+    return semi_markov_crf_amd
+
+
+def dev(w):
+    import torch
+    d = torch.device("cuda:0")
+    return (torch.from_numpy(w.em).to(d), torch.from_numpy(w.lengths).to(d),
+            torch.from_numpy(w.trans).to(d), torch.from_numpy(w.dur).to(d))
+
+
+def np_(t):
+    return t.detach().cpu().numpy()
+
+
+def assert_scalar_close(gpu, ref, rtol, what):
+    gpu, ref = np.asarray(gpu, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    err = np.abs(gpu - ref)
+    bound = rtol * np.maximum(1.0, np.abs(ref))
+    bad = err > bound
+    assert not bad.any(), f"{what}: max err {err.max():.3e}, worst ratio {(err / bound).max():.2f}"
+
+
+def assert_abs_close(gpu, ref, atol, what):
+    err = np.abs(np.asarray(gpu, dtype=np.float64) - np.asarray(ref, dtype=np.float64))
+    assert err.max() <= atol, f"{what}: max abs err {err.max():.3e} > {atol}"
+
+
+def check_viterbi(w, score, labels, seg, ref):
+    """Exact where the oracle's margin > 1e-4, else validity + optimality by rescoring."""
+    assert_scalar_close(score, ref["score"], LOGZ_RTOL, "viterbi score")
+    for b in range(w.B):
+        L = int(w.lengths[b])
+        assert np.all(labels[b, L:] == -1) and np.all(seg[b, L:] == 0)
+        if ref["margin"][b] > 1e-4 and "labels" in ref:
+            np.testing.assert_array_equal(labels[b, :L], ref["labels"][b, :L])
+            np.testing.assert_array_equal(seg[b, :L], ref["seg_start"][b, :L])
+        _, S = oracle.centered_prefix(w.em[b], L)
+        got = oracle.segmentation_score(S, w.trans, w.dur, w.K, seg[b, :L], labels[b, :L])
+        best = float(ref["score"][b])
+        assert got >= best - LOGZ_RTOL * max(1.0, abs(best)), (b, got, best)
+
+
+SMALL = [
+    # seed, B, T, C, K, em_scale, ragged
+    (1, 3, 40, 4, 6, 1.0, True),
+    (2, 2, 17, 3, 20, 2.0, True),       # K > T
+    (3, 4, 65, 5, 1, 1.0, True),        # K = 1: linear chain
+    (4, 2, 30, 1, 7, 1.0, True),        # C = 1
+    (5, 5, 9, 6, 4, 1.0, True),         # many length-1..9 sequences
+    (6, 2, 300, 6, 40, 3.0, True),      # several S chunks, rebases, ragged tail
+    (7, 2, 150, 39, 30, 1.0, True),     # speech-like label count (G=16 instance)
+    (8, 2, 70, 64, 64, 1.0, False),     # large label set, NT = 1024
+    (9, 1, 1, 3, 5, 1.0, False),        # L = T = 1
+    (10, 3, 129, 20, 70, 1.0, True),    # G=32 instance, K not a multiple of 32
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"s{c[0]}" for c in SMALL])
+def test_small_cases_against_oracle(crf, case):
+    import torch
+    seed, B, T, C, K, scale, ragged = case
+    w = workloads.make_custom(seed, B, T, C, K, em_scale=scale, ragged=ragged)
+    em, lengths, trans, dur = dev(w)
+    g = np.random.default_rng(seed).uniform(0.5, 1.5, B).astype(np.float32)
+    ref = oracle.batch(w.em, w.lengths, w.trans, w.dur, K, grad_log_z=g)
+
+    lz = crf.logz(em, lengths, trans, dur, check_status=True)
+    assert_scalar_close(np_(lz), ref["logZ"], LOGZ_RTOL, "logz")
+
+    out = crf.backward(em, lengths, trans, dur, grad_log_z=torch.from_numpy(g).cuda(),
+                       check_status=True)
+    assert_scalar_close(np_(out["log_z"]), ref["logZ"], LOGZ_RTOL, "backward log_z")
+    assert_abs_close(np_(out["marginals"]), ref["mu"], MARG_ATOL, "marginals")
+    assert_abs_close(np_(out["grad_em"]), ref["grad_em"], MARG_ATOL, "grad_em")
+    assert_scalar_close(np_(out["grad_trans"]), ref["grad_trans"], GRAD_RTOL, "grad_trans")
+    assert_scalar_close(np_(out["grad_dur"]), ref["grad_dur"], GRAD_RTOL, "grad_dur")
+
+    score, labels, seg = crf.viterbi(em, lengths, trans, dur, check_status=True)
+    check_viterbi(w, np_(score), np_(labels), np_(seg), ref)
+
+
+def test_checkpoint_interval_invariance_and_determinism(crf):
+    w = workloads.make_custom(21, 2, 400, 6, 30, em_scale=2.0, ragged=True)
+    em, lengths, trans, dur = dev(w)
+    ref = oracle.batch(w.em, w.lengths, w.trans, w.dur, w.K, want_viterbi=False)
+    lz = np_(crf.logz(em, lengths, trans, dur))
+    outs = {}
+    for delta in (0, 1, 7, 30, 64, 399, 400):
+        o = crf.backward(em, lengths, trans, dur, delta=delta)
+        outs[delta] = {k: np_(v) for k, v in o.items()}
+        # log Z of the backward call comes from the restored last span: bitwise equal
+        np.testing.assert_array_equal(outs[delta]["log_z"], lz)
+        assert_abs_close(outs[delta]["marginals"], ref["mu"], MARG_ATOL, f"marginals delta={delta}")
+        assert_abs_close(outs[delta]["grad_em"], ref["grad_em"], MARG_ATOL, f"grad_em delta={delta}")
+        assert_scalar_close(outs[delta]["grad_dur"], ref["grad_dur"], GRAD_RTOL, f"dur delta={delta}")
+        assert_scalar_close(outs[delta]["grad_trans"], ref["grad_trans"], GRAD_RTOL, f"tr delta={delta}")
+    again = crf.backward(em, lengths, trans, dur, delta=30)
+    for k in ("grad_em", "grad_trans", "grad_dur", "marginals", "log_z"):
+        np.testing.assert_array_equal(np_(again[k]), outs[30][k])     # bitwise reproducible
+
+
+def test_forbidden_transitions_and_durations(crf):
+    """-inf entries: transitions c -> c forbidden, durations above 5 forbidden for label 0."""
+    w = workloads.make_custom(31, 2, 60, 4, 8, ragged=True)
+    w.trans[np.arange(4), np.arange(4)] = -np.inf
+    w.dur[5:, 0] = -np.inf
+    em, lengths, trans, dur = dev(w)
+    ref = oracle.batch(w.em, w.lengths, w.trans, w.dur, w.K)
+    assert_scalar_close(np_(crf.logz(em, lengths, trans, dur)), ref["logZ"], LOGZ_RTOL, "logz")
+    out = crf.backward(em, lengths, trans, dur)
+    assert_abs_close(np_(out["marginals"]), ref["mu"], MARG_ATOL, "marginals")
+    assert_scalar_close(np_(out["grad_trans"]), ref["grad_trans"], GRAD_RTOL, "grad_trans")
+    assert_scalar_close(np_(out["grad_dur"]), ref["grad_dur"], GRAD_RTOL, "grad_dur")
+    score, labels, seg = crf.viterbi(em, lengths, trans, dur)
+    check_viterbi(w, np_(score), np_(labels), np_(seg), ref)
+
+
+def test_invalid_length_is_flagged(crf):
+    import torch
+    w = workloads.make_custom(41, 3, 20, 3, 4, ragged=False)
+    em, lengths, trans, dur = dev(w)
+    bad = torch.tensor([20, 0, 21], dtype=torch.int32, device=em.device)
+    lz = crf.logz(em, bad, trans, dur)
+    ws = torch.empty(crf.workspace_bytes(crf.OP_LOGZ, 3, 20, 3, 4), dtype=torch.uint8,
+                     device=em.device)
+    lz = crf.logz(em, bad, trans, dur, workspace=ws)
+    assert crf.read_status(ws) == 1
+    v = np_(lz)
+    assert np.isfinite(v[0]) and np.isnan(v[1]) and np.isnan(v[2])
+    crf.logz(em, lengths, trans, dur, workspace=ws)
+    assert crf.read_status(ws) == 0
+
+
+def test_autograd_matches_backward(crf):
+    import torch
+    w = workloads.make_custom(51, 2, 50, 5, 10, ragged=True)
+    em, lengths, trans, dur = dev(w)
+    em.requires_grad_(True); trans.requires_grad_(True); dur.requires_grad_(True)
+    lz = crf.log_partition(em, lengths, trans, dur)
+    wts = torch.tensor([0.3, -1.7], device=em.device)
+    (lz * wts).sum().backward()
+    out = crf.backward(em.detach(), lengths, trans.detach(), dur.detach(), grad_log_z=wts)
+    np.testing.assert_allclose(np_(em.grad), np_(out["grad_em"]), atol=1e-6)
+    np.testing.assert_allclose(np_(trans.grad), np_(out["grad_trans"]), rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(np_(dur.grad), np_(out["grad_dur"]), rtol=1e-6, atol=1e-6)
+
+
+# --------------------------------------------------------------------------- the five configs
+
+
+def _fixture(i):
+    path = os.path.join(GOLDEN, f"oracle_cfg{i}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    return dict(np.load(path, allow_pickle=False))
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_config_against_oracle_fixture(crf, cfg):
+    ref = _fixture(cfg)
+    w = workloads.make(cfg)
+    em, lengths, trans, dur = dev(w)
+    print(f"\n[config {cfg}: {w.name} B={w.B} T={w.T} C={w.C} K={w.K}]", flush=True)
+    lz = np_(crf.logz(em, lengths, trans, dur, check_status=True))
+    assert_scalar_close(lz, ref["logZ"], LOGZ_RTOL, "logz")
+    out = crf.backward(em, lengths, trans, dur, check_status=True)
+    assert_scalar_close(np_(out["log_z"]), ref["logZ"], LOGZ_RTOL, "backward log_z")
+    mu, ge = np_(out["marginals"]), np_(out["grad_em"])
+    if "mu" in ref:
+        assert_abs_close(mu, ref["mu"], MARG_ATOL, "marginals")
+        assert_abs_close(ge, ref["grad_em"], MARG_ATOL, "grad_em")
+    else:
+        b = np.arange(w.B)[:, None]
+        pos = ref["positions"]
+        assert_abs_close(mu[b, pos], ref["mu_sample"], MARG_ATOL, "marginals (sampled)")
+        assert_abs_close(ge[b, pos], ref["grad_em_sample"], MARG_ATOL, "grad_em (sampled)")
+    assert_scalar_close(np_(out["grad_trans"]), ref["grad_trans"], GRAD_RTOL, "grad_trans")
+    assert_scalar_close(np_(out["grad_dur"]), ref["grad_dur"], GRAD_RTOL, "grad_dur")
+    # properties that hold at every position
+    for b in range(w.B):
+        L = int(w.lengths[b])
+        assert np.abs(mu[b, :L].sum(axis=1) - 1.0).max() < 1e-5
+        assert mu[b, :L].min() > -1e-6 and np.all(mu[b, L:] == 0)
+        assert np.abs(ge[b, :L].sum(axis=0)).max() < 1e-3 * max(1, L / 1000)
+    k = np.arange(1, w.K + 1)[:, None]
+    total = float(w.lengths.astype(np.int64).sum())
+    assert abs((k * np_(out["grad_dur"]).astype(np.float64)).sum() - total) < 1e-4 * total
+    score, labels, seg = crf.viterbi(em, lengths, trans, dur, check_status=True)
+    vref = {"score": ref["score"], "margin": ref["margin"]}
+    if "labels" in ref:
+        vref["labels"], vref["seg_start"] = ref["labels"], ref["seg_start"]
+    check_viterbi(w, np_(score), np_(labels), np_(seg), vref)
