@@ -74,12 +74,13 @@ def centered_prefix(em_b: np.ndarray, L: int, nu: np.ndarray | None = None):
     em_b: [T, C]; only rows t < L are used.  Returns (nu [C], S [L+1, C]) in
     fp64 with S[0] = 0 and S[t] = sum_{u<t} (em[u] - nu).  Passing ``nu``
     freezes the centring mean (used to isolate d logZ / d S)."""
-    x = np.asarray(em_b[:L], dtype=np.float64)
-    if nu is None:
-        nu = x.mean(axis=0)
+    # Accumulated in extended precision and rounded to fp64: a sequential fp64
+    # cumulative sum drifts by up to ~T * 2^-53 * max|S| (about 1e-7 at T = 1e6).
+    x = np.asarray(em_b[:L], dtype=np.longdouble)
+    nu_l = x.mean(axis=0) if nu is None else np.asarray(nu, dtype=np.longdouble)
     S = np.zeros((L + 1, x.shape[1]), dtype=np.float64)
-    S[1:] = np.cumsum(x - nu[None, :], axis=0)
-    return nu, S
+    S[1:] = np.cumsum(x - nu_l[None, :], axis=0).astype(np.float64)
+    return nu_l.astype(np.float64), S
 
 
 def _trans_with_start(trans: np.ndarray) -> np.ndarray:
