@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Throughput of the streaming semi-CRF hot path on one MI355X.
+
+One step = one pass of every hot-path stage over one batch of the genomic
+workload (B=4, T=100,000, K=200, C=6, synthetic, seeded): semicrf_backward
+(centring + prefix scan, forward and backward checkpoint sweeps, span recompute,
+segment posteriors, marginals and gradients, log Z) followed by semicrf_viterbi
+(prefix scan, max-plus sweep, backtrace).  Inputs are resident in HBM before the
+timed region; W warm-up steps, then K timed steps between two device
+synchronisations.  Prints one JSON line.
+
+The roofline object describes the dominant kernel (the checkpoint sweep pair,
+timed live with events recorded by the library on the stream it launches on):
+algorithmic transcendental operations per launch / its mean duration, against the
+chip's exp2/log2 issue rate (256 CUs x 32 lanes/clock x 2.4 GHz: transcendentals
+issue at half the 64 lanes/clock of plain fp32 ops on gfx950).  The centring +
+prefix scan is also reported against HBM bandwidth on a shape larger than the
+256 MB last-level cache.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+CONFIG = 2                       # genomic: B=4, T=1e5, K=200, C=6
+PEAK_TRANS_PER_S = 256 * 32 * 2.4e9     # exp2/log2 issue: half of 64 lanes/clock per CU
+PEAK_HBM_BPS = 8.0e12
+
+
+def hip_runtime():
+    hip = ctypes.CDLL("libamdhip64.so.7")       # the runtime torch already loaded
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+class EventSet:
+    """n+1 HIP events per step for a staged call (stage i spans events i..i+1)."""
+
+    def __init__(self, hip, steps, nstages):
+        self.hip, self.n = hip, nstages + 1
+        self.arr = [(ctypes.c_void_p * self.n)() for _ in range(steps)]
+        for a in self.arr:
+            for i in range(self.n):
+                p = ctypes.c_void_p()
+                assert hip.hipEventCreate(ctypes.byref(p)) == 0
+                a[i] = p.value
+
+    def stage_ms(self):
+        out = []
+        for a in self.arr:
+            row = []
+            for i in range(self.n - 1):
+                ms = ctypes.c_float()
+                assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a[i], a[i + 1]) == 0
+                row.append(ms.value)
+            out.append(row)
+        return out
+
+    def close(self):
+        for a in self.arr:
+            for i in range(self.n):
+                self.hip.hipEventDestroy(a[i])
+
+
+def cpu_baseline(w, sample_positions):
+    """The fp64 oracle (untuned) on one host core: forward, backward, posteriors and
+    Viterbi over the first `sample_positions` positions of sequence 0."""
+    import oracle
+    t0 = time.perf_counter()
+    oracle.sequence(w.em[0], sample_positions, w.trans, w.dur, w.K, want_viterbi=True,
+                    want_grads=True)
+    dt = time.perf_counter() - t0
+    return {"value": sample_positions / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"fwd+bwd+posteriors+viterbi over positions [0, {sample_positions}) of "
+                      f"sequence 0 of the genomic workload, fp64 NumPy, one process",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--delta", type=int, default=0, help="checkpoint interval (0: ceil(sqrt(TK)))")
+    ap.add_argument("--cpu-sample", type=int, default=12_000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-scan-roofline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
+              f"multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import semi_markov_crf_amd as crf
+    import workloads
+    from semi_markov_crf_amd import _native
+
+    lib = _native.load()
+    hip = hip_runtime()
+    w = workloads.make(CONFIG)
+    d = torch.device("cuda:0")
+    em = torch.from_numpy(w.em).to(d)
+    lengths = torch.from_numpy(w.lengths).to(d)
+    trans = torch.from_numpy(w.trans).to(d)
+    dur = torch.from_numpy(w.dur).to(d)
+    B, T, C, K = w.B, w.T, w.C, w.K
+    delta = crf.checkpoint_interval(T, K, args.delta)
+    nb = crf.workspace_bytes(crf.OP_BACKWARD, B, T, C, K, args.delta)
+    nv = crf.workspace_bytes(crf.OP_VITERBI, B, T, C, K)
+    ws_b = torch.empty(nb, dtype=torch.uint8, device=d)
+    ws_v = torch.empty(nv, dtype=torch.uint8, device=d)
+    g_em, g_tr, g_du = torch.empty_like(em), torch.empty_like(trans), torch.empty_like(dur)
+    mu, lz = torch.empty_like(em), torch.empty(B, dtype=torch.float32, device=d)
+    score = torch.empty(B, dtype=torch.float32, device=d)
+    labels = torch.empty((B, T), dtype=torch.int32, device=d)
+    seg = torch.empty((B, T), dtype=torch.uint8, device=d)
+    stream = torch.cuda.current_stream(d).cuda_stream
+
+    def step(ev_b=None, ev_v=None):
+        if ev_b is None:
+            rc = lib.semicrf_backward(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
+                                      dur.data_ptr(), B, T, C, K, args.delta, stream,
+                                      ws_b.data_ptr(), nb, None, g_em.data_ptr(), g_tr.data_ptr(),
+                                      g_du.data_ptr(), mu.data_ptr(), lz.data_ptr())
+        else:
+            rc = lib.semicrf_backward_staged(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
+                                             dur.data_ptr(), B, T, C, K, args.delta, stream,
+                                             ws_b.data_ptr(), nb, None, g_em.data_ptr(),
+                                             g_tr.data_ptr(), g_du.data_ptr(), mu.data_ptr(),
+                                             lz.data_ptr(), ev_b)
+        _native.check("semicrf_backward", rc)
+        if ev_v is None:
+            rc = lib.semicrf_viterbi(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
+                                     dur.data_ptr(), B, T, C, K, stream, ws_v.data_ptr(), nv,
+                                     score.data_ptr(), labels.data_ptr(), seg.data_ptr())
+        else:
+            rc = lib.semicrf_viterbi_staged(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
+                                            dur.data_ptr(), B, T, C, K, stream, ws_v.data_ptr(),
+                                            nv, score.data_ptr(), labels.data_ptr(),
+                                            seg.data_ptr(), ev_v)
+        _native.check("semicrf_viterbi", rc)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(d)
+    assert crf.read_status(ws_b) == 0 and crf.read_status(ws_v) == 0
+
+    evb = EventSet(hip, args.steps, _native.STAGES["backward"])
+    evv = EventSet(hip, args.steps, _native.STAGES["viterbi"])
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(d)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(evb.arr[i], evv.arr[i])
+    t_end.record()
+    torch.cuda.synchronize(d)
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    sb = np.array(evb.stage_ms())
+    sv = np.array(evv.stage_ms())
+    evb.close(); evv.close()
+    assert np.isfinite(lz.cpu().numpy()).all()
+
+    positions = w.positions()
+    value = positions / (ms_step * 1e-3)
+    bwd_ms = float(sb.sum(axis=1).mean())
+    vit_ms = float(sv.sum(axis=1).mean())
+    # dominant kernel: both checkpoint sweeps in one launch (stage 1), or the span
+    # recompute when delta >= T
+    nspans = -(-T // delta)
+    dom_stage = 1 if nspans > 1 else 2
+    dom_ms = float(sb[:, dom_stage].mean())
+    trans_per_pos = K * C + C * C + 2 * C          # exp2 of the K*C and C*C terms, 2C log2
+    algo = 2 * positions * trans_per_pos           # both directions
+    achieved = algo / (dom_ms * 1e-3)
+    busy_cus = 2 * B if dom_stage == 1 else min(256, 2 * B * nspans)
+
+    out = {
+        "metric": "fwd+bwd positions/s at T=1e5,K=200,C=6; % of VALU-exp/HBM roofline",
+        "value": value,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"genomic semi-CRF B={B} T={T} K={K} C={C}, delta={delta} "
+                               f"({nspans} checkpoint spans); step = semicrf_backward + "
+                               f"semicrf_viterbi",
+                   "B": B, "T": T, "K": K, "C": C, "delta": delta, "parallelism": "none (1 GPU)"},
+        "roofline": {
+            "bound": "alu",
+            "kernel": "k_sweep (checkpoint sweeps, forward and backward in one launch)",
+            "achieved": achieved / 1e12,
+            "peak": PEAK_TRANS_PER_S / 1e12,
+            "unit": "Ttrans/s",
+            "frac": achieved / PEAK_TRANS_PER_S,
+            "traffic": None,
+            "algorithmic_per_launch": algo,
+            "launch_ms": dom_ms,
+            "busy_cus": busy_cus,
+            "frac_of_busy_cus": achieved / (PEAK_TRANS_PER_S * busy_cus / 256),
+        },
+        "stages_ms": {
+            "backward": dict(zip(["prefix", "ckpt_sweeps", "span_recompute", "posteriors",
+                                  "marginals_grads"], sb.mean(axis=0).round(4).tolist())),
+            "viterbi": dict(zip(["prefix", "maxplus_sweep", "backtrace"],
+                                sv.mean(axis=0).round(4).tolist())),
+        },
+        "fwd_bwd_positions_per_s": positions / (bwd_ms * 1e-3),
+        "viterbi_positions_per_s": positions / (vit_ms * 1e-3),
+        "edges_per_s_nominal": positions * K * C * C / (bwd_ms * 1e-3),
+        "wall_s_timed_region": wall,
+    }
+
+    if not args.no_scan_roofline:
+        # centring + prefix scan alone on a shape far larger than the last-level cache
+        Bs, Ts = 64, 1 << 20
+        em_big = torch.randn((Bs, Ts, C), dtype=torch.float32, device=d)
+        len_big = torch.full((Bs,), Ts, dtype=torch.int32, device=d)
+        S_big = torch.empty((Bs, Ts + 1, C), dtype=torch.float64, device=d)
+        nws = crf.workspace_bytes(crf.OP_PREFIX, Bs, Ts, C, 1)
+        ws_s = torch.empty(nws, dtype=torch.uint8, device=d)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(4):
+            e0.record()
+            _native.check("semicrf_prefix", lib.semicrf_prefix(
+                em_big.data_ptr(), len_big.data_ptr(), Bs, Ts, C, stream, ws_s.data_ptr(), nws,
+                S_big.data_ptr()))
+            e1.record()
+            torch.cuda.synchronize(d)
+            times.append(e0.elapsed_time(e1))
+        ms = min(times[1:])
+        nbytes = Bs * Ts * C * (4 + 4 + 8)        # em read twice (mean, then scan), S written
+        out["scan_roofline"] = {"bound": "hbm", "shape": f"B={Bs} T={Ts} C={C}",
+                                "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": 8000.0,
+                                "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / PEAK_HBM_BPS,
+                                "ms": ms, "algorithmic_bytes": nbytes}
+        del em_big, S_big, ws_s
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,7 +33,8 @@
  *    reductions, no floating-point atomics).
  *  - Errors: every call returns a semicrf_status and never aborts.  Host-side
  *    checks: B, T, C, K >= 1, required pointers non-NULL, workspace large enough,
- *    shape supported (SEMICRF_ERR_UNSUPPORTED: C > 1024 or K > 1024).  A failed
+ *    shape supported (SEMICRF_ERR_UNSUPPORTED: C > 128; K above 2048 when C <= 16,
+ *    1024 when C <= 32, 512 when C <= 64, 256 when C <= 128).  A failed
  *    kernel launch returns SEMICRF_ERR_DEVICE.  A length outside [1, T] is only
  *    visible on the device: that sequence is processed as if clamped to [1, T],
  *    its log Z / Viterbi score is set to NaN, and a flag is raised in the
@@ -64,7 +65,8 @@ typedef enum {
 typedef enum {
     SEMICRF_OP_LOGZ = 0,
     SEMICRF_OP_BACKWARD = 1,
-    SEMICRF_OP_VITERBI = 2
+    SEMICRF_OP_VITERBI = 2,
+    SEMICRF_OP_PREFIX = 3
 } semicrf_op;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -78,6 +80,15 @@ int semicrf_checkpoint_interval(int T, int K, int delta);
 /* Bytes of workspace that `op` needs for these shapes (delta as above; ignored by
  * LOGZ and VITERBI).  0 if the arguments are invalid or unsupported. */
 size_t semicrf_workspace_bytes(int op, int B, int T, int C, int K, int delta);
+
+/* Centred prefix sums alone (EN explainer, "2. Methodology": "Emission Baseline
+ * Centering" then "On-the-Fly Edge Computation via Prefix Sums"):
+ *   S[b, 0, c] = 0,  S[b, t, c] = sum_{u < t} (em[b, u, c] - nu[b, c])  for t <= L_b,
+ * nu[b, c] = mean of em[b, :L_b, c]; S[b, t, c] = S[b, L_b, c] for t > L_b.
+ * Output: S [B, T+1, C] float64 (device).  Workspace: semicrf_workspace_bytes(
+ * SEMICRF_OP_PREFIX, ...).  The other calls compute the same S internally. */
+int semicrf_prefix(const float* emissions, const int32_t* lengths, int B, int T, int C,
+                   hipStream_t stream, void* workspace, size_t workspace_bytes, double* S);
 
 /* log Z for every sequence: the log-sum-exp of the scores of all segmentations
  * (EN explainer, "2. Methodology", "Streaming Forward-Backward with Ring Buffers",
@@ -115,6 +126,33 @@ int semicrf_viterbi(const float* emissions, const int32_t* lengths, const float*
                     const float* dur, int B, int T, int C, int K, hipStream_t stream,
                     void* workspace, size_t workspace_bytes, float* best_score,
                     int32_t* labels, uint8_t* seg_start);
+
+/* Stage-timed variants, for profiling.  Identical results to the calls above; in
+ * addition, events[i] (created by the caller with hipEventCreate) is recorded on
+ * `stream` when stage i begins, and events[NSTAGES] when the call's work ends, so
+ * hipEventElapsedTime(events[i], events[i+1]) is the device time of stage i.
+ * events must be non-NULL (else SEMICRF_ERR_INVALID).  No synchronisation.
+ *   logz:     0 centring + prefix scan, 1 forward sweep
+ *   backward: 0 centring + prefix scan, 1 checkpoint sweeps (both directions at once;
+ *             empty when delta >= T), 2 span recompute, 3 segment posteriors,
+ *             4 node marginals and gradient reductions
+ *   viterbi:  0 centring + prefix scan, 1 max-plus sweep, 2 backtrace */
+#define SEMICRF_LOGZ_STAGES 2
+#define SEMICRF_BACKWARD_STAGES 5
+#define SEMICRF_VITERBI_STAGES 3
+int semicrf_logz_staged(const float* emissions, const int32_t* lengths, const float* trans,
+                        const float* dur, int B, int T, int C, int K, hipStream_t stream,
+                        void* workspace, size_t workspace_bytes, float* log_z,
+                        hipEvent_t* events);
+int semicrf_backward_staged(const float* emissions, const int32_t* lengths, const float* trans,
+                            const float* dur, int B, int T, int C, int K, int delta,
+                            hipStream_t stream, void* workspace, size_t workspace_bytes,
+                            const float* grad_log_z, float* grad_emissions, float* grad_trans,
+                            float* grad_dur, float* marginals, float* log_z, hipEvent_t* events);
+int semicrf_viterbi_staged(const float* emissions, const int32_t* lengths, const float* trans,
+                           const float* dur, int B, int T, int C, int K, hipStream_t stream,
+                           void* workspace, size_t workspace_bytes, float* best_score,
+                           int32_t* labels, uint8_t* seg_start, hipEvent_t* events);
 
 /* Synchronously reads the device status flag left in `workspace` by the last call
  * that used it (after waiting for `stream`).  SEMICRF_OK, SEMICRF_ERR_INVALID if a

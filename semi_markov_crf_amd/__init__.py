@@ -19,11 +19,11 @@ from __future__ import annotations
 import torch
 
 from . import _native
-from ._native import OP_BACKWARD, OP_LOGZ, OP_VITERBI, SemiCRFError
+from ._native import OP_BACKWARD, OP_LOGZ, OP_PREFIX, OP_VITERBI, SemiCRFError
 
-__all__ = ["logz", "backward", "viterbi", "log_partition", "workspace_bytes",
+__all__ = ["prefix", "logz", "backward", "viterbi", "log_partition", "workspace_bytes",
            "checkpoint_interval", "read_status", "SemiCRFError",
-           "OP_LOGZ", "OP_BACKWARD", "OP_VITERBI"]
+           "OP_LOGZ", "OP_BACKWARD", "OP_VITERBI", "OP_PREFIX"]
 
 
 def checkpoint_interval(T: int, K: int, delta: int = 0) -> int:
@@ -32,6 +32,24 @@ def checkpoint_interval(T: int, K: int, delta: int = 0) -> int:
 
 def workspace_bytes(op: int, B: int, T: int, C: int, K: int, delta: int = 0) -> int:
     return int(_native.load().semicrf_workspace_bytes(op, B, T, C, K, delta))
+
+
+def prefix(em, lengths, *, workspace=None, check_status=False) -> torch.Tensor:
+    """Centred prefix sums S [B, T+1, C] float64."""
+    if em.dim() != 3 or em.dtype != torch.float32 or lengths.dtype != torch.int32:
+        raise TypeError("emissions float32 [B, T, C] and lengths int32 [B] required")
+    if em.device.type != "cuda" or lengths.device != em.device:
+        raise ValueError("emissions and lengths must be on the same GPU")
+    if not (em.is_contiguous() and lengths.is_contiguous()) or lengths.shape != em.shape[:1]:
+        raise ValueError("contiguous emissions [B, T, C] and lengths [B] required")
+    B, T, C = (int(v) for v in em.shape)
+    ws, n = _workspace(OP_PREFIX, B, T, C, 1, 0, em.device, workspace)
+    S = torch.empty((B, T + 1, C), dtype=torch.float64, device=em.device)
+    rc = _native.load().semicrf_prefix(em.data_ptr(), lengths.data_ptr(), B, T, C,
+                                       _stream(em.device), ws.data_ptr(), n, S.data_ptr())
+    _native.check("semicrf_prefix", rc)
+    _maybe_check(ws, check_status, "semicrf_prefix")
+    return S
 
 
 def _check_inputs(em, lengths, trans, dur):

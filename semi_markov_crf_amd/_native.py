@@ -14,7 +14,7 @@ import torch  # noqa: F401  (must precede the dlopen below, see module docstring
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsemicrf.so")
 
-OP_LOGZ, OP_BACKWARD, OP_VITERBI = 0, 1, 2
+OP_LOGZ, OP_BACKWARD, OP_VITERBI, OP_PREFIX = 0, 1, 2, 3
 STATUS_NAMES = {0: "SEMICRF_OK", 1: "SEMICRF_ERR_INVALID", 2: "SEMICRF_ERR_WORKSPACE",
                 3: "SEMICRF_ERR_UNSUPPORTED", 4: "SEMICRF_ERR_DEVICE"}
 
@@ -32,7 +32,15 @@ SIGNATURES = {
     "semicrf_viterbi": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
                                  _c_size, _vp, _vp, _vp]),
     "semicrf_read_status": (_c_int, [_vp, _vp]),
+    "semicrf_prefix": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
+    "semicrf_logz_staged": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
+                                     _c_size, _vp, _vp]),
+    "semicrf_backward_staged": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                         _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "semicrf_viterbi_staged": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
+                                        _c_size, _vp, _vp, _vp, _vp]),
 }
+STAGES = {"logz": 2, "backward": 5, "viterbi": 3}
 
 
 class SemiCRFError(RuntimeError):

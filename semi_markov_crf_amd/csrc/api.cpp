@@ -93,6 +93,10 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         lo.zt = m.take(sizeof(double) * B * lo.ntm);
         lo.pd = m.take(sizeof(double) * B * lo.ntm * K * C);
         lo.pt = m.take(sizeof(double) * B * lo.ntm * C * C);
+    } else if (op == SEMICRF_OP_PREFIX) {
+        // S goes to the caller's buffer: drop the internal copy
+        lo.total = lo.S;
+        return true;
     } else if (op == SEMICRF_OP_VITERBI) {
         lo.bp = m.take(sizeof(uint32_t) * BT1C);
         lo.vscore = m.take(sizeof(double) * B);
@@ -119,6 +123,13 @@ int check_ws(void* ws, size_t have, const Layout& lo) {
 #define LAUNCH(expr)                                   \
     do {                                               \
         if ((expr) != hipSuccess) return SEMICRF_ERR_DEVICE; \
+    } while (0)
+
+// Optional stage timing: events[i] is recorded on the stream before stage i.
+#define STAGE(i)                                                                   \
+    do {                                                                           \
+        if (events && hipEventRecord(events[i], stream) != hipSuccess)             \
+            return SEMICRF_ERR_DEVICE;                                             \
     } while (0)
 
 // centring + prefix sums: fills Leff, status and S
@@ -163,6 +174,23 @@ const char* semicrf_status_string(int status) {
 
 int semicrf_checkpoint_interval(int T, int K, int delta) { return resolve_delta(T, K, delta); }
 
+int semicrf_prefix(const float* em, const int32_t* lengths, int B, int T, int C,
+                   hipStream_t stream, void* workspace, size_t workspace_bytes, double* S) {
+    if (!em || !lengths || !S) return SEMICRF_ERR_INVALID;
+    if (!shape_ok(B, T, C, 1)) return SEMICRF_ERR_INVALID;
+    Layout lo;
+    if (!make_layout(SEMICRF_OP_PREFIX, B, T, C, 1, 0, lo)) return SEMICRF_ERR_UNSUPPORTED;
+    int rc = check_ws(workspace, workspace_bytes, lo);
+    if (rc) return rc;
+    int* Leff = at<int>(workspace, lo.Leff);
+    LAUNCH(launch_em_tile_sums(em, lengths, B, T, C, at<double>(workspace, lo.tsum), Leff, stream));
+    LAUNCH(launch_tile_scan(at<double>(workspace, lo.tsum), B, lo.nts, C, false,
+                            at<double>(workspace, lo.toff), at<double>(workspace, lo.ttot), stream));
+    LAUNCH(launch_prefix(em, Leff, B, T, C, at<double>(workspace, lo.toff),
+                         at<double>(workspace, lo.ttot), S, at<int>(workspace, lo.status), stream));
+    return SEMICRF_OK;
+}
+
 size_t semicrf_workspace_bytes(int op, int B, int T, int C, int K, int delta) {
     Layout lo;
     if (!make_layout(op, B, T, C, K, delta, lo)) return 0;
@@ -177,36 +205,42 @@ static int common_checks(const float* em, const int32_t* lengths, const float* t
     return SEMICRF_OK;
 }
 
-int semicrf_logz(const float* em, const int32_t* lengths, const float* trans, const float* dur,
-                 int B, int T, int C, int K, hipStream_t stream, void* workspace,
-                 size_t workspace_bytes, float* log_z) {
+static int run_logz(const float* em, const int32_t* lengths, const float* trans, const float* dur,
+                    int B, int T, int C, int K, hipStream_t stream, void* workspace,
+                    size_t workspace_bytes, float* log_z, hipEvent_t* events) {
     int rc = common_checks(em, lengths, trans, dur, B, T, C, K);
     if (rc) return rc;
     if (!log_z) return SEMICRF_ERR_INVALID;
     Layout lo;
     if (!make_layout(SEMICRF_OP_LOGZ, B, T, C, K, 0, lo)) return SEMICRF_ERR_UNSUPPORTED;
     if ((rc = check_ws(workspace, workspace_bytes, lo))) return rc;
+    STAGE(0);
     if ((rc = run_prefix(em, lengths, B, T, C, workspace, lo, stream))) return rc;
+    STAGE(1);
     const SweepCfg cfg = choose_sweep(C, K);
     SweepArgs a = base_args(trans, dur, B, T, C, K, workspace, lo);
     a.mode = MODE_FULL;
     a.logz = at<double>(workspace, lo.logz);
     LAUNCH(launch_sweep(cfg, false, a, 1, stream));
     LAUNCH(launch_write_logz(a.logz, B, log_z, stream));
+    STAGE(2);
     return SEMICRF_OK;
 }
 
-int semicrf_backward(const float* em, const int32_t* lengths, const float* trans, const float* dur,
-                     int B, int T, int C, int K, int delta, hipStream_t stream, void* workspace,
-                     size_t workspace_bytes, const float* grad_log_z, float* grad_em,
-                     float* grad_trans, float* grad_dur, float* marginals, float* log_z) {
+static int run_backward(const float* em, const int32_t* lengths, const float* trans,
+                        const float* dur, int B, int T, int C, int K, int delta,
+                        hipStream_t stream, void* workspace, size_t workspace_bytes,
+                        const float* grad_log_z, float* grad_em, float* grad_trans,
+                        float* grad_dur, float* marginals, float* log_z, hipEvent_t* events) {
     int rc = common_checks(em, lengths, trans, dur, B, T, C, K);
     if (rc) return rc;
     if (!grad_em || !grad_trans || !grad_dur || delta < 0) return SEMICRF_ERR_INVALID;
     Layout lo;
     if (!make_layout(SEMICRF_OP_BACKWARD, B, T, C, K, delta, lo)) return SEMICRF_ERR_UNSUPPORTED;
     if ((rc = check_ws(workspace, workspace_bytes, lo))) return rc;
+    STAGE(0);
     if ((rc = run_prefix(em, lengths, B, T, C, workspace, lo, stream))) return rc;
+    STAGE(1);
     const SweepCfg cfg = choose_sweep(C, K);
     SweepArgs a = base_args(trans, dur, B, T, C, K, workspace, lo);
     a.delta = lo.delta;
@@ -228,11 +262,13 @@ int semicrf_backward(const float* em, const int32_t* lengths, const float* trans
         a.write_xa = 0;
         LAUNCH(launch_sweep(cfg, false, a, 2, stream));
     }
+    STAGE(2);
     // recompute every checkpoint span in parallel, writing the per-position values
     a.mode = MODE_SPAN;
     a.write_ckpt = 0;
     a.write_xa = 1;
     LAUNCH(launch_sweep(cfg, false, a, 2, stream));
+    STAGE(3);
 
     MargArgs m{};
     m.S = a.S; m.Leff = a.Leff; m.trans = trans; m.dur = dur;
@@ -244,6 +280,7 @@ int semicrf_backward(const float* em, const int32_t* lengths, const float* trans
     m.part_dur = at<double>(workspace, lo.pd);
     m.part_trans = at<double>(workspace, lo.pt);
     LAUNCH(launch_marginals(m, stream));
+    STAGE(4);
     LAUNCH(launch_tile_scan(m.dn_tile, B, lo.ntm, C, false, at<double>(workspace, lo.dno), nullptr,
                             stream));
     float* mu = marginals ? marginals : at<float>(workspace, lo.mu);
@@ -258,20 +295,23 @@ int semicrf_backward(const float* em, const int32_t* lengths, const float* trans
                                   grad_log_z, B, T, C, K, lo.tm, lo.ntm, grad_dur, grad_trans,
                                   stream));
     if (log_z) LAUNCH(launch_write_logz(a.logz, B, log_z, stream));
+    STAGE(5);
     return SEMICRF_OK;
 }
 
-int semicrf_viterbi(const float* em, const int32_t* lengths, const float* trans, const float* dur,
-                    int B, int T, int C, int K, hipStream_t stream, void* workspace,
-                    size_t workspace_bytes, float* best_score, int32_t* labels,
-                    uint8_t* seg_start) {
+static int run_viterbi(const float* em, const int32_t* lengths, const float* trans,
+                       const float* dur, int B, int T, int C, int K, hipStream_t stream,
+                       void* workspace, size_t workspace_bytes, float* best_score,
+                       int32_t* labels, uint8_t* seg_start, hipEvent_t* events) {
     int rc = common_checks(em, lengths, trans, dur, B, T, C, K);
     if (rc) return rc;
     if (!best_score || !labels || !seg_start) return SEMICRF_ERR_INVALID;
     Layout lo;
     if (!make_layout(SEMICRF_OP_VITERBI, B, T, C, K, 0, lo)) return SEMICRF_ERR_UNSUPPORTED;
     if ((rc = check_ws(workspace, workspace_bytes, lo))) return rc;
+    STAGE(0);
     if ((rc = run_prefix(em, lengths, B, T, C, workspace, lo, stream))) return rc;
+    STAGE(1);
     const SweepCfg cfg = choose_sweep(C, K);
     SweepArgs a = base_args(trans, dur, B, T, C, K, workspace, lo);
     a.mode = MODE_FULL;
@@ -279,9 +319,64 @@ int semicrf_viterbi(const float* em, const int32_t* lengths, const float* trans,
     a.vscore = at<double>(workspace, lo.vscore);
     a.vcstar = at<int>(workspace, lo.vcstar);
     LAUNCH(launch_sweep(cfg, true, a, 1, stream));
+    STAGE(2);
     LAUNCH(launch_backtrace(a.bp, a.vscore, a.vcstar, a.Leff, B, T, C, at<int32_t>(workspace, lo.seg),
                             best_score, labels, seg_start, stream));
+    STAGE(3);
     return SEMICRF_OK;
+}
+
+int semicrf_logz(const float* em, const int32_t* lengths, const float* trans, const float* dur,
+                 int B, int T, int C, int K, hipStream_t stream, void* workspace,
+                 size_t workspace_bytes, float* log_z) {
+    return run_logz(em, lengths, trans, dur, B, T, C, K, stream, workspace, workspace_bytes, log_z,
+                    nullptr);
+}
+
+int semicrf_logz_staged(const float* em, const int32_t* lengths, const float* trans,
+                        const float* dur, int B, int T, int C, int K, hipStream_t stream,
+                        void* workspace, size_t workspace_bytes, float* log_z,
+                        hipEvent_t* events) {
+    if (!events) return SEMICRF_ERR_INVALID;
+    return run_logz(em, lengths, trans, dur, B, T, C, K, stream, workspace, workspace_bytes, log_z,
+                    events);
+}
+
+int semicrf_backward(const float* em, const int32_t* lengths, const float* trans, const float* dur,
+                     int B, int T, int C, int K, int delta, hipStream_t stream, void* workspace,
+                     size_t workspace_bytes, const float* grad_log_z, float* grad_em,
+                     float* grad_trans, float* grad_dur, float* marginals, float* log_z) {
+    return run_backward(em, lengths, trans, dur, B, T, C, K, delta, stream, workspace,
+                        workspace_bytes, grad_log_z, grad_em, grad_trans, grad_dur, marginals, log_z,
+                        nullptr);
+}
+
+int semicrf_backward_staged(const float* em, const int32_t* lengths, const float* trans,
+                            const float* dur, int B, int T, int C, int K, int delta,
+                            hipStream_t stream, void* workspace, size_t workspace_bytes,
+                            const float* grad_log_z, float* grad_em, float* grad_trans,
+                            float* grad_dur, float* marginals, float* log_z, hipEvent_t* events) {
+    if (!events) return SEMICRF_ERR_INVALID;
+    return run_backward(em, lengths, trans, dur, B, T, C, K, delta, stream, workspace,
+                        workspace_bytes, grad_log_z, grad_em, grad_trans, grad_dur, marginals, log_z,
+                        events);
+}
+
+int semicrf_viterbi(const float* em, const int32_t* lengths, const float* trans, const float* dur,
+                    int B, int T, int C, int K, hipStream_t stream, void* workspace,
+                    size_t workspace_bytes, float* best_score, int32_t* labels,
+                    uint8_t* seg_start) {
+    return run_viterbi(em, lengths, trans, dur, B, T, C, K, stream, workspace, workspace_bytes,
+                       best_score, labels, seg_start, nullptr);
+}
+
+int semicrf_viterbi_staged(const float* em, const int32_t* lengths, const float* trans,
+                           const float* dur, int B, int T, int C, int K, hipStream_t stream,
+                           void* workspace, size_t workspace_bytes, float* best_score,
+                           int32_t* labels, uint8_t* seg_start, hipEvent_t* events) {
+    if (!events) return SEMICRF_ERR_INVALID;
+    return run_viterbi(em, lengths, trans, dur, B, T, C, K, stream, workspace, workspace_bytes,
+                       best_score, labels, seg_start, events);
 }
 
 int semicrf_read_status(const void* workspace, hipStream_t stream) {

@@ -20,14 +20,20 @@ int marg_tile(int C, int K);
 // ------------------------------------------------------------------ sweep configuration
 // Lanes are grouped G per label; each lane covers KPL durations and CPL previous labels.
 struct SweepCfg {
-    int G, KPL, CPL;     // instantiated kernel shape
+    int G, KPL, CPL, GT; // instantiated kernel shape (KPL: register capacity per lane)
+    int kpl;             // durations k >= 3 per lane actually used
     int NT;              // threads per workgroup (multiple of 64)
-    int RS, RSP;         // ring slots (power of two >= K+1) and padded row pitch
+    int RS, RSP;         // ring slots (power of two) and the padded row pitch
     int CH;              // positions per prefetch chunk of S
-    size_t lds_bytes;    // dynamic LDS
+    size_t lds_bytes;    // dynamic LDS (log-sum-exp sweep)
+    size_t lds_bytes_vit;  // dynamic LDS (max-plus sweep)
+    int layout;          // SWEEP_MIRRORED | SWEEP_LINEAR bits
     bool ok;
 };
 SweepCfg choose_sweep(int C, int K);
+// ring layout bits: each position stored twice, RS apart (contiguous windows); E = 2^R
+// ring for the linear-space bulk sum of the log-sum-exp sweep
+enum { SWEEP_MIRRORED = 1, SWEEP_LINEAR = 2 };
 
 enum SweepMode { MODE_FULL = 0, MODE_SPAN = 1 };
 

@@ -79,7 +79,8 @@ def test_workspace_bytes(native):
         assert ws(op, 4, 2000, 6, 20, 0) > a           # and with T
     # backward holds O(B*T*C) per-position values plus checkpoints
     assert ws(1, 1, 10_000, 6, 200, 0) > 5 * 8 * 10_001 * 6
-    assert ws(3, 1, 10, 2, 2, 0) == 0                  # unknown op
+    assert ws(4, 1, 10, 2, 2, 0) == 0                  # unknown op
+    assert 0 < ws(3, 1, 10, 2, 2, 0) < ws(0, 1, 10, 2, 2, 0)   # prefix: S goes to the caller
     assert ws(0, 0, 10, 2, 2, 0) == 0 and ws(0, 1, 0, 2, 2, 0) == 0
     assert ws(0, 1, 10, 2000, 2, 0) == 0               # C beyond the supported range
     assert ws(0, 1, 10, 2, 70000, 0) == 0              # K beyond 65535
@@ -111,3 +112,9 @@ def test_argument_validation_returns_before_any_launch(native):
     need = lib.semicrf_workspace_bytes(2, 1, 4, 2, 2, 0)
     assert lib.semicrf_viterbi(p, p, p, p, 1, 4, 2, 2, n, p, need, p, n, p) == 1
     assert lib.semicrf_read_status(n, n) == 2
+    need = lib.semicrf_workspace_bytes(3, 1, 4, 2, 1, 0)
+    assert lib.semicrf_prefix(p, p, 1, 4, 2, n, p, need, n) == 1
+    assert lib.semicrf_prefix(p, p, 1, 4, 2, n, p, need - 1, p) == 2
+    for f in ("semicrf_logz_staged", "semicrf_viterbi_staged"):
+        args = [p, p, p, p, 1, 4, 2, 2, n, p, 1 << 20, p] + ([n] if f == "semicrf_logz_staged" else [p, p, n])
+        assert getattr(lib, f)(*args) == 1          # events pointer required
