@@ -32,7 +32,9 @@ FLAGS = [
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
 
-SOURCES = ["api.cpp", "scan.hip", "sweep.hip", "marginals.hip", "viterbi.hip"]
+SOURCES = ["api.cpp", "sweep_cfg.cpp", "scan.hip", "sweep_lse_mirror.hip", "sweep_lse_plain.hip",
+           "sweep_lse_log.hip", "sweep_maxplus_mirror.hip", "sweep_maxplus_plain.hip",
+           "marginals.hip", "viterbi.hip"]
 
 
 def _compile(src: str) -> str:

@@ -221,7 +221,7 @@ static int run_logz(const float* em, const int32_t* lengths, const float* trans,
     SweepArgs a = base_args(trans, dur, B, T, C, K, workspace, lo);
     a.mode = MODE_FULL;
     a.logz = at<double>(workspace, lo.logz);
-    LAUNCH(launch_sweep(cfg, false, a, 1, stream));
+    LAUNCH(launch_lse(cfg, a, 1, stream));
     LAUNCH(launch_write_logz(a.logz, B, log_z, stream));
     STAGE(2);
     return SEMICRF_OK;
@@ -260,14 +260,14 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
         a.mode = MODE_FULL;
         a.write_ckpt = 1;
         a.write_xa = 0;
-        LAUNCH(launch_sweep(cfg, false, a, 2, stream));
+        LAUNCH(launch_lse(cfg, a, 2, stream));
     }
     STAGE(2);
     // recompute every checkpoint span in parallel, writing the per-position values
     a.mode = MODE_SPAN;
     a.write_ckpt = 0;
     a.write_xa = 1;
-    LAUNCH(launch_sweep(cfg, false, a, 2, stream));
+    LAUNCH(launch_lse(cfg, a, 2, stream));
     STAGE(3);
 
     MargArgs m{};
@@ -318,7 +318,7 @@ static int run_viterbi(const float* em, const int32_t* lengths, const float* tra
     a.bp = at<uint32_t>(workspace, lo.bp);
     a.vscore = at<double>(workspace, lo.vscore);
     a.vcstar = at<int>(workspace, lo.vcstar);
-    LAUNCH(launch_sweep(cfg, true, a, 1, stream));
+    LAUNCH(launch_maxplus(cfg, a, stream));
     STAGE(2);
     LAUNCH(launch_backtrace(a.bp, a.vscore, a.vcstar, a.Leff, B, T, C, at<int32_t>(workspace, lo.seg),
                             best_score, labels, seg_start, stream));

@@ -19,21 +19,45 @@ int marg_tile(int C, int K);
 
 // ------------------------------------------------------------------ sweep configuration
 // Lanes are grouped G per label; each lane covers KPL durations and CPL previous labels.
+// ring layout bits: each position stored twice, RS apart (contiguous windows); E = 2^R
+// ring for the linear-space bulk sum of the log-semiring sweep
+enum { SWEEP_MIRRORED = 1, SWEEP_LINEAR = 2 };
+
+struct SweepLds {
+    int layout;          // SWEEP_MIRRORED | SWEEP_LINEAR bits
+    int P;               // ring row pitch (floats)
+    int CH;              // positions per staged chunk of S
+    size_t bytes;        // dynamic LDS per workgroup (0: does not fit)
+};
+
 struct SweepCfg {
     int G, KPL, CPL, GT; // instantiated kernel shape (KPL: register capacity per lane)
     int kpl;             // durations k >= 3 per lane actually used
     int NT;              // threads per workgroup (multiple of 64)
-    int RS, RSP;         // ring slots (power of two) and the padded row pitch
-    int CH;              // positions per prefetch chunk of S
-    size_t lds_bytes;    // dynamic LDS (log-sum-exp sweep)
-    size_t lds_bytes_vit;  // dynamic LDS (max-plus sweep)
-    int layout;          // SWEEP_MIRRORED | SWEEP_LINEAR bits
+    int RS;              // ring slots per copy (power of two)
+    SweepLds lse;        // log-semiring sweep
+    SweepLds vit;        // max-plus sweep
     bool ok;
 };
 SweepCfg choose_sweep(int C, int K);
-// ring layout bits: each position stored twice, RS apart (contiguous windows); E = 2^R
-// ring for the linear-space bulk sum of the log-sum-exp sweep
-enum { SWEEP_MIRRORED = 1, SWEEP_LINEAR = 2 };
+
+// S rows staged per LDS chunk (at most): log-semiring sweep (plus one look-ahead row),
+// max-plus sweep
+__host__ __device__ constexpr int lse_chunk_max(int G) { return G >= 16 ? 64 : 16; }
+constexpr int MAXPLUS_CHUNK_MAX = 64;
+
+// Dynamic LDS of the log-semiring sweep: S chunks [2][CH+1][C] + S(L) [C] (fp64), then
+// the R ring (and the E ring when linear) [C+1][P], messages p and u [2][UP] each, and a
+// per-thread sink [NT] (fp32).
+inline size_t lse_lds_bytes(int C, int NT, int UP, int P, int CH, bool lin) {
+    return (size_t)(2 * (CH + 1) * C + C) * 8 +
+           (size_t)((lin ? 2 : 1) * (C + 1) * P + 4 * UP + NT) * 4;
+}
+// Dynamic LDS of the max-plus sweep: S chunks [2][CH][C] (fp64), R ring [C+1][P] and
+// u [2][UP] (fp32).
+inline size_t maxplus_lds_bytes(int C, int UP, int P, int CH) {
+    return (size_t)(2 * CH * C) * 8 + (size_t)((C + 1) * P + 2 * UP) * 4;
+}
 
 enum SweepMode { MODE_FULL = 0, MODE_SPAN = 1 };
 
@@ -66,8 +90,16 @@ struct SweepArgs {
     int* vcstar;            // [B] final label
 };
 
-hipError_t launch_sweep(const SweepCfg& cfg, bool viterbi, const SweepArgs& a, int ndir,
-                        hipStream_t stream);
+// log-semiring sweep: grid (B, ndir) in MODE_FULL, (nspans, B, ndir) in MODE_SPAN;
+// dispatches on cfg.lse.layout to the per-layout translation units
+hipError_t launch_lse(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream);
+hipError_t launch_lse_mirror(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream);
+hipError_t launch_lse_plain(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream);
+hipError_t launch_lse_log(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream);
+// max-plus sweep (Viterbi): MODE_FULL, forward only, grid (B); dispatches on cfg.vit.layout
+hipError_t launch_maxplus(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream);
+hipError_t launch_maxplus_mirror(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream);
+hipError_t launch_maxplus_plain(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream);
 
 // ------------------------------------------------------------------ scans
 // Per-tile column sums of the valid emissions; also writes the clamped lengths Leff

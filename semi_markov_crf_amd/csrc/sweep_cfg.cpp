@@ -1,0 +1,88 @@
+// Host-side shape selection for the sweep kernels: lane grouping, ring size and the LDS
+// layout that fits the 160 KB of a gfx950 compute unit.
+#include <algorithm>
+
+#include "internal.h"
+
+namespace semicrf {
+
+namespace {
+
+constexpr size_t LDS_BUDGET = 150 * 1024;   // leaves room for the compiler's own LDS use
+
+int pow2_at_least(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+}  // namespace
+
+SweepCfg choose_sweep(int C, int K) {
+    SweepCfg s{};
+    s.ok = false;
+    if (C < 1 || K < 1) return s;
+    // lane groups: aim at <= 4 waves (one per SIMD) where the label count allows
+    int G, CPL, GT;
+    if (C <= 4) { G = 64; GT = 4; CPL = 1; }
+    else if (C <= 8) { G = 32; GT = 8; CPL = 1; }
+    else if (C <= 16) { G = 16; GT = 16; CPL = 1; }
+    else if (C <= 32) { G = 8; GT = 8; CPL = 4; }
+    else if (C <= 64) { G = 8; GT = 8; CPL = 8; }
+    else if (C <= 128) { G = 4; GT = 4; CPL = 32; }
+    else return s;
+    // lanes cover k = 3 .. K+1: the bulk terms plus one more slot kept in the current base
+    const int kpl = K > 1 ? (K - 1 + G - 1) / G : 0;
+    static const int kInst[] = {0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 16, 24, 32};
+    int kmax = -1;
+    for (int v : kInst)
+        if (v >= kpl) { kmax = v; break; }
+    if (kmax < 0) return s;
+    s.G = G; s.KPL = kmax; s.CPL = CPL; s.GT = GT; s.kpl = kpl;
+    s.NT = ((C * G + 63) / 64) * 64;
+    // RS >= K + 2 live positions and >= the widest window a lane addresses (2 + KPL*G)
+    s.RS = pow2_at_least(std::max(K + 2, 3 + kmax * G));
+    const int pad = G < 32 ? G : 0;   // staggers the label rows over the LDS banks
+    const int UP = GT * CPL;
+    auto pitch = [&](int layout) { return ((layout & SWEEP_MIRRORED) ? 2 : 1) * s.RS + pad; };
+
+    // log-semiring sweep: mirrored + linear, plain + linear, plain + log-space only
+    for (int lay : {int(SWEEP_MIRRORED | SWEEP_LINEAR), int(SWEEP_LINEAR), 0}) {
+        const int P = pitch(lay);
+        for (int ch = lse_chunk_max(G); ch >= 8 && s.lse.bytes == 0; ch >>= 1) {
+            const size_t n = lse_lds_bytes(C, s.NT, UP, P, ch, lay & SWEEP_LINEAR);
+            if (n <= LDS_BUDGET) s.lse = SweepLds{lay, P, ch, n};
+        }
+        if (s.lse.bytes) break;
+    }
+    // max-plus sweep: mirrored, then plain
+    for (int lay : {int(SWEEP_MIRRORED), 0}) {
+        const int P = pitch(lay);
+        for (int ch = MAXPLUS_CHUNK_MAX; ch >= 8 && s.vit.bytes == 0; ch >>= 1) {
+            const size_t n = maxplus_lds_bytes(C, UP, P, ch);
+            if (n <= LDS_BUDGET) s.vit = SweepLds{lay, P, ch, n};
+        }
+        if (s.vit.bytes) break;
+    }
+    s.ok = s.NT <= 1024 && s.lse.bytes > 0 && s.vit.bytes > 0;
+    return s;
+}
+
+hipError_t launch_lse(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream) {
+    switch (cfg.lse.layout) {
+        case SWEEP_MIRRORED | SWEEP_LINEAR: return launch_lse_mirror(cfg, a, ndir, stream);
+        case SWEEP_LINEAR: return launch_lse_plain(cfg, a, ndir, stream);
+        case 0: return launch_lse_log(cfg, a, ndir, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_maxplus(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream) {
+    switch (cfg.vit.layout) {
+        case SWEEP_MIRRORED: return launch_maxplus_mirror(cfg, a, stream);
+        case 0: return launch_maxplus_plain(cfg, a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace semicrf

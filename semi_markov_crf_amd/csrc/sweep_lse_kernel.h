@@ -1,0 +1,498 @@
+// Log-semiring streaming sweep on gfx950: forward (alpha) and backward (beta, run as a
+// forward sweep over the mirrored sequence), with checkpoints or per-position outputs.
+//
+// Method ("Streaming Structured Inference with Flash-SemiCRF", gist.science EN explainer,
+// "2. Methodology"): segment potentials S[s+k,c] - S[s,c] + dur[k-1,c] + trans[c',c] are
+// evaluated on the fly from the prefix sums; only a ring of the last K messages per label
+// is kept ("Streaming Forward-Backward with Ring Buffers"); the ring and the cumulative
+// normaliser are written out every delta positions and a later pass restarts from them
+// ("Checkpointing").
+//
+// Factored recurrence (exact: the potential is a sum of a (start, length, label) term and
+// a (previous label, label) term):
+//     abar[s, c]  = LSE_{c'} (alpha[s, c'] + trans[c', c])                  (C^2 terms)
+//     alpha[t, c] = S[t, c] + LSE_k (abar[t-k, c] - S[t-k, c] + dur[k-1, c])    (K*C terms)
+// with abar[0, c] = 0 (no transition into the first segment).  The ring holds
+// A[s, c] = abar[s, c] - S[s, c].  The backward sweep runs the same recurrence on the
+// reversed sequence: S'[t] = S[L] - S[L-t], trans' = trans^T; its "alpha" is beta_bar[s, c]
+// and its "A" is beta[u, c] + S[u, c] - S[L, c].
+//
+// Work layout: one workgroup per (sequence, direction), or per (checkpoint span, sequence,
+// direction) for the recompute.  Lanes form groups of G per label; a group never straddles
+// a wavefront, so each label's ring is private to one wavefront.  Only the per-label
+// message of the newest position crosses groups, through a double-buffered LDS row and one
+// workgroup barrier per position.
+//
+// Arithmetic: base 2, fp32, mostly in LINEAR space.  Every value is kept relative to a
+// reference: ring entries R = A - B_c (per-label fp64 base B_c, moved every REBASE
+// positions) with E = 2^R alongside; messages p[c] = 2^(alpha[t, c] - H) relative to a
+// common fp64 reference H that all groups advance by the same power of two (the exponent
+// of sum_c p).  The steps of position t are then
+//   [C] combine   sig = E(t-1) 2^d0 + E(t-2) 2^d1 + Q(t)           (2 FMAs)
+//       message   p(t) = sig * 2^(S[t] + B_c - H(t-1) + dmax) * 2^-e  (2 multiplies)
+//   [D] bulk      Q(t+2) = sum_k E(t+2-k) 2^(dur[k-1] - dmax)      (one FMA per term)
+//   [B] transition s = sum_c' p(t)[c'] 2^(trans[c', c] - tmax)      -> E(t), R(t)
+// so the chain from one barrier to the next holds a handful of FMAs and one DPP sum, and
+// the logarithms (R, the log-space copy of each message) are off it.  Every linear sum is
+// range-checked: outside [LIN_LO, LIN_HI] (underflow, overflow, inf, NaN, forbidden
+// transitions or durations) that step is recomputed exactly in log space from R and from
+// the log-space messages, so the result never depends on the linear path being in range.
+// Outputs are fp64, natural-log units.
+#pragma once
+
+#include "internal.h"
+#include "ring.h"
+
+namespace semicrf {
+
+namespace {
+
+constexpr float LIN_LO = 0x1p-60f;   // linear sums are trusted inside [LIN_LO, LIN_HI]:
+constexpr float LIN_HI = 0x1p+60f;   // terms lost to fp32 underflow are then < 2^-66 of it
+
+__device__ __forceinline__ double nan_d() { return __longlong_as_double(0x7ff8000000000000LL); }
+// Range test on the bit pattern: false for 0, denormals, negatives, inf and NaN whatever
+// the floating-point flags of the build.
+__device__ __forceinline__ bool in_lin_range(float s) {
+    constexpr uint32_t lo = __builtin_bit_cast(uint32_t, LIN_LO);
+    constexpr uint32_t hi = __builtin_bit_cast(uint32_t, LIN_HI);
+    return __float_as_uint(s) - lo <= hi - lo;
+}
+__device__ __forceinline__ float exp2_or_zero(float x) { return x > NEG_HALF ? fast_exp2(x) : 0.0f; }
+// true in every lane when any lane of the wavefront has `bad` set (a scalar branch)
+__device__ __forceinline__ bool wave_any(bool bad) { return __builtin_amdgcn_ballot_w64(bad) != 0; }
+
+}  // namespace
+
+// G: lanes per label; KPL: durations k >= 3 per lane (k = 3 + j + i*G, i < KPL, covering
+// k <= K + 1); CPL, GT: previous labels per lane and the lane count of the transition
+// reduction (GT * CPL >= C, GT <= G); NTMAX: largest workgroup routed here.
+//
+// Loop iteration t (between the barriers that publish the messages of t and of t+1):
+//   rebase (every REBASE positions)
+//   [B] transition step of position t  ||  [D] bulk sum of position t+2
+//   (one scalar branch: exact log-space redo of any of the three sums out of range)
+//   ring entry of t, normaliser update, checkpoint
+//   [C] message of position t+1 from E(t), E(t-1), bulk(t+1); publish
+// LAY: ring layout bits (SWEEP_MIRRORED, SWEEP_LINEAR), fixed at compile time.
+template <int G, int KPL, int CPL, int GT, int NTMAX, int LAY>
+__global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, const int P,
+                                              const int CH) {
+    constexpr int PF = (lse_chunk_max(G) + 1 + G - 1) / G;   // prefetched doubles per lane
+    constexpr int UP = GT * CPL;                               // padded message row (>= C)
+    constexpr int KP = KPL > 0 ? KPL : 1;
+    extern __shared__ double lds[];
+    const int C = a.C, K = a.K, T = a.T;
+    const int tid = threadIdx.x, NT = blockDim.x;
+    const int c = tid / G;
+    const int j = tid - c * G;
+    const int jt = j & (GT - 1);             // every GT-subgroup repeats the transition step
+    const bool act = c < C;
+    const int cr = act ? c : C;              // inactive lanes use the spare ring row C
+    const int cc = act ? c : 0;
+    const bool writer = act && j == 0;       // one lane per label publishes
+
+    int b, span, dir;
+    if (a.mode == MODE_FULL) {
+        b = blockIdx.x; dir = blockIdx.y; span = 0;
+    } else {
+        span = blockIdx.x; b = blockIdx.y; dir = blockIdx.z;
+    }
+    const int Lr = a.Leff[b];
+    const bool bad = Lr < 0;
+    const int L = bad ? -Lr : Lr;
+    int t0 = 0, t1 = L;
+    if (a.mode == MODE_SPAN) {
+        t0 = span * a.delta;
+        if (t0 >= L) return;
+        t1 = min(L, t0 + a.delta);
+    }
+    const int RMASK = RS - 1;
+    const int rowsN = (CH + 1) * C;           // staged S values per chunk
+    constexpr bool MIR = LAY & SWEEP_MIRRORED;
+    constexpr bool LIN = LAY & SWEEP_LINEAR;
+
+    double* Sbuf = lds;                                   // [2][CH+1][C]
+    double* SL = Sbuf + 2 * rowsN;                        // [C]
+    float* R = (float*)(SL + C);                          // [C+1][P]
+    float* E = R + (C + 1) * P;                           // [C+1][P] (linear bulk only)
+    float* p_sh = E + (LIN ? (C + 1) * P : 0);            // [2][UP] messages, linear
+    float* u_sh = p_sh + 2 * UP;                          // [2][UP] messages, log2
+    float* dummy = u_sh + 2 * UP;                         // [NT] sink for non-publishing lanes
+    float* Rrow = R + cr * P;
+    float* Erow = E + cr * P;
+
+    const double* Sb = a.S + (size_t)b * (T + 1) * C;
+    for (int q = tid; q < C; q += NT) SL[q] = Sb[(size_t)L * C + q];
+    for (int q = tid; q < (C + 1) * P; q += NT) {
+        R[q] = NEG;
+        if constexpr (LIN) E[q] = 0.0f;
+    }
+    for (int q = tid; q < 2 * UP; q += NT) {
+        p_sh[q] = 0.0f;
+        u_sh[q] = NEG;
+    }
+
+    // ---------------------------------------------------------------- constants, base 2
+    auto durv = [&](int k) -> float {
+        return (act && k <= K) ? fmaxf((float)((double)a.dur[(k - 1) * C + c] * LOG2E), NEG) : NEG;
+    };
+    float dreg[KP], dlin[KP];
+    float dmx = NEG;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        dreg[i] = durv(3 + j + i * G);
+        dmx = fmaxf(dmx, dreg[i]);
+    }
+    const float d0 = durv(1), d1 = durv(2);
+    dmx = group_reduce<G>(fmaxf(dmx, fmaxf(d0, d1)), OpMax());
+    const float dmax = dmx > NEG_HALF ? dmx : 0.0f;      // linear durations are 2^(dur - dmax)
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) dlin[i] = exp2_or_zero(dreg[i] - dmax);
+    const float D0 = exp2_or_zero(d0 - dmax), D1 = exp2_or_zero(d1 - dmax);
+
+    float treg[CPL], wreg[CPL], zero[CPL];
+    float tmx = NEG;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int cp = jt + i * GT;
+        float v = NEG;
+        if (act && cp < C) {
+            const float tv = dir == 0 ? a.trans[cp * C + c] : a.trans[c * C + cp];
+            v = fmaxf((float)((double)tv * LOG2E), NEG);
+        }
+        treg[i] = v;
+        zero[i] = 0.0f;
+        tmx = fmaxf(tmx, v);
+    }
+    tmx = group_reduce<GT>(tmx, OpMax());
+    const float tmax = tmx > NEG_HALF ? tmx : 0.0f;      // linear transitions: 2^(trans - tmax)
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) wreg[i] = exp2_or_zero(treg[i] - tmax);
+    __syncthreads();   // ring and messages cleared, SL visible
+
+    // bulk of position tq: linear sum (dlin weights) when in range, else exact log space
+    auto bulk = [&](int tq, float& qlin, float& qlog) {
+        qlin = 0.0f;
+        qlog = NEG;
+        if constexpr (KPL > 0) {
+            float v[KP];
+            bool ok = false;
+            if constexpr (LIN) {
+                ring_load<G, KPL, MIR>(Erow, tq, j, RS, v);
+                float sm = 0.0f;
+#pragma unroll
+                for (int i = 0; i < KPL; ++i) sm = fmaf(v[i], dlin[i], sm);
+                sm = group_reduce<G>(sm, OpSum());
+                ok = in_lin_range(sm) || !act;
+                qlin = sm;
+                qlog = fast_log2(sm) + dmax;
+            }
+            if (wave_any(!ok)) {
+                ring_load<G, KPL, MIR>(Rrow, tq, j, RS, v);
+                const float lg = group_lse<G, KPL>(v, dreg);
+                if (!ok) {
+                    qlog = lg;
+                    qlin = exp2_or_zero(lg - dmax);
+                }
+            }
+        }
+    };
+
+    // ---------------------------------------------------------------- state after trans(t0)
+    const size_t ckrow = ((size_t)dir * a.B + b) * a.nspans;
+    const size_t outrow = (size_t)b * (T + 1);
+    double* Xout = dir == 0 ? a.XF : a.XB;
+    double* Aout = dir == 0 ? a.AF : a.AB;
+    auto put_all = [&](int pos, float r) {   // every ring copy of one position
+        ring_put<MIR>(Rrow, pos, RS, r);
+        if constexpr (LIN) ring_put<MIR>(Erow, pos, RS, exp2_or_zero(r));
+    };
+    double Bc = 0.0, H = 0.0;
+    float Mref = 0.0f, Rn1, Rn2;
+    if (t0 == 0) {
+        if (writer) put_all(0, 0.0f);       // position 0: no transition into it
+        Rn1 = 0.0f;
+        Rn2 = NEG;
+    } else {
+        const size_t ck = ckrow + span;
+        if (act)
+            for (int q = j; q < K; q += G) put_all(t0 - q, a.ck_ring[(ck * K + q) * C + c]);
+        Bc = a.ck_base[ck * C + cc];
+        Mref = a.ck_mprev[ck * C + cc];
+        H = a.ck_href[ck];
+        Rn1 = a.ck_ring[(ck * K + 0) * C + cc];
+        Rn2 = K >= 2 ? a.ck_ring[(ck * K + 1) * C + cc] : NEG;
+    }
+    if (writer && a.write_xa)
+        Aout[(outrow + (dir == 0 ? t0 : L - t0)) * C + c] = (Bc + (double)Rn1) * LN2;
+    float En1 = exp2_or_zero(Rn1), En2 = exp2_or_zero(Rn2);
+
+    // ---------------------------------------------------------------- S staging
+    auto sidx = [&](int t, int q) -> size_t { return (size_t)(dir == 0 ? t : L - t) * C + q; };
+    auto spub = [&](double raw, int q) -> double {
+        return dir == 0 ? raw * LOG2E : (SL[q] - raw) * LOG2E;
+    };
+    // chunk n holds rows t = t0 + 1 + n*CH + r, r = 0..CH (the last row repeats the next
+    // chunk's first, so position t+1 is always at hand)
+    for (int q = tid; q < rowsN; q += NT) {
+        const int row = q / C, l = q - row * C;
+        const int t = t0 + 1 + row;
+        Sbuf[q] = (t <= t1) ? spub(Sb[sidx(t, l)], l) : 0.0;
+    }
+    double pf[PF];   // raw values of chunk n+1, fetched one chunk ahead
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        const int q = tid + i * NT;
+        pf[i] = 0.0;
+        if (q < rowsN) {
+            const int row = q / C, l = q - row * C;
+            const int t = t0 + 1 + CH + row;
+            if (t <= t1) pf[i] = Sb[sidx(t, l)];
+        }
+    }
+    __syncthreads();   // restored ring and chunk 0 visible
+    __builtin_amdgcn_s_waitcnt(0);   // nothing loaded before the loop is waited on inside it
+
+    // ---------------------------------------------------------------- message of t0+1
+    float Qla, Qga;           // bulk of the next message's position (linear, log2)
+    bulk(t0 + 1, Qla, Qga);
+    double BH = Bc - H;       // B_c - H
+    double Scur = Sbuf[cc];   // S(t0+1), base 2
+    float rps = 1.0f;         // 2^-e of the last normaliser step
+    auto publish = [&](int tn, double Sn, float z, float ql, float qg) {
+        // message of position tn from E(tn-1) = En1, E(tn-2) = En2 and bulk (ql, qg);
+        // z = 2^(S(tn) + B_c - H(tn-1) + dmax)
+        const float hn = (float)(Sn + BH);                  // S(tn) + B_c - H(tn)
+        const float sg = fmaf(En1, D0, fmaf(En2, D1, ql));
+        const bool ok = in_lin_range(sg) || !act;
+        float sigma = fast_log2(sg) + dmax;
+        float p = sg * z * rps;
+        if (wave_any(!ok)) {
+            const float e1 = Rn1 + d0, e2 = Rn2 + d1;
+            const float m3 = fmaxf(fmaxf(qg, e1), e2);
+            const float lg =
+                m3 + fast_log2(fast_exp2(qg - m3) + fast_exp2(e1 - m3) + fast_exp2(e2 - m3));
+            if (!ok) {
+                sigma = lg;
+                p = fast_exp2(hn + lg);
+            }
+        }
+        const int o = (tn & 1) * UP + c;
+        *(writer ? p_sh + o : dummy + tid) = p;
+        *(writer ? u_sh + o : dummy + tid) = hn + sigma;
+        if (a.write_xa && writer)
+            Xout[(outrow + (dir == 0 ? tn : L - tn)) * C + c] = (Sn + Bc + (double)sigma) * LN2;
+    };
+    publish(t0 + 1, Scur, fast_exp2((float)(Scur + BH) + dmax), Qla, Qga);
+    bulk(t0 + 2, Qla, Qga);
+    double lz = 0.0;
+    int next_ck = (a.mode == MODE_FULL && a.write_ckpt) ? a.delta : INT_MAX;
+    __syncthreads();
+
+    // ---------------------------------------------------------------- main loop
+    for (int tc = t0 + 1, nch = 0; tc <= t1; tc += CH, ++nch) {
+        const double* Srow = Sbuf + (nch & 1) * rowsN;
+        const int rows = min(CH, t1 - tc + 1);
+        for (int row = 0; row < rows; ++row) {
+            const int t = tc + row;
+            if (row == 0 && tc + CH <= t1) {
+                // publish chunk n+1 (its buffer was last read in chunk n-1), fetch n+2;
+                // this position's barrier makes it visible
+                double* dst = Sbuf + ((nch + 1) & 1) * rowsN;
+#pragma unroll
+                for (int i = 0; i < PF; ++i) {
+                    const int q = tid + i * NT;
+                    if (q < rowsN) dst[q] = spub(pf[i], q - (q / C) * C);
+                }
+#pragma unroll
+                for (int i = 0; i < PF; ++i) {
+                    const int q = tid + i * NT;
+                    if (q < rowsN) {
+                        const int rr = q / C, l = q - rr * C;
+                        const int tt = tc + 2 * CH + rr;
+                        pf[i] = (tt <= t1) ? Sb[sidx(tt, l)] : 0.0;
+                    }
+                }
+            }
+            // ---- rebase: move this label's values to a new base (every REBASE positions)
+            if ((t & (REBASE - 1)) == 0) {
+                const float ref = fmaxf(Mref, Rn1);
+                const float dl = ref > NEG_HALF ? ref : 0.0f;
+                const float sc = fast_exp2(-dl);
+                Bc += (double)dl;
+                BH += (double)dl;
+                Rn1 -= dl; Rn2 -= dl; Mref -= dl; Qga -= dl;
+                En1 *= sc; En2 *= sc; Qla *= sc;
+                if constexpr (KPL > 0) {
+                    // every slot of positions t-1 .. t-KPL*G (all later bulks and
+                    // checkpoints read inside it; the older ones are dead and distinct)
+                    float v[KP];
+                    ring_load<G, KPL, MIR>(Rrow, t + 2, j, RS, v);
+#pragma unroll
+                    for (int i = 0; i < KPL; ++i) v[i] -= dl;
+                    ring_store<G, KPL, MIR>(Rrow, t + 2, j, RS, v);
+                    if constexpr (LIN) {
+#pragma unroll
+                        for (int i = 0; i < KPL; ++i) v[i] = exp2_or_zero(v[i]);
+                        ring_store<G, KPL, MIR>(Erow, t + 2, j, RS, v);
+                    }
+                }
+            }
+            const double Snx = Srow[(row + 1) * C + cc];      // S(t+1)
+            const float h = (float)(Scur + BH);                 // S(t) + B_c - H(t)
+            const float f = fast_exp2(tmax - h);                // E(t) = s * f
+            const float z = fast_exp2((float)(Snx + BH) + dmax);
+
+            // ---- loads: bulk window of t+2 and the messages of t
+            float bv[KP];
+            if constexpr (KPL > 0) ring_load<G, KPL, MIR>(LIN ? Erow : Rrow, t + 2, j, RS, bv);
+            float pv[CPL];
+            {
+                const float* pr = p_sh + (t & 1) * UP;
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) pv[i] = pr[jt + i * GT];
+            }
+            // ---- [B] transition sums and [D] bulk sum, linear
+            float s = 0.0f, q = 0.0f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
+                s = fmaf(pv[i], wreg[i], s);
+                q += pv[i];
+            }
+            float bs = 0.0f;
+            if constexpr (LIN) {
+#pragma unroll
+                for (int i = 0; i < KPL; ++i) bs = fmaf(bv[i], dlin[i], bs);
+                bs = group_reduce<G>(bs, OpSum());
+            }
+            s = group_reduce<GT>(s, OpSum());
+            q = group_reduce<GT>(q, OpSum());
+            const bool okS = in_lin_range(s) || !act;
+            const bool okQ = in_lin_range(q);               // the same in every lane
+            const bool okD = KPL == 0 || !act || (LIN && in_lin_range(bs));
+            float Rnew = fast_log2(s) + tmax - h;
+            float Enew = s * f;
+            int e = __builtin_amdgcn_frexp_expf(q);          // q = m 2^e, m in [1/2, 1)
+            float Qlc = bs, Qgc = KPL == 0 ? NEG : fast_log2(bs) + dmax;
+            float lq = 0.0f;                                 // log2 q where it is needed
+            if (wave_any(!(okS && okQ))) {
+                // exact log-space transition step from the log-space messages
+                float uv[CPL];
+                const float* ur = u_sh + (t & 1) * UP;
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) uv[i] = ur[jt + i * GT];
+                const float ls = group_lse<GT, CPL>(uv, treg) - h;
+                const float lqq = group_lse<GT, CPL>(uv, zero);
+                if (!okS) {
+                    Rnew = ls;
+                    Enew = exp2_or_zero(ls);
+                }
+                if (!okQ) {
+                    lq = lqq;
+                    e = lqq > NEG_HALF ? (int)floorf(lqq) + 1 : 0;
+                }
+            }
+            if constexpr (KPL > 0) {
+                if (wave_any(!okD)) {
+                    // exact log-space bulk from the R ring
+                    ring_load<G, KPL, MIR>(Rrow, t + 2, j, RS, bv);
+                    const float lg = group_lse<G, KPL>(bv, dreg);
+                    if (!okD) {
+                        Qgc = lg;
+                        Qlc = exp2_or_zero(lg - dmax);
+                    }
+                }
+            }
+            if (t == L) lz = H + (double)(okQ ? fast_log2(q) : lq);   // log2 Z
+            rps = __builtin_amdgcn_ldexpf(1.0f, -e);
+            H += (double)e;
+            BH -= (double)e;
+            {
+                const int s0 = t & RMASK;
+                *(writer ? Rrow + s0 : dummy + tid) = Rnew;
+                if constexpr (MIR) *(writer ? Rrow + s0 + RS : dummy + tid) = Rnew;
+                if constexpr (LIN) {
+                    *(writer ? Erow + s0 : dummy + tid) = Enew;
+                    if constexpr (MIR) *(writer ? Erow + s0 + RS : dummy + tid) = Enew;
+                }
+            }
+            if (a.write_xa && writer && t < t1)
+                Aout[(outrow + (dir == 0 ? t : L - t)) * C + c] = (Bc + (double)Rnew) * LN2;
+            Rn2 = Rn1; En2 = En1;
+            Rn1 = Rnew; En1 = Enew;
+            if (Qgc > NEG_HALF) Mref = Qgc;
+            // ---- checkpoint: state right after the transition step of position t
+            if (t == next_ck) {
+                if (t < L) {
+                    const size_t ck = ckrow + t / a.delta;
+                    if (act)
+                        for (int qq = j; qq < K; qq += G)
+                            a.ck_ring[(ck * K + qq) * C + c] = Rrow[(t - qq) & RMASK];
+                    if (writer) {
+                        a.ck_base[ck * C + c] = Bc;
+                        a.ck_mprev[ck * C + c] = Mref;
+                    }
+                    if (tid == 0) a.ck_href[ck] = H;
+                }
+                next_ck += a.delta;
+            }
+            // ---- [C] message of t+1
+            if (t < t1) publish(t + 1, Snx, z, Qla, Qga);
+            Scur = Snx;
+            Qla = Qlc;
+            Qga = Qgc;
+            __syncthreads();
+        }
+    }
+
+    // ---------------------------------------------------------------- end of sequence
+    if (t1 == L && tid == 0) (dir == 0 ? a.logz : a.logz_b)[b] = bad ? nan_d() : lz * LN2;
+}
+
+// ------------------------------------------------------------------ launch
+template <int G, int KPL, int CPL, int GT, int NTMAX, int LAY>
+static hipError_t launch_lse_inst(const SweepArgs& a, dim3 grid, const SweepCfg& cfg,
+                                  hipStream_t stream) {
+    if (cfg.NT > NTMAX || cfg.lse.CH > lse_chunk_max(G)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_lse<G, KPL, CPL, GT, NTMAX, LAY>), grid, dim3(cfg.NT), cfg.lse.bytes,
+                       stream, a, cfg.RS, cfg.lse.P, cfg.lse.CH);
+    return hipGetLastError();
+}
+
+#define LSE_KPL_CASES(G, CPL, GT, NTMAX)                                                \
+    switch (cfg.KPL) {                                                                  \
+        case 0: return launch_lse_inst<G, 0, CPL, GT, NTMAX, LAY>(a, grid, cfg, stream);   \
+        case 1: return launch_lse_inst<G, 1, CPL, GT, NTMAX, LAY>(a, grid, cfg, stream);   \
+        case 2: return launch_lse_inst<G, 2, CPL, GT, NTMAX, LAY>(a, grid, cfg, stream);   \
+        case 3: return launch_lse_inst<G, 3, CPL, GT, NTMAX, LAY>(a, grid, cfg, stream);   \
+        case 4: return launch_lse_inst<G, 4, CPL, GT, NTMAX, LAY>(a, grid, cfg, stream);   \
+        case 5: return launch_lse_inst<G, 5, CPL, GT, NTMAX, LAY>(a, grid, cfg, stream);   \
+        case 6: return launch_lse_inst<G, 6, CPL, GT, NTMAX, LAY>(a, grid, cfg, stream);   \
+        case 7: return launch_lse_inst<G, 7, CPL, GT, NTMAX, LAY>(a, grid, cfg, stream);   \
+        case 8: return launch_lse_inst<G, 8, CPL, GT, NTMAX, LAY>(a, grid, cfg, stream);   \
+        case 10: return launch_lse_inst<G, 10, CPL, GT, NTMAX, LAY>(a, grid, cfg, stream); \
+        case 12: return launch_lse_inst<G, 12, CPL, GT, NTMAX, LAY>(a, grid, cfg, stream); \
+        case 16: return launch_lse_inst<G, 16, CPL, GT, NTMAX, LAY>(a, grid, cfg, stream); \
+        case 24: return launch_lse_inst<G, 24, CPL, GT, NTMAX, LAY>(a, grid, cfg, stream); \
+        case 32: return launch_lse_inst<G, 32, CPL, GT, NTMAX, LAY>(a, grid, cfg, stream); \
+        default: return hipErrorInvalidValue;                                           \
+    }
+
+// every kernel shape of one ring layout (one translation unit per layout)
+template <int LAY>
+hipError_t launch_lse_layout(const SweepCfg& cfg, const SweepArgs& a, int ndir,
+                             hipStream_t stream) {
+    dim3 grid = a.mode == MODE_FULL ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);
+    if (cfg.G == 64) { LSE_KPL_CASES(64, 1, 4, 256) }
+    if (cfg.G == 32) { LSE_KPL_CASES(32, 1, 8, 256) }
+    if (cfg.G == 16) { LSE_KPL_CASES(16, 1, 16, 256) }
+    if (cfg.G == 8 && cfg.CPL == 4) { LSE_KPL_CASES(8, 4, 8, 256) }
+    if (cfg.G == 8 && cfg.CPL == 8) { LSE_KPL_CASES(8, 8, 8, 512) }
+    if (cfg.G == 4) { LSE_KPL_CASES(4, 32, 4, 512) }
+    return hipErrorInvalidValue;
+}
+
+#undef LSE_KPL_CASES
+
+}  // namespace semicrf

@@ -1,0 +1,286 @@
+// Max-plus streaming sweep on gfx950 (Viterbi): the recurrence of the log-semiring sweep
+// with LSE replaced by max, plus backpointers.
+//
+// Method ("Streaming Structured Inference with Flash-SemiCRF", gist.science EN explainer,
+// "2. Methodology"; decoding is the (max, +) form of the same forward recursion).  In the
+// factored form
+//     abar[s, c]  = max_{c'} (V[s, c'] + trans[c', c])
+//     V[t, c]     = S[t, c] + max_k (abar[t-k, c] - S[t-k, c] + dur[k-1, c])
+// with abar[0, c] = 0.  The backpointer of (t, c) is the lowest k attaining the inner max
+// and, for the segment start s = t - k, the lowest c' attaining abar[s, c]; packed as
+// k | c' << 16 (c' stored at the start position s).
+//
+// Work layout as in the log-semiring sweep: one workgroup per sequence, lanes in groups
+// of G per label, the label's ring of A = abar - S (relative to a per-label fp64 base,
+// moved every REBASE positions) in LDS, one barrier per position.  Iteration t runs
+//   [B] transition step of position t-1: max over u(t-1)[c'] + T[c', c] (DPP) -> A[t-1, c]
+//   [C] V(t): three-term max of the k = 1, 2 terms and the bulk value of t -> u(t) to LDS
+//   [D] bulk value for position t+2: max over this label's ring (lane j owns k = 3+j+i*G)
+// fp32 arithmetic on values kept small (u = V - H with a common fp64 reference H).
+#pragma once
+
+#include "internal.h"
+#include "ring.h"
+
+namespace semicrf {
+
+namespace {
+
+__device__ __forceinline__ double nan_d() { return __longlong_as_double(0x7ff8000000000000LL); }
+
+// Bulk value of position tq (terms k >= 3): max over the group and the lowest k attaining it.
+template <int G, int KPL, bool MIR>
+__device__ __forceinline__ float bulk_max(const float* Rrow, int tq, int j, int RS,
+                                          const float* dreg, int* kbest) {
+    if constexpr (KPL == 0) {
+        *kbest = INT_MAX;
+        return NEG;
+    } else {
+        float v[KPL];
+        ring_load<G, KPL, MIR>(Rrow, tq, j, RS, v);
+        return group_argmax<G, KPL>(v, dreg, j, kbest);
+    }
+}
+
+}  // namespace
+
+// G: lanes per label; KPL: durations k >= 3 per lane (k = 3 + j + i*G, i < KPL, covering
+// k <= K + 1); CPL, GT: previous labels per lane and the lane count of the transition
+// reduction (GT * CPL >= C, GT <= G); NTMAX: largest workgroup routed here.
+// Grid: one workgroup per sequence.  Natural-log units (max-plus needs no base change).
+template <int G, int KPL, int CPL, int GT, int NTMAX, bool MIR>
+__global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int RS, const int P,
+                                                  const int CH) {
+    constexpr int PF = (MAXPLUS_CHUNK_MAX + G - 1) / G;   // prefetched doubles per lane (NT >= C*G)
+    constexpr int UP = GT * CPL;                   // padded u row (>= C)
+    extern __shared__ double lds[];
+    const int C = a.C, K = a.K, T = a.T;
+    const int tid = threadIdx.x, NT = blockDim.x;
+    const int c = tid / G;
+    const int j = tid - c * G;
+    const int jt = j & (GT - 1);             // every GT-subgroup repeats the transition step
+    const bool act = c < C;
+    const int cr = act ? c : C;              // inactive lanes use the spare LDS row C
+    const int cc = act ? c : 0;
+
+    const int b = blockIdx.x;
+    const int Lr = a.Leff[b];
+    const bool bad = Lr < 0;
+    const int L = bad ? -Lr : Lr;
+    const int RMASK = RS - 1;
+    const int chunkN = CH * C;
+
+    double* Sbuf = lds;                                  // [2][CH][C]
+    float* R = (float*)(Sbuf + 2 * chunkN);              // [C+1][P]
+    float* u_sh = R + (C + 1) * P;                       // [2][UP]
+    float* Rrow = R + cr * P;
+
+    const double* Sb = a.S + (size_t)b * (T + 1) * C;
+    for (int q = tid; q < (C + 1) * P; q += NT) R[q] = NEG;
+    for (int q = tid; q < 2 * UP; q += NT) u_sh[q] = NEG;
+
+    // durations (k >= 3 per lane; k = 1, 2 group-uniform) and transitions
+    auto durv = [&](int k) -> float {
+        return (act && k <= K) ? fmaxf(a.dur[(k - 1) * C + c], NEG) : NEG;
+    };
+    float dreg[KPL > 0 ? KPL : 1];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) dreg[i] = durv(3 + j + i * G);
+    const float d0 = durv(1), d1 = durv(2);
+    float treg[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int cp = jt + i * GT;
+        treg[i] = (act && cp < C) ? fmaxf(a.trans[cp * C + c], NEG) : NEG;
+    }
+    __syncthreads();   // ring and u cleared
+
+    auto put = [&](int pos, float r) { ring_put<MIR>(Rrow, pos, RS, r); };
+
+    double Bc = 0.0, H = 0.0;
+    float Mref = 0.0f, Rn1 = 0.0f, Rn2 = NEG;
+    if (act && j == 0) put(0, 0.0f);        // position 0: no transition into it
+    __syncthreads();
+
+    int kQa = 0, kQb = 0, kb_prev = 0;
+    float Qa = bulk_max<G, KPL, MIR>(Rrow, 1, j, RS, dreg, &kQa);
+    float Qb = bulk_max<G, KPL, MIR>(Rrow, 2, j, RS, dreg, &kQb);
+
+    // ---------------------------------------------------------------- S staging
+    for (int q = tid; q < chunkN; q += NT) {
+        const int t = 1 + q / C;
+        Sbuf[q] = (t <= L) ? Sb[(size_t)C + q] : 0.0;
+    }
+    // the chunk after: values in registers, published CH positions later
+    double pf[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        const int q = tid + i * NT;
+        pf[i] = 0.0;
+        if (q < chunkN && 1 + CH + q / C <= L) pf[i] = Sb[(size_t)(1 + CH) * C + q];
+    }
+    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);   // nothing loaded before the loop is waited on inside it
+
+    float h_prev = 0.0f;
+    const size_t outrow = (size_t)b * (T + 1);
+
+    // ---------------------------------------------------------------- main loop
+    for (int tc = 1, nch = 0; tc <= L; tc += CH, ++nch) {
+        const double* Srow = Sbuf + (nch & 1) * chunkN;
+        const int rows = min(CH, L - tc + 1);
+        for (int row = 0; row < rows; ++row) {
+            const int t = tc + row;
+            if (t > 1) {
+                // ---- [B] A(t-1) = max_{c'} (u(t-1)[c'] + T[c'][c]) - h(t-1); H(t)
+                const float* us = u_sh + ((t - 1) & 1) * UP;
+                float y[CPL], uv[CPL];
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) {
+                    uv[i] = us[jt + i * GT];
+                    y[i] = uv[i] + treg[i];
+                }
+                float mt = y[0], mu = uv[0];
+#pragma unroll
+                for (int i = 1; i < CPL; ++i) {
+                    mt = fmaxf(mt, y[i]);
+                    mu = fmaxf(mu, uv[i]);
+                }
+                mt = group_reduce<GT>(mt, OpMax());
+                mu = group_reduce<GT>(mu, OpMax());
+                int cb = INT_MAX;
+#pragma unroll
+                for (int i = CPL - 1; i >= 0; --i)
+                    if (y[i] == mt) cb = jt + i * GT;
+                const int cbest = group_min_int<GT>(cb);
+                const float Rnew = mt - h_prev;
+                H += (double)mu;
+                Rn2 = Rn1;
+                Rn1 = Rnew;
+                if (j == 0) {
+                    put(t - 1, Rnew);
+                    if (act) a.bp[(outrow + t - 1) * C + c] = (uint32_t)kb_prev | ((uint32_t)cbest << 16);
+                }
+            }
+
+            // ---- [C] V(t): k = 1, 2 from registers, k >= 3 from the bulk value
+            const float e1 = Rn1 + d0, e2 = Rn2 + d1;
+            const float sig = fmaxf(fmaxf(Qa, e1), e2);
+            kb_prev = (e1 == sig) ? 1 : (e2 == sig) ? 2 : kQa;
+            const double g = Srow[row * C + cc] + Bc;
+            const float h = (float)(g - H);
+            if (j == 0) u_sh[(t & 1) * UP + cr] = h + sig;
+            h_prev = h;
+
+            // ---- [D] rebase, then the bulk value for position t+2
+            if ((t & (REBASE - 1)) == 0) {
+                const float ref = fmaxf(Mref, Rn1);
+                const float dl = ref > NEG_HALF ? ref : 0.0f;
+                Bc += (double)dl;
+                Qb -= dl;
+                Rn1 -= dl;
+                Rn2 -= dl;
+                h_prev += dl;
+                if constexpr (KPL > 0) {
+                    // every slot of positions t-1 .. t-KPL*G (the live window and older,
+                    // dead, distinct slots): reads first, then writes
+                    float v[KPL];
+                    ring_load<G, KPL, MIR>(Rrow, t + 2, j, RS, v);
+#pragma unroll
+                    for (int i = 0; i < KPL; ++i) v[i] -= dl;
+                    ring_store<G, KPL, MIR>(Rrow, t + 2, j, RS, v);
+                }
+            }
+            int kQn = 0;
+            const float Qn = bulk_max<G, KPL, MIR>(Rrow, t + 2, j, RS, dreg, &kQn);
+            if (Qn > NEG_HALF) Mref = Qn;
+            Qa = Qb;
+            Qb = Qn;
+            kQa = kQb;
+            kQb = kQn;
+            __syncthreads();
+        }
+        // ---- S staging: publish the next chunk, fetch the one after
+        if (tc + CH <= L) {
+            double* dst = Sbuf + ((nch + 1) & 1) * chunkN;
+#pragma unroll
+            for (int i = 0; i < PF; ++i) {
+                const int q = tid + i * NT;
+                if (q < chunkN) dst[q] = pf[i];
+            }
+#pragma unroll
+            for (int i = 0; i < PF; ++i) {
+                const int q = tid + i * NT;
+                if (q < chunkN) {
+                    const int tt = tc + 2 * CH + q / C;
+                    pf[i] = (tt <= L) ? Sb[(size_t)(tc + 2 * CH) * C + q] : 0.0;
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---------------------------------------------------------------- end of sequence
+    const float* us = u_sh + (L & 1) * UP;
+    if (act && j == 0) a.bp[(outrow + L) * C + c] = (uint32_t)kb_prev;
+    if (c == 0) {
+        float mu = NEG;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) mu = fmaxf(mu, us[jt + i * GT]);
+        mu = group_reduce<GT>(mu, OpMax());
+        int cb = INT_MAX;
+#pragma unroll
+        for (int i = CPL - 1; i >= 0; --i)
+            if (us[jt + i * GT] == mu) cb = jt + i * GT;
+        cb = group_min_int<GT>(cb);
+        if (j == 0) {
+            a.vscore[b] = bad ? nan_d() : H + (double)mu;
+            a.vcstar[b] = cb;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ launch
+template <int G, int KPL, int CPL, int GT, int NTMAX, bool MIR>
+static hipError_t launch_maxplus_inst(const SweepArgs& a, const SweepCfg& cfg,
+                                      hipStream_t stream) {
+    if (cfg.NT > NTMAX || cfg.vit.CH > MAXPLUS_CHUNK_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_maxplus<G, KPL, CPL, GT, NTMAX, MIR>), dim3(a.B), dim3(cfg.NT),
+                       cfg.vit.bytes, stream, a, cfg.RS, cfg.vit.P, cfg.vit.CH);
+    return hipGetLastError();
+}
+
+#define MAXPLUS_KPL_CASES(G, CPL, GT, NTMAX)                                         \
+    switch (cfg.KPL) {                                                               \
+        case 0: return launch_maxplus_inst<G, 0, CPL, GT, NTMAX, MIR>(a, cfg, stream);   \
+        case 1: return launch_maxplus_inst<G, 1, CPL, GT, NTMAX, MIR>(a, cfg, stream);   \
+        case 2: return launch_maxplus_inst<G, 2, CPL, GT, NTMAX, MIR>(a, cfg, stream);   \
+        case 3: return launch_maxplus_inst<G, 3, CPL, GT, NTMAX, MIR>(a, cfg, stream);   \
+        case 4: return launch_maxplus_inst<G, 4, CPL, GT, NTMAX, MIR>(a, cfg, stream);   \
+        case 5: return launch_maxplus_inst<G, 5, CPL, GT, NTMAX, MIR>(a, cfg, stream);   \
+        case 6: return launch_maxplus_inst<G, 6, CPL, GT, NTMAX, MIR>(a, cfg, stream);   \
+        case 7: return launch_maxplus_inst<G, 7, CPL, GT, NTMAX, MIR>(a, cfg, stream);   \
+        case 8: return launch_maxplus_inst<G, 8, CPL, GT, NTMAX, MIR>(a, cfg, stream);   \
+        case 10: return launch_maxplus_inst<G, 10, CPL, GT, NTMAX, MIR>(a, cfg, stream); \
+        case 12: return launch_maxplus_inst<G, 12, CPL, GT, NTMAX, MIR>(a, cfg, stream); \
+        case 16: return launch_maxplus_inst<G, 16, CPL, GT, NTMAX, MIR>(a, cfg, stream); \
+        case 24: return launch_maxplus_inst<G, 24, CPL, GT, NTMAX, MIR>(a, cfg, stream); \
+        case 32: return launch_maxplus_inst<G, 32, CPL, GT, NTMAX, MIR>(a, cfg, stream); \
+        default: return hipErrorInvalidValue;                                        \
+    }
+
+// every kernel shape of one ring layout (one translation unit per layout)
+template <bool MIR>
+hipError_t launch_maxplus_layout(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream) {
+    if (cfg.G == 64) { MAXPLUS_KPL_CASES(64, 1, 4, 256) }
+    if (cfg.G == 32) { MAXPLUS_KPL_CASES(32, 1, 8, 256) }
+    if (cfg.G == 16) { MAXPLUS_KPL_CASES(16, 1, 16, 256) }
+    if (cfg.G == 8 && cfg.CPL == 4) { MAXPLUS_KPL_CASES(8, 4, 8, 256) }
+    if (cfg.G == 8 && cfg.CPL == 8) { MAXPLUS_KPL_CASES(8, 8, 8, 512) }
+    if (cfg.G == 4) { MAXPLUS_KPL_CASES(4, 32, 4, 512) }
+    return hipErrorInvalidValue;
+}
+
+#undef MAXPLUS_KPL_CASES
+
+}  // namespace semicrf

@@ -1,0 +1,11 @@
+// Max-plus (Viterbi) sweep kernels for one ring layout (plain); the kernel itself is in
+// sweep_maxplus_kernel.h.  One translation unit per layout keeps the builds parallel.
+#include "sweep_maxplus_kernel.h"
+
+namespace semicrf {
+
+hipError_t launch_maxplus_plain(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream) {
+    return launch_maxplus_layout<false>(cfg, a, stream);
+}
+
+}  // namespace semicrf
