@@ -21,7 +21,7 @@ struct Layout {
     size_t logz = 0, logzb = 0;
     size_t ckR = 0, ckB = 0, ckM = 0, ckH = 0, XF = 0, AF = 0, XB = 0, AB = 0;
     size_t Dn = 0, dnt = 0, dno = 0, mu = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0;
-    size_t bp = 0, vscore = 0, vcstar = 0, seg = 0;
+    size_t bp = 0, vscore = 0, vcstar = 0, btr = 0, bent = 0;
     size_t total = 0;
 };
 
@@ -101,7 +101,9 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         lo.bp = m.take(sizeof(uint32_t) * BT1C);
         lo.vscore = m.take(sizeof(double) * B);
         lo.vcstar = m.take(sizeof(int) * B);
-        lo.seg = m.take(sizeof(int32_t) * 2 * (size_t)B * T);
+        const size_t nch = (size_t)backtrace_chunks(T, C, K);
+        lo.btr = m.take(sizeof(int32_t) * B * nch * K * C);
+        lo.bent = m.take(sizeof(int32_t) * B * nch);
     } else {
         return false;
     }
@@ -320,7 +322,8 @@ static int run_viterbi(const float* em, const int32_t* lengths, const float* tra
     a.vcstar = at<int>(workspace, lo.vcstar);
     LAUNCH(launch_maxplus(cfg, a, stream));
     STAGE(2);
-    LAUNCH(launch_backtrace(a.bp, a.vscore, a.vcstar, a.Leff, B, T, C, at<int32_t>(workspace, lo.seg),
+    LAUNCH(launch_backtrace(a.bp, a.vscore, a.vcstar, a.Leff, B, T, C, K,
+                            at<int32_t>(workspace, lo.btr), at<int32_t>(workspace, lo.bent),
                             best_score, labels, seg_start, stream));
     STAGE(3);
     return SEMICRF_OK;

@@ -149,9 +149,13 @@ hipError_t launch_reduce_partials(const double* part_dur, const double* part_tra
 hipError_t launch_write_logz(const double* logz, int B, float* out, hipStream_t stream);
 
 // ------------------------------------------------------------------ Viterbi
+// chunk length and chunk count of the parallel backtrace
+int backtrace_chunk(int C, int K);
+int backtrace_chunks(int T, int C, int K);
+// tr: [B][nch][K*C] and ent: [B][nch] int32 scratch
 hipError_t launch_backtrace(const uint32_t* bp, const double* vscore, const int* vcstar,
-                            const int* Leff, int B, int T, int C, int32_t* seg_ws,
-                            float* best_score, int32_t* labels, uint8_t* seg_start,
-                            hipStream_t stream);
+                            const int* Leff, int B, int T, int C, int K, int32_t* tr,
+                            int32_t* ent, float* best_score, int32_t* labels,
+                            uint8_t* seg_start, hipStream_t stream);
 
 }  // namespace semicrf
