@@ -86,6 +86,18 @@ def test_workspace_bytes(native):
     assert ws(0, 1, 10, 2, 70000, 0) == 0              # K beyond 65535
 
 
+@pytest.mark.parametrize("C,kmax", [(1, 2049), (4, 2049), (5, 1025), (8, 1025), (9, 513), (16, 513),
+                                    (17, 257), (39, 257), (64, 257), (128, 97)])
+def test_supported_duration_range(native, C, kmax):
+    """The largest K each label count supports, as the header states it."""
+    lib = native.load()
+    ws = lib.semicrf_workspace_bytes
+    for op in range(3):
+        assert ws(op, 2, 1000, C, kmax, 0) > 0, (op, C, kmax)
+        assert ws(op, 2, 1000, C, kmax + 1, 0) == 0, (op, C, kmax + 1)
+    assert ws(0, 1, 10, 129, 1, 0) == 0
+
+
 def test_argument_validation_returns_before_any_launch(native):
     lib = native.load()
     p = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
