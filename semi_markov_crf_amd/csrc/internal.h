@@ -33,7 +33,10 @@ struct SweepLds {
 struct SweepCfg {
     int G, KPL, CPL, GT; // instantiated kernel shape (KPL: register capacity per lane)
     int kpl;             // durations k >= 3 per lane actually used
-    int NT;              // threads per workgroup (multiple of 64)
+    int KPLr;            // round kernel: durations k >= 2*ROUND per bulk lane (instance)
+    int NT;              // threads per workgroup of the log-semiring sweep (multiple of 64)
+    int NTv;             // threads per workgroup of the max-plus sweep
+    bool split;          // log-semiring sweep by role, ROUND positions per barrier (C <= 16)
     int RS;              // ring slots per copy (power of two)
     SweepLds lse;        // log-semiring sweep
     SweepLds vit;        // max-plus sweep
@@ -52,6 +55,16 @@ constexpr int MAXPLUS_CHUNK_MAX = 64;
 inline size_t lse_lds_bytes(int C, int NT, int UP, int P, int CH, bool lin) {
     return (size_t)(2 * (CH + 1) * C + C) * 8 +
            (size_t)((lin ? 2 : 1) * (C + 1) * P + 4 * UP + NT) * 4;
+}
+// The round kernel (C <= 16): ROUND positions per workgroup barrier; the chain wavefront
+// sums durations k = 1 .. DIRECT itself, the bulk wavefronts k >= DIRECT + 1 = 2*ROUND.
+constexpr int ROUND = 4;
+constexpr int DIRECT = 2 * ROUND - 1;
+// Dynamic LDS of the round kernel: S chunks and S(L) (fp64), the rings, bulk sums and
+// ring entries [2 rounds][ROUND][2][CP] each, rebase shifts and dmax [CP], a sink [NT].
+inline size_t lse_round_lds_bytes(int C, int NT, int CP, int P, int CH, bool lin) {
+    return (size_t)(2 * (CH + 1) * C + C) * 8 +
+           (size_t)((lin ? 2 : 1) * (C + 1) * P + (8 * ROUND + 2) * CP + NT) * 4;
 }
 // Dynamic LDS of the max-plus sweep: S chunks [2][CH][C] (fp64), R ring [C+1][P] and
 // u [2][UP] (fp32).

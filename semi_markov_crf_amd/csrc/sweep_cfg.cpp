@@ -39,9 +39,24 @@ SweepCfg choose_sweep(int C, int K) {
         if (v >= kpl) { kmax = v; break; }
     if (kmax < 0) return s;
     s.G = G; s.KPL = kmax; s.CPL = CPL; s.GT = GT; s.kpl = kpl;
-    s.NT = ((C * G + 63) / 64) * 64;
+    s.NTv = ((C * G + 63) / 64) * 64;
+    // C <= 16: a chain wavefront in front of the label groups (k_lse_split)
+    s.split = G >= 16;
+    s.NT = s.split ? 64 + s.NTv : s.NTv;
     // RS >= K + 2 live positions and >= the widest window a lane addresses (2 + KPL*G)
     s.RS = pow2_at_least(std::max(K + 2, 3 + kmax * G));
+    s.KPLr = 0;
+    if (G >= 16) {
+        // round kernel (C <= 16): bulk lanes take k >= 2*ROUND; the ring also keeps the
+        // entries of the rounds in flight
+        const int kplr = K >= 2 * ROUND ? (K - 2 * ROUND + 1 + G - 1) / G : 0;
+        int kr = -1;
+        for (int v : kInst)
+            if (v >= kplr) { kr = v; break; }
+        if (kr < 0) return s;
+        s.KPLr = kr;
+        s.RS = pow2_at_least(std::max({s.RS, K + 3 * ROUND + 2, 2 * ROUND + kr * G + 1}));
+    }
     const int pad = G < 32 ? G : 0;   // staggers the label rows over the LDS banks
     const int UP = GT * CPL;
     auto pitch = [&](int layout) { return ((layout & SWEEP_MIRRORED) ? 2 : 1) * s.RS + pad; };
@@ -50,7 +65,8 @@ SweepCfg choose_sweep(int C, int K) {
     for (int lay : {int(SWEEP_MIRRORED | SWEEP_LINEAR), int(SWEEP_LINEAR), 0}) {
         const int P = pitch(lay);
         for (int ch = lse_chunk_max(G); ch >= 8 && s.lse.bytes == 0; ch >>= 1) {
-            const size_t n = lse_lds_bytes(C, s.NT, UP, P, ch, lay & SWEEP_LINEAR);
+            const size_t n = s.split ? lse_round_lds_bytes(C, s.NT, 256 / G, P, ch, lay & SWEEP_LINEAR)
+                                     : lse_lds_bytes(C, s.NT, UP, P, ch, lay & SWEEP_LINEAR);
             if (n <= LDS_BUDGET) s.lse = SweepLds{lay, P, ch, n};
         }
         if (s.lse.bytes) break;
@@ -64,7 +80,7 @@ SweepCfg choose_sweep(int C, int K) {
         }
         if (s.vit.bytes) break;
     }
-    s.ok = s.NT <= 1024 && s.lse.bytes > 0 && s.vit.bytes > 0;
+    s.ok = s.NT <= 1024 && s.NTv <= 1024 && s.lse.bytes > 0 && s.vit.bytes > 0;
     return s;
 }
 

@@ -479,14 +479,12 @@ static hipError_t launch_lse_inst(const SweepArgs& a, dim3 grid, const SweepCfg&
         default: return hipErrorInvalidValue;                                           \
     }
 
-// every kernel shape of one ring layout (one translation unit per layout)
+// every kernel shape of one ring layout for C > 16 (one translation unit per layout)
 template <int LAY>
 hipError_t launch_lse_layout(const SweepCfg& cfg, const SweepArgs& a, int ndir,
                              hipStream_t stream) {
     dim3 grid = a.mode == MODE_FULL ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);
-    if (cfg.G == 64) { LSE_KPL_CASES(64, 1, 4, 256) }
-    if (cfg.G == 32) { LSE_KPL_CASES(32, 1, 8, 256) }
-    if (cfg.G == 16) { LSE_KPL_CASES(16, 1, 16, 256) }
+    // C <= 16 (G >= 16) runs the split-role kernel instead
     if (cfg.G == 8 && cfg.CPL == 4) { LSE_KPL_CASES(8, 4, 8, 256) }
     if (cfg.G == 8 && cfg.CPL == 8) { LSE_KPL_CASES(8, 8, 8, 512) }
     if (cfg.G == 4) { LSE_KPL_CASES(4, 32, 4, 512) }

@@ -244,8 +244,8 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
 template <int G, int KPL, int CPL, int GT, int NTMAX, bool MIR>
 static hipError_t launch_maxplus_inst(const SweepArgs& a, const SweepCfg& cfg,
                                       hipStream_t stream) {
-    if (cfg.NT > NTMAX || cfg.vit.CH > MAXPLUS_CHUNK_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_maxplus<G, KPL, CPL, GT, NTMAX, MIR>), dim3(a.B), dim3(cfg.NT),
+    if (cfg.NTv > NTMAX || cfg.vit.CH > MAXPLUS_CHUNK_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_maxplus<G, KPL, CPL, GT, NTMAX, MIR>), dim3(a.B), dim3(cfg.NTv),
                        cfg.vit.bytes, stream, a, cfg.RS, cfg.vit.P, cfg.vit.CH);
     return hipGetLastError();
 }
