@@ -66,6 +66,12 @@ inline size_t lse_round_lds_bytes(int C, int NT, int CP, int P, int CH, bool lin
     return (size_t)(2 * (CH + 1) * C + C) * 8 +
            (size_t)((lin ? 2 : 1) * (C + 1) * P + (8 * ROUND + 2) * CP + NT) * 4;
 }
+// Dynamic LDS of the max-plus round kernel (C <= 16): S chunks [2][CH+1][C] (fp64), the
+// ring, bulk maxima with their k and ring entries [2 rounds][ROUND][CP] each, rebase
+// shifts [CP], a sink [NT].
+inline size_t maxplus_round_lds_bytes(int C, int NT, int CP, int P, int CH) {
+    return (size_t)(2 * (CH + 1) * C) * 8 + (size_t)((C + 1) * P + (6 * ROUND + 1) * CP + NT) * 4;
+}
 // Dynamic LDS of the max-plus sweep: S chunks [2][CH][C] (fp64), R ring [C+1][P] and
 // u [2][UP] (fp32).
 inline size_t maxplus_lds_bytes(int C, int UP, int P, int CH) {

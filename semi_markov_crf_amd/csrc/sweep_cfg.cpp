@@ -40,7 +40,7 @@ SweepCfg choose_sweep(int C, int K) {
     if (kmax < 0) return s;
     s.G = G; s.KPL = kmax; s.CPL = CPL; s.GT = GT; s.kpl = kpl;
     s.NTv = ((C * G + 63) / 64) * 64;
-    // C <= 16: a chain wavefront in front of the label groups (k_lse_split)
+    // C <= 16: a chain wavefront in front of the label groups (round kernels)
     s.split = G >= 16;
     s.NT = s.split ? 64 + s.NTv : s.NTv;
     // RS >= K + 2 live positions and >= the widest window a lane addresses (2 + KPL*G)
@@ -75,7 +75,8 @@ SweepCfg choose_sweep(int C, int K) {
     for (int lay : {int(SWEEP_MIRRORED), 0}) {
         const int P = pitch(lay);
         for (int ch = MAXPLUS_CHUNK_MAX; ch >= 8 && s.vit.bytes == 0; ch >>= 1) {
-            const size_t n = maxplus_lds_bytes(C, UP, P, ch);
+            const size_t n = s.split ? maxplus_round_lds_bytes(C, s.NT, 256 / G, P, ch)
+                                     : maxplus_lds_bytes(C, UP, P, ch);
             if (n <= LDS_BUDGET) s.vit = SweepLds{lay, P, ch, n};
         }
         if (s.vit.bytes) break;

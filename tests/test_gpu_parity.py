@@ -82,10 +82,13 @@ SMALL = [
     (4, 2, 30, 1, 7, 1.0, True),        # C = 1
     (5, 5, 9, 6, 4, 1.0, True),         # many length-1..9 sequences
     (6, 2, 300, 6, 40, 3.0, True),      # several S chunks, rebases, ragged tail
-    (7, 2, 150, 39, 30, 1.0, True),     # speech-like label count (G=16 instance)
+    (7, 2, 150, 39, 30, 1.0, True),     # speech-like label count (8 lanes per label)
     (8, 2, 70, 64, 64, 1.0, False),     # large label set, NT = 1024
     (9, 1, 1, 3, 5, 1.0, False),        # L = T = 1
-    (10, 3, 129, 20, 70, 1.0, True),    # G=32 instance, K not a multiple of 32
+    (10, 3, 129, 20, 70, 1.0, True),    # 8 lanes per label, K not a multiple of 8
+    (11, 2, 220, 12, 50, 1.5, True),    # 9..16 labels: 16 bulk lanes per label
+    (12, 2, 160, 16, 9, 1.0, True),     # 16 labels, one bulk duration (k = 8, 9)
+    (13, 2, 400, 8, 150, 2.0, True),    # 32 bulk lanes per label, many ring rescales
 ]
 
 
