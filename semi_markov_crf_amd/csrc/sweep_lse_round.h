@@ -186,7 +186,7 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
                     qg[m] = fast_log2(ql[m]) + dmax_b;
-                    ok = ok && (in_lin_range(ql[m]) || !bact || p0 + m > t1);
+                    ok &= in_lin_range(ql[m]) | !bact | (p0 + m > t1);
                 }
             } else {
                 ok = false;
@@ -288,6 +288,7 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
     // bulk lanes at the start of round r (rs = its first position - 1): apply the chain's
     // rebase of round r-1 to the ring, insert the chain's entries of round r-1, copy the
     // rings of the checkpoints the chain took in round r-1
+    int next_ckb = ckpt ? a.delta : INT_MAX;   // next checkpoint whose ring is to copy
     auto ring_round = [&](int r, int rs) {
         // the chain rebased last round: move the entries it wrote before that.  Live
         // entries are positions rs-K-M+2 .. rs; lane j takes rs - j - i*G, reads first
@@ -299,12 +300,12 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
             for (int i = 0; i < KR; ++i) v[i] = Rrow[(rs - j - i * G) & RMASK];
 #pragma unroll
             for (int i = 0; i < KR; ++i) {
+                // slots outside the live window go to the spare row (read by idle lanes only)
                 const int q = j + i * G;
-                if (q < K + M && rs - q >= 0) {
-                    const float rv = v[i] - dl;
-                    ring_put<MIR>(Rrow, rs - q, RS, rv);
-                    if constexpr (LIN) ring_put<MIR>(Erow, rs - q, RS, exp2_or_zero(rv));
-                }
+                const bool live = (q < K + M) & (rs - q >= 0);
+                const float rv = v[i] - dl;
+                ring_put<MIR>(live ? Rrow : R + C * P, rs - q, RS, rv);
+                if constexpr (LIN) ring_put<MIR>(live ? Erow : E + C * P, rs - q, RS, exp2_or_zero(rv));
             }
         }
         // insert the chain's entries of round r-1 (positions rs-M+1 .. rs)
@@ -314,15 +315,12 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
             put_all(pos, ns[cb], ns[CP + cb]);
         }
         // checkpoint rings of the positions the chain checkpointed last round
-        if (ckpt && r >= 1 && bact) {
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const int pc = rs - M + 1 + m;
-                if (pc % a.delta == 0 && pc < L) {
-                    const size_t ck = ckrow + pc / a.delta;
-                    for (int qq = j; qq < K; qq += G)
-                        a.ck_ring[(ck * K + qq) * C + cb] = Rrow[(pc - qq) & RMASK];
-                }
+        for (; next_ckb <= rs; next_ckb += a.delta) {
+            const int pc = next_ckb;
+            if (bact && pc < L) {
+                const size_t ck = ckrow + pc / a.delta;
+                for (int qq = j; qq < K; qq += G)
+                    a.ck_ring[(ck * K + qq) * C + cb] = Rrow[(pc - qq) & RMASK];
             }
         }
     };
@@ -431,8 +429,7 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                     }
                 const float s = sv[0], q = qa[0];
                 // label lanes only: lanes outside row 0 broadcast their own (empty) row
-                ok = ok && (p > t1 || !cact ||
-                            (in_lin_range(sg) && in_lin_range(s) && in_lin_range(q)));
+                ok &= (p > t1) | !cact | (in_lin_range(sg) & in_lin_range(s) & in_lin_range(q));
                 const int e = __builtin_amdgcn_frexp_expf(q);          // q = m 2^e
                 Eh[DIRECT + m] = __builtin_amdgcn_ldexpf(s * fb[m], eacc);
                 Rh[DIRECT + m] = fast_log2(s) + (tmax - hb[m]) + (float)eacc;
@@ -500,7 +497,7 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                 BH = Bc - H;
             }
             // ---- publish the round: ring entries for the bulk lanes, outputs, checkpoints
-            double Hc = H0;
+            int ec = 0;                                    // steps taken so far this round
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const int p = rs + 1 + m;
@@ -516,7 +513,7 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                         Aout[(outrow + (dir == 0 ? p : L - p)) * C + cl] =
                             (Bc + (double)Rh[DIRECT + m]) * LN2;
                 }
-                Hc += (double)ev[m];                     // H after the transition step of p
+                ec += ev[m];                             // H after the transition step of p
                 if (QG[m] > NEG_HALF) Mref = QG[m];
                 if (p == next_ck) {
                     // chain half of the checkpoint after the transition step of p; the ring
@@ -527,7 +524,7 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                             a.ck_base[ck * C + cl] = Bc;
                             a.ck_mprev[ck * C + cl] = Mref;
                         }
-                        if (tid == 0) a.ck_href[ck] = Hc;
+                        if (tid == 0) a.ck_href[ck] = H0 + (double)ec;
                     }
                     next_ck += a.delta;
                 }

@@ -275,8 +275,10 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
                 for (int i = 0; i < KR; ++i) v[i] = Rrow[(rs - j - i * G) & RMASK];
 #pragma unroll
                 for (int i = 0; i < KR; ++i) {
+                    // slots outside the live window go to the spare row (read by idle lanes)
                     const int q = j + i * G;
-                    if (q < K + M && rs - q >= 0) ring_put<MIR>(Rrow, rs - q, RS, v[i] - dl);
+                    const bool live = (q < K + M) & (rs - q >= 0);
+                    ring_put<MIR>(live ? Rrow : R + C * P, rs - q, RS, v[i] - dl);
                 }
             }
             // insert the chain's entries of round r-1
