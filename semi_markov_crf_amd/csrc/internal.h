@@ -33,7 +33,9 @@ struct SweepLds {
 struct SweepCfg {
     int G, KPL, CPL, GT; // instantiated kernel shape (KPL: register capacity per lane)
     int kpl;             // durations k >= 3 per lane actually used
-    int KPLr;            // round kernel: durations k >= 2*ROUND per bulk lane (instance)
+    int KPLr;            // max-plus round kernel: durations k >= 2*ROUND per bulk lane
+    int BPL;             // log-semiring round kernel: ring blocks of ROUND positions per bulk lane
+    int CPr;             // round kernels: labels the chain wavefront broadcasts (>= C)
     int NT;              // threads per workgroup of the log-semiring sweep (multiple of 64)
     int NTv;             // threads per workgroup of the max-plus sweep
     bool split;          // log-semiring sweep by role, ROUND positions per barrier (C <= 16)
@@ -56,15 +58,19 @@ inline size_t lse_lds_bytes(int C, int NT, int UP, int P, int CH, bool lin) {
     return (size_t)(2 * (CH + 1) * C + C) * 8 +
            (size_t)((lin ? 2 : 1) * (C + 1) * P + 4 * UP + NT) * 4;
 }
-// The round kernel (C <= 16): ROUND positions per workgroup barrier; the chain wavefront
-// sums durations k = 1 .. DIRECT itself, the bulk wavefronts k >= DIRECT + 1 = 2*ROUND.
+// The round kernels (C <= 16): ROUND positions per workgroup barrier.  Max-plus: the
+// chain wavefront takes durations k = 1 .. DIRECT itself, the bulk wavefronts the rest.
 constexpr int ROUND = 4;
 constexpr int DIRECT = 2 * ROUND - 1;
-// Dynamic LDS of the round kernel: S chunks and S(L) (fp64), the rings, bulk sums and
-// ring entries [2 rounds][ROUND][2][CP] each, rebase shifts and dmax [CP], a sink [NT].
-inline size_t lse_round_lds_bytes(int C, int NT, int CP, int P, int CH, bool lin) {
-    return (size_t)(2 * (CH + 1) * C + C) * 8 +
-           (size_t)((lin ? 2 : 1) * (C + 1) * P + (8 * ROUND + 2) * CP + NT) * 4;
+// Dynamic LDS of the log-semiring round kernel: S chunks [2][C][CH] and S(L) (fp64), the
+// rings [C+1][P] (two when linear), bulk sums [2][CP][2][ROUND], staged ring entries
+// [2][CP+1][2][ROUND], rebase shifts and dmax [CP rounded to 4], a sink and two constant
+// blocks [16] (fp32).
+inline size_t lse_round_lds_bytes(int C, int CP, int P, int CH, bool lin) {
+    const int cp4 = (CP + 3) / 4 * 4;
+    return (size_t)(2 * CH * C + (C + 1) / 2 * 2) * 8 +
+           (size_t)((lin ? 2 : 1) * (C + 1) * P + 4 * CP * ROUND + 4 * (CP + 1) * ROUND +
+                    2 * cp4 + 16) * 4;
 }
 // Dynamic LDS of the max-plus round kernel (C <= 16): S chunks [2][CH+1][C] (fp64), the
 // ring, bulk maxima with their k and ring entries [2 rounds][ROUND][CP] each, rebase

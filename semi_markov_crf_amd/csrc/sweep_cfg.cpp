@@ -46,8 +46,10 @@ SweepCfg choose_sweep(int C, int K) {
     // RS >= K + 2 live positions and >= the widest window a lane addresses (2 + KPL*G)
     s.RS = pow2_at_least(std::max(K + 2, 3 + kmax * G));
     s.KPLr = 0;
+    s.BPL = 0;
+    s.CPr = 0;
     if (G >= 16) {
-        // round kernel (C <= 16): bulk lanes take k >= 2*ROUND; the ring also keeps the
+        // max-plus round kernel: bulk lanes take k >= 2*ROUND; the ring also keeps the
         // entries of the rounds in flight
         const int kplr = K >= 2 * ROUND ? (K - 2 * ROUND + 1 + G - 1) / G : 0;
         int kr = -1;
@@ -55,17 +57,26 @@ SweepCfg choose_sweep(int C, int K) {
             if (v >= kplr) { kr = v; break; }
         if (kr < 0) return s;
         s.KPLr = kr;
-        s.RS = pow2_at_least(std::max({s.RS, K + 3 * ROUND + 2, 2 * ROUND + kr * G + 1}));
+        // log-semiring round kernel: ring blocks of ROUND positions; a bulk sum reaches
+        // back bmax blocks, the ring holds those plus the rounds in flight
+        const int bmax = (K + ROUND - 1) / ROUND;
+        s.BPL = (std::max(bmax - 1, 0) + G - 1) / G;
+        if (s.BPL > 8) return s;
+        s.CPr = C <= 4 ? 4 : C <= 6 ? 6 : C <= 8 ? 8 : C <= 12 ? 12 : 16;
+        s.RS = pow2_at_least(std::max({s.RS, K + 3 * ROUND + 2, 2 * ROUND + kr * G + 1,
+                                       ROUND * (bmax + 5)}));
     }
     const int pad = G < 32 ? G : 0;   // staggers the label rows over the LDS banks
     const int UP = GT * CPL;
     auto pitch = [&](int layout) { return ((layout & SWEEP_MIRRORED) ? 2 : 1) * s.RS + pad; };
 
-    // log-semiring sweep: mirrored + linear, plain + linear, plain + log-space only
+    // log-semiring sweep: mirrored + linear, plain + linear, plain + log-space only; the
+    // round kernel keeps one copy of each ring (float4 blocks), rows 16 bytes apart in bank
     for (int lay : {int(SWEEP_MIRRORED | SWEEP_LINEAR), int(SWEEP_LINEAR), 0}) {
-        const int P = pitch(lay);
+        if (s.split && (lay & SWEEP_MIRRORED)) continue;
+        const int P = s.split ? s.RS + 4 : pitch(lay);
         for (int ch = lse_chunk_max(G); ch >= 8 && s.lse.bytes == 0; ch >>= 1) {
-            const size_t n = s.split ? lse_round_lds_bytes(C, s.NT, 256 / G, P, ch, lay & SWEEP_LINEAR)
+            const size_t n = s.split ? lse_round_lds_bytes(C, s.CPr, P, ch, lay & SWEEP_LINEAR)
                                      : lse_lds_bytes(C, s.NT, UP, P, ch, lay & SWEEP_LINEAR);
             if (n <= LDS_BUDGET) s.lse = SweepLds{lay, P, ch, n};
         }

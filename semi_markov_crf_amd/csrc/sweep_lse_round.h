@@ -1,22 +1,27 @@
-// Log-semiring streaming sweep for small label counts (C <= 16), ROUND positions per
+// Log-semiring streaming sweep for small label counts (C <= 16), ROUND = 4 positions per
 // workgroup barrier.
 //
 // Same recurrence, base-2 linear-space arithmetic and checkpoints as k_lse
-// (sweep_lse_kernel.h); the work is divided between wavefronts by role, and the chain of
-// positions runs ROUND steps between two workgroup barriers.
+// (sweep_lse_kernel.h); the work is divided between wavefronts by role.
 //
-//  * chain wavefront (threads 0..63): lane c holds label c.  Per position p it forms the
-//    message of p from its label's last DIRECT = 2*ROUND-1 ring entries (registers) and
-//    the bulk sum of the older ones, then the transition step of p: every lane reads the
-//    other labels' messages with v_readlane and sums them with FMA trees.  Messages never
-//    leave the wavefront.  The range checks of the linear sums of a round are combined;
-//    if any failed, the round is replayed exactly in log space (the replay rewrites
-//    everything the fast pass stored).
-//  * bulk wavefronts (threads 64..): lanes grouped G per label.  They own the label rings
-//    in LDS; in round r they apply the chain's rebase of round r-1 to the ring, insert
-//    the chain's ring entries of round r-1, copy checkpoint rings, and compute the bulk
-//    sums (durations k >= 2*ROUND) of the positions of round r+1 -- these only need
-//    entries up to the end of round r-1.  They also stage S.
+// Ring layout: the positions of round rho (rounds counted from the sweep start t0; round
+// -1 ends at t0) fill one 16-byte block of a label's ring row, so every ring access of
+// the hot loop is a float4.
+//
+//  * chain wavefront (threads 0..63): lane c holds label c.  The message of position
+//    p = (round start) + 1 + m takes durations k = 1 .. m + 4 from registers (the
+//    previous round's block and this round's entries) and the older ones from the bulk
+//    sum; then the transition step of p: DPP row broadcasts of every label's message and
+//    FMA trees.  The normaliser moves once per round.  Range checks of the linear sums
+//    are combined; if any failed, the round is replayed exactly in log space.  At the end
+//    of a round the chain writes its block of linear ring entries and, for the log ring,
+//    each entry as a (linear value, log2 offset) pair to a staging area.
+//  * bulk wavefronts (threads 64..): lanes grouped G per label.  In round r they turn the
+//    staged entries of round r-1 into the log ring, apply the chain's rebase of round r-1
+//    to the rings, copy checkpoint rings, and compute the bulk sums of round r+1
+//    (durations k >= m + 5, i.e. ring blocks of rounds <= r-1): lane j takes blocks
+//    b = 2 + j + i*G rounds back, 16 FMAs per block with per-lane coefficients.  They
+//    also stage S, label-major.
 // Per-label bases move at the start of every second round; the chain corrects the bulk
 // sums that the bulk wavefronts formed from the ring before they rescaled it.
 #pragma once
@@ -35,19 +40,28 @@ __device__ __forceinline__ void row_bcast_all(float v, float* out) {
     }
 }
 
-// G: bulk lanes per label (C <= 256/G); KPL: durations per bulk lane
-// (k = 2*ROUND + j + i*G); LAY: ring layout bits.  Block: 64 + ceil(C*G/64)*64 threads.
-template <int G, int KPL, int LAY>
+// first ring slot of round rho's block
+__device__ __forceinline__ int round_slot(int rho, int RMASK) { return (rho * ROUND) & RMASK; }
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ float at4(const float4& v, int d) {
+    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+}
+
+// G: bulk lanes per label (C <= 256/G); BPL: ring blocks per bulk lane; CP: labels the
+// chain broadcasts (>= C); LIN: linear ring and sums (else log-space bulk sums only).
+// Block: 64 + ceil(C*G/64)*64 threads.
+template <int G, int BPL, int CP, bool LIN>
 __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int RS, const int P,
                                                   const int CH) {
     constexpr int M = ROUND;
-    constexpr int CP = 256 / G;                                // chain lanes in use (>= C)
-    static_assert(CP <= 16, "the labels of the chain wavefront share one DPP row");
-    constexpr int PF = (lse_chunk_max(G) + 1 + G - 1) / G;     // prefetched doubles per bulk lane
-    constexpr int KP = KPL > 0 ? KPL : 1;
-    constexpr int HN = DIRECT + M;                             // history + this round
-    constexpr bool MIR = LAY & SWEEP_MIRRORED;
-    constexpr bool LIN = LAY & SWEEP_LINEAR;
+    static_assert(M == 4, "ring blocks are float4");
+    static_assert(CP <= 16 && CP * G <= 256, "the labels of the chain wavefront share one DPP row");
+    constexpr int PF = (lse_chunk_max(G) + G - 1) / G;        // prefetched doubles per bulk lane
+    constexpr int BP = BPL > 0 ? BPL : 1;
+    constexpr int KD = 2 * M - 1;                              // chain durations, last step
+    constexpr int CP4 = (CP + 3) / 4 * 4;
     extern __shared__ double lds[];
     const int C = a.C, K = a.K, T = a.T;
     const int tid = threadIdx.x, NT = blockDim.x, NB = NT - 64;
@@ -77,18 +91,21 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
         t1 = min(L, t0 + a.delta);
     }
     const int RMASK = RS - 1;
-    const int rowsN = (CH + 1) * C;
     const bool ckpt = a.mode == MODE_FULL && a.write_ckpt;
+    const int bmax = (K + M - 1) / M;             // oldest block a bulk sum reaches
+    const int NR = bmax + 3;                      // live blocks behind a round (rescale)
 
-    double* Sbuf = lds;                                    // [2][CH+1][C]
-    double* SL = Sbuf + 2 * rowsN;                         // [C]
-    float* R = (float*)(SL + C);                           // [C+1][P]
-    float* E = R + (C + 1) * P;                            // [C+1][P] (linear bulk only)
-    float* qsh = E + (LIN ? (C + 1) * P : 0);              // [2 rounds][M][lin, log][CP]
-    float* nsh = qsh + 2 * M * 2 * CP;                     // [2 rounds][M][R, E][CP]
-    float* dlsh = nsh + 2 * M * 2 * CP;                    // [CP] rebase shift per label
-    float* dmsh = dlsh + CP;                               // [CP] dmax per label
-    float* dummy = dmsh + CP;                              // [NT] sink for non-writing lanes
+    double* Sbuf = lds;                                    // [2][C][CH] label-major
+    double* SL = Sbuf + 2 * C * CH;                        // [C] (padded to 16 bytes)
+    float* R = (float*)(SL + (C + 1) / 2 * 2);             // [C+1][P] log ring
+    float* E = R + (C + 1) * P;                            // [C+1][P] linear ring
+    float* qsh = E + (LIN ? (C + 1) * P : 0);              // [2 rounds][CP][lin, log][M]
+    float* nsh = qsh + 2 * CP * 2 * M;                     // [2 rounds][CP+1][s, offset][M]
+    float* dlsh = nsh + 2 * (CP + 1) * 2 * M;              // [CP4] rebase shift per label
+    float* dmsh = dlsh + CP4;                              // [CP4] dmax per label
+    float* sink = dmsh + CP4;                              // [8] for non-writing lanes
+    float* zblk = sink + 8;                                // [4] zeros: linear blocks past K
+    float* nblk = zblk + 4;                                // [4] NEG: log blocks past K
     float* Rrow = R + cr * P;
     float* Erow = E + cr * P;
 
@@ -98,34 +115,39 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
         R[q] = NEG;
         if constexpr (LIN) E[q] = 0.0f;
     }
-    for (int q = tid; q < 2 * M * CP; q += NT) {
-        qsh[(q / CP) * 2 * CP + q % CP] = 0.0f;
-        qsh[(q / CP) * 2 * CP + CP + q % CP] = NEG;
+    for (int q = tid; q < 2 * CP * 2 * M; q += NT) qsh[q] = ((q / M) & 1) ? NEG : 0.0f;
+    if (tid < M) {
+        zblk[tid] = 0.0f;
+        nblk[tid] = NEG;
     }
 
     // ---------------------------------------------------------------- constants, base 2
     auto durv = [&](int c, int k) -> float {
-        return k <= K ? fmaxf((float)((double)a.dur[(k - 1) * C + c] * LOG2E), NEG) : NEG;
+        return (k >= 1 && k <= K) ? fmaxf((float)((double)a.dur[(k - 1) * C + c] * LOG2E), NEG) : NEG;
     };
-    // bulk lanes: durations k = 2M + j + i*G of label cb, scaled by the label's largest
-    float dreg[KP], dlin[KP];
+    // bulk lanes: block i of lane j lies bb = 2 + j + i*G rounds back; its entry d enters
+    // the sum of step m with duration k = 4*bb + m - d = 4*bb + t - 3, t = m - d + 3
     float dmx = NEG;
+    if (bact) {
+        for (int k = 1; k <= KD; ++k) dmx = fmaxf(dmx, durv(cb, k));
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        dreg[i] = bact ? durv(cb, 2 * M + j + i * G) : NEG;
-        dmx = fmaxf(dmx, dreg[i]);
+        for (int i = 0; i < BPL; ++i)
+#pragma unroll
+            for (int t = 0; t < 2 * M - 1; ++t) dmx = fmaxf(dmx, durv(cb, M * (2 + j + i * G) + t - 3));
     }
-    if (bact)
-        for (int k = 1; k < 2 * M; ++k) dmx = fmaxf(dmx, durv(cb, k));
     if (!chain) dmx = group_reduce<G>(dmx, OpMax());
     const float dmax_b = dmx > NEG_HALF ? dmx : 0.0f;
+    float Dc[BP][2 * M - 1];                               // 2^(dur - dmax), 0 beyond K
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) dlin[i] = exp2_or_zero(dreg[i] - dmax_b);
+    for (int i = 0; i < BPL; ++i)
+#pragma unroll
+        for (int t = 0; t < 2 * M - 1; ++t)
+            Dc[i][t] = bact ? exp2_or_zero(durv(cb, M * (2 + j + i * G) + t - 3) - dmax_b) : 0.0f;
     if (bact && j == 0) dmsh[cb] = dmax_b;
-    // chain lanes: durations k = 1 .. DIRECT and the transitions into label cl
-    float dlog[DIRECT];
+    // chain lanes: durations k = 1 .. KD and the transitions into label cl
+    float dlog[KD];
 #pragma unroll
-    for (int k = 0; k < DIRECT; ++k) dlog[k] = cact ? durv(cl, k + 1) : NEG;
+    for (int k = 0; k < KD; ++k) dlog[k] = cact ? durv(cl, k + 1) : NEG;
     float treg[CP], wreg[CP], zero[CP];
     float tmx = NEG;
 #pragma unroll
@@ -145,67 +167,74 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
     __syncthreads();   // ring cleared, SL and dmax visible
 
     const float dmax = chain ? dmsh[cl] : dmax_b;
-    float Dl[DIRECT];                                      // 2^(dur - dmax), k = 1 .. DIRECT
+    float Dl[KD];                                          // 2^(dur - dmax), k = 1 .. KD
 #pragma unroll
-    for (int k = 0; k < DIRECT; ++k) Dl[k] = exp2_or_zero(dlog[k] - dmax);
+    for (int k = 0; k < KD; ++k) Dl[k] = exp2_or_zero(dlog[k] - dmax);
 
-    auto publish_q = [&](int r, int m, float ql, float qg) {   // bulk sum, round r, step m
-        float* slot = qsh + ((r & 1) * M + m) * 2 * CP;
-        *(bact && j == 0 ? slot + cb : dummy + tid) = ql;
-        *(bact && j == 0 ? slot + CP + cb : dummy + tid) = qg;
-    };
-    // the M bulk sums of round r (positions p0 .. p0+M-1) at once: loads, products, trees
-    // and DPP reductions of the M sums interleave; one wavefront-uniform fallback
-    auto bulk_round = [&](int r, int p0) {
+    // bulk sums of round rr (positions p0 .. p0+M-1): ring blocks of rounds <= rr-2
+    auto bulk_round = [&](int rr, int p0) {
         float ql[M], qg[M];
-        if constexpr (KPL == 0) {
 #pragma unroll
-            for (int m = 0; m < M; ++m) publish_q(r, m, 0.0f, NEG);
-        } else {
-            bool ok = true;
-            float v[M][KP];
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                ql[m] = 0.0f;
-                qg[m] = NEG;
-            }
+        for (int m = 0; m < M; ++m) {
+            ql[m] = 0.0f;
+            qg[m] = NEG;
+        }
+        if constexpr (BPL > 0) {
+            bool ok = LIN;
             if constexpr (LIN) {
+                float4 v[BP];
 #pragma unroll
-                for (int m = 0; m < M; ++m) ring_load<G, KPL, MIR>(Erow, p0 + m - 2 * M + 3, j, RS, v[m]);
+                for (int i = 0; i < BPL; ++i) {
+                    const int bb = 2 + j + i * G;
+                    v[i] = ld4(bb <= bmax ? Erow + round_slot(rr - bb, RMASK) : zblk);
+                }
+                float acc[M];
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
+                    acc[m] = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < KPL; ++i) v[m][i] *= dlin[i];
+                    for (int i = 0; i < BPL; ++i)
 #pragma unroll
-                    for (int w = 1; w < KPL; w *= 2)
-#pragma unroll
-                        for (int i = 0; i + w < KPL; i += 2 * w) v[m][i] += v[m][i + w];
+                        for (int d = 0; d < M; ++d) acc[m] = fmaf(at4(v[i], d), Dc[i][m - d + 3], acc[m]);
                 }
 #pragma unroll
-                for (int m = 0; m < M; ++m) ql[m] = group_reduce<G>(v[m][0], OpSum());
+                for (int m = 0; m < M; ++m) ql[m] = group_reduce<G>(acc[m], OpSum());
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
                     qg[m] = fast_log2(ql[m]) + dmax_b;
                     ok &= in_lin_range(ql[m]) | !bact | (p0 + m > t1);
                 }
-            } else {
-                ok = false;
             }
             if (wave_any(!ok)) {
+                // exact log-space sums (durations from global memory: a rare path)
+                float4 w[BP];
+#pragma unroll
+                for (int i = 0; i < BPL; ++i) {
+                    const int bb = 2 + j + i * G;
+                    w[i] = ld4(bb <= bmax ? Rrow + round_slot(rr - bb, RMASK) : nblk);
+                }
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
-                    float w[KP];
-                    ring_load<G, KPL, MIR>(Rrow, p0 + m - 2 * M + 3, j, RS, w);
-                    const float lg = group_lse<G, KPL>(w, dreg);
+                    float x[BP * M], dd[BP * M];
+#pragma unroll
+                    for (int i = 0; i < BPL; ++i)
+#pragma unroll
+                        for (int d = 0; d < M; ++d) {
+                            x[i * M + d] = at4(w[i], d);
+                            dd[i * M + d] = bact ? durv(cb, M * (2 + j + i * G) + m - d) : NEG;
+                        }
+                    const float lg = group_lse<G, BPL * M>(x, dd);
                     if (!LIN || !(in_lin_range(ql[m]) || !bact)) {
                         qg[m] = lg;
                         ql[m] = exp2_or_zero(lg - dmax_b);
                     }
                 }
             }
-#pragma unroll
-            for (int m = 0; m < M; ++m) publish_q(r, m, ql[m], qg[m]);
         }
+        const bool wr = bact && j == 0;
+        float* slot = qsh + ((rr & 1) * CP + cb) * 2 * M;
+        st4(wr ? slot : sink, make_float4(ql[0], ql[1], ql[2], ql[3]));
+        st4(wr ? slot + M : sink, make_float4(qg[0], qg[1], qg[2], qg[3]));
     };
 
     // ---------------------------------------------------------------- state after trans(t0)
@@ -213,48 +242,51 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
     const size_t outrow = (size_t)b * (T + 1);
     double* Xout = dir == 0 ? a.XF : a.XB;
     double* Aout = dir == 0 ? a.AF : a.AB;
-    auto put_all = [&](int pos, float rv, float ev) {
-        ring_put<MIR>(Rrow, pos, RS, rv);
-        if constexpr (LIN) ring_put<MIR>(Erow, pos, RS, ev);
-    };
+    auto slot_of = [&](int pos) { return (pos - t0 - 1) & RMASK; };
     double Bc = 0.0, H = 0.0;
     float Mref = 0.0f;
-    // chain history: Rh[i], Eh[i] = ring entry of position (round start) - (DIRECT-1) + i
-    // for i < DIRECT; entries DIRECT .. DIRECT+M-1 are the positions of the round
-    float Rh[HN], Eh[HN];
+    // chain history, i < M: the previous round's positions (round start) - 3 + i; i >= M:
+    // this round's.  Eh: linear ring entry; its log2 is log2(sH) + fH.
+    float Eh[2 * M], sH[2 * M], fH[2 * M];
 #pragma unroll
-    for (int i = 0; i < HN; ++i) {
-        Rh[i] = NEG;
+    for (int i = 0; i < 2 * M; ++i) {
         Eh[i] = 0.0f;
+        sH[i] = 1.0f;
+        fH[i] = NEG;
     }
     if (t0 == 0) {
-        if (bact && j == 0) put_all(0, 0.0f, 1.0f);   // position 0: no transition into it
-        Rh[DIRECT - 1] = 0.0f;
-        Eh[DIRECT - 1] = 1.0f;
+        if (bact && j == 0) {                              // position 0: no transition into it
+            Rrow[slot_of(0)] = 0.0f;
+            if constexpr (LIN) Erow[slot_of(0)] = 1.0f;
+        }
+        Eh[M - 1] = 1.0f;
+        fH[M - 1] = 0.0f;
     } else {
         const size_t ck = ckrow + span;
         if (bact)
             for (int q = j; q < K; q += G) {
                 const float rv = a.ck_ring[(ck * K + q) * C + cb];
-                put_all(t0 - q, rv, exp2_or_zero(rv));
+                Rrow[slot_of(t0 - q)] = rv;
+                if constexpr (LIN) Erow[slot_of(t0 - q)] = exp2_or_zero(rv);
             }
         if (chain) {
             Bc = a.ck_base[ck * C + cl];
             Mref = a.ck_mprev[ck * C + cl];
             H = a.ck_href[ck];
 #pragma unroll
-            for (int i = 0; i < DIRECT; ++i) {
-                const int q = DIRECT - 1 - i;           // position t0 - q
+            for (int i = 0; i < M; ++i) {
+                const int q = M - 1 - i;                   // position t0 - q
                 const float rv = (q < K && t0 - q >= 0) ? a.ck_ring[(ck * K + q) * C + cl] : NEG;
-                Rh[i] = rv;
+                fH[i] = rv;
                 Eh[i] = exp2_or_zero(rv);
             }
         }
     }
     if (cact && a.write_xa)
-        Aout[(outrow + (dir == 0 ? t0 : L - t0)) * C + cl] = (Bc + (double)Rh[DIRECT - 1]) * LN2;
+        Aout[(outrow + (dir == 0 ? t0 : L - t0)) * C + cl] = (Bc + (double)fH[M - 1]) * LN2;
 
     // ---------------------------------------------------------------- S staging (bulk lanes)
+    const int chunkN = CH * C;
     auto sidx = [&](int t, int q) -> size_t { return (size_t)(dir == 0 ? t : L - t) * C + q; };
     auto spub = [&](double raw, int q) -> double {
         return dir == 0 ? raw * LOG2E : (SL[q] - raw) * LOG2E;
@@ -263,15 +295,15 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
 #pragma unroll
     for (int i = 0; i < PF; ++i) pf[i] = 0.0;
     if (!chain) {
-        for (int q = bt; q < rowsN; q += NB) {
+        for (int q = bt; q < chunkN; q += NB) {
             const int row = q / C, l = q - row * C;
             const int t = t0 + 1 + row;
-            Sbuf[q] = (t <= t1) ? spub(Sb[sidx(t, l)], l) : 0.0;
+            Sbuf[l * CH + row] = (t <= t1) ? spub(Sb[sidx(t, l)], l) : 0.0;
         }
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
             const int q = bt + i * NB;
-            if (q < rowsN) {
+            if (q < chunkN) {
                 const int row = q / C, l = q - row * C;
                 const int t = t0 + 1 + CH + row;
                 if (t <= t1) pf[i] = Sb[sidx(t, l)];
@@ -281,38 +313,47 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
     __syncthreads();   // restored ring and chunk 0 visible
     __builtin_amdgcn_s_waitcnt(0);
 
-    // bulk sums of round 0 (positions t0+1 .. t0+M need entries <= t0)
+    // bulk sums of round 0 (ring blocks of rounds <= -2)
     if (!chain) bulk_round(0, t0 + 1);
     __syncthreads();
 
-    // bulk lanes at the start of round r (rs = its first position - 1): apply the chain's
-    // rebase of round r-1 to the ring, insert the chain's entries of round r-1, copy the
-    // rings of the checkpoints the chain took in round r-1
+    // bulk lanes at the start of round r (rs = its first position - 1): the log ring block
+    // of round r-1 from the chain's staging, the chain's rebase of round r-1 applied to the
+    // rings, the rings of the checkpoints the chain took in round r-1
     int next_ckb = ckpt ? a.delta : INT_MAX;   // next checkpoint whose ring is to copy
     auto ring_round = [&](int r, int rs) {
-        // the chain rebased last round: move the entries it wrote before that.  Live
-        // entries are positions rs-K-M+2 .. rs; lane j takes rs - j - i*G, reads first
-        if (r >= 3 && (r & 1) == 1) {
-            const float dl = bact ? dlsh[cb] : 0.0f;
-            constexpr int KR = KPL + 1;
-            float v[KR];
-#pragma unroll
-            for (int i = 0; i < KR; ++i) v[i] = Rrow[(rs - j - i * G) & RMASK];
-#pragma unroll
-            for (int i = 0; i < KR; ++i) {
-                // slots outside the live window go to the spare row (read by idle lanes only)
-                const int q = j + i * G;
-                const bool live = (q < K + M) & (rs - q >= 0);
-                const float rv = v[i] - dl;
-                ring_put<MIR>(live ? Rrow : R + C * P, rs - q, RS, rv);
-                if constexpr (LIN) ring_put<MIR>(live ? Erow : E + C * P, rs - q, RS, exp2_or_zero(rv));
-            }
+        if (r >= 1 && bact && j == 0) {
+            const float* ns = nsh + (((r - 1) & 1) * (CP + 1) + cb) * 2 * M;
+            const float4 s4 = ld4(ns), f4 = ld4(ns + M);
+            st4(Rrow + round_slot(r - 1, RMASK),
+                make_float4(fmaxf(fast_log2(s4.x) + f4.x, NEG), fmaxf(fast_log2(s4.y) + f4.y, NEG),
+                            fmaxf(fast_log2(s4.z) + f4.z, NEG), fmaxf(fast_log2(s4.w) + f4.w, NEG)));
         }
-        // insert the chain's entries of round r-1 (positions rs-M+1 .. rs)
-        if (r >= 1 && bact && j < M && rs - M + 1 + j <= t1) {
-            const int pos = rs - M + 1 + j;
-            const float* ns = nsh + (((r - 1) & 1) * M + j) * 2 * CP;
-            put_all(pos, ns[cb], ns[CP + cb]);
+        // the chain rebased last round: move the blocks of rounds <= r-2 (reads first)
+        if (r >= 3 && (r & 1) == 1) {
+            constexpr int BR = BPL + 1;               // covers NR = bmax + 3 <= BPL*G + G blocks
+            const float dl = bact ? dlsh[cb] : 0.0f;
+            float4 v[BR];
+#pragma unroll
+            for (int i = 0; i < BR; ++i) v[i] = ld4(Rrow + round_slot(r - 2 - j - i * G, RMASK));
+#pragma unroll
+            for (int i = 0; i < BR; ++i) {
+                const int q = j + i * G;
+                const int rho = r - 2 - q;
+                // blocks outside the live window go to the spare row (read by idle lanes)
+                const bool live = (q < NR) & (t0 + M * rho + M >= 0);
+                const int sl = round_slot(rho, RMASK);
+                float4 rv = v[i];
+                rv.x -= dl;
+                rv.y -= dl;
+                rv.z -= dl;
+                rv.w -= dl;
+                st4((live ? Rrow : R + C * P) + sl, rv);
+                if constexpr (LIN)
+                    st4((live ? Erow : E + C * P) + sl,
+                        make_float4(exp2_or_zero(rv.x), exp2_or_zero(rv.y), exp2_or_zero(rv.z),
+                                    exp2_or_zero(rv.w)));
+            }
         }
         // checkpoint rings of the positions the chain checkpointed last round
         for (; next_ckb <= rs; next_ckb += a.delta) {
@@ -320,7 +361,7 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
             if (bact && pc < L) {
                 const size_t ck = ckrow + pc / a.delta;
                 for (int qq = j; qq < K; qq += G)
-                    a.ck_ring[(ck * K + qq) * C + cb] = Rrow[(pc - qq) & RMASK];
+                    a.ck_ring[(ck * K + qq) * C + cb] = Rrow[slot_of(pc - qq)];
             }
         }
     };
@@ -339,16 +380,13 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
             tc += CH;
             ++nch;
         }
-        const double* Srow = Sbuf + (nch & 1) * rowsN;
+        const double* Sch = Sbuf + (nch & 1) * chunkN;
         const int row0 = rs + 1 - tc;                  // chunk row of position rs+1
         if (chain) {
-            float QL[M], QG[M];
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const float* slot = qsh + ((r & 1) * M + m) * 2 * CP;
-                QL[m] = slot[cl];
-                QG[m] = slot[CP + cl];
-            }
+            const float* slot = qsh + ((r & 1) * CP + cl) * 2 * M;
+            const float4 ql4 = ld4(slot), qg4 = ld4(slot + M);
+            float QL[M] = {ql4.x, ql4.y, ql4.z, ql4.w};
+            float QG[M] = {qg4.x, qg4.y, qg4.z, qg4.w};
             if (pend) {                                // summed before the ring was rebased
                 const float sc = fast_exp2(-pdl);
 #pragma unroll
@@ -360,15 +398,16 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
             }
             if ((r & 1) == 0 && r > 0) {
                 // ---- rebase: this label's values move to a new base
-                const float ref = fmaxf(Mref, Rh[DIRECT - 1]);
+                const float rn = fmaxf(fast_log2(sH[M - 1]) + fH[M - 1], NEG);
+                const float ref = fmaxf(Mref, rn);
                 const float dl = cact && ref > NEG_HALF ? ref : 0.0f;
                 const float sc = fast_exp2(-dl);
                 Bc += (double)dl;
                 BH += (double)dl;
                 Mref -= dl;
 #pragma unroll
-                for (int i = 0; i < DIRECT; ++i) {
-                    Rh[i] -= dl;
+                for (int i = 0; i < M; ++i) {
+                    fH[i] -= dl;
                     Eh[i] *= sc;
                 }
 #pragma unroll
@@ -376,42 +415,45 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                     QL[m] *= sc;
                     QG[m] -= dl;
                 }
-                *(cact ? dlsh + cl : dummy + tid) = dl;
+                *(cact ? dlsh + cl : sink + (tid & 7)) = dl;
                 pdl = dl;
                 pend = true;
             }
-            // ---- per-round constants.  Inside the round H moves by integer exponents
-            // only: H(p_m) = H0 + eacc_m with eacc_m the sum of the earlier steps' e, so
-            // 2^(S(p_m) + B_c - H(p_m)) = 2^hb[m] * 2^-eacc_m exactly.
+            // ---- per-round constants (H fixed inside the round)
             const double H0 = H;
-            float hb[M], yv[M], fb[M];
+            float hb[M], yv[M], fb[M], fo[M];
+            {
+                // S(p_m) of label cl, rows row0 .. row0+3 (row0 % 4 == 0: 16-byte loads)
+                const double2* sp = reinterpret_cast<const double2*>(Sch + cl * CH + row0);
+                const double2 s01 = sp[0], s23 = sp[1];
+                const double sv4[M] = {s01.x, s01.y, s23.x, s23.y};
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                hb[m] = (float)(Srow[(row0 + m) * C + cl] + BH);   // S(p_m) + B_c - H0
-                yv[m] = fast_exp2(hb[m] + dmax);                  // message scale
-                fb[m] = fast_exp2(tmax - hb[m]);                   // ring-entry scale
+                for (int m = 0; m < M; ++m) {
+                    hb[m] = (float)(sv4[m] + BH);            // S(p_m) + B_c - H0
+                    yv[m] = fast_exp2(hb[m] + dmax);         // message scale
+                    fo[m] = tmax - hb[m];
+                    fb[m] = fast_exp2(fo[m]);                // ring-entry scale
+                }
             }
             // ---- fast pass (linear space, no branches)
             bool ok = true;
-            int ev[M];                 // normaliser exponent of each step
             float sig[M];              // combined message sum (linear) or its log2 (replay)
-            float qv[M];               // message total of each step (log Z at p = L)
-            int eacc = 0;
-            // terms k >= 2 of the first message; each step forms the next one's ahead of
-            // its transition step, so only one FMA waits for the newest ring entry
+            float qv[M];               // message total of each step (log2 in a replay)
+            // terms k = 2 .. m+4 of step m are formed ahead of its transition step, so only
+            // one FMA waits for the newest ring entry
             float part = QL[0];
 #pragma unroll
-            for (int k = DIRECT; k >= 2; --k) part = fmaf(Eh[DIRECT - k], Dl[k - 1], part);
+            for (int k = M; k >= 2; --k) part = fmaf(Eh[M - k], Dl[k - 1], part);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const int p = rs + 1 + m;
-                const float sg = fmaf(Eh[DIRECT - 1 + m], Dl[0], part);
+                const float sg = fmaf(Eh[M - 1 + m], Dl[0], part);
                 sig[m] = sg;
-                const float pn = cact ? __builtin_amdgcn_ldexpf(sg * yv[m], -eacc) : 0.0f;
+                const float pn = cact ? sg * yv[m] : 0.0f;
                 if (m + 1 < M) {
                     float nx = QL[m + 1];
 #pragma unroll
-                    for (int k = DIRECT; k >= 2; --k) nx = fmaf(Eh[DIRECT + m + 1 - k], Dl[k - 1], nx);
+                    for (int k = m + 1 + M; k >= 2; --k) nx = fmaf(Eh[M + m + 1 - k], Dl[k - 1], nx);
                     part = nx;
                 }
                 // transition step of p: row broadcasts of every label's message (labels sit
@@ -430,34 +472,31 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                 const float s = sv[0], q = qa[0];
                 // label lanes only: lanes outside row 0 broadcast their own (empty) row
                 ok &= (p > t1) | !cact | (in_lin_range(sg) & in_lin_range(s) & in_lin_range(q));
-                const int e = __builtin_amdgcn_frexp_expf(q);          // q = m 2^e
-                Eh[DIRECT + m] = __builtin_amdgcn_ldexpf(s * fb[m], eacc);
-                Rh[DIRECT + m] = fast_log2(s) + (tmax - hb[m]) + (float)eacc;
+                Eh[M + m] = s * fb[m];
+                sH[M + m] = s;
+                fH[M + m] = fo[m];
                 qv[m] = q;
-                ev[m] = e;
-                eacc += e;
             }
             bool replayed = false;
             if (wave_any(!ok)) {
                 // ---- exact replay of the round in log space
                 replayed = true;
-                eacc = 0;
+                float Rl[2 * M];
+#pragma unroll
+                for (int i = 0; i < M; ++i) Rl[i] = fmaxf(fast_log2(sH[i]) + fH[i], NEG);
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
-                    const int p = rs + 1 + m;
-                    if (p > t1) break;
-                    const float hp = hb[m] - (float)eacc;
-                    float x[DIRECT + 1];
+                    const float hp = hb[m];
+                    // durations 1 .. m+4 from the history, then the bulk sum; unused: NEG
+                    float x[2 * M + 1], xd[2 * M + 1];
 #pragma unroll
-                    for (int k = 1; k <= DIRECT; ++k) x[k - 1] = Rh[DIRECT - 1 + m + 1 - k] + dlog[k - 1];
-                    x[DIRECT] = QG[m];
-                    float mx = x[0];
-#pragma unroll
-                    for (int k = 1; k <= DIRECT; ++k) mx = fmaxf(mx, x[k]);
-                    float sm = 0.0f;
-#pragma unroll
-                    for (int k = 0; k <= DIRECT; ++k) sm += fast_exp2(x[k] - mx);
-                    const float sigma = mx + fast_log2(sm);
+                    for (int k = 1; k <= 2 * M; ++k) {
+                        x[k - 1] = k <= m + M ? Rl[M + m - k] : NEG;
+                        xd[k - 1] = k <= m + M ? dlog[k - 1] : 0.0f;
+                    }
+                    x[2 * M] = QG[m];
+                    xd[2 * M] = 0.0f;
+                    const float sigma = group_lse<1, 2 * M + 1>(x, xd);
                     sig[m] = sigma;
                     const float u = cact ? hp + sigma : NEG;
                     float uv[CP];
@@ -466,54 +505,52 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                         uv[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), i));
                     const float rn = group_lse<1, CP>(uv, treg) - hp;
                     const float lq = group_lse<1, CP>(uv, zero);
-                    const int e = lq > NEG_HALF ? (int)floorf(lq) + 1 : 0;
-                    Rh[DIRECT + m] = rn;
-                    Eh[DIRECT + m] = exp2_or_zero(rn);
+                    Rl[M + m] = rn;
+                    Eh[M + m] = exp2_or_zero(rn);
+                    sH[M + m] = 1.0f;
+                    fH[M + m] = rn;
                     qv[m] = lq;
-                    ev[m] = e;
-                    eacc += e;
                 }
             }
             {
-                const int mL = L - rs - 1;                 // log Z when the round holds L
-                if (mL >= 0 && mL < M) {
-                    int eb = 0;
+                // log Z when the round holds L; the normaliser follows the round's last step
+                const int mL = L - rs - 1;
+                const int ml = min(M - 1, t1 - rs - 1);
+                float ql = qv[0], qe = qv[0];
 #pragma unroll
-                    for (int m = 0; m < M; ++m)
-                        if (m < mL) eb += ev[m];
-                    float ql = qv[0];
-#pragma unroll
-                    for (int m = 1; m < M; ++m)
-                        if (m == mL) ql = qv[m];
-                    lz = H0 + (double)eb + (double)(replayed ? ql : fast_log2(ql));
+                for (int m = 1; m < M; ++m) {
+                    if (m == mL) ql = qv[m];
+                    if (m == ml) qe = qv[m];
                 }
-            }
-            {
-                int et = 0;                                // H moves by the steps taken
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-                    if (rs + 1 + m <= t1) et += ev[m];
-                H = H0 + (double)et;
+                if (mL >= 0 && mL < M) lz = H0 + (double)(replayed ? ql : fast_log2(ql));
+                int e;
+                if (replayed) e = qe > NEG_HALF ? (int)floorf(qe) + 1 : 0;
+                else e = __builtin_amdgcn_frexp_expf(qe);
+                H = H0 + (double)e;
                 BH = Bc - H;
             }
-            // ---- publish the round: ring entries for the bulk lanes, outputs, checkpoints
-            int ec = 0;                                    // steps taken so far this round
+            // ---- publish the round: ring block, staging for the log ring, outputs, checkpoints
+            if constexpr (LIN)
+                st4(E + (cact ? cl : C) * P + round_slot(r, RMASK),
+                    make_float4(Eh[M], Eh[M + 1], Eh[M + 2], Eh[M + 3]));
+            {
+                float* ns = nsh + ((r & 1) * (CP + 1) + (cact ? cl : CP)) * 2 * M;
+                st4(ns, make_float4(sH[M], sH[M + 1], sH[M + 2], sH[M + 3]));
+                st4(ns + M, make_float4(fH[M], fH[M + 1], fH[M + 2], fH[M + 3]));
+            }
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const int p = rs + 1 + m;
                 if (p > t1) break;
-                float* ns = nsh + ((r & 1) * M + m) * 2 * CP;
-                *(cact ? ns + cl : dummy + tid) = Rh[DIRECT + m];
-                *(cact ? ns + CP + cl : dummy + tid) = Eh[DIRECT + m];
                 if (a.write_xa && cact) {
-                    const double Sp = Srow[(row0 + m) * C + cl];
+                    const double Sp = Sch[cl * CH + row0 + m];
                     const float sgl = replayed ? sig[m] : fast_log2(sig[m]) + dmax;
                     Xout[(outrow + (dir == 0 ? p : L - p)) * C + cl] = (Sp + Bc + (double)sgl) * LN2;
-                    if (p < t1)
-                        Aout[(outrow + (dir == 0 ? p : L - p)) * C + cl] =
-                            (Bc + (double)Rh[DIRECT + m]) * LN2;
+                    if (p < t1) {
+                        const float rl = replayed ? fH[M + m] : fast_log2(sH[M + m]) + fH[M + m];
+                        Aout[(outrow + (dir == 0 ? p : L - p)) * C + cl] = (Bc + (double)rl) * LN2;
+                    }
                 }
-                ec += ev[m];                             // H after the transition step of p
                 if (QG[m] > NEG_HALF) Mref = QG[m];
                 if (p == next_ck) {
                     // chain half of the checkpoint after the transition step of p; the ring
@@ -524,29 +561,33 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                             a.ck_base[ck * C + cl] = Bc;
                             a.ck_mprev[ck * C + cl] = Mref;
                         }
-                        if (tid == 0) a.ck_href[ck] = H0 + (double)ec;
+                        if (tid == 0) a.ck_href[ck] = H0;
                     }
                     next_ck += a.delta;
                 }
             }
 #pragma unroll
-            for (int i = 0; i < DIRECT; ++i) {   // history for the next round
-                Rh[i] = Rh[i + M];
+            for (int i = 0; i < M; ++i) {   // history for the next round
                 Eh[i] = Eh[i + M];
+                sH[i] = sH[i + M];
+                fH[i] = fH[i + M];
             }
         } else {
             // ---- S staging: in the first round of a chunk publish the next one
             if (rs + 1 == tc && tc + CH <= t1) {
-                double* dst = Sbuf + ((nch + 1) & 1) * rowsN;
+                double* dst = Sbuf + ((nch + 1) & 1) * chunkN;
 #pragma unroll
                 for (int i = 0; i < PF; ++i) {
                     const int q = bt + i * NB;
-                    if (q < rowsN) dst[q] = spub(pf[i], q - (q / C) * C);
+                    if (q < chunkN) {
+                        const int row = q / C, l = q - row * C;
+                        dst[l * CH + row] = spub(pf[i], l);
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < PF; ++i) {
                     const int q = bt + i * NB;
-                    if (q < rowsN) {
+                    if (q < chunkN) {
                         const int rr = q / C, l = q - rr * C;
                         const int tt = tc + 2 * CH + rr;
                         pf[i] = (tt <= t1) ? Sb[sidx(tt, l)] : 0.0;
@@ -554,7 +595,7 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                 }
             }
             ring_round(r, rs);
-            // ---- bulk sums of round r+1 (entries <= rs suffice)
+            // ---- bulk sums of round r+1 (ring blocks of rounds <= r-1)
             bulk_round(r + 1, rs + M + 1);
         }
         __syncthreads();
@@ -568,45 +609,44 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
 }
 
 // ------------------------------------------------------------------ launch
-template <int G, int KPL, int LAY>
+template <int G, int BPL, int CP, bool LIN>
 static hipError_t launch_lse_round_inst(const SweepArgs& a, dim3 grid, const SweepCfg& cfg,
                                         hipStream_t stream) {
-    if (cfg.NT > 320 || cfg.lse.CH > lse_chunk_max(G) || cfg.lse.CH % ROUND != 0)
+    if (cfg.NT > 320 || cfg.lse.CH > lse_chunk_max(G) || cfg.lse.CH % ROUND != 0 ||
+        cfg.lse.P % 4 != 0 || cfg.RS % ROUND != 0)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_lse_round<G, KPL, LAY>), grid, dim3(cfg.NT), cfg.lse.bytes, stream, a,
-                       cfg.RS, cfg.lse.P, cfg.lse.CH);
+    hipLaunchKernelGGL((k_lse_round<G, BPL, CP, LIN>), grid, dim3(cfg.NT), cfg.lse.bytes, stream,
+                       a, cfg.RS, cfg.lse.P, cfg.lse.CH);
     return hipGetLastError();
 }
 
-#define LSE_ROUND_KPL_CASES(G)                                                       \
-    switch (cfg.KPLr) {                                                              \
-        case 0: return launch_lse_round_inst<G, 0, LAY>(a, grid, cfg, stream);          \
-        case 1: return launch_lse_round_inst<G, 1, LAY>(a, grid, cfg, stream);          \
-        case 2: return launch_lse_round_inst<G, 2, LAY>(a, grid, cfg, stream);          \
-        case 3: return launch_lse_round_inst<G, 3, LAY>(a, grid, cfg, stream);          \
-        case 4: return launch_lse_round_inst<G, 4, LAY>(a, grid, cfg, stream);          \
-        case 5: return launch_lse_round_inst<G, 5, LAY>(a, grid, cfg, stream);          \
-        case 6: return launch_lse_round_inst<G, 6, LAY>(a, grid, cfg, stream);          \
-        case 7: return launch_lse_round_inst<G, 7, LAY>(a, grid, cfg, stream);          \
-        case 8: return launch_lse_round_inst<G, 8, LAY>(a, grid, cfg, stream);          \
-        case 10: return launch_lse_round_inst<G, 10, LAY>(a, grid, cfg, stream);        \
-        case 12: return launch_lse_round_inst<G, 12, LAY>(a, grid, cfg, stream);        \
-        case 16: return launch_lse_round_inst<G, 16, LAY>(a, grid, cfg, stream);        \
-        case 24: return launch_lse_round_inst<G, 24, LAY>(a, grid, cfg, stream);        \
-        case 32: return launch_lse_round_inst<G, 32, LAY>(a, grid, cfg, stream);        \
+#define LSE_ROUND_BPL_CASES(G, CP)                                                   \
+    switch (cfg.BPL) {                                                               \
+        case 0: return launch_lse_round_inst<G, 0, CP, LIN>(a, grid, cfg, stream);      \
+        case 1: return launch_lse_round_inst<G, 1, CP, LIN>(a, grid, cfg, stream);      \
+        case 2: return launch_lse_round_inst<G, 2, CP, LIN>(a, grid, cfg, stream);      \
+        case 3: return launch_lse_round_inst<G, 3, CP, LIN>(a, grid, cfg, stream);      \
+        case 4: return launch_lse_round_inst<G, 4, CP, LIN>(a, grid, cfg, stream);      \
+        case 5: return launch_lse_round_inst<G, 5, CP, LIN>(a, grid, cfg, stream);      \
+        case 6: return launch_lse_round_inst<G, 6, CP, LIN>(a, grid, cfg, stream);      \
+        case 7: return launch_lse_round_inst<G, 7, CP, LIN>(a, grid, cfg, stream);      \
+        case 8: return launch_lse_round_inst<G, 8, CP, LIN>(a, grid, cfg, stream);      \
         default: return hipErrorInvalidValue;                                        \
     }
 
-template <int LAY>
+// every shape of the round kernel with (LIN) or without the linear ring
+template <bool LIN>
 hipError_t launch_lse_round_layout(const SweepCfg& cfg, const SweepArgs& a, int ndir,
                                    hipStream_t stream) {
-    dim3 grid = a.mode == MODE_FULL ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);
-    if (cfg.G == 64) { LSE_ROUND_KPL_CASES(64) }
-    if (cfg.G == 32) { LSE_ROUND_KPL_CASES(32) }
-    if (cfg.G == 16) { LSE_ROUND_KPL_CASES(16) }
+    const dim3 grid = a.mode == MODE_FULL ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);
+    if (cfg.G == 64 && cfg.CPr == 4) { LSE_ROUND_BPL_CASES(64, 4) }
+    if (cfg.G == 32 && cfg.CPr == 6) { LSE_ROUND_BPL_CASES(32, 6) }
+    if (cfg.G == 32 && cfg.CPr == 8) { LSE_ROUND_BPL_CASES(32, 8) }
+    if (cfg.G == 16 && cfg.CPr == 12) { LSE_ROUND_BPL_CASES(16, 12) }
+    if (cfg.G == 16 && cfg.CPr == 16) { LSE_ROUND_BPL_CASES(16, 16) }
     return hipErrorInvalidValue;
 }
 
-#undef LSE_ROUND_KPL_CASES
+#undef LSE_ROUND_BPL_CASES
 
 }  // namespace semicrf

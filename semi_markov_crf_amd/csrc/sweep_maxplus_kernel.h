@@ -272,9 +272,7 @@ static hipError_t launch_maxplus_inst(const SweepArgs& a, const SweepCfg& cfg,
 // every kernel shape of one ring layout (one translation unit per layout)
 template <bool MIR>
 hipError_t launch_maxplus_layout(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream) {
-    if (cfg.G == 64) { MAXPLUS_KPL_CASES(64, 1, 4, 256) }
-    if (cfg.G == 32) { MAXPLUS_KPL_CASES(32, 1, 8, 256) }
-    if (cfg.G == 16) { MAXPLUS_KPL_CASES(16, 1, 16, 256) }
+    // C <= 16 (G >= 16) runs the round kernel instead
     if (cfg.G == 8 && cfg.CPL == 4) { MAXPLUS_KPL_CASES(8, 4, 8, 256) }
     if (cfg.G == 8 && cfg.CPL == 8) { MAXPLUS_KPL_CASES(8, 8, 8, 512) }
     if (cfg.G == 4) { MAXPLUS_KPL_CASES(4, 32, 4, 512) }
