@@ -33,8 +33,7 @@ struct SweepLds {
 struct SweepCfg {
     int G, KPL, CPL, GT; // instantiated kernel shape (KPL: register capacity per lane)
     int kpl;             // durations k >= 3 per lane actually used
-    int KPLr;            // max-plus round kernel: durations k >= 2*ROUND per bulk lane
-    int BPL;             // log-semiring round kernel: ring blocks of ROUND positions per bulk lane
+    int BPL;             // round kernels: ring blocks of ROUND positions per bulk lane
     int CPr;             // round kernels: labels the chain wavefront broadcasts (>= C)
     int NT;              // threads per workgroup of the log-semiring sweep (multiple of 64)
     int NTv;             // threads per workgroup of the max-plus sweep
@@ -58,10 +57,8 @@ inline size_t lse_lds_bytes(int C, int NT, int UP, int P, int CH, bool lin) {
     return (size_t)(2 * (CH + 1) * C + C) * 8 +
            (size_t)((lin ? 2 : 1) * (C + 1) * P + 4 * UP + NT) * 4;
 }
-// The round kernels (C <= 16): ROUND positions per workgroup barrier.  Max-plus: the
-// chain wavefront takes durations k = 1 .. DIRECT itself, the bulk wavefronts the rest.
+// The round kernels (C <= 16): ROUND positions per workgroup barrier.
 constexpr int ROUND = 4;
-constexpr int DIRECT = 2 * ROUND - 1;
 // Dynamic LDS of the log-semiring round kernel: S chunks [2][C][CH] and S(L) (fp64), the
 // rings [C+1][P] (two when linear), bulk sums [2][CP][2][ROUND], staged ring entries
 // [2][CP+1][2][ROUND], rebase shifts and dmax [CP rounded to 4], a sink and two constant
@@ -72,11 +69,12 @@ inline size_t lse_round_lds_bytes(int C, int CP, int P, int CH, bool lin) {
            (size_t)((lin ? 2 : 1) * (C + 1) * P + 4 * CP * ROUND + 4 * (CP + 1) * ROUND +
                     2 * cp4 + 16) * 4;
 }
-// Dynamic LDS of the max-plus round kernel (C <= 16): S chunks [2][CH+1][C] (fp64), the
-// ring, bulk maxima with their k and ring entries [2 rounds][ROUND][CP] each, rebase
-// shifts [CP], a sink [NT].
-inline size_t maxplus_round_lds_bytes(int C, int NT, int CP, int P, int CH) {
-    return (size_t)(2 * (CH + 1) * C) * 8 + (size_t)((C + 1) * P + (6 * ROUND + 1) * CP + NT) * 4;
+// Dynamic LDS of the max-plus round kernel (C <= 16): S chunks [2][C][CH] (fp64), the
+// ring [C+1][P], bulk maxima and their k [2][CP][2][ROUND], rebase shifts [CP rounded to
+// 4], a sink and a constant block [12] (fp32).
+inline size_t maxplus_round_lds_bytes(int C, int CP, int P, int CH) {
+    const int cp4 = (CP + 3) / 4 * 4;
+    return (size_t)(2 * CH * C) * 8 + (size_t)((C + 1) * P + 4 * CP * ROUND + cp4 + 12) * 4;
 }
 // Dynamic LDS of the max-plus sweep: S chunks [2][CH][C] (fp64), R ring [C+1][P] and
 // u [2][UP] (fp32).

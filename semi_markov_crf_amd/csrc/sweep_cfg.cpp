@@ -45,26 +45,16 @@ SweepCfg choose_sweep(int C, int K) {
     s.NT = s.split ? 64 + s.NTv : s.NTv;
     // RS >= K + 2 live positions and >= the widest window a lane addresses (2 + KPL*G)
     s.RS = pow2_at_least(std::max(K + 2, 3 + kmax * G));
-    s.KPLr = 0;
     s.BPL = 0;
     s.CPr = 0;
     if (G >= 16) {
-        // max-plus round kernel: bulk lanes take k >= 2*ROUND; the ring also keeps the
-        // entries of the rounds in flight
-        const int kplr = K >= 2 * ROUND ? (K - 2 * ROUND + 1 + G - 1) / G : 0;
-        int kr = -1;
-        for (int v : kInst)
-            if (v >= kplr) { kr = v; break; }
-        if (kr < 0) return s;
-        s.KPLr = kr;
-        // log-semiring round kernel: ring blocks of ROUND positions; a bulk sum reaches
-        // back bmax blocks, the ring holds those plus the rounds in flight
+        // round kernels: ring blocks of ROUND positions; a bulk sum reaches back bmax
+        // blocks, the ring holds those plus the rounds in flight
         const int bmax = (K + ROUND - 1) / ROUND;
         s.BPL = (std::max(bmax - 1, 0) + G - 1) / G;
         if (s.BPL > 8) return s;
         s.CPr = C <= 4 ? 4 : C <= 6 ? 6 : C <= 8 ? 8 : C <= 12 ? 12 : 16;
-        s.RS = pow2_at_least(std::max({s.RS, K + 3 * ROUND + 2, 2 * ROUND + kr * G + 1,
-                                       ROUND * (bmax + 5)}));
+        s.RS = pow2_at_least(ROUND * (bmax + 5));
     }
     const int pad = G < 32 ? G : 0;   // staggers the label rows over the LDS banks
     const int UP = GT * CPL;
@@ -82,11 +72,12 @@ SweepCfg choose_sweep(int C, int K) {
         }
         if (s.lse.bytes) break;
     }
-    // max-plus sweep: mirrored, then plain
+    // max-plus sweep: mirrored, then plain (the round kernel: one copy, float4 blocks)
     for (int lay : {int(SWEEP_MIRRORED), 0}) {
-        const int P = pitch(lay);
-        for (int ch = MAXPLUS_CHUNK_MAX; ch >= 8 && s.vit.bytes == 0; ch >>= 1) {
-            const size_t n = s.split ? maxplus_round_lds_bytes(C, s.NT, 256 / G, P, ch)
+        if (s.split && (lay & SWEEP_MIRRORED)) continue;
+        const int P = s.split ? s.RS + 4 : pitch(lay);
+        for (int ch = s.split ? lse_chunk_max(G) : MAXPLUS_CHUNK_MAX; ch >= 8 && s.vit.bytes == 0; ch >>= 1) {
+            const size_t n = s.split ? maxplus_round_lds_bytes(C, s.CPr, P, ch)
                                      : maxplus_lds_bytes(C, UP, P, ch);
             if (n <= LDS_BUDGET) s.vit = SweepLds{lay, P, ch, n};
         }

@@ -1,17 +1,20 @@
-// Max-plus (Viterbi) streaming sweep for small label counts (C <= 16), ROUND positions per
-// workgroup barrier: the (max, +) form of k_lse_round (sweep_lse_round.h) with backpointers.
+// Max-plus (Viterbi) streaming sweep for small label counts (C <= 16), ROUND = 4 positions
+// per workgroup barrier: the (max, +) form of k_lse_round (sweep_lse_round.h) with
+// backpointers, on the same float4 ring blocks.
 //
-//  * chain wavefront (threads 0..63): lane c holds label c.  Per position p: the best
-//    segment ending at p with label c over durations k = 1 .. DIRECT (register history of
-//    the label's ring entries) and the bulk best over k >= 2*ROUND; then the transition
-//    step over every label's value (DPP row broadcast), lowest-index argmax on ties
-//    (durations before previous labels, k = 1 first).  Backpointer of (p, c):
-//    k | c' << 16 (c' = best previous label of a segment of label c starting at p).
-//  * bulk wavefronts (threads 64..): label rings in LDS, bulk max and its lowest k over
-//    durations k >= 2*ROUND for the positions of the next round, ring insertion and
-//    rebases one round late, S staging.
-// Values are natural-log scores kept relative to a per-label fp64 base (moved every
-// second round) and a common fp64 reference H that advances by integers.
+//  * chain wavefront (threads 0..63): lane c holds label c.  Per position p = (round
+//    start) + 1 + m: the best segment of label c ending at p over durations k = 1 .. m+4
+//    (registers: the previous round's block and this round's entries) and the bulk best
+//    over the older ones; then the transition step of p over every label's value (DPP row
+//    broadcast).  Ties go to the lowest index: durations before previous labels, k = 1
+//    first.  Backpointer of (p, c): k | c' << 16 (c' = best previous label of a segment
+//    of label c starting at p).  The chain writes its round's ring block itself.
+//  * bulk wavefronts (threads 64..): lanes grouped G per label.  In round r they apply
+//    the chain's rebase of round r-1 to the ring and form the bulk best (and its lowest
+//    k) of each position of round r+1 over ring blocks of rounds <= r-1; they also stage
+//    S, label-major.
+// Values are natural-log scores relative to a per-label fp64 base (moved every second
+// round) and a common fp64 reference H that advances by whole units once per round.
 #pragma once
 
 #include "internal.h"
@@ -32,20 +35,45 @@ __device__ __forceinline__ void row_bcast_all_mp(float v, float* out) {
 }
 
 __device__ __forceinline__ double nan_mp() { return __longlong_as_double(0x7ff8000000000000LL); }
+__device__ __forceinline__ int slot_mp(int rho, int RMASK) { return (rho * ROUND) & RMASK; }
+__device__ __forceinline__ float4 ld4_mp(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void st4_mp(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ float at4_mp(const float4& v, int d) {
+    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+}
+
+// max of n values (tree of v_max3)
+template <int N>
+__device__ __forceinline__ float max_tree(const float* x) {
+    if constexpr (N == 1) return x[0];
+    else if constexpr (N == 2) return fmaxf(x[0], x[1]);
+    else {
+        float y[(N + 2) / 3];
+#pragma unroll
+        for (int i = 0; i < (N + 2) / 3; ++i) {
+            const float a0 = x[3 * i];
+            const float a1 = 3 * i + 1 < N ? x[3 * i + 1] : a0;
+            const float a2 = 3 * i + 2 < N ? x[3 * i + 2] : a0;
+            y[i] = fmaxf(fmaxf(a0, a1), a2);
+        }
+        return max_tree<(N + 2) / 3>(y);
+    }
+}
 
 }  // namespace
 
-// G: bulk lanes per label (C <= 256/G); KPL: durations per bulk lane (k = 2*ROUND + j +
-// i*G); MIR: mirrored ring.  Grid (B), block 64 + ceil(C*G/64)*64 threads.
-template <int G, int KPL, bool MIR>
+// G: bulk lanes per label (C <= 256/G); BPL: ring blocks per bulk lane; CP: labels the
+// chain broadcasts (>= C).  Grid (B), block 64 + ceil(C*G/64)*64 threads.
+template <int G, int BPL, int CP>
 __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const int RS,
                                                       const int P, const int CH) {
     constexpr int M = ROUND;
-    constexpr int CP = 256 / G;
-    static_assert(CP <= 16, "the labels of the chain wavefront share one DPP row");
-    constexpr int PF = (lse_chunk_max(G) + 1 + G - 1) / G;
-    constexpr int KP = KPL > 0 ? KPL : 1;
-    constexpr int HN = DIRECT + M;
+    static_assert(M == 4, "ring blocks are float4");
+    static_assert(CP <= 16 && CP * G <= 256, "the labels of the chain wavefront share one DPP row");
+    constexpr int PF = (lse_chunk_max(G) + G - 1) / G;
+    constexpr int BP = BPL > 0 ? BPL : 1;
+    constexpr int KD = 2 * M - 1;
+    constexpr int CP4 = (CP + 3) / 4 * 4;
     extern __shared__ double lds[];
     const int C = a.C, K = a.K, T = a.T;
     const int tid = threadIdx.x, NT = blockDim.x, NB = NT - 64;
@@ -64,78 +92,116 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
     const int L = bad ? -Lr : Lr;
     const int t0 = 0, t1 = L;
     const int RMASK = RS - 1;
-    const int rowsN = (CH + 1) * C;
+    const int bmax = (K + M - 1) / M;
+    const int NR = bmax + 3;
 
-    double* Sbuf = lds;                                    // [2][CH+1][C]
-    float* R = (float*)(Sbuf + 2 * rowsN);                 // [C+1][P]
-    float* qsh = R + (C + 1) * P;                          // [2 rounds][M][max, k][CP]
-    float* nsh = qsh + 2 * M * 2 * CP;                     // [2 rounds][M][CP] ring entries
-    float* dlsh = nsh + 2 * M * CP;                        // [CP] rebase shift per label
-    float* dummy = dlsh + CP;                              // [NT]
+    double* Sbuf = lds;                                    // [2][C][CH] label-major
+    float* R = (float*)(Sbuf + 2 * C * CH);                // [C+1][P]
+    float* qsh = R + (C + 1) * P;                          // [2 rounds][CP][max, k][M]
+    float* dlsh = qsh + 2 * CP * 2 * M;                    // [CP4] rebase shift per label
+    float* sink = dlsh + CP4;                              // [8]
+    float* nblk = sink + 8;                                // [4] NEG: blocks past K
     float* Rrow = R + cr * P;
 
     const double* Sb = a.S + (size_t)b * (T + 1) * C;
     for (int q = tid; q < (C + 1) * P; q += NT) R[q] = NEG;
+    for (int q = tid; q < 2 * CP * 2 * M; q += NT) qsh[q] = ((q / M) & 1) ? __int_as_float(INT_MAX) : NEG;
+    if (tid < M) nblk[tid] = NEG;
 
     // ---------------------------------------------------------------- constants
     auto durv = [&](int c, int k) -> float {
-        return k <= K ? fmaxf(a.dur[(k - 1) * C + c], NEG) : NEG;
+        return (k >= 1 && k <= K) ? fmaxf(a.dur[(k - 1) * C + c], NEG) : NEG;
     };
-    float dreg[KP];
+    // bulk lanes: block i of lane j lies bb = 2 + j + i*G rounds back; its entry d enters
+    // step m with duration k = 4*bb + m - d = 4*bb + t - 3, t = m - d + 3
+    float Dc[BP][2 * M - 1];
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) dreg[i] = bact ? durv(cb, 2 * M + j + i * G) : NEG;
-    float dlog[DIRECT];
+    for (int i = 0; i < BPL; ++i)
 #pragma unroll
-    for (int k = 0; k < DIRECT; ++k) dlog[k] = cact ? durv(cl, k + 1) : NEG;
+        for (int t = 0; t < 2 * M - 1; ++t) Dc[i][t] = bact ? durv(cb, M * (2 + j + i * G) + t - 3) : NEG;
+    float dlog[KD];
+#pragma unroll
+    for (int k = 0; k < KD; ++k) dlog[k] = cact ? durv(cl, k + 1) : NEG;
     float treg[CP];
 #pragma unroll
     for (int i = 0; i < CP; ++i) treg[i] = (cact && i < C) ? fmaxf(a.trans[i * C + cl], NEG) : NEG;
     __syncthreads();   // ring cleared
 
-    // bulk best (k >= 2M) of the M positions p0 .. p0+M-1, published for round r
-    auto bulk_round = [&](int r, int p0) {
+    // bulk best (durations k >= m + 5) of the positions of round rr and its lowest k
+    auto bulk_round = [&](int rr) {
+        float Q[M];
+        int kq[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            float best = NEG;
-            int kb = INT_MAX;
-            if constexpr (KPL > 0) {
-                float v[KP];
-                ring_load<G, KPL, MIR>(Rrow, p0 + m - 2 * M + 3, j, RS, v);
-                best = group_argmax<G, KPL>(v, dreg, j, &kb);   // k = 3 + j + i*G here
-                kb += 2 * M - 3;                                 // shift to k = 2M + j + i*G
-            }
-            float* slot = qsh + ((r & 1) * M + m) * 2 * CP;
-            *(bact && j == 0 ? slot + cb : dummy + tid) = best;
-            *(bact && j == 0 ? slot + CP + cb : dummy + tid) = __int_as_float(kb);
+            Q[m] = NEG;
+            kq[m] = INT_MAX;
         }
+        if constexpr (BPL > 0) {
+            float4 v[BP];
+#pragma unroll
+            for (int i = 0; i < BPL; ++i) {
+                const int bb = 2 + j + i * G;
+                v[i] = ld4_mp(bb <= bmax ? Rrow + slot_mp(rr - bb, RMASK) : nblk);
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float x[BP * M];
+#pragma unroll
+                for (int i = 0; i < BPL; ++i)
+#pragma unroll
+                    for (int d = 0; d < M; ++d) x[i * M + d] = at4_mp(v[i], d) + Dc[i][m - d + 3];
+                const float mx = group_reduce<G>(max_tree<BPL * M>(x), OpMax());
+                int kk = INT_MAX;                           // candidates by decreasing k
+#pragma unroll
+                for (int i = BPL - 1; i >= 0; --i)
+#pragma unroll
+                    for (int d = 0; d < M; ++d)
+                        if (x[i * M + d] == mx) kk = M * (2 + j + i * G) + m - d;
+                Q[m] = mx;
+                kq[m] = group_min_int<G>(kk);
+            }
+        }
+        const bool wr = bact && j == 0;
+        float* slot = qsh + ((rr & 1) * CP + cb) * 2 * M;
+        st4_mp(wr ? slot : sink, make_float4(Q[0], Q[1], Q[2], Q[3]));
+        st4_mp(wr ? slot + M : sink, make_float4(__int_as_float(kq[0]), __int_as_float(kq[1]),
+                                                 __int_as_float(kq[2]), __int_as_float(kq[3])));
     };
 
     // ---------------------------------------------------------------- start state
-    if (bact && j == 0) ring_put<MIR>(Rrow, 0, RS, 0.0f);   // position 0: no transition into it
-    float Rh[HN];
+    if (bact && j == 0) Rrow[slot_mp(-1, RMASK) + M - 1] = 0.0f;   // position 0
+    // chain history, i < M: the previous round's positions (round start) - 3 + i; i >= M:
+    // this round's (ring entries A - B_c)
+    float Rh[2 * M];
 #pragma unroll
-    for (int i = 0; i < HN; ++i) Rh[i] = NEG;
-    Rh[DIRECT - 1] = 0.0f;
+    for (int i = 0; i < 2 * M; ++i) Rh[i] = NEG;
+    Rh[M - 1] = 0.0f;
     double Bc = 0.0, H = 0.0;
     float Mref = 0.0f;
 
+    const int chunkN = CH * C;
     double pf[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) pf[i] = 0.0;
     if (!chain) {
-        for (int q = bt; q < rowsN; q += NB) {
-            const int t = t0 + 1 + q / C;
-            Sbuf[q] = (t <= t1) ? Sb[(size_t)(t0 + 1) * C + q] : 0.0;
+        for (int q = bt; q < chunkN; q += NB) {
+            const int row = q / C, l = q - row * C;
+            const int t = t0 + 1 + row;
+            Sbuf[l * CH + row] = (t <= t1) ? Sb[(size_t)t * C + l] : 0.0;
         }
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
             const int q = bt + i * NB;
-            if (q < rowsN && t0 + 1 + CH + q / C <= t1) pf[i] = Sb[(size_t)(t0 + 1 + CH) * C + q];
+            if (q < chunkN) {
+                const int row = q / C, l = q - row * C;
+                const int t = t0 + 1 + CH + row;
+                if (t <= t1) pf[i] = Sb[(size_t)t * C + l];
+            }
         }
     }
     __syncthreads();
     __builtin_amdgcn_s_waitcnt(0);
-    if (!chain) bulk_round(0, t0 + 1);
+    if (!chain) bulk_round(0);
     __syncthreads();
 
     // ---------------------------------------------------------------- main loop
@@ -151,184 +217,183 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
             tc += CH;
             ++nch;
         }
-        const double* Srow = Sbuf + (nch & 1) * rowsN;
+        const double* Sch = Sbuf + (nch & 1) * chunkN;
         const int row0 = rs + 1 - tc;
         if (chain) {
-            float Q[M];
-            int kQ[M];
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const float* slot = qsh + ((r & 1) * M + m) * 2 * CP;
-                Q[m] = slot[cl];
-                kQ[m] = __float_as_int(slot[CP + cl]);
-            }
+            const float* slot = qsh + ((r & 1) * CP + cl) * 2 * M;
+            const float4 q4 = ld4_mp(slot), k4 = ld4_mp(slot + M);
+            float Q[M] = {q4.x, q4.y, q4.z, q4.w};
+            const int kQ[M] = {__float_as_int(k4.x), __float_as_int(k4.y), __float_as_int(k4.z),
+                               __float_as_int(k4.w)};
             if (pend) {
 #pragma unroll
                 for (int m = 0; m < M; ++m) Q[m] -= pdl;
                 pend = false;
             }
             if ((r & 1) == 0 && r > 0) {
-                const float ref = fmaxf(Mref, Rh[DIRECT - 1]);
+                const float ref = fmaxf(Mref, Rh[M - 1]);
                 const float dl = cact && ref > NEG_HALF ? ref : 0.0f;
                 Bc += (double)dl;
                 BH += (double)dl;
                 Mref -= dl;
 #pragma unroll
-                for (int i = 0; i < DIRECT; ++i) Rh[i] -= dl;
+                for (int i = 0; i < M; ++i) Rh[i] -= dl;
 #pragma unroll
                 for (int m = 0; m < M; ++m) Q[m] -= dl;
-                *(cact ? dlsh + cl : dummy + tid) = dl;
+                *(cact ? dlsh + cl : sink + (tid & 7)) = dl;
                 pdl = dl;
                 pend = true;
             }
             const double H0 = H;
             float hb[M];
+            {
+                const double2* sp = reinterpret_cast<const double2*>(Sch + cl * CH + row0);
+                const double2 s01 = sp[0], s23 = sp[1];
+                const double sv4[M] = {s01.x, s01.y, s23.x, s23.y};
 #pragma unroll
-            for (int m = 0; m < M; ++m) hb[m] = (float)(Srow[(row0 + m) * C + cl] + BH);
-            int eacc = 0;
-            int ev[M];
+                for (int m = 0; m < M; ++m) hb[m] = (float)(sv4[m] + BH);   // S(p_m) + B_c - H0
+            }
+            float mu[M];
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const int p = rs + 1 + m;
-                // best segment of label cl ending at p: durations 1 .. DIRECT, then the bulk
-                float best = Q[m];
+                // best segment of label cl ending at p: durations 1 .. m+4 (entries past
+                // them NEG), then the bulk
+                float x[2 * M + 1];
+#pragma unroll
+                for (int k = 1; k <= 2 * M; ++k) x[k - 1] = k <= m + M ? Rh[M + m - k] + dlog[k - 1] : NEG;
+                x[2 * M] = Q[m];
+                const float best = max_tree<2 * M + 1>(x);
                 int kbest = kQ[m];
 #pragma unroll
-                for (int k = DIRECT; k >= 1; --k) {         // later k first: ties go to lower k
-                    const float x = Rh[DIRECT - 1 + m + 1 - k] + dlog[k - 1];
-                    if (x >= best) {
-                        best = x;
-                        kbest = k;
-                    }
-                }
-                const float hp = hb[m] - (float)eacc;          // S(p) + B_c - H(p)
-                const float u = cact ? hp + best : NEG;        // V(p, cl) - H(p)
+                for (int k = 2 * M; k >= 1; --k)
+                    if (k <= m + M && x[k - 1] == best) kbest = k;
+                const float u = cact ? hb[m] + best : NEG;     // V(p, cl) - H0
                 // transition step of p over every label's value
-                float uv[CP];
+                float uv[CP], y[CP];
                 row_bcast_all_mp<CP>(u, uv);
-                float mt = NEG, mu = NEG;
+#pragma unroll
+                for (int i = 0; i < CP; ++i) y[i] = uv[i] + treg[i];
+                const float mt = max_tree<CP>(y);
                 int cbest = 0;
 #pragma unroll
-                for (int i = 0; i < CP; ++i) {
-                    const float y = uv[i] + treg[i];
-                    if (y > mt) {                               // strict: lowest c' on ties
-                        mt = y;
-                        cbest = i;
-                    }
-                    mu = fmaxf(mu, uv[i]);
-                }
-                const int e = mu > NEG_HALF ? (int)floorf(mu) : 0;
-                Rh[DIRECT + m] = mt - hp;
+                for (int i = CP - 1; i >= 0; --i)
+                    if (y[i] == mt) cbest = i;
+                mu[m] = max_tree<CP>(uv);
+                Rh[M + m] = mt - hb[m];
                 if (p <= t1 && cact)   // the label of position L + 1 is never read
                     a.bp[(outrow + p) * C + cl] = (uint32_t)kbest | ((uint32_t)cbest << 16);
                 if (p == L) {
                     // final label: lowest argmax of V(L, c)
                     int cs = 0;
-                    float vs = uv[0];
 #pragma unroll
-                    for (int i = 1; i < CP; ++i)
-                        if (uv[i] > vs) {
-                            vs = uv[i];
-                            cs = i;
-                        }
+                    for (int i = CP - 1; i >= 0; --i)
+                        if (uv[i] == mu[m]) cs = i;
                     if (tid == 0) {
-                        a.vscore[b] = bad ? nan_mp() : H0 + (double)eacc + (double)vs;
+                        a.vscore[b] = bad ? nan_mp() : H0 + (double)mu[m];
                         a.vcstar[b] = cs;
                     }
                 }
-                ev[m] = e;
-                eacc += e;
             }
-            int et = 0;
+            // the normaliser follows the round's last step
+            const int ml = min(M - 1, t1 - rs - 1);
+            float me = mu[0];
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                const int p = rs + 1 + m;
-                if (p > t1) break;
-                et += ev[m];
-                *(cact ? nsh + ((r & 1) * M + m) * CP + cl : dummy + tid) = Rh[DIRECT + m];
-                if (Q[m] > NEG_HALF) Mref = Q[m];
-            }
-            H = H0 + (double)et;
+            for (int m = 1; m < M; ++m)
+                if (m == ml) me = mu[m];
+            H = H0 + (me > NEG_HALF ? (double)floorf(me) : 0.0);
             BH = Bc - H;
+            st4_mp(R + (cact ? cl : C) * P + slot_mp(r, RMASK),
+                   make_float4(Rh[M], Rh[M + 1], Rh[M + 2], Rh[M + 3]));
 #pragma unroll
-            for (int i = 0; i < DIRECT; ++i) Rh[i] = Rh[i + M];
+            for (int m = 0; m < M; ++m)
+                if (rs + 1 + m <= t1 && Q[m] > NEG_HALF) Mref = Q[m];
+#pragma unroll
+            for (int i = 0; i < M; ++i) Rh[i] = Rh[i + M];
         } else {
             if (rs + 1 == tc && tc + CH <= t1) {
-                double* dst = Sbuf + ((nch + 1) & 1) * rowsN;
+                double* dst = Sbuf + ((nch + 1) & 1) * chunkN;
 #pragma unroll
                 for (int i = 0; i < PF; ++i) {
                     const int q = bt + i * NB;
-                    if (q < rowsN) dst[q] = pf[i];
+                    if (q < chunkN) {
+                        const int row = q / C, l = q - row * C;
+                        dst[l * CH + row] = pf[i];
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < PF; ++i) {
                     const int q = bt + i * NB;
-                    if (q < rowsN) pf[i] = (tc + 2 * CH + q / C <= t1) ? Sb[(size_t)(tc + 2 * CH) * C + q] : 0.0;
+                    if (q < chunkN) {
+                        const int rr = q / C, l = q - rr * C;
+                        const int tt = tc + 2 * CH + rr;
+                        pf[i] = (tt <= t1) ? Sb[(size_t)tt * C + l] : 0.0;
+                    }
                 }
             }
-            // the chain rebased last round: move the live entries (positions rs-K-M+2 .. rs)
+            // the chain rebased last round: move the blocks of rounds <= r-2 (reads first)
             if (r >= 3 && (r & 1) == 1) {
+                constexpr int BR = BPL + 1;
                 const float dl = bact ? dlsh[cb] : 0.0f;
-                constexpr int KR = KPL + 1;
-                float v[KR];
+                float4 v[BR];
 #pragma unroll
-                for (int i = 0; i < KR; ++i) v[i] = Rrow[(rs - j - i * G) & RMASK];
+                for (int i = 0; i < BR; ++i) v[i] = ld4_mp(Rrow + slot_mp(r - 2 - j - i * G, RMASK));
 #pragma unroll
-                for (int i = 0; i < KR; ++i) {
-                    // slots outside the live window go to the spare row (read by idle lanes)
+                for (int i = 0; i < BR; ++i) {
                     const int q = j + i * G;
-                    const bool live = (q < K + M) & (rs - q >= 0);
-                    ring_put<MIR>(live ? Rrow : R + C * P, rs - q, RS, v[i] - dl);
+                    const int rho = r - 2 - q;
+                    // blocks outside the live window go to the spare row (read by idle lanes)
+                    const bool live = (q < NR) & (t0 + M * rho + M >= 0);
+                    float4 rv = v[i];
+                    rv.x -= dl;
+                    rv.y -= dl;
+                    rv.z -= dl;
+                    rv.w -= dl;
+                    st4_mp((live ? Rrow : R + C * P) + slot_mp(rho, RMASK), rv);
                 }
             }
-            // insert the chain's entries of round r-1
-            if (r >= 1 && bact && j < M && rs - M + 1 + j <= t1)
-                ring_put<MIR>(Rrow, rs - M + 1 + j, RS, nsh[(((r - 1) & 1) * M + j) * CP + cb]);
-            bulk_round(r + 1, rs + M + 1);
+            bulk_round(r + 1);
         }
         __syncthreads();
     }
 }
 
 // ------------------------------------------------------------------ launch
-template <int G, int KPL, bool MIR>
+template <int G, int BPL, int CP>
 static hipError_t launch_maxplus_round_inst(const SweepArgs& a, const SweepCfg& cfg,
                                             hipStream_t stream) {
-    if (cfg.NT > 320 || cfg.vit.CH > lse_chunk_max(G) || cfg.vit.CH % ROUND != 0)
+    if (cfg.NT > 320 || cfg.vit.CH > lse_chunk_max(G) || cfg.vit.CH % ROUND != 0 ||
+        cfg.vit.P % 4 != 0 || cfg.RS % ROUND != 0)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_maxplus_round<G, KPL, MIR>), dim3(a.B), dim3(cfg.NT), cfg.vit.bytes,
+    hipLaunchKernelGGL((k_maxplus_round<G, BPL, CP>), dim3(a.B), dim3(cfg.NT), cfg.vit.bytes,
                        stream, a, cfg.RS, cfg.vit.P, cfg.vit.CH);
     return hipGetLastError();
 }
 
-#define MAXPLUS_ROUND_KPL_CASES(G)                                               \
-    switch (cfg.KPLr) {                                                          \
-        case 0: return launch_maxplus_round_inst<G, 0, MIR>(a, cfg, stream);        \
-        case 1: return launch_maxplus_round_inst<G, 1, MIR>(a, cfg, stream);        \
-        case 2: return launch_maxplus_round_inst<G, 2, MIR>(a, cfg, stream);        \
-        case 3: return launch_maxplus_round_inst<G, 3, MIR>(a, cfg, stream);        \
-        case 4: return launch_maxplus_round_inst<G, 4, MIR>(a, cfg, stream);        \
-        case 5: return launch_maxplus_round_inst<G, 5, MIR>(a, cfg, stream);        \
-        case 6: return launch_maxplus_round_inst<G, 6, MIR>(a, cfg, stream);        \
-        case 7: return launch_maxplus_round_inst<G, 7, MIR>(a, cfg, stream);        \
-        case 8: return launch_maxplus_round_inst<G, 8, MIR>(a, cfg, stream);        \
-        case 10: return launch_maxplus_round_inst<G, 10, MIR>(a, cfg, stream);      \
-        case 12: return launch_maxplus_round_inst<G, 12, MIR>(a, cfg, stream);      \
-        case 16: return launch_maxplus_round_inst<G, 16, MIR>(a, cfg, stream);      \
-        case 24: return launch_maxplus_round_inst<G, 24, MIR>(a, cfg, stream);      \
-        case 32: return launch_maxplus_round_inst<G, 32, MIR>(a, cfg, stream);      \
-        default: return hipErrorInvalidValue;                                    \
+#define MAXPLUS_ROUND_BPL_CASES(G, CP)                                         \
+    switch (cfg.BPL) {                                                         \
+        case 0: return launch_maxplus_round_inst<G, 0, CP>(a, cfg, stream);       \
+        case 1: return launch_maxplus_round_inst<G, 1, CP>(a, cfg, stream);       \
+        case 2: return launch_maxplus_round_inst<G, 2, CP>(a, cfg, stream);       \
+        case 3: return launch_maxplus_round_inst<G, 3, CP>(a, cfg, stream);       \
+        case 4: return launch_maxplus_round_inst<G, 4, CP>(a, cfg, stream);       \
+        case 5: return launch_maxplus_round_inst<G, 5, CP>(a, cfg, stream);       \
+        case 6: return launch_maxplus_round_inst<G, 6, CP>(a, cfg, stream);       \
+        case 7: return launch_maxplus_round_inst<G, 7, CP>(a, cfg, stream);       \
+        case 8: return launch_maxplus_round_inst<G, 8, CP>(a, cfg, stream);       \
+        default: return hipErrorInvalidValue;                                  \
     }
 
-template <bool MIR>
-hipError_t launch_maxplus_round_layout(const SweepCfg& cfg, const SweepArgs& a,
+inline hipError_t launch_maxplus_round(const SweepCfg& cfg, const SweepArgs& a,
                                        hipStream_t stream) {
-    if (cfg.G == 64) { MAXPLUS_ROUND_KPL_CASES(64) }
-    if (cfg.G == 32) { MAXPLUS_ROUND_KPL_CASES(32) }
-    if (cfg.G == 16) { MAXPLUS_ROUND_KPL_CASES(16) }
+    if (cfg.G == 64 && cfg.CPr == 4) { MAXPLUS_ROUND_BPL_CASES(64, 4) }
+    if (cfg.G == 32 && cfg.CPr == 6) { MAXPLUS_ROUND_BPL_CASES(32, 6) }
+    if (cfg.G == 32 && cfg.CPr == 8) { MAXPLUS_ROUND_BPL_CASES(32, 8) }
+    if (cfg.G == 16 && cfg.CPr == 12) { MAXPLUS_ROUND_BPL_CASES(16, 12) }
+    if (cfg.G == 16 && cfg.CPr == 16) { MAXPLUS_ROUND_BPL_CASES(16, 16) }
     return hipErrorInvalidValue;
 }
 
-#undef MAXPLUS_ROUND_KPL_CASES
+#undef MAXPLUS_ROUND_BPL_CASES
 
 }  // namespace semicrf
