@@ -30,14 +30,54 @@
 
 namespace semicrf {
 
-// out[i] = v of lane i of this lane's 16-lane row, i < N (DPP row_newbcast, gfx90a+)
+// out[i] = v of lane i of this lane's 16-lane row, i < N (DPP row_newbcast, gfx90a+; every
+// lane has a source, so the bound control only lets the move fold into its consumer)
 template <int N, int I = 0>
 __device__ __forceinline__ void row_bcast_all(float v, float* out) {
     if constexpr (I < N) {
         out[I] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                                       0x150 + I, 0xF, 0xF, false));
+                                                                       0x150 + I, 0xF, 0xF, true));
         row_bcast_all<N, I + 1>(v, out);
     }
+}
+
+// Sums of four values over an aligned group of G >= 16 lanes, transposed: lane j ends with
+// the group sum of acc[sum_step(j)].  Two exchange steps leave one value per lane, then
+// the lanes of equal j & 3 are added (row rotations, then the swaps across rows).
+__device__ __forceinline__ int sum_step(int j) { return 2 * (j & 1) + ((j >> 1) & 1); }
+template <int G>
+__device__ __forceinline__ float group_sum4(const float* acc, int j) {
+    static_assert(G >= 16 && G <= 64, "group size");
+    const bool o1 = j & 1, o2 = j & 2;
+    const float s0 = o1 ? acc[0] : acc[2], s1 = o1 ? acc[1] : acc[3];
+    const float k0 = o1 ? acc[2] : acc[0], k1 = o1 ? acc[3] : acc[1];
+    const float n0 = k0 + dpp_f<DPP_QUAD_1032>(s0), n1 = k1 + dpp_f<DPP_QUAD_1032>(s1);
+    float v = (o2 ? n1 : n0) + dpp_f<DPP_QUAD_2301>(o2 ? n0 : n1);
+    v += dpp_f<0x128>(v);                                  // row_ror:8
+    v += dpp_f<0x124>(v);                                  // row_ror:4
+    if constexpr (G >= 32) {
+        const int iv = __builtin_bit_cast(int, v);
+        auto p = __builtin_amdgcn_permlane16_swap(iv, iv, false, false);
+        v = __builtin_bit_cast(float, (int)p[0]) + __builtin_bit_cast(float, (int)p[1]);
+    }
+    if constexpr (G >= 64) {
+        const int iv = __builtin_bit_cast(int, v);
+        auto p = __builtin_amdgcn_permlane32_swap(iv, iv, false, false);
+        v = __builtin_bit_cast(float, (int)p[0]) + __builtin_bit_cast(float, (int)p[1]);
+    }
+    return v;
+}
+
+// 0 if every value is in [2^-60, 2^60] (positive, finite), else 1
+template <int N>
+__device__ __forceinline__ bool any_out_of_lin_range(const float* x) {
+    uint32_t lo = __float_as_uint(x[0]), hi = lo;
+#pragma unroll
+    for (int i = 1; i < N; ++i) {
+        lo = min(lo, __float_as_uint(x[i]));
+        hi = max(hi, __float_as_uint(x[i]));
+    }
+    return (lo < 0x21800000u) | (hi > 0x5d800000u);       // 2^-60, 2^60 (sign bit: huge)
 }
 
 // first ring slot of round rho's block
@@ -173,12 +213,8 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
 
     // bulk sums of round rr (positions p0 .. p0+M-1): ring blocks of rounds <= rr-2
     auto bulk_round = [&](int rr, int p0) {
-        float ql[M], qg[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            ql[m] = 0.0f;
-            qg[m] = NEG;
-        }
+        const int mj = sum_step(j);                        // the step this lane publishes
+        float ql = 0.0f, qg = NEG;
         if constexpr (BPL > 0) {
             bool ok = LIN;
             if constexpr (LIN) {
@@ -197,13 +233,9 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
 #pragma unroll
                         for (int d = 0; d < M; ++d) acc[m] = fmaf(at4(v[i], d), Dc[i][m - d + 3], acc[m]);
                 }
-#pragma unroll
-                for (int m = 0; m < M; ++m) ql[m] = group_reduce<G>(acc[m], OpSum());
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    qg[m] = fast_log2(ql[m]) + dmax_b;
-                    ok &= in_lin_range(ql[m]) | !bact | (p0 + m > t1);
-                }
+                ql = group_sum4<G>(acc, j);
+                qg = fast_log2(ql) + dmax_b;
+                ok = in_lin_range(ql) | !bact | (p0 + mj > t1);
             }
             if (wave_any(!ok)) {
                 // exact log-space sums (durations from global memory: a rare path)
@@ -224,17 +256,17 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                             dd[i * M + d] = bact ? durv(cb, M * (2 + j + i * G) + m - d) : NEG;
                         }
                     const float lg = group_lse<G, BPL * M>(x, dd);
-                    if (!LIN || !(in_lin_range(ql[m]) || !bact)) {
-                        qg[m] = lg;
-                        ql[m] = exp2_or_zero(lg - dmax_b);
+                    if (m == mj && (!LIN || !(in_lin_range(ql) || !bact))) {
+                        qg = lg;
+                        ql = exp2_or_zero(lg - dmax_b);
                     }
                 }
             }
         }
-        const bool wr = bact && j == 0;
-        float* slot = qsh + ((rr & 1) * CP + cb) * 2 * M;
-        st4(wr ? slot : sink, make_float4(ql[0], ql[1], ql[2], ql[3]));
-        st4(wr ? slot + M : sink, make_float4(qg[0], qg[1], qg[2], qg[3]));
+        const bool wr = bact && j < M;
+        float* slot = qsh + ((rr & 1) * CP + cb) * 2 * M + mj;
+        *(wr ? slot : sink + (tid & 7)) = ql;
+        *(wr ? slot + M : sink + (tid & 7)) = qg;
     };
 
     // ---------------------------------------------------------------- state after trans(t0)
@@ -322,12 +354,9 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
     // rings, the rings of the checkpoints the chain took in round r-1
     int next_ckb = ckpt ? a.delta : INT_MAX;   // next checkpoint whose ring is to copy
     auto ring_round = [&](int r, int rs) {
-        if (r >= 1 && bact && j == 0) {
-            const float* ns = nsh + (((r - 1) & 1) * (CP + 1) + cb) * 2 * M;
-            const float4 s4 = ld4(ns), f4 = ld4(ns + M);
-            st4(Rrow + round_slot(r - 1, RMASK),
-                make_float4(fmaxf(fast_log2(s4.x) + f4.x, NEG), fmaxf(fast_log2(s4.y) + f4.y, NEG),
-                            fmaxf(fast_log2(s4.z) + f4.z, NEG), fmaxf(fast_log2(s4.w) + f4.w, NEG)));
+        if (r >= 1 && bact && j < M) {
+            const float* ns = nsh + (((r - 1) & 1) * (CP + 1) + cb) * 2 * M + j;
+            Rrow[round_slot(r - 1, RMASK) + j] = fmaxf(fast_log2(ns[0]) + ns[M], NEG);
         }
         // the chain rebased last round: move the blocks of rounds <= r-2 (reads first)
         if (r >= 3 && (r & 1) == 1) {
@@ -430,13 +459,13 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
                     hb[m] = (float)(sv4[m] + BH);            // S(p_m) + B_c - H0
-                    yv[m] = fast_exp2(hb[m] + dmax);         // message scale
+                    yv[m] = cact ? fast_exp2(hb[m] + dmax) : 0.0f;   // message scale
                     fo[m] = tmax - hb[m];
                     fb[m] = fast_exp2(fo[m]);                // ring-entry scale
                 }
             }
             // ---- fast pass (linear space, no branches)
-            bool ok = true;
+            float chk[3 * M];          // values the linear pass relies on
             float sig[M];              // combined message sum (linear) or its log2 (replay)
             float qv[M];               // message total of each step (log2 in a replay)
             // terms k = 2 .. m+4 of step m are formed ahead of its transition step, so only
@@ -446,10 +475,9 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
             for (int k = M; k >= 2; --k) part = fmaf(Eh[M - k], Dl[k - 1], part);
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                const int p = rs + 1 + m;
                 const float sg = fmaf(Eh[M - 1 + m], Dl[0], part);
                 sig[m] = sg;
-                const float pn = cact ? sg * yv[m] : 0.0f;
+                const float pn = sg * yv[m];
                 if (m + 1 < M) {
                     float nx = QL[m + 1];
 #pragma unroll
@@ -471,14 +499,19 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                     }
                 const float s = sv[0], q = qa[0];
                 // label lanes only: lanes outside row 0 broadcast their own (empty) row
-                ok &= (p > t1) | !cact | (in_lin_range(sg) & in_lin_range(s) & in_lin_range(q));
+                chk[3 * m] = sg;
+                chk[3 * m + 1] = s;
+                chk[3 * m + 2] = q;
                 Eh[M + m] = s * fb[m];
                 sH[M + m] = s;
                 fH[M + m] = fo[m];
                 qv[m] = q;
             }
+            // label lanes only (lanes outside row 0 broadcast their own, empty row); a
+            // round past the sweep end may replay for nothing
+            const uint64_t lanes = (C >= 64) ? ~0ull : ((1ull << C) - 1);
             bool replayed = false;
-            if (wave_any(!ok)) {
+            if (__builtin_amdgcn_ballot_w64(any_out_of_lin_range<3 * M>(chk)) & lanes) {
                 // ---- exact replay of the round in log space
                 replayed = true;
                 float Rl[2 * M];
@@ -513,16 +546,18 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                 }
             }
             {
-                // log Z when the round holds L; the normaliser follows the round's last step
-                const int mL = L - rs - 1;
-                const int ml = min(M - 1, t1 - rs - 1);
-                float ql = qv[0], qe = qv[0];
+                // the normaliser follows the round's last step; log Z when the round holds L
+                float qe = qv[M - 1];
+                if (rs + M >= t1) {
+                    const int mL = L - rs - 1, ml = t1 - rs - 1;
+                    float ql = qv[0];
 #pragma unroll
-                for (int m = 1; m < M; ++m) {
-                    if (m == mL) ql = qv[m];
-                    if (m == ml) qe = qv[m];
+                    for (int m = 1; m < M; ++m) {
+                        if (m == mL) ql = qv[m];
+                        if (m == ml) qe = qv[m];
+                    }
+                    if (mL >= 0 && mL < M) lz = H0 + (double)(replayed ? ql : fast_log2(ql));
                 }
-                if (mL >= 0 && mL < M) lz = H0 + (double)(replayed ? ql : fast_log2(ql));
                 int e;
                 if (replayed) e = qe > NEG_HALF ? (int)floorf(qe) + 1 : 0;
                 else e = __builtin_amdgcn_frexp_expf(qe);
@@ -538,33 +573,46 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                 st4(ns, make_float4(sH[M], sH[M + 1], sH[M + 2], sH[M + 3]));
                 st4(ns + M, make_float4(fH[M], fH[M + 1], fH[M + 2], fH[M + 3]));
             }
+            if (a.write_xa) {
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const int p = rs + 1 + m;
+                    if (p <= t1 && cact) {
+                        const double Sp = Sch[cl * CH + row0 + m];
+                        const float sgl = replayed ? sig[m] : fast_log2(sig[m]) + dmax;
+                        Xout[(outrow + (dir == 0 ? p : L - p)) * C + cl] = (Sp + Bc + (double)sgl) * LN2;
+                        if (p < t1) {
+                            const float rl = replayed ? fH[M + m] : fast_log2(sH[M + m]) + fH[M + m];
+                            Aout[(outrow + (dir == 0 ? p : L - p)) * C + cl] = (Bc + (double)rl) * LN2;
+                        }
+                    }
+                }
+            }
+            if (next_ck <= rs + M) {
+                // chain half of a checkpoint after the transition step of p; the ring half
+                // is copied by the bulk lanes next round
+                float mr = Mref;
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const int p = rs + 1 + m;
+                    if (p <= t1 && QG[m] > NEG_HALF) mr = QG[m];
+                    if (p == next_ck) {
+                        if (p < L) {
+                            const size_t ck = ckrow + p / a.delta;
+                            if (cact) {
+                                a.ck_base[ck * C + cl] = Bc;
+                                a.ck_mprev[ck * C + cl] = mr;
+                            }
+                            if (tid == 0) a.ck_href[ck] = H0;
+                        }
+                        next_ck += a.delta;
+                    }
+                }
+            }
 #pragma unroll
             for (int m = 0; m < M; ++m) {
-                const int p = rs + 1 + m;
-                if (p > t1) break;
-                if (a.write_xa && cact) {
-                    const double Sp = Sch[cl * CH + row0 + m];
-                    const float sgl = replayed ? sig[m] : fast_log2(sig[m]) + dmax;
-                    Xout[(outrow + (dir == 0 ? p : L - p)) * C + cl] = (Sp + Bc + (double)sgl) * LN2;
-                    if (p < t1) {
-                        const float rl = replayed ? fH[M + m] : fast_log2(sH[M + m]) + fH[M + m];
-                        Aout[(outrow + (dir == 0 ? p : L - p)) * C + cl] = (Bc + (double)rl) * LN2;
-                    }
-                }
-                if (QG[m] > NEG_HALF) Mref = QG[m];
-                if (p == next_ck) {
-                    // chain half of the checkpoint after the transition step of p; the ring
-                    // half is copied by the bulk lanes next round
-                    if (p < L) {
-                        const size_t ck = ckrow + p / a.delta;
-                        if (cact) {
-                            a.ck_base[ck * C + cl] = Bc;
-                            a.ck_mprev[ck * C + cl] = Mref;
-                        }
-                        if (tid == 0) a.ck_href[ck] = H0;
-                    }
-                    next_ck += a.delta;
-                }
+                const bool use = (rs + 1 + m <= t1) & (QG[m] > NEG_HALF);
+                Mref = use ? QG[m] : Mref;
             }
 #pragma unroll
             for (int i = 0; i < M; ++i) {   // history for the next round

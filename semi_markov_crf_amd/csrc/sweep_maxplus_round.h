@@ -24,12 +24,13 @@ namespace semicrf {
 
 namespace {
 
-// out[i] = v of lane i of this lane's 16-lane row, i < N (DPP row_newbcast, gfx90a+)
+// out[i] = v of lane i of this lane's 16-lane row, i < N (DPP row_newbcast, gfx90a+; every
+// lane has a source, so the bound control only lets the move fold into its consumer)
 template <int N, int I = 0>
 __device__ __forceinline__ void row_bcast_all_mp(float v, float* out) {
     if constexpr (I < N) {
         out[I] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                                       0x150 + I, 0xF, 0xF, false));
+                                                                       0x150 + I, 0xF, 0xF, true));
         row_bcast_all_mp<N, I + 1>(v, out);
     }
 }
