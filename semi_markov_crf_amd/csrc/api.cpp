@@ -21,7 +21,7 @@ struct Layout {
     size_t logz = 0, logzb = 0;
     size_t ckR = 0, ckB = 0, ckM = 0, ckH = 0, XF = 0, AF = 0, XB = 0, AB = 0;
     size_t Dn = 0, dnt = 0, dno = 0, mu = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0;
-    size_t bp = 0, vscore = 0, vcstar = 0, btr = 0, bent = 0;
+    size_t bp = 0, vscore = 0, vcstar = 0, vwin = 0, split = 0, btr = 0, bent = 0;
     size_t total = 0;
 };
 
@@ -98,12 +98,14 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         lo.total = lo.S;
         return true;
     } else if (op == SEMICRF_OP_VITERBI) {
-        lo.bp = m.take(sizeof(uint32_t) * BT1C);
+        lo.bp = m.take(sizeof(uint32_t) * 2 * BT1C);
         lo.vscore = m.take(sizeof(double) * B);
         lo.vcstar = m.take(sizeof(int) * B);
+        lo.vwin = m.take(sizeof(double) * 2 * B * K * C);
+        lo.split = m.take(sizeof(int) * 4 * B);
         const size_t nch = (size_t)backtrace_chunks(T, C, K);
-        lo.btr = m.take(sizeof(int32_t) * B * nch * K * C);
-        lo.bent = m.take(sizeof(int32_t) * B * nch);
+        lo.btr = m.take(sizeof(int32_t) * 2 * B * nch * K * C);
+        lo.bent = m.take(sizeof(int32_t) * 2 * B * nch);
     } else {
         return false;
     }
@@ -320,11 +322,14 @@ static int run_viterbi(const float* em, const int32_t* lengths, const float* tra
     a.bp = at<uint32_t>(workspace, lo.bp);
     a.vscore = at<double>(workspace, lo.vscore);
     a.vcstar = at<int>(workspace, lo.vcstar);
+    a.vwin = at<double>(workspace, lo.vwin);
     LAUNCH(launch_maxplus(cfg, a, stream));
     STAGE(2);
-    LAUNCH(launch_backtrace(a.bp, a.vscore, a.vcstar, a.Leff, B, T, C, K,
-                            at<int32_t>(workspace, lo.btr), at<int32_t>(workspace, lo.bent),
-                            best_score, labels, seg_start, stream));
+    int* split = at<int>(workspace, lo.split);
+    LAUNCH(launch_vit_combine(a.vwin, trans, a.Leff, B, C, K, cfg.split, a.vscore, a.vcstar,
+                              split, best_score, stream));
+    LAUNCH(launch_backtrace(a.bp, split, B, T, C, K, at<int32_t>(workspace, lo.btr),
+                            at<int32_t>(workspace, lo.bent), labels, seg_start, stream));
     STAGE(3);
     return SEMICRF_OK;
 }

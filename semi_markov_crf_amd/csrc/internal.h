@@ -69,12 +69,13 @@ inline size_t lse_round_lds_bytes(int C, int CP, int P, int CH, bool lin) {
            (size_t)((lin ? 2 : 1) * (C + 1) * P + 4 * CP * ROUND + 4 * (CP + 1) * ROUND +
                     2 * cp4 + 16) * 4;
 }
-// Dynamic LDS of the max-plus round kernel (C <= 16): S chunks [2][C][CH] (fp64), the
+// Dynamic LDS of the max-plus round kernel (C <= 16): S chunks [2][C][CH] and S(L) (fp64), the
 // ring [C+1][P], bulk maxima and their k [2][CP][2][ROUND], rebase shifts [CP rounded to
 // 4], a sink and a constant block [12] (fp32).
 inline size_t maxplus_round_lds_bytes(int C, int CP, int P, int CH) {
     const int cp4 = (CP + 3) / 4 * 4;
-    return (size_t)(2 * CH * C) * 8 + (size_t)((C + 1) * P + 4 * CP * ROUND + cp4 + 12) * 4;
+    return (size_t)(2 * CH * C + (C + 1) / 2 * 2) * 8 +
+           (size_t)((C + 1) * P + 4 * CP * ROUND + cp4 + 12) * 4;
 }
 // Dynamic LDS of the max-plus sweep: S chunks [2][CH][C] (fp64), R ring [C+1][P] and
 // u [2][UP] (fp32).
@@ -108,9 +109,10 @@ struct SweepArgs {
     double* logz;           // [B] forward log Z
     double* logz_b;         // [B] log Z from the backward sweep (consistency check)
     // Viterbi
-    uint32_t* bp;           // [B][T+1][C]: (k) | (previous label << 16)
-    double* vscore;         // [B]
-    int* vcstar;            // [B] final label
+    uint32_t* bp;           // [2 dirs][B][T+1][C]: (k) | (previous label << 16)
+    double* vscore;         // [B] (one-direction sweep)
+    int* vcstar;            // [B] final label (one-direction sweep)
+    double* vwin;           // [2 dirs][B][K][C] values over the meeting window (round kernel)
 };
 
 // log-semiring sweep: grid (B, ndir) in MODE_FULL, (nspans, B, ndir) in MODE_SPAN;
@@ -175,10 +177,16 @@ hipError_t launch_write_logz(const double* logz, int B, float* out, hipStream_t 
 // chunk length and chunk count of the parallel backtrace
 int backtrace_chunk(int C, int K);
 int backtrace_chunks(int T, int C, int K);
-// tr: [B][nch][K*C] and ent: [B][nch] int32 scratch
-hipError_t launch_backtrace(const uint32_t* bp, const double* vscore, const int* vcstar,
-                            const int* Leff, int B, int T, int C, int K, int32_t* tr,
-                            int32_t* ent, float* best_score, int32_t* labels,
-                            uint8_t* seg_start, hipStream_t stream);
+// split[b] = {t*, c_left, c_right, L}: the best segmentation's boundary in the meeting
+// window of the two-direction sweep (bidir), or t* = L and the one-direction sweep's final
+// label; best_score[b] its score (NaN for an invalid length)
+hipError_t launch_vit_combine(const double* vwin, const float* trans, const int* Leff, int B,
+                              int C, int K, bool bidir, const double* vscore, const int* vcstar,
+                              int* split, float* best_score, hipStream_t stream);
+// bp: [2][B][T+1][C] (part 1: the mirrored sequence); tr: [2][B][nch][K*C] and ent:
+// [2][B][nch] int32 scratch
+hipError_t launch_backtrace(const uint32_t* bp, const int* split, int B, int T, int C, int K,
+                            int32_t* tr, int32_t* ent, int32_t* labels, uint8_t* seg_start,
+                            hipStream_t stream);
 
 }  // namespace semicrf

@@ -15,6 +15,13 @@
 //    S, label-major.
 // Values are natural-log scores relative to a per-label fp64 base (moved every second
 // round) and a common fp64 reference H that advances by whole units once per round.
+//
+// The two directions meet in the middle: direction 0 runs forward over [0, mm], direction
+// 1 runs the same recurrence on the mirrored sequence (S'(t) = S(L) - S(L - t), trans
+// transposed) over original positions [lo, L], lo = max(0, mm - K + 1).  Every
+// segmentation has a segment boundary in [lo, mm], so the best one is the best of
+// V(t, c) + trans[c][c'] + W(t, c') over that window, V the forward and W the backward
+// value; both are written for the window in fp64 and combined afterwards.
 #pragma once
 
 #include "internal.h"
@@ -35,7 +42,6 @@ __device__ __forceinline__ void row_bcast_all_mp(float v, float* out) {
     }
 }
 
-__device__ __forceinline__ double nan_mp() { return __longlong_as_double(0x7ff8000000000000LL); }
 __device__ __forceinline__ int slot_mp(int rho, int RMASK) { return (rho * ROUND) & RMASK; }
 __device__ __forceinline__ float4 ld4_mp(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ __forceinline__ void st4_mp(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
@@ -61,10 +67,28 @@ __device__ __forceinline__ float max_tree(const float* x) {
     }
 }
 
+// min of n values (tree of v_min3)
+template <int N>
+__device__ __forceinline__ int min_tree_i(const int* x) {
+    if constexpr (N == 1) return x[0];
+    else if constexpr (N == 2) return min(x[0], x[1]);
+    else {
+        int y[(N + 2) / 3];
+#pragma unroll
+        for (int i = 0; i < (N + 2) / 3; ++i) {
+            const int a0 = x[3 * i];
+            const int a1 = 3 * i + 1 < N ? x[3 * i + 1] : a0;
+            const int a2 = 3 * i + 2 < N ? x[3 * i + 2] : a0;
+            y[i] = min(min(a0, a1), a2);
+        }
+        return min_tree_i<(N + 2) / 3>(y);
+    }
+}
+
 }  // namespace
 
 // G: bulk lanes per label (C <= 256/G); BPL: ring blocks per bulk lane; CP: labels the
-// chain broadcasts (>= C).  Grid (B), block 64 + ceil(C*G/64)*64 threads.
+// chain broadcasts (>= C).  Grid (B, 2 directions), block 64 + ceil(C*G/64)*64 threads.
 template <int G, int BPL, int CP>
 __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const int RS,
                                                       const int P, const int CH) {
@@ -87,17 +111,19 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
     const bool cact = chain && tid < C;
     const int cl = cact ? tid : 0;
 
-    const int b = blockIdx.x;
+    const int b = blockIdx.x, dir = blockIdx.y;
     const int Lr = a.Leff[b];
-    const bool bad = Lr < 0;
-    const int L = bad ? -Lr : Lr;
-    const int t0 = 0, t1 = L;
+    const int L = Lr < 0 ? -Lr : Lr;
+    const int mm = min(L, (L + K - 1) / 2);             // meeting window [lo, mm]
+    const int lo = max(0, mm - K + 1);
+    const int t0 = 0, t1 = dir == 0 ? mm : L - lo;
     const int RMASK = RS - 1;
     const int bmax = (K + M - 1) / M;
     const int NR = bmax + 3;
 
     double* Sbuf = lds;                                    // [2][C][CH] label-major
-    float* R = (float*)(Sbuf + 2 * C * CH);                // [C+1][P]
+    double* SL = Sbuf + 2 * C * CH;                        // [C] (padded to 16 bytes)
+    float* R = (float*)(SL + (C + 1) / 2 * 2);             // [C+1][P]
     float* qsh = R + (C + 1) * P;                          // [2 rounds][CP][max, k][M]
     float* dlsh = qsh + 2 * CP * 2 * M;                    // [CP4] rebase shift per label
     float* sink = dlsh + CP4;                              // [8]
@@ -105,6 +131,7 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
     float* Rrow = R + cr * P;
 
     const double* Sb = a.S + (size_t)b * (T + 1) * C;
+    for (int q = tid; q < C; q += NT) SL[q] = Sb[(size_t)L * C + q];
     for (int q = tid; q < (C + 1) * P; q += NT) R[q] = NEG;
     for (int q = tid; q < 2 * CP * 2 * M; q += NT) qsh[q] = ((q / M) & 1) ? __int_as_float(INT_MAX) : NEG;
     if (tid < M) nblk[tid] = NEG;
@@ -125,8 +152,9 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
     for (int k = 0; k < KD; ++k) dlog[k] = cact ? durv(cl, k + 1) : NEG;
     float treg[CP];
 #pragma unroll
-    for (int i = 0; i < CP; ++i) treg[i] = (cact && i < C) ? fmaxf(a.trans[i * C + cl], NEG) : NEG;
-    __syncthreads();   // ring cleared
+    for (int i = 0; i < CP; ++i)
+        treg[i] = (cact && i < C) ? fmaxf(dir == 0 ? a.trans[i * C + cl] : a.trans[cl * C + i], NEG) : NEG;
+    __syncthreads();   // ring cleared, SL visible
 
     // bulk best (durations k >= m + 5) of the positions of round rr and its lowest k
     auto bulk_round = [&](int rr) {
@@ -181,6 +209,8 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
     float Mref = 0.0f;
 
     const int chunkN = CH * C;
+    auto sidx = [&](int t, int q) -> size_t { return (size_t)(dir == 0 ? t : L - t) * C + q; };
+    auto spub = [&](double raw, int q) -> double { return dir == 0 ? raw : SL[q] - raw; };
     double pf[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) pf[i] = 0.0;
@@ -188,7 +218,7 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
         for (int q = bt; q < chunkN; q += NB) {
             const int row = q / C, l = q - row * C;
             const int t = t0 + 1 + row;
-            Sbuf[l * CH + row] = (t <= t1) ? Sb[(size_t)t * C + l] : 0.0;
+            Sbuf[l * CH + row] = (t <= t1) ? spub(Sb[sidx(t, l)], l) : 0.0;
         }
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
@@ -196,7 +226,7 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
             if (q < chunkN) {
                 const int row = q / C, l = q - row * C;
                 const int t = t0 + 1 + CH + row;
-                if (t <= t1) pf[i] = Sb[(size_t)t * C + l];
+                if (t <= t1) pf[i] = Sb[sidx(t, l)];
             }
         }
     }
@@ -246,15 +276,21 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
                 pend = true;
             }
             const double H0 = H;
-            float hb[M];
+            float hb[M], hbx[M];
             {
                 const double2* sp = reinterpret_cast<const double2*>(Sch + cl * CH + row0);
                 const double2 s01 = sp[0], s23 = sp[1];
                 const double sv4[M] = {s01.x, s01.y, s23.x, s23.y};
 #pragma unroll
-                for (int m = 0; m < M; ++m) hb[m] = (float)(sv4[m] + BH);   // S(p_m) + B_c - H0
+                for (int m = 0; m < M; ++m) {
+                    hb[m] = (float)(sv4[m] + BH);            // S(p_m) + B_c - H0
+                    hbx[m] = cact ? hb[m] : NEG;
+                }
             }
-            float mu[M];
+            // the round's last step inside the sweep sets the normaliser
+            const int ml = min(M - 1, t1 - rs - 1);
+            float me = NEG;
+            uint32_t* bpp = a.bp + (size_t)dir * a.B * (T + 1) * C + (outrow + rs + 1) * C + cl;
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const int p = rs + 1 + m;
@@ -265,43 +301,37 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
                 for (int k = 1; k <= 2 * M; ++k) x[k - 1] = k <= m + M ? Rh[M + m - k] + dlog[k - 1] : NEG;
                 x[2 * M] = Q[m];
                 const float best = max_tree<2 * M + 1>(x);
-                int kbest = kQ[m];
+                // lowest duration attaining it: each direct one gives its k or a sentinel,
+                // a min tree picks; the bulk's otherwise
+                int kd[2 * M];
 #pragma unroll
-                for (int k = 2 * M; k >= 1; --k)
-                    if (k <= m + M && x[k - 1] == best) kbest = k;
-                const float u = cact ? hb[m] + best : NEG;     // V(p, cl) - H0
-                // transition step of p over every label's value
+                for (int k = 1; k <= 2 * M; ++k) kd[k - 1] = (k <= m + M && x[k - 1] == best) ? k : INT_MAX;
+                const int kmin = min_tree_i<2 * M>(kd);
+                const int kbest = kmin != INT_MAX ? kmin : kQ[m];
+                const float u = hbx[m] + best;                 // V(p, cl) - H0
+                // transition step of p over every label's value, lowest c' on ties
                 float uv[CP], y[CP];
                 row_bcast_all_mp<CP>(u, uv);
 #pragma unroll
                 for (int i = 0; i < CP; ++i) y[i] = uv[i] + treg[i];
                 const float mt = max_tree<CP>(y);
-                int cbest = 0;
+                int ci[CP];
 #pragma unroll
-                for (int i = CP - 1; i >= 0; --i)
-                    if (y[i] == mt) cbest = i;
-                mu[m] = max_tree<CP>(uv);
+                for (int i = 0; i < CP; ++i) ci[i] = y[i] == mt ? i : INT_MAX;
+                const int cbest = min_tree_i<CP>(ci);
                 Rh[M + m] = mt - hb[m];
                 if (p <= t1 && cact)   // the label of position L + 1 is never read
-                    a.bp[(outrow + p) * C + cl] = (uint32_t)kbest | ((uint32_t)cbest << 16);
-                if (p == L) {
-                    // final label: lowest argmax of V(L, c)
-                    int cs = 0;
-#pragma unroll
-                    for (int i = CP - 1; i >= 0; --i)
-                        if (uv[i] == mu[m]) cs = i;
-                    if (tid == 0) {
-                        a.vscore[b] = bad ? nan_mp() : H0 + (double)mu[m];
-                        a.vcstar[b] = cs;
-                    }
+                    bpp[m * C] = (uint32_t)kbest | ((uint32_t)cbest << 16);
+                if (m == ml) {
+                    float uw[CP];
+                    row_bcast_all_mp<CP>(u, uw);
+                    me = max_tree<CP>(uw);
                 }
+                // value at an original position of the meeting window
+                const int tw = dir == 0 ? p : L - p;
+                if (p <= t1 && tw >= lo && tw <= mm && cact)
+                    a.vwin[(((size_t)dir * a.B + b) * K + (tw - lo)) * C + cl] = H0 + (double)u;
             }
-            // the normaliser follows the round's last step
-            const int ml = min(M - 1, t1 - rs - 1);
-            float me = mu[0];
-#pragma unroll
-            for (int m = 1; m < M; ++m)
-                if (m == ml) me = mu[m];
             H = H0 + (me > NEG_HALF ? (double)floorf(me) : 0.0);
             BH = Bc - H;
             st4_mp(R + (cact ? cl : C) * P + slot_mp(r, RMASK),
@@ -319,7 +349,7 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
                     const int q = bt + i * NB;
                     if (q < chunkN) {
                         const int row = q / C, l = q - row * C;
-                        dst[l * CH + row] = pf[i];
+                        dst[l * CH + row] = spub(pf[i], l);
                     }
                 }
 #pragma unroll
@@ -328,7 +358,7 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
                     if (q < chunkN) {
                         const int rr = q / C, l = q - rr * C;
                         const int tt = tc + 2 * CH + rr;
-                        pf[i] = (tt <= t1) ? Sb[(size_t)tt * C + l] : 0.0;
+                        pf[i] = (tt <= t1) ? Sb[sidx(tt, l)] : 0.0;
                     }
                 }
             }
@@ -366,7 +396,7 @@ static hipError_t launch_maxplus_round_inst(const SweepArgs& a, const SweepCfg& 
     if (cfg.NT > 320 || cfg.vit.CH > lse_chunk_max(G) || cfg.vit.CH % ROUND != 0 ||
         cfg.vit.P % 4 != 0 || cfg.RS % ROUND != 0)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_maxplus_round<G, BPL, CP>), dim3(a.B), dim3(cfg.NT), cfg.vit.bytes,
+    hipLaunchKernelGGL((k_maxplus_round<G, BPL, CP>), dim3(a.B, 2), dim3(cfg.NT), cfg.vit.bytes,
                        stream, a, cfg.RS, cfg.vit.P, cfg.vit.CH);
     return hipGetLastError();
 }
