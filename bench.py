@@ -14,7 +14,9 @@ The roofline object describes the dominant kernel (the checkpoint sweep pair,
 timed live with events recorded by the library on the stream it launches on):
 algorithmic transcendental operations per launch / its mean duration, against the
 chip's exp2/log2 issue rate (256 CUs x 32 lanes/clock x 2.4 GHz: transcendentals
-issue at half the 64 lanes/clock of plain fp32 ops on gfx950).  The centring +
+issue at half the 64 lanes/clock of plain fp32 ops on gfx950).  Its HBM traffic comes
+from FETCH_SIZE / WRITE_SIZE counter runs calibrated on a plain copy; it is reported
+only while the kernel source is the one those counters were taken on.  The centring +
 prefix scan is also reported against HBM bandwidth on a shape larger than the
 256 MB last-level cache.
 """
@@ -23,6 +25,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import math
 import os
@@ -35,6 +38,12 @@ sys.path.insert(0, ROOT)
 CONFIG = 2                       # genomic: B=4, T=1e5, K=200, C=6
 PEAK_TRANS_PER_S = 256 * 32 * 2.4e9     # exp2/log2 issue: half of 64 lanes/clock per CU
 PEAK_HBM_BPS = 8.0e12
+# HBM bytes per checkpoint-sweep launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per
+# dispatch, scaled by 2.0 / 1.0, what the counters read for a 1 GiB copy), valid for the
+# kernel source with this SHA-256
+SWEEP_SRC = os.path.join(ROOT, "semi_markov_crf_amd", "csrc", "sweep_lse_round.h")
+SWEEP_TRAFFIC = {"sha256": "dc589ac14dc3a2f0b7f7c891b98c37cf15c966996f055b81ac567089d0a60d0e",
+                 "bytes": (19102.75 * 2.0 + 840.0 * 1.0) * 1024}
 
 
 def hip_runtime():
@@ -201,6 +210,12 @@ def main():
     algo = 2 * positions * trans_per_pos           # both directions
     achieved = algo / (dom_ms * 1e-3)
     busy_cus = 2 * B if dom_stage == 1 else min(256, 2 * B * nspans)
+    # algorithmic bytes of the sweep pair: S read once per direction, checkpoints written
+    nck = sum(max(0, (int(L) - 1) // delta) for L in w.lengths)
+    algo_bytes = 2 * B * (T + 1) * C * 8 + 2 * nck * (K * C * 4 + C * 8 + C * 4 + 8)
+    with open(SWEEP_SRC, "rb") as f:
+        same_src = hashlib.sha256(f.read()).hexdigest() == SWEEP_TRAFFIC["sha256"]
+    traffic = SWEEP_TRAFFIC["bytes"] if (same_src and dom_stage == 1 and delta == 4473) else None
 
     out = {
         "metric": "fwd+bwd positions/s at T=1e5,K=200,C=6; % of VALU-exp/HBM roofline",
@@ -221,12 +236,14 @@ def main():
                    "B": B, "T": T, "K": K, "C": C, "delta": delta, "parallelism": "none (1 GPU)"},
         "roofline": {
             "bound": "alu",
-            "kernel": "k_sweep (checkpoint sweeps, forward and backward in one launch)",
+            "kernel": "k_lse_round (checkpoint sweeps: forward and backward of every sequence, "
+                      "one workgroup each, one launch)",
             "achieved": achieved / 1e12,
             "peak": PEAK_TRANS_PER_S / 1e12,
             "unit": "Ttrans/s",
             "frac": achieved / PEAK_TRANS_PER_S,
-            "traffic": None,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": algo_bytes,
             "algorithmic_per_launch": algo,
             "launch_ms": dom_ms,
             "busy_cus": busy_cus,

@@ -119,8 +119,13 @@ int semicrf_backward(const float* emissions, const int32_t* lengths, const float
                      float* grad_dur, float* marginals, float* log_z);
 
 /* Max-plus decode of the best segmentation (the Viterbi counterpart of the forward
- * pass).  Ties go to the shortest final segment, then the lowest previous label,
- * and the lowest label at the end of the sequence.  Outputs:
+ * pass).  Each max-plus step breaks ties toward the shortest segment, then the lowest
+ * previous label.  For C <= 16 the forward sweep and a sweep over the mirrored sequence
+ * meet in the middle and the best boundary of the meeting window joins them (lowest
+ * position, then labels, on ties); for C > 16 one forward sweep ends at the lowest best
+ * final label.  When several segmentations share the best score (to fp32 rounding),
+ * which one is returned is therefore implementation-defined; a best segmentation that
+ * beats every other by more than rounding is returned exactly.  Outputs:
  *   best_score [B]    float32  score of the best segmentation
  *   labels     [B, T] int32    label of every position, -1 at t >= lengths[b]
  *   seg_start  [B, T] uint8    1 where a segment starts, else 0 */
@@ -138,7 +143,7 @@ int semicrf_viterbi(const float* emissions, const int32_t* lengths, const float*
  *   backward: 0 centring + prefix scan, 1 checkpoint sweeps (both directions at once;
  *             empty when delta >= T), 2 span recompute, 3 segment posteriors,
  *             4 node marginals and gradient reductions
- *   viterbi:  0 centring + prefix scan, 1 max-plus sweep, 2 backtrace */
+ *   viterbi:  0 centring + prefix scan, 1 max-plus sweep, 2 combine and backtrace */
 #define SEMICRF_LOGZ_STAGES 2
 #define SEMICRF_BACKWARD_STAGES 5
 #define SEMICRF_VITERBI_STAGES 3
