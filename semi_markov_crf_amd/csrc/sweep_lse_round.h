@@ -114,6 +114,10 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
     const int cr = bact ? cb : C;                 // inactive lanes use the spare ring row C
     const bool cact = chain && tid < C;
     const int cl = cact ? tid : 0;
+    // CP < 16: chain lane 15 is no label; with unit transition weights from every label
+    // its transition sum is the message total q of the step
+    constexpr bool QLANE = CP < 16;
+    const bool qlane = QLANE && chain && tid == 15;
 
     int b, span, dir;
     if (a.mode == MODE_FULL) {
@@ -196,6 +200,8 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
         if (cact && i < C) {
             const float tv = dir == 0 ? a.trans[i * C + cl] : a.trans[cl * C + i];
             v = fmaxf((float)((double)tv * LOG2E), NEG);
+        } else if (qlane && i < C) {
+            v = 0.0f;
         }
         treg[i] = v;
         zero[i] = 0.0f;
@@ -468,6 +474,8 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
             float chk[3 * M];          // values the linear pass relies on
             float sig[M];              // combined message sum (linear) or its log2 (replay)
             float qv[M];               // message total of each step (log2 in a replay)
+#pragma unroll
+            for (int m = 0; m < M; ++m) qv[m] = 0.0f;
             // terms k = 2 .. m+4 of step m are formed ahead of its transition step, so only
             // one FMA waits for the newest ring entry
             float part = QL[0];
@@ -495,21 +503,24 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
 #pragma unroll
                     for (int i = 0; i + w < CP; i += 2 * w) {
                         sv[i] += sv[i + w];
-                        qa[i] += qa[i + w];
+                        if constexpr (!QLANE) qa[i] += qa[i + w];
                     }
-                const float s = sv[0], q = qa[0];
-                // label lanes only: lanes outside row 0 broadcast their own (empty) row
-                chk[3 * m] = sg;
+                const float s = sv[0];
+                chk[3 * m] = cact ? sg : 1.0f;   // the q lane's sg is not a message
                 chk[3 * m + 1] = s;
-                chk[3 * m + 2] = q;
+                if constexpr (QLANE) {
+                    chk[3 * m + 2] = s;
+                } else {
+                    chk[3 * m + 2] = qa[0];
+                    qv[m] = qa[0];
+                }
                 Eh[M + m] = s * fb[m];
                 sH[M + m] = s;
                 fH[M + m] = fo[m];
-                qv[m] = q;
             }
             // label lanes only (lanes outside row 0 broadcast their own, empty row); a
             // round past the sweep end may replay for nothing
-            const uint64_t lanes = (C >= 64) ? ~0ull : ((1ull << C) - 1);
+            const uint64_t lanes = ((1ull << C) - 1) | (QLANE ? (1ull << 15) : 0ull);
             bool replayed = false;
             if (__builtin_amdgcn_ballot_w64(any_out_of_lin_range<3 * M>(chk)) & lanes) {
                 // ---- exact replay of the round in log space
@@ -543,6 +554,14 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                     sH[M + m] = 1.0f;
                     fH[M + m] = rn;
                     qv[m] = lq;
+                }
+            }
+            if constexpr (QLANE) {
+                if (!replayed) {   // message totals: the q lane's transition sums
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        qv[m] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                    0, __builtin_bit_cast(int, sH[M + m]), 0x15F, 0xF, 0xF, true));
                 }
             }
             {
