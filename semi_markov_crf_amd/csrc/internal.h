@@ -60,14 +60,14 @@ inline size_t lse_lds_bytes(int C, int NT, int UP, int P, int CH, bool lin) {
 // The round kernels (C <= 16): ROUND positions per workgroup barrier.
 constexpr int ROUND = 4;
 // Dynamic LDS of the log-semiring round kernel: S chunks [2][C][CH] and S(L) (fp64), the
-// rings [C+1][P] (two when linear), bulk sums [2][CP][2][ROUND], staged ring entries
-// [2][CP+1][2][ROUND], rebase shifts and dmax [CP rounded to 4], a sink and two constant
-// blocks [16] (fp32).
+// chunks' per-position factors [2][3][C][CH], the rings [C+1][P] (two when linear), bulk
+// sums [2][CP][2][ROUND], staged ring entries [2][CP+1][2][ROUND], rebase shifts and dmax
+// [CP rounded to 4], a sink and two constant blocks [16] (fp32).
 inline size_t lse_round_lds_bytes(int C, int CP, int P, int CH, bool lin) {
     const int cp4 = (CP + 3) / 4 * 4;
     return (size_t)(2 * CH * C + (C + 1) / 2 * 2) * 8 +
-           (size_t)((lin ? 2 : 1) * (C + 1) * P + 4 * CP * ROUND + 4 * (CP + 1) * ROUND +
-                    2 * cp4 + 16) * 4;
+           (size_t)(6 * C * CH + (lin ? 2 : 1) * (C + 1) * P + 4 * CP * ROUND +
+                    4 * (CP + 1) * ROUND + 2 * cp4 + 16) * 4;
 }
 // Dynamic LDS of the max-plus round kernel (C <= 16): S chunks [2][C][CH] and S(L) (fp64), the
 // ring [C+1][P], bulk maxima and their k [2][CP][2][ROUND], rebase shifts [CP rounded to

@@ -98,13 +98,12 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
     constexpr int M = ROUND;
     static_assert(M == 4, "ring blocks are float4");
     static_assert(CP <= 16 && CP * G <= 256, "the labels of the chain wavefront share one DPP row");
-    constexpr int PF = (lse_chunk_max(G) + G - 1) / G;        // prefetched doubles per bulk lane
     constexpr int BP = BPL > 0 ? BPL : 1;
     constexpr int KD = 2 * M - 1;                              // chain durations, last step
     constexpr int CP4 = (CP + 3) / 4 * 4;
     extern __shared__ double lds[];
     const int C = a.C, K = a.K, T = a.T;
-    const int tid = threadIdx.x, NT = blockDim.x, NB = NT - 64;
+    const int tid = threadIdx.x, NT = blockDim.x;
     // the role is a property of the wavefront: a wave-uniform value, scalar branches
     const bool chain = __builtin_amdgcn_readfirstlane(tid >> 6) == 0;
     const int bt = tid - 64;
@@ -141,7 +140,10 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
 
     double* Sbuf = lds;                                    // [2][C][CH] label-major
     double* SL = Sbuf + 2 * C * CH;                        // [C] (padded to 16 bytes)
-    float* R = (float*)(SL + (C + 1) / 2 * 2);             // [C+1][P] log ring
+    // per position of a staged chunk, relative to the first position p0 of its round:
+    // 2^(S(p) - S(p0)), its inverse, S(p) - S(p0)  [2][3][C][CH]
+    float* Fst = (float*)(SL + (C + 1) / 2 * 2);
+    float* R = Fst + 6 * C * CH;                           // [C+1][P] log ring
     float* E = R + (C + 1) * P;                            // [C+1][P] linear ring
     float* qsh = E + (LIN ? (C + 1) * P : 0);              // [2 rounds][CP][lin, log][M]
     float* nsh = qsh + 2 * CP * 2 * M;                     // [2 rounds][CP+1][s, offset][M]
@@ -329,24 +331,38 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
     auto spub = [&](double raw, int q) -> double {
         return dir == 0 ? raw * LOG2E : (SL[q] - raw) * LOG2E;
     };
-    double pf[PF];
+    // bulk lane bt stages label sl's rows of round sq of a chunk (C*CH/4 <= C*G pairs)
+    const bool stg = !chain && bt < C * (CH / M);
+    const int sq = stg ? bt / C : 0;
+    const int sl = stg ? bt - sq * C : 0;
+    double pf[M];                                          // raw S of the chunk after next
+    auto stage_load = [&](int tcs) {
 #pragma unroll
-    for (int i = 0; i < PF; ++i) pf[i] = 0.0;
+        for (int d = 0; d < M; ++d) {
+            const int t = tcs + M * sq + d;
+            pf[d] = (stg && t <= t1) ? Sb[sidx(t, sl)] : 0.0;
+        }
+    };
+    auto stage_store = [&](int buf) {
+        if (!stg) return;
+        double sv[M];
+#pragma unroll
+        for (int d = 0; d < M; ++d) sv[d] = spub(pf[d], sl);
+        double2* dS = reinterpret_cast<double2*>(Sbuf + buf * chunkN + sl * CH + M * sq);
+        dS[0] = make_double2(sv[0], sv[1]);
+        dS[1] = make_double2(sv[2], sv[3]);
+        float g[M];
+#pragma unroll
+        for (int d = 0; d < M; ++d) g[d] = (float)(sv[d] - sv[0]);
+        float* f = Fst + (size_t)buf * 3 * C * CH + sl * CH + M * sq;
+        st4(f, make_float4(1.0f, fast_exp2(g[1]), fast_exp2(g[2]), fast_exp2(g[3])));
+        st4(f + C * CH, make_float4(1.0f, fast_exp2(-g[1]), fast_exp2(-g[2]), fast_exp2(-g[3])));
+        st4(f + 2 * C * CH, make_float4(0.0f, g[1], g[2], g[3]));
+    };
     if (!chain) {
-        for (int q = bt; q < chunkN; q += NB) {
-            const int row = q / C, l = q - row * C;
-            const int t = t0 + 1 + row;
-            Sbuf[l * CH + row] = (t <= t1) ? spub(Sb[sidx(t, l)], l) : 0.0;
-        }
-#pragma unroll
-        for (int i = 0; i < PF; ++i) {
-            const int q = bt + i * NB;
-            if (q < chunkN) {
-                const int row = q / C, l = q - row * C;
-                const int t = t0 + 1 + CH + row;
-                if (t <= t1) pf[i] = Sb[sidx(t, l)];
-            }
-        }
+        stage_load(t0 + 1);
+        stage_store(0);
+        stage_load(t0 + 1 + CH);
     }
     __syncthreads();   // restored ring and chunk 0 visible
     __builtin_amdgcn_s_waitcnt(0);
@@ -364,13 +380,20 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
             const float* ns = nsh + (((r - 1) & 1) * (CP + 1) + cb) * 2 * M + j;
             Rrow[round_slot(r - 1, RMASK) + j] = fmaxf(fast_log2(ns[0]) + ns[M], NEG);
         }
-        // the chain rebased last round: move the blocks of rounds <= r-2 (reads first)
+        // the chain rebased last round: move the blocks of rounds <= r-2 (reads first).
+        // Linear entries are scaled by 2^-dl: one that underflowed is below 2^-126 and
+        // negligible next to any linear sum the range checks accept (>= 2^-60); sums
+        // that fail them are redone from the log ring.
         if (r >= 3 && (r & 1) == 1) {
             constexpr int BR = BPL + 1;               // covers NR = bmax + 3 <= BPL*G + G blocks
             const float dl = bact ? dlsh[cb] : 0.0f;
-            float4 v[BR];
+            const float sc = fast_exp2(-dl);
+            float4 v[BR], e[BR];
 #pragma unroll
-            for (int i = 0; i < BR; ++i) v[i] = ld4(Rrow + round_slot(r - 2 - j - i * G, RMASK));
+            for (int i = 0; i < BR; ++i) {
+                v[i] = ld4(Rrow + round_slot(r - 2 - j - i * G, RMASK));
+                if constexpr (LIN) e[i] = ld4(Erow + round_slot(r - 2 - j - i * G, RMASK));
+            }
 #pragma unroll
             for (int i = 0; i < BR; ++i) {
                 const int q = j + i * G;
@@ -386,8 +409,7 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                 st4((live ? Rrow : R + C * P) + sl, rv);
                 if constexpr (LIN)
                     st4((live ? Erow : E + C * P) + sl,
-                        make_float4(exp2_or_zero(rv.x), exp2_or_zero(rv.y), exp2_or_zero(rv.z),
-                                    exp2_or_zero(rv.w)));
+                        make_float4(e[i].x * sc, e[i].y * sc, e[i].z * sc, e[i].w * sc));
             }
         }
         // checkpoint rings of the positions the chain checkpointed last round
@@ -458,16 +480,23 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
             const double H0 = H;
             float hb[M], yv[M], fb[M], fo[M];
             {
-                // S(p_m) of label cl, rows row0 .. row0+3 (row0 % 4 == 0: 16-byte loads)
-                const double2* sp = reinterpret_cast<const double2*>(Sch + cl * CH + row0);
-                const double2 s01 = sp[0], s23 = sp[1];
-                const double sv4[M] = {s01.x, s01.y, s23.x, s23.y};
+                // S(p_m) + B_c - H0 from S(p_0) and the staged differences; the scales
+                // 2^(hb + dmax) and 2^(tmax - hb) from one exp2 each and staged factors
+                const float* f = Fst + (size_t)(nch & 1) * 3 * C * CH + cl * CH + row0;
+                const float4 sg4 = ld4(f), is4 = ld4(f + C * CH), g4 = ld4(f + 2 * C * CH);
+                const float hb0 = (float)(Sch[cl * CH + row0] + BH);
+                const float y0 = cact ? fast_exp2(hb0 + dmax) : 0.0f;
+                const float fo0 = tmax - hb0;
+                const float f0 = fast_exp2(fo0);
+                const float gs[M] = {g4.x, g4.y, g4.z, g4.w};
+                const float ss[M] = {sg4.x, sg4.y, sg4.z, sg4.w};
+                const float is[M] = {is4.x, is4.y, is4.z, is4.w};
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
-                    hb[m] = (float)(sv4[m] + BH);            // S(p_m) + B_c - H0
-                    yv[m] = cact ? fast_exp2(hb[m] + dmax) : 0.0f;   // message scale
-                    fo[m] = tmax - hb[m];
-                    fb[m] = fast_exp2(fo[m]);                // ring-entry scale
+                    hb[m] = hb0 + gs[m];
+                    yv[m] = y0 * ss[m];                      // message scale
+                    fo[m] = fo0 - gs[m];
+                    fb[m] = f0 * is[m];                      // ring-entry scale
                 }
             }
             // ---- fast pass (linear space, no branches)
@@ -642,24 +671,8 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
         } else {
             // ---- S staging: in the first round of a chunk publish the next one
             if (rs + 1 == tc && tc + CH <= t1) {
-                double* dst = Sbuf + ((nch + 1) & 1) * chunkN;
-#pragma unroll
-                for (int i = 0; i < PF; ++i) {
-                    const int q = bt + i * NB;
-                    if (q < chunkN) {
-                        const int row = q / C, l = q - row * C;
-                        dst[l * CH + row] = spub(pf[i], l);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < PF; ++i) {
-                    const int q = bt + i * NB;
-                    if (q < chunkN) {
-                        const int rr = q / C, l = q - rr * C;
-                        const int tt = tc + 2 * CH + rr;
-                        pf[i] = (tt <= t1) ? Sb[sidx(tt, l)] : 0.0;
-                    }
-                }
+                stage_store((nch + 1) & 1);
+                stage_load(tc + 2 * CH);
             }
             ring_round(r, rs);
             // ---- bulk sums of round r+1 (ring blocks of rounds <= r-1)
