@@ -20,7 +20,7 @@ struct Layout {
     size_t status = 0, Leff = 0, tsum = 0, toff = 0, ttot = 0, S = 0;
     size_t logz = 0, logzb = 0;
     size_t ckR = 0, ckB = 0, ckM = 0, ckH = 0, XF = 0, AF = 0, XB = 0, AB = 0;
-    size_t Dn = 0, dnt = 0, dno = 0, mu = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0;
+    size_t Dn = 0, dnt = 0, dno = 0, mu = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0, rps = 0;
     size_t bp = 0, vscore = 0, vcstar = 0, vwin = 0, split = 0, btr = 0, bent = 0;
     size_t total = 0;
 };
@@ -93,6 +93,7 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         lo.zt = m.take(sizeof(double) * B * lo.ntm);
         lo.pd = m.take(sizeof(double) * B * lo.ntm * K * C);
         lo.pt = m.take(sizeof(double) * B * lo.ntm * C * C);
+        lo.rps = m.take(sizeof(double) * reduce_scratch_doubles(C, K));
     } else if (op == SEMICRF_OP_PREFIX) {
         // S goes to the caller's buffer: drop the internal copy
         lo.total = lo.S;
@@ -296,8 +297,8 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
     LAUNCH(launch_grad_em(mu, at<double>(workspace, lo.mutot), a.Leff, grad_log_z, B, T, C, grad_em,
                           stream));
     LAUNCH(launch_reduce_partials(m.part_dur, m.part_trans, at<double>(workspace, lo.zt), a.Leff,
-                                  grad_log_z, B, T, C, K, lo.tm, lo.ntm, grad_dur, grad_trans,
-                                  stream));
+                                  grad_log_z, B, T, C, K, lo.tm, lo.ntm,
+                                  at<double>(workspace, lo.rps), grad_dur, grad_trans, stream));
     if (log_z) LAUNCH(launch_write_logz(a.logz, B, log_z, stream));
     STAGE(5);
     return SEMICRF_OK;

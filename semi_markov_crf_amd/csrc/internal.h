@@ -167,10 +167,13 @@ hipError_t launch_node_marginals(const double* Dn, const double* dn_off, const i
 hipError_t launch_grad_em(const float* mu, const double* mu_tot, const int* Leff,
                           const float* grad_log_z, int B, int T, int C, float* grad_em,
                           hipStream_t stream);
+// scratch: reduce_scratch_doubles(C, K) doubles
+size_t reduce_scratch_doubles(int C, int K);
 hipError_t launch_reduce_partials(const double* part_dur, const double* part_trans,
                                   const double* z_tile, const int* Leff, const float* grad_log_z,
                                   int B, int T, int C, int K, int tile, int ntiles,
-                                  float* grad_dur, float* grad_trans, hipStream_t stream);
+                                  double* scratch, float* grad_dur, float* grad_trans,
+                                  hipStream_t stream);
 hipError_t launch_write_logz(const double* logz, int B, float* out, hipStream_t stream);
 
 // ------------------------------------------------------------------ Viterbi

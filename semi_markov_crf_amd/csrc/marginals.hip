@@ -261,38 +261,63 @@ hipError_t launch_grad_em(const float* mu, const double* mu_tot, const int* Leff
 }
 
 // one thread per output element of grad_dur [K*C] followed by grad_trans [C*C]
+// grad_dur / grad_trans = sum over sequences b of g_b * sum over tiles j of
+// part[b][j] / z_tile[b][j].  Pass 1: grid (ceil(n / 64), RP_SLICES / 4), block 256; lane
+// (e, slice) sums the tiles j = slice, slice + RP_SLICES, ... of every sequence into
+// scratch[slice][e].  Pass 2: one lane per output adds the slices in order.  Fixed order
+// throughout: bitwise reproducible.
+constexpr int RP_SLICES = 32;
+
 __global__ __launch_bounds__(256) void k_reduce_partials(const double* __restrict__ part_dur,
                                                          const double* __restrict__ part_trans,
                                                          const double* __restrict__ z_tile,
                                                          const float* __restrict__ grad_log_z,
                                                          int B, int C, int K, int ntiles,
-                                                         float* __restrict__ grad_dur,
-                                                         float* __restrict__ grad_trans) {
-    const int q = blockIdx.x * 256 + threadIdx.x;
-    const int nd = K * C, nt = C * C;
-    if (q >= nd + nt) return;
-    const bool isd = q < nd;
-    const int e = isd ? q : q - nd;
-    const int stride = isd ? nd : nt;
+                                                         double* __restrict__ scratch) {
+    const int n = K * C + C * C;
+    const int e = blockIdx.x * 64 + (threadIdx.x & 63);
+    const int slice = blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (e >= n) return;
+    const int nd = K * C;
+    const bool isd = e < nd;
+    const int ee = isd ? e : e - nd;
+    const int stride = isd ? nd : C * C;
     const double* src = isd ? part_dur : part_trans;
     double total = 0.0;
     for (int b = 0; b < B; ++b) {
         double s = 0.0;
-        for (int j = 0; j < ntiles; ++j)
-            s += src[((size_t)b * ntiles + j) * stride + e] / z_tile[(size_t)b * ntiles + j];
+        for (int j = slice; j < ntiles; j += RP_SLICES)
+            s += src[((size_t)b * ntiles + j) * stride + ee] / z_tile[(size_t)b * ntiles + j];
         total += (grad_log_z ? (double)grad_log_z[b] : 1.0) * s;
     }
-    (isd ? grad_dur : grad_trans)[e] = (float)total;
+    scratch[(size_t)slice * n + e] = total;
 }
+
+__global__ __launch_bounds__(256) void k_reduce_slices(const double* __restrict__ scratch, int C,
+                                                       int K, float* __restrict__ grad_dur,
+                                                       float* __restrict__ grad_trans) {
+    const int n = K * C + C * C;
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= n) return;
+    double total = 0.0;
+    for (int sl = 0; sl < RP_SLICES; ++sl) total += scratch[(size_t)sl * n + e];
+    if (e < K * C) grad_dur[e] = (float)total;
+    else grad_trans[e - K * C] = (float)total;
+}
+
+size_t reduce_scratch_doubles(int C, int K) { return (size_t)RP_SLICES * (K * C + C * C); }
 
 hipError_t launch_reduce_partials(const double* part_dur, const double* part_trans,
                                   const double* z_tile, const int* Leff, const float* grad_log_z,
                                   int B, int T, int C, int K, int tile, int ntiles,
-                                  float* grad_dur, float* grad_trans, hipStream_t stream) {
+                                  double* scratch, float* grad_dur, float* grad_trans,
+                                  hipStream_t stream) {
     (void)Leff; (void)T; (void)tile;
     const int n = K * C + C * C;
-    hipLaunchKernelGGL(k_reduce_partials, dim3((n + 255) / 256), dim3(256), 0, stream, part_dur,
-                       part_trans, z_tile, grad_log_z, B, C, K, ntiles, grad_dur, grad_trans);
+    hipLaunchKernelGGL(k_reduce_partials, dim3((n + 63) / 64, RP_SLICES / 4), dim3(256), 0, stream,
+                       part_dur, part_trans, z_tile, grad_log_z, B, C, K, ntiles, scratch);
+    hipLaunchKernelGGL(k_reduce_slices, dim3((n + 255) / 256), dim3(256), 0, stream, scratch, C, K,
+                       grad_dur, grad_trans);
     return hipGetLastError();
 }
 
