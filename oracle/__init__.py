@@ -24,4 +24,7 @@ from .semicrf import (  # noqa: F401
     segmentation_score,
     sequence,
     batch,
+    gold_features,
+    nll_sequence,
+    nll_batch,
 )

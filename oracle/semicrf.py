@@ -46,6 +46,8 @@ Readings taken where the pages are silent (each is listed in the design doc):
    along the decoded path (including the final label), of the gap between
    the chosen value and the runner-up; it equals the score gap between the
    best and the second-best segmentation.
+8. The training loss of a gold segmentation is its negative log-probability,
+   log Z - score(y*); its gradient is expected minus gold feature counts.
 """
 
 from __future__ import annotations
@@ -273,6 +275,67 @@ def segmentation_score(S, trans, dur, K: int, seg_start: np.ndarray, labels: np.
             total += trans[prev, c]
         prev = c
     return total
+
+
+def gold_features(labels, seg_start, L: int, K: int, C: int):
+    """Feature counts of one segmentation, from its definition: the per-position
+    label indicator [L, C], the number of segments of each length k and label c
+    [K, C], and the number of transitions c' -> c between consecutive segments
+    [C, C].  Raises ValueError for an invalid segmentation (same checks as
+    ``segmentation_score``)."""
+    starts = [int(i) for i in np.nonzero(np.asarray(seg_start)[:L])[0]]
+    if not starts or starts[0] != 0:
+        raise ValueError("segmentation must start at position 0")
+    ind = np.zeros((L, C))
+    dcount = np.zeros((K, C))
+    tcount = np.zeros((C, C))
+    prev = None
+    for s, e in zip(starts, starts[1:] + [L]):
+        k = e - s
+        c = int(labels[s])
+        if not (1 <= k <= K) or not (0 <= c < C) or np.any(np.asarray(labels[s:e]) != c):
+            raise ValueError(f"invalid segment [{s}, {e}) label {c}")
+        ind[s:e, c] = 1.0
+        dcount[k - 1, c] += 1.0
+        if prev is not None:
+            tcount[prev, c] += 1.0
+        prev = c
+    return ind, dcount, tcount
+
+
+def nll_sequence(em_b, L: int, trans, dur, K: int, labels, seg_start, g: float = 1.0):
+    """Training loss of one gold segmentation y*: nll = log Z - score(y*), minus
+    the log-probability the model gives y* (the loss of the pages' training
+    convergence check, EN explainer, "4. Results and Benchmarks").  Gradients of
+    g * nll: the posterior expectations of the features (the gradients of log Z)
+    minus the features of y*, with the centring in the function (reading 6)."""
+    r = sequence(em_b, L, trans, dur, K, g=g, want_viterbi=False)
+    C = r["S"].shape[1]
+    score = segmentation_score(r["S"], trans, dur, K, seg_start, labels)
+    ind, dcount, tcount = gold_features(labels, seg_start, L, K, C)
+    grad_em = r["grad_em"] - g * (ind - ind.mean(axis=0, keepdims=True))
+    return {"nll": r["logZ"] - score, "score": score, "logZ": r["logZ"], "grad_em": grad_em,
+            "grad_trans": r["grad_trans"] - g * tcount, "grad_dur": r["grad_dur"] - g * dcount}
+
+
+def nll_batch(em, lengths, trans, dur, K: int, gold_labels, gold_seg_start, grad_nll=None):
+    """``nll_sequence`` for every b, packed with the ABI's conventions (zeros at
+    t >= L; grad_trans and grad_dur summed over the batch)."""
+    em = np.asarray(em)
+    B, T, C = em.shape
+    g = np.ones(B) if grad_nll is None else np.asarray(grad_nll, dtype=np.float64)
+    out = {"nll": np.zeros(B), "score": np.zeros(B), "logZ": np.zeros(B),
+           "grad_em": np.zeros((B, T, C)), "grad_trans": np.zeros((C, C)),
+           "grad_dur": np.zeros(np.asarray(dur).shape)}
+    for b in range(B):
+        L = int(lengths[b])
+        r = nll_sequence(em[b], L, trans, dur, K, gold_labels[b, :L], gold_seg_start[b, :L],
+                         float(g[b]))
+        out["nll"][b], out["score"][b], out["logZ"][b] = r["nll"], r["score"], r["logZ"]
+        out["grad_em"][b, :L] = r["grad_em"]
+        out["grad_trans"] += r["grad_trans"]
+        out["grad_dur"] += r["grad_dur"]
+    return out
 
 
 def sequence(em_b, L: int, trans, dur, K: int, g: float = 1.0, *, want_viterbi=True,

@@ -121,6 +121,34 @@ def brute_force(em_b, L: int, trans, dur, K: int):
             "labels": labels, "seg_start": seg, "n": int(flat.size)}
 
 
+def brute_force_nll(em_b, L: int, trans, dur, K: int, labels, seg_start) -> float:
+    """-log P(y*) of the segmentation given by (labels, seg_start): every
+    segmentation is enumerated and scored position by position (centred emissions
+    summed over each segment, no prefix sums), and the gold one is picked out by its
+    segments."""
+    x = centred_emissions(em_b, L)
+    C = len(x[0])
+    trans = np.asarray(trans, dtype=np.float64)
+    dur = np.asarray(dur, dtype=np.float64)
+    starts = [t for t in range(L) if seg_start[t]]
+    gold = tuple((s, e - s, int(labels[s])) for s, e in zip(starts, starts[1:] + [L]))
+    scores = []
+    gold_score = None
+    for comp in compositions(L, K):
+        st = [sum(comp[:i]) for i in range(len(comp))]
+        for labs in itertools.product(range(C), repeat=len(comp)):
+            sc = 0.0
+            for i, (s, k) in enumerate(zip(st, comp)):
+                sc += sum(x[u][labs[i]] for u in range(s, s + k)) + dur[k - 1, labs[i]]
+                if i > 0:
+                    sc += trans[labs[i - 1], labs[i]]
+            scores.append(sc)
+            if tuple(zip(st, comp, labs)) == gold:
+                gold_score = sc
+    assert gold_score is not None, "gold segmentation not among the enumerated ones"
+    return _logsumexp_list(scores) - gold_score
+
+
 def linear_chain(unary, trans):
     """Textbook linear-chain CRF over L positions and C states with scores
     unary[t][c] and trans[c'][c] (no start / end scores): forward, backward,

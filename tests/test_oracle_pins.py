@@ -241,6 +241,88 @@ def test_finite_differences():
     assert a @ b / (np.linalg.norm(a) * np.linalg.norm(b)) >= 0.9999
 
 
+# --------------------------------------------------------------------------- gold-segmentation loss
+
+
+def _gold(seed, L, T, K, C):
+    labels, seg = workloads.gold_segmentation(seed, np.array([L]), T, C, K)
+    return labels[0, :L], seg[0, :L]
+
+
+@pytest.mark.parametrize("seed,L,T,K,C", BF_CASES)
+def test_nll_matches_brute_force(seed, L, T, K, C):
+    em, L, trans, dur, K = _case(seed, L, T, K, C)
+    labels, seg = _gold(100 + seed, L, T, K, C)
+    r = oracle.nll_sequence(em, L, trans, dur, K, labels, seg)
+    ref = pins.brute_force_nll(em, L, trans, dur, K, labels, seg)
+    assert abs(r["nll"] - ref) < 1e-10 * max(1.0, abs(ref))
+    assert r["nll"] >= -1e-12                      # log Z >= the score of any segmentation
+    # the centred emission gradient sums to zero over labels at every position
+    assert np.abs(r["grad_em"].sum(axis=1)).max() < 1e-12
+
+
+def test_nll_finite_differences():
+    em, L, trans, dur, K = _case(57, 6, 6, 3, 2, scale=1.2, trans_sd=0.8, dur_sd=0.8)
+    labels, seg = _gold(157, L, 6, K, 2)
+    g = 0.7
+    r = oracle.nll_sequence(em, L, trans, dur, K, labels, seg, g=g)
+    f = lambda e, t, d: g * pins.brute_force_nll(e, L, t, d, K, labels, seg)
+    h = 1e-5
+    for arr, key in ((em, "grad_em"), (trans, "grad_trans"), (dur, "grad_dur")):
+        fd = np.zeros(r[key].shape)
+        for idx in np.ndindex(*fd.shape):
+            e = np.zeros_like(arr)
+            e[idx] = h
+            args_p = [em, trans, dur]
+            args_m = [em, trans, dur]
+            pos = 0 if arr is em else (1 if arr is trans else 2)
+            args_p[pos] = arr + e
+            args_m[pos] = arr - e
+            fd[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+        np.testing.assert_allclose(r[key], fd, atol=1e-7, err_msg=key)
+
+
+def _mut_gold_no_trans(labels, seg_start, L, K, C, _orig=osc.gold_features):
+    ind, dc, tc = _orig(labels, seg_start, L, K, C)
+    return ind, dc, np.zeros_like(tc)              # transitions of y* not counted
+
+
+def _mut_gold_dur_index(labels, seg_start, L, K, C, _orig=osc.gold_features):
+    ind, dc, tc = _orig(labels, seg_start, L, K, C)
+    return ind, np.vstack([dc[1:], dc[:1]]), tc    # length k counted as k - 1
+
+
+def _mut_gold_extent(labels, seg_start, L, K, C, _orig=osc.gold_features):
+    ind, dc, tc = _orig(labels, seg_start, L, K, C)
+    return np.roll(ind, 1, axis=0), dc, tc         # segment extents off by one position
+
+
+@pytest.mark.parametrize("name,fn", [
+    ("gold transitions dropped", _mut_gold_no_trans),
+    ("gold duration index", _mut_gold_dur_index),
+    ("gold segment extents", _mut_gold_extent),
+])
+def test_nll_pins_catch_planted_mistakes(monkeypatch, name, fn):
+    em, L, trans, dur, K = _case(59, 6, 6, 3, 2, scale=1.2, trans_sd=0.8, dur_sd=0.8)
+    labels, seg = _gold(159, L, 6, K, 2)
+    h = 1e-5
+    monkeypatch.setattr(osc, "gold_features", fn)
+    bad = oracle.nll_sequence(em, L, trans, dur, K, labels, seg)
+    f = lambda e, t, d: pins.brute_force_nll(e, L, t, d, K, labels, seg)
+    err = 0.0
+    for arr, key in ((em, "grad_em"), (trans, "grad_trans"), (dur, "grad_dur")):
+        for idx in np.ndindex(*bad[key].shape):
+            e = np.zeros_like(arr)
+            e[idx] = h
+            a = [em, trans, dur]
+            b = [em, trans, dur]
+            pos = 0 if arr is em else (1 if arr is trans else 2)
+            a[pos] = arr + e
+            b[pos] = arr - e
+            err = max(err, abs(bad[key][idx] - (f(*a) - f(*b)) / (2 * h)))
+    assert err > 1e-3, f"pin missed planted mistake: {name}"
+
+
 # --------------------------------------------------------------------------- planted mistakes
 
 

@@ -185,3 +185,23 @@ def make_custom(seed: int, B: int, T: int, C: int, K: int, *, em_scale: float = 
     dur = rng.normal(0.0, dur_sd, size=(K, C))
     return Workload(f"custom{seed}", em.astype(np.float32), lengths, trans.astype(np.float32),
                     dur.astype(np.float32), K, None)
+
+
+def gold_segmentation(seed: int, lengths, T: int, C: int, K: int):
+    """A random valid segmentation of every sequence, as training targets: segment
+    lengths uniform in [1, min(K, rest)], labels uniform in [0, C).  Returns labels
+    int32 [B, T] (-1 at t >= L) and seg_start uint8 [B, T] (1 at each segment's first
+    position)."""
+    rng = np.random.default_rng(seed)
+    B = len(lengths)
+    labels = np.full((B, T), -1, dtype=np.int32)
+    seg = np.zeros((B, T), dtype=np.uint8)
+    for b in range(B):
+        L = int(lengths[b])
+        t = 0
+        while t < L:
+            k = int(rng.integers(1, min(K, L - t) + 1))
+            labels[b, t:t + k] = int(rng.integers(0, C))
+            seg[b, t] = 1
+            t += k
+    return labels, seg
