@@ -118,6 +118,28 @@ int semicrf_backward(const float* emissions, const int32_t* lengths, const float
                      const float* grad_log_z, float* grad_emissions, float* grad_trans,
                      float* grad_dur, float* marginals, float* log_z);
 
+/* Training loss of gold segmentations and its gradients.  nll[b] = log Z_b - score_b(y*),
+ * the negative log-probability of the gold segmentation y* (the training loss of the
+ * pages' convergence check, EN explainer, "4. Results and Benchmarks"); score sums, over
+ * the gold segments [s, e) of label c, S[e,c] - S[s,c] + dur[e-s-1, c] and, between
+ * consecutive segments, trans[c', c] (the same centred potential as log Z, "2.
+ * Methodology").  Inputs as semicrf_backward plus
+ *   gold_labels    [B, T] int32  label of every position t < lengths[b]
+ *   gold_seg_start [B, T] uint8  1 at each gold segment's first position (t = 0 must be 1)
+ *   grad_nll       [B] float32 or NULL for all ones
+ * Outputs: nll [B] float32, and the gradients of sum_b grad_nll[b] * nll[b] in
+ * grad_emissions [B, T, C], grad_trans [C, C], grad_dur [K, C] (expected minus gold feature
+ * counts; the emission gradient includes the centring; 0 at padding).  A gold segmentation
+ * with a segment longer than K, a label outside [0, C), a label change inside a segment or
+ * no start at t = 0 gives NaN for that sequence and raises the status flag, like an
+ * invalid length; its gold counts are then left out of the gradients, which keep only
+ * its log Z half.  Workspace: semicrf_workspace_bytes(SEMICRF_OP_BACKWARD, ...). */
+int semicrf_nll(const float* emissions, const int32_t* lengths, const float* trans,
+                const float* dur, const int32_t* gold_labels, const uint8_t* gold_seg_start,
+                int B, int T, int C, int K, int delta, hipStream_t stream, void* workspace,
+                size_t workspace_bytes, const float* grad_nll, float* nll,
+                float* grad_emissions, float* grad_trans, float* grad_dur);
+
 /* Max-plus decode of the best segmentation (the Viterbi counterpart of the forward
  * pass).  Each max-plus step breaks ties toward the shortest segment, then the lowest
  * previous label.  For C <= 16 the forward sweep and a sweep over the mirrored sequence

@@ -138,6 +138,38 @@ def backward(em, lengths, trans, dur, *, grad_log_z=None, delta=0, want_marginal
             "marginals": mu, "log_z": lz}
 
 
+def nll(em, lengths, trans, dur, gold_labels, gold_seg_start, *, grad_nll=None, delta=0,
+        workspace=None, check_status=False) -> dict:
+    """Training loss of gold segmentations, nll[b] = log Z_b - score_b(y*), and the
+    gradients of sum_b grad_nll[b] * nll[b] (all ones when None).  gold_labels int32
+    [B,T] and gold_seg_start uint8 [B,T] on the emissions' device.  Returns a dict with
+    nll [B], grad_em [B,T,C], grad_trans [C,C], grad_dur [K,C]."""
+    B, T, C, K = _check_inputs(em, lengths, trans, dur)
+    dev = em.device
+    for name, x, dt in (("gold_labels", gold_labels, torch.int32),
+                        ("gold_seg_start", gold_seg_start, torch.uint8)):
+        if x.shape != (B, T) or x.dtype != dt or x.device != dev:
+            raise ValueError(f"{name} must be a {dt} [B, T] tensor on the emissions' device")
+    if grad_nll is not None:
+        if grad_nll.shape != (B,) or grad_nll.dtype != torch.float32 or grad_nll.device != dev:
+            raise ValueError("grad_nll must be a float32 [B] tensor on the emissions' device")
+        grad_nll = grad_nll.contiguous()
+    gold_labels, gold_seg_start = gold_labels.contiguous(), gold_seg_start.contiguous()
+    ws, n = _workspace(OP_BACKWARD, B, T, C, K, delta, dev, workspace)
+    out = torch.empty(B, dtype=torch.float32, device=dev)
+    grad_em = torch.empty_like(em)
+    grad_trans = torch.empty_like(trans)
+    grad_dur = torch.empty_like(dur)
+    rc = _native.load().semicrf_nll(
+        em.data_ptr(), lengths.data_ptr(), trans.data_ptr(), dur.data_ptr(),
+        gold_labels.data_ptr(), gold_seg_start.data_ptr(), B, T, C, K, delta, _stream(dev),
+        ws.data_ptr(), n, None if grad_nll is None else grad_nll.data_ptr(), out.data_ptr(),
+        grad_em.data_ptr(), grad_trans.data_ptr(), grad_dur.data_ptr())
+    _native.check("semicrf_nll", rc)
+    _maybe_check(ws, check_status, "semicrf_nll")
+    return {"nll": out, "grad_em": grad_em, "grad_trans": grad_trans, "grad_dur": grad_dur}
+
+
 def viterbi(em, lengths, trans, dur, *, workspace=None, check_status=False):
     """Returns (best_score [B] float32, labels [B,T] int32, seg_start [B,T] uint8)."""
     B, T, C, K = _check_inputs(em, lengths, trans, dur)

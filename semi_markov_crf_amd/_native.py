@@ -31,6 +31,8 @@ SIGNATURES = {
                                   _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp]),
     "semicrf_viterbi": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
                                  _c_size, _vp, _vp, _vp]),
+    "semicrf_nll": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                             _c_int, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp]),
     "semicrf_read_status": (_c_int, [_vp, _vp]),
     "semicrf_prefix": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
     "semicrf_logz_staged": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,

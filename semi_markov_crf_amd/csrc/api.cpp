@@ -21,6 +21,7 @@ struct Layout {
     size_t logz = 0, logzb = 0;
     size_t ckR = 0, ckB = 0, ckM = 0, ckH = 0, XF = 0, AF = 0, XB = 0, AB = 0;
     size_t Dn = 0, dnt = 0, dno = 0, mu = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0, rps = 0;
+    size_t gcnt = 0, gpart = 0;
     size_t bp = 0, vscore = 0, vcstar = 0, vwin = 0, split = 0, btr = 0, bent = 0;
     size_t total = 0;
 };
@@ -94,6 +95,9 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         lo.pd = m.take(sizeof(double) * B * lo.ntm * K * C);
         lo.pt = m.take(sizeof(double) * B * lo.ntm * C * C);
         lo.rps = m.take(sizeof(double) * reduce_scratch_doubles(C, K));
+        // gold-segmentation loss (semicrf_nll): counters and block sums
+        lo.gcnt = m.take(sizeof(int) * (size_t)B * (K * C + C * C + C + 1));
+        lo.gpart = m.take(sizeof(double) * (size_t)B * gold_blocks(T));
     } else if (op == SEMICRF_OP_PREFIX) {
         // S goes to the caller's buffer: drop the internal copy
         lo.total = lo.S;
@@ -369,6 +373,39 @@ int semicrf_backward_staged(const float* em, const int32_t* lengths, const float
     return run_backward(em, lengths, trans, dur, B, T, C, K, delta, stream, workspace,
                         workspace_bytes, grad_log_z, grad_em, grad_trans, grad_dur, marginals, log_z,
                         events);
+}
+
+int semicrf_nll(const float* em, const int32_t* lengths, const float* trans, const float* dur,
+                const int32_t* gold_labels, const uint8_t* gold_seg_start, int B, int T, int C,
+                int K, int delta, hipStream_t stream, void* workspace, size_t workspace_bytes,
+                const float* grad_nll, float* nll, float* grad_em, float* grad_trans,
+                float* grad_dur) {
+    if (!gold_labels || !gold_seg_start || !nll) return SEMICRF_ERR_INVALID;
+    int rc = run_backward(em, lengths, trans, dur, B, T, C, K, delta, stream, workspace,
+                          workspace_bytes, grad_nll, grad_em, grad_trans, grad_dur, nullptr,
+                          nullptr, nullptr);
+    if (rc) return rc;
+    Layout lo;
+    if (!make_layout(SEMICRF_OP_BACKWARD, B, T, C, K, delta, lo)) return SEMICRF_ERR_UNSUPPORTED;
+    GoldArgs g{};
+    g.S = at<double>(workspace, lo.S);
+    g.Leff = at<int>(workspace, lo.Leff);
+    g.trans = trans;
+    g.dur = dur;
+    g.labels = gold_labels;
+    g.seg_start = gold_seg_start;
+    g.B = B; g.T = T; g.C = C; g.K = K;
+    g.logz = at<double>(workspace, lo.logz);
+    g.grad_nll = grad_nll;
+    g.cnt = at<int>(workspace, lo.gcnt);
+    g.part = at<double>(workspace, lo.gpart);
+    g.status = at<int>(workspace, lo.status);
+    g.nll = nll;
+    g.grad_em = grad_em;
+    g.grad_trans = grad_trans;
+    g.grad_dur = grad_dur;
+    LAUNCH(launch_gold(g, stream));
+    return SEMICRF_OK;
 }
 
 int semicrf_viterbi(const float* em, const int32_t* lengths, const float* trans, const float* dur,

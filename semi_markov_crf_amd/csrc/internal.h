@@ -176,6 +176,28 @@ hipError_t launch_reduce_partials(const double* part_dur, const double* part_tra
                                   hipStream_t stream);
 hipError_t launch_write_logz(const double* logz, int B, float* out, hipStream_t stream);
 
+// ------------------------------------------------------------------ gold-segmentation loss
+struct GoldArgs {
+    const double* S;            // [B][T+1][C] centred prefix sums
+    const int* Leff;            // [B]
+    const float* trans;         // [C][C]
+    const float* dur;           // [K][C]
+    const int32_t* labels;      // [B][T] gold label per position
+    const uint8_t* seg_start;   // [B][T] 1 at each gold segment's first position
+    int B, T, C, K;
+    const double* logz;         // [B] from the backward pass
+    const float* grad_nll;      // [B] or NULL (ones)
+    int* cnt;                   // [B][K*C + C*C + C + 1] scratch counters
+    double* part;               // [B][gold_blocks(T)] scratch block sums
+    int* status;                // status word of the workspace
+    float* nll;                 // [B]
+    float* grad_em;             // [B][T][C] gradients of the backward pass, corrected in place
+    float* grad_trans;          // [C][C]
+    float* grad_dur;            // [K][C]
+};
+int gold_blocks(int T);
+hipError_t launch_gold(const GoldArgs& g, hipStream_t stream);
+
 // ------------------------------------------------------------------ Viterbi
 // chunk length and chunk count of the parallel backtrace
 int backtrace_chunk(int C, int K);
