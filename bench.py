@@ -40,10 +40,11 @@ PEAK_TRANS_PER_S = 256 * 32 * 2.4e9     # exp2/log2 issue: half of 64 lanes/cloc
 PEAK_HBM_BPS = 8.0e12
 # HBM bytes per checkpoint-sweep launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per
 # dispatch, scaled by 2.0 / 1.0, what the counters read for a 1 GiB copy), valid for the
-# kernel source with this SHA-256
-SWEEP_SRC = os.path.join(ROOT, "semi_markov_crf_amd", "csrc", "sweep_lse_round.h")
-SWEEP_TRAFFIC = {"sha256": "dc589ac14dc3a2f0b7f7c891b98c37cf15c966996f055b81ac567089d0a60d0e",
-                 "bytes": (19102.75 * 2.0 + 840.0 * 1.0) * 1024}
+# kernel sources with this SHA-256 (of their concatenation, in this order)
+SWEEP_SRCS = [os.path.join(ROOT, "semi_markov_crf_amd", "csrc", f)
+              for f in ("sweep_lse_round.h", "sweep_lse_kernel.h", "ring.h", "common.h")]
+SWEEP_TRAFFIC = {"sha256": "674a0d294aac687fefb3e9f49f915e73ee7ce519c126b36dfd17bfd7f0523fc6",
+                 "bytes": (19106.03 * 2.0 + 840.0 * 1.0) * 1024}
 
 
 def hip_runtime():
@@ -213,8 +214,11 @@ def main():
     # algorithmic bytes of the sweep pair: S read once per direction, checkpoints written
     nck = sum(max(0, (int(L) - 1) // delta) for L in w.lengths)
     algo_bytes = 2 * B * (T + 1) * C * 8 + 2 * nck * (K * C * 4 + C * 8 + C * 4 + 8)
-    with open(SWEEP_SRC, "rb") as f:
-        same_src = hashlib.sha256(f.read()).hexdigest() == SWEEP_TRAFFIC["sha256"]
+    digest = hashlib.sha256()
+    for src in SWEEP_SRCS:
+        with open(src, "rb") as f:
+            digest.update(f.read())
+    same_src = digest.hexdigest() == SWEEP_TRAFFIC["sha256"]
     traffic = SWEEP_TRAFFIC["bytes"] if (same_src and dom_stage == 1 and delta == 4473) else None
 
     out = {
