@@ -48,6 +48,15 @@ Readings taken where the pages are silent (each is listed in the design doc):
    best and the second-best segmentation.
 8. The training loss of a gold segmentation is its negative log-probability,
    log Z - score(y*); its gradient is expected minus gold feature counts.
+9. Boundary projections (EN explainer, "2. Methodology", "Boundary
+   Projections": separate start and end features added to the edge
+   potential): P_start[t, c] scores a segment of label c that starts at t,
+   P_end[t, c] one whose last position is t, so segment [s, s+k) of label c
+   gains P_start[s, c] + P_end[s+k-1, c].  Both are [L, C] per sequence, not
+   centred.  Their gradients are the start and end marginals; the boundary
+   probability at t (EN explainer, "4. Results and Benchmarks": boundary
+   probabilities checked at genome scale) is the probability that some
+   segment starts at t, sum_c start[t, c].
 """
 
 from __future__ import annotations
@@ -93,12 +102,13 @@ def _trans_with_start(trans: np.ndarray) -> np.ndarray:
 
 
 def edge_potentials(S: np.ndarray, trans: np.ndarray, dur: np.ndarray, K: int, L: int,
-                    s_lo: int, s_hi: int) -> np.ndarray:
+                    s_lo: int, s_hi: int, proj=None) -> np.ndarray:
     """Dense edge potentials psi[s - s_lo, k - 1, c', c] for segment starts
     s in [s_lo, s_hi), lengths k = 1..K, previous label c' in 0..C (C = start)
     and label c:
 
         psi = S[s+k, c] - S[s, c] + dur[k-1, c] + trans_start[c', c]
+              (+ P_start[s, c] + P_end[s+k-1, c] with proj = (P_start, P_end))
 
     and -inf where the segment would end past L.  This is one tile of the
     O(T*K*C^2) tensor the pages say standard implementations materialise
@@ -112,6 +122,9 @@ def edge_potentials(S: np.ndarray, trans: np.ndarray, dur: np.ndarray, K: int, L
     valid = end <= L
     content = S[np.minimum(end, L)] - S[s][:, None, :]  # [n, K, C]
     seg = content + dur[None, :, :]                     # [n, K, C]
+    if proj is not None:
+        ps, pe = (np.asarray(x, dtype=np.float64) for x in proj)
+        seg = seg + ps[s][:, None, :] + pe[np.minimum(end, L) - 1]
     psi = seg[:, :, None, :] + ts[None, None, :, :]     # [n, K, C+1, C]
     psi[~valid] = NEG_INF
     return psi
@@ -121,7 +134,7 @@ def _tile(K: int, C: int) -> int:
     return int(max(1, min(1024, (1 << 22) // max(1, K * (C + 1) * C))))
 
 
-def forward(S, trans, dur, K: int, L: int):
+def forward(S, trans, dur, K: int, L: int, proj=None):
     """alpha[t, c'] = log-sum over segmentations of [0, t) whose last segment
     has label c' (column C: the virtual start, alive only at t = 0), by
 
@@ -136,7 +149,7 @@ def forward(S, trans, dur, K: int, L: int):
     for t0 in range(1, L + 1, tile):
         t1 = min(L + 1, t0 + tile)
         s_lo = max(0, t0 - K)
-        psi = edge_potentials(S, trans, dur, K, L, s_lo, t1 - 1)
+        psi = edge_potentials(S, trans, dur, K, L, s_lo, t1 - 1, proj)
         for t in range(t0, t1):
             ks = ks_all[: min(K, t)]
             edges = psi[t - ks - s_lo, ks - 1]                   # [k, C+1, C]
@@ -145,7 +158,7 @@ def forward(S, trans, dur, K: int, L: int):
     return alpha, float(_lse(alpha[L, :C]))
 
 
-def backward(S, trans, dur, K: int, L: int):
+def backward(S, trans, dur, K: int, L: int, proj=None):
     """beta[s, c'] = log-sum over segmentations of [s, L) given that the
     previous segment (label c') ends at s:
 
@@ -160,7 +173,7 @@ def backward(S, trans, dur, K: int, L: int):
     starts = list(range(0, L, tile))
     for s_lo in reversed(starts):
         s_hi = min(L, s_lo + tile)
-        psi = edge_potentials(S, trans, dur, K, L, s_lo, s_hi)
+        psi = edge_potentials(S, trans, dur, K, L, s_lo, s_hi, proj)
         for s in range(s_hi - 1, s_lo - 1, -1):
             kmax = min(K, L - s)
             scores = psi[s - s_lo, :kmax] + beta[s + 1: s + kmax + 1, :C][:, None, :]   # [k, C+1, C]
@@ -168,14 +181,15 @@ def backward(S, trans, dur, K: int, L: int):
     return beta
 
 
-def posteriors(S, trans, dur, K: int, L: int, alpha, beta, logZ: float):
+def posteriors(S, trans, dur, K: int, L: int, alpha, beta, logZ: float, proj=None):
     """Edge marginals p(s, k, c', c) = exp(alpha[s, c'] + psi + beta[s+k, c] - logZ)
     summed into the feature expectations (= gradients of log Z):
 
     * grad_dur[k-1, c]  = sum_{s, c'} p           (d logZ / d dur)
     * grad_trans[c', c] = sum_{s, k}  p, real c'   (d logZ / d trans)
     * start[s, c] / end[e, c]: probability that a segment of label c starts at s
-      / ends at e;  d logZ / d S[t, c] = end[t, c] - start[t, c]
+      / ends at e;  d logZ / d S[t, c] = end[t, c] - start[t, c];
+      d logZ / d P_start[s, c] = start[s, c], d logZ / d P_end[t, c] = end[t+1, c]
     * mu[t, c] = P(position t lies in a segment of label c), via a difference
       array over the segment marginals."""
     C = S.shape[1]
@@ -186,7 +200,7 @@ def posteriors(S, trans, dur, K: int, L: int, alpha, beta, logZ: float):
     tile = _tile(K, C)
     for s_lo in range(0, L, tile):
         s_hi = min(L, s_lo + tile)
-        psi = edge_potentials(S, trans, dur, K, L, s_lo, s_hi)            # [n, K, C+1, C]
+        psi = edge_potentials(S, trans, dur, K, L, s_lo, s_hi, proj)      # [n, K, C+1, C]
         s = np.arange(s_lo, s_hi)
         e = np.minimum(s[:, None] + np.arange(1, K + 1)[None, :], L)      # [n, K]
         logp = alpha[s_lo:s_hi][:, None, :, None] + psi + beta[e][:, :, None, :C] - logZ
@@ -202,7 +216,7 @@ def posteriors(S, trans, dur, K: int, L: int, alpha, beta, logZ: float):
             "mu": mu, "dS": end - start}
 
 
-def viterbi(S, trans, dur, K: int, L: int):
+def viterbi(S, trans, dur, K: int, L: int, proj=None):
     """Max-plus version of ``forward`` with backpointers.  Ties go to the
     lexicographically lowest (k, c'), then the lowest final label (reading 7).
     Returns score, labels [L], seg_start [L] (uint8), margin, segments."""
@@ -216,7 +230,7 @@ def viterbi(S, trans, dur, K: int, L: int):
     for t0 in range(1, L + 1, tile):
         t1 = min(L + 1, t0 + tile)
         s_lo = max(0, t0 - K)
-        psi = edge_potentials(S, trans, dur, K, L, s_lo, t1 - 1)
+        psi = edge_potentials(S, trans, dur, K, L, s_lo, t1 - 1, proj)
         for t in range(t0, t1):
             ks = ks_all[: min(K, t)]
             scores = (V[t - ks][:, :, None] + psi[t - ks - s_lo, ks - 1]).reshape(-1, C)
@@ -251,11 +265,13 @@ def viterbi(S, trans, dur, K: int, L: int):
             "segments": segments}
 
 
-def segmentation_score(S, trans, dur, K: int, seg_start: np.ndarray, labels: np.ndarray) -> float:
+def segmentation_score(S, trans, dur, K: int, seg_start: np.ndarray, labels: np.ndarray,
+                       proj=None) -> float:
     """Score of one segmentation given per-position labels and segment-start
     flags, straight from the definition: sum of content + duration scores of
-    its segments and the transition scores between consecutive segments.
-    Raises ValueError if the segmentation is not valid."""
+    its segments (+ the start and end projections of each, reading 9) and the
+    transition scores between consecutive segments.  Raises ValueError if the
+    segmentation is not valid."""
     L = len(labels)
     starts = [int(i) for i in np.nonzero(seg_start[:L])[0]]
     if not starts or starts[0] != 0:
@@ -271,17 +287,21 @@ def segmentation_score(S, trans, dur, K: int, seg_start: np.ndarray, labels: np.
         if not (1 <= k <= K) or np.any(labels[s:e] != c) or not (0 <= c < S.shape[1]):
             raise ValueError(f"invalid segment [{s}, {e}) label {c}")
         total += S[e, c] - S[s, c] + dur[k - 1, c]
+        if proj is not None:
+            total += float(proj[0][s, c]) + float(proj[1][e - 1, c])
         if prev is not None:
             total += trans[prev, c]
         prev = c
     return total
 
 
-def gold_features(labels, seg_start, L: int, K: int, C: int):
+def gold_features(labels, seg_start, L: int, K: int, C: int, *, boundaries=False):
     """Feature counts of one segmentation, from its definition: the per-position
     label indicator [L, C], the number of segments of each length k and label c
     [K, C], and the number of transitions c' -> c between consecutive segments
-    [C, C].  Raises ValueError for an invalid segmentation (same checks as
+    [C, C]; with ``boundaries`` also the segment-start and segment-end (last
+    position) indicators [L, C] each, the features of the projections.  Raises
+    ValueError for an invalid segmentation (same checks as
     ``segmentation_score``)."""
     starts = [int(i) for i in np.nonzero(np.asarray(seg_start)[:L])[0]]
     if not starts or starts[0] != 0:
@@ -289,6 +309,8 @@ def gold_features(labels, seg_start, L: int, K: int, C: int):
     ind = np.zeros((L, C))
     dcount = np.zeros((K, C))
     tcount = np.zeros((C, C))
+    sind = np.zeros((L, C))
+    eind = np.zeros((L, C))
     prev = None
     for s, e in zip(starts, starts[1:] + [L]):
         k = e - s
@@ -296,29 +318,49 @@ def gold_features(labels, seg_start, L: int, K: int, C: int):
         if not (1 <= k <= K) or not (0 <= c < C) or np.any(np.asarray(labels[s:e]) != c):
             raise ValueError(f"invalid segment [{s}, {e}) label {c}")
         ind[s:e, c] = 1.0
+        sind[s, c] = 1.0
+        eind[e - 1, c] = 1.0
         dcount[k - 1, c] += 1.0
         if prev is not None:
             tcount[prev, c] += 1.0
         prev = c
+    if boundaries:
+        return ind, dcount, tcount, sind, eind
     return ind, dcount, tcount
 
 
-def nll_sequence(em_b, L: int, trans, dur, K: int, labels, seg_start, g: float = 1.0):
+def nll_sequence(em_b, L: int, trans, dur, K: int, labels, seg_start, g: float = 1.0,
+                 proj=None):
     """Training loss of one gold segmentation y*: nll = log Z - score(y*), minus
     the log-probability the model gives y* (the loss of the pages' training
     convergence check, EN explainer, "4. Results and Benchmarks").  Gradients of
     g * nll: the posterior expectations of the features (the gradients of log Z)
     minus the features of y*, with the centring in the function (reading 6)."""
-    r = sequence(em_b, L, trans, dur, K, g=g, want_viterbi=False)
+    r = sequence(em_b, L, trans, dur, K, g=g, want_viterbi=False, proj=proj)
     C = r["S"].shape[1]
-    score = segmentation_score(r["S"], trans, dur, K, seg_start, labels)
-    ind, dcount, tcount = gold_features(labels, seg_start, L, K, C)
+    score = segmentation_score(r["S"], trans, dur, K, seg_start, labels, proj)
+    ind, dcount, tcount, sind, eind = gold_features(labels, seg_start, L, K, C, boundaries=True)
     grad_em = r["grad_em"] - g * (ind - ind.mean(axis=0, keepdims=True))
-    return {"nll": r["logZ"] - score, "score": score, "logZ": r["logZ"], "grad_em": grad_em,
-            "grad_trans": r["grad_trans"] - g * tcount, "grad_dur": r["grad_dur"] - g * dcount}
+    out = {"nll": r["logZ"] - score, "score": score, "logZ": r["logZ"], "grad_em": grad_em,
+           "grad_trans": r["grad_trans"] - g * tcount, "grad_dur": r["grad_dur"] - g * dcount}
+    if proj is not None:
+        out.update(grad_proj_start=r["grad_proj_start"] - g * sind,
+                   grad_proj_end=r["grad_proj_end"] - g * eind)
+    return out
 
 
-def nll_batch(em, lengths, trans, dur, K: int, gold_labels, gold_seg_start, grad_nll=None):
+def _proj_of(proj_start, proj_end, b: int, L: int, C: int):
+    """(P_start, P_end) rows t < L of sequence b; a missing array counts as zeros."""
+    if proj_start is None and proj_end is None:
+        return None
+    z = np.zeros((L, C))
+    ps = z if proj_start is None else np.asarray(proj_start[b, :L], dtype=np.float64)
+    pe = z if proj_end is None else np.asarray(proj_end[b, :L], dtype=np.float64)
+    return ps, pe
+
+
+def nll_batch(em, lengths, trans, dur, K: int, gold_labels, gold_seg_start, grad_nll=None,
+              proj_start=None, proj_end=None):
     """``nll_sequence`` for every b, packed with the ABI's conventions (zeros at
     t >= L; grad_trans and grad_dur summed over the batch)."""
     em = np.asarray(em)
@@ -326,51 +368,64 @@ def nll_batch(em, lengths, trans, dur, K: int, gold_labels, gold_seg_start, grad
     g = np.ones(B) if grad_nll is None else np.asarray(grad_nll, dtype=np.float64)
     out = {"nll": np.zeros(B), "score": np.zeros(B), "logZ": np.zeros(B),
            "grad_em": np.zeros((B, T, C)), "grad_trans": np.zeros((C, C)),
-           "grad_dur": np.zeros(np.asarray(dur).shape)}
+           "grad_dur": np.zeros(np.asarray(dur).shape),
+           "grad_proj_start": np.zeros((B, T, C)), "grad_proj_end": np.zeros((B, T, C))}
     for b in range(B):
         L = int(lengths[b])
+        proj = _proj_of(proj_start, proj_end, b, L, C)
         r = nll_sequence(em[b], L, trans, dur, K, gold_labels[b, :L], gold_seg_start[b, :L],
-                         float(g[b]))
+                         float(g[b]), proj)
         out["nll"][b], out["score"][b], out["logZ"][b] = r["nll"], r["score"], r["logZ"]
         out["grad_em"][b, :L] = r["grad_em"]
+        if proj is not None:
+            out["grad_proj_start"][b, :L] = r["grad_proj_start"]
+            out["grad_proj_end"][b, :L] = r["grad_proj_end"]
         out["grad_trans"] += r["grad_trans"]
         out["grad_dur"] += r["grad_dur"]
     return out
 
 
 def sequence(em_b, L: int, trans, dur, K: int, g: float = 1.0, *, want_viterbi=True,
-             want_grads=True):
+             want_grads=True, proj=None):
     """Everything for one sequence (fp64): log Z, mu, grad_em (with the
     centring in the function, reading 6), grad_trans, grad_dur scaled by the
-    upstream gradient g, and the Viterbi decode."""
+    upstream gradient g, and the Viterbi decode.  With proj = (P_start [L, C],
+    P_end [L, C]) the projections enter every segment (reading 9) and the
+    gradients include grad_proj_start / grad_proj_end (g times the start / end
+    marginals); ``boundary`` [L] is the probability that a segment starts at t."""
     _, S = centered_prefix(em_b, L)
-    alpha, logZ = forward(S, trans, dur, K, L)
+    alpha, logZ = forward(S, trans, dur, K, L, proj)
     out = {"logZ": logZ, "S": S}
     if want_grads:
-        beta = backward(S, trans, dur, K, L)
-        post = posteriors(S, trans, dur, K, L, alpha, beta, logZ)
+        beta = backward(S, trans, dur, K, L, proj)
+        post = posteriors(S, trans, dur, K, L, alpha, beta, logZ, proj)
         mu = post["mu"]
         out.update(mu=mu, grad_em=g * (mu - mu.mean(axis=0, keepdims=True)),
                    grad_trans=g * post["grad_trans"], grad_dur=g * post["grad_dur"],
-                   dS=post["dS"], logZ_backward=float(beta[0, S.shape[1]]))
+                   dS=post["dS"], logZ_backward=float(beta[0, S.shape[1]]),
+                   grad_proj_start=g * post["start"][:L], grad_proj_end=g * post["end"][1:],
+                   boundary=post["start"][:L].sum(axis=1))
     if want_viterbi:
-        out["viterbi"] = viterbi(S, trans, dur, K, L)
+        out["viterbi"] = viterbi(S, trans, dur, K, L, proj)
     return out
 
 
 def _sequence_job(args):
-    return sequence(*args[:5], g=args[5], want_viterbi=args[6], want_grads=args[7])
+    return sequence(*args[:5], g=args[5], want_viterbi=args[6], want_grads=args[7],
+                    proj=args[8])
 
 
 def batch(em, lengths, trans, dur, K: int, grad_log_z=None, *, want_viterbi=True,
-          want_grads=True, workers: int = 1):
+          want_grads=True, workers: int = 1, proj_start=None, proj_end=None):
     """Run ``sequence`` for every b and pack the results into padded arrays
     with the ABI's conventions (zeros / -1 at t >= L).  grad_trans and grad_dur
-    are summed over the batch."""
+    are summed over the batch.  proj_start / proj_end: [B, T, C] or None
+    (zeros)."""
     em = np.asarray(em)
     B, T, C = em.shape
     g = np.ones(B) if grad_log_z is None else np.asarray(grad_log_z, dtype=np.float64)
-    jobs = [(em[b], int(lengths[b]), trans, dur, K, float(g[b]), want_viterbi, want_grads)
+    jobs = [(em[b], int(lengths[b]), trans, dur, K, float(g[b]), want_viterbi, want_grads,
+             _proj_of(proj_start, proj_end, b, int(lengths[b]), C))
             for b in range(B)]
     if workers > 1 and B > 1:
         import multiprocessing as mp
@@ -382,11 +437,17 @@ def batch(em, lengths, trans, dur, K: int, grad_log_z=None, *, want_viterbi=True
     if want_grads:
         mu = np.zeros((B, T, C))
         ge = np.zeros((B, T, C))
+        gps = np.zeros((B, T, C))
+        gpe = np.zeros((B, T, C))
+        bnd = np.zeros((B, T))
         for b, r in enumerate(res):
             L = int(lengths[b])
             mu[b, :L] = r["mu"]
             ge[b, :L] = r["grad_em"]
-        out.update(mu=mu, grad_em=ge,
+            gps[b, :L] = r["grad_proj_start"]
+            gpe[b, :L] = r["grad_proj_end"]
+            bnd[b, :L] = r["boundary"]
+        out.update(mu=mu, grad_em=ge, grad_proj_start=gps, grad_proj_end=gpe, boundary=bnd,
                    grad_trans=sum(r["grad_trans"] for r in res),
                    grad_dur=sum(r["grad_dur"] for r in res),
                    logZ_backward=np.array([r["logZ_backward"] for r in res]))

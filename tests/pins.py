@@ -56,23 +56,33 @@ def centred_emissions(em_b, L):
     return [[float(em_b[t][c]) - nu[c] for c in range(C)] for t in range(L)]
 
 
-def brute_force(em_b, L: int, trans, dur, K: int):
+def _proj_rows(proj, L, C):
+    if proj is None:
+        z = [[0.0] * C for _ in range(L)]
+        return z, z
+    return ([[float(v) for v in row] for row in proj[0][:L]],
+            [[float(v) for v in row] for row in proj[1][:L]])
+
+
+def brute_force(em_b, L: int, trans, dur, K: int, proj=None):
     """Enumerate every segmentation of [0, L) (lengths <= K, C labels, no
     transition into the first segment).  Returns log Z, posterior expectations
     (mu, grad_dur, grad_trans, start / end marginals) and the best and
-    second-best scores with the best segmentation."""
+    second-best scores with the best segmentation.  proj = (P_start, P_end):
+    a segment [s, s+k) of label c also scores P_start[s][c] + P_end[s+k-1][c]."""
     x = centred_emissions(em_b, L)
     C = len(x[0])
     trans = np.asarray(trans, dtype=np.float64)
     dur = np.asarray(dur, dtype=np.float64)
+    ps, pe = _proj_rows(proj, L, C)
     scores_all = []
     records = []
     for comp in compositions(L, K):
         m = len(comp)
         starts = [sum(comp[:i]) for i in range(m)]
         # content of segment i with label c, summed position by position
-        cont = np.array([[sum(x[u][c] for u in range(s, s + k)) for c in range(C)]
-                         for s, k in zip(starts, comp)])                 # [m, C]
+        cont = np.array([[sum(x[u][c] for u in range(s, s + k)) + ps[s][c] + pe[s + k - 1][c]
+                          for c in range(C)] for s, k in zip(starts, comp)])   # [m, C]
         labs = np.array(list(itertools.product(range(C), repeat=m)))     # [C^m, m]
         sc = np.zeros(len(labs))
         for i, k in enumerate(comp):
@@ -121,13 +131,14 @@ def brute_force(em_b, L: int, trans, dur, K: int):
             "labels": labels, "seg_start": seg, "n": int(flat.size)}
 
 
-def brute_force_nll(em_b, L: int, trans, dur, K: int, labels, seg_start) -> float:
+def brute_force_nll(em_b, L: int, trans, dur, K: int, labels, seg_start, proj=None) -> float:
     """-log P(y*) of the segmentation given by (labels, seg_start): every
     segmentation is enumerated and scored position by position (centred emissions
-    summed over each segment, no prefix sums), and the gold one is picked out by its
-    segments."""
+    summed over each segment, no prefix sums, plus the projections of its first and
+    last position), and the gold one is picked out by its segments."""
     x = centred_emissions(em_b, L)
     C = len(x[0])
+    ps, pe = _proj_rows(proj, L, C)
     trans = np.asarray(trans, dtype=np.float64)
     dur = np.asarray(dur, dtype=np.float64)
     starts = [t for t in range(L) if seg_start[t]]
@@ -140,6 +151,7 @@ def brute_force_nll(em_b, L: int, trans, dur, K: int, labels, seg_start) -> floa
             sc = 0.0
             for i, (s, k) in enumerate(zip(st, comp)):
                 sc += sum(x[u][labs[i]] for u in range(s, s + k)) + dur[k - 1, labs[i]]
+                sc += ps[s][labs[i]] + pe[s + k - 1][labs[i]]
                 if i > 0:
                     sc += trans[labs[i - 1], labs[i]]
             scores.append(sc)

@@ -282,19 +282,22 @@ def test_nll_finite_differences():
         np.testing.assert_allclose(r[key], fd, atol=1e-7, err_msg=key)
 
 
-def _mut_gold_no_trans(labels, seg_start, L, K, C, _orig=osc.gold_features):
-    ind, dc, tc = _orig(labels, seg_start, L, K, C)
-    return ind, dc, np.zeros_like(tc)              # transitions of y* not counted
+def _mut_gold_no_trans(labels, seg_start, L, K, C, _orig=osc.gold_features, **kw):
+    f = list(_orig(labels, seg_start, L, K, C, **kw))
+    f[2] = np.zeros_like(f[2])                     # transitions of y* not counted
+    return tuple(f)
 
 
-def _mut_gold_dur_index(labels, seg_start, L, K, C, _orig=osc.gold_features):
-    ind, dc, tc = _orig(labels, seg_start, L, K, C)
-    return ind, np.vstack([dc[1:], dc[:1]]), tc    # length k counted as k - 1
+def _mut_gold_dur_index(labels, seg_start, L, K, C, _orig=osc.gold_features, **kw):
+    f = list(_orig(labels, seg_start, L, K, C, **kw))
+    f[1] = np.vstack([f[1][1:], f[1][:1]])         # length k counted as k - 1
+    return tuple(f)
 
 
-def _mut_gold_extent(labels, seg_start, L, K, C, _orig=osc.gold_features):
-    ind, dc, tc = _orig(labels, seg_start, L, K, C)
-    return np.roll(ind, 1, axis=0), dc, tc         # segment extents off by one position
+def _mut_gold_extent(labels, seg_start, L, K, C, _orig=osc.gold_features, **kw):
+    f = list(_orig(labels, seg_start, L, K, C, **kw))
+    f[0] = np.roll(f[0], 1, axis=0)                # segment extents off by one position
+    return tuple(f)
 
 
 @pytest.mark.parametrize("name,fn", [
@@ -326,21 +329,21 @@ def test_nll_pins_catch_planted_mistakes(monkeypatch, name, fn):
 # --------------------------------------------------------------------------- planted mistakes
 
 
-def _mut_transpose(S, trans, dur, K, L, s_lo, s_hi, _orig=osc.edge_potentials):
-    return _orig(S, np.asarray(trans).T, dur, K, L, s_lo, s_hi)
+def _mut_transpose(S, trans, dur, K, L, s_lo, s_hi, proj=None, _orig=osc.edge_potentials):
+    return _orig(S, np.asarray(trans).T, dur, K, L, s_lo, s_hi, proj)
 
 
-def _mut_dur_shift(S, trans, dur, K, L, s_lo, s_hi, _orig=osc.edge_potentials):
+def _mut_dur_shift(S, trans, dur, K, L, s_lo, s_hi, proj=None, _orig=osc.edge_potentials):
     d = np.vstack([np.asarray(dur)[1:], np.zeros((1, np.asarray(dur).shape[1]))])
-    return _orig(S, trans, d, K, L, s_lo, s_hi)
+    return _orig(S, trans, d, K, L, s_lo, s_hi, proj)
 
 
-def _mut_drop_dur(S, trans, dur, K, L, s_lo, s_hi, _orig=osc.edge_potentials):
-    return _orig(S, trans, np.zeros_like(dur), K, L, s_lo, s_hi)
+def _mut_drop_dur(S, trans, dur, K, L, s_lo, s_hi, proj=None, _orig=osc.edge_potentials):
+    return _orig(S, trans, np.zeros_like(dur), K, L, s_lo, s_hi, proj)
 
 
-def _mut_sign(S, trans, dur, K, L, s_lo, s_hi, _orig=osc.edge_potentials):
-    return _orig(-S, trans, dur, K, L, s_lo, s_hi)
+def _mut_sign(S, trans, dur, K, L, s_lo, s_hi, proj=None, _orig=osc.edge_potentials):
+    return _orig(-S, trans, dur, K, L, s_lo, s_hi, proj)
 
 
 def _mut_start_trans(trans, _orig=osc._trans_with_start):
@@ -370,4 +373,165 @@ def test_pins_catch_planted_mistakes(monkeypatch, name, attr, fn):
     bad = oracle.sequence(em, L, trans, dur, K)
     err = max(abs(bad["logZ"] - bf["logZ"]), np.abs(bad["mu"] - bf["mu"]).max(),
               np.abs(bad["grad_trans"] - bf["grad_trans"]).max())
+    assert err > 1e-3, f"pin missed planted mistake: {name}"
+
+
+# --------------------------------------------------------------------------- boundary projections
+
+
+def _proj(seed, L, C, sd=0.8):
+    rng = np.random.default_rng(seed)
+    return rng.normal(0, sd, (L, C)), rng.normal(0, sd, (L, C))
+
+
+@pytest.mark.parametrize("seed,L,T,K,C", BF_CASES)
+def test_projections_match_brute_force(seed, L, T, K, C):
+    """Start / end projections (reading 9) against the enumeration, which adds them to
+    each segment's score position by position: log Z, every expectation, the start and
+    end marginals (the projections' gradients), the boundary probability and Viterbi."""
+    em, L, trans, dur, K = _case(seed, L, T, K, C)
+    proj = _proj(seed + 500, L, C)
+    bf = pins.brute_force(em, L, trans, dur, K, proj=proj)
+    r = oracle.sequence(em, L, trans, dur, K, g=1.0, proj=proj)
+    assert abs(r["logZ"] - bf["logZ"]) < 1e-12
+    assert abs(r["logZ_backward"] - bf["logZ"]) < 1e-12
+    np.testing.assert_allclose(r["mu"], bf["mu"], atol=1e-12)
+    np.testing.assert_allclose(r["grad_dur"], bf["grad_dur"], atol=1e-12)
+    np.testing.assert_allclose(r["grad_trans"], bf["grad_trans"], atol=1e-12)
+    np.testing.assert_allclose(r["grad_proj_start"], bf["start"][:L], atol=1e-12)
+    np.testing.assert_allclose(r["grad_proj_end"], bf["end"][1:], atol=1e-12)
+    np.testing.assert_allclose(r["boundary"], bf["start"][:L].sum(axis=1), atol=1e-12)
+    v = r["viterbi"]
+    assert abs(v["score"] - bf["best"]) < 1e-12
+    if bf["best"] - bf["second"] > 1e-9:
+        np.testing.assert_array_equal(v["labels"], bf["labels"])
+        np.testing.assert_array_equal(v["seg_start"], bf["seg_start"])
+    assert abs(oracle.segmentation_score(r["S"], trans, dur, K, v["seg_start"], v["labels"], proj)
+               - v["score"]) < 1e-12
+
+
+@pytest.mark.parametrize("side", [0, 1])
+def test_constant_projection_is_a_duration_shift(side):
+    """P_start[t, c] = x_c for every t (or P_end) adds x_c once per segment of label c,
+    exactly what adding x_c to dur[k-1, c] for every k does."""
+    em, L, trans, dur, K = _case(91, 40, 40, 6, 3)
+    x = np.array([0.7, -1.1, 0.4])
+    proj = [np.zeros((L, 3)), np.zeros((L, 3))]
+    proj[side] = np.tile(x, (L, 1))
+    a = oracle.sequence(em, L, trans, dur, K, proj=tuple(proj))
+    b = oracle.sequence(em, L, trans, dur + x[None, :], K)
+    assert abs(a["logZ"] - b["logZ"]) < 1e-11
+    np.testing.assert_allclose(a["mu"], b["mu"], atol=1e-12)
+    np.testing.assert_allclose(a["grad_dur"], b["grad_dur"], atol=1e-12)
+    np.testing.assert_allclose(a["grad_trans"], b["grad_trans"], atol=1e-12)
+    assert abs(a["viterbi"]["score"] - b["viterbi"]["score"]) < 1e-11
+    np.testing.assert_array_equal(a["viterbi"]["labels"], b["viterbi"]["labels"])
+    # the projection's gradient sums to the expected segment count of each label
+    g = a["grad_proj_start" if side == 0 else "grad_proj_end"]
+    np.testing.assert_allclose(g.sum(axis=0), a["grad_dur"].sum(axis=0), atol=1e-11)
+
+
+def test_k1_projections_are_unary_scores():
+    """K = 1: every position is a segment, so both projections act as unary scores of
+    the textbook linear-chain CRF; every position is a boundary."""
+    em, L, trans, dur, K = _case(92, 30, 30, 1, 4)
+    ps, pe = _proj(93, L, 4)
+    x = np.array(pins.centred_emissions(em, L))
+    lc = pins.linear_chain(x + dur[0][None, :] + ps + pe, trans)
+    r = oracle.sequence(em, L, trans, dur, 1, proj=(ps, pe))
+    assert abs(r["logZ"] - lc["logZ"]) < 1e-11
+    np.testing.assert_allclose(r["mu"], lc["node"], atol=1e-12)
+    np.testing.assert_allclose(r["grad_proj_start"], lc["node"], atol=1e-12)
+    np.testing.assert_allclose(r["grad_proj_end"], lc["node"], atol=1e-12)
+    np.testing.assert_allclose(r["boundary"], 1.0, atol=1e-12)
+    assert abs(r["viterbi"]["score"] - lc["score"]) < 1e-11
+    np.testing.assert_array_equal(r["viterbi"]["labels"], lc["path"])
+
+
+def test_boundary_probability_invariants():
+    """A segment always starts at 0 and one always ends at L - 1; boundary
+    probabilities lie in [0, 1] and sum to the expected number of segments."""
+    em, L, trans, dur, K = _case(94, 120, 120, 15, 4, scale=1.5)
+    ps, pe = _proj(95, L, 4, sd=1.5)
+    r = oracle.sequence(em, L, trans, dur, K, proj=(ps, pe))
+    bnd = r["boundary"]
+    assert abs(bnd[0] - 1.0) < 1e-12
+    assert abs(r["grad_proj_end"][L - 1].sum() - 1.0) < 1e-12
+    assert bnd.min() > -1e-12 and bnd.max() < 1 + 1e-12
+    assert abs(bnd.sum() - r["grad_dur"].sum()) < 1e-9
+    assert abs(r["grad_proj_end"].sum() - r["grad_dur"].sum()) < 1e-9
+    # a position strictly inside every segment that can cover it is no boundary:
+    # forbid starts at t = 5 for every label
+    ps2 = ps.copy()
+    ps2[5] = -np.inf
+    r2 = oracle.sequence(em, L, trans, dur, K, proj=(ps2, pe), want_viterbi=True)
+    assert r2["boundary"][5] == 0.0 and r2["viterbi"]["seg_start"][5] == 0
+
+
+def test_projection_finite_differences():
+    em, L, trans, dur, K = _case(96, 9, 9, 4, 3)
+    ps, pe = _proj(97, L, 3)
+    r = oracle.sequence(em, L, trans, dur, K, g=0.6, proj=(ps, pe), want_viterbi=False)
+    h = 1e-5
+
+    def lz(a, b):
+        _, S = oracle.centered_prefix(em, L)
+        return oracle.forward(S, trans, dur, K, L, (a, b))[1]
+
+    for arr, key, which in ((ps, "grad_proj_start", 0), (pe, "grad_proj_end", 1)):
+        for idx in np.ndindex(*arr.shape):
+            e = np.zeros_like(arr)
+            e[idx] = h
+            up = (ps + e, pe) if which == 0 else (ps, pe + e)
+            dn = (ps - e, pe) if which == 0 else (ps, pe - e)
+            fd = 0.6 * (lz(*up) - lz(*dn)) / (2 * h)
+            assert abs(r[key][idx] - fd) < 1e-8, (key, idx)
+
+
+def test_nll_with_projections_matches_brute_force():
+    em, L, trans, dur, K = _case(98, 6, 6, 3, 2)
+    proj = _proj(99, L, 2)
+    labels, seg = _gold(198, L, 6, K, 2)
+    r = oracle.nll_sequence(em, L, trans, dur, K, labels, seg, 0.8, proj)
+    assert abs(r["nll"] - pins.brute_force_nll(em, L, trans, dur, K, labels, seg, proj)) < 1e-12
+    h = 1e-5
+    for which, key in ((0, "grad_proj_start"), (1, "grad_proj_end")):
+        for idx in np.ndindex(L, 2):
+            e = np.zeros((L, 2))
+            e[idx] = h
+            up = [proj[0], proj[1]]
+            dn = [proj[0], proj[1]]
+            up[which] = proj[which] + e
+            dn[which] = proj[which] - e
+            fd = 0.8 * (pins.brute_force_nll(em, L, trans, dur, K, labels, seg, up)
+                        - pins.brute_force_nll(em, L, trans, dur, K, labels, seg, dn)) / (2 * h)
+            assert abs(r[key][idx] - fd) < 1e-7, (key, idx)
+
+
+def _mut_proj_end_shift(S, trans, dur, K, L, s_lo, s_hi, proj=None, _orig=osc.edge_potentials):
+    ps, pe = proj
+    return _orig(S, trans, dur, K, L, s_lo, s_hi, (ps, np.roll(pe, -1, axis=0)))   # P_end[s+k]
+
+
+def _mut_proj_swap(S, trans, dur, K, L, s_lo, s_hi, proj=None, _orig=osc.edge_potentials):
+    return _orig(S, trans, dur, K, L, s_lo, s_hi, (proj[1], proj[0]))
+
+
+def _mut_proj_drop_start(S, trans, dur, K, L, s_lo, s_hi, proj=None, _orig=osc.edge_potentials):
+    return _orig(S, trans, dur, K, L, s_lo, s_hi, (np.zeros_like(proj[0]), proj[1]))
+
+
+@pytest.mark.parametrize("name,fn", [
+    ("end projection off by one", _mut_proj_end_shift),
+    ("start and end projections swapped", _mut_proj_swap),
+    ("start projection dropped", _mut_proj_drop_start),
+])
+def test_projection_pins_catch_planted_mistakes(monkeypatch, name, fn):
+    em, L, trans, dur, K = _case(101, 6, 6, 3, 3)
+    proj = _proj(102, L, 3)
+    bf = pins.brute_force(em, L, trans, dur, K, proj=proj)
+    monkeypatch.setattr(osc, "edge_potentials", fn)
+    bad = oracle.sequence(em, L, trans, dur, K, proj=proj)
+    err = max(abs(bad["logZ"] - bf["logZ"]), np.abs(bad["grad_proj_start"] - bf["start"][:L]).max(),
+              np.abs(bad["grad_proj_end"] - bf["end"][1:]).max())
     assert err > 1e-3, f"pin missed planted mistake: {name}"
