@@ -150,25 +150,27 @@ def main():
     def step(ev_b=None, ev_v=None):
         if ev_b is None:
             rc = lib.semicrf_backward(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
-                                      dur.data_ptr(), B, T, C, K, args.delta, stream_b,
+                                      dur.data_ptr(), None, None, B, T, C, K, args.delta, stream_b,
                                       ws_b.data_ptr(), nb, None, g_em.data_ptr(), g_tr.data_ptr(),
-                                      g_du.data_ptr(), mu.data_ptr(), lz.data_ptr())
+                                      g_du.data_ptr(), mu.data_ptr(), lz.data_ptr(), None, None,
+                                      None)
         else:
             rc = lib.semicrf_backward_staged(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
-                                             dur.data_ptr(), B, T, C, K, args.delta, stream_b,
-                                             ws_b.data_ptr(), nb, None, g_em.data_ptr(),
+                                             dur.data_ptr(), None, None, B, T, C, K, args.delta,
+                                             stream_b, ws_b.data_ptr(), nb, None, g_em.data_ptr(),
                                              g_tr.data_ptr(), g_du.data_ptr(), mu.data_ptr(),
-                                             lz.data_ptr(), ev_b)
+                                             lz.data_ptr(), None, None, None, ev_b)
         _native.check("semicrf_backward", rc)
         if ev_v is None:
             rc = lib.semicrf_viterbi(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
-                                     dur.data_ptr(), B, T, C, K, stream_v, ws_v.data_ptr(), nv,
-                                     score.data_ptr(), labels.data_ptr(), seg.data_ptr())
+                                     dur.data_ptr(), None, None, B, T, C, K, stream_v,
+                                     ws_v.data_ptr(), nv, score.data_ptr(), labels.data_ptr(),
+                                     seg.data_ptr())
         else:
             rc = lib.semicrf_viterbi_staged(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
-                                            dur.data_ptr(), B, T, C, K, stream_v, ws_v.data_ptr(),
-                                            nv, score.data_ptr(), labels.data_ptr(),
-                                            seg.data_ptr(), ev_v)
+                                            dur.data_ptr(), None, None, B, T, C, K, stream_v,
+                                            ws_v.data_ptr(), nv, score.data_ptr(),
+                                            labels.data_ptr(), seg.data_ptr(), ev_v)
         _native.check("semicrf_viterbi", rc)
 
     torch.cuda.synchronize(d)          # inputs are resident before either stream starts

@@ -92,12 +92,23 @@ size_t semicrf_workspace_bytes(int op, int B, int T, int C, int K, int delta);
 int semicrf_prefix(const float* emissions, const int32_t* lengths, int B, int T, int C,
                    hipStream_t stream, void* workspace, size_t workspace_bytes, double* S);
 
+/* Boundary projections (EN explainer, "2. Methodology", "Boundary Projections": start
+ * and end features computed apart and added to the edge potential).  Every call below
+ * that takes them accepts
+ *   proj_start [B, T, C] float32 or NULL  score of a segment of label c that starts at t
+ *   proj_end   [B, T, C] float32 or NULL  score of a segment of label c whose last
+ *                                         position is t
+ * so a segment [s, e) of label c gains proj_start[b, s, c] + proj_end[b, e-1, c].  NULL
+ * means zeros; values at t >= lengths[b] are ignored; the values must be finite (a large
+ * negative value, e.g. -1e4, effectively forbids a start or end).  They are not centred. */
+
 /* log Z for every sequence: the log-sum-exp of the scores of all segmentations
  * (EN explainer, "2. Methodology", "Streaming Forward-Backward with Ring Buffers",
  * forward pass).  Output: log_z [B] float32. */
 int semicrf_logz(const float* emissions, const int32_t* lengths, const float* trans,
-                 const float* dur, int B, int T, int C, int K, hipStream_t stream,
-                 void* workspace, size_t workspace_bytes, float* log_z);
+                 const float* dur, const float* proj_start, const float* proj_end, int B,
+                 int T, int C, int K, hipStream_t stream, void* workspace,
+                 size_t workspace_bytes, float* log_z);
 
 /* Exact gradients of sum_b grad_log_z[b] * log Z_b (EN explainer, "2. Methodology",
  * backward pass with recomputation from checkpoints every `delta` positions;
@@ -110,35 +121,45 @@ int semicrf_logz(const float* emissions, const int32_t* lengths, const float* tr
  *   marginals      [B, T, C] float32  or NULL: posterior probability that position t
  *                                     lies in a segment of label c (sums to 1 over c)
  *   log_z          [B]       float32  or NULL
+ *   grad_proj_start [B, T, C] float32 or NULL: d/d proj_start, g_b times the probability
+ *                                     that a segment of label c starts at t
+ *   grad_proj_end   [B, T, C] float32 or NULL: d/d proj_end, g_b times the probability
+ *                                     that a segment of label c has its last position at t
+ *   boundary       [B, T]    float32  or NULL: probability that a segment starts at t
+ *                                     (1 at t = 0; EN explainer, "4. Results and
+ *                                     Benchmarks": boundary probabilities)
  * delta: checkpoint interval (0 = ceil(sqrt(T*K))); results do not depend on it
  * beyond rounding. */
 int semicrf_backward(const float* emissions, const int32_t* lengths, const float* trans,
-                     const float* dur, int B, int T, int C, int K, int delta,
-                     hipStream_t stream, void* workspace, size_t workspace_bytes,
-                     const float* grad_log_z, float* grad_emissions, float* grad_trans,
-                     float* grad_dur, float* marginals, float* log_z);
+                     const float* dur, const float* proj_start, const float* proj_end, int B,
+                     int T, int C, int K, int delta, hipStream_t stream, void* workspace,
+                     size_t workspace_bytes, const float* grad_log_z, float* grad_emissions,
+                     float* grad_trans, float* grad_dur, float* marginals, float* log_z,
+                     float* grad_proj_start, float* grad_proj_end, float* boundary);
 
 /* Training loss of gold segmentations and its gradients.  nll[b] = log Z_b - score_b(y*),
  * the negative log-probability of the gold segmentation y* (the training loss of the
  * pages' convergence check, EN explainer, "4. Results and Benchmarks"); score sums, over
- * the gold segments [s, e) of label c, S[e,c] - S[s,c] + dur[e-s-1, c] and, between
- * consecutive segments, trans[c', c] (the same centred potential as log Z, "2.
- * Methodology").  Inputs as semicrf_backward plus
+ * the gold segments [s, e) of label c, S[e,c] - S[s,c] + dur[e-s-1, c] (+ the
+ * projections) and, between consecutive segments, trans[c', c] (the same centred
+ * potential as log Z, "2. Methodology").  Inputs as semicrf_backward plus
  *   gold_labels    [B, T] int32  label of every position t < lengths[b]
  *   gold_seg_start [B, T] uint8  1 at each gold segment's first position (t = 0 must be 1)
  *   grad_nll       [B] float32 or NULL for all ones
  * Outputs: nll [B] float32, and the gradients of sum_b grad_nll[b] * nll[b] in
- * grad_emissions [B, T, C], grad_trans [C, C], grad_dur [K, C] (expected minus gold feature
- * counts; the emission gradient includes the centring; 0 at padding).  A gold segmentation
+ * grad_emissions [B, T, C], grad_trans [C, C], grad_dur [K, C] and, each optional (NULL),
+ * grad_proj_start / grad_proj_end [B, T, C] (expected minus gold feature counts; the
+ * emission gradient includes the centring; 0 at padding).  A gold segmentation
  * with a segment longer than K, a label outside [0, C), a label change inside a segment or
  * no start at t = 0 gives NaN for that sequence and raises the status flag, like an
  * invalid length; its gold counts are then left out of the gradients, which keep only
  * its log Z half.  Workspace: semicrf_workspace_bytes(SEMICRF_OP_BACKWARD, ...). */
 int semicrf_nll(const float* emissions, const int32_t* lengths, const float* trans,
-                const float* dur, const int32_t* gold_labels, const uint8_t* gold_seg_start,
-                int B, int T, int C, int K, int delta, hipStream_t stream, void* workspace,
-                size_t workspace_bytes, const float* grad_nll, float* nll,
-                float* grad_emissions, float* grad_trans, float* grad_dur);
+                const float* dur, const float* proj_start, const float* proj_end,
+                const int32_t* gold_labels, const uint8_t* gold_seg_start, int B, int T, int C,
+                int K, int delta, hipStream_t stream, void* workspace, size_t workspace_bytes,
+                const float* grad_nll, float* nll, float* grad_emissions, float* grad_trans,
+                float* grad_dur, float* grad_proj_start, float* grad_proj_end);
 
 /* Max-plus decode of the best segmentation (the Viterbi counterpart of the forward
  * pass).  Each max-plus step breaks ties toward the shortest segment, then the lowest
@@ -152,9 +173,10 @@ int semicrf_nll(const float* emissions, const int32_t* lengths, const float* tra
  *   labels     [B, T] int32    label of every position, -1 at t >= lengths[b]
  *   seg_start  [B, T] uint8    1 where a segment starts, else 0 */
 int semicrf_viterbi(const float* emissions, const int32_t* lengths, const float* trans,
-                    const float* dur, int B, int T, int C, int K, hipStream_t stream,
-                    void* workspace, size_t workspace_bytes, float* best_score,
-                    int32_t* labels, uint8_t* seg_start);
+                    const float* dur, const float* proj_start, const float* proj_end, int B,
+                    int T, int C, int K, hipStream_t stream, void* workspace,
+                    size_t workspace_bytes, float* best_score, int32_t* labels,
+                    uint8_t* seg_start);
 
 /* Stage-timed variants, for profiling.  Identical results to the calls above; in
  * addition, events[i] (created by the caller with hipEventCreate) is recorded on
@@ -170,18 +192,21 @@ int semicrf_viterbi(const float* emissions, const int32_t* lengths, const float*
 #define SEMICRF_BACKWARD_STAGES 5
 #define SEMICRF_VITERBI_STAGES 3
 int semicrf_logz_staged(const float* emissions, const int32_t* lengths, const float* trans,
-                        const float* dur, int B, int T, int C, int K, hipStream_t stream,
-                        void* workspace, size_t workspace_bytes, float* log_z,
-                        hipEvent_t* events);
+                        const float* dur, const float* proj_start, const float* proj_end, int B,
+                        int T, int C, int K, hipStream_t stream, void* workspace,
+                        size_t workspace_bytes, float* log_z, hipEvent_t* events);
 int semicrf_backward_staged(const float* emissions, const int32_t* lengths, const float* trans,
-                            const float* dur, int B, int T, int C, int K, int delta,
-                            hipStream_t stream, void* workspace, size_t workspace_bytes,
-                            const float* grad_log_z, float* grad_emissions, float* grad_trans,
-                            float* grad_dur, float* marginals, float* log_z, hipEvent_t* events);
+                            const float* dur, const float* proj_start, const float* proj_end,
+                            int B, int T, int C, int K, int delta, hipStream_t stream,
+                            void* workspace, size_t workspace_bytes, const float* grad_log_z,
+                            float* grad_emissions, float* grad_trans, float* grad_dur,
+                            float* marginals, float* log_z, float* grad_proj_start,
+                            float* grad_proj_end, float* boundary, hipEvent_t* events);
 int semicrf_viterbi_staged(const float* emissions, const int32_t* lengths, const float* trans,
-                           const float* dur, int B, int T, int C, int K, hipStream_t stream,
-                           void* workspace, size_t workspace_bytes, float* best_score,
-                           int32_t* labels, uint8_t* seg_start, hipEvent_t* events);
+                           const float* dur, const float* proj_start, const float* proj_end,
+                           int B, int T, int C, int K, hipStream_t stream, void* workspace,
+                           size_t workspace_bytes, float* best_score, int32_t* labels,
+                           uint8_t* seg_start, hipEvent_t* events);
 
 /* Synchronously reads the device status flag left in `workspace` by the last call
  * that used it (after waiting for `stream`).  SEMICRF_OK, SEMICRF_ERR_INVALID if a

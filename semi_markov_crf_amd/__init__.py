@@ -6,12 +6,15 @@ device memory and the current stream) and call ``libsemicrf.so``.  Every step of
 the computation runs in the library's HIP kernels.
 
     logz(em, lengths, trans, dur)            -> log Z  [B]
-    backward(em, lengths, trans, dur, ...)   -> gradients, marginals, log Z
+    backward(em, lengths, trans, dur, ...)   -> gradients, marginals, log Z, boundaries
     viterbi(em, lengths, trans, dur)         -> best score, labels, segment starts
+    nll(em, lengths, trans, dur, gold...)    -> training loss of gold segmentations
     log_partition(em, lengths, trans, dur)   -> log Z with autograd support
 
 Shapes: em [B, T, C] float32, lengths [B] int32, trans [C, C] float32 (row =
-previous label), dur [K, C] float32 (row k-1 scores length k).
+previous label), dur [K, C] float32 (row k-1 scores length k).  Every call also
+takes optional boundary projections proj_start / proj_end [B, T, C] float32: a
+segment [s, e) of label c gains proj_start[b, s, c] + proj_end[b, e-1, c].
 """
 
 from __future__ import annotations
@@ -21,7 +24,7 @@ import torch
 from . import _native
 from ._native import OP_BACKWARD, OP_LOGZ, OP_PREFIX, OP_VITERBI, SemiCRFError
 
-__all__ = ["prefix", "logz", "backward", "viterbi", "log_partition", "workspace_bytes",
+__all__ = ["prefix", "logz", "backward", "viterbi", "nll", "log_partition", "workspace_bytes",
            "checkpoint_interval", "read_status", "SemiCRFError",
            "OP_LOGZ", "OP_BACKWARD", "OP_VITERBI", "OP_PREFIX"]
 
@@ -97,25 +100,50 @@ def _maybe_check(workspace, check_status, fn):
         _native.check(fn, read_status(workspace))
 
 
-def logz(em, lengths, trans, dur, *, workspace=None, check_status=False) -> torch.Tensor:
+def _proj(em, proj_start, proj_end):
+    """Checked projection pointers (None for an absent array) and the tensors to keep."""
+    out = []
+    for name, x in (("proj_start", proj_start), ("proj_end", proj_end)):
+        if x is None:
+            out.append(None)
+            continue
+        if x.shape != em.shape or x.dtype != torch.float32 or x.device != em.device:
+            raise ValueError(f"{name} must be a float32 tensor shaped like the emissions, on "
+                             f"their device")
+        out.append(x.contiguous())
+    return out
+
+
+def _ptr(x):
+    return None if x is None else x.data_ptr()
+
+
+def logz(em, lengths, trans, dur, *, proj_start=None, proj_end=None, workspace=None,
+         check_status=False) -> torch.Tensor:
     B, T, C, K = _check_inputs(em, lengths, trans, dur)
+    ps, pe = _proj(em, proj_start, proj_end)
     ws, n = _workspace(OP_LOGZ, B, T, C, K, 0, em.device, workspace)
     out = torch.empty(B, dtype=torch.float32, device=em.device)
     rc = _native.load().semicrf_logz(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
-                                     dur.data_ptr(), B, T, C, K, _stream(em.device),
-                                     ws.data_ptr(), n, out.data_ptr())
+                                     dur.data_ptr(), _ptr(ps), _ptr(pe), B, T, C, K,
+                                     _stream(em.device), ws.data_ptr(), n, out.data_ptr())
     _native.check("semicrf_logz", rc)
     _maybe_check(ws, check_status, "semicrf_logz")
     return out
 
 
-def backward(em, lengths, trans, dur, *, grad_log_z=None, delta=0, want_marginals=True,
-             workspace=None, check_status=False) -> dict:
+def backward(em, lengths, trans, dur, *, proj_start=None, proj_end=None, grad_log_z=None,
+             delta=0, want_marginals=True, want_boundaries=False, workspace=None,
+             check_status=False) -> dict:
     """Gradients of sum_b grad_log_z[b] * log Z_b (all ones when None).  Returns a dict
     with grad_em [B,T,C], grad_trans [C,C], grad_dur [K,C], marginals [B,T,C] (or
-    None) and log_z [B]."""
+    None) and log_z [B]; with want_boundaries (or projections given) also
+    grad_proj_start / grad_proj_end [B,T,C] and boundary [B,T], the probability that a
+    segment starts at t."""
     B, T, C, K = _check_inputs(em, lengths, trans, dur)
     dev = em.device
+    ps, pe = _proj(em, proj_start, proj_end)
+    want_b = want_boundaries or ps is not None or pe is not None
     if grad_log_z is not None:
         if grad_log_z.shape != (B,) or grad_log_z.dtype != torch.float32 or grad_log_z.device != dev:
             raise ValueError("grad_log_z must be a float32 [B] tensor on the emissions' device")
@@ -126,26 +154,34 @@ def backward(em, lengths, trans, dur, *, grad_log_z=None, delta=0, want_marginal
     grad_dur = torch.empty_like(dur)
     mu = torch.empty_like(em) if want_marginals else None
     lz = torch.empty(B, dtype=torch.float32, device=dev)
+    gps = torch.empty_like(em) if want_b else None
+    gpe = torch.empty_like(em) if want_b else None
+    bnd = torch.empty((B, T), dtype=torch.float32, device=dev) if want_b else None
     rc = _native.load().semicrf_backward(
-        em.data_ptr(), lengths.data_ptr(), trans.data_ptr(), dur.data_ptr(), B, T, C, K, delta,
-        _stream(dev), ws.data_ptr(), n,
-        None if grad_log_z is None else grad_log_z.data_ptr(),
-        grad_em.data_ptr(), grad_trans.data_ptr(), grad_dur.data_ptr(),
-        None if mu is None else mu.data_ptr(), lz.data_ptr())
+        em.data_ptr(), lengths.data_ptr(), trans.data_ptr(), dur.data_ptr(), _ptr(ps), _ptr(pe),
+        B, T, C, K, delta, _stream(dev), ws.data_ptr(), n, _ptr(grad_log_z),
+        grad_em.data_ptr(), grad_trans.data_ptr(), grad_dur.data_ptr(), _ptr(mu),
+        lz.data_ptr(), _ptr(gps), _ptr(gpe), _ptr(bnd))
     _native.check("semicrf_backward", rc)
     _maybe_check(ws, check_status, "semicrf_backward")
-    return {"grad_em": grad_em, "grad_trans": grad_trans, "grad_dur": grad_dur,
-            "marginals": mu, "log_z": lz}
+    out = {"grad_em": grad_em, "grad_trans": grad_trans, "grad_dur": grad_dur,
+           "marginals": mu, "log_z": lz}
+    if want_b:
+        out.update(grad_proj_start=gps, grad_proj_end=gpe, boundary=bnd)
+    return out
 
 
-def nll(em, lengths, trans, dur, gold_labels, gold_seg_start, *, grad_nll=None, delta=0,
-        workspace=None, check_status=False) -> dict:
+def nll(em, lengths, trans, dur, gold_labels, gold_seg_start, *, proj_start=None,
+        proj_end=None, grad_nll=None, delta=0, workspace=None, check_status=False) -> dict:
     """Training loss of gold segmentations, nll[b] = log Z_b - score_b(y*), and the
     gradients of sum_b grad_nll[b] * nll[b] (all ones when None).  gold_labels int32
     [B,T] and gold_seg_start uint8 [B,T] on the emissions' device.  Returns a dict with
-    nll [B], grad_em [B,T,C], grad_trans [C,C], grad_dur [K,C]."""
+    nll [B], grad_em [B,T,C], grad_trans [C,C], grad_dur [K,C] and, with projections,
+    grad_proj_start / grad_proj_end [B,T,C]."""
     B, T, C, K = _check_inputs(em, lengths, trans, dur)
     dev = em.device
+    ps, pe = _proj(em, proj_start, proj_end)
+    want_p = ps is not None or pe is not None
     for name, x, dt in (("gold_labels", gold_labels, torch.int32),
                         ("gold_seg_start", gold_seg_start, torch.uint8)):
         if x.shape != (B, T) or x.dtype != dt or x.device != dev:
@@ -160,27 +196,35 @@ def nll(em, lengths, trans, dur, gold_labels, gold_seg_start, *, grad_nll=None, 
     grad_em = torch.empty_like(em)
     grad_trans = torch.empty_like(trans)
     grad_dur = torch.empty_like(dur)
+    gps = torch.empty_like(em) if want_p else None
+    gpe = torch.empty_like(em) if want_p else None
     rc = _native.load().semicrf_nll(
-        em.data_ptr(), lengths.data_ptr(), trans.data_ptr(), dur.data_ptr(),
+        em.data_ptr(), lengths.data_ptr(), trans.data_ptr(), dur.data_ptr(), _ptr(ps), _ptr(pe),
         gold_labels.data_ptr(), gold_seg_start.data_ptr(), B, T, C, K, delta, _stream(dev),
-        ws.data_ptr(), n, None if grad_nll is None else grad_nll.data_ptr(), out.data_ptr(),
-        grad_em.data_ptr(), grad_trans.data_ptr(), grad_dur.data_ptr())
+        ws.data_ptr(), n, _ptr(grad_nll), out.data_ptr(), grad_em.data_ptr(),
+        grad_trans.data_ptr(), grad_dur.data_ptr(), _ptr(gps), _ptr(gpe))
     _native.check("semicrf_nll", rc)
     _maybe_check(ws, check_status, "semicrf_nll")
-    return {"nll": out, "grad_em": grad_em, "grad_trans": grad_trans, "grad_dur": grad_dur}
+    res = {"nll": out, "grad_em": grad_em, "grad_trans": grad_trans, "grad_dur": grad_dur}
+    if want_p:
+        res.update(grad_proj_start=gps, grad_proj_end=gpe)
+    return res
 
 
-def viterbi(em, lengths, trans, dur, *, workspace=None, check_status=False):
+def viterbi(em, lengths, trans, dur, *, proj_start=None, proj_end=None, workspace=None,
+            check_status=False):
     """Returns (best_score [B] float32, labels [B,T] int32, seg_start [B,T] uint8)."""
     B, T, C, K = _check_inputs(em, lengths, trans, dur)
     dev = em.device
+    ps, pe = _proj(em, proj_start, proj_end)
     ws, n = _workspace(OP_VITERBI, B, T, C, K, 0, dev, workspace)
     score = torch.empty(B, dtype=torch.float32, device=dev)
     labels = torch.empty((B, T), dtype=torch.int32, device=dev)
     seg = torch.empty((B, T), dtype=torch.uint8, device=dev)
     rc = _native.load().semicrf_viterbi(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
-                                        dur.data_ptr(), B, T, C, K, _stream(dev), ws.data_ptr(), n,
-                                        score.data_ptr(), labels.data_ptr(), seg.data_ptr())
+                                        dur.data_ptr(), _ptr(ps), _ptr(pe), B, T, C, K,
+                                        _stream(dev), ws.data_ptr(), n, score.data_ptr(),
+                                        labels.data_ptr(), seg.data_ptr())
     _native.check("semicrf_viterbi", rc)
     _maybe_check(ws, check_status, "semicrf_viterbi")
     return score, labels, seg
@@ -188,19 +232,23 @@ def viterbi(em, lengths, trans, dur, *, workspace=None, check_status=False):
 
 class _LogPartition(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, em, lengths, trans, dur, delta):
-        ctx.save_for_backward(em, lengths, trans, dur)
+    def forward(ctx, em, lengths, trans, dur, proj_start, proj_end, delta):
+        ctx.save_for_backward(em, lengths, trans, dur, proj_start, proj_end)
         ctx.delta = delta
-        return logz(em, lengths, trans, dur)
+        return logz(em, lengths, trans, dur, proj_start=proj_start, proj_end=proj_end)
 
     @staticmethod
     def backward(ctx, g):
-        em, lengths, trans, dur = ctx.saved_tensors
-        out = backward(em, lengths, trans, dur, grad_log_z=g.contiguous().float(),
-                       delta=ctx.delta, want_marginals=False)
-        return out["grad_em"], None, out["grad_trans"], out["grad_dur"], None
+        em, lengths, trans, dur, ps, pe = ctx.saved_tensors
+        out = backward(em, lengths, trans, dur, proj_start=ps, proj_end=pe,
+                       grad_log_z=g.contiguous().float(), delta=ctx.delta, want_marginals=False)
+        return (out["grad_em"], None, out["grad_trans"], out["grad_dur"],
+                out.get("grad_proj_start") if ps is not None else None,
+                out.get("grad_proj_end") if pe is not None else None, None)
 
 
-def log_partition(em, lengths, trans, dur, delta: int = 0) -> torch.Tensor:
-    """log Z [B] as a differentiable op (a drop-in CRF-layer loss term)."""
-    return _LogPartition.apply(em, lengths, trans, dur, delta)
+def log_partition(em, lengths, trans, dur, proj_start=None, proj_end=None,
+                  delta: int = 0) -> torch.Tensor:
+    """log Z [B] as a differentiable op (a drop-in CRF-layer loss term); the optional
+    boundary projections receive gradients too."""
+    return _LogPartition.apply(em, lengths, trans, dur, proj_start, proj_end, delta)

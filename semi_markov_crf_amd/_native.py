@@ -25,22 +25,25 @@ SIGNATURES = {
     "semicrf_status_string": (ctypes.c_char_p, [_c_int]),
     "semicrf_checkpoint_interval": (_c_int, [_c_int, _c_int, _c_int]),
     "semicrf_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
-    "semicrf_logz": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
-                              _c_size, _vp]),
-    "semicrf_backward": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                  _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "semicrf_viterbi": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
-                                 _c_size, _vp, _vp, _vp]),
-    "semicrf_nll": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
-                             _c_int, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp]),
+    "semicrf_logz": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                              _vp, _vp, _c_size, _vp]),
+    "semicrf_backward": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                  _c_int, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _vp]),
+    "semicrf_viterbi": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                 _vp, _vp, _c_size, _vp, _vp, _vp]),
+    "semicrf_nll": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                             _c_int, _c_int, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp]),
     "semicrf_read_status": (_c_int, [_vp, _vp]),
     "semicrf_prefix": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp]),
-    "semicrf_logz_staged": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
-                                     _c_size, _vp, _vp]),
-    "semicrf_backward_staged": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
-                                         _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
-    "semicrf_viterbi_staged": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
-                                        _c_size, _vp, _vp, _vp, _vp]),
+    "semicrf_logz_staged": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                                     _c_int, _vp, _vp, _c_size, _vp, _vp]),
+    "semicrf_backward_staged": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                                         _c_int, _c_int, _vp, _vp, _c_size, _vp, _vp, _vp, _vp,
+                                         _vp, _vp, _vp, _vp, _vp, _vp]),
+    "semicrf_viterbi_staged": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                                        _c_int, _vp, _vp, _c_size, _vp, _vp, _vp, _vp]),
 }
 STAGES = {"logz": 2, "backward": 5, "viterbi": 3}
 

@@ -21,7 +21,7 @@ struct Layout {
     size_t logz = 0, logzb = 0;
     size_t ckR = 0, ckB = 0, ckM = 0, ckH = 0, XF = 0, AF = 0, XB = 0, AB = 0;
     size_t Dn = 0, dnt = 0, dno = 0, mu = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0, rps = 0;
-    size_t gcnt = 0, gpart = 0;
+    size_t gcnt = 0, gpart = 0, pst = 0, pen = 0;
     size_t bp = 0, vscore = 0, vcstar = 0, vwin = 0, split = 0, btr = 0, bent = 0;
     size_t total = 0;
 };
@@ -95,6 +95,9 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         lo.pd = m.take(sizeof(double) * B * lo.ntm * K * C);
         lo.pt = m.take(sizeof(double) * B * lo.ntm * C * C);
         lo.rps = m.take(sizeof(double) * reduce_scratch_doubles(C, K));
+        // raw start / end masses for the boundary outputs
+        lo.pst = m.take(sizeof(float) * (size_t)B * T * C);
+        lo.pen = m.take(sizeof(float) * (size_t)B * T * C);
         // gold-segmentation loss (semicrf_nll): counters and block sums
         lo.gcnt = m.take(sizeof(int) * (size_t)B * (K * C + C * C + C + 1));
         lo.gpart = m.take(sizeof(double) * (size_t)B * gold_blocks(T));
@@ -153,10 +156,23 @@ int run_prefix(const float* em, const int32_t* lengths, int B, int T, int C, voi
     return SEMICRF_OK;
 }
 
-SweepArgs base_args(const float* trans, const float* dur, int B, int T, int C, int K, void* ws,
-                    const Layout& lo) {
+// optional boundary projections (inputs) and boundary outputs of the backward pass
+struct Proj {
+    const float* start;
+    const float* end;
+};
+struct BoundaryRes {
+    float* grad_start;
+    float* grad_end;
+    float* prob;
+};
+
+SweepArgs base_args(const float* trans, const float* dur, const Proj& pj, int B, int T, int C,
+                    int K, void* ws, const Layout& lo) {
     SweepArgs a{};
     a.S = at<double>(ws, lo.S);
+    a.proj_start = pj.start;
+    a.proj_end = pj.end;
     a.Leff = at<int>(ws, lo.Leff);
     a.trans = trans;
     a.dur = dur;
@@ -215,8 +231,8 @@ static int common_checks(const float* em, const int32_t* lengths, const float* t
 }
 
 static int run_logz(const float* em, const int32_t* lengths, const float* trans, const float* dur,
-                    int B, int T, int C, int K, hipStream_t stream, void* workspace,
-                    size_t workspace_bytes, float* log_z, hipEvent_t* events) {
+                    const Proj& pj, int B, int T, int C, int K, hipStream_t stream,
+                    void* workspace, size_t workspace_bytes, float* log_z, hipEvent_t* events) {
     int rc = common_checks(em, lengths, trans, dur, B, T, C, K);
     if (rc) return rc;
     if (!log_z) return SEMICRF_ERR_INVALID;
@@ -227,7 +243,7 @@ static int run_logz(const float* em, const int32_t* lengths, const float* trans,
     if ((rc = run_prefix(em, lengths, B, T, C, workspace, lo, stream))) return rc;
     STAGE(1);
     const SweepCfg cfg = choose_sweep(C, K);
-    SweepArgs a = base_args(trans, dur, B, T, C, K, workspace, lo);
+    SweepArgs a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
     a.mode = MODE_FULL;
     a.logz = at<double>(workspace, lo.logz);
     LAUNCH(launch_lse(cfg, a, 1, stream));
@@ -237,10 +253,11 @@ static int run_logz(const float* em, const int32_t* lengths, const float* trans,
 }
 
 static int run_backward(const float* em, const int32_t* lengths, const float* trans,
-                        const float* dur, int B, int T, int C, int K, int delta,
+                        const float* dur, const Proj& pj, int B, int T, int C, int K, int delta,
                         hipStream_t stream, void* workspace, size_t workspace_bytes,
                         const float* grad_log_z, float* grad_em, float* grad_trans,
-                        float* grad_dur, float* marginals, float* log_z, hipEvent_t* events) {
+                        float* grad_dur, float* marginals, float* log_z, const BoundaryRes& br,
+                        hipEvent_t* events) {
     int rc = common_checks(em, lengths, trans, dur, B, T, C, K);
     if (rc) return rc;
     if (!grad_em || !grad_trans || !grad_dur || delta < 0) return SEMICRF_ERR_INVALID;
@@ -251,7 +268,7 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
     if ((rc = run_prefix(em, lengths, B, T, C, workspace, lo, stream))) return rc;
     STAGE(1);
     const SweepCfg cfg = choose_sweep(C, K);
-    SweepArgs a = base_args(trans, dur, B, T, C, K, workspace, lo);
+    SweepArgs a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
     a.delta = lo.delta;
     a.nspans = lo.nspans;
     a.ck_ring = at<float>(workspace, lo.ckR);
@@ -288,14 +305,28 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
     m.dn_tile = at<double>(workspace, lo.dnt);
     m.part_dur = at<double>(workspace, lo.pd);
     m.part_trans = at<double>(workspace, lo.pt);
+    const bool want_b = br.grad_start || br.grad_end || br.prob;
+    if (want_b) {
+        m.pstart = at<float>(workspace, lo.pst);
+        m.pend = at<float>(workspace, lo.pen);
+    }
     LAUNCH(launch_marginals(m, stream));
     STAGE(4);
     LAUNCH(launch_tile_scan(m.dn_tile, B, lo.ntm, C, false, at<double>(workspace, lo.dno), nullptr,
                             stream));
     float* mu = marginals ? marginals : at<float>(workspace, lo.mu);
+    BoundaryOut bo{};
+    if (want_b) {
+        bo.pstart = m.pstart;
+        bo.pend = m.pend;
+        bo.grad_log_z = grad_log_z;
+        bo.grad_proj_start = br.grad_start;
+        bo.grad_proj_end = br.grad_end;
+        bo.boundary = br.prob;
+    }
     LAUNCH(launch_node_marginals(m.Dn, at<double>(workspace, lo.dno), a.Leff, B, T, C, lo.tm,
                                  lo.ntm, mu, at<double>(workspace, lo.mut),
-                                 at<double>(workspace, lo.zt), stream));
+                                 at<double>(workspace, lo.zt), bo, stream));
     LAUNCH(launch_tile_scan(at<double>(workspace, lo.mut), B, lo.ntm, C, false, nullptr,
                             at<double>(workspace, lo.mutot), stream));
     LAUNCH(launch_grad_em(mu, at<double>(workspace, lo.mutot), a.Leff, grad_log_z, B, T, C, grad_em,
@@ -309,9 +340,10 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
 }
 
 static int run_viterbi(const float* em, const int32_t* lengths, const float* trans,
-                       const float* dur, int B, int T, int C, int K, hipStream_t stream,
-                       void* workspace, size_t workspace_bytes, float* best_score,
-                       int32_t* labels, uint8_t* seg_start, hipEvent_t* events) {
+                       const float* dur, const Proj& pj, int B, int T, int C, int K,
+                       hipStream_t stream, void* workspace, size_t workspace_bytes,
+                       float* best_score, int32_t* labels, uint8_t* seg_start,
+                       hipEvent_t* events) {
     int rc = common_checks(em, lengths, trans, dur, B, T, C, K);
     if (rc) return rc;
     if (!best_score || !labels || !seg_start) return SEMICRF_ERR_INVALID;
@@ -322,7 +354,7 @@ static int run_viterbi(const float* em, const int32_t* lengths, const float* tra
     if ((rc = run_prefix(em, lengths, B, T, C, workspace, lo, stream))) return rc;
     STAGE(1);
     const SweepCfg cfg = choose_sweep(C, K);
-    SweepArgs a = base_args(trans, dur, B, T, C, K, workspace, lo);
+    SweepArgs a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
     a.mode = MODE_FULL;
     a.bp = at<uint32_t>(workspace, lo.bp);
     a.vscore = at<double>(workspace, lo.vscore);
@@ -340,50 +372,58 @@ static int run_viterbi(const float* em, const int32_t* lengths, const float* tra
 }
 
 int semicrf_logz(const float* em, const int32_t* lengths, const float* trans, const float* dur,
-                 int B, int T, int C, int K, hipStream_t stream, void* workspace,
-                 size_t workspace_bytes, float* log_z) {
-    return run_logz(em, lengths, trans, dur, B, T, C, K, stream, workspace, workspace_bytes, log_z,
-                    nullptr);
+                 const float* proj_start, const float* proj_end, int B, int T, int C, int K,
+                 hipStream_t stream, void* workspace, size_t workspace_bytes, float* log_z) {
+    return run_logz(em, lengths, trans, dur, Proj{proj_start, proj_end}, B, T, C, K, stream,
+                    workspace, workspace_bytes, log_z, nullptr);
 }
 
 int semicrf_logz_staged(const float* em, const int32_t* lengths, const float* trans,
-                        const float* dur, int B, int T, int C, int K, hipStream_t stream,
-                        void* workspace, size_t workspace_bytes, float* log_z,
-                        hipEvent_t* events) {
+                        const float* dur, const float* proj_start, const float* proj_end, int B,
+                        int T, int C, int K, hipStream_t stream, void* workspace,
+                        size_t workspace_bytes, float* log_z, hipEvent_t* events) {
     if (!events) return SEMICRF_ERR_INVALID;
-    return run_logz(em, lengths, trans, dur, B, T, C, K, stream, workspace, workspace_bytes, log_z,
-                    events);
+    return run_logz(em, lengths, trans, dur, Proj{proj_start, proj_end}, B, T, C, K, stream,
+                    workspace, workspace_bytes, log_z, events);
 }
 
 int semicrf_backward(const float* em, const int32_t* lengths, const float* trans, const float* dur,
-                     int B, int T, int C, int K, int delta, hipStream_t stream, void* workspace,
-                     size_t workspace_bytes, const float* grad_log_z, float* grad_em,
-                     float* grad_trans, float* grad_dur, float* marginals, float* log_z) {
-    return run_backward(em, lengths, trans, dur, B, T, C, K, delta, stream, workspace,
-                        workspace_bytes, grad_log_z, grad_em, grad_trans, grad_dur, marginals, log_z,
-                        nullptr);
+                     const float* proj_start, const float* proj_end, int B, int T, int C, int K,
+                     int delta, hipStream_t stream, void* workspace, size_t workspace_bytes,
+                     const float* grad_log_z, float* grad_em, float* grad_trans, float* grad_dur,
+                     float* marginals, float* log_z, float* grad_proj_start,
+                     float* grad_proj_end, float* boundary) {
+    return run_backward(em, lengths, trans, dur, Proj{proj_start, proj_end}, B, T, C, K, delta,
+                        stream, workspace, workspace_bytes, grad_log_z, grad_em, grad_trans,
+                        grad_dur, marginals, log_z,
+                        BoundaryRes{grad_proj_start, grad_proj_end, boundary}, nullptr);
 }
 
 int semicrf_backward_staged(const float* em, const int32_t* lengths, const float* trans,
-                            const float* dur, int B, int T, int C, int K, int delta,
-                            hipStream_t stream, void* workspace, size_t workspace_bytes,
-                            const float* grad_log_z, float* grad_em, float* grad_trans,
-                            float* grad_dur, float* marginals, float* log_z, hipEvent_t* events) {
+                            const float* dur, const float* proj_start, const float* proj_end,
+                            int B, int T, int C, int K, int delta, hipStream_t stream,
+                            void* workspace, size_t workspace_bytes, const float* grad_log_z,
+                            float* grad_em, float* grad_trans, float* grad_dur, float* marginals,
+                            float* log_z, float* grad_proj_start, float* grad_proj_end,
+                            float* boundary, hipEvent_t* events) {
     if (!events) return SEMICRF_ERR_INVALID;
-    return run_backward(em, lengths, trans, dur, B, T, C, K, delta, stream, workspace,
-                        workspace_bytes, grad_log_z, grad_em, grad_trans, grad_dur, marginals, log_z,
-                        events);
+    return run_backward(em, lengths, trans, dur, Proj{proj_start, proj_end}, B, T, C, K, delta,
+                        stream, workspace, workspace_bytes, grad_log_z, grad_em, grad_trans,
+                        grad_dur, marginals, log_z,
+                        BoundaryRes{grad_proj_start, grad_proj_end, boundary}, events);
 }
 
 int semicrf_nll(const float* em, const int32_t* lengths, const float* trans, const float* dur,
-                const int32_t* gold_labels, const uint8_t* gold_seg_start, int B, int T, int C,
-                int K, int delta, hipStream_t stream, void* workspace, size_t workspace_bytes,
+                const float* proj_start, const float* proj_end, const int32_t* gold_labels,
+                const uint8_t* gold_seg_start, int B, int T, int C, int K, int delta,
+                hipStream_t stream, void* workspace, size_t workspace_bytes,
                 const float* grad_nll, float* nll, float* grad_em, float* grad_trans,
-                float* grad_dur) {
+                float* grad_dur, float* grad_proj_start, float* grad_proj_end) {
     if (!gold_labels || !gold_seg_start || !nll) return SEMICRF_ERR_INVALID;
-    int rc = run_backward(em, lengths, trans, dur, B, T, C, K, delta, stream, workspace,
+    const Proj pj{proj_start, proj_end};
+    int rc = run_backward(em, lengths, trans, dur, pj, B, T, C, K, delta, stream, workspace,
                           workspace_bytes, grad_nll, grad_em, grad_trans, grad_dur, nullptr,
-                          nullptr, nullptr);
+                          nullptr, BoundaryRes{grad_proj_start, grad_proj_end, nullptr}, nullptr);
     if (rc) return rc;
     Layout lo;
     if (!make_layout(SEMICRF_OP_BACKWARD, B, T, C, K, delta, lo)) return SEMICRF_ERR_UNSUPPORTED;
@@ -392,6 +432,8 @@ int semicrf_nll(const float* em, const int32_t* lengths, const float* trans, con
     g.Leff = at<int>(workspace, lo.Leff);
     g.trans = trans;
     g.dur = dur;
+    g.proj_start = proj_start;
+    g.proj_end = proj_end;
     g.labels = gold_labels;
     g.seg_start = gold_seg_start;
     g.B = B; g.T = T; g.C = C; g.K = K;
@@ -404,25 +446,28 @@ int semicrf_nll(const float* em, const int32_t* lengths, const float* trans, con
     g.grad_em = grad_em;
     g.grad_trans = grad_trans;
     g.grad_dur = grad_dur;
+    g.grad_proj_start = grad_proj_start;
+    g.grad_proj_end = grad_proj_end;
     LAUNCH(launch_gold(g, stream));
     return SEMICRF_OK;
 }
 
 int semicrf_viterbi(const float* em, const int32_t* lengths, const float* trans, const float* dur,
-                    int B, int T, int C, int K, hipStream_t stream, void* workspace,
-                    size_t workspace_bytes, float* best_score, int32_t* labels,
-                    uint8_t* seg_start) {
-    return run_viterbi(em, lengths, trans, dur, B, T, C, K, stream, workspace, workspace_bytes,
-                       best_score, labels, seg_start, nullptr);
+                    const float* proj_start, const float* proj_end, int B, int T, int C, int K,
+                    hipStream_t stream, void* workspace, size_t workspace_bytes,
+                    float* best_score, int32_t* labels, uint8_t* seg_start) {
+    return run_viterbi(em, lengths, trans, dur, Proj{proj_start, proj_end}, B, T, C, K, stream,
+                       workspace, workspace_bytes, best_score, labels, seg_start, nullptr);
 }
 
 int semicrf_viterbi_staged(const float* em, const int32_t* lengths, const float* trans,
-                           const float* dur, int B, int T, int C, int K, hipStream_t stream,
-                           void* workspace, size_t workspace_bytes, float* best_score,
-                           int32_t* labels, uint8_t* seg_start, hipEvent_t* events) {
+                           const float* dur, const float* proj_start, const float* proj_end,
+                           int B, int T, int C, int K, hipStream_t stream, void* workspace,
+                           size_t workspace_bytes, float* best_score, int32_t* labels,
+                           uint8_t* seg_start, hipEvent_t* events) {
     if (!events) return SEMICRF_ERR_INVALID;
-    return run_viterbi(em, lengths, trans, dur, B, T, C, K, stream, workspace, workspace_bytes,
-                       best_score, labels, seg_start, events);
+    return run_viterbi(em, lengths, trans, dur, Proj{proj_start, proj_end}, B, T, C, K, stream,
+                       workspace, workspace_bytes, best_score, labels, seg_start, events);
 }
 
 int semicrf_read_status(const void* workspace, hipStream_t stream) {

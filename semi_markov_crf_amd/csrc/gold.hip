@@ -2,9 +2,10 @@
 // the gold half of its gradients.
 //
 // The score of a segmentation sums, over its segments [s, e) of label c, the potential
-// S[e,c] - S[s,c] + dur[e-s-1, c] and, between consecutive segments, trans[c', c] -- the
-// same centred, additive potential as log Z ("Streaming Structured Inference with
-// Flash-SemiCRF", gist.science EN explainer, "2. Methodology").  nll is the negative
+// S[e,c] - S[s,c] + dur[e-s-1, c] (+ the boundary projections P_start[s,c] + P_end[e-1,c])
+// and, between consecutive segments, trans[c', c] -- the same centred, additive potential
+// as log Z ("Streaming Structured Inference with Flash-SemiCRF", gist.science EN
+// explainer, "2. Methodology").  nll is the negative
 // log-probability of y*, the training loss of the pages' convergence check ("4. Results
 // and Benchmarks"); its gradient is the posterior expectation of the features (the
 // gradients of log Z, from the backward pass) minus the features of y*.
@@ -17,7 +18,9 @@
 //   k_gold_finish    grid (B): fixed-order sum of the block sums; nll = log Z - score,
 //                    NaN and the status flag for an invalid length or segmentation
 //   k_gold_params    grad_dur / grad_trans -= sum_b g_b * counts (fixed order over b)
-//   k_gold_em        grad_em[b,t,c] -= g_b * (1[y*_t = c] - n_c / L)  (the centring)
+//   k_gold_em        grad_em[b,t,c] -= g_b * (1[y*_t = c] - n_c / L)  (the centring);
+//                    grad_proj_start / grad_proj_end -= g_b * the gold segments'
+//                    start / last-position indicators
 // A sequence whose gold segmentation is invalid keeps only its log Z half of the
 // gradients.
 #include "common.h"
@@ -64,6 +67,8 @@ __global__ __launch_bounds__(GT) void k_gold_segments(const GoldArgs g) {
             bad |= k > K;
             if (!bad) {
                 v = S[(size_t)e * C + c] - S[(size_t)t * C + c] + (double)g.dur[(k - 1) * C + c];
+                if (g.proj_start) v += (double)g.proj_start[((size_t)b * T + t) * C + c];
+                if (g.proj_end) v += (double)g.proj_end[((size_t)b * T + e - 1) * C + c];
                 atomicAdd(cnt + (k - 1) * C + c, 1);
                 atomicAdd(cnt + K * C + C * C + c, k);
                 if (t > 0) {
@@ -132,10 +137,17 @@ __global__ __launch_bounds__(256) void k_gold_em(const GoldArgs g) {
     const int* cnt = g.cnt + (size_t)b * ncnt;
     if (cnt[ncnt - 1]) return;   // invalid gold segmentation: no gold counts
     const double gb = g.grad_nll ? (double)g.grad_nll[b] : 1.0;
-    const double ind = g.labels[(size_t)b * T + t] == c ? 1.0 : 0.0;
+    const bool lab = g.labels[(size_t)b * T + t] == c;
+    const double ind = lab ? 1.0 : 0.0;
     const double mean = (double)cnt[g.K * C + C * C + c] / (double)L;
-    float* out = g.grad_em + ((size_t)b * T + t) * C + c;
+    const size_t idx = ((size_t)b * T + t) * C + c;
+    float* out = g.grad_em + idx;
     *out = (float)((double)*out - gb * (ind - mean));
+    const uint8_t* st = g.seg_start + (size_t)b * T;
+    if (g.grad_proj_start && lab && (t == 0 || st[t]))
+        g.grad_proj_start[idx] = (float)((double)g.grad_proj_start[idx] - gb);
+    if (g.grad_proj_end && lab && (t + 1 == L || st[t + 1]))
+        g.grad_proj_end[idx] = (float)((double)g.grad_proj_end[idx] - gb);
 }
 
 hipError_t launch_gold(const GoldArgs& g, hipStream_t stream) {

@@ -50,43 +50,51 @@ SweepCfg choose_sweep(int C, int K);
 __host__ __device__ constexpr int lse_chunk_max(int G) { return G >= 16 ? 64 : 16; }
 constexpr int MAXPLUS_CHUNK_MAX = 64;
 
-// Dynamic LDS of the log-semiring sweep: S chunks [2][CH+1][C] + S(L) [C] (fp64), then
-// the R ring (and the E ring when linear) [C+1][P], messages p and u [2][UP] each, and a
-// per-thread sink [NT] (fp32).
+// Dynamic LDS of the log-semiring sweep: end-side and start-side S chunks [2][2][CH+1][C]
+// + S(L) [C] (fp64), then the R ring (and the E ring when linear) [C+1][P], messages p and
+// u [2][UP] each, and a per-thread sink [NT] (fp32).
 inline size_t lse_lds_bytes(int C, int NT, int UP, int P, int CH, bool lin) {
-    return (size_t)(2 * (CH + 1) * C + C) * 8 +
+    return (size_t)(4 * (CH + 1) * C + C) * 8 +
            (size_t)((lin ? 2 : 1) * (C + 1) * P + 4 * UP + NT) * 4;
 }
 // The round kernels (C <= 16): ROUND positions per workgroup barrier.
 constexpr int ROUND = 4;
 // Dynamic LDS of the log-semiring round kernel: S chunks [2][C][CH] and S(L) (fp64), the
-// chunks' per-position factors [2][3][C][CH], the rings [C+1][P] (two when linear), bulk
+// chunks' per-position factors [2][5][C][CH], the rings [C+1][P] (two when linear), bulk
 // sums [2][CP][2][ROUND], staged ring entries [2][CP+1][2][ROUND], rebase shifts and dmax
 // [CP rounded to 4], a sink and two constant blocks [16] (fp32).
 inline size_t lse_round_lds_bytes(int C, int CP, int P, int CH, bool lin) {
     const int cp4 = (CP + 3) / 4 * 4;
     return (size_t)(2 * CH * C + (C + 1) / 2 * 2) * 8 +
-           (size_t)(6 * C * CH + (lin ? 2 : 1) * (C + 1) * P + 4 * CP * ROUND +
+           (size_t)(10 * C * CH + (lin ? 2 : 1) * (C + 1) * P + 4 * CP * ROUND +
                     4 * (CP + 1) * ROUND + 2 * cp4 + 16) * 4;
 }
-// Dynamic LDS of the max-plus round kernel (C <= 16): S chunks [2][C][CH] and S(L) (fp64), the
-// ring [C+1][P], bulk maxima and their k [2][CP][2][ROUND], rebase shifts [CP rounded to
-// 4], a sink and a constant block [12] (fp32).
+// Dynamic LDS of the max-plus round kernel (C <= 16): S chunks [2][C][CH] and S(L) (fp64),
+// the chunks' end-side and start-side projections [2][2][C][CH], the ring [C+1][P], bulk
+// maxima and their k [2][CP][2][ROUND], rebase shifts [CP rounded to 4], a sink and a
+// constant block [12] (fp32).
 inline size_t maxplus_round_lds_bytes(int C, int CP, int P, int CH) {
     const int cp4 = (CP + 3) / 4 * 4;
     return (size_t)(2 * CH * C + (C + 1) / 2 * 2) * 8 +
-           (size_t)((C + 1) * P + 4 * CP * ROUND + cp4 + 12) * 4;
+           (size_t)(4 * C * CH + (C + 1) * P + 4 * CP * ROUND + cp4 + 12) * 4;
 }
-// Dynamic LDS of the max-plus sweep: S chunks [2][CH][C] (fp64), R ring [C+1][P] and
-// u [2][UP] (fp32).
+// Dynamic LDS of the max-plus sweep: end-side and start-side S chunks [2][2][CH][C]
+// (fp64), R ring [C+1][P] and u [2][UP] (fp32).
 inline size_t maxplus_lds_bytes(int C, int UP, int P, int CH) {
-    return (size_t)(2 * CH * C) * 8 + (size_t)((C + 1) * P + 2 * UP) * 4;
+    return (size_t)(4 * CH * C) * 8 + (size_t)((C + 1) * P + 2 * UP) * 4;
 }
 
 enum SweepMode { MODE_FULL = 0, MODE_SPAN = 1 };
 
 struct SweepArgs {
     const double* S;        // [B][T+1][C] centred prefix sums
+    // boundary projections [B][T][C] or NULL (zeros): a segment [s, e) of label c gains
+    // proj_start[s, c] + proj_end[e-1, c].  Sweep position p of direction 0 adds
+    // proj_end[p-1] to the messages that end there and proj_start[p] to the ring entries
+    // that start there; on the mirrored sequence the two swap roles (proj_start[L-p] at
+    // the end side, proj_end[L-1-p] at the start side).
+    const float* proj_start;
+    const float* proj_end;
     const int* Leff;        // [B] clamped length, negated when the input length was invalid
     const float* trans;     // [C][C]
     const float* dur;       // [K][C]
@@ -121,6 +129,10 @@ hipError_t launch_lse(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStre
 hipError_t launch_lse_mirror(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream);
 hipError_t launch_lse_plain(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream);
 hipError_t launch_lse_log(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream);
+// round kernels (C <= 16) with boundary projections
+hipError_t launch_lse_round_proj(const SweepCfg& cfg, const SweepArgs& a, int ndir, bool lin,
+                                 hipStream_t stream);
+hipError_t launch_maxplus_round_proj(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream);
 // max-plus sweep (Viterbi): MODE_FULL, forward only, grid (B); dispatches on cfg.vit.layout
 hipError_t launch_maxplus(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream);
 hipError_t launch_maxplus_mirror(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream);
@@ -156,14 +168,27 @@ struct MargArgs {
     double* dn_tile;        // [B][ntiles][C]: tile sums of Dn
     double* part_dur;       // [B][ntiles][K][C]
     double* part_trans;     // [B][ntiles][C][C]
+    float* pstart;          // [B][T][C] or NULL: start mass of segments at each position
+    float* pend;            // [B][T][C] or NULL: mass of segments whose last position it is
 };
 hipError_t launch_marginals(const MargArgs& a, hipStream_t stream);
 
 // mu = prefix sum of Dn, normalised per position; writes marginals, per-tile sums of
-// mu and the per-tile mean normaliser.
+// mu and the per-tile mean normaliser.  With pstart / pend (the raw start and end masses
+// of k_marginals) also the boundary probability [B][T] and g times the normalised start
+// and end marginals [B][T][C] (any of the three outputs may be NULL).
+struct BoundaryOut {
+    const float* pstart;
+    const float* pend;
+    const float* grad_log_z;
+    float* grad_proj_start;
+    float* grad_proj_end;
+    float* boundary;
+};
 hipError_t launch_node_marginals(const double* Dn, const double* dn_off, const int* Leff,
                                  int B, int T, int C, int tile, int ntiles, float* mu,
-                                 double* mu_tile, double* z_tile, hipStream_t stream);
+                                 double* mu_tile, double* z_tile, const BoundaryOut& bo,
+                                 hipStream_t stream);
 hipError_t launch_grad_em(const float* mu, const double* mu_tot, const int* Leff,
                           const float* grad_log_z, int B, int T, int C, float* grad_em,
                           hipStream_t stream);
@@ -182,6 +207,8 @@ struct GoldArgs {
     const int* Leff;            // [B]
     const float* trans;         // [C][C]
     const float* dur;           // [K][C]
+    const float* proj_start;    // [B][T][C] or NULL
+    const float* proj_end;      // [B][T][C] or NULL
     const int32_t* labels;      // [B][T] gold label per position
     const uint8_t* seg_start;   // [B][T] 1 at each gold segment's first position
     int B, T, C, K;
@@ -194,6 +221,8 @@ struct GoldArgs {
     float* grad_em;             // [B][T][C] gradients of the backward pass, corrected in place
     float* grad_trans;          // [C][C]
     float* grad_dur;            // [K][C]
+    float* grad_proj_start;     // [B][T][C] or NULL, corrected in place
+    float* grad_proj_end;       // [B][T][C] or NULL, corrected in place
 };
 int gold_blocks(int T);
 hipError_t launch_gold(const GoldArgs& g, hipStream_t stream);

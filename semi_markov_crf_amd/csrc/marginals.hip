@@ -1,9 +1,10 @@
 // Posterior marginals and gradients of log Z on gfx950.
 //
 // From the per-position forward / backward quantities written by the span recompute
-//   XF[s,c] = alpha[s,c]        AF[s,c] = abar[s,c] - S[s,c]
-//   XB[s,c] = beta_bar[s,c]     AB[u,c] = beta[u,c] + S[u,c] - S[L,c]
-// the posterior of one segment [s, s+k) of label c is
+//   XF[s,c] = alpha[s,c]        AF[s,c] = abar[s,c] - S[s,c] + P_start[s,c]
+//   XB[s,c] = beta_bar[s,c]     AB[u,c] = beta[u,c] + S[u,c] + P_end[u-1,c] - S[L,c]
+// (the boundary projections P_start / P_end are zero when absent) the posterior of one
+// segment [s, s+k) of label c is
 //   p(s,k,c) = exp(AF[s,c] + AB[s+k,c] + S[L,c] + dur[k-1,c] - logZ)
 // and that of a transition c' -> c at s is exp(XF[s,c'] + trans[c',c] + XB[s,c] - logZ).
 // Their sums are the gradients of log Z with respect to dur and trans, and the
@@ -18,6 +19,11 @@
 // position (1 in exact arithmetic).  This per-position normalisation removes the slow
 // drift between the forward and backward sweeps' rounding over 10^5..10^6 positions;
 // the dur / trans partial sums of a tile are divided by the tile's mean normaliser.
+// The start and end masses at each position, divided by the same per-position
+// normaliser, are the gradients with respect to the projections; their sum over labels
+// at t is the probability that a segment boundary (a segment start) lies at t (the pages
+// check that these boundary probabilities are valid at genome scale, "4. Results and
+// Benchmarks").
 #include "common.h"
 #include "internal.h"
 
@@ -113,6 +119,8 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
         const double d = st - en;
         Dsh[q] = d;
         if (t <= T) Dn[(size_t)t * C + c] = d;
+        if (a.pstart && t < L) a.pstart[((size_t)b * T + t) * C + c] = (float)st;
+        if (a.pend && t >= 1 && t <= L) a.pend[((size_t)b * T + t - 1) * C + c] = (float)en;
     }
     __syncthreads();
     for (int c = tid; c < C; c += 256) {
@@ -156,7 +164,8 @@ __global__ __launch_bounds__(256) void k_node_marginals(const double* __restrict
                                                         const int* __restrict__ Leff, int T, int C,
                                                         int TM, float* __restrict__ mu,
                                                         double* __restrict__ mu_tile,
-                                                        double* __restrict__ z_tile) {
+                                                        double* __restrict__ z_tile,
+                                                        const BoundaryOut bo) {
     extern __shared__ double lds[];
     const int tile = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, ntiles = gridDim.x;
     const int L = abs(Leff[b]);
@@ -196,6 +205,31 @@ __global__ __launch_bounds__(256) void k_node_marginals(const double* __restrict
         zrow[r] = z;
     }
     __syncthreads();
+    if (bo.pstart) {
+        // boundary probabilities and the projections' gradients: the raw start / end
+        // masses over the same per-position normaliser (0 at padding)
+        const size_t base = (size_t)b * T * C;
+        const double g = bo.grad_log_z ? (double)bo.grad_log_z[b] : 1.0;
+        for (int r = tid; r < TM; r += 256) {
+            const int t = p0 + r;
+            if (t >= T || !bo.boundary) continue;
+            double s = 0.0;
+            if (r < rows)
+                for (int c = 0; c < C; ++c) s += (double)bo.pstart[base + (size_t)t * C + c];
+            bo.boundary[(size_t)b * T + t] = r < rows ? (float)(s / zrow[r]) : 0.0f;
+        }
+        for (int q = tid; q < TM * C; q += 256) {
+            const int r = q / C;
+            const int t = p0 + r;
+            if (t >= T) continue;
+            const size_t idx = base + (size_t)p0 * C + q;
+            const bool in = r < rows;
+            if (bo.grad_proj_start)
+                bo.grad_proj_start[idx] = in ? (float)(g * (double)bo.pstart[idx] / zrow[r]) : 0.0f;
+            if (bo.grad_proj_end)
+                bo.grad_proj_end[idx] = in ? (float)(g * (double)bo.pend[idx] / zrow[r]) : 0.0f;
+        }
+    }
     float* mub = mu + (size_t)b * T * C;
     for (int q = tid; q < TM * C; q += 256) {
         const int r = q / C;
@@ -224,10 +258,10 @@ __global__ __launch_bounds__(256) void k_node_marginals(const double* __restrict
 
 hipError_t launch_node_marginals(const double* Dn, const double* dn_off, const int* Leff, int B,
                                  int T, int C, int tile, int ntiles, float* mu, double* mu_tile,
-                                 double* z_tile, hipStream_t stream) {
+                                 double* z_tile, const BoundaryOut& bo, hipStream_t stream) {
     const size_t lds = (size_t)8 * ((size_t)tile * C + 256 + tile);
     hipLaunchKernelGGL(k_node_marginals, dim3(ntiles, B), dim3(256), lds, stream, Dn, dn_off, Leff,
-                       T, C, tile, mu, mu_tile, z_tile);
+                       T, C, tile, mu, mu_tile, z_tile, bo);
     return hipGetLastError();
 }
 

@@ -65,7 +65,7 @@ SweepCfg choose_sweep(int C, int K) {
     for (int lay : {int(SWEEP_MIRRORED | SWEEP_LINEAR), int(SWEEP_LINEAR), 0}) {
         if (s.split && (lay & SWEEP_MIRRORED)) continue;
         const int P = s.split ? s.RS + 4 : pitch(lay);
-        for (int ch = lse_chunk_max(G); ch >= 8 && s.lse.bytes == 0; ch >>= 1) {
+        for (int ch = lse_chunk_max(G); ch >= 4 && s.lse.bytes == 0; ch >>= 1) {
             const size_t n = s.split ? lse_round_lds_bytes(C, s.CPr, P, ch, lay & SWEEP_LINEAR)
                                      : lse_lds_bytes(C, s.NT, UP, P, ch, lay & SWEEP_LINEAR);
             if (n <= LDS_BUDGET) s.lse = SweepLds{lay, P, ch, n};
@@ -76,7 +76,7 @@ SweepCfg choose_sweep(int C, int K) {
     for (int lay : {int(SWEEP_MIRRORED), 0}) {
         if (s.split && (lay & SWEEP_MIRRORED)) continue;
         const int P = s.split ? s.RS + 4 : pitch(lay);
-        for (int ch = s.split ? lse_chunk_max(G) : MAXPLUS_CHUNK_MAX; ch >= 8 && s.vit.bytes == 0; ch >>= 1) {
+        for (int ch = s.split ? lse_chunk_max(G) : MAXPLUS_CHUNK_MAX; ch >= 4 && s.vit.bytes == 0; ch >>= 1) {
             const size_t n = s.split ? maxplus_round_lds_bytes(C, s.CPr, P, ch)
                                      : maxplus_lds_bytes(C, UP, P, ch);
             if (n <= LDS_BUDGET) s.vit = SweepLds{lay, P, ch, n};

@@ -108,12 +108,14 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
         t1 = min(L, t0 + a.delta);
     }
     const int RMASK = RS - 1;
-    const int rowsN = (CH + 1) * C;           // staged S values per chunk
+    const int rowsN = (CH + 1) * C;           // staged S values per chunk and side
     constexpr bool MIR = LAY & SWEEP_MIRRORED;
     constexpr bool LIN = LAY & SWEEP_LINEAR;
 
-    double* Sbuf = lds;                                   // [2][CH+1][C]
-    double* SL = Sbuf + 2 * rowsN;                        // [C]
+    // end side S(p) + pe(p) and start side S(p) - ps(p) (projections, base 2):
+    // [2 chunks][2 sides][CH+1][C]
+    double* Sbuf = lds;
+    double* SL = Sbuf + 4 * rowsN;                        // [C]
     float* R = (float*)(SL + C);                          // [C+1][P]
     float* E = R + (C + 1) * P;                           // [C+1][P] (linear bulk only)
     float* p_sh = E + (LIN ? (C + 1) * P : 0);            // [2][UP] messages, linear
@@ -124,6 +126,20 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
 
     const double* Sb = a.S + (size_t)b * (T + 1) * C;
     for (int q = tid; q < C; q += NT) SL[q] = Sb[(size_t)L * C + q];
+    // projections of sweep position p, base 2: end side (segments ending at p) and start
+    // side (segments starting at p); 0 without projections or outside [1, L] / [0, L-1]
+    const float* PSb = a.proj_start ? a.proj_start + (size_t)b * T * C : nullptr;
+    const float* PEb = a.proj_end ? a.proj_end + (size_t)b * T * C : nullptr;
+    auto proj_e = [&](int p, int q) -> double {
+        const float* src = dir == 0 ? PEb : PSb;
+        const int t = dir == 0 ? p - 1 : L - p;
+        return (src && p >= 1 && p <= L) ? (double)src[(size_t)t * C + q] * LOG2E : 0.0;
+    };
+    auto proj_s = [&](int p, int q) -> double {
+        const float* src = dir == 0 ? PSb : PEb;
+        const int t = dir == 0 ? p : L - 1 - p;
+        return (src && p >= 0 && p < L) ? (double)src[(size_t)t * C + q] * LOG2E : 0.0;
+    };
     for (int q = tid; q < (C + 1) * P; q += NT) {
         R[q] = NEG;
         if constexpr (LIN) E[q] = 0.0f;
@@ -211,8 +227,9 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
     double Bc = 0.0, H = 0.0;
     float Mref = 0.0f, Rn1, Rn2;
     if (t0 == 0) {
-        if (writer) put_all(0, 0.0f);       // position 0: no transition into it
-        Rn1 = 0.0f;
+        // position 0: no transition into it; the ring entry is its start-side projection
+        Rn1 = act ? fmaxf((float)proj_s(0, c), NEG) : 0.0f;
+        if (writer) put_all(0, Rn1);
         Rn2 = NEG;
     } else {
         const size_t ck = ckrow + span;
@@ -238,17 +255,25 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
     for (int q = tid; q < rowsN; q += NT) {
         const int row = q / C, l = q - row * C;
         const int t = t0 + 1 + row;
-        Sbuf[q] = (t <= t1) ? spub(Sb[sidx(t, l)], l) : 0.0;
+        const double sv = (t <= t1) ? spub(Sb[sidx(t, l)], l) : 0.0;
+        Sbuf[q] = (t <= t1) ? sv + proj_e(t, l) : 0.0;
+        Sbuf[rowsN + q] = (t <= t1) ? sv - proj_s(t, l) : 0.0;
     }
     double pf[PF];   // raw values of chunk n+1, fetched one chunk ahead
+    float pfe[PF], pfs[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
         const int q = tid + i * NT;
         pf[i] = 0.0;
+        pfe[i] = pfs[i] = 0.0f;
         if (q < rowsN) {
             const int row = q / C, l = q - row * C;
             const int t = t0 + 1 + CH + row;
-            if (t <= t1) pf[i] = Sb[sidx(t, l)];
+            if (t <= t1) {
+                pf[i] = Sb[sidx(t, l)];
+                pfe[i] = (float)proj_e(t, l);
+                pfs[i] = (float)proj_s(t, l);
+            }
         }
     }
     __syncthreads();   // restored ring and chunk 0 visible
@@ -258,7 +283,7 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
     float Qla, Qga;           // bulk of the next message's position (linear, log2)
     bulk(t0 + 1, Qla, Qga);
     double BH = Bc - H;       // B_c - H
-    double Scur = Sbuf[cc];   // S(t0+1), base 2
+    double Scur = Sbuf[rowsN + cc];   // start side of t0+1, base 2
     float rps = 1.0f;         // 2^-e of the last normaliser step
     auto publish = [&](int tn, double Sn, float z, float ql, float qg) {
         // message of position tn from E(tn-1) = En1, E(tn-2) = En2 and bulk (ql, qg);
@@ -284,7 +309,7 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
         if (a.write_xa && writer)
             Xout[(outrow + (dir == 0 ? tn : L - tn)) * C + c] = (Sn + Bc + (double)sigma) * LN2;
     };
-    publish(t0 + 1, Scur, fast_exp2((float)(Scur + BH) + dmax), Qla, Qga);
+    publish(t0 + 1, Sbuf[cc], fast_exp2((float)(Sbuf[cc] + BH) + dmax), Qla, Qga);
     bulk(t0 + 2, Qla, Qga);
     double lz = 0.0;
     int next_ck = (a.mode == MODE_FULL && a.write_ckpt) ? a.delta : INT_MAX;
@@ -292,18 +317,22 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
 
     // ---------------------------------------------------------------- main loop
     for (int tc = t0 + 1, nch = 0; tc <= t1; tc += CH, ++nch) {
-        const double* Srow = Sbuf + (nch & 1) * rowsN;
+        const double* Srow = Sbuf + (nch & 1) * 2 * rowsN;   // end side; start side at +rowsN
         const int rows = min(CH, t1 - tc + 1);
         for (int row = 0; row < rows; ++row) {
             const int t = tc + row;
             if (row == 0 && tc + CH <= t1) {
                 // publish chunk n+1 (its buffer was last read in chunk n-1), fetch n+2;
                 // this position's barrier makes it visible
-                double* dst = Sbuf + ((nch + 1) & 1) * rowsN;
+                double* dst = Sbuf + ((nch + 1) & 1) * 2 * rowsN;
 #pragma unroll
                 for (int i = 0; i < PF; ++i) {
                     const int q = tid + i * NT;
-                    if (q < rowsN) dst[q] = spub(pf[i], q - (q / C) * C);
+                    if (q < rowsN) {
+                        const double sv = spub(pf[i], q - (q / C) * C);
+                        dst[q] = sv + (double)pfe[i];
+                        dst[rowsN + q] = sv - (double)pfs[i];
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < PF; ++i) {
@@ -311,7 +340,10 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
                     if (q < rowsN) {
                         const int rr = q / C, l = q - rr * C;
                         const int tt = tc + 2 * CH + rr;
-                        pf[i] = (tt <= t1) ? Sb[sidx(tt, l)] : 0.0;
+                        const bool in = tt <= t1;
+                        pf[i] = in ? Sb[sidx(tt, l)] : 0.0;
+                        pfe[i] = in ? (float)proj_e(tt, l) : 0.0f;
+                        pfs[i] = in ? (float)proj_s(tt, l) : 0.0f;
                     }
                 }
             }
@@ -339,8 +371,8 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
                     }
                 }
             }
-            const double Snx = Srow[(row + 1) * C + cc];      // S(t+1)
-            const float h = (float)(Scur + BH);                 // S(t) + B_c - H(t)
+            const double Snx = Srow[(row + 1) * C + cc];      // end side of t+1
+            const float h = (float)(Scur + BH);                 // start side of t + B_c - H(t)
             const float f = fast_exp2(tmax - h);                // E(t) = s * f
             const float z = fast_exp2((float)(Snx + BH) + dmax);
 
@@ -439,7 +471,7 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
             }
             // ---- [C] message of t+1
             if (t < t1) publish(t + 1, Snx, z, Qla, Qga);
-            Scur = Snx;
+            Scur = Srow[rowsN + (row + 1) * C + cc];            // start side of t+1
             Qla = Qlc;
             Qga = Qgc;
             __syncthreads();

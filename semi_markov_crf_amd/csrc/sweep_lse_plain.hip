@@ -6,7 +6,9 @@
 namespace semicrf {
 
 hipError_t launch_lse_plain(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream) {
-    if (cfg.split) return launch_lse_round_layout<true>(cfg, a, ndir, stream);
+    if (cfg.split)
+        return (a.proj_start || a.proj_end) ? launch_lse_round_proj(cfg, a, ndir, true, stream)
+                                            : launch_lse_round_layout<true, false>(cfg, a, ndir, stream);
     return launch_lse_layout<SWEEP_LINEAR>(cfg, a, ndir, stream);
 }
 

@@ -24,6 +24,9 @@
 //    also stage S, label-major.
 // Per-label bases move at the start of every second round; the chain corrects the bulk
 // sums that the bulk wavefronts formed from the ring before they rescaled it.
+// Boundary projections (PROJ) split S into an end side S(p) + pe(p), which scales the
+// messages of segments ending at p, and a start side S(p) - ps(p), which scales the ring
+// entries of segments starting at p; the staged per-position factors carry both.
 #pragma once
 
 #include "sweep_lse_kernel.h"
@@ -90,9 +93,10 @@ __device__ __forceinline__ float at4(const float4& v, int d) {
 }
 
 // G: bulk lanes per label (C <= 256/G); BPL: ring blocks per bulk lane; CP: labels the
-// chain broadcasts (>= C); LIN: linear ring and sums (else log-space bulk sums only).
+// chain broadcasts (>= C); LIN: linear ring and sums (else log-space bulk sums only);
+// PROJ: boundary projections present (else the end and start sides coincide).
 // Block: 64 + ceil(C*G/64)*64 threads.
-template <int G, int BPL, int CP, bool LIN>
+template <int G, int BPL, int CP, bool LIN, bool PROJ>
 __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int RS, const int P,
                                                   const int CH) {
     constexpr int M = ROUND;
@@ -140,10 +144,11 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
 
     double* Sbuf = lds;                                    // [2][C][CH] label-major
     double* SL = Sbuf + 2 * C * CH;                        // [C] (padded to 16 bytes)
-    // per position of a staged chunk, relative to the first position p0 of its round:
-    // 2^(S(p) - S(p0)), its inverse, S(p) - S(p0)  [2][3][C][CH]
+    // per position p of a staged chunk, relative to S(p0), p0 the first position of its
+    // round: ge = S(p) + pe(p) - S(p0) and gs = S(p) - ps(p) - S(p0), with pe / ps the
+    // end-side / start-side projections (base 2): 2^ge, 2^-gs, ge, gs, pe  [2][5][C][CH]
     float* Fst = (float*)(SL + (C + 1) / 2 * 2);
-    float* R = Fst + 6 * C * CH;                           // [C+1][P] log ring
+    float* R = Fst + 10 * C * CH;                          // [C+1][P] log ring
     float* E = R + (C + 1) * P;                            // [C+1][P] linear ring
     float* qsh = E + (LIN ? (C + 1) * P : 0);              // [2 rounds][CP][lin, log][M]
     float* nsh = qsh + 2 * CP * 2 * M;                     // [2 rounds][CP+1][s, offset][M]
@@ -157,6 +162,22 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
 
     const double* Sb = a.S + (size_t)b * (T + 1) * C;
     for (int q = tid; q < C; q += NT) SL[q] = Sb[(size_t)L * C + q];
+    // projections of sweep position p, base 2: end side (segments ending at p) and start
+    // side (segments starting at p); 0 without projections or outside [1, L] / [0, L-1]
+    const float* PSb = a.proj_start ? a.proj_start + (size_t)b * T * C : nullptr;
+    const float* PEb = a.proj_end ? a.proj_end + (size_t)b * T * C : nullptr;
+    auto proj_e = [&](int p, int q) -> float {
+        if constexpr (!PROJ) return 0.0f;
+        const float* src = dir == 0 ? PEb : PSb;
+        const int t = dir == 0 ? p - 1 : L - p;
+        return (src && p >= 1 && p <= L) ? (float)((double)src[(size_t)t * C + q] * LOG2E) : 0.0f;
+    };
+    auto proj_s = [&](int p, int q) -> float {
+        if constexpr (!PROJ) return 0.0f;
+        const float* src = dir == 0 ? PSb : PEb;
+        const int t = dir == 0 ? p : L - 1 - p;
+        return (src && p >= 0 && p < L) ? (float)((double)src[(size_t)t * C + q] * LOG2E) : 0.0f;
+    };
     for (int q = tid; q < (C + 1) * P; q += NT) {
         R[q] = NEG;
         if constexpr (LIN) E[q] = 0.0f;
@@ -295,12 +316,15 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
         fH[i] = NEG;
     }
     if (t0 == 0) {
-        if (bact && j == 0) {                              // position 0: no transition into it
-            Rrow[slot_of(0)] = 0.0f;
-            if constexpr (LIN) Erow[slot_of(0)] = 1.0f;
+        // position 0: no transition into it; the ring entry is its start-side projection
+        if (bact && j == 0) {
+            const float r0 = fmaxf(proj_s(0, cb), NEG);
+            Rrow[slot_of(0)] = r0;
+            if constexpr (LIN) Erow[slot_of(0)] = exp2_or_zero(r0);
         }
-        Eh[M - 1] = 1.0f;
-        fH[M - 1] = 0.0f;
+        const float r0 = cact ? fmaxf(proj_s(0, cl), NEG) : 0.0f;
+        Eh[M - 1] = exp2_or_zero(r0);
+        fH[M - 1] = r0;
     } else {
         const size_t ck = ckrow + span;
         if (bact)
@@ -336,11 +360,15 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
     const int sq = stg ? bt / C : 0;
     const int sl = stg ? bt - sq * C : 0;
     double pf[M];                                          // raw S of the chunk after next
+    float pfe[M], pfs[M];                                  // and its projections (base 2)
     auto stage_load = [&](int tcs) {
 #pragma unroll
         for (int d = 0; d < M; ++d) {
             const int t = tcs + M * sq + d;
-            pf[d] = (stg && t <= t1) ? Sb[sidx(t, sl)] : 0.0;
+            const bool in = stg && t <= t1;
+            pf[d] = in ? Sb[sidx(t, sl)] : 0.0;
+            pfe[d] = in ? proj_e(t, sl) : 0.0f;
+            pfs[d] = in ? proj_s(t, sl) : 0.0f;
         }
     };
     auto stage_store = [&](int buf) {
@@ -351,13 +379,31 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
         double2* dS = reinterpret_cast<double2*>(Sbuf + buf * chunkN + sl * CH + M * sq);
         dS[0] = make_double2(sv[0], sv[1]);
         dS[1] = make_double2(sv[2], sv[3]);
-        float g[M];
+        float* f = Fst + (size_t)buf * 5 * C * CH + sl * CH + M * sq;
+        if constexpr (PROJ) {
+            float ge[M], gs[M];
 #pragma unroll
-        for (int d = 0; d < M; ++d) g[d] = (float)(sv[d] - sv[0]);
-        float* f = Fst + (size_t)buf * 3 * C * CH + sl * CH + M * sq;
-        st4(f, make_float4(1.0f, fast_exp2(g[1]), fast_exp2(g[2]), fast_exp2(g[3])));
-        st4(f + C * CH, make_float4(1.0f, fast_exp2(-g[1]), fast_exp2(-g[2]), fast_exp2(-g[3])));
-        st4(f + 2 * C * CH, make_float4(0.0f, g[1], g[2], g[3]));
+            for (int d = 0; d < M; ++d) {
+                const float g = (float)(sv[d] - sv[0]);
+                ge[d] = g + pfe[d];
+                gs[d] = g - pfs[d];
+            }
+            st4(f, make_float4(fast_exp2(ge[0]), fast_exp2(ge[1]), fast_exp2(ge[2]),
+                               fast_exp2(ge[3])));
+            st4(f + C * CH, make_float4(fast_exp2(-gs[0]), fast_exp2(-gs[1]), fast_exp2(-gs[2]),
+                                        fast_exp2(-gs[3])));
+            st4(f + 2 * C * CH, make_float4(ge[0], ge[1], ge[2], ge[3]));
+            st4(f + 3 * C * CH, make_float4(gs[0], gs[1], gs[2], gs[3]));
+            st4(f + 4 * C * CH, make_float4(pfe[0], pfe[1], pfe[2], pfe[3]));
+        } else {
+            // one side: ge = gs = g
+            float g[M];
+#pragma unroll
+            for (int d = 0; d < M; ++d) g[d] = (float)(sv[d] - sv[0]);
+            st4(f, make_float4(1.0f, fast_exp2(g[1]), fast_exp2(g[2]), fast_exp2(g[3])));
+            st4(f + C * CH, make_float4(1.0f, fast_exp2(-g[1]), fast_exp2(-g[2]), fast_exp2(-g[3])));
+            st4(f + 2 * C * CH, make_float4(0.0f, g[1], g[2], g[3]));
+        }
     };
     if (!chain) {
         stage_load(t0 + 1);
@@ -478,25 +524,29 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
             }
             // ---- per-round constants (H fixed inside the round)
             const double H0 = H;
-            float hb[M], yv[M], fb[M], fo[M];
+            float hbe[M], hbs[M], yv[M], fb[M], fo[M];
             {
-                // S(p_m) + B_c - H0 from S(p_0) and the staged differences; the scales
-                // 2^(hb + dmax) and 2^(tmax - hb) from one exp2 each and staged factors
-                const float* f = Fst + (size_t)(nch & 1) * 3 * C * CH + cl * CH + row0;
-                const float4 sg4 = ld4(f), is4 = ld4(f + C * CH), g4 = ld4(f + 2 * C * CH);
+                // end side S(p_m) + pe + B_c - H0 and start side S(p_m) - ps + B_c - H0
+                // from S(p_0) and the staged differences; the scales 2^(hbe + dmax) and
+                // 2^(tmax - hbs) from one exp2 each and staged factors
+                const float* f = Fst + (size_t)(nch & 1) * 5 * C * CH + cl * CH + row0;
+                const float4 fe4 = ld4(f), fs4 = ld4(f + C * CH), ge4 = ld4(f + 2 * C * CH);
+                const float4 gs4 = PROJ ? ld4(f + 3 * C * CH) : ge4;
                 const float hb0 = (float)(Sch[cl * CH + row0] + BH);
                 const float y0 = cact ? fast_exp2(hb0 + dmax) : 0.0f;
                 const float fo0 = tmax - hb0;
                 const float f0 = fast_exp2(fo0);
-                const float gs[M] = {g4.x, g4.y, g4.z, g4.w};
-                const float ss[M] = {sg4.x, sg4.y, sg4.z, sg4.w};
-                const float is[M] = {is4.x, is4.y, is4.z, is4.w};
+                const float ge[M] = {ge4.x, ge4.y, ge4.z, ge4.w};
+                const float gs[M] = {gs4.x, gs4.y, gs4.z, gs4.w};
+                const float fe[M] = {fe4.x, fe4.y, fe4.z, fe4.w};
+                const float fs[M] = {fs4.x, fs4.y, fs4.z, fs4.w};
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
-                    hb[m] = hb0 + gs[m];
-                    yv[m] = y0 * ss[m];                      // message scale
+                    hbe[m] = hb0 + ge[m];
+                    hbs[m] = hb0 + gs[m];
+                    yv[m] = y0 * fe[m];                      // message scale
                     fo[m] = fo0 - gs[m];
-                    fb[m] = f0 * is[m];                      // ring-entry scale
+                    fb[m] = f0 * fs[m];                      // ring-entry scale
                 }
             }
             // ---- fast pass (linear space, no branches)
@@ -559,7 +609,6 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                 for (int i = 0; i < M; ++i) Rl[i] = fmaxf(fast_log2(sH[i]) + fH[i], NEG);
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
-                    const float hp = hb[m];
                     // durations 1 .. m+4 from the history, then the bulk sum; unused: NEG
                     float x[2 * M + 1], xd[2 * M + 1];
 #pragma unroll
@@ -571,12 +620,12 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                     xd[2 * M] = 0.0f;
                     const float sigma = group_lse<1, 2 * M + 1>(x, xd);
                     sig[m] = sigma;
-                    const float u = cact ? hp + sigma : NEG;
+                    const float u = cact ? hbe[m] + sigma : NEG;
                     float uv[CP];
 #pragma unroll
                     for (int i = 0; i < CP; ++i)
                         uv[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), i));
-                    const float rn = group_lse<1, CP>(uv, treg) - hp;
+                    const float rn = group_lse<1, CP>(uv, treg) - hbs[m];
                     const float lq = group_lse<1, CP>(uv, zero);
                     Rl[M + m] = rn;
                     Eh[M + m] = exp2_or_zero(rn);
@@ -622,11 +671,13 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
                 st4(ns + M, make_float4(fH[M], fH[M + 1], fH[M + 2], fH[M + 3]));
             }
             if (a.write_xa) {
+                const float* fpe = Fst + (size_t)(nch & 1) * 5 * C * CH + 4 * C * CH + cl * CH + row0;
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
                     const int p = rs + 1 + m;
                     if (p <= t1 && cact) {
-                        const double Sp = Sch[cl * CH + row0 + m];
+                        double Sp = Sch[cl * CH + row0 + m];
+                        if constexpr (PROJ) Sp += (double)fpe[m];
                         const float sgl = replayed ? sig[m] : fast_log2(sig[m]) + dmax;
                         Xout[(outrow + (dir == 0 ? p : L - p)) * C + cl] = (Sp + Bc + (double)sgl) * LN2;
                         if (p < t1) {
@@ -689,33 +740,34 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
 }
 
 // ------------------------------------------------------------------ launch
-template <int G, int BPL, int CP, bool LIN>
+template <int G, int BPL, int CP, bool LIN, bool PROJ>
 static hipError_t launch_lse_round_inst(const SweepArgs& a, dim3 grid, const SweepCfg& cfg,
                                         hipStream_t stream) {
     if (cfg.NT > 320 || cfg.lse.CH > lse_chunk_max(G) || cfg.lse.CH % ROUND != 0 ||
         cfg.lse.P % 4 != 0 || cfg.RS % ROUND != 0)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_lse_round<G, BPL, CP, LIN>), grid, dim3(cfg.NT), cfg.lse.bytes, stream,
+    hipLaunchKernelGGL((k_lse_round<G, BPL, CP, LIN, PROJ>), grid, dim3(cfg.NT), cfg.lse.bytes, stream,
                        a, cfg.RS, cfg.lse.P, cfg.lse.CH);
     return hipGetLastError();
 }
 
 #define LSE_ROUND_BPL_CASES(G, CP)                                                   \
     switch (cfg.BPL) {                                                               \
-        case 0: return launch_lse_round_inst<G, 0, CP, LIN>(a, grid, cfg, stream);      \
-        case 1: return launch_lse_round_inst<G, 1, CP, LIN>(a, grid, cfg, stream);      \
-        case 2: return launch_lse_round_inst<G, 2, CP, LIN>(a, grid, cfg, stream);      \
-        case 3: return launch_lse_round_inst<G, 3, CP, LIN>(a, grid, cfg, stream);      \
-        case 4: return launch_lse_round_inst<G, 4, CP, LIN>(a, grid, cfg, stream);      \
-        case 5: return launch_lse_round_inst<G, 5, CP, LIN>(a, grid, cfg, stream);      \
-        case 6: return launch_lse_round_inst<G, 6, CP, LIN>(a, grid, cfg, stream);      \
-        case 7: return launch_lse_round_inst<G, 7, CP, LIN>(a, grid, cfg, stream);      \
-        case 8: return launch_lse_round_inst<G, 8, CP, LIN>(a, grid, cfg, stream);      \
+        case 0: return launch_lse_round_inst<G, 0, CP, LIN, PROJ>(a, grid, cfg, stream);      \
+        case 1: return launch_lse_round_inst<G, 1, CP, LIN, PROJ>(a, grid, cfg, stream);      \
+        case 2: return launch_lse_round_inst<G, 2, CP, LIN, PROJ>(a, grid, cfg, stream);      \
+        case 3: return launch_lse_round_inst<G, 3, CP, LIN, PROJ>(a, grid, cfg, stream);      \
+        case 4: return launch_lse_round_inst<G, 4, CP, LIN, PROJ>(a, grid, cfg, stream);      \
+        case 5: return launch_lse_round_inst<G, 5, CP, LIN, PROJ>(a, grid, cfg, stream);      \
+        case 6: return launch_lse_round_inst<G, 6, CP, LIN, PROJ>(a, grid, cfg, stream);      \
+        case 7: return launch_lse_round_inst<G, 7, CP, LIN, PROJ>(a, grid, cfg, stream);      \
+        case 8: return launch_lse_round_inst<G, 8, CP, LIN, PROJ>(a, grid, cfg, stream);      \
         default: return hipErrorInvalidValue;                                        \
     }
 
-// every shape of the round kernel with (LIN) or without the linear ring
-template <bool LIN>
+// every shape of the round kernel with (LIN) or without the linear ring, with (PROJ) or
+// without boundary projections
+template <bool LIN, bool PROJ>
 hipError_t launch_lse_round_layout(const SweepCfg& cfg, const SweepArgs& a, int ndir,
                                    hipStream_t stream) {
     const dim3 grid = a.mode == MODE_FULL ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);

@@ -70,12 +70,22 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
     const int RMASK = RS - 1;
     const int chunkN = CH * C;
 
-    double* Sbuf = lds;                                  // [2][CH][C]
-    float* R = (float*)(Sbuf + 2 * chunkN);              // [C+1][P]
+    // end side S(t) + proj_end[t-1] and start side S(t) - proj_start[t]:
+    // [2 chunks][2 sides][CH][C]
+    double* Sbuf = lds;
+    float* R = (float*)(Sbuf + 4 * chunkN);              // [C+1][P]
     float* u_sh = R + (C + 1) * P;                       // [2][UP]
     float* Rrow = R + cr * P;
 
     const double* Sb = a.S + (size_t)b * (T + 1) * C;
+    const float* PSb = a.proj_start ? a.proj_start + (size_t)b * T * C : nullptr;
+    const float* PEb = a.proj_end ? a.proj_end + (size_t)b * T * C : nullptr;
+    // projections at position t (flat index q = t*C + l): 0 when absent or outside
+    // [1, L] (end side) / [0, L-1] (start side)
+    auto proj_e = [&](int t, size_t q) -> float {
+        return (PEb && t >= 1 && t <= L) ? PEb[q - C] : 0.0f;
+    };
+    auto proj_s = [&](int t, size_t q) -> float { return (PSb && t < L) ? PSb[q] : 0.0f; };
     for (int q = tid; q < (C + 1) * P; q += NT) R[q] = NEG;
     for (int q = tid; q < 2 * UP; q += NT) u_sh[q] = NEG;
 
@@ -98,8 +108,9 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
     auto put = [&](int pos, float r) { ring_put<MIR>(Rrow, pos, RS, r); };
 
     double Bc = 0.0, H = 0.0;
-    float Mref = 0.0f, Rn1 = 0.0f, Rn2 = NEG;
-    if (act && j == 0) put(0, 0.0f);        // position 0: no transition into it
+    // position 0: no transition into it; the ring entry is its start-side projection
+    float Mref = 0.0f, Rn1 = act ? fmaxf(proj_s(0, cc), NEG) : 0.0f, Rn2 = NEG;
+    if (act && j == 0) put(0, Rn1);
     __syncthreads();
 
     int kQa = 0, kQb = 0, kb_prev = 0;
@@ -109,25 +120,33 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
     // ---------------------------------------------------------------- S staging
     for (int q = tid; q < chunkN; q += NT) {
         const int t = 1 + q / C;
-        Sbuf[q] = (t <= L) ? Sb[(size_t)C + q] : 0.0;
+        const size_t gq = (size_t)C + q;
+        const double sv = (t <= L) ? Sb[gq] : 0.0;
+        Sbuf[q] = (t <= L) ? sv + (double)proj_e(t, gq) : 0.0;
+        Sbuf[chunkN + q] = (t <= L) ? sv - (double)proj_s(t, gq) : 0.0;
     }
     // the chunk after: values in registers, published CH positions later
-    double pf[PF];
+    double pf[PF], pfs[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
         const int q = tid + i * NT;
-        pf[i] = 0.0;
-        if (q < chunkN && 1 + CH + q / C <= L) pf[i] = Sb[(size_t)(1 + CH) * C + q];
+        pf[i] = pfs[i] = 0.0;
+        const int t = 1 + CH + q / C;
+        if (q < chunkN && t <= L) {
+            const size_t gq = (size_t)(1 + CH) * C + q;
+            pf[i] = Sb[gq] + (double)proj_e(t, gq);
+            pfs[i] = Sb[gq] - (double)proj_s(t, gq);
+        }
     }
     __syncthreads();
     __builtin_amdgcn_s_waitcnt(0);   // nothing loaded before the loop is waited on inside it
 
-    float h_prev = 0.0f;
+    float h_prev = 0.0f;      // start side of the previous position, relative to H
     const size_t outrow = (size_t)b * (T + 1);
 
     // ---------------------------------------------------------------- main loop
     for (int tc = 1, nch = 0; tc <= L; tc += CH, ++nch) {
-        const double* Srow = Sbuf + (nch & 1) * chunkN;
+        const double* Srow = Sbuf + (nch & 1) * 2 * chunkN;   // end side; start side at +chunkN
         const int rows = min(CH, L - tc + 1);
         for (int row = 0; row < rows; ++row) {
             const int t = tc + row;
@@ -167,10 +186,9 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
             const float e1 = Rn1 + d0, e2 = Rn2 + d1;
             const float sig = fmaxf(fmaxf(Qa, e1), e2);
             kb_prev = (e1 == sig) ? 1 : (e2 == sig) ? 2 : kQa;
-            const double g = Srow[row * C + cc] + Bc;
-            const float h = (float)(g - H);
+            const float h = (float)(Srow[row * C + cc] + Bc - H);
             if (j == 0) u_sh[(t & 1) * UP + cr] = h + sig;
-            h_prev = h;
+            h_prev = (float)(Srow[chunkN + row * C + cc] + Bc - H);
 
             // ---- [D] rebase, then the bulk value for position t+2
             if ((t & (REBASE - 1)) == 0) {
@@ -202,18 +220,23 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
         }
         // ---- S staging: publish the next chunk, fetch the one after
         if (tc + CH <= L) {
-            double* dst = Sbuf + ((nch + 1) & 1) * chunkN;
+            double* dst = Sbuf + ((nch + 1) & 1) * 2 * chunkN;
 #pragma unroll
             for (int i = 0; i < PF; ++i) {
                 const int q = tid + i * NT;
-                if (q < chunkN) dst[q] = pf[i];
+                if (q < chunkN) {
+                    dst[q] = pf[i];
+                    dst[chunkN + q] = pfs[i];
+                }
             }
 #pragma unroll
             for (int i = 0; i < PF; ++i) {
                 const int q = tid + i * NT;
                 if (q < chunkN) {
                     const int tt = tc + 2 * CH + q / C;
-                    pf[i] = (tt <= L) ? Sb[(size_t)(tc + 2 * CH) * C + q] : 0.0;
+                    const size_t gq = (size_t)(tc + 2 * CH) * C + q;
+                    pf[i] = (tt <= L) ? Sb[gq] + (double)proj_e(tt, gq) : 0.0;
+                    pfs[i] = (tt <= L) ? Sb[gq] - (double)proj_s(tt, gq) : 0.0;
                 }
             }
             __syncthreads();

@@ -6,7 +6,9 @@
 namespace semicrf {
 
 hipError_t launch_maxplus_plain(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream) {
-    if (cfg.split) return launch_maxplus_round(cfg, a, stream);
+    if (cfg.split)
+        return (a.proj_start || a.proj_end) ? launch_maxplus_round_proj(cfg, a, stream)
+                                            : launch_maxplus_round<false>(cfg, a, stream);
     return launch_maxplus_layout<false>(cfg, a, stream);
 }
 

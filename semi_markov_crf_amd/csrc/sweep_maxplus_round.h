@@ -88,8 +88,9 @@ __device__ __forceinline__ int min_tree_i(const int* x) {
 }  // namespace
 
 // G: bulk lanes per label (C <= 256/G); BPL: ring blocks per bulk lane; CP: labels the
-// chain broadcasts (>= C).  Grid (B, 2 directions), block 64 + ceil(C*G/64)*64 threads.
-template <int G, int BPL, int CP>
+// chain broadcasts (>= C); PROJ: boundary projections present.  Grid (B, 2 directions),
+// block 64 + ceil(C*G/64)*64 threads.
+template <int G, int BPL, int CP, bool PROJ>
 __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const int RS,
                                                       const int P, const int CH) {
     constexpr int M = ROUND;
@@ -123,7 +124,8 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
 
     double* Sbuf = lds;                                    // [2][C][CH] label-major
     double* SL = Sbuf + 2 * C * CH;                        // [C] (padded to 16 bytes)
-    float* R = (float*)(SL + (C + 1) / 2 * 2);             // [C+1][P]
+    float* Pst = (float*)(SL + (C + 1) / 2 * 2);           // [2][end, start][C][CH] projections
+    float* R = Pst + 4 * C * CH;                           // [C+1][P]
     float* qsh = R + (C + 1) * P;                          // [2 rounds][CP][max, k][M]
     float* dlsh = qsh + 2 * CP * 2 * M;                    // [CP4] rebase shift per label
     float* sink = dlsh + CP4;                              // [8]
@@ -132,6 +134,22 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
 
     const double* Sb = a.S + (size_t)b * (T + 1) * C;
     for (int q = tid; q < C; q += NT) SL[q] = Sb[(size_t)L * C + q];
+    // projections of sweep position p: end side (segments ending at p) and start side
+    // (segments starting at p); 0 without projections or outside [1, L] / [0, L-1]
+    const float* PSb = a.proj_start ? a.proj_start + (size_t)b * T * C : nullptr;
+    const float* PEb = a.proj_end ? a.proj_end + (size_t)b * T * C : nullptr;
+    auto proj_e = [&](int p, int q) -> float {
+        if constexpr (!PROJ) return 0.0f;
+        const float* src = dir == 0 ? PEb : PSb;
+        const int t = dir == 0 ? p - 1 : L - p;
+        return (src && p >= 1 && p <= L) ? src[(size_t)t * C + q] : 0.0f;
+    };
+    auto proj_s = [&](int p, int q) -> float {
+        if constexpr (!PROJ) return 0.0f;
+        const float* src = dir == 0 ? PSb : PEb;
+        const int t = dir == 0 ? p : L - 1 - p;
+        return (src && p >= 0 && p < L) ? src[(size_t)t * C + q] : 0.0f;
+    };
     for (int q = tid; q < (C + 1) * P; q += NT) R[q] = NEG;
     for (int q = tid; q < 2 * CP * 2 * M; q += NT) qsh[q] = ((q / M) & 1) ? __int_as_float(INT_MAX) : NEG;
     if (tid < M) nblk[tid] = NEG;
@@ -198,13 +216,14 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
     };
 
     // ---------------------------------------------------------------- start state
-    if (bact && j == 0) Rrow[slot_mp(-1, RMASK) + M - 1] = 0.0f;   // position 0
+    // position 0: no transition into it; the ring entry is its start-side projection
+    if (bact && j == 0) Rrow[slot_mp(-1, RMASK) + M - 1] = fmaxf(proj_s(0, cb), NEG);
     // chain history, i < M: the previous round's positions (round start) - 3 + i; i >= M:
     // this round's (ring entries A - B_c)
     float Rh[2 * M];
 #pragma unroll
     for (int i = 0; i < 2 * M; ++i) Rh[i] = NEG;
-    Rh[M - 1] = 0.0f;
+    Rh[M - 1] = cact ? fmaxf(proj_s(0, cl), NEG) : 0.0f;
     double Bc = 0.0, H = 0.0;
     float Mref = 0.0f;
 
@@ -212,13 +231,22 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
     auto sidx = [&](int t, int q) -> size_t { return (size_t)(dir == 0 ? t : L - t) * C + q; };
     auto spub = [&](double raw, int q) -> double { return dir == 0 ? raw : SL[q] - raw; };
     double pf[PF];
+    float pfe[PF], pfs[PF];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) pf[i] = 0.0;
+    for (int i = 0; i < PF; ++i) {
+        pf[i] = 0.0;
+        pfe[i] = pfs[i] = 0.0f;
+    }
     if (!chain) {
         for (int q = bt; q < chunkN; q += NB) {
             const int row = q / C, l = q - row * C;
             const int t = t0 + 1 + row;
-            Sbuf[l * CH + row] = (t <= t1) ? spub(Sb[sidx(t, l)], l) : 0.0;
+            const bool in = t <= t1;
+            Sbuf[l * CH + row] = in ? spub(Sb[sidx(t, l)], l) : 0.0;
+            if constexpr (PROJ) {
+                Pst[l * CH + row] = in ? proj_e(t, l) : 0.0f;
+                Pst[C * CH + l * CH + row] = in ? proj_s(t, l) : 0.0f;
+            }
         }
 #pragma unroll
         for (int i = 0; i < PF; ++i) {
@@ -226,7 +254,11 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
             if (q < chunkN) {
                 const int row = q / C, l = q - row * C;
                 const int t = t0 + 1 + CH + row;
-                if (t <= t1) pf[i] = Sb[sidx(t, l)];
+                if (t <= t1) {
+                    pf[i] = Sb[sidx(t, l)];
+                    pfe[i] = proj_e(t, l);
+                    pfs[i] = proj_s(t, l);
+                }
             }
         }
     }
@@ -276,15 +308,28 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
                 pend = true;
             }
             const double H0 = H;
-            float hb[M], hbx[M];
+            float hbs[M], hbx[M];
             {
                 const double2* sp = reinterpret_cast<const double2*>(Sch + cl * CH + row0);
                 const double2 s01 = sp[0], s23 = sp[1];
                 const double sv4[M] = {s01.x, s01.y, s23.x, s23.y};
+                if constexpr (PROJ) {
+                    const float* pp = Pst + (size_t)(nch & 1) * 2 * C * CH + cl * CH + row0;
+                    const float4 pe4 = ld4_mp(pp), ps4 = ld4_mp(pp + C * CH);
+                    const float pe[M] = {pe4.x, pe4.y, pe4.z, pe4.w};
+                    const float ps[M] = {ps4.x, ps4.y, ps4.z, ps4.w};
 #pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    hb[m] = (float)(sv4[m] + BH);            // S(p_m) + B_c - H0
-                    hbx[m] = cact ? hb[m] : NEG;
+                    for (int m = 0; m < M; ++m) {
+                        const double hm = sv4[m] + BH;       // S(p_m) + B_c - H0
+                        hbs[m] = (float)(hm - (double)ps[m]); // start side
+                        hbx[m] = cact ? (float)(hm + (double)pe[m]) : NEG;   // end side
+                    }
+                } else {
+#pragma unroll
+                    for (int m = 0; m < M; ++m) {
+                        hbs[m] = (float)(sv4[m] + BH);       // S(p_m) + B_c - H0, both sides
+                        hbx[m] = cact ? hbs[m] : NEG;
+                    }
                 }
             }
             // the round's last step inside the sweep sets the normaliser
@@ -319,7 +364,7 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
 #pragma unroll
                 for (int i = 0; i < CP; ++i) ci[i] = y[i] == mt ? i : INT_MAX;
                 const int cbest = min_tree_i<CP>(ci);
-                Rh[M + m] = mt - hb[m];
+                Rh[M + m] = mt - hbs[m];
                 if (p <= t1 && cact)   // the label of position L + 1 is never read
                     bpp[m * C] = (uint32_t)kbest | ((uint32_t)cbest << 16);
                 if (m == ml) {
@@ -344,12 +389,17 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
         } else {
             if (rs + 1 == tc && tc + CH <= t1) {
                 double* dst = Sbuf + ((nch + 1) & 1) * chunkN;
+                float* dp = Pst + (size_t)((nch + 1) & 1) * 2 * C * CH;
 #pragma unroll
                 for (int i = 0; i < PF; ++i) {
                     const int q = bt + i * NB;
                     if (q < chunkN) {
                         const int row = q / C, l = q - row * C;
                         dst[l * CH + row] = spub(pf[i], l);
+                        if constexpr (PROJ) {
+                            dp[l * CH + row] = pfe[i];
+                            dp[C * CH + l * CH + row] = pfs[i];
+                        }
                     }
                 }
 #pragma unroll
@@ -358,7 +408,10 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
                     if (q < chunkN) {
                         const int rr = q / C, l = q - rr * C;
                         const int tt = tc + 2 * CH + rr;
-                        pf[i] = (tt <= t1) ? Sb[sidx(tt, l)] : 0.0;
+                        const bool in = tt <= t1;
+                        pf[i] = in ? Sb[sidx(tt, l)] : 0.0;
+                        pfe[i] = in ? proj_e(tt, l) : 0.0f;
+                        pfs[i] = in ? proj_s(tt, l) : 0.0f;
                     }
                 }
             }
@@ -390,33 +443,33 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
 }
 
 // ------------------------------------------------------------------ launch
-template <int G, int BPL, int CP>
+template <int G, int BPL, int CP, bool PROJ>
 static hipError_t launch_maxplus_round_inst(const SweepArgs& a, const SweepCfg& cfg,
                                             hipStream_t stream) {
     if (cfg.NT > 320 || cfg.vit.CH > lse_chunk_max(G) || cfg.vit.CH % ROUND != 0 ||
         cfg.vit.P % 4 != 0 || cfg.RS % ROUND != 0)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_maxplus_round<G, BPL, CP>), dim3(a.B, 2), dim3(cfg.NT), cfg.vit.bytes,
+    hipLaunchKernelGGL((k_maxplus_round<G, BPL, CP, PROJ>), dim3(a.B, 2), dim3(cfg.NT), cfg.vit.bytes,
                        stream, a, cfg.RS, cfg.vit.P, cfg.vit.CH);
     return hipGetLastError();
 }
 
 #define MAXPLUS_ROUND_BPL_CASES(G, CP)                                         \
     switch (cfg.BPL) {                                                         \
-        case 0: return launch_maxplus_round_inst<G, 0, CP>(a, cfg, stream);       \
-        case 1: return launch_maxplus_round_inst<G, 1, CP>(a, cfg, stream);       \
-        case 2: return launch_maxplus_round_inst<G, 2, CP>(a, cfg, stream);       \
-        case 3: return launch_maxplus_round_inst<G, 3, CP>(a, cfg, stream);       \
-        case 4: return launch_maxplus_round_inst<G, 4, CP>(a, cfg, stream);       \
-        case 5: return launch_maxplus_round_inst<G, 5, CP>(a, cfg, stream);       \
-        case 6: return launch_maxplus_round_inst<G, 6, CP>(a, cfg, stream);       \
-        case 7: return launch_maxplus_round_inst<G, 7, CP>(a, cfg, stream);       \
-        case 8: return launch_maxplus_round_inst<G, 8, CP>(a, cfg, stream);       \
+        case 0: return launch_maxplus_round_inst<G, 0, CP, PROJ>(a, cfg, stream);       \
+        case 1: return launch_maxplus_round_inst<G, 1, CP, PROJ>(a, cfg, stream);       \
+        case 2: return launch_maxplus_round_inst<G, 2, CP, PROJ>(a, cfg, stream);       \
+        case 3: return launch_maxplus_round_inst<G, 3, CP, PROJ>(a, cfg, stream);       \
+        case 4: return launch_maxplus_round_inst<G, 4, CP, PROJ>(a, cfg, stream);       \
+        case 5: return launch_maxplus_round_inst<G, 5, CP, PROJ>(a, cfg, stream);       \
+        case 6: return launch_maxplus_round_inst<G, 6, CP, PROJ>(a, cfg, stream);       \
+        case 7: return launch_maxplus_round_inst<G, 7, CP, PROJ>(a, cfg, stream);       \
+        case 8: return launch_maxplus_round_inst<G, 8, CP, PROJ>(a, cfg, stream);       \
         default: return hipErrorInvalidValue;                                  \
     }
 
-inline hipError_t launch_maxplus_round(const SweepCfg& cfg, const SweepArgs& a,
-                                       hipStream_t stream) {
+template <bool PROJ>
+hipError_t launch_maxplus_round(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream) {
     if (cfg.G == 64 && cfg.CPr == 4) { MAXPLUS_ROUND_BPL_CASES(64, 4) }
     if (cfg.G == 32 && cfg.CPr == 6) { MAXPLUS_ROUND_BPL_CASES(32, 6) }
     if (cfg.G == 32 && cfg.CPr == 8) { MAXPLUS_ROUND_BPL_CASES(32, 8) }

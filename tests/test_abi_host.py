@@ -102,31 +102,40 @@ def test_argument_validation_returns_before_any_launch(native):
     lib = native.load()
     p = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
     n = None
-    # NULL inputs / outputs
-    assert lib.semicrf_logz(n, p, p, p, 1, 4, 2, 2, n, p, 1 << 20, p) == 1
-    assert lib.semicrf_logz(p, p, p, p, 1, 4, 2, 2, n, p, 1 << 20, n) == 1
+    # NULL inputs / outputs (projections NULL: absent)
+    assert lib.semicrf_logz(n, p, p, p, n, n, 1, 4, 2, 2, n, p, 1 << 20, p) == 1
+    assert lib.semicrf_logz(p, p, p, p, n, n, 1, 4, 2, 2, n, p, 1 << 20, n) == 1
     # bad sizes
-    assert lib.semicrf_logz(p, p, p, p, 0, 4, 2, 2, n, p, 1 << 20, p) == 1
-    assert lib.semicrf_logz(p, p, p, p, 1, 4, 2, 0, n, p, 1 << 20, p) == 1
+    assert lib.semicrf_logz(p, p, p, p, n, n, 0, 4, 2, 2, n, p, 1 << 20, p) == 1
+    assert lib.semicrf_logz(p, p, p, p, n, n, 1, 4, 2, 0, n, p, 1 << 20, p) == 1
     # unsupported label count
-    assert lib.semicrf_logz(p, p, p, p, 1, 4, 4096, 2, n, p, 1 << 20, p) == 3
+    assert lib.semicrf_logz(p, p, p, p, n, n, 1, 4, 4096, 2, n, p, 1 << 20, p) == 3
     # workspace missing, too small, misaligned
     need = lib.semicrf_workspace_bytes(0, 1, 4, 2, 2, 0)
-    assert lib.semicrf_logz(p, p, p, p, 1, 4, 2, 2, n, n, need, p) == 2
-    assert lib.semicrf_logz(p, p, p, p, 1, 4, 2, 2, n, p, need - 1, p) == 2
-    assert lib.semicrf_logz(p, p, p, p, 1, 4, 2, 2, n, ctypes.c_void_p(0x1008), need, p) == 2
+    assert lib.semicrf_logz(p, p, p, p, p, p, 1, 4, 2, 2, n, n, need, p) == 2
+    assert lib.semicrf_logz(p, p, p, p, p, p, 1, 4, 2, 2, n, p, need - 1, p) == 2
+    assert lib.semicrf_logz(p, p, p, p, n, n, 1, 4, 2, 2, n, ctypes.c_void_p(0x1008), need, p) == 2
     # backward: required gradient outputs, negative delta
     need = lib.semicrf_workspace_bytes(1, 1, 4, 2, 2, 0)
-    assert lib.semicrf_backward(p, p, p, p, 1, 4, 2, 2, 0, n, p, need, n, n, p, p, n, n) == 1
-    assert lib.semicrf_backward(p, p, p, p, 1, 4, 2, 2, -1, n, p, need, n, p, p, p, n, n) == 1
-    assert lib.semicrf_backward(p, p, p, p, 1, 4, 2, 2, 0, n, p, 16, n, p, p, p, n, n) == 2
+    assert lib.semicrf_backward(p, p, p, p, n, n, 1, 4, 2, 2, 0, n, p, need, n, n, p, p, n, n,
+                                n, n, n) == 1
+    assert lib.semicrf_backward(p, p, p, p, n, n, 1, 4, 2, 2, -1, n, p, need, n, p, p, p, n, n,
+                                p, p, p) == 1
+    assert lib.semicrf_backward(p, p, p, p, p, p, 1, 4, 2, 2, 0, n, p, 16, n, p, p, p, n, n,
+                                n, n, n) == 2
+    # training loss: gold segmentation and loss output required
+    assert lib.semicrf_nll(p, p, p, p, n, n, n, p, 1, 4, 2, 2, 0, n, p, need, n, p, p, p, p,
+                           n, n) == 1
+    assert lib.semicrf_nll(p, p, p, p, n, n, p, p, 1, 4, 2, 2, 0, n, p, need, n, n, p, p, p,
+                           n, n) == 1
     # viterbi outputs
     need = lib.semicrf_workspace_bytes(2, 1, 4, 2, 2, 0)
-    assert lib.semicrf_viterbi(p, p, p, p, 1, 4, 2, 2, n, p, need, p, n, p) == 1
+    assert lib.semicrf_viterbi(p, p, p, p, n, n, 1, 4, 2, 2, n, p, need, p, n, p) == 1
     assert lib.semicrf_read_status(n, n) == 2
     need = lib.semicrf_workspace_bytes(3, 1, 4, 2, 1, 0)
     assert lib.semicrf_prefix(p, p, 1, 4, 2, n, p, need, n) == 1
     assert lib.semicrf_prefix(p, p, 1, 4, 2, n, p, need - 1, p) == 2
     for f in ("semicrf_logz_staged", "semicrf_viterbi_staged"):
-        args = [p, p, p, p, 1, 4, 2, 2, n, p, 1 << 20, p] + ([n] if f == "semicrf_logz_staged" else [p, p, n])
+        args = [p, p, p, p, n, n, 1, 4, 2, 2, n, p, 1 << 20, p] + (
+            [n] if f == "semicrf_logz_staged" else [p, p, n])
         assert getattr(lib, f)(*args) == 1          # events pointer required
