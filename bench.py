@@ -99,6 +99,64 @@ def cpu_baseline(w, sample_positions):
             "seconds": dt}
 
 
+def _time_ms(fn, d, reps):
+    """Mean device time of fn() over reps calls after one untimed call (events on the
+    current stream, which the binding launches on)."""
+    import torch
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(d)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize(d)
+    return e0.elapsed_time(e1) / reps
+
+
+def extras(crf, w, em, lengths, trans, dur, d):
+    """Timings beyond the step: the training loss of gold segmentations and the backward
+    pass with boundary projections (both at the genomic shape), and the genome-scale
+    long-duration workload (B=1, T=10^6, K=2000, C=6: backward and Viterbi)."""
+    import numpy as np
+    import torch
+
+    import workloads
+    out = {}
+    pos = w.positions()
+    ws = torch.empty(crf.workspace_bytes(crf.OP_BACKWARD, w.B, w.T, w.C, w.K), dtype=torch.uint8,
+                     device=d)
+    labels, seg = workloads.gold_segmentation(7, w.lengths, w.T, w.C, w.K)
+    gl, gs = torch.from_numpy(labels).to(d), torch.from_numpy(seg).to(d)
+    ms = _time_ms(lambda: crf.nll(em, lengths, trans, dur, gl, gs, workspace=ws), d, 3)
+    ms0 = _time_ms(lambda: crf.backward(em, lengths, trans, dur, workspace=ws), d, 3)
+    out["nll"] = {"ms": ms, "positions_per_s": pos / (ms * 1e-3), "backward_alone_ms": ms0,
+                  "what": "semicrf_nll (backward pass + gold-segmentation kernels), genomic shape"}
+    g = torch.Generator(device="cpu").manual_seed(11)
+    ps = torch.randn(em.shape, generator=g).to(d)
+    pe = torch.randn(em.shape, generator=g).to(d)
+    ms = _time_ms(lambda: crf.backward(em, lengths, trans, dur, proj_start=ps, proj_end=pe,
+                                       workspace=ws), d, 3)
+    out["projections"] = {"ms": ms, "positions_per_s": pos / (ms * 1e-3),
+                          "what": "semicrf_backward with proj_start / proj_end N(0,1), their "
+                                  "gradients and the boundary probabilities, genomic shape"}
+    del ws
+    x = workloads.long_duration()
+    xe, xl, xt, xd = (torch.from_numpy(a).to(d) for a in (x.em, x.lengths, x.trans, x.dur))
+    wsb = torch.empty(crf.workspace_bytes(crf.OP_BACKWARD, x.B, x.T, x.C, x.K), dtype=torch.uint8,
+                      device=d)
+    wsv = torch.empty(crf.workspace_bytes(crf.OP_VITERBI, x.B, x.T, x.C, x.K), dtype=torch.uint8,
+                      device=d)
+    mb = _time_ms(lambda: crf.backward(xe, xl, xt, xd, workspace=wsb), d, 1)
+    mv = _time_ms(lambda: crf.viterbi(xe, xl, xt, xd, workspace=wsv), d, 1)
+    lz = crf.backward(xe, xl, xt, xd, workspace=wsb)["log_z"]
+    assert np.isfinite(lz.cpu().numpy()).all() and crf.read_status(wsb) == 0
+    out["long_duration"] = {"B": x.B, "T": x.T, "K": x.K, "C": x.C, "backward_ms": mb,
+                            "viterbi_ms": mv, "fwd_bwd_positions_per_s": x.positions() / (mb * 1e-3),
+                            "viterbi_positions_per_s": x.positions() / (mv * 1e-3)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +166,9 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=12_000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-scan-roofline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the timings of the training loss, the projections and the "
+                         "long-duration workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
@@ -292,6 +353,9 @@ def main():
                                 "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / PEAK_HBM_BPS,
                                 "ms": ms, "algorithmic_bytes": nbytes}
         del em_big, S_big, ws_s
+
+    if not args.no_extras:
+        out["extras"] = extras(crf, w, em, lengths, trans, dur, d)
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)

@@ -33,8 +33,8 @@
  *    reductions, no floating-point atomics).
  *  - Errors: every call returns a semicrf_status and never aborts.  Host-side
  *    checks: B, T, C, K >= 1, required pointers non-NULL, workspace large enough,
- *    shape supported (SEMICRF_ERR_UNSUPPORTED: C > 128; K above 2049 when C <= 4,
- *    1025 when C <= 8, 513 when C <= 16, 257 when C <= 64, and for 64 < C <= 128
+ *    shape supported (SEMICRF_ERR_UNSUPPORTED: C > 128; K above 2049 when C <= 7,
+ *    1025 when C = 8, 513 when C <= 16, 257 when C <= 64, and for 64 < C <= 128
  *    whatever the 160 KB of LDS of a compute unit holds: 129 down to 97 at C = 128;
  *    semicrf_workspace_bytes returns 0 for such shapes).  A failed
  *    kernel launch returns SEMICRF_ERR_DEVICE.  A length outside [1, T] is only

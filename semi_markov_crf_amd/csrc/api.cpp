@@ -299,7 +299,7 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
     MargArgs m{};
     m.S = a.S; m.Leff = a.Leff; m.trans = trans; m.dur = dur;
     m.B = B; m.T = T; m.C = C; m.K = K;
-    m.tile = lo.tm; m.ntiles = lo.ntm;
+    m.tile = lo.tm; m.ntiles = lo.ntm; m.kchunk = marg_kchunk(C, K);
     m.XF = a.XF; m.AF = a.AF; m.XB = a.XB; m.AB = a.AB; m.logz = a.logz;
     m.Dn = at<double>(workspace, lo.Dn);
     m.dn_tile = at<double>(workspace, lo.dnt);

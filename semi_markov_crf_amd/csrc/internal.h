@@ -14,8 +14,10 @@ struct Shape {
 
 // Positions per tile of the emission reduction / prefix-scan kernels.
 int scan_tile(int C);
-// Positions per tile of the marginal and node-marginal kernels.
+// Positions per tile of the marginal and node-marginal kernels, and durations per chunk
+// of the marginal kernel.
 int marg_tile(int C, int K);
+int marg_kchunk(int C, int K);
 
 // ------------------------------------------------------------------ sweep configuration
 // Lanes are grouped G per label; each lane covers KPL durations and CPL previous labels.
@@ -161,6 +163,7 @@ struct MargArgs {
     const float* dur;
     int B, T, C, K;
     int tile;               // positions per tile
+    int kchunk;             // durations per staged chunk
     int ntiles;             // ceil((T+1) / tile)
     const double* XF; const double* AF; const double* XB; const double* AB;
     const double* logz;

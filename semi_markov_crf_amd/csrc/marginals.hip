@@ -24,39 +24,77 @@
 // at t is the probability that a segment boundary (a segment start) lies at t (the pages
 // check that these boundary probabilities are valid at genome scale, "4. Results and
 // Benchmarks").
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
 namespace semicrf {
 
-int marg_tile(int C, int K) {
-    // LDS (bytes) = 8*C*(2*(TM+K) + 1 + 3*TM) + 4*(K*C + C*C); keep it near 100 KB
-    int tm = 512;
-    auto lds = [&](int t) {
-        return (size_t)8 * C * (2 * (t + K) + 1 + 3 * t) + (size_t)4 * (K * C + C * C);
+// LDS of k_marginals for tile TM and duration chunk KC: the tile's own start / end values,
+// the two shifted windows of a chunk, XF / XB, start / end mass accumulators (fp64), the
+// chunk's durations and the transitions (fp32).
+static size_t marg_lds(int C, int TM, int KC) {
+    return (size_t)8 * C * (8 * TM + 2 * KC) + (size_t)4 * ((size_t)KC * C + (size_t)C * C);
+}
+
+// Tile and duration chunk: the largest tile (fewer per-tile partial sums) whose LDS fits
+// with a chunk of at least min(K, 64) durations; the smallest tile takes any chunk.
+static void marg_shape(int C, int K, int* tm, int* kc) {
+    constexpr size_t BUDGET = 150 * 1024;
+    auto chunks = [&](int t, int min_kc) {
+        if (K <= 512 && marg_lds(C, t, K) <= BUDGET) return K;
+        for (int k = 512; k >= min_kc; k >>= 1)
+            if (k < K && marg_lds(C, t, k) <= BUDGET) return k;
+        return 0;
     };
-    while (tm > 8 && lds(tm) > 100 * 1024) tm >>= 1;
+    for (int t = 512; t >= 8; t >>= 1) {
+        const int k = chunks(t, t > 8 ? std::min(K, 64) : 1);
+        if (k > 0) {
+            *tm = t;
+            *kc = k;
+            return;
+        }
+    }
+    *tm = 8;
+    *kc = 1;
+}
+
+int marg_tile(int C, int K) {
+    int tm, kc;
+    marg_shape(C, K, &tm, &kc);
     return tm;
+}
+
+int marg_kchunk(int C, int K) {
+    int tm, kc;
+    marg_shape(C, K, &tm, &kc);
+    return kc;
 }
 
 constexpr double DNEG = -1.0e300;
 
-// grid (ntiles, B), block 256
+// grid (ntiles, B), block 256.  Durations are taken in chunks [kc0, kc1] of at most KC:
+// per chunk the starts [p0 - kc1, p0 + TM - 1 - kc0] and the ends [p0 + kc0,
+// p0 + TM - 1 + kc1] are staged beside the tile's own starts and ends.
 __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
     extern __shared__ double lds[];
-    const int C = a.C, K = a.K, T = a.T, TM = a.tile;
+    const int C = a.C, K = a.K, T = a.T, TM = a.tile, KC = a.kchunk;
     const int tile = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int L = abs(a.Leff[b]);
     const int p0 = tile * TM;
     const size_t rowC = (size_t)(T + 1) * C;
 
-    double* AFs = lds;                               // [TM + K][C]: starts p0-K .. p0+TM-1
-    double* ABs = AFs + (size_t)(TM + K) * C;        // [TM + K + 1][C]: ends p0 .. p0+TM+K
-    double* XFs = ABs + (size_t)(TM + K + 1) * C;    // [TM][C]
+    double* AFt = lds;                               // [TM][C]: starts p0 .. p0+TM-1
+    double* ABt = AFt + (size_t)TM * C;              // [TM][C]: ends p0 .. p0+TM-1
+    double* AFw = ABt + (size_t)TM * C;              // [TM+KC][C]: starts of the chunk's ends
+    double* ABw = AFw + (size_t)(TM + KC) * C;       // [TM+KC][C]: ends of the chunk's starts
+    double* XFs = ABw + (size_t)(TM + KC) * C;       // [TM][C]
     double* XBs = XFs + (size_t)TM * C;              // [TM][C]
-    double* Dsh = XBs + (size_t)TM * C;              // [TM][C]
-    float* dur2 = (float*)(Dsh + (size_t)TM * C);    // [K][C]
-    float* tr2 = dur2 + (size_t)K * C;               // [C][C]
+    double* Dst = XBs + (size_t)TM * C;              // [TM][C] start mass
+    double* Den = Dst + (size_t)TM * C;              // [TM][C] end mass
+    float* dur2 = (float*)(Den + (size_t)TM * C);    // [KC][C]
+    float* tr2 = dur2 + (size_t)KC * C;              // [C][C]
 
     double* part_dur = a.part_dur + ((size_t)b * a.ntiles + tile) * K * C;
     double* part_trans = a.part_trans + ((size_t)b * a.ntiles + tile) * C * C;
@@ -77,47 +115,77 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
     const double* AF = a.AF + (size_t)b * rowC;
     const double* XB = a.XB + (size_t)b * rowC;
     const double* AB = a.AB + (size_t)b * rowC;
+    // invalid starts / ends get DNEG so that their exponentials vanish
+    auto af = [&](int s, int c) -> double {
+        return (s >= 0 && s <= L - 1) ? AF[(size_t)s * C + c] + Sb[(size_t)L * C + c] - logZ : DNEG;
+    };
+    auto ab = [&](int u, int c) -> double {
+        return (u >= 1 && u <= L) ? AB[(size_t)u * C + c] : DNEG;
+    };
 
-    // stage (invalid positions get DNEG so that their exponentials vanish)
-    for (int q = tid; q < (TM + K) * C; q += 256) {
-        const int r = q / C, c = q - r * C;
-        const int s = p0 - K + r;            // segment start
-        AFs[q] = (s >= 0 && s <= L - 1) ? AF[(size_t)s * C + c] + Sb[(size_t)L * C + c] - logZ : DNEG;
-    }
-    for (int q = tid; q < (TM + K + 1) * C; q += 256) {
-        const int r = q / C, c = q - r * C;
-        const int u = p0 + r;                // segment end
-        ABs[q] = (u >= 1 && u <= L) ? AB[(size_t)u * C + c] : DNEG;
-    }
     for (int q = tid; q < TM * C; q += 256) {
         const int r = q / C, c = q - r * C;
         const int s = p0 + r;
+        AFt[q] = af(s, c);
+        ABt[q] = ab(s, c);
         XFs[q] = (s >= 1 && s <= L - 1) ? XF[(size_t)s * C + c] : DNEG;
         XBs[q] = (s >= 1 && s <= L - 1) ? XB[(size_t)s * C + c] - logZ : DNEG;
+        Dst[q] = 0.0;
+        Den[q] = 0.0;
     }
-    for (int q = tid; q < K * C; q += 256) dur2[q] = fmaxf((float)((double)a.dur[q] * LOG2E), NEG);
     for (int q = tid; q < C * C; q += 256) tr2[q] = fmaxf((float)((double)a.trans[q] * LOG2E), NEG);
+
+    auto seg = [&](double v, float d) -> float { return fast_exp2((float)(v * LOG2E) + d); };
+
+    for (int kc0 = 1; kc0 <= K; kc0 += KC) {
+        const int kc1 = min(K, kc0 + KC - 1);
+        const int nk = kc1 - kc0 + 1;
+        __syncthreads();   // the previous chunk's windows are no longer read
+        for (int q = tid; q < (TM + nk - 1) * C; q += 256) {
+            const int r = q / C, c = q - r * C;
+            AFw[q] = af(p0 - kc1 + r, c);
+            ABw[q] = ab(p0 + kc0 + r, c);
+        }
+        for (int q = tid; q < nk * C; q += 256)
+            dur2[q] = fmaxf((float)((double)a.dur[(size_t)(kc0 - 1) * C + q] * LOG2E), NEG);
+        __syncthreads();
+
+        // ---- phase 1: per position, start and end mass of the chunk's segments
+        for (int q = tid; q < TM * C; q += 256) {
+            const int r = q / C, c = q - r * C;
+            if (p0 + r > L) continue;
+            double st = Dst[q], en = Den[q];
+            const double a0 = AFt[q], b0 = ABt[q];
+#pragma unroll 4
+            for (int k = kc0; k <= kc1; ++k) {
+                const float d = dur2[(k - kc0) * C + c];
+                st += (double)seg(a0 + ABw[(size_t)(r + k - kc0) * C + c], d);   // [t, t+k)
+                en += (double)seg(AFw[(size_t)(r + kc1 - k) * C + c] + b0, d);   // [t-k, t)
+            }
+            Dst[q] = st;
+            Den[q] = en;
+        }
+
+        // ---- phase 2: duration partials, lanes over (k, c), segments starting in the tile
+        for (int q = tid; q < nk * C; q += 256) {
+            const int kk = q / C, c = q - kk * C;
+            const float d = dur2[q];
+            double acc = 0.0;
+#pragma unroll 4
+            for (int r = 0; r < TM; ++r)
+                acc += (double)seg(AFt[(size_t)r * C + c] + ABw[(size_t)(r + kk) * C + c], d);
+            part_dur[(size_t)(kc0 - 1) * C + q] = acc;
+        }
+    }
     __syncthreads();
 
-    // segment posterior from staged values: start s (AF row s - p0 + K), end e (AB row e - p0)
-    auto seg = [&](int ra, int rb, int k, int c) -> float {
-        const double v = AFs[(size_t)ra * C + c] + ABs[(size_t)rb * C + c];
-        return fast_exp2((float)(v * LOG2E) + dur2[(k - 1) * C + c]);
-    };
-
-    // ---- phase 1: per position, start mass - end mass (lanes over (t, c))
+    // ---- start mass - end mass per position, the tile's sums, boundary masses
     for (int q = tid; q < TM * C; q += 256) {
         const int r = q / C, c = q - r * C;
         const int t = p0 + r;
-        double st = 0.0, en = 0.0;
-        if (t <= L) {
-            for (int k = 1; k <= K; ++k) {
-                st += (double)seg(r + K, r + k, k, c);       // segment [t, t+k)
-                en += (double)seg(r + K - k, r, k, c);       // segment [t-k, t)
-            }
-        }
+        const double st = Dst[q], en = Den[q];
         const double d = st - en;
-        Dsh[q] = d;
+        Dst[q] = d;
         if (t <= T) Dn[(size_t)t * C + c] = d;
         if (a.pstart && t < L) a.pstart[((size_t)b * T + t) * C + c] = (float)st;
         if (a.pend && t >= 1 && t <= L) a.pend[((size_t)b * T + t - 1) * C + c] = (float)en;
@@ -125,16 +193,8 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
     __syncthreads();
     for (int c = tid; c < C; c += 256) {
         double s = 0.0;
-        for (int r = 0; r < TM; ++r) s += Dsh[(size_t)r * C + c];
+        for (int r = 0; r < TM; ++r) s += Dst[(size_t)r * C + c];
         dn_tile[c] = s;
-    }
-
-    // ---- phase 2: duration partials, lanes over (k, c), segments starting in the tile
-    for (int q = tid; q < K * C; q += 256) {
-        const int k = q / C + 1, c = q - (k - 1) * C;
-        double acc = 0.0;
-        for (int r = 0; r < TM; ++r) acc += (double)seg(r + K, r + k, k, c);
-        part_dur[(size_t)(k - 1) * C + c] = acc;
     }
 
     // ---- phase 3: transition partials, lanes over (c', c)
@@ -151,8 +211,7 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
 }
 
 hipError_t launch_marginals(const MargArgs& a, hipStream_t stream) {
-    const int TM = a.tile, K = a.K, C = a.C;
-    const size_t lds = (size_t)8 * C * (2 * (TM + K) + 1 + 3 * TM) + (size_t)4 * (K * C + C * C);
+    const size_t lds = marg_lds(a.C, a.tile, a.kchunk);
     hipLaunchKernelGGL(k_marginals, dim3(a.ntiles, a.B), dim3(256), lds, stream, a);
     return hipGetLastError();
 }

@@ -24,7 +24,11 @@ SweepCfg choose_sweep(int C, int K) {
     if (C < 1 || K < 1) return s;
     // lane groups: aim at <= 4 waves (one per SIMD) where the label count allows
     int G, CPL, GT;
+    // a lane covers at most 32 durations (8 ring blocks of ROUND positions in the round
+    // kernels), so 32 lanes per label reach K = 1025; above it up to 7 labels take 64
+    // lanes each (7 bulk waves beside the chain)
     if (C <= 4) { G = 64; GT = 4; CPL = 1; }
+    else if (C <= 7 && K > 32 * 32 + 1) { G = 64; GT = 8; CPL = 1; }
     else if (C <= 8) { G = 32; GT = 8; CPL = 1; }
     else if (C <= 16) { G = 16; GT = 16; CPL = 1; }
     else if (C <= 32) { G = 8; GT = 8; CPL = 4; }

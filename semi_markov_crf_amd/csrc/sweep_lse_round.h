@@ -97,11 +97,12 @@ __device__ __forceinline__ float at4(const float4& v, int d) {
 // PROJ: boundary projections present (else the end and start sides coincide).
 // Block: 64 + ceil(C*G/64)*64 threads.
 template <int G, int BPL, int CP, bool LIN, bool PROJ>
-__global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int RS, const int P,
+__global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int RS, const int P,
                                                   const int CH) {
     constexpr int M = ROUND;
     static_assert(M == 4, "ring blocks are float4");
-    static_assert(CP <= 16 && CP * G <= 256, "the labels of the chain wavefront share one DPP row");
+    static_assert(CP <= 16, "the labels of the chain wavefront share one DPP row");
+    static_assert(CP * G <= 512, "at most 7 bulk wavefronts beside the chain");
     constexpr int BP = BPL > 0 ? BPL : 1;
     constexpr int KD = 2 * M - 1;                              // chain durations, last step
     constexpr int CP4 = (CP + 3) / 4 * 4;
@@ -432,30 +433,36 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
         // that fail them are redone from the log ring.
         if (r >= 3 && (r & 1) == 1) {
             constexpr int BR = BPL + 1;               // covers NR = bmax + 3 <= BPL*G + G blocks
+            constexpr int RB = 3;                     // blocks in flight (register pressure)
             const float dl = bact ? dlsh[cb] : 0.0f;
             const float sc = fast_exp2(-dl);
-            float4 v[BR], e[BR];
+            // each live block belongs to one (lane, i): batches need no ordering among lanes
 #pragma unroll
-            for (int i = 0; i < BR; ++i) {
-                v[i] = ld4(Rrow + round_slot(r - 2 - j - i * G, RMASK));
-                if constexpr (LIN) e[i] = ld4(Erow + round_slot(r - 2 - j - i * G, RMASK));
-            }
+            for (int i0 = 0; i0 < BR; i0 += RB) {
+                float4 v[RB], e[RB];
 #pragma unroll
-            for (int i = 0; i < BR; ++i) {
-                const int q = j + i * G;
-                const int rho = r - 2 - q;
-                // blocks outside the live window go to the spare row (read by idle lanes)
-                const bool live = (q < NR) & (t0 + M * rho + M >= 0);
-                const int sl = round_slot(rho, RMASK);
-                float4 rv = v[i];
-                rv.x -= dl;
-                rv.y -= dl;
-                rv.z -= dl;
-                rv.w -= dl;
-                st4((live ? Rrow : R + C * P) + sl, rv);
-                if constexpr (LIN)
-                    st4((live ? Erow : E + C * P) + sl,
-                        make_float4(e[i].x * sc, e[i].y * sc, e[i].z * sc, e[i].w * sc));
+                for (int ii = 0; ii < RB && i0 + ii < BR; ++ii) {
+                    const int slot = round_slot(r - 2 - j - (i0 + ii) * G, RMASK);
+                    v[ii] = ld4(Rrow + slot);
+                    if constexpr (LIN) e[ii] = ld4(Erow + slot);
+                }
+#pragma unroll
+                for (int ii = 0; ii < RB && i0 + ii < BR; ++ii) {
+                    const int q = j + (i0 + ii) * G;
+                    const int rho = r - 2 - q;
+                    // blocks outside the live window go to the spare row (read by idle lanes)
+                    const bool live = (q < NR) & (t0 + M * rho + M >= 0);
+                    const int sl = round_slot(rho, RMASK);
+                    float4 rv = v[ii];
+                    rv.x -= dl;
+                    rv.y -= dl;
+                    rv.z -= dl;
+                    rv.w -= dl;
+                    st4((live ? Rrow : R + C * P) + sl, rv);
+                    if constexpr (LIN)
+                        st4((live ? Erow : E + C * P) + sl,
+                            make_float4(e[ii].x * sc, e[ii].y * sc, e[ii].z * sc, e[ii].w * sc));
+                }
             }
         }
         // checkpoint rings of the positions the chain checkpointed last round
@@ -743,7 +750,7 @@ __global__ __launch_bounds__(320) void k_lse_round(const SweepArgs a, const int 
 template <int G, int BPL, int CP, bool LIN, bool PROJ>
 static hipError_t launch_lse_round_inst(const SweepArgs& a, dim3 grid, const SweepCfg& cfg,
                                         hipStream_t stream) {
-    if (cfg.NT > 320 || cfg.lse.CH > lse_chunk_max(G) || cfg.lse.CH % ROUND != 0 ||
+    if (cfg.NT > 512 || cfg.NT < 64 + cfg.G * a.C || cfg.lse.CH > lse_chunk_max(G) || cfg.lse.CH % ROUND != 0 ||
         cfg.lse.P % 4 != 0 || cfg.RS % ROUND != 0)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_lse_round<G, BPL, CP, LIN, PROJ>), grid, dim3(cfg.NT), cfg.lse.bytes, stream,
@@ -772,6 +779,8 @@ hipError_t launch_lse_round_layout(const SweepCfg& cfg, const SweepArgs& a, int 
                                    hipStream_t stream) {
     const dim3 grid = a.mode == MODE_FULL ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);
     if (cfg.G == 64 && cfg.CPr == 4) { LSE_ROUND_BPL_CASES(64, 4) }
+    if (cfg.G == 64 && cfg.CPr == 6) { LSE_ROUND_BPL_CASES(64, 6) }
+    if (cfg.G == 64 && cfg.CPr == 8) { LSE_ROUND_BPL_CASES(64, 8) }
     if (cfg.G == 32 && cfg.CPr == 6) { LSE_ROUND_BPL_CASES(32, 6) }
     if (cfg.G == 32 && cfg.CPr == 8) { LSE_ROUND_BPL_CASES(32, 8) }
     if (cfg.G == 16 && cfg.CPr == 12) { LSE_ROUND_BPL_CASES(16, 12) }

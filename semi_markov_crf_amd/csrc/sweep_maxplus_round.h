@@ -91,11 +91,12 @@ __device__ __forceinline__ int min_tree_i(const int* x) {
 // chain broadcasts (>= C); PROJ: boundary projections present.  Grid (B, 2 directions),
 // block 64 + ceil(C*G/64)*64 threads.
 template <int G, int BPL, int CP, bool PROJ>
-__global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const int RS,
+__global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const int RS,
                                                       const int P, const int CH) {
     constexpr int M = ROUND;
     static_assert(M == 4, "ring blocks are float4");
-    static_assert(CP <= 16 && CP * G <= 256, "the labels of the chain wavefront share one DPP row");
+    static_assert(CP <= 16, "the labels of the chain wavefront share one DPP row");
+    static_assert(CP * G <= 512, "at most 7 bulk wavefronts beside the chain");
     constexpr int PF = (lse_chunk_max(G) + G - 1) / G;
     constexpr int BP = BPL > 0 ? BPL : 1;
     constexpr int KD = 2 * M - 1;
@@ -446,7 +447,7 @@ __global__ __launch_bounds__(320) void k_maxplus_round(const SweepArgs a, const 
 template <int G, int BPL, int CP, bool PROJ>
 static hipError_t launch_maxplus_round_inst(const SweepArgs& a, const SweepCfg& cfg,
                                             hipStream_t stream) {
-    if (cfg.NT > 320 || cfg.vit.CH > lse_chunk_max(G) || cfg.vit.CH % ROUND != 0 ||
+    if (cfg.NT > 512 || cfg.NT < 64 + cfg.G * a.C || cfg.vit.CH > lse_chunk_max(G) || cfg.vit.CH % ROUND != 0 ||
         cfg.vit.P % 4 != 0 || cfg.RS % ROUND != 0)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_maxplus_round<G, BPL, CP, PROJ>), dim3(a.B, 2), dim3(cfg.NT), cfg.vit.bytes,
@@ -471,6 +472,8 @@ static hipError_t launch_maxplus_round_inst(const SweepArgs& a, const SweepCfg& 
 template <bool PROJ>
 hipError_t launch_maxplus_round(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream) {
     if (cfg.G == 64 && cfg.CPr == 4) { MAXPLUS_ROUND_BPL_CASES(64, 4) }
+    if (cfg.G == 64 && cfg.CPr == 6) { MAXPLUS_ROUND_BPL_CASES(64, 6) }
+    if (cfg.G == 64 && cfg.CPr == 8) { MAXPLUS_ROUND_BPL_CASES(64, 8) }
     if (cfg.G == 32 && cfg.CPr == 6) { MAXPLUS_ROUND_BPL_CASES(32, 6) }
     if (cfg.G == 32 && cfg.CPr == 8) { MAXPLUS_ROUND_BPL_CASES(32, 8) }
     if (cfg.G == 16 && cfg.CPr == 12) { MAXPLUS_ROUND_BPL_CASES(16, 12) }

@@ -86,7 +86,7 @@ def test_workspace_bytes(native):
     assert ws(0, 1, 10, 2, 70000, 0) == 0              # K beyond 65535
 
 
-@pytest.mark.parametrize("C,kmax", [(1, 2049), (4, 2049), (5, 1025), (8, 1025), (9, 513), (16, 513),
+@pytest.mark.parametrize("C,kmax", [(1, 2049), (4, 2049), (5, 2049), (7, 2049), (8, 1025), (9, 513), (16, 513),
                                     (17, 257), (39, 257), (64, 257), (128, 97)])
 def test_supported_duration_range(native, C, kmax):
     """The largest K each label count supports, as the header states it."""

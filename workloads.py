@@ -123,12 +123,12 @@ def _genomic_labels(rng, C):
     return draw
 
 
-def _genomic(rng, B=4, T=100_000, name="genomic"):
-    K, C = 200, 6
+def _genomic(rng, B=4, T=100_000, name="genomic", K=200, mean=50.0):
+    C = 6
     lengths = np.full(B, T, dtype=np.int32)
     return _assemble(
         name, rng, B, T, C, K, lengths,
-        draw_dur=lambda n: np.minimum(rng.geometric(1.0 / 50.0, size=n), K),
+        draw_dur=lambda n: np.minimum(rng.geometric(1.0 / mean, size=n), K),
         draw_label=_genomic_labels(rng, C),
         bump=1.5, trans_sd=0.1, dur_sd=0.1)
 
@@ -160,6 +160,13 @@ def make(index: int) -> Workload:
     """Configuration ``index`` (0..4) drawn with seed 1000 + index."""
     _, fn = CONFIGS[index]
     return fn(np.random.default_rng(1000 + index))
+
+
+def long_duration(seed: int = 1005, B: int = 1, T: int = 1_000_000, K: int = 2000) -> Workload:
+    """The genomic generator (C = 6, one label on 70% of the segments) with a long maximum
+    duration: segment lengths geometric with mean K/4, capped at K."""
+    return _genomic(np.random.default_rng(seed), B=B, T=T, name=f"long_duration_K{K}", K=K,
+                    mean=K / 4.0)
 
 
 def tiny_slice(T: int = 8) -> Workload:
