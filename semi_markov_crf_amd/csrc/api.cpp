@@ -167,9 +167,9 @@ struct BoundaryRes {
     float* prob;
 };
 
-SweepArgs base_args(const float* trans, const float* dur, const Proj& pj, int B, int T, int C,
-                    int K, void* ws, const Layout& lo) {
-    SweepArgs a{};
+SweepLaunch base_args(const float* trans, const float* dur, const Proj& pj, int B, int T, int C,
+                      int K, void* ws, const Layout& lo) {
+    SweepLaunch a{};
     a.S = at<double>(ws, lo.S);
     a.proj_start = pj.start;
     a.proj_end = pj.end;
@@ -243,7 +243,7 @@ static int run_logz(const float* em, const int32_t* lengths, const float* trans,
     if ((rc = run_prefix(em, lengths, B, T, C, workspace, lo, stream))) return rc;
     STAGE(1);
     const SweepCfg cfg = choose_sweep(C, K);
-    SweepArgs a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
+    SweepLaunch a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
     a.mode = MODE_FULL;
     a.logz = at<double>(workspace, lo.logz);
     LAUNCH(launch_lse(cfg, a, 1, stream));
@@ -268,7 +268,7 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
     if ((rc = run_prefix(em, lengths, B, T, C, workspace, lo, stream))) return rc;
     STAGE(1);
     const SweepCfg cfg = choose_sweep(C, K);
-    SweepArgs a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
+    SweepLaunch a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
     a.delta = lo.delta;
     a.nspans = lo.nspans;
     a.ck_ring = at<float>(workspace, lo.ckR);
@@ -354,7 +354,7 @@ static int run_viterbi(const float* em, const int32_t* lengths, const float* tra
     if ((rc = run_prefix(em, lengths, B, T, C, workspace, lo, stream))) return rc;
     STAGE(1);
     const SweepCfg cfg = choose_sweep(C, K);
-    SweepArgs a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
+    SweepLaunch a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
     a.mode = MODE_FULL;
     a.bp = at<uint32_t>(workspace, lo.bp);
     a.vscore = at<double>(workspace, lo.vscore);

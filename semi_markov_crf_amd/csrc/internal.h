@@ -62,23 +62,23 @@ inline size_t lse_lds_bytes(int C, int NT, int UP, int P, int CH, bool lin) {
 // The round kernels (C <= 16): ROUND positions per workgroup barrier.
 constexpr int ROUND = 4;
 // Dynamic LDS of the log-semiring round kernel: S chunks [2][C][CH] and S(L) (fp64), the
-// chunks' per-position factors [2][5][C][CH], the rings [C+1][P] (two when linear), bulk
-// sums [2][CP][2][ROUND], staged ring entries [2][CP+1][2][ROUND], rebase shifts and dmax
-// [CP rounded to 4], a sink and two constant blocks [16] (fp32).
-inline size_t lse_round_lds_bytes(int C, int CP, int P, int CH, bool lin) {
+// chunks' per-position factors [2][5 with projections, else 3][C][CH], the rings [C+1][P]
+// (two when linear), bulk sums [2][CP][2][ROUND], staged ring entries [2][CP+1][2][ROUND],
+// rebase shifts and dmax [CP rounded to 4], a sink and two constant blocks [16] (fp32).
+inline size_t lse_round_lds_bytes(int C, int CP, int P, int CH, bool lin, bool proj) {
     const int cp4 = (CP + 3) / 4 * 4;
     return (size_t)(2 * CH * C + (C + 1) / 2 * 2) * 8 +
-           (size_t)(10 * C * CH + (lin ? 2 : 1) * (C + 1) * P + 4 * CP * ROUND +
+           (size_t)((proj ? 10 : 6) * C * CH + (lin ? 2 : 1) * (C + 1) * P + 4 * CP * ROUND +
                     4 * (CP + 1) * ROUND + 2 * cp4 + 16) * 4;
 }
 // Dynamic LDS of the max-plus round kernel (C <= 16): S chunks [2][C][CH] and S(L) (fp64),
-// the chunks' end-side and start-side projections [2][2][C][CH], the ring [C+1][P], bulk
-// maxima and their k [2][CP][2][ROUND], rebase shifts [CP rounded to 4], a sink and a
-// constant block [12] (fp32).
-inline size_t maxplus_round_lds_bytes(int C, int CP, int P, int CH) {
+// with projections the chunks' end-side and start-side projections [2][2][C][CH], the
+// ring [C+1][P], bulk maxima and their k [2][CP][2][ROUND], rebase shifts [CP rounded to
+// 4], a sink and a constant block [12] (fp32).
+inline size_t maxplus_round_lds_bytes(int C, int CP, int P, int CH, bool proj) {
     const int cp4 = (CP + 3) / 4 * 4;
     return (size_t)(2 * CH * C + (C + 1) / 2 * 2) * 8 +
-           (size_t)(4 * C * CH + (C + 1) * P + 4 * CP * ROUND + cp4 + 12) * 4;
+           (size_t)((proj ? 4 : 0) * C * CH + (C + 1) * P + 4 * CP * ROUND + cp4 + 12) * 4;
 }
 // Dynamic LDS of the max-plus sweep: end-side and start-side S chunks [2][2][CH][C]
 // (fp64), R ring [C+1][P] and u [2][UP] (fp32).
@@ -90,13 +90,6 @@ enum SweepMode { MODE_FULL = 0, MODE_SPAN = 1 };
 
 struct SweepArgs {
     const double* S;        // [B][T+1][C] centred prefix sums
-    // boundary projections [B][T][C] or NULL (zeros): a segment [s, e) of label c gains
-    // proj_start[s, c] + proj_end[e-1, c].  Sweep position p of direction 0 adds
-    // proj_end[p-1] to the messages that end there and proj_start[p] to the ring entries
-    // that start there; on the mirrored sequence the two swap roles (proj_start[L-p] at
-    // the end side, proj_end[L-1-p] at the start side).
-    const float* proj_start;
-    const float* proj_end;
     const int* Leff;        // [B] clamped length, negated when the input length was invalid
     const float* trans;     // [C][C]
     const float* dur;       // [K][C]
@@ -125,20 +118,31 @@ struct SweepArgs {
     double* vwin;           // [2 dirs][B][K][C] values over the meeting window (round kernel)
 };
 
+// What the launchers receive: the kernels' arguments plus the boundary projections, which
+// the kernels take as separate trailing arguments.  Projections are [B][T][C] or NULL
+// (zeros): a segment [s, e) of label c gains proj_start[s, c] + proj_end[e-1, c].  Sweep
+// position p of direction 0 adds proj_end[p-1] to the messages that end there and
+// proj_start[p] to the ring entries that start there; on the mirrored sequence the two
+// swap roles (proj_start[L-p] at the end side, proj_end[L-1-p] at the start side).
+struct SweepLaunch : SweepArgs {
+    const float* proj_start = nullptr;
+    const float* proj_end = nullptr;
+};
+
 // log-semiring sweep: grid (B, ndir) in MODE_FULL, (nspans, B, ndir) in MODE_SPAN;
 // dispatches on cfg.lse.layout to the per-layout translation units
-hipError_t launch_lse(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream);
-hipError_t launch_lse_mirror(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream);
-hipError_t launch_lse_plain(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream);
-hipError_t launch_lse_log(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream);
+hipError_t launch_lse(const SweepCfg& cfg, const SweepLaunch& a, int ndir, hipStream_t stream);
+hipError_t launch_lse_mirror(const SweepCfg& cfg, const SweepLaunch& a, int ndir, hipStream_t stream);
+hipError_t launch_lse_plain(const SweepCfg& cfg, const SweepLaunch& a, int ndir, hipStream_t stream);
+hipError_t launch_lse_log(const SweepCfg& cfg, const SweepLaunch& a, int ndir, hipStream_t stream);
 // round kernels (C <= 16) with boundary projections
-hipError_t launch_lse_round_proj(const SweepCfg& cfg, const SweepArgs& a, int ndir, bool lin,
+hipError_t launch_lse_round_proj(const SweepCfg& cfg, const SweepLaunch& a, int ndir, bool lin,
                                  hipStream_t stream);
-hipError_t launch_maxplus_round_proj(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream);
+hipError_t launch_maxplus_round_proj(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream);
 // max-plus sweep (Viterbi): MODE_FULL, forward only, grid (B); dispatches on cfg.vit.layout
-hipError_t launch_maxplus(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream);
-hipError_t launch_maxplus_mirror(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream);
-hipError_t launch_maxplus_plain(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream);
+hipError_t launch_maxplus(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream);
+hipError_t launch_maxplus_mirror(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream);
+hipError_t launch_maxplus_plain(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream);
 
 // ------------------------------------------------------------------ scans
 // Per-tile column sums of the valid emissions; also writes the clamped lengths Leff

@@ -70,7 +70,8 @@ SweepCfg choose_sweep(int C, int K) {
         if (s.split && (lay & SWEEP_MIRRORED)) continue;
         const int P = s.split ? s.RS + 4 : pitch(lay);
         for (int ch = lse_chunk_max(G); ch >= 4 && s.lse.bytes == 0; ch >>= 1) {
-            const size_t n = s.split ? lse_round_lds_bytes(C, s.CPr, P, ch, lay & SWEEP_LINEAR)
+            // sized for the projection instances, the larger of the two
+            const size_t n = s.split ? lse_round_lds_bytes(C, s.CPr, P, ch, lay & SWEEP_LINEAR, true)
                                      : lse_lds_bytes(C, s.NT, UP, P, ch, lay & SWEEP_LINEAR);
             if (n <= LDS_BUDGET) s.lse = SweepLds{lay, P, ch, n};
         }
@@ -81,7 +82,7 @@ SweepCfg choose_sweep(int C, int K) {
         if (s.split && (lay & SWEEP_MIRRORED)) continue;
         const int P = s.split ? s.RS + 4 : pitch(lay);
         for (int ch = s.split ? lse_chunk_max(G) : MAXPLUS_CHUNK_MAX; ch >= 4 && s.vit.bytes == 0; ch >>= 1) {
-            const size_t n = s.split ? maxplus_round_lds_bytes(C, s.CPr, P, ch)
+            const size_t n = s.split ? maxplus_round_lds_bytes(C, s.CPr, P, ch, true)
                                      : maxplus_lds_bytes(C, UP, P, ch);
             if (n <= LDS_BUDGET) s.vit = SweepLds{lay, P, ch, n};
         }
@@ -91,7 +92,7 @@ SweepCfg choose_sweep(int C, int K) {
     return s;
 }
 
-hipError_t launch_lse(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream) {
+hipError_t launch_lse(const SweepCfg& cfg, const SweepLaunch& a, int ndir, hipStream_t stream) {
     switch (cfg.lse.layout) {
         case SWEEP_MIRRORED | SWEEP_LINEAR: return launch_lse_mirror(cfg, a, ndir, stream);
         case SWEEP_LINEAR: return launch_lse_plain(cfg, a, ndir, stream);
@@ -100,7 +101,7 @@ hipError_t launch_lse(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStre
     }
 }
 
-hipError_t launch_maxplus(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream) {
+hipError_t launch_maxplus(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream) {
     switch (cfg.vit.layout) {
         case SWEEP_MIRRORED: return launch_maxplus_mirror(cfg, a, stream);
         case 0: return launch_maxplus_plain(cfg, a, stream);

@@ -77,7 +77,9 @@ __device__ __forceinline__ bool wave_any(bool bad) { return __builtin_amdgcn_bal
 // LAY: ring layout bits (SWEEP_MIRRORED, SWEEP_LINEAR), fixed at compile time.
 template <int G, int KPL, int CPL, int GT, int NTMAX, int LAY>
 __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, const int P,
-                                              const int CH) {
+                                              const int CH,
+                                              const float* __restrict__ proj_start,
+                                              const float* __restrict__ proj_end) {
     constexpr int PF = (lse_chunk_max(G) + 1 + G - 1) / G;   // prefetched doubles per lane
     constexpr int UP = GT * CPL;                               // padded message row (>= C)
     constexpr int KP = KPL > 0 ? KPL : 1;
@@ -128,8 +130,8 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
     for (int q = tid; q < C; q += NT) SL[q] = Sb[(size_t)L * C + q];
     // projections of sweep position p, base 2: end side (segments ending at p) and start
     // side (segments starting at p); 0 without projections or outside [1, L] / [0, L-1]
-    const float* PSb = a.proj_start ? a.proj_start + (size_t)b * T * C : nullptr;
-    const float* PEb = a.proj_end ? a.proj_end + (size_t)b * T * C : nullptr;
+    const float* PSb = proj_start ? proj_start + (size_t)b * T * C : nullptr;
+    const float* PEb = proj_end ? proj_end + (size_t)b * T * C : nullptr;
     auto proj_e = [&](int p, int q) -> double {
         const float* src = dir == 0 ? PEb : PSb;
         const int t = dir == 0 ? p - 1 : L - p;
@@ -484,11 +486,12 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
 
 // ------------------------------------------------------------------ launch
 template <int G, int KPL, int CPL, int GT, int NTMAX, int LAY>
-static hipError_t launch_lse_inst(const SweepArgs& a, dim3 grid, const SweepCfg& cfg,
+static hipError_t launch_lse_inst(const SweepLaunch& a, dim3 grid, const SweepCfg& cfg,
                                   hipStream_t stream) {
     if (cfg.NT > NTMAX || cfg.lse.CH > lse_chunk_max(G)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_lse<G, KPL, CPL, GT, NTMAX, LAY>), grid, dim3(cfg.NT), cfg.lse.bytes,
-                       stream, a, cfg.RS, cfg.lse.P, cfg.lse.CH);
+                       stream, static_cast<const SweepArgs&>(a), cfg.RS, cfg.lse.P, cfg.lse.CH,
+                       a.proj_start, a.proj_end);
     return hipGetLastError();
 }
 
@@ -513,7 +516,7 @@ static hipError_t launch_lse_inst(const SweepArgs& a, dim3 grid, const SweepCfg&
 
 // every kernel shape of one ring layout for C > 16 (one translation unit per layout)
 template <int LAY>
-hipError_t launch_lse_layout(const SweepCfg& cfg, const SweepArgs& a, int ndir,
+hipError_t launch_lse_layout(const SweepCfg& cfg, const SweepLaunch& a, int ndir,
                              hipStream_t stream) {
     dim3 grid = a.mode == MODE_FULL ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);
     // C <= 16 (G >= 16) runs the split-role kernel instead

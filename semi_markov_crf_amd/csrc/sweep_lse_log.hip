@@ -5,7 +5,7 @@
 
 namespace semicrf {
 
-hipError_t launch_lse_log(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream) {
+hipError_t launch_lse_log(const SweepCfg& cfg, const SweepLaunch& a, int ndir, hipStream_t stream) {
     if (cfg.split)
         return (a.proj_start || a.proj_end) ? launch_lse_round_proj(cfg, a, ndir, false, stream)
                                             : launch_lse_round_layout<false, false>(cfg, a, ndir, stream);

@@ -4,7 +4,7 @@
 
 namespace semicrf {
 
-hipError_t launch_lse_mirror(const SweepCfg& cfg, const SweepArgs& a, int ndir, hipStream_t stream) {
+hipError_t launch_lse_mirror(const SweepCfg& cfg, const SweepLaunch& a, int ndir, hipStream_t stream) {
     if (cfg.split) return hipErrorInvalidValue;   // the round kernel keeps one ring copy
     return launch_lse_layout<SWEEP_MIRRORED|SWEEP_LINEAR>(cfg, a, ndir, stream);
 }

@@ -98,7 +98,9 @@ __device__ __forceinline__ float at4(const float4& v, int d) {
 // Block: 64 + ceil(C*G/64)*64 threads.
 template <int G, int BPL, int CP, bool LIN, bool PROJ>
 __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int RS, const int P,
-                                                  const int CH) {
+                                                  const int CH,
+                                                  const float* __restrict__ proj_start,
+                                                  const float* __restrict__ proj_end) {
     constexpr int M = ROUND;
     static_assert(M == 4, "ring blocks are float4");
     static_assert(CP <= 16, "the labels of the chain wavefront share one DPP row");
@@ -147,9 +149,11 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     double* SL = Sbuf + 2 * C * CH;                        // [C] (padded to 16 bytes)
     // per position p of a staged chunk, relative to S(p0), p0 the first position of its
     // round: ge = S(p) + pe(p) - S(p0) and gs = S(p) - ps(p) - S(p0), with pe / ps the
-    // end-side / start-side projections (base 2): 2^ge, 2^-gs, ge, gs, pe  [2][5][C][CH]
+    // end-side / start-side projections (base 2): 2^ge, 2^-gs, ge, gs, pe  [2][5][C][CH];
+    // without projections ge = gs = g: 2^g, 2^-g, g  [2][3][C][CH]
+    constexpr int NPL = PROJ ? 5 : 3;
     float* Fst = (float*)(SL + (C + 1) / 2 * 2);
-    float* R = Fst + 10 * C * CH;                          // [C+1][P] log ring
+    float* R = Fst + 2 * NPL * C * CH;                     // [C+1][P] log ring
     float* E = R + (C + 1) * P;                            // [C+1][P] linear ring
     float* qsh = E + (LIN ? (C + 1) * P : 0);              // [2 rounds][CP][lin, log][M]
     float* nsh = qsh + 2 * CP * 2 * M;                     // [2 rounds][CP+1][s, offset][M]
@@ -165,8 +169,8 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     for (int q = tid; q < C; q += NT) SL[q] = Sb[(size_t)L * C + q];
     // projections of sweep position p, base 2: end side (segments ending at p) and start
     // side (segments starting at p); 0 without projections or outside [1, L] / [0, L-1]
-    const float* PSb = a.proj_start ? a.proj_start + (size_t)b * T * C : nullptr;
-    const float* PEb = a.proj_end ? a.proj_end + (size_t)b * T * C : nullptr;
+    const float* PSb = proj_start ? proj_start + (size_t)b * T * C : nullptr;
+    const float* PEb = proj_end ? proj_end + (size_t)b * T * C : nullptr;
     auto proj_e = [&](int p, int q) -> float {
         if constexpr (!PROJ) return 0.0f;
         const float* src = dir == 0 ? PEb : PSb;
@@ -380,7 +384,7 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
         double2* dS = reinterpret_cast<double2*>(Sbuf + buf * chunkN + sl * CH + M * sq);
         dS[0] = make_double2(sv[0], sv[1]);
         dS[1] = make_double2(sv[2], sv[3]);
-        float* f = Fst + (size_t)buf * 5 * C * CH + sl * CH + M * sq;
+        float* f = Fst + (size_t)buf * NPL * C * CH + sl * CH + M * sq;
         if constexpr (PROJ) {
             float ge[M], gs[M];
 #pragma unroll
@@ -433,27 +437,23 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
         // that fail them are redone from the log ring.
         if (r >= 3 && (r & 1) == 1) {
             constexpr int BR = BPL + 1;               // covers NR = bmax + 3 <= BPL*G + G blocks
-            constexpr int RB = 3;                     // blocks in flight (register pressure)
             const float dl = bact ? dlsh[cb] : 0.0f;
             const float sc = fast_exp2(-dl);
-            // each live block belongs to one (lane, i): batches need no ordering among lanes
+            if constexpr (BR <= 3) {
+                float4 v[BR], e[BR];
 #pragma unroll
-            for (int i0 = 0; i0 < BR; i0 += RB) {
-                float4 v[RB], e[RB];
-#pragma unroll
-                for (int ii = 0; ii < RB && i0 + ii < BR; ++ii) {
-                    const int slot = round_slot(r - 2 - j - (i0 + ii) * G, RMASK);
-                    v[ii] = ld4(Rrow + slot);
-                    if constexpr (LIN) e[ii] = ld4(Erow + slot);
+                for (int i = 0; i < BR; ++i) {
+                    v[i] = ld4(Rrow + round_slot(r - 2 - j - i * G, RMASK));
+                    if constexpr (LIN) e[i] = ld4(Erow + round_slot(r - 2 - j - i * G, RMASK));
                 }
 #pragma unroll
-                for (int ii = 0; ii < RB && i0 + ii < BR; ++ii) {
-                    const int q = j + (i0 + ii) * G;
+                for (int i = 0; i < BR; ++i) {
+                    const int q = j + i * G;
                     const int rho = r - 2 - q;
                     // blocks outside the live window go to the spare row (read by idle lanes)
                     const bool live = (q < NR) & (t0 + M * rho + M >= 0);
                     const int sl = round_slot(rho, RMASK);
-                    float4 rv = v[ii];
+                    float4 rv = v[i];
                     rv.x -= dl;
                     rv.y -= dl;
                     rv.z -= dl;
@@ -461,7 +461,36 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
                     st4((live ? Rrow : R + C * P) + sl, rv);
                     if constexpr (LIN)
                         st4((live ? Erow : E + C * P) + sl,
-                            make_float4(e[ii].x * sc, e[ii].y * sc, e[ii].z * sc, e[ii].w * sc));
+                            make_float4(e[i].x * sc, e[i].y * sc, e[i].z * sc, e[i].w * sc));
+                }
+            } else {
+                // more blocks: batches of three (register pressure); each live block belongs
+                // to one (lane, i), so the batches need no ordering among lanes
+                constexpr int RB = 3;
+#pragma unroll
+                for (int i0 = 0; i0 < BR; i0 += RB) {
+                    float4 v[RB], e[RB];
+#pragma unroll
+                    for (int ii = 0; ii < RB && i0 + ii < BR; ++ii) {
+                        v[ii] = ld4(Rrow + round_slot(r - 2 - j - (i0 + ii) * G, RMASK));
+                        if constexpr (LIN) e[ii] = ld4(Erow + round_slot(r - 2 - j - (i0 + ii) * G, RMASK));
+                    }
+#pragma unroll
+                    for (int ii = 0; ii < RB && i0 + ii < BR; ++ii) {
+                        const int q = j + (i0 + ii) * G;
+                        const int rho = r - 2 - q;
+                        const bool live = (q < NR) & (t0 + M * rho + M >= 0);
+                        const int sl = round_slot(rho, RMASK);
+                        float4 rv = v[ii];
+                        rv.x -= dl;
+                        rv.y -= dl;
+                        rv.z -= dl;
+                        rv.w -= dl;
+                        st4((live ? Rrow : R + C * P) + sl, rv);
+                        if constexpr (LIN)
+                            st4((live ? Erow : E + C * P) + sl,
+                                make_float4(e[ii].x * sc, e[ii].y * sc, e[ii].z * sc, e[ii].w * sc));
+                    }
                 }
             }
         }
@@ -532,13 +561,33 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
             // ---- per-round constants (H fixed inside the round)
             const double H0 = H;
             float hbe[M], hbs[M], yv[M], fb[M], fo[M];
-            {
+            if constexpr (!PROJ) {
+                // S(p_m) + B_c - H0 from S(p_0) and the staged differences; the scales
+                // 2^(hb + dmax) and 2^(tmax - hb) from one exp2 each and staged factors
+                const float* f = Fst + (size_t)(nch & 1) * NPL * C * CH + cl * CH + row0;
+                const float4 sg4 = ld4(f), is4 = ld4(f + C * CH), g4 = ld4(f + 2 * C * CH);
+                const float hb0 = (float)(Sch[cl * CH + row0] + BH);
+                const float y0 = cact ? fast_exp2(hb0 + dmax) : 0.0f;
+                const float fo0 = tmax - hb0;
+                const float f0 = fast_exp2(fo0);
+                const float gs[M] = {g4.x, g4.y, g4.z, g4.w};
+                const float ss[M] = {sg4.x, sg4.y, sg4.z, sg4.w};
+                const float is[M] = {is4.x, is4.y, is4.z, is4.w};
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    hbe[m] = hb0 + gs[m];
+                    hbs[m] = hbe[m];
+                    yv[m] = y0 * ss[m];                      // message scale
+                    fo[m] = fo0 - gs[m];
+                    fb[m] = f0 * is[m];                      // ring-entry scale
+                }
+            } else {
                 // end side S(p_m) + pe + B_c - H0 and start side S(p_m) - ps + B_c - H0
                 // from S(p_0) and the staged differences; the scales 2^(hbe + dmax) and
                 // 2^(tmax - hbs) from one exp2 each and staged factors
-                const float* f = Fst + (size_t)(nch & 1) * 5 * C * CH + cl * CH + row0;
+                const float* f = Fst + (size_t)(nch & 1) * NPL * C * CH + cl * CH + row0;
                 const float4 fe4 = ld4(f), fs4 = ld4(f + C * CH), ge4 = ld4(f + 2 * C * CH);
-                const float4 gs4 = PROJ ? ld4(f + 3 * C * CH) : ge4;
+                const float4 gs4 = ld4(f + 3 * C * CH);
                 const float hb0 = (float)(Sch[cl * CH + row0] + BH);
                 const float y0 = cact ? fast_exp2(hb0 + dmax) : 0.0f;
                 const float fo0 = tmax - hb0;
@@ -678,7 +727,7 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
                 st4(ns + M, make_float4(fH[M], fH[M + 1], fH[M + 2], fH[M + 3]));
             }
             if (a.write_xa) {
-                const float* fpe = Fst + (size_t)(nch & 1) * 5 * C * CH + 4 * C * CH + cl * CH + row0;
+                const float* fpe = Fst + (size_t)(nch & 1) * NPL * C * CH + 4 * C * CH + cl * CH + row0;
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
                     const int p = rs + 1 + m;
@@ -748,13 +797,15 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
 
 // ------------------------------------------------------------------ launch
 template <int G, int BPL, int CP, bool LIN, bool PROJ>
-static hipError_t launch_lse_round_inst(const SweepArgs& a, dim3 grid, const SweepCfg& cfg,
+static hipError_t launch_lse_round_inst(const SweepLaunch& a, dim3 grid, const SweepCfg& cfg,
                                         hipStream_t stream) {
     if (cfg.NT > 512 || cfg.NT < 64 + cfg.G * a.C || cfg.lse.CH > lse_chunk_max(G) || cfg.lse.CH % ROUND != 0 ||
         cfg.lse.P % 4 != 0 || cfg.RS % ROUND != 0)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_lse_round<G, BPL, CP, LIN, PROJ>), grid, dim3(cfg.NT), cfg.lse.bytes, stream,
-                       a, cfg.RS, cfg.lse.P, cfg.lse.CH);
+    const size_t bytes = lse_round_lds_bytes(a.C, CP, cfg.lse.P, cfg.lse.CH, LIN, PROJ);
+    hipLaunchKernelGGL((k_lse_round<G, BPL, CP, LIN, PROJ>), grid, dim3(cfg.NT), bytes, stream,
+                       static_cast<const SweepArgs&>(a), cfg.RS, cfg.lse.P, cfg.lse.CH,
+                       a.proj_start, a.proj_end);
     return hipGetLastError();
 }
 
@@ -775,7 +826,7 @@ static hipError_t launch_lse_round_inst(const SweepArgs& a, dim3 grid, const Swe
 // every shape of the round kernel with (LIN) or without the linear ring, with (PROJ) or
 // without boundary projections
 template <bool LIN, bool PROJ>
-hipError_t launch_lse_round_layout(const SweepCfg& cfg, const SweepArgs& a, int ndir,
+hipError_t launch_lse_round_layout(const SweepCfg& cfg, const SweepLaunch& a, int ndir,
                                    hipStream_t stream) {
     const dim3 grid = a.mode == MODE_FULL ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);
     if (cfg.G == 64 && cfg.CPr == 4) { LSE_ROUND_BPL_CASES(64, 4) }

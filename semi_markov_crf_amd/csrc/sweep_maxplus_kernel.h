@@ -50,7 +50,9 @@ __device__ __forceinline__ float bulk_max(const float* Rrow, int tq, int j, int 
 // Grid: one workgroup per sequence.  Natural-log units (max-plus needs no base change).
 template <int G, int KPL, int CPL, int GT, int NTMAX, bool MIR>
 __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int RS, const int P,
-                                                  const int CH) {
+                                                  const int CH,
+                                                  const float* __restrict__ proj_start,
+                                                  const float* __restrict__ proj_end) {
     constexpr int PF = (MAXPLUS_CHUNK_MAX + G - 1) / G;   // prefetched doubles per lane (NT >= C*G)
     constexpr int UP = GT * CPL;                   // padded u row (>= C)
     extern __shared__ double lds[];
@@ -78,8 +80,8 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
     float* Rrow = R + cr * P;
 
     const double* Sb = a.S + (size_t)b * (T + 1) * C;
-    const float* PSb = a.proj_start ? a.proj_start + (size_t)b * T * C : nullptr;
-    const float* PEb = a.proj_end ? a.proj_end + (size_t)b * T * C : nullptr;
+    const float* PSb = proj_start ? proj_start + (size_t)b * T * C : nullptr;
+    const float* PEb = proj_end ? proj_end + (size_t)b * T * C : nullptr;
     // projections at position t (flat index q = t*C + l): 0 when absent or outside
     // [1, L] (end side) / [0, L-1] (start side)
     auto proj_e = [&](int t, size_t q) -> float {
@@ -265,11 +267,12 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
 
 // ------------------------------------------------------------------ launch
 template <int G, int KPL, int CPL, int GT, int NTMAX, bool MIR>
-static hipError_t launch_maxplus_inst(const SweepArgs& a, const SweepCfg& cfg,
+static hipError_t launch_maxplus_inst(const SweepLaunch& a, const SweepCfg& cfg,
                                       hipStream_t stream) {
     if (cfg.NTv > NTMAX || cfg.vit.CH > MAXPLUS_CHUNK_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_maxplus<G, KPL, CPL, GT, NTMAX, MIR>), dim3(a.B), dim3(cfg.NTv),
-                       cfg.vit.bytes, stream, a, cfg.RS, cfg.vit.P, cfg.vit.CH);
+                       cfg.vit.bytes, stream, static_cast<const SweepArgs&>(a), cfg.RS,
+                       cfg.vit.P, cfg.vit.CH, a.proj_start, a.proj_end);
     return hipGetLastError();
 }
 
@@ -294,7 +297,7 @@ static hipError_t launch_maxplus_inst(const SweepArgs& a, const SweepCfg& cfg,
 
 // every kernel shape of one ring layout (one translation unit per layout)
 template <bool MIR>
-hipError_t launch_maxplus_layout(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream) {
+hipError_t launch_maxplus_layout(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream) {
     // C <= 16 (G >= 16) runs the round kernel instead
     if (cfg.G == 8 && cfg.CPL == 4) { MAXPLUS_KPL_CASES(8, 4, 8, 256) }
     if (cfg.G == 8 && cfg.CPL == 8) { MAXPLUS_KPL_CASES(8, 8, 8, 512) }

@@ -4,7 +4,7 @@
 
 namespace semicrf {
 
-hipError_t launch_maxplus_mirror(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream) {
+hipError_t launch_maxplus_mirror(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream) {
     if (cfg.split) return hipErrorInvalidValue;   // the round kernel keeps one ring copy
     return launch_maxplus_layout<true>(cfg, a, stream);
 }

@@ -5,7 +5,7 @@
 
 namespace semicrf {
 
-hipError_t launch_maxplus_plain(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream) {
+hipError_t launch_maxplus_plain(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream) {
     if (cfg.split)
         return (a.proj_start || a.proj_end) ? launch_maxplus_round_proj(cfg, a, stream)
                                             : launch_maxplus_round<false>(cfg, a, stream);

@@ -92,7 +92,9 @@ __device__ __forceinline__ int min_tree_i(const int* x) {
 // block 64 + ceil(C*G/64)*64 threads.
 template <int G, int BPL, int CP, bool PROJ>
 __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const int RS,
-                                                      const int P, const int CH) {
+                                                      const int P, const int CH,
+                                                      const float* __restrict__ proj_start,
+                                                      const float* __restrict__ proj_end) {
     constexpr int M = ROUND;
     static_assert(M == 4, "ring blocks are float4");
     static_assert(CP <= 16, "the labels of the chain wavefront share one DPP row");
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
     double* Sbuf = lds;                                    // [2][C][CH] label-major
     double* SL = Sbuf + 2 * C * CH;                        // [C] (padded to 16 bytes)
     float* Pst = (float*)(SL + (C + 1) / 2 * 2);           // [2][end, start][C][CH] projections
-    float* R = Pst + 4 * C * CH;                           // [C+1][P]
+    float* R = Pst + (PROJ ? 4 * C * CH : 0);              // [C+1][P]
     float* qsh = R + (C + 1) * P;                          // [2 rounds][CP][max, k][M]
     float* dlsh = qsh + 2 * CP * 2 * M;                    // [CP4] rebase shift per label
     float* sink = dlsh + CP4;                              // [8]
@@ -137,8 +139,8 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
     for (int q = tid; q < C; q += NT) SL[q] = Sb[(size_t)L * C + q];
     // projections of sweep position p: end side (segments ending at p) and start side
     // (segments starting at p); 0 without projections or outside [1, L] / [0, L-1]
-    const float* PSb = a.proj_start ? a.proj_start + (size_t)b * T * C : nullptr;
-    const float* PEb = a.proj_end ? a.proj_end + (size_t)b * T * C : nullptr;
+    const float* PSb = proj_start ? proj_start + (size_t)b * T * C : nullptr;
+    const float* PEb = proj_end ? proj_end + (size_t)b * T * C : nullptr;
     auto proj_e = [&](int p, int q) -> float {
         if constexpr (!PROJ) return 0.0f;
         const float* src = dir == 0 ? PEb : PSb;
@@ -445,13 +447,15 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
 
 // ------------------------------------------------------------------ launch
 template <int G, int BPL, int CP, bool PROJ>
-static hipError_t launch_maxplus_round_inst(const SweepArgs& a, const SweepCfg& cfg,
+static hipError_t launch_maxplus_round_inst(const SweepLaunch& a, const SweepCfg& cfg,
                                             hipStream_t stream) {
     if (cfg.NT > 512 || cfg.NT < 64 + cfg.G * a.C || cfg.vit.CH > lse_chunk_max(G) || cfg.vit.CH % ROUND != 0 ||
         cfg.vit.P % 4 != 0 || cfg.RS % ROUND != 0)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_maxplus_round<G, BPL, CP, PROJ>), dim3(a.B, 2), dim3(cfg.NT), cfg.vit.bytes,
-                       stream, a, cfg.RS, cfg.vit.P, cfg.vit.CH);
+    const size_t bytes = maxplus_round_lds_bytes(a.C, CP, cfg.vit.P, cfg.vit.CH, PROJ);
+    hipLaunchKernelGGL((k_maxplus_round<G, BPL, CP, PROJ>), dim3(a.B, 2), dim3(cfg.NT), bytes,
+                       stream, static_cast<const SweepArgs&>(a), cfg.RS, cfg.vit.P, cfg.vit.CH,
+                       a.proj_start, a.proj_end);
     return hipGetLastError();
 }
 
@@ -470,7 +474,7 @@ static hipError_t launch_maxplus_round_inst(const SweepArgs& a, const SweepCfg& 
     }
 
 template <bool PROJ>
-hipError_t launch_maxplus_round(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream) {
+hipError_t launch_maxplus_round(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream) {
     if (cfg.G == 64 && cfg.CPr == 4) { MAXPLUS_ROUND_BPL_CASES(64, 4) }
     if (cfg.G == 64 && cfg.CPr == 6) { MAXPLUS_ROUND_BPL_CASES(64, 6) }
     if (cfg.G == 64 && cfg.CPr == 8) { MAXPLUS_ROUND_BPL_CASES(64, 8) }

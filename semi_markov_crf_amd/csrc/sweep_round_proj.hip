@@ -6,13 +6,13 @@
 
 namespace semicrf {
 
-hipError_t launch_lse_round_proj(const SweepCfg& cfg, const SweepArgs& a, int ndir, bool lin,
+hipError_t launch_lse_round_proj(const SweepCfg& cfg, const SweepLaunch& a, int ndir, bool lin,
                                  hipStream_t stream) {
     return lin ? launch_lse_round_layout<true, true>(cfg, a, ndir, stream)
                : launch_lse_round_layout<false, true>(cfg, a, ndir, stream);
 }
 
-hipError_t launch_maxplus_round_proj(const SweepCfg& cfg, const SweepArgs& a, hipStream_t stream) {
+hipError_t launch_maxplus_round_proj(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream) {
     return launch_maxplus_round<true>(cfg, a, stream);
 }
 
