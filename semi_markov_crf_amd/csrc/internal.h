@@ -64,12 +64,14 @@ constexpr int ROUND = 4;
 // Dynamic LDS of the log-semiring round kernel: S chunks [2][C][CH] and S(L) (fp64), the
 // chunks' per-position factors [2][5 with projections, else 3][C][CH], the rings [C+1][P]
 // (two when linear), bulk sums [2][CP][2][ROUND], staged ring entries [2][CP+1][2][ROUND],
-// rebase shifts and dmax [CP rounded to 4], a sink and two constant blocks [16] (fp32).
+// rebase shifts and dmax [CP rounded to 4], a sink and two constant blocks [16], staged
+// message sums [2][CP][ROUND] and replay flags [4] (fp32), staged bases [2][CP] (fp64).
 inline size_t lse_round_lds_bytes(int C, int CP, int P, int CH, bool lin, bool proj) {
     const int cp4 = (CP + 3) / 4 * 4;
     return (size_t)(2 * CH * C + (C + 1) / 2 * 2) * 8 +
            (size_t)((proj ? 10 : 6) * C * CH + (lin ? 2 : 1) * (C + 1) * P + 4 * CP * ROUND +
-                    4 * (CP + 1) * ROUND + 2 * cp4 + 16) * 4;
+                    4 * (CP + 1) * ROUND + 2 * cp4 + 16 + 2 * CP * ROUND + 4) * 4 +
+           (size_t)2 * CP * 8;
 }
 // Dynamic LDS of the max-plus round kernel (C <= 16): S chunks [2][C][CH] and S(L) (fp64),
 // with projections the chunks' end-side and start-side projections [2][2][C][CH], the

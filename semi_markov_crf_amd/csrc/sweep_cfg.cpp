@@ -69,7 +69,9 @@ SweepCfg choose_sweep(int C, int K) {
     for (int lay : {int(SWEEP_MIRRORED | SWEEP_LINEAR), int(SWEEP_LINEAR), 0}) {
         if (s.split && (lay & SWEEP_MIRRORED)) continue;
         const int P = s.split ? s.RS + 4 : pitch(lay);
-        for (int ch = lse_chunk_max(G); ch >= 4 && s.lse.bytes == 0; ch >>= 1) {
+        // the round kernel needs two rounds per chunk (it restages one round late)
+        for (int ch = lse_chunk_max(G); ch >= (s.split ? 2 * ROUND : 4) && s.lse.bytes == 0;
+             ch >>= 1) {
             // sized for the projection instances, the larger of the two
             const size_t n = s.split ? lse_round_lds_bytes(C, s.CPr, P, ch, lay & SWEEP_LINEAR, true)
                                      : lse_lds_bytes(C, s.NT, UP, P, ch, lay & SWEEP_LINEAR);

@@ -94,9 +94,10 @@ __device__ __forceinline__ float at4(const float4& v, int d) {
 
 // G: bulk lanes per label (C <= 256/G); BPL: ring blocks per bulk lane; CP: labels the
 // chain broadcasts (>= C); LIN: linear ring and sums (else log-space bulk sums only);
-// PROJ: boundary projections present (else the end and start sides coincide).
+// PROJ: boundary projections present (else the end and start sides coincide); XA: write
+// the per-position outputs X / A (the span recompute; the checkpoint sweep writes none).
 // Block: 64 + ceil(C*G/64)*64 threads.
-template <int G, int BPL, int CP, bool LIN, bool PROJ>
+template <int G, int BPL, int CP, bool LIN, bool PROJ, bool XA>
 __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int RS, const int P,
                                                   const int CH,
                                                   const float* __restrict__ proj_start,
@@ -162,6 +163,11 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     float* sink = dmsh + CP4;                              // [8] for non-writing lanes
     float* zblk = sink + 8;                                // [4] zeros: linear blocks past K
     float* nblk = zblk + 4;                                // [4] NEG: log blocks past K
+    // per-position outputs of round r, written by the bulk lanes in round r+1: the message
+    // sums (linear, or log2 when the round was replayed), the replay flag, the base B_c
+    float* sgsh = nblk + 4;                                // [2 rounds][CP][M]
+    int* rpsh = (int*)(sgsh + 2 * CP * M);                 // [2 rounds] (padded to 4)
+    double* bcsh = (double*)(rpsh + 4);                    // [2 rounds][CP]
     float* Rrow = R + cr * P;
     float* Erow = E + cr * P;
 
@@ -426,10 +432,25 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     // of round r-1 from the chain's staging, the chain's rebase of round r-1 applied to the
     // rings, the rings of the checkpoints the chain took in round r-1
     int next_ckb = ckpt ? a.delta : INT_MAX;   // next checkpoint whose ring is to copy
-    auto ring_round = [&](int r, int rs) {
+    // Sprev: the staged S of round r-1's first position for this lane's label; Fprev: its
+    // end-side projection plane (projections only)
+    auto ring_round = [&](int r, int rs, const double* Sprev, const float* Fprev) {
         if (r >= 1 && bact && j < M) {
             const float* ns = nsh + (((r - 1) & 1) * (CP + 1) + cb) * 2 * M + j;
-            Rrow[round_slot(r - 1, RMASK) + j] = fmaxf(fast_log2(ns[0]) + ns[M], NEG);
+            const float rl = fast_log2(ns[0]) + ns[M];
+            Rrow[round_slot(r - 1, RMASK) + j] = fmaxf(rl, NEG);
+            // per-position outputs of round r-1 (position p = rs - M + 1 + j), natural log
+            const int p = rs - M + 1 + j;
+            if (XA && p <= t1) {
+                const double Bp = bcsh[((r - 1) & 1) * CP + cb];
+                const float sg = sgsh[(((r - 1) & 1) * CP + cb) * M + j];
+                const float sgl = rpsh[(r - 1) & 1] ? sg : fast_log2(sg) + dmax_b;
+                double Sp = Sprev[j];
+                if constexpr (PROJ) Sp += (double)Fprev[j];
+                const size_t o = (outrow + (dir == 0 ? p : L - p)) * C + cb;
+                Xout[o] = (Sp + Bp + (double)sgl) * LN2;
+                if (p < t1) Aout[o] = (Bp + (double)rl) * LN2;
+            }
         }
         // the chain rebased last round: move the blocks of rounds <= r-2 (reads first).
         // Linear entries are scaled by 2^-dl: one that underflowed is below 2^-126 and
@@ -726,7 +747,16 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
                 st4(ns, make_float4(sH[M], sH[M + 1], sH[M + 2], sH[M + 3]));
                 st4(ns + M, make_float4(fH[M], fH[M + 1], fH[M + 2], fH[M + 3]));
             }
-            if (a.write_xa) {
+            if constexpr (XA) {
+                // per-position outputs: staged here, written by the bulk lanes next round
+                if (cact) {
+                    st4(sgsh + ((r & 1) * CP + cl) * M, make_float4(sig[0], sig[1], sig[2], sig[3]));
+                    bcsh[(r & 1) * CP + cl] = Bc;
+                }
+                if (tid == 0) rpsh[r & 1] = replayed ? 1 : 0;
+            } else if (a.write_xa) {
+                // never taken (the launch picks XA when writing outputs); kept because the
+                // register allocation of this instance is the faster one with it
                 const float* fpe = Fst + (size_t)(nch & 1) * NPL * C * CH + 4 * C * CH + cl * CH + row0;
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
@@ -776,12 +806,24 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
                 fH[i] = fH[i + M];
             }
         } else {
-            // ---- S staging: in the first round of a chunk publish the next one
-            if (rs + 1 == tc && tc + CH <= t1) {
+            // ---- S staging: in the first round of a chunk publish the next one; with the
+            // outputs, in the second (the first still writes those of the previous chunk's
+            // last round)
+            if (rs + 1 == tc + (XA ? M : 0) && tc + CH <= t1) {
                 stage_store((nch + 1) & 1);
                 stage_load(tc + 2 * CH);
             }
-            ring_round(r, rs);
+            if constexpr (XA) {
+                // chunk row of round r-1's first position: this chunk, or the last row block
+                // of the previous one
+                const bool prevc = rs + 1 - M < tc;
+                const int buf = (prevc ? nch - 1 : nch) & 1;
+                const int rowp = rs + 1 - M - (prevc ? tc - CH : tc);
+                ring_round(r, rs, Sbuf + buf * chunkN + cb * CH + rowp,
+                           Fst + (size_t)buf * NPL * C * CH + (NPL - 1) * C * CH + cb * CH + rowp);
+            } else {
+                ring_round(r, rs, nullptr, nullptr);
+            }
             // ---- bulk sums of round r+1 (ring blocks of rounds <= r-1)
             bulk_round(r + 1, rs + M + 1);
         }
@@ -789,21 +831,34 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     }
 
     // checkpoints taken in the last round: their rings are copied here
-    if (ckpt && !chain) ring_round(nrounds, t0 + nrounds * M);
+    // checkpoints taken and outputs staged in the last round
+    if constexpr (XA) {
+        if (!chain && nrounds > 0) {
+            const int rs = t0 + nrounds * M;
+            const int tcl = t0 + 1 + ((nrounds - 1) * M) / CH * CH;   // chunk of the last round
+            const int nchl = ((nrounds - 1) * M) / CH;
+            const int rowp = rs + 1 - M - tcl;
+            ring_round(nrounds, rs, Sbuf + (nchl & 1) * chunkN + cb * CH + rowp,
+                       Fst + (size_t)(nchl & 1) * NPL * C * CH + (NPL - 1) * C * CH + cb * CH + rowp);
+        }
+    } else {
+        if (ckpt && !chain) ring_round(nrounds, t0 + nrounds * M, nullptr, nullptr);
+    }
 
     // ---------------------------------------------------------------- end of sequence
     if (t1 == L && tid == 0) (dir == 0 ? a.logz : a.logz_b)[b] = bad ? nan_d() : lz * LN2;
 }
 
 // ------------------------------------------------------------------ launch
-template <int G, int BPL, int CP, bool LIN, bool PROJ>
+template <int G, int BPL, int CP, bool LIN, bool PROJ, bool XA>
 static hipError_t launch_lse_round_inst(const SweepLaunch& a, dim3 grid, const SweepCfg& cfg,
                                         hipStream_t stream) {
-    if (cfg.NT > 512 || cfg.NT < 64 + cfg.G * a.C || cfg.lse.CH > lse_chunk_max(G) || cfg.lse.CH % ROUND != 0 ||
+    if (cfg.NT > 512 || cfg.NT < 64 + cfg.G * a.C || cfg.lse.CH > lse_chunk_max(G) ||
+        cfg.lse.CH % ROUND != 0 || cfg.lse.CH < 2 * ROUND ||
         cfg.lse.P % 4 != 0 || cfg.RS % ROUND != 0)
         return hipErrorInvalidValue;
     const size_t bytes = lse_round_lds_bytes(a.C, CP, cfg.lse.P, cfg.lse.CH, LIN, PROJ);
-    hipLaunchKernelGGL((k_lse_round<G, BPL, CP, LIN, PROJ>), grid, dim3(cfg.NT), bytes, stream,
+    hipLaunchKernelGGL((k_lse_round<G, BPL, CP, LIN, PROJ, XA>), grid, dim3(cfg.NT), bytes, stream,
                        static_cast<const SweepArgs&>(a), cfg.RS, cfg.lse.P, cfg.lse.CH,
                        a.proj_start, a.proj_end);
     return hipGetLastError();
@@ -811,15 +866,24 @@ static hipError_t launch_lse_round_inst(const SweepLaunch& a, dim3 grid, const S
 
 #define LSE_ROUND_BPL_CASES(G, CP)                                                   \
     switch (cfg.BPL) {                                                               \
-        case 0: return launch_lse_round_inst<G, 0, CP, LIN, PROJ>(a, grid, cfg, stream);      \
-        case 1: return launch_lse_round_inst<G, 1, CP, LIN, PROJ>(a, grid, cfg, stream);      \
-        case 2: return launch_lse_round_inst<G, 2, CP, LIN, PROJ>(a, grid, cfg, stream);      \
-        case 3: return launch_lse_round_inst<G, 3, CP, LIN, PROJ>(a, grid, cfg, stream);      \
-        case 4: return launch_lse_round_inst<G, 4, CP, LIN, PROJ>(a, grid, cfg, stream);      \
-        case 5: return launch_lse_round_inst<G, 5, CP, LIN, PROJ>(a, grid, cfg, stream);      \
-        case 6: return launch_lse_round_inst<G, 6, CP, LIN, PROJ>(a, grid, cfg, stream);      \
-        case 7: return launch_lse_round_inst<G, 7, CP, LIN, PROJ>(a, grid, cfg, stream);      \
-        case 8: return launch_lse_round_inst<G, 8, CP, LIN, PROJ>(a, grid, cfg, stream);      \
+        case 0: return a.write_xa ? launch_lse_round_inst<G, 0, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
+                             : launch_lse_round_inst<G, 0, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
+        case 1: return a.write_xa ? launch_lse_round_inst<G, 1, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
+                             : launch_lse_round_inst<G, 1, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
+        case 2: return a.write_xa ? launch_lse_round_inst<G, 2, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
+                             : launch_lse_round_inst<G, 2, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
+        case 3: return a.write_xa ? launch_lse_round_inst<G, 3, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
+                             : launch_lse_round_inst<G, 3, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
+        case 4: return a.write_xa ? launch_lse_round_inst<G, 4, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
+                             : launch_lse_round_inst<G, 4, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
+        case 5: return a.write_xa ? launch_lse_round_inst<G, 5, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
+                             : launch_lse_round_inst<G, 5, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
+        case 6: return a.write_xa ? launch_lse_round_inst<G, 6, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
+                             : launch_lse_round_inst<G, 6, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
+        case 7: return a.write_xa ? launch_lse_round_inst<G, 7, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
+                             : launch_lse_round_inst<G, 7, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
+        case 8: return a.write_xa ? launch_lse_round_inst<G, 8, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
+                             : launch_lse_round_inst<G, 8, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
         default: return hipErrorInvalidValue;                                        \
     }
 
