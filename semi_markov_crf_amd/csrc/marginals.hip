@@ -115,12 +115,14 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
     const double* AF = a.AF + (size_t)b * rowC;
     const double* XB = a.XB + (size_t)b * rowC;
     const double* AB = a.AB + (size_t)b * rowC;
-    // invalid starts / ends get DNEG so that their exponentials vanish
+    // staged in base 2 (times log2 e); invalid starts / ends get DNEG so that their
+    // exponentials vanish
     auto af = [&](int s, int c) -> double {
-        return (s >= 0 && s <= L - 1) ? AF[(size_t)s * C + c] + Sb[(size_t)L * C + c] - logZ : DNEG;
+        return (s >= 0 && s <= L - 1) ? (AF[(size_t)s * C + c] + Sb[(size_t)L * C + c] - logZ) * LOG2E
+                                      : DNEG;
     };
     auto ab = [&](int u, int c) -> double {
-        return (u >= 1 && u <= L) ? AB[(size_t)u * C + c] : DNEG;
+        return (u >= 1 && u <= L) ? AB[(size_t)u * C + c] * LOG2E : DNEG;
     };
 
     for (int q = tid; q < TM * C; q += 256) {
@@ -128,14 +130,14 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
         const int s = p0 + r;
         AFt[q] = af(s, c);
         ABt[q] = ab(s, c);
-        XFs[q] = (s >= 1 && s <= L - 1) ? XF[(size_t)s * C + c] : DNEG;
-        XBs[q] = (s >= 1 && s <= L - 1) ? XB[(size_t)s * C + c] - logZ : DNEG;
+        XFs[q] = (s >= 1 && s <= L - 1) ? XF[(size_t)s * C + c] * LOG2E : DNEG;
+        XBs[q] = (s >= 1 && s <= L - 1) ? (XB[(size_t)s * C + c] - logZ) * LOG2E : DNEG;
         Dst[q] = 0.0;
         Den[q] = 0.0;
     }
     for (int q = tid; q < C * C; q += 256) tr2[q] = fmaxf((float)((double)a.trans[q] * LOG2E), NEG);
 
-    auto seg = [&](double v, float d) -> float { return fast_exp2((float)(v * LOG2E) + d); };
+    auto seg = [&](double v, float d) -> float { return fast_exp2((float)v + d); };
 
     for (int kc0 = 1; kc0 <= K; kc0 += KC) {
         const int kc1 = min(K, kc0 + KC - 1);
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
         double acc = 0.0;
         for (int r = 0; r < TM; ++r) {
             const double v = XFs[(size_t)r * C + cp] + XBs[(size_t)r * C + c];
-            acc += (double)fast_exp2((float)(v * LOG2E) + tv);
+            acc += (double)fast_exp2((float)v + tv);
         }
         part_trans[q] = acc;
     }

@@ -53,19 +53,36 @@ def close_abs(gpu, ref, atol, what):
     assert err.max() <= atol, f"{what}: max abs err {err.max():.3e} > {atol}"
 
 
-@pytest.mark.parametrize("name", ["x1", "x2", "x3"])
+def _projections(seed, B, T, C, sd):
+    """The fixture script's seeded N(0, sd) projections (tests/golden/make_extreme_k_fixture.py)."""
+    if sd == 0.0:
+        return None, None
+    rng = np.random.default_rng(seed)
+    return (rng.normal(0, sd, (B, T, C)).astype(np.float32),
+            rng.normal(0, sd, (B, T, C)).astype(np.float32))
+
+
+@pytest.mark.parametrize("name", ["x1", "x2", "x3", "x4", "x5"])
 def test_long_durations_against_oracle(crf, name):
     if not os.path.exists(FIXTURE):
         pytest.skip(f"{FIXTURE} not generated")
     f = np.load(FIXTURE, allow_pickle=False)
-    seed, B, T, C, K, scale, ragged = f[f"{name}_case"]
+    seed, B, T, C, K, scale, ragged, sd = f[f"{name}_case"]
     seed, B, T, C, K = int(seed), int(B), int(T), int(C), int(K)
-    print(f"\n[long durations {name}: B={B} T={T} C={C} K={K}]", flush=True)
+    print(f"\n[long durations {name}: B={B} T={T} C={C} K={K} projections sd={sd}]", flush=True)
     w = workloads.make_custom(seed, B, T, C, K, em_scale=float(scale), ragged=bool(ragged))
+    ps, pe = _projections(seed + 1000, B, T, C, float(sd))
     em, lengths, trans, dur = to_dev(w.em, w.lengths, w.trans, w.dur)
-    lz = np_(crf.logz(em, lengths, trans, dur, check_status=True))
+    kw = {}
+    if ps is not None:
+        tps, tpe = to_dev(ps, pe)
+        kw = {"proj_start": tps, "proj_end": tpe}
+    lz = np_(crf.logz(em, lengths, trans, dur, check_status=True, **kw))
     close_rel(lz, f[f"{name}_logZ"], LOGZ_RTOL, f[f"{name}_logZ"], "logz")
-    out = crf.backward(em, lengths, trans, dur, check_status=True)
+    out = crf.backward(em, lengths, trans, dur, want_boundaries=True, check_status=True, **kw)
+    close_abs(np_(out["grad_proj_start"]), f[f"{name}_grad_proj_start"], MARG_ATOL, "grad_proj_start")
+    close_abs(np_(out["grad_proj_end"]), f[f"{name}_grad_proj_end"], MARG_ATOL, "grad_proj_end")
+    close_abs(np_(out["boundary"]), f[f"{name}_boundary"], MARG_ATOL, "boundary")
     close_rel(np_(out["log_z"]), f[f"{name}_logZ"], LOGZ_RTOL, f[f"{name}_logZ"], "backward log_z")
     close_abs(np_(out["marginals"]), f[f"{name}_mu"], MARG_ATOL, "marginals")
     close_abs(np_(out["grad_em"]), f[f"{name}_grad_em"], MARG_ATOL, "grad_em")
@@ -73,7 +90,7 @@ def test_long_durations_against_oracle(crf, name):
               "grad_trans")
     close_rel(np_(out["grad_dur"]), f[f"{name}_grad_dur"], GRAD_RTOL, f[f"{name}_grad_dur"],
               "grad_dur")
-    score, labels, seg = crf.viterbi(em, lengths, trans, dur, check_status=True)
+    score, labels, seg = crf.viterbi(em, lengths, trans, dur, check_status=True, **kw)
     close_rel(np_(score), f[f"{name}_score"], LOGZ_RTOL, f[f"{name}_score"], "viterbi score")
     labels, seg = np_(labels), np_(seg)
     for b in range(B):
@@ -82,7 +99,8 @@ def test_long_durations_against_oracle(crf, name):
             np.testing.assert_array_equal(labels[b, :L], f[f"{name}_labels"][b, :L])
             np.testing.assert_array_equal(seg[b, :L], f[f"{name}_seg_start"][b, :L])
         _, S = oracle.centered_prefix(w.em[b], L)
-        got = oracle.segmentation_score(S, w.trans, w.dur, K, seg[b, :L], labels[b, :L])
+        proj = None if ps is None else (ps[b, :L], pe[b, :L])
+        got = oracle.segmentation_score(S, w.trans, w.dur, K, seg[b, :L], labels[b, :L], proj)
         best = float(f[f"{name}_score"][b])
         assert got >= best - LOGZ_RTOL * max(1.0, abs(best)), (b, got, best)
 
