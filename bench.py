@@ -163,7 +163,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--delta", type=int, default=0, help="checkpoint interval (0: ceil(sqrt(TK)))")
-    ap.add_argument("--cpu-sample", type=int, default=12_000)
+    ap.add_argument("--cpu-sample", type=int, default=40_000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-scan-roofline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
