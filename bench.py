@@ -43,7 +43,7 @@ PEAK_HBM_BPS = 8.0e12
 # kernel sources with this SHA-256 (of their concatenation, in this order)
 SWEEP_SRCS = [os.path.join(ROOT, "semi_markov_crf_amd", "csrc", f)
               for f in ("sweep_lse_round.h", "sweep_lse_kernel.h", "ring.h", "common.h")]
-SWEEP_TRAFFIC = {"sha256": "60cedde9b0073c9efe8829453abab37082b5ae4169cfc6d4876e51496da8e91a",
+SWEEP_TRAFFIC = {"sha256": "80e4448cf00fc0a04cf04d3cfa50108d320defcbb64f09c74720172186c70928",
                  "bytes": (19112.97 * 2.0 + 840.0 * 1.0) * 1024}
 
 

@@ -177,18 +177,22 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     // side (segments starting at p); 0 without projections or outside [1, L] / [0, L-1]
     const float* PSb = proj_start ? proj_start + (size_t)b * T * C : nullptr;
     const float* PEb = proj_end ? proj_end + (size_t)b * T * C : nullptr;
-    auto proj_e = [&](int p, int q) -> float {
+    // (the raw natural-log values, then their base-2 form: staging loads the raw values a
+    // chunk ahead and converts them when it stores, so its loads are in flight together)
+    auto proj_e_raw = [&](int p, int q) -> float {
         if constexpr (!PROJ) return 0.0f;
         const float* src = dir == 0 ? PEb : PSb;
         const int t = dir == 0 ? p - 1 : L - p;
-        return (src && p >= 1 && p <= L) ? (float)((double)src[(size_t)t * C + q] * LOG2E) : 0.0f;
+        return (src && p >= 1 && p <= L) ? src[(size_t)t * C + q] : 0.0f;
     };
-    auto proj_s = [&](int p, int q) -> float {
+    auto proj_s_raw = [&](int p, int q) -> float {
         if constexpr (!PROJ) return 0.0f;
         const float* src = dir == 0 ? PSb : PEb;
         const int t = dir == 0 ? p : L - 1 - p;
-        return (src && p >= 0 && p < L) ? (float)((double)src[(size_t)t * C + q] * LOG2E) : 0.0f;
+        return (src && p >= 0 && p < L) ? src[(size_t)t * C + q] : 0.0f;
     };
+    auto base2 = [](float raw) -> float { return (float)((double)raw * LOG2E); };
+    auto proj_s = [&](int p, int q) -> float { return base2(proj_s_raw(p, q)); };
     for (int q = tid; q < (C + 1) * P; q += NT) {
         R[q] = NEG;
         if constexpr (LIN) E[q] = 0.0f;
@@ -371,15 +375,15 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     const int sq = stg ? bt / C : 0;
     const int sl = stg ? bt - sq * C : 0;
     double pf[M];                                          // raw S of the chunk after next
-    float pfe[M], pfs[M];                                  // and its projections (base 2)
+    float pfe[M], pfs[M];                                  // and its raw projections
     auto stage_load = [&](int tcs) {
 #pragma unroll
         for (int d = 0; d < M; ++d) {
             const int t = tcs + M * sq + d;
             const bool in = stg && t <= t1;
             pf[d] = in ? Sb[sidx(t, sl)] : 0.0;
-            pfe[d] = in ? proj_e(t, sl) : 0.0f;
-            pfs[d] = in ? proj_s(t, sl) : 0.0f;
+            pfe[d] = in ? proj_e_raw(t, sl) : 0.0f;
+            pfs[d] = in ? proj_s_raw(t, sl) : 0.0f;
         }
     };
     auto stage_store = [&](int buf) {
@@ -392,12 +396,13 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
         dS[1] = make_double2(sv[2], sv[3]);
         float* f = Fst + (size_t)buf * NPL * C * CH + sl * CH + M * sq;
         if constexpr (PROJ) {
-            float ge[M], gs[M];
+            float ge[M], gs[M], pe2[M];
 #pragma unroll
             for (int d = 0; d < M; ++d) {
                 const float g = (float)(sv[d] - sv[0]);
-                ge[d] = g + pfe[d];
-                gs[d] = g - pfs[d];
+                pe2[d] = base2(pfe[d]);
+                ge[d] = g + pe2[d];
+                gs[d] = g - base2(pfs[d]);
             }
             st4(f, make_float4(fast_exp2(ge[0]), fast_exp2(ge[1]), fast_exp2(ge[2]),
                                fast_exp2(ge[3])));
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
                                         fast_exp2(-gs[3])));
             st4(f + 2 * C * CH, make_float4(ge[0], ge[1], ge[2], ge[3]));
             st4(f + 3 * C * CH, make_float4(gs[0], gs[1], gs[2], gs[3]));
-            st4(f + 4 * C * CH, make_float4(pfe[0], pfe[1], pfe[2], pfe[3]));
+            st4(f + 4 * C * CH, make_float4(pe2[0], pe2[1], pe2[2], pe2[3]));
         } else {
             // one side: ge = gs = g
             float g[M];
