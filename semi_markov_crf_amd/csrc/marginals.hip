@@ -38,18 +38,31 @@ static size_t marg_lds(int C, int TM, int KC) {
     return (size_t)8 * C * (8 * TM + 2 * KC) + (size_t)4 * ((size_t)KC * C + (size_t)C * C);
 }
 
-// Tile and duration chunk: the largest tile (fewer per-tile partial sums) whose LDS fits
-// with a chunk of at least min(K, 64) durations; the smallest tile takes any chunk.
+// Tile and duration chunk.  First choice: the largest tile of at least max(32, K/4)
+// positions (the per-tile duration partials, K*C values, then cost at most a quarter of
+// the per-position inputs) whose LDS, with a chunk of at least min(K, 64) durations, lets
+// three workgroups share a CU (12 wavefronts to hide the latency of the exponentials and
+// the fp64 sums).  Otherwise the largest tile that fits one workgroup per CU with such a
+// chunk; the smallest tile takes any chunk.
 static void marg_shape(int C, int K, int* tm, int* kc) {
-    constexpr size_t BUDGET = 150 * 1024;
-    auto chunks = [&](int t, int min_kc) {
-        if (K <= 512 && marg_lds(C, t, K) <= BUDGET) return K;
+    auto chunks = [&](int t, int min_kc, size_t budget) {
+        if (K <= 512 && marg_lds(C, t, K) <= budget) return K;
         for (int k = 512; k >= min_kc; k >>= 1)
-            if (k < K && marg_lds(C, t, k) <= BUDGET) return k;
+            if (k < K && marg_lds(C, t, k) <= budget) return k;
         return 0;
     };
+    int tmin = 32;
+    while (tmin < 512 && 4 * tmin < K) tmin *= 2;
+    for (int t = 512; t >= tmin; t >>= 1) {
+        const int k = chunks(t, std::min(K, 64), 52 * 1024);
+        if (k > 0) {
+            *tm = t;
+            *kc = k;
+            return;
+        }
+    }
     for (int t = 512; t >= 8; t >>= 1) {
-        const int k = chunks(t, t > 8 ? std::min(K, 64) : 1);
+        const int k = chunks(t, t > 8 ? std::min(K, 64) : 1, 150 * 1024);
         if (k > 0) {
             *tm = t;
             *kc = k;
@@ -361,7 +374,7 @@ hipError_t launch_grad_em(const float* mu, const double* mu_tot, const int* Leff
 // (e, slice) sums the tiles j = slice, slice + RP_SLICES, ... of every sequence into
 // scratch[slice][e].  Pass 2: one lane per output adds the slices in order.  Fixed order
 // throughout: bitwise reproducible.
-constexpr int RP_SLICES = 32;
+constexpr int RP_SLICES = 128;
 
 __global__ __launch_bounds__(256) void k_reduce_partials(const double* __restrict__ part_dur,
                                                          const double* __restrict__ part_trans,
