@@ -6,10 +6,15 @@
 // "On-the-Fly Edge Computation via Prefix Sums").  Positions t > L_b repeat S[b, L_b].
 //
 // Three streaming passes, all HBM bound, with fp64 accumulation:
-//   1. per-tile column sums of the valid emissions (coalesced rows of C floats),
+//   1. per-tile column sums of the valid emissions,
 //   2. an exclusive scan of the tile sums per sequence (also gives nu),
-//   3. the in-tile centred prefix sum, staged through LDS so that both the fp32 reads
-//      and the fp64 writes of the tile are contiguous.
+//   3. the in-tile centred prefix sum.
+// For C <= 8 (tile 1024 rows) passes 1 and 3 give each lane four consecutive rows, so a
+// wavefront's loads and stores cover one contiguous stretch of the tile; every load of a
+// lane is issued before the first is used, and the tile's prefix comes from a wavefront
+// scan of the lanes' row sums (DPP row shifts and row broadcasts, fp64) plus one LDS
+// exchange between the four wavefronts.  Larger C keeps the column-per-thread kernels,
+// which stage the tile through LDS.
 #include "common.h"
 #include "internal.h"
 
@@ -154,10 +159,156 @@ __global__ __launch_bounds__(256) void k_prefix(const float* __restrict__ em,
         for (int c = tid; c < C; c += 256) Sb[c] = 0.0;
 }
 
+// ---------------------------------------------------------------- C <= 8: rows per lane
+constexpr int SCAN_ROWS = 4;   // consecutive rows per lane; 256 lanes x 4 = the 1024-row tile
+
+// one 32-bit half of a double moved by a DPP control; lanes without a source (or outside
+// row_mask) read 0
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_d(double v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWMASK, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWMASK, 0xF, false);
+    return __hiloint2double(hi, lo);
+}
+
+// inclusive sum over the 64 lanes of a wavefront, in lane order: shifts by 1, 2, 4, 8
+// inside each row of 16 lanes, then the last lane of row 0 / 2 into rows 1 / 3, then the
+// last lane of row 1 into rows 2 and 3
+__device__ __forceinline__ double wave_inclusive_sum(double x) {
+    x += dpp_d<0x111, 0xF>(x);
+    x += dpp_d<0x112, 0xF>(x);
+    x += dpp_d<0x114, 0xF>(x);
+    x += dpp_d<0x118, 0xF>(x);
+    x += dpp_d<0x142, 0xA>(x);
+    x += dpp_d<0x143, 0xC>(x);
+    return x;
+}
+
+__device__ __forceinline__ double lane63(double v) {
+    return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 63),
+                            __builtin_amdgcn_readlane(__double2loint(v), 63));
+}
+
+// the lane's rows t0 + 4*tid + i of sequence b, C = CC floats each (0 past T)
+template <int CC>
+__device__ __forceinline__ void load_rows(const float* __restrict__ em, int b, int T, int tr,
+                                          float (&v)[SCAN_ROWS][CC]) {
+    const float* e = em + ((size_t)b * T + tr) * CC;
+    if (tr + SCAN_ROWS <= T) {
+#pragma unroll
+        for (int i = 0; i < SCAN_ROWS; ++i)
+#pragma unroll
+            for (int c = 0; c < CC; ++c) v[i][c] = e[i * CC + c];
+    } else {
+#pragma unroll
+        for (int i = 0; i < SCAN_ROWS; ++i)
+#pragma unroll
+            for (int c = 0; c < CC; ++c) v[i][c] = tr + i < T ? e[i * CC + c] : 0.0f;
+    }
+}
+
+// grid (ntiles, B), block 256, tile 1024 rows
+template <int CC>
+__global__ __launch_bounds__(256) void k_em_tile_sums_rows(const float* __restrict__ em,
+                                                           const int32_t* __restrict__ lengths,
+                                                           int T, double* __restrict__ tile_sums,
+                                                           int* __restrict__ Leff) {
+    __shared__ double wsum[4][CC];
+    const int tile = blockIdx.x, b = blockIdx.y, ntiles = gridDim.x, tid = threadIdx.x;
+    const int Lraw = lengths[b];
+    const bool bad = Lraw < 1 || Lraw > T;
+    const int L = min(max(Lraw, 1), T);
+    if (tile == 0 && tid == 0) Leff[b] = bad ? -L : L;   // negated: length was invalid
+    const int tr = tile * 1024 + SCAN_ROWS * tid;
+    float v[SCAN_ROWS][CC];
+    load_rows<CC>(em, b, T, tr, v);
+#pragma unroll
+    for (int c = 0; c < CC; ++c) {
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < SCAN_ROWS; ++i) s += tr + i < L ? (double)v[i][c] : 0.0;
+        s = lane63(wave_inclusive_sum(s));
+        if ((tid & 63) == 0) wsum[tid >> 6][c] = s;
+    }
+    __syncthreads();
+    if (tid < CC)
+        tile_sums[((size_t)b * ntiles + tile) * CC + tid] =
+            ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
+}
+
+// grid (ntiles, B), block 256, tile 1024 rows
+template <int CC>
+__global__ __launch_bounds__(256) void k_prefix_rows(const float* __restrict__ em,
+                                                     const int* __restrict__ Leff, int B, int T,
+                                                     const double* __restrict__ tile_off,
+                                                     const double* __restrict__ totals,
+                                                     double* __restrict__ S,
+                                                     int* __restrict__ status) {
+    __shared__ double wsum[4][CC];
+    const int tile = blockIdx.x, b = blockIdx.y, ntiles = gridDim.x, tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int L = abs(Leff[b]);
+    const int t0 = tile * 1024;
+    if (tile == 0 && b == 0 && tid == 0) {
+        int flag = 0;
+        for (int i = 0; i < B; ++i) flag |= Leff[i] < 0;
+        status[0] = flag;
+    }
+    const int tr = t0 + SCAN_ROWS * tid;
+    float v[SCAN_ROWS][CC];
+    load_rows<CC>(em, b, T, tr, v);
+    const double* off = tile_off + ((size_t)b * ntiles + tile) * CC;
+    const double* tot = totals + (size_t)b * CC;
+    double x[SCAN_ROWS][CC], excl[CC];
+#pragma unroll
+    for (int c = 0; c < CC; ++c) {
+        const double nu = tot[c] / (double)L;
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < SCAN_ROWS; ++i) {
+            x[i][c] = tr + i < L ? (double)v[i][c] - nu : 0.0;
+            s += x[i][c];
+        }
+        const double incl = wave_inclusive_sum(s);
+        excl[c] = incl - s;
+        if ((tid & 63) == 63) wsum[w][c] = incl;
+    }
+    __syncthreads();
+    double* Sb = S + (size_t)b * (T + 1) * CC;
+#pragma unroll
+    for (int c = 0; c < CC; ++c) {
+        const double nu = tot[c] / (double)L;
+        double run = off[c] - nu * (double)min(t0, L);
+        for (int q = 0; q < w; ++q) run += wsum[q][c];
+        excl[c] += run;
+    }
+#pragma unroll
+    for (int i = 0; i < SCAN_ROWS; ++i) {
+        if (tr + i >= T) break;
+#pragma unroll
+        for (int c = 0; c < CC; ++c) {
+            excl[c] += x[i][c];
+            Sb[(size_t)(tr + i + 1) * CC + c] = excl[c];
+        }
+    }
+    if (tile == 0 && tid < CC) Sb[tid] = 0.0;
+}
+
 hipError_t launch_em_tile_sums(const float* em, const int32_t* lengths, int B, int T, int C,
                                double* tile_sums, int* Leff, hipStream_t stream) {
     const int TS = scan_tile(C);
     const int nt = (T + TS - 1) / TS;
+#define SEMICRF_ROWS_CASE(CC)                                                                  \
+    case CC:                                                                                   \
+        hipLaunchKernelGGL(k_em_tile_sums_rows<CC>, dim3(nt, B), dim3(256), 0, stream, em,     \
+                           lengths, T, tile_sums, Leff);                                       \
+        return hipGetLastError();
+    if (TS == 1024) switch (C) {
+            SEMICRF_ROWS_CASE(1) SEMICRF_ROWS_CASE(2) SEMICRF_ROWS_CASE(3) SEMICRF_ROWS_CASE(4)
+            SEMICRF_ROWS_CASE(5) SEMICRF_ROWS_CASE(6) SEMICRF_ROWS_CASE(7) SEMICRF_ROWS_CASE(8)
+            default: break;
+        }
+#undef SEMICRF_ROWS_CASE
     hipLaunchKernelGGL(k_em_tile_sums, dim3(nt, B), dim3(256), 0, stream, em, lengths, T, C, TS,
                        tile_sums, Leff);
     return hipGetLastError();
@@ -175,6 +326,17 @@ hipError_t launch_prefix(const float* em, const int* Leff, int B, int T, int C,
                          hipStream_t stream) {
     const int TS = scan_tile(C);
     const int nt = (T + TS - 1) / TS;
+#define SEMICRF_ROWS_CASE(CC)                                                                  \
+    case CC:                                                                                   \
+        hipLaunchKernelGGL(k_prefix_rows<CC>, dim3(nt, B), dim3(256), 0, stream, em, Leff, B,  \
+                           T, tile_offsets, totals, S, status);                                \
+        return hipGetLastError();
+    if (TS == 1024) switch (C) {
+            SEMICRF_ROWS_CASE(1) SEMICRF_ROWS_CASE(2) SEMICRF_ROWS_CASE(3) SEMICRF_ROWS_CASE(4)
+            SEMICRF_ROWS_CASE(5) SEMICRF_ROWS_CASE(6) SEMICRF_ROWS_CASE(7) SEMICRF_ROWS_CASE(8)
+            default: break;
+        }
+#undef SEMICRF_ROWS_CASE
     const size_t lds = (size_t)TS * C * 8 + 256 * 8 + (size_t)TS * C * 4;
     hipLaunchKernelGGL(k_prefix, dim3(nt, B), dim3(256), lds, stream, em, Leff, B, T, C, TS,
                        tile_offsets, totals, S, status);

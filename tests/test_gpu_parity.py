@@ -230,11 +230,18 @@ def test_config_against_oracle_fixture(crf, cfg):
     check_viterbi(w, np_(score), np_(labels), np_(seg), vref)
 
 
-@pytest.mark.parametrize("cfg_or_case", ["tiny", "ragged", "speech", "long"])
+# label counts 1..8 take the rows-per-lane kernels (odd T: a partial last lane, lengths
+# inside the last tile), 39 and 64 the column kernels
+SCAN_CUSTOM = {"ragged": (61, 5, 3000, 7), "c1_odd": (62, 3, 2051, 1), "c3_odd": (63, 4, 1027, 3),
+               "c8_odd": (64, 2, 4093, 8), "c5_short": (65, 3, 5, 5), "c64": (66, 2, 777, 64)}
+
+
+@pytest.mark.parametrize("cfg_or_case", ["tiny", "speech", "long"] + list(SCAN_CUSTOM))
 def test_prefix_scan_against_oracle(crf, cfg_or_case):
     """Centring + prefix sums (fp64 on both sides): |gpu - ref| <= 1e-9 * max(1, |ref|)."""
-    if cfg_or_case == "ragged":
-        w = workloads.make_custom(61, 5, 3000, 7, 3, em_scale=3.0, ragged=True)
+    if cfg_or_case in SCAN_CUSTOM:
+        seed, B, T, C = SCAN_CUSTOM[cfg_or_case]
+        w = workloads.make_custom(seed, B, T, C, 3, em_scale=3.0, ragged=True)
     else:
         w = workloads.make({"tiny": 0, "speech": 1, "long": 3}[cfg_or_case])
     em, lengths, _, _ = dev(w)
