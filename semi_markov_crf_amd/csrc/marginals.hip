@@ -39,8 +39,8 @@ static size_t marg_lds(int C, int TM, int KC) {
 }
 
 // Tile and duration chunk.  First choice: the largest tile of at least max(32, K/4)
-// positions (the per-tile duration partials, K*C values, then cost at most a quarter of
-// the per-position inputs) whose LDS, with a chunk of at least min(K, 64) durations, lets
+// positions (the per-tile duration partials, K*C doubles, then take at most as much memory
+// as the four per-position input arrays) whose LDS, with a chunk of at least min(K, 64) durations, lets
 // three workgroups share a CU (12 wavefronts to hide the latency of the exponentials and
 // the fp64 sums).  Otherwise the largest tile that fits one workgroup per CU with such a
 // chunk; the smallest tile takes any chunk.

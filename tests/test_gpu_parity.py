@@ -255,3 +255,28 @@ def test_prefix_scan_against_oracle(crf, cfg_or_case):
         flat = np.abs(S[b, L + 1:] - S[b, L]) / np.maximum(1.0, np.abs(S[b, L]))
         assert flat.size == 0 or flat.max() <= 1e-9      # flat beyond the length
         assert np.abs(S[b, L]).max() < 1e-9 * max(1, L)  # centred: S[L] = 0
+
+
+def test_long_genomic_peak_device_memory(crf):
+    """The long genomic configuration (B=1, T=10^6, K=200, C=6) streams: the backward pass
+    and the Viterbi decode together allocate well under 1 GB of device memory, where the
+    dense edge tensor alone would take T*K*C^2*4 B = 28.8 GB (about 29 GB in the EN
+    explainer, "1. Problem Statement")."""
+    import torch
+    w = workloads.make(3)
+    print(f"\n[peak memory: {w.name} B={w.B} T={w.T} C={w.C} K={w.K}]", flush=True)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    em, lengths, trans, dur = dev(w)
+    out = crf.backward(em, lengths, trans, dur, check_status=True)
+    score, labels, seg = crf.viterbi(em, lengths, trans, dur, check_status=True)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    dense = w.T * w.K * w.C * w.C * 4
+    print(f"peak device memory {peak / 2**20:.1f} MiB (inputs, outputs and workspaces); "
+          f"dense edge tensor {dense / 1e9:.1f} GB", flush=True)
+    assert np.isfinite(np_(out["log_z"])).all() and np.isfinite(np_(score)).all()
+    assert peak < 1 << 30
+    assert dense > 25 * peak
