@@ -132,6 +132,14 @@ def extras(crf, w, em, lengths, trans, dur, d):
     ms0 = _time_ms(lambda: crf.backward(em, lengths, trans, dur, workspace=ws), d, 3)
     out["nll"] = {"ms": ms, "positions_per_s": pos / (ms * 1e-3), "backward_alone_ms": ms0,
                   "what": "semicrf_nll (backward pass + gold-segmentation kernels), genomic shape"}
+    # inference alone, and an autograd-style forward then backward as two calls
+    ml = _time_ms(lambda: crf.logz(em, lengths, trans, dur, workspace=ws), d, 3)
+    mlb = _time_ms(lambda: (crf.logz(em, lengths, trans, dur, workspace=ws),
+                            crf.backward(em, lengths, trans, dur, workspace=ws)), d, 3)
+    out["logz"] = {"ms": ml, "positions_per_s": pos / (ml * 1e-3),
+                   "logz_then_backward_ms": mlb,
+                   "what": "semicrf_logz alone (one forward sweep per sequence), and semicrf_logz "
+                           "followed by semicrf_backward, genomic shape"}
     g = torch.Generator(device="cpu").manual_seed(11)
     ps = torch.randn(em.shape, generator=g).to(d)
     pe = torch.randn(em.shape, generator=g).to(d)
@@ -325,6 +333,9 @@ def main():
         "fwd_bwd_positions_per_s": positions / (bwd_ms * 1e-3),
         "viterbi_positions_per_s": positions / (vit_ms * 1e-3),
         "edges_per_s_nominal": positions * K * C * C / (bwd_ms * 1e-3),
+        # recurrence passes over every position in one backward call: the forward and the
+        # mirrored checkpoint sweeps, then the span recompute in both directions
+        "recurrence_passes": 4,
         "wall_s_timed_region": wall,
     }
 
@@ -348,11 +359,22 @@ def main():
             times.append(e0.elapsed_time(e1))
         ms = min(times[1:])
         nbytes = Bs * Ts * C * (4 + 4 + 8)        # em read twice (mean, then scan), S written
+        # for scale: a plain device copy of S (read and write 8 B per element)
+        S_copy = torch.empty_like(S_big)
+        ctimes = []
+        for _ in range(4):
+            e0.record()
+            S_copy.copy_(S_big)
+            e1.record()
+            torch.cuda.synchronize(d)
+            ctimes.append(e0.elapsed_time(e1))
+        cms = min(ctimes[1:])
         out["scan_roofline"] = {"bound": "hbm", "shape": f"B={Bs} T={Ts} C={C}",
                                 "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": 8000.0,
                                 "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / PEAK_HBM_BPS,
-                                "ms": ms, "algorithmic_bytes": nbytes}
-        del em_big, S_big, ws_s
+                                "ms": ms, "algorithmic_bytes": nbytes,
+                                "device_copy_GBps": 2 * S_big.numel() * 8 / (cms * 1e-3) / 1e9}
+        del em_big, S_big, S_copy, ws_s
 
     if not args.no_extras:
         out["extras"] = extras(crf, w, em, lengths, trans, dur, d)
