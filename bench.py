@@ -216,30 +216,21 @@ def main():
     stream_b, stream_v = s_b.cuda_stream, s_v.cuda_stream
     stream = main.cuda_stream
 
+    def _opt(ev):
+        if ev is None:
+            return None
+        return ctypes.byref(_native.options(events=ctypes.cast(ev, ctypes.c_void_p).value))
+
     def step(ev_b=None, ev_v=None):
-        if ev_b is None:
-            rc = lib.semicrf_backward(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
-                                      dur.data_ptr(), None, None, B, T, C, K, args.delta, stream_b,
-                                      ws_b.data_ptr(), nb, None, g_em.data_ptr(), g_tr.data_ptr(),
-                                      g_du.data_ptr(), mu.data_ptr(), lz.data_ptr(), None, None,
-                                      None)
-        else:
-            rc = lib.semicrf_backward_staged(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
-                                             dur.data_ptr(), None, None, B, T, C, K, args.delta,
-                                             stream_b, ws_b.data_ptr(), nb, None, g_em.data_ptr(),
-                                             g_tr.data_ptr(), g_du.data_ptr(), mu.data_ptr(),
-                                             lz.data_ptr(), None, None, None, ev_b)
+        rc = lib.semicrf_backward_ex(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
+                                     dur.data_ptr(), B, T, C, K, args.delta, stream_b,
+                                     ws_b.data_ptr(), nb, None, g_em.data_ptr(), g_tr.data_ptr(),
+                                     g_du.data_ptr(), mu.data_ptr(), lz.data_ptr(), _opt(ev_b))
         _native.check("semicrf_backward", rc)
-        if ev_v is None:
-            rc = lib.semicrf_viterbi(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
-                                     dur.data_ptr(), None, None, B, T, C, K, stream_v,
-                                     ws_v.data_ptr(), nv, score.data_ptr(), labels.data_ptr(),
-                                     seg.data_ptr())
-        else:
-            rc = lib.semicrf_viterbi_staged(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
-                                            dur.data_ptr(), None, None, B, T, C, K, stream_v,
-                                            ws_v.data_ptr(), nv, score.data_ptr(),
-                                            labels.data_ptr(), seg.data_ptr(), ev_v)
+        rc = lib.semicrf_viterbi_ex(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
+                                    dur.data_ptr(), B, T, C, K, stream_v, ws_v.data_ptr(), nv,
+                                    score.data_ptr(), labels.data_ptr(), seg.data_ptr(),
+                                    _opt(ev_v))
         _native.check("semicrf_viterbi", rc)
 
     torch.cuda.synchronize(d)          # inputs are resident before either stream starts

@@ -61,7 +61,8 @@ typedef enum {
     SEMICRF_ERR_INVALID = 1,      /* bad scalar argument or NULL pointer, or a device-flagged length */
     SEMICRF_ERR_WORKSPACE = 2,    /* workspace NULL, too small or misaligned */
     SEMICRF_ERR_UNSUPPORTED = 3,  /* shape outside the supported range */
-    SEMICRF_ERR_DEVICE = 4        /* a HIP launch or copy failed */
+    SEMICRF_ERR_DEVICE = 4,       /* a HIP launch or copy failed */
+    SEMICRF_ERR_UNIMPLEMENTED = 5 /* reserved: no entry point of this library returns it */
 } semicrf_status;
 
 typedef enum {
@@ -74,14 +75,14 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* semicrf_status_string(int status);
 
-/* Checkpoint interval used by semicrf_backward for a padded length T and maximum
- * duration K: delta if delta > 0, else ceil(sqrt(T*K)) (EN explainer, "2. Methodology",
- * "Checkpointing": interval of about sqrt(TK)); clamped to [1, T].  0 on bad input. */
+/* Checkpoint interval for a padded length T and maximum duration K: delta if delta > 0,
+ * else ceil(sqrt(T*K)) (EN explainer, "2. Methodology", "Checkpointing": an interval of
+ * about sqrt(TK)); clamped to [1, T].  0 on bad input. */
 int semicrf_checkpoint_interval(int T, int K, int delta);
 
-/* Bytes of workspace that `op` needs for these shapes (delta as above; ignored by
- * LOGZ and VITERBI).  0 if the arguments are invalid or unsupported. */
-size_t semicrf_workspace_bytes(int op, int B, int T, int C, int K, int delta);
+/* Bytes of workspace that `op` needs for these shapes (delta as above).  0 if the
+ * arguments are invalid or unsupported. */
+size_t semicrf_workspace_bytes(semicrf_op op, int B, int T, int C, int K, int delta);
 
 /* Centred prefix sums alone (EN explainer, "2. Methodology": "Emission Baseline
  * Centering" then "On-the-Fly Edge Computation via Prefix Sums"):
@@ -92,23 +93,17 @@ size_t semicrf_workspace_bytes(int op, int B, int T, int C, int K, int delta);
 int semicrf_prefix(const float* emissions, const int32_t* lengths, int B, int T, int C,
                    hipStream_t stream, void* workspace, size_t workspace_bytes, double* S);
 
-/* Boundary projections (EN explainer, "2. Methodology", "Boundary Projections": start
- * and end features computed apart and added to the edge potential).  Every call below
- * that takes them accepts
- *   proj_start [B, T, C] float32 or NULL  score of a segment of label c that starts at t
- *   proj_end   [B, T, C] float32 or NULL  score of a segment of label c whose last
- *                                         position is t
- * so a segment [s, e) of label c gains proj_start[b, s, c] + proj_end[b, e-1, c].  NULL
- * means zeros; values at t >= lengths[b] are ignored; the values must be finite (a large
- * negative value, e.g. -1e4, effectively forbids a start or end).  They are not centred. */
+/* ------------------------------------------------------------------ the three calls
+ * Each takes (emissions, lengths, trans, dur, sizes, stream) as the problem statement
+ * gives them, plus a caller-owned workspace and the outputs. */
 
 /* log Z for every sequence: the log-sum-exp of the scores of all segmentations
  * (EN explainer, "2. Methodology", "Streaming Forward-Backward with Ring Buffers",
- * forward pass).  Output: log_z [B] float32. */
+ * forward pass).  delta: checkpoint interval (0 = ceil(sqrt(T*K))), the same value as
+ * given to semicrf_workspace_bytes.  Output: log_z [B] float32. */
 int semicrf_logz(const float* emissions, const int32_t* lengths, const float* trans,
-                 const float* dur, const float* proj_start, const float* proj_end, int B,
-                 int T, int C, int K, hipStream_t stream, void* workspace,
-                 size_t workspace_bytes, float* log_z);
+                 const float* dur, int B, int T, int C, int K, int delta, hipStream_t stream,
+                 void* workspace, size_t workspace_bytes, float* log_z);
 
 /* Exact gradients of sum_b grad_log_z[b] * log Z_b (EN explainer, "2. Methodology",
  * backward pass with recomputation from checkpoints every `delta` positions;
@@ -121,21 +116,109 @@ int semicrf_logz(const float* emissions, const int32_t* lengths, const float* tr
  *   marginals      [B, T, C] float32  or NULL: posterior probability that position t
  *                                     lies in a segment of label c (sums to 1 over c)
  *   log_z          [B]       float32  or NULL
- *   grad_proj_start [B, T, C] float32 or NULL: d/d proj_start, g_b times the probability
- *                                     that a segment of label c starts at t
- *   grad_proj_end   [B, T, C] float32 or NULL: d/d proj_end, g_b times the probability
- *                                     that a segment of label c has its last position at t
- *   boundary       [B, T]    float32  or NULL: probability that a segment starts at t
- *                                     (1 at t = 0; EN explainer, "4. Results and
- *                                     Benchmarks": boundary probabilities)
  * delta: checkpoint interval (0 = ceil(sqrt(T*K))); results do not depend on it
  * beyond rounding. */
 int semicrf_backward(const float* emissions, const int32_t* lengths, const float* trans,
-                     const float* dur, const float* proj_start, const float* proj_end, int B,
-                     int T, int C, int K, int delta, hipStream_t stream, void* workspace,
-                     size_t workspace_bytes, const float* grad_log_z, float* grad_emissions,
-                     float* grad_trans, float* grad_dur, float* marginals, float* log_z,
-                     float* grad_proj_start, float* grad_proj_end, float* boundary);
+                     const float* dur, int B, int T, int C, int K, int delta,
+                     hipStream_t stream, void* workspace, size_t workspace_bytes,
+                     const float* grad_log_z, float* grad_emissions, float* grad_trans,
+                     float* grad_dur, float* marginals, float* log_z);
+
+/* Max-plus decode of the best segmentation (the Viterbi counterpart of the forward
+ * pass).  Every max-plus step keeps the shortest segment, then the lowest previous
+ * label, among equal candidates, and the decode ends at the lowest best final label.
+ * When several segmentations share the best score (to fp32 rounding), the one returned
+ * may differ from the one these rules give in exact arithmetic; a decision that beats
+ * every alternative by more than rounding is always taken as in exact arithmetic.
+ * Outputs:
+ *   best_score [B]    float32  score of the best segmentation
+ *   labels     [B, T] int32    label of every position, -1 at t >= lengths[b]
+ *   seg_start  [B, T] uint8    1 where a segment starts, else 0 */
+int semicrf_viterbi(const float* emissions, const int32_t* lengths, const float* trans,
+                    const float* dur, int B, int T, int C, int K, hipStream_t stream,
+                    void* workspace, size_t workspace_bytes, float* best_score,
+                    int32_t* labels, uint8_t* seg_start);
+
+/* ------------------------------------------------------------------ extended calls
+ * The same three calls (and the training loss) with optional extras.  A NULL options
+ * pointer, or a zero-initialised struct, gives exactly the plain call. */
+typedef struct semicrf_options {
+    /* Boundary projections (EN explainer, "2. Methodology", "Boundary Projections": start
+     * and end features computed apart and added to the edge potential), inputs of every
+     * call:
+     *   proj_start [B, T, C] or NULL: score of a segment of label c that starts at t
+     *   proj_end   [B, T, C] or NULL: score of a segment of label c whose last position is t
+     * so a segment [s, e) of label c gains proj_start[b, s, c] + proj_end[b, e-1, c].  NULL
+     * means zeros; values at t >= lengths[b] are ignored; the values must be finite (a
+     * large negative value, e.g. -1e4, effectively forbids a start or end); not centred. */
+    const float* proj_start;
+    const float* proj_end;
+    /* Backward and training-loss outputs, each optional (NULL):
+     *   grad_proj_start [B, T, C]  g_b times the probability that a segment of label c
+     *                              starts at t (d/d proj_start)
+     *   grad_proj_end   [B, T, C]  g_b times the probability that a segment of label c has
+     *                              its last position at t (d/d proj_end) */
+    float* grad_proj_start;
+    float* grad_proj_end;
+    /* Backward outputs, each optional (NULL):
+     *   boundary  [B, T]  probability that a segment starts at t (1 at t = 0; EN explainer,
+     *                     "4. Results and Benchmarks": boundary probabilities)
+     *   node_mass [B, T]  the sum over labels of the node marginals as the forward and
+     *                     backward values give them, before the marginals are divided by
+     *                     it: 1 in exact arithmetic, so |node_mass - 1| measures the
+     *                     rounding of the streamed recurrences (0 at padding) */
+    float* boundary;
+    float* node_mass;
+    /* Stage timing: NULL, or events created by the caller (hipEventCreate), one more than
+     * the call's stage count; events[i] is recorded on `stream` when stage i begins and
+     * the last when the call's work ends.  No synchronisation.
+     *   logz:     0 centring + prefix scan, 1 forward sweep
+     *   backward: 0 centring + prefix scan, 1 the checkpoint spans of both directions
+     *             with their per-position values, 2 seam check and repair, 3 segment
+     *             posteriors, 4 node marginals and gradient reductions (for C > 16: 1
+     *             checkpoint sweeps, 2 span recompute)
+     *   viterbi:  0 centring + prefix scan, 1 max-plus sweep, 2 combine and backtrace */
+    hipEvent_t* events;
+    /* Checkpoint spans swept at once.  The sweeps are sequential in the position; every
+     * span of delta positions is swept at the same time instead, starting 3K positions
+     * early (at least 64) from a ring in which every entry is equal.  The values a span
+     * then reaches equal the exact ones plus one constant, to within rounding; at each
+     * checkpoint the library compares the two spans' ring values over the K positions
+     * before it, takes the constant from them and accepts the seam when every entry is
+     * within seam_tolerance of it (natural-log units; 0 = the default, 1e-4).  From the
+     * first seam that is not accepted the sequence is swept again in order, exactly as a
+     * single sweep would.  C <= 16; for C > 16 the sweeps run in order.
+     *   seam_bound   [B] float32 or NULL: per sequence, the sum over both directions'
+     *                accepted seams of the largest deviation from the constant; no value
+     *                of the call moves by more than it (beyond rounding) from the values
+     *                of sweeps run in order
+     *   seam_repairs [B] int32 or NULL: the number of directions (0..2) swept again in
+     *                order from a seam that was not accepted
+     * A negative seam_tolerance accepts no seam (every sequence is swept in order after
+     * its first span: the exact fallback, for testing). */
+    float* seam_bound;
+    int32_t* seam_repairs;
+    double seam_tolerance;
+} semicrf_options;
+
+#define SEMICRF_LOGZ_STAGES 2
+#define SEMICRF_BACKWARD_STAGES 5
+#define SEMICRF_VITERBI_STAGES 3
+
+int semicrf_logz_ex(const float* emissions, const int32_t* lengths, const float* trans,
+                    const float* dur, int B, int T, int C, int K, int delta,
+                    hipStream_t stream, void* workspace, size_t workspace_bytes, float* log_z,
+                    const semicrf_options* options);
+int semicrf_backward_ex(const float* emissions, const int32_t* lengths, const float* trans,
+                        const float* dur, int B, int T, int C, int K, int delta,
+                        hipStream_t stream, void* workspace, size_t workspace_bytes,
+                        const float* grad_log_z, float* grad_emissions, float* grad_trans,
+                        float* grad_dur, float* marginals, float* log_z,
+                        const semicrf_options* options);
+int semicrf_viterbi_ex(const float* emissions, const int32_t* lengths, const float* trans,
+                       const float* dur, int B, int T, int C, int K, hipStream_t stream,
+                       void* workspace, size_t workspace_bytes, float* best_score,
+                       int32_t* labels, uint8_t* seg_start, const semicrf_options* options);
 
 /* Training loss of gold segmentations and its gradients.  nll[b] = log Z_b - score_b(y*),
  * the negative log-probability of the gold segmentation y* (the training loss of the
@@ -147,66 +230,20 @@ int semicrf_backward(const float* emissions, const int32_t* lengths, const float
  *   gold_seg_start [B, T] uint8  1 at each gold segment's first position (t = 0 must be 1)
  *   grad_nll       [B] float32 or NULL for all ones
  * Outputs: nll [B] float32, and the gradients of sum_b grad_nll[b] * nll[b] in
- * grad_emissions [B, T, C], grad_trans [C, C], grad_dur [K, C] and, each optional (NULL),
+ * grad_emissions [B, T, C], grad_trans [C, C], grad_dur [K, C] and, through the options,
  * grad_proj_start / grad_proj_end [B, T, C] (expected minus gold feature counts; the
- * emission gradient includes the centring; 0 at padding).  A gold segmentation
- * with a segment longer than K, a label outside [0, C), a label change inside a segment or
- * no start at t = 0 gives NaN for that sequence and raises the status flag, like an
- * invalid length; its gold counts are then left out of the gradients, which keep only
- * its log Z half.  Workspace: semicrf_workspace_bytes(SEMICRF_OP_BACKWARD, ...). */
+ * emission gradient includes the centring; 0 at padding).  Options: projections and
+ * their gradients only (the other fields must be NULL).  A gold segmentation with a
+ * segment longer than K, a label outside [0, C), a label change inside a segment or no
+ * start at t = 0 gives NaN for that sequence and raises the status flag, like an invalid
+ * length; its gold counts are then left out of the gradients, which keep only its log Z
+ * half.  Workspace: semicrf_workspace_bytes(SEMICRF_OP_BACKWARD, ...). */
 int semicrf_nll(const float* emissions, const int32_t* lengths, const float* trans,
-                const float* dur, const float* proj_start, const float* proj_end,
-                const int32_t* gold_labels, const uint8_t* gold_seg_start, int B, int T, int C,
-                int K, int delta, hipStream_t stream, void* workspace, size_t workspace_bytes,
-                const float* grad_nll, float* nll, float* grad_emissions, float* grad_trans,
-                float* grad_dur, float* grad_proj_start, float* grad_proj_end);
-
-/* Max-plus decode of the best segmentation (the Viterbi counterpart of the forward
- * pass).  Each max-plus step breaks ties toward the shortest segment, then the lowest
- * previous label.  For C <= 16 the forward sweep and a sweep over the mirrored sequence
- * meet in the middle and the best boundary of the meeting window joins them (lowest
- * position, then labels, on ties); for C > 16 one forward sweep ends at the lowest best
- * final label.  When several segmentations share the best score (to fp32 rounding),
- * which one is returned is therefore implementation-defined; a best segmentation that
- * beats every other by more than rounding is returned exactly.  Outputs:
- *   best_score [B]    float32  score of the best segmentation
- *   labels     [B, T] int32    label of every position, -1 at t >= lengths[b]
- *   seg_start  [B, T] uint8    1 where a segment starts, else 0 */
-int semicrf_viterbi(const float* emissions, const int32_t* lengths, const float* trans,
-                    const float* dur, const float* proj_start, const float* proj_end, int B,
-                    int T, int C, int K, hipStream_t stream, void* workspace,
-                    size_t workspace_bytes, float* best_score, int32_t* labels,
-                    uint8_t* seg_start);
-
-/* Stage-timed variants, for profiling.  Identical results to the calls above; in
- * addition, events[i] (created by the caller with hipEventCreate) is recorded on
- * `stream` when stage i begins, and events[NSTAGES] when the call's work ends, so
- * hipEventElapsedTime(events[i], events[i+1]) is the device time of stage i.
- * events must be non-NULL (else SEMICRF_ERR_INVALID).  No synchronisation.
- *   logz:     0 centring + prefix scan, 1 forward sweep
- *   backward: 0 centring + prefix scan, 1 checkpoint sweeps (both directions at once;
- *             empty when delta >= T), 2 span recompute, 3 segment posteriors,
- *             4 node marginals and gradient reductions
- *   viterbi:  0 centring + prefix scan, 1 max-plus sweep, 2 combine and backtrace */
-#define SEMICRF_LOGZ_STAGES 2
-#define SEMICRF_BACKWARD_STAGES 5
-#define SEMICRF_VITERBI_STAGES 3
-int semicrf_logz_staged(const float* emissions, const int32_t* lengths, const float* trans,
-                        const float* dur, const float* proj_start, const float* proj_end, int B,
-                        int T, int C, int K, hipStream_t stream, void* workspace,
-                        size_t workspace_bytes, float* log_z, hipEvent_t* events);
-int semicrf_backward_staged(const float* emissions, const int32_t* lengths, const float* trans,
-                            const float* dur, const float* proj_start, const float* proj_end,
-                            int B, int T, int C, int K, int delta, hipStream_t stream,
-                            void* workspace, size_t workspace_bytes, const float* grad_log_z,
-                            float* grad_emissions, float* grad_trans, float* grad_dur,
-                            float* marginals, float* log_z, float* grad_proj_start,
-                            float* grad_proj_end, float* boundary, hipEvent_t* events);
-int semicrf_viterbi_staged(const float* emissions, const int32_t* lengths, const float* trans,
-                           const float* dur, const float* proj_start, const float* proj_end,
-                           int B, int T, int C, int K, hipStream_t stream, void* workspace,
-                           size_t workspace_bytes, float* best_score, int32_t* labels,
-                           uint8_t* seg_start, hipEvent_t* events);
+                const float* dur, const int32_t* gold_labels, const uint8_t* gold_seg_start,
+                int B, int T, int C, int K, int delta, hipStream_t stream, void* workspace,
+                size_t workspace_bytes, const float* grad_nll, float* nll,
+                float* grad_emissions, float* grad_trans, float* grad_dur,
+                const semicrf_options* options);
 
 /* Synchronously reads the device status flag left in `workspace` by the last call
  * that used it (after waiting for `stream`).  SEMICRF_OK, SEMICRF_ERR_INVALID if a

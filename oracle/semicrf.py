@@ -219,7 +219,14 @@ def posteriors(S, trans, dur, K: int, L: int, alpha, beta, logZ: float, proj=Non
 def viterbi(S, trans, dur, K: int, L: int, proj=None):
     """Max-plus version of ``forward`` with backpointers.  Ties go to the
     lexicographically lowest (k, c'), then the lowest final label (reading 7).
-    Returns score, labels [L], seg_start [L] (uint8), margin, segments."""
+    Returns score, labels [L], seg_start [L] (uint8), margin, segments (s, k, c)
+    in order, and the decision gaps: ``gaps[i]`` is the gap at the node where
+    segment i ends (its label fixed), between the chosen (k, c') and the best
+    other choice there; ``final_gap`` the gap of the final label.  Because the
+    decoded path continues optimally from every node it visits, a segmentation
+    that also has a segment of label c ending where segment i ends, but a
+    different length or previous label, scores at most score - gaps[i]; one with
+    another final label at most score - final_gap."""
     C = S.shape[1]
     V = np.full((L + 1, C + 1), NEG_INF)
     V[0, C] = 0.0
@@ -247,12 +254,15 @@ def viterbi(S, trans, dur, K: int, L: int, proj=None):
     score = float(final[c])
     others = np.delete(final, c)
     margin = float(score - others.max()) if others.size else np.inf
+    final_gap = margin
     labels = np.empty(L, dtype=np.int32)
     seg_start = np.zeros(L, dtype=np.uint8)
     segments = []
+    gaps = []
     t = L
     while t > 0:
         margin = min(margin, float(gap[t, c]))
+        gaps.append(float(gap[t, c]))
         k_idx, cp = divmod(int(bp[t, c]), C + 1)
         k = k_idx + 1
         s = t - k
@@ -261,8 +271,9 @@ def viterbi(S, trans, dur, K: int, L: int, proj=None):
         segments.append((s, k, c))
         t, c = s, cp
     segments.reverse()
+    gaps.reverse()
     return {"score": score, "labels": labels, "seg_start": seg_start, "margin": margin,
-            "segments": segments}
+            "segments": segments, "gaps": np.array(gaps), "final_gap": final_gap}
 
 
 def segmentation_score(S, trans, dur, K: int, seg_start: np.ndarray, labels: np.ndarray,
@@ -420,7 +431,8 @@ def batch(em, lengths, trans, dur, K: int, grad_log_z=None, *, want_viterbi=True
     """Run ``sequence`` for every b and pack the results into padded arrays
     with the ABI's conventions (zeros / -1 at t >= L).  grad_trans and grad_dur
     are summed over the batch.  proj_start / proj_end: [B, T, C] or None
-    (zeros)."""
+    (zeros).  With Viterbi, ``paths[b]`` holds the decoded segments [n, 3] as
+    (start, length, label) rows with their decision gaps (see ``viterbi``)."""
     em = np.asarray(em)
     B, T, C = em.shape
     g = np.ones(B) if grad_log_z is None else np.asarray(grad_log_z, dtype=np.float64)
@@ -460,5 +472,8 @@ def batch(em, lengths, trans, dur, K: int, grad_log_z=None, *, want_viterbi=True
             seg[b, :L] = r["viterbi"]["seg_start"]
         out.update(score=np.array([r["viterbi"]["score"] for r in res]),
                    margin=np.array([r["viterbi"]["margin"] for r in res]),
-                   labels=labels, seg_start=seg)
+                   labels=labels, seg_start=seg,
+                   paths=[{"segments": np.array(r["viterbi"]["segments"], dtype=np.int64)
+                           .reshape(-1, 3), "gaps": r["viterbi"]["gaps"],
+                           "final_gap": r["viterbi"]["final_gap"]} for r in res])
     return out

@@ -118,28 +118,48 @@ def _ptr(x):
     return None if x is None else x.data_ptr()
 
 
-def logz(em, lengths, trans, dur, *, proj_start=None, proj_end=None, workspace=None,
-         check_status=False) -> torch.Tensor:
+def _options(**fields):
+    """Options struct for the *_ex calls (None when every field is NULL)."""
+    fields = {k: v for k, v in fields.items() if v is not None}
+    return _native.options(**fields) if fields else None
+
+
+def _seams(B, dev, want):
+    if not want:
+        return None, None
+    return (torch.empty(B, dtype=torch.float32, device=dev),
+            torch.empty(B, dtype=torch.int32, device=dev))
+
+
+def logz(em, lengths, trans, dur, *, proj_start=None, proj_end=None, delta=0, workspace=None,
+         seam_tolerance=0.0, want_seams=False, check_status=False):
+    """log Z [B].  With want_seams, returns (log Z, seam_bound [B], seam_repairs [B]) (see
+    semicrf_options in include/semicrf.h); seam_tolerance < 0 forces the in-order sweep."""
     B, T, C, K = _check_inputs(em, lengths, trans, dur)
     ps, pe = _proj(em, proj_start, proj_end)
-    ws, n = _workspace(OP_LOGZ, B, T, C, K, 0, em.device, workspace)
+    ws, n = _workspace(OP_LOGZ, B, T, C, K, delta, em.device, workspace)
     out = torch.empty(B, dtype=torch.float32, device=em.device)
-    rc = _native.load().semicrf_logz(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
-                                     dur.data_ptr(), _ptr(ps), _ptr(pe), B, T, C, K,
-                                     _stream(em.device), ws.data_ptr(), n, out.data_ptr())
+    sb, sr = _seams(B, em.device, want_seams)
+    opt = _options(proj_start=_ptr(ps), proj_end=_ptr(pe), seam_bound=_ptr(sb),
+                   seam_repairs=_ptr(sr), seam_tolerance=float(seam_tolerance) or None)
+    rc = _native.load().semicrf_logz_ex(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
+                                        dur.data_ptr(), B, T, C, K, delta, _stream(em.device),
+                                        ws.data_ptr(), n, out.data_ptr(), opt)
     _native.check("semicrf_logz", rc)
     _maybe_check(ws, check_status, "semicrf_logz")
-    return out
+    return (out, sb, sr) if want_seams else out
 
 
 def backward(em, lengths, trans, dur, *, proj_start=None, proj_end=None, grad_log_z=None,
-             delta=0, want_marginals=True, want_boundaries=False, workspace=None,
-             check_status=False) -> dict:
+             delta=0, want_marginals=True, want_boundaries=False, want_node_mass=False,
+             seam_tolerance=0.0, want_seams=False, workspace=None, check_status=False) -> dict:
     """Gradients of sum_b grad_log_z[b] * log Z_b (all ones when None).  Returns a dict
     with grad_em [B,T,C], grad_trans [C,C], grad_dur [K,C], marginals [B,T,C] (or
     None) and log_z [B]; with want_boundaries (or projections given) also
     grad_proj_start / grad_proj_end [B,T,C] and boundary [B,T], the probability that a
-    segment starts at t."""
+    segment starts at t; with want_node_mass the per-position sum over labels of the
+    marginals before normalisation, node_mass [B,T]; with want_seams seam_bound [B] and
+    seam_repairs [B] (semicrf_options); seam_tolerance < 0 forces the in-order sweeps."""
     B, T, C, K = _check_inputs(em, lengths, trans, dur)
     dev = em.device
     ps, pe = _proj(em, proj_start, proj_end)
@@ -157,17 +177,26 @@ def backward(em, lengths, trans, dur, *, proj_start=None, proj_end=None, grad_lo
     gps = torch.empty_like(em) if want_b else None
     gpe = torch.empty_like(em) if want_b else None
     bnd = torch.empty((B, T), dtype=torch.float32, device=dev) if want_b else None
-    rc = _native.load().semicrf_backward(
-        em.data_ptr(), lengths.data_ptr(), trans.data_ptr(), dur.data_ptr(), _ptr(ps), _ptr(pe),
-        B, T, C, K, delta, _stream(dev), ws.data_ptr(), n, _ptr(grad_log_z),
-        grad_em.data_ptr(), grad_trans.data_ptr(), grad_dur.data_ptr(), _ptr(mu),
-        lz.data_ptr(), _ptr(gps), _ptr(gpe), _ptr(bnd))
+    nm = torch.empty((B, T), dtype=torch.float32, device=dev) if want_node_mass else None
+    sb, sr = _seams(B, dev, want_seams)
+    opt = _options(proj_start=_ptr(ps), proj_end=_ptr(pe), grad_proj_start=_ptr(gps),
+                   grad_proj_end=_ptr(gpe), boundary=_ptr(bnd), node_mass=_ptr(nm),
+                   seam_bound=_ptr(sb), seam_repairs=_ptr(sr),
+                   seam_tolerance=float(seam_tolerance) or None)
+    rc = _native.load().semicrf_backward_ex(
+        em.data_ptr(), lengths.data_ptr(), trans.data_ptr(), dur.data_ptr(), B, T, C, K, delta,
+        _stream(dev), ws.data_ptr(), n, _ptr(grad_log_z), grad_em.data_ptr(),
+        grad_trans.data_ptr(), grad_dur.data_ptr(), _ptr(mu), lz.data_ptr(), opt)
     _native.check("semicrf_backward", rc)
     _maybe_check(ws, check_status, "semicrf_backward")
     out = {"grad_em": grad_em, "grad_trans": grad_trans, "grad_dur": grad_dur,
            "marginals": mu, "log_z": lz}
     if want_b:
         out.update(grad_proj_start=gps, grad_proj_end=gpe, boundary=bnd)
+    if want_node_mass:
+        out["node_mass"] = nm
+    if want_seams:
+        out.update(seam_bound=sb, seam_repairs=sr)
     return out
 
 
@@ -198,11 +227,13 @@ def nll(em, lengths, trans, dur, gold_labels, gold_seg_start, *, proj_start=None
     grad_dur = torch.empty_like(dur)
     gps = torch.empty_like(em) if want_p else None
     gpe = torch.empty_like(em) if want_p else None
+    opt = _options(proj_start=_ptr(ps), proj_end=_ptr(pe), grad_proj_start=_ptr(gps),
+                   grad_proj_end=_ptr(gpe))
     rc = _native.load().semicrf_nll(
-        em.data_ptr(), lengths.data_ptr(), trans.data_ptr(), dur.data_ptr(), _ptr(ps), _ptr(pe),
+        em.data_ptr(), lengths.data_ptr(), trans.data_ptr(), dur.data_ptr(),
         gold_labels.data_ptr(), gold_seg_start.data_ptr(), B, T, C, K, delta, _stream(dev),
         ws.data_ptr(), n, _ptr(grad_nll), out.data_ptr(), grad_em.data_ptr(),
-        grad_trans.data_ptr(), grad_dur.data_ptr(), _ptr(gps), _ptr(gpe))
+        grad_trans.data_ptr(), grad_dur.data_ptr(), opt)
     _native.check("semicrf_nll", rc)
     _maybe_check(ws, check_status, "semicrf_nll")
     res = {"nll": out, "grad_em": grad_em, "grad_trans": grad_trans, "grad_dur": grad_dur}
@@ -212,8 +243,9 @@ def nll(em, lengths, trans, dur, gold_labels, gold_seg_start, *, proj_start=None
 
 
 def viterbi(em, lengths, trans, dur, *, proj_start=None, proj_end=None, workspace=None,
-            check_status=False):
-    """Returns (best_score [B] float32, labels [B,T] int32, seg_start [B,T] uint8)."""
+            seam_tolerance=0.0, want_seams=False, check_status=False):
+    """Returns (best_score [B] float32, labels [B,T] int32, seg_start [B,T] uint8), and with
+    want_seams also seam_bound [B] and seam_repairs [B] (semicrf_options)."""
     B, T, C, K = _check_inputs(em, lengths, trans, dur)
     dev = em.device
     ps, pe = _proj(em, proj_start, proj_end)
@@ -221,12 +253,17 @@ def viterbi(em, lengths, trans, dur, *, proj_start=None, proj_end=None, workspac
     score = torch.empty(B, dtype=torch.float32, device=dev)
     labels = torch.empty((B, T), dtype=torch.int32, device=dev)
     seg = torch.empty((B, T), dtype=torch.uint8, device=dev)
-    rc = _native.load().semicrf_viterbi(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
-                                        dur.data_ptr(), _ptr(ps), _ptr(pe), B, T, C, K,
-                                        _stream(dev), ws.data_ptr(), n, score.data_ptr(),
-                                        labels.data_ptr(), seg.data_ptr())
+    sb, sr = _seams(B, dev, want_seams)
+    opt = _options(proj_start=_ptr(ps), proj_end=_ptr(pe), seam_bound=_ptr(sb),
+                   seam_repairs=_ptr(sr), seam_tolerance=float(seam_tolerance) or None)
+    rc = _native.load().semicrf_viterbi_ex(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
+                                           dur.data_ptr(), B, T, C, K, _stream(dev),
+                                           ws.data_ptr(), n, score.data_ptr(), labels.data_ptr(),
+                                           seg.data_ptr(), opt)
     _native.check("semicrf_viterbi", rc)
     _maybe_check(ws, check_status, "semicrf_viterbi")
+    if want_seams:
+        return score, labels, seg, sb, sr
     return score, labels, seg
 
 
@@ -235,7 +272,8 @@ class _LogPartition(torch.autograd.Function):
     def forward(ctx, em, lengths, trans, dur, proj_start, proj_end, delta):
         ctx.save_for_backward(em, lengths, trans, dur, proj_start, proj_end)
         ctx.delta = delta
-        return logz(em, lengths, trans, dur, proj_start=proj_start, proj_end=proj_end)
+        return logz(em, lengths, trans, dur, proj_start=proj_start, proj_end=proj_end,
+                    delta=delta)
 
     @staticmethod
     def backward(ctx, g):

@@ -35,7 +35,7 @@ FLAGS = [
 
 SOURCES = ["api.cpp", "sweep_cfg.cpp", "scan.hip", "sweep_lse_mirror.hip", "sweep_lse_plain.hip",
            "sweep_lse_log.hip", "sweep_maxplus_mirror.hip", "sweep_maxplus_plain.hip",
-           "sweep_round_proj.hip", "marginals.hip", "gold.hip", "viterbi.hip"]
+           "sweep_round_proj.hip", "sweep_round_proj_log.hip", "marginals.hip", "gold.hip", "viterbi.hip", "seam.hip"]
 
 
 def _compile(src: str) -> str:

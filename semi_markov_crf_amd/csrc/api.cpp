@@ -16,13 +16,14 @@ constexpr size_t ALIGN = 256;
 constexpr int MAX_T = 1 << 29;   // keeps position arithmetic (t + delta) inside int
 
 struct Layout {
-    int nts = 0, ntm = 0, tm = 0, delta = 0, nspans = 0;
+    int nts = 0, ntm = 0, tm = 0, delta = 0, nspans = 0, ndir = 0;
     size_t status = 0, Leff = 0, tsum = 0, toff = 0, ttot = 0, S = 0;
     size_t logz = 0, logzb = 0;
+    size_t head = 0, tail = 0, lzloc = 0, soff = 0, fbad = 0, diag = 0;
     size_t ckR = 0, ckB = 0, ckM = 0, ckH = 0, XF = 0, AF = 0, XB = 0, AB = 0;
     size_t Dn = 0, dnt = 0, dno = 0, mu = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0, rps = 0;
     size_t gcnt = 0, gpart = 0, pst = 0, pen = 0;
-    size_t bp = 0, vscore = 0, vcstar = 0, vwin = 0, split = 0, btr = 0, bent = 0;
+    size_t bp = 0, vscore = 0, vcstar = 0, vwin = 0, vfin = 0, split = 0, btr = 0, bent = 0;
     size_t total = 0;
 };
 
@@ -66,21 +67,31 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
     lo.toff = m.take(sizeof(double) * B * lo.nts * C);
     lo.ttot = m.take(sizeof(double) * B * C);
     lo.S = m.take(sizeof(double) * BT1C);
-    if (op == SEMICRF_OP_LOGZ) {
-        lo.logz = m.take(sizeof(double) * B);
-    } else if (op == SEMICRF_OP_BACKWARD) {
-        lo.delta = resolve_delta(T, K, delta);
+    if (op == SEMICRF_OP_LOGZ || op == SEMICRF_OP_BACKWARD || op == SEMICRF_OP_VITERBI) {
+        // checkpoint spans: checkpoints, seam windows and frame offsets per direction (the
+        // decode runs forward only, with the default interval)
+        lo.delta = resolve_delta(T, K, op == SEMICRF_OP_VITERBI ? 0 : delta);
         if (lo.delta < 1) return false;
         lo.nspans = (T + lo.delta - 1) / lo.delta;
-        lo.tm = marg_tile(C, K);
-        lo.ntm = (T + 1 + lo.tm - 1) / lo.tm;
-        const size_t nck = (size_t)2 * B * lo.nspans;
+        lo.ndir = op == SEMICRF_OP_BACKWARD ? 2 : 1;
+        const size_t nck = (size_t)lo.ndir * B * lo.nspans;
         lo.logz = m.take(sizeof(double) * B);
         lo.logzb = m.take(sizeof(double) * B);
         lo.ckR = m.take(sizeof(float) * nck * K * C);
         lo.ckB = m.take(sizeof(double) * nck * C);
         lo.ckM = m.take(sizeof(float) * nck * C);
         lo.ckH = m.take(sizeof(double) * nck);
+        lo.head = m.take(sizeof(double) * nck * K * C);
+        lo.tail = m.take(sizeof(double) * nck * K * C);
+        lo.lzloc = m.take(sizeof(double) * lo.ndir * B);
+        lo.soff = m.take(sizeof(double) * nck);
+        lo.fbad = m.take(sizeof(int) * lo.ndir * B);
+        lo.diag = m.take(sizeof(double) * lo.ndir * B * 4);
+    }
+    if (op == SEMICRF_OP_LOGZ) {
+    } else if (op == SEMICRF_OP_BACKWARD) {
+        lo.tm = marg_tile(C, K);
+        lo.ntm = (T + 1 + lo.tm - 1) / lo.tm;
         lo.XF = m.take(sizeof(double) * BT1C);
         lo.AF = m.take(sizeof(double) * BT1C);
         lo.XB = m.take(sizeof(double) * BT1C);
@@ -110,6 +121,7 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         lo.vscore = m.take(sizeof(double) * B);
         lo.vcstar = m.take(sizeof(int) * B);
         lo.vwin = m.take(sizeof(double) * 2 * B * K * C);
+        lo.vfin = m.take(sizeof(double) * B * C);
         lo.split = m.take(sizeof(int) * 4 * B);
         const size_t nch = (size_t)backtrace_chunks(T, C, K);
         lo.btr = m.take(sizeof(int32_t) * 2 * B * nch * K * C);
@@ -165,6 +177,14 @@ struct BoundaryRes {
     float* grad_start;
     float* grad_end;
     float* prob;
+    float* node_mass;
+};
+
+// speculative spans: tolerance of the seam check and its optional reports
+struct SpecOpt {
+    double tol;
+    float* bound;
+    int* repairs;
 };
 
 SweepLaunch base_args(const float* trans, const float* dur, const Proj& pj, int B, int T, int C,
@@ -179,7 +199,53 @@ SweepLaunch base_args(const float* trans, const float* dur, const Proj& pj, int 
     a.B = B; a.T = T; a.C = C; a.K = K;
     a.delta = T;
     a.nspans = 1;
+    if (lo.ndir > 0) {
+        a.delta = lo.delta;
+        a.nspans = lo.nspans;
+        a.warm = spec_warm(K);
+        a.logz = at<double>(ws, lo.logz);
+        a.logz_b = at<double>(ws, lo.logzb);
+        a.ck_ring = at<float>(ws, lo.ckR);
+        a.ck_base = at<double>(ws, lo.ckB);
+        a.ck_mprev = at<float>(ws, lo.ckM);
+        a.ck_href = at<double>(ws, lo.ckH);
+        a.head = at<double>(ws, lo.head);
+        a.tail = at<double>(ws, lo.tail);
+        a.lzloc = at<double>(ws, lo.lzloc);
+        a.first_bad = at<int>(ws, lo.fbad);
+        a.off = at<double>(ws, lo.soff);
+    }
     return a;
+}
+
+// Every checkpoint span swept at once (MODE_SPEC), the seam check, and the sequential
+// repair from the first failed seam (MODE_REPAIR; its workgroups exit at once where no seam
+// failed).  Leaves log Z in a.logz (and a.logz_b with two directions) and, with write_xa,
+// the per-position outputs in their spans' frames with the offsets in a.off.
+int run_spans(const SweepCfg& cfg, SweepLaunch a, int ndir, const Layout& lo, void* ws,
+              const SpecOpt& so, hipStream_t stream, hipEvent_t* events, int stage) {
+    a.mode = MODE_SPEC;
+    a.write_ckpt = 0;
+    LAUNCH(launch_lse(cfg, a, ndir, stream));
+    if (events && stage >= 0 && hipEventRecord(events[stage], stream) != hipSuccess)
+        return SEMICRF_ERR_DEVICE;
+    SeamArgs sa{};
+    sa.head = a.head;
+    sa.tail = a.tail;
+    sa.lzloc = a.lzloc;
+    sa.Leff = a.Leff;
+    sa.B = a.B; sa.C = a.C; sa.K = a.K; sa.delta = a.delta; sa.nspans = a.nspans;
+    sa.tol = so.tol;
+    sa.off = at<double>(ws, lo.soff);
+    sa.first_bad = at<int>(ws, lo.fbad);
+    sa.logz = a.logz;
+    sa.logz_b = a.logz_b;
+    sa.diag = at<double>(ws, lo.diag);
+    LAUNCH(launch_seam(sa, ndir, stream));
+    a.mode = MODE_REPAIR;
+    LAUNCH(launch_lse(cfg, a, ndir, stream));
+    LAUNCH(launch_seam_report(sa.diag, a.B, ndir, so.bound, so.repairs, stream));
+    return SEMICRF_OK;
 }
 
 }  // namespace
@@ -193,6 +259,7 @@ const char* semicrf_status_string(int status) {
         case SEMICRF_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
         case SEMICRF_ERR_UNSUPPORTED: return "unsupported shape";
         case SEMICRF_ERR_DEVICE: return "device error";
+        case SEMICRF_ERR_UNIMPLEMENTED: return "not implemented";
         default: return "unknown status";
     }
 }
@@ -216,7 +283,7 @@ int semicrf_prefix(const float* em, const int32_t* lengths, int B, int T, int C,
     return SEMICRF_OK;
 }
 
-size_t semicrf_workspace_bytes(int op, int B, int T, int C, int K, int delta) {
+size_t semicrf_workspace_bytes(semicrf_op op, int B, int T, int C, int K, int delta) {
     Layout lo;
     if (!make_layout(op, B, T, C, K, delta, lo)) return 0;
     return lo.total;
@@ -231,22 +298,31 @@ static int common_checks(const float* em, const int32_t* lengths, const float* t
 }
 
 static int run_logz(const float* em, const int32_t* lengths, const float* trans, const float* dur,
-                    const Proj& pj, int B, int T, int C, int K, hipStream_t stream,
-                    void* workspace, size_t workspace_bytes, float* log_z, hipEvent_t* events) {
+                    const Proj& pj, int B, int T, int C, int K, int delta, hipStream_t stream,
+                    void* workspace, size_t workspace_bytes, float* log_z, const SpecOpt& so,
+                    hipEvent_t* events) {
     int rc = common_checks(em, lengths, trans, dur, B, T, C, K);
     if (rc) return rc;
-    if (!log_z) return SEMICRF_ERR_INVALID;
+    if (!log_z || delta < 0) return SEMICRF_ERR_INVALID;
     Layout lo;
-    if (!make_layout(SEMICRF_OP_LOGZ, B, T, C, K, 0, lo)) return SEMICRF_ERR_UNSUPPORTED;
+    if (!make_layout(SEMICRF_OP_LOGZ, B, T, C, K, delta, lo)) return SEMICRF_ERR_UNSUPPORTED;
     if ((rc = check_ws(workspace, workspace_bytes, lo))) return rc;
     STAGE(0);
     if ((rc = run_prefix(em, lengths, B, T, C, workspace, lo, stream))) return rc;
     STAGE(1);
     const SweepCfg cfg = choose_sweep(C, K);
     SweepLaunch a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
-    a.mode = MODE_FULL;
-    a.logz = at<double>(workspace, lo.logz);
-    LAUNCH(launch_lse(cfg, a, 1, stream));
+    if (cfg.split) {
+        // every checkpoint span at once, then the seam check
+        a.write_xa = 0;
+        if ((rc = run_spans(cfg, a, 1, lo, workspace, so, stream, nullptr, -1))) return rc;
+    } else {
+        a.mode = MODE_FULL;
+        a.delta = T;
+        a.nspans = 1;
+        LAUNCH(launch_lse(cfg, a, 1, stream));
+        LAUNCH(launch_seam_report(nullptr, B, 0, so.bound, so.repairs, stream));
+    }
     LAUNCH(launch_write_logz(a.logz, B, log_z, stream));
     STAGE(2);
     return SEMICRF_OK;
@@ -257,7 +333,7 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
                         hipStream_t stream, void* workspace, size_t workspace_bytes,
                         const float* grad_log_z, float* grad_em, float* grad_trans,
                         float* grad_dur, float* marginals, float* log_z, const BoundaryRes& br,
-                        hipEvent_t* events) {
+                        const SpecOpt& so, hipEvent_t* events) {
     int rc = common_checks(em, lengths, trans, dur, B, T, C, K);
     if (rc) return rc;
     if (!grad_em || !grad_trans || !grad_dur || delta < 0) return SEMICRF_ERR_INVALID;
@@ -269,31 +345,31 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
     STAGE(1);
     const SweepCfg cfg = choose_sweep(C, K);
     SweepLaunch a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
-    a.delta = lo.delta;
-    a.nspans = lo.nspans;
-    a.ck_ring = at<float>(workspace, lo.ckR);
-    a.ck_base = at<double>(workspace, lo.ckB);
-    a.ck_mprev = at<float>(workspace, lo.ckM);
-    a.ck_href = at<double>(workspace, lo.ckH);
     a.XF = at<double>(workspace, lo.XF);
     a.AF = at<double>(workspace, lo.AF);
     a.XB = at<double>(workspace, lo.XB);
     a.AB = at<double>(workspace, lo.AB);
-    a.logz = at<double>(workspace, lo.logz);
-    a.logz_b = at<double>(workspace, lo.logzb);
-    if (lo.nspans > 1) {
-        // streaming sweeps in both directions at once: checkpoints every delta positions
-        a.mode = MODE_FULL;
-        a.write_ckpt = 1;
-        a.write_xa = 0;
-        LAUNCH(launch_lse(cfg, a, 2, stream));
-    }
-    STAGE(2);
-    // recompute every checkpoint span in parallel, writing the per-position values
-    a.mode = MODE_SPAN;
-    a.write_ckpt = 0;
     a.write_xa = 1;
-    LAUNCH(launch_lse(cfg, a, 2, stream));
+    if (cfg.split) {
+        // every checkpoint span of both directions at once with its per-position values,
+        // then the seam check and the repair of failed seams
+        if ((rc = run_spans(cfg, a, 2, lo, workspace, so, stream, events, 2))) return rc;
+    } else {
+        if (lo.nspans > 1) {
+            // streaming sweeps in both directions at once: checkpoints every delta positions
+            a.mode = MODE_FULL;
+            a.write_ckpt = 1;
+            a.write_xa = 0;
+            LAUNCH(launch_lse(cfg, a, 2, stream));
+        }
+        STAGE(2);
+        // recompute every checkpoint span in parallel, writing the per-position values
+        a.mode = MODE_SPAN;
+        a.write_ckpt = 0;
+        a.write_xa = 1;
+        LAUNCH(launch_lse(cfg, a, 2, stream));
+        LAUNCH(launch_seam_report(nullptr, B, 0, so.bound, so.repairs, stream));
+    }
     STAGE(3);
 
     MargArgs m{};
@@ -301,6 +377,9 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
     m.B = B; m.T = T; m.C = C; m.K = K;
     m.tile = lo.tm; m.ntiles = lo.ntm; m.kchunk = marg_kchunk(C, K);
     m.XF = a.XF; m.AF = a.AF; m.XB = a.XB; m.AB = a.AB; m.logz = a.logz;
+    m.off = cfg.split ? a.off : nullptr;
+    m.delta = lo.delta;
+    m.nspans = lo.nspans;
     m.Dn = at<double>(workspace, lo.Dn);
     m.dn_tile = at<double>(workspace, lo.dnt);
     m.part_dur = at<double>(workspace, lo.pd);
@@ -324,6 +403,7 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
         bo.grad_proj_end = br.grad_end;
         bo.boundary = br.prob;
     }
+    bo.node_mass = br.node_mass;
     LAUNCH(launch_node_marginals(m.Dn, at<double>(workspace, lo.dno), a.Leff, B, T, C, lo.tm,
                                  lo.ntm, mu, at<double>(workspace, lo.mut),
                                  at<double>(workspace, lo.zt), bo, stream));
@@ -343,7 +423,7 @@ static int run_viterbi(const float* em, const int32_t* lengths, const float* tra
                        const float* dur, const Proj& pj, int B, int T, int C, int K,
                        hipStream_t stream, void* workspace, size_t workspace_bytes,
                        float* best_score, int32_t* labels, uint8_t* seg_start,
-                       hipEvent_t* events) {
+                       const SpecOpt& so, hipEvent_t* events) {
     int rc = common_checks(em, lengths, trans, dur, B, T, C, K);
     if (rc) return rc;
     if (!best_score || !labels || !seg_start) return SEMICRF_ERR_INVALID;
@@ -355,15 +435,42 @@ static int run_viterbi(const float* em, const int32_t* lengths, const float* tra
     STAGE(1);
     const SweepCfg cfg = choose_sweep(C, K);
     SweepLaunch a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
-    a.mode = MODE_FULL;
     a.bp = at<uint32_t>(workspace, lo.bp);
     a.vscore = at<double>(workspace, lo.vscore);
     a.vcstar = at<int>(workspace, lo.vcstar);
     a.vwin = at<double>(workspace, lo.vwin);
-    LAUNCH(launch_maxplus(cfg, a, stream));
+    a.vfin = at<double>(workspace, lo.vfin);
+    if (cfg.split) {
+        // every checkpoint span of the forward decode at once, the seam check (the frame
+        // offsets, no log Z), the in-order repair from a failed seam, the final label
+        a.mode = MODE_SPEC;
+        LAUNCH(launch_maxplus(cfg, a, stream));
+        SeamArgs sa{};
+        sa.head = a.head;
+        sa.tail = a.tail;
+        sa.lzloc = a.lzloc;
+        sa.Leff = a.Leff;
+        sa.B = B; sa.C = C; sa.K = K; sa.delta = a.delta; sa.nspans = a.nspans;
+        sa.tol = so.tol;
+        sa.off = at<double>(workspace, lo.soff);
+        sa.first_bad = at<int>(workspace, lo.fbad);
+        sa.logz = a.logz;
+        sa.logz_b = a.logz_b;
+        sa.diag = at<double>(workspace, lo.diag);
+        LAUNCH(launch_seam(sa, 1, stream));
+        a.mode = MODE_REPAIR;
+        LAUNCH(launch_maxplus(cfg, a, stream));
+        LAUNCH(launch_vit_final(a.vfin, sa.off, a.Leff, B, C, a.delta, a.nspans, a.vscore,
+                                a.vcstar, stream));
+        LAUNCH(launch_seam_report(sa.diag, B, 1, so.bound, so.repairs, stream));
+    } else {
+        a.mode = MODE_FULL;
+        LAUNCH(launch_maxplus(cfg, a, stream));
+        LAUNCH(launch_seam_report(nullptr, B, 0, so.bound, so.repairs, stream));
+    }
     STAGE(2);
     int* split = at<int>(workspace, lo.split);
-    LAUNCH(launch_vit_combine(a.vwin, trans, a.Leff, B, C, K, cfg.split, a.vscore, a.vcstar,
+    LAUNCH(launch_vit_combine(a.vwin, trans, a.Leff, B, C, K, false, a.vscore, a.vcstar,
                               split, best_score, stream));
     LAUNCH(launch_backtrace(a.bp, split, B, T, C, K, at<int32_t>(workspace, lo.btr),
                             at<int32_t>(workspace, lo.bent), labels, seg_start, stream));
@@ -371,59 +478,72 @@ static int run_viterbi(const float* em, const int32_t* lengths, const float* tra
     return SEMICRF_OK;
 }
 
-int semicrf_logz(const float* em, const int32_t* lengths, const float* trans, const float* dur,
-                 const float* proj_start, const float* proj_end, int B, int T, int C, int K,
-                 hipStream_t stream, void* workspace, size_t workspace_bytes, float* log_z) {
-    return run_logz(em, lengths, trans, dur, Proj{proj_start, proj_end}, B, T, C, K, stream,
-                    workspace, workspace_bytes, log_z, nullptr);
+namespace {
+
+const semicrf_options kNoOptions{};
+
+const semicrf_options& opts(const semicrf_options* o) { return o ? *o : kNoOptions; }
+
+SpecOpt spec_opt(const semicrf_options& o) {
+    return SpecOpt{o.seam_tolerance == 0.0 ? SEAM_TOL : o.seam_tolerance, o.seam_bound,
+                   o.seam_repairs};
 }
 
-int semicrf_logz_staged(const float* em, const int32_t* lengths, const float* trans,
-                        const float* dur, const float* proj_start, const float* proj_end, int B,
-                        int T, int C, int K, hipStream_t stream, void* workspace,
-                        size_t workspace_bytes, float* log_z, hipEvent_t* events) {
-    if (!events) return SEMICRF_ERR_INVALID;
-    return run_logz(em, lengths, trans, dur, Proj{proj_start, proj_end}, B, T, C, K, stream,
-                    workspace, workspace_bytes, log_z, events);
+}  // namespace
+
+int semicrf_logz(const float* em, const int32_t* lengths, const float* trans, const float* dur,
+                 int B, int T, int C, int K, int delta, hipStream_t stream, void* workspace,
+                 size_t workspace_bytes, float* log_z) {
+    return semicrf_logz_ex(em, lengths, trans, dur, B, T, C, K, delta, stream, workspace,
+                           workspace_bytes, log_z, nullptr);
+}
+
+int semicrf_logz_ex(const float* em, const int32_t* lengths, const float* trans,
+                    const float* dur, int B, int T, int C, int K, int delta, hipStream_t stream,
+                    void* workspace, size_t workspace_bytes, float* log_z,
+                    const semicrf_options* options) {
+    const semicrf_options& o = opts(options);
+    if (delta < 0) return SEMICRF_ERR_INVALID;
+    return run_logz(em, lengths, trans, dur, Proj{o.proj_start, o.proj_end}, B, T, C, K, delta,
+                    stream, workspace, workspace_bytes, log_z, spec_opt(o), o.events);
 }
 
 int semicrf_backward(const float* em, const int32_t* lengths, const float* trans, const float* dur,
-                     const float* proj_start, const float* proj_end, int B, int T, int C, int K,
-                     int delta, hipStream_t stream, void* workspace, size_t workspace_bytes,
-                     const float* grad_log_z, float* grad_em, float* grad_trans, float* grad_dur,
-                     float* marginals, float* log_z, float* grad_proj_start,
-                     float* grad_proj_end, float* boundary) {
-    return run_backward(em, lengths, trans, dur, Proj{proj_start, proj_end}, B, T, C, K, delta,
-                        stream, workspace, workspace_bytes, grad_log_z, grad_em, grad_trans,
-                        grad_dur, marginals, log_z,
-                        BoundaryRes{grad_proj_start, grad_proj_end, boundary}, nullptr);
+                     int B, int T, int C, int K, int delta, hipStream_t stream, void* workspace,
+                     size_t workspace_bytes, const float* grad_log_z, float* grad_em,
+                     float* grad_trans, float* grad_dur, float* marginals, float* log_z) {
+    return semicrf_backward_ex(em, lengths, trans, dur, B, T, C, K, delta, stream, workspace,
+                               workspace_bytes, grad_log_z, grad_em, grad_trans, grad_dur,
+                               marginals, log_z, nullptr);
 }
 
-int semicrf_backward_staged(const float* em, const int32_t* lengths, const float* trans,
-                            const float* dur, const float* proj_start, const float* proj_end,
-                            int B, int T, int C, int K, int delta, hipStream_t stream,
-                            void* workspace, size_t workspace_bytes, const float* grad_log_z,
-                            float* grad_em, float* grad_trans, float* grad_dur, float* marginals,
-                            float* log_z, float* grad_proj_start, float* grad_proj_end,
-                            float* boundary, hipEvent_t* events) {
-    if (!events) return SEMICRF_ERR_INVALID;
-    return run_backward(em, lengths, trans, dur, Proj{proj_start, proj_end}, B, T, C, K, delta,
-                        stream, workspace, workspace_bytes, grad_log_z, grad_em, grad_trans,
-                        grad_dur, marginals, log_z,
-                        BoundaryRes{grad_proj_start, grad_proj_end, boundary}, events);
+int semicrf_backward_ex(const float* em, const int32_t* lengths, const float* trans,
+                        const float* dur, int B, int T, int C, int K, int delta,
+                        hipStream_t stream, void* workspace, size_t workspace_bytes,
+                        const float* grad_log_z, float* grad_em, float* grad_trans,
+                        float* grad_dur, float* marginals, float* log_z,
+                        const semicrf_options* options) {
+    const semicrf_options& o = opts(options);
+    return run_backward(em, lengths, trans, dur, Proj{o.proj_start, o.proj_end}, B, T, C, K,
+                        delta, stream, workspace, workspace_bytes, grad_log_z, grad_em,
+                        grad_trans, grad_dur, marginals, log_z,
+                        BoundaryRes{o.grad_proj_start, o.grad_proj_end, o.boundary, o.node_mass},
+                        spec_opt(o), o.events);
 }
 
 int semicrf_nll(const float* em, const int32_t* lengths, const float* trans, const float* dur,
-                const float* proj_start, const float* proj_end, const int32_t* gold_labels,
-                const uint8_t* gold_seg_start, int B, int T, int C, int K, int delta,
-                hipStream_t stream, void* workspace, size_t workspace_bytes,
+                const int32_t* gold_labels, const uint8_t* gold_seg_start, int B, int T, int C,
+                int K, int delta, hipStream_t stream, void* workspace, size_t workspace_bytes,
                 const float* grad_nll, float* nll, float* grad_em, float* grad_trans,
-                float* grad_dur, float* grad_proj_start, float* grad_proj_end) {
+                float* grad_dur, const semicrf_options* options) {
+    const semicrf_options& o = opts(options);
     if (!gold_labels || !gold_seg_start || !nll) return SEMICRF_ERR_INVALID;
-    const Proj pj{proj_start, proj_end};
+    if (o.boundary || o.node_mass || o.events) return SEMICRF_ERR_INVALID;
+    const Proj pj{o.proj_start, o.proj_end};
     int rc = run_backward(em, lengths, trans, dur, pj, B, T, C, K, delta, stream, workspace,
                           workspace_bytes, grad_nll, grad_em, grad_trans, grad_dur, nullptr,
-                          nullptr, BoundaryRes{grad_proj_start, grad_proj_end, nullptr}, nullptr);
+                          nullptr, BoundaryRes{o.grad_proj_start, o.grad_proj_end, nullptr, nullptr},
+                          spec_opt(o), nullptr);
     if (rc) return rc;
     Layout lo;
     if (!make_layout(SEMICRF_OP_BACKWARD, B, T, C, K, delta, lo)) return SEMICRF_ERR_UNSUPPORTED;
@@ -432,8 +552,8 @@ int semicrf_nll(const float* em, const int32_t* lengths, const float* trans, con
     g.Leff = at<int>(workspace, lo.Leff);
     g.trans = trans;
     g.dur = dur;
-    g.proj_start = proj_start;
-    g.proj_end = proj_end;
+    g.proj_start = o.proj_start;
+    g.proj_end = o.proj_end;
     g.labels = gold_labels;
     g.seg_start = gold_seg_start;
     g.B = B; g.T = T; g.C = C; g.K = K;
@@ -446,28 +566,30 @@ int semicrf_nll(const float* em, const int32_t* lengths, const float* trans, con
     g.grad_em = grad_em;
     g.grad_trans = grad_trans;
     g.grad_dur = grad_dur;
-    g.grad_proj_start = grad_proj_start;
-    g.grad_proj_end = grad_proj_end;
+    g.grad_proj_start = o.grad_proj_start;
+    g.grad_proj_end = o.grad_proj_end;
     LAUNCH(launch_gold(g, stream));
     return SEMICRF_OK;
 }
 
 int semicrf_viterbi(const float* em, const int32_t* lengths, const float* trans, const float* dur,
-                    const float* proj_start, const float* proj_end, int B, int T, int C, int K,
-                    hipStream_t stream, void* workspace, size_t workspace_bytes,
-                    float* best_score, int32_t* labels, uint8_t* seg_start) {
-    return run_viterbi(em, lengths, trans, dur, Proj{proj_start, proj_end}, B, T, C, K, stream,
-                       workspace, workspace_bytes, best_score, labels, seg_start, nullptr);
+                    int B, int T, int C, int K, hipStream_t stream, void* workspace,
+                    size_t workspace_bytes, float* best_score, int32_t* labels,
+                    uint8_t* seg_start) {
+    return semicrf_viterbi_ex(em, lengths, trans, dur, B, T, C, K, stream, workspace,
+                              workspace_bytes, best_score, labels, seg_start, nullptr);
 }
 
-int semicrf_viterbi_staged(const float* em, const int32_t* lengths, const float* trans,
-                           const float* dur, const float* proj_start, const float* proj_end,
-                           int B, int T, int C, int K, hipStream_t stream, void* workspace,
-                           size_t workspace_bytes, float* best_score, int32_t* labels,
-                           uint8_t* seg_start, hipEvent_t* events) {
-    if (!events) return SEMICRF_ERR_INVALID;
-    return run_viterbi(em, lengths, trans, dur, Proj{proj_start, proj_end}, B, T, C, K, stream,
-                       workspace, workspace_bytes, best_score, labels, seg_start, events);
+int semicrf_viterbi_ex(const float* em, const int32_t* lengths, const float* trans,
+                       const float* dur, int B, int T, int C, int K, hipStream_t stream,
+                       void* workspace, size_t workspace_bytes, float* best_score,
+                       int32_t* labels, uint8_t* seg_start, const semicrf_options* options) {
+    const semicrf_options& o = opts(options);
+    if (o.grad_proj_start || o.grad_proj_end || o.boundary || o.node_mass)
+        return SEMICRF_ERR_INVALID;
+    return run_viterbi(em, lengths, trans, dur, Proj{o.proj_start, o.proj_end}, B, T, C, K,
+                       stream, workspace, workspace_bytes, best_score, labels, seg_start,
+                       spec_opt(o), o.events);
 }
 
 int semicrf_read_status(const void* workspace, hipStream_t stream) {

@@ -88,7 +88,18 @@ inline size_t maxplus_lds_bytes(int C, int UP, int P, int CH) {
     return (size_t)(4 * CH * C) * 8 + (size_t)((C + 1) * P + 2 * UP) * 4;
 }
 
-enum SweepMode { MODE_FULL = 0, MODE_SPAN = 1 };
+// MODE_FULL: one workgroup per (sequence, direction) from position 0 to L.
+// MODE_SPAN: one per (checkpoint span, sequence, direction), restored from the checkpoint
+//            at the span's start.
+// MODE_SPEC: one per (span, sequence, direction), all at once: a span other than the first
+//            starts `warm` positions early from a uniform ring (every entry equal) instead
+//            of a checkpoint; its values then equal the exact ones up to a constant, to
+//            within the rounding of the sweep, which the seam check verifies.  It writes its
+//            outputs in its own frame, the ring values of the K positions that end its
+//            burn-in (head) and its span (tail), and a checkpoint at its end.
+// MODE_REPAIR: one per (sequence, direction): where a seam check failed, the sequence is
+//            swept again from the checkpoint at the first failed seam to its end.
+enum SweepMode { MODE_FULL = 0, MODE_SPAN = 1, MODE_SPEC = 2, MODE_REPAIR = 3 };
 
 struct SweepArgs {
     const double* S;        // [B][T+1][C] centred prefix sums
@@ -113,11 +124,19 @@ struct SweepArgs {
     double* AB;             // backward: beta[u, c] + S[u, c] - S[L, c]
     double* logz;           // [B] forward log Z
     double* logz_b;         // [B] log Z from the backward sweep (consistency check)
+    // speculative spans (MODE_SPEC) and their repair (MODE_REPAIR)
+    int warm;               // burn-in positions before a span
+    double* head;           // [2 dirs][B][nspans][K][C] ring values (natural log, the
+    double* tail;           //   span's own frame) of positions t0-K+1 .. t0 / t1-K+1 .. t1
+    double* lzloc;          // [2 dirs][B] log Z of the last span, in its own frame
+    const int* first_bad;   // [2 dirs][B] first span whose seam failed (nspans: none)
+    const double* off;      // [2 dirs][B][nspans] frame offsets (natural log)
     // Viterbi
     uint32_t* bp;           // [2 dirs][B][T+1][C]: (k) | (previous label << 16)
     double* vscore;         // [B] (one-direction sweep)
     int* vcstar;            // [B] final label (one-direction sweep)
     double* vwin;           // [2 dirs][B][K][C] values over the meeting window (round kernel)
+    double* vfin;           // [B][C] values V(L, c) of the span that holds L, in its frame
 };
 
 // What the launchers receive: the kernels' arguments plus the boundary projections, which
@@ -146,6 +165,29 @@ hipError_t launch_maxplus(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t
 hipError_t launch_maxplus_mirror(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream);
 hipError_t launch_maxplus_plain(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream);
 
+// ------------------------------------------------------------------ seam check
+struct SeamArgs {
+    const double* head;     // [ndir][B][nspans][K][C] (see SweepArgs)
+    const double* tail;
+    const double* lzloc;    // [ndir][B]
+    const int* Leff;        // [B]
+    int B, C, K, delta, nspans;
+    double tol;             // accepted half-range of tail - head (natural log); < 0: none
+    double* off;            // [ndir][B][nspans] frame offsets (out)
+    int* first_bad;         // [ndir][B] first failed seam, nspans if none (out)
+    double* logz;           // [B] direction 0 (out, where no seam failed)
+    double* logz_b;         // [B] direction 1 (out, where no seam failed)
+    double* diag;           // [ndir][B][4]: sum and max of the accepted half-ranges, first
+                            //   failed seam (-1: none), number of seams (out)
+};
+hipError_t launch_seam(const SeamArgs& s, int ndir, hipStream_t stream);
+// bound [B] / repairs [B] (either may be NULL) from the seam check's diag
+hipError_t launch_seam_report(const double* diag, int B, int ndir, float* bound, int* repairs,
+                              hipStream_t stream);
+// burn-in length of a speculative span and the default seam tolerance (natural log)
+int spec_warm(int K);
+constexpr double SEAM_TOL = 1.0e-4;
+
 // ------------------------------------------------------------------ scans
 // Per-tile column sums of the valid emissions; also writes the clamped lengths Leff
 // (negated where the input length was outside [1, T]).
@@ -173,6 +215,11 @@ struct MargArgs {
     int ntiles;             // ceil((T+1) / tile)
     const double* XF; const double* AF; const double* XB; const double* AB;
     const double* logz;
+    // frame offsets of the speculative spans, [2 dirs][B][nspans] (NULL: none): added to
+    // XF / AF of forward span floor((s-1)/delta) / floor(s/delta) and to XB / AB of the
+    // mirrored span of L - s likewise
+    const double* off;
+    int delta, nspans;
     double* Dn;             // [B][T+1][C]: start mass - end mass of segments at each position
     double* dn_tile;        // [B][ntiles][C]: tile sums of Dn
     double* part_dur;       // [B][ntiles][K][C]
@@ -193,6 +240,7 @@ struct BoundaryOut {
     float* grad_proj_start;
     float* grad_proj_end;
     float* boundary;
+    float* node_mass;           // [B][T] or NULL: the per-position normaliser itself
 };
 hipError_t launch_node_marginals(const double* Dn, const double* dn_off, const int* Leff,
                                  int B, int T, int C, int tile, int ntiles, float* mu,
@@ -243,6 +291,11 @@ int backtrace_chunks(int T, int C, int K);
 // split[b] = {t*, c_left, c_right, L}: the best segmentation's boundary in the meeting
 // window of the two-direction sweep (bidir), or t* = L and the one-direction sweep's final
 // label; best_score[b] its score (NaN for an invalid length)
+// vscore[b] = max_c vfin[b][c] + off[b][last span], vcstar[b] the lowest maximising c (NaN
+// for an invalid length): the end of the one-direction decode over speculative spans
+hipError_t launch_vit_final(const double* vfin, const double* off, const int* Leff, int B,
+                            int C, int delta, int nspans, double* vscore, int* vcstar,
+                            hipStream_t stream);
 hipError_t launch_vit_combine(const double* vwin, const float* trans, const int* Leff, int B,
                               int C, int K, bool bidir, const double* vscore, const int* vcstar,
                               int* split, float* best_score, hipStream_t stream);

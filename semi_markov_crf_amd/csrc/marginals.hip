@@ -128,14 +128,24 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
     const double* AF = a.AF + (size_t)b * rowC;
     const double* XB = a.XB + (size_t)b * rowC;
     const double* AB = a.AB + (size_t)b * rowC;
+    // frame offsets of the spans that wrote each value (0 without speculative spans):
+    // forward X / A of position s from span floor((s-1)/delta) / floor(s/delta), backward
+    // ones of s from the mirrored position L - s
+    const double* offF = a.off ? a.off + (size_t)b * a.nspans : nullptr;
+    const double* offB = a.off ? a.off + ((size_t)a.B + b) * a.nspans : nullptr;
+    auto oAF = [&](int s) { return offF ? offF[s / a.delta] : 0.0; };
+    auto oXF = [&](int s) { return offF ? offF[(s - 1) / a.delta] : 0.0; };
+    auto oAB = [&](int u) { return offB ? offB[(L - u) / a.delta] : 0.0; };
+    auto oXB = [&](int s) { return offB ? offB[(L - s - 1) / a.delta] : 0.0; };
     // staged in base 2 (times log2 e); invalid starts / ends get DNEG so that their
     // exponentials vanish
     auto af = [&](int s, int c) -> double {
-        return (s >= 0 && s <= L - 1) ? (AF[(size_t)s * C + c] + Sb[(size_t)L * C + c] - logZ) * LOG2E
-                                      : DNEG;
+        return (s >= 0 && s <= L - 1)
+                   ? (AF[(size_t)s * C + c] + oAF(s) + Sb[(size_t)L * C + c] - logZ) * LOG2E
+                   : DNEG;
     };
     auto ab = [&](int u, int c) -> double {
-        return (u >= 1 && u <= L) ? AB[(size_t)u * C + c] * LOG2E : DNEG;
+        return (u >= 1 && u <= L) ? (AB[(size_t)u * C + c] + oAB(u)) * LOG2E : DNEG;
     };
 
     for (int q = tid; q < TM * C; q += 256) {
@@ -143,8 +153,9 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
         const int s = p0 + r;
         AFt[q] = af(s, c);
         ABt[q] = ab(s, c);
-        XFs[q] = (s >= 1 && s <= L - 1) ? XF[(size_t)s * C + c] * LOG2E : DNEG;
-        XBs[q] = (s >= 1 && s <= L - 1) ? (XB[(size_t)s * C + c] - logZ) * LOG2E : DNEG;
+        XFs[q] = (s >= 1 && s <= L - 1) ? (XF[(size_t)s * C + c] + oXF(s)) * LOG2E : DNEG;
+        XBs[q] = (s >= 1 && s <= L - 1) ? (XB[(size_t)s * C + c] + oXB(s) - logZ) * LOG2E
+                                        : DNEG;
         Dst[q] = 0.0;
         Den[q] = 0.0;
     }
@@ -279,6 +290,11 @@ __global__ __launch_bounds__(256) void k_node_marginals(const double* __restrict
         zrow[r] = z;
     }
     __syncthreads();
+    if (bo.node_mass)
+        for (int r = tid; r < TM; r += 256) {
+            const int t = p0 + r;
+            if (t < T) bo.node_mass[(size_t)b * T + t] = r < rows ? (float)zrow[r] : 0.0f;
+        }
     if (bo.pstart) {
         // boundary probabilities and the projections' gradients: the raw start / end
         // masses over the same per-position normaliser (0 at padding)

@@ -59,6 +59,10 @@ __device__ __forceinline__ bool in_lin_range(float s) {
     return __float_as_uint(s) - lo <= hi - lo;
 }
 __device__ __forceinline__ float exp2_or_zero(float x) { return x > NEG_HALF ? fast_exp2(x) : 0.0f; }
+// 2^-n for a whole number n (a rebase shift), exactly (0 below the fp32 range)
+__device__ __forceinline__ float pow2_neg(float n) {
+    return __builtin_amdgcn_ldexpf(1.0f, -(int)fminf(fmaxf(n, -1.0e9f), 1.0e9f));
+}
 // true in every lane when any lane of the wavefront has `bad` set (a scalar branch)
 __device__ __forceinline__ bool wave_any(bool bad) { return __builtin_amdgcn_ballot_w64(bad) != 0; }
 
@@ -170,7 +174,6 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
     const float D0 = exp2_or_zero(d0 - dmax), D1 = exp2_or_zero(d1 - dmax);
 
     float treg[CPL], wreg[CPL], zero[CPL];
-    float tmx = NEG;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int cp = jt + i * GT;
@@ -181,10 +184,16 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
         }
         treg[i] = v;
         zero[i] = 0.0f;
-        tmx = fmaxf(tmx, v);
     }
-    tmx = group_reduce<GT>(tmx, OpMax());
-    const float tmax = tmx > NEG_HALF ? tmx : 0.0f;      // linear transitions: 2^(trans - tmax)
+    // linear transitions 2^(trans - tmax) with one tmax over the whole matrix, so that both
+    // sweep directions multiply by bit-identical weights (block-wide max through the sink)
+    float tmx = NEG;
+    for (int q = tid; q < C * C; q += NT) tmx = fmaxf(tmx, fmaxf((float)((double)a.trans[q] * LOG2E), NEG));
+    dummy[tid] = tmx;
+    __syncthreads();
+    for (int q = 0; q < NT; ++q) tmx = fmaxf(tmx, dummy[q]);
+    __syncthreads();
+    const float tmax = tmx > NEG_HALF ? tmx : 0.0f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) wreg[i] = exp2_or_zero(treg[i] - tmax);
     __syncthreads();   // ring and messages cleared, SL visible
@@ -352,8 +361,9 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
             // ---- rebase: move this label's values to a new base (every REBASE positions)
             if ((t & (REBASE - 1)) == 0) {
                 const float ref = fmaxf(Mref, Rn1);
-                const float dl = ref > NEG_HALF ? ref : 0.0f;
-                const float sc = fast_exp2(-dl);
+                // a whole number of octaves: the linear values scale exactly
+                const float dl = ref > NEG_HALF ? floorf(ref) : 0.0f;
+                const float sc = pow2_neg(dl);
                 Bc += (double)dl;
                 BH += (double)dl;
                 Rn1 -= dl; Rn2 -= dl; Mref -= dl; Qga -= dl;

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     const bool qlane = QLANE && chain && tid == 15;
 
     int b, span, dir;
-    if (a.mode == MODE_FULL) {
+    if (a.mode == MODE_FULL || a.mode == MODE_REPAIR) {
         b = blockIdx.x; dir = blockIdx.y; span = 0;
     } else {
         span = blockIdx.x; b = blockIdx.y; dir = blockIdx.z;
@@ -135,14 +135,30 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     const int Lr = a.Leff[b];
     const bool bad = Lr < 0;
     const int L = bad ? -Lr : Lr;
-    int t0 = 0, t1 = L;
-    if (a.mode == MODE_SPAN) {
-        t0 = span * a.delta;
-        if (t0 >= L) return;
-        t1 = min(L, t0 + a.delta);
+    // [tout, t1]: the positions this workgroup writes; t0: where its sweep starts (a
+    // speculative span runs a burn-in from t0 = tout - warm, or exactly from 0)
+    int t0 = 0, t1 = L, tout = 0;
+    const bool spec = a.mode == MODE_SPEC;
+    if (a.mode == MODE_SPAN || spec) {
+        tout = span * a.delta;
+        if (tout >= L) return;
+        t1 = min(L, tout + a.delta);
+        t0 = spec ? max(0, tout - a.warm) : tout;
+    } else if (a.mode == MODE_REPAIR) {
+        span = a.first_bad[dir * a.B + b];
+        if (span >= a.nspans) return;
+        tout = span * a.delta;
+        if (tout >= L) return;
+        t0 = tout;
     }
     const int RMASK = RS - 1;
-    const bool ckpt = a.mode == MODE_FULL && a.write_ckpt;
+    // checkpoints: every delta positions (MODE_FULL), or at the end of a speculative span
+    const bool ckpt = (a.mode == MODE_FULL && a.write_ckpt) || (spec && t1 < L);
+    // ring values of the windows the seam check compares (MODE_SPEC): head [hlo, tout] of
+    // every span but the first, tail [tlo, t1] of every span but the last
+    const int hlo = (spec && span > 0) ? tout - K + 1 : INT_MAX;
+    const int tlo = (spec && t1 < L) ? t1 - K + 1 : INT_MAX;
+    const size_t winrow = (((size_t)dir * a.B + b) * a.nspans + span) * K;
     const int bmax = (K + M - 1) / M;             // oldest block a bulk sum reaches
     const int NR = bmax + 3;                      // live blocks behind a round (rescale)
 
@@ -231,7 +247,6 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
 #pragma unroll
     for (int k = 0; k < KD; ++k) dlog[k] = cact ? durv(cl, k + 1) : NEG;
     float treg[CP], wreg[CP], zero[CP];
-    float tmx = NEG;
 #pragma unroll
     for (int i = 0; i < CP; ++i) {
         float v = NEG;
@@ -243,9 +258,15 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
         }
         treg[i] = v;
         zero[i] = 0.0f;
-        tmx = fmaxf(tmx, v);
     }
-    const float tmax = tmx > NEG_HALF ? tmx : 0.0f;       // linear transitions: 2^(trans - tmax)
+    // linear transitions 2^(trans - tmax) with one tmax over the whole matrix: both sweep
+    // directions then multiply by bit-identical weights (a per-label tmax would round the
+    // weights of the two directions differently, a bias that builds up over the sequence);
+    // the q lane's unit weights keep tmax = 0
+    float tmx = qlane ? 0.0f : NEG;
+    if (cact)
+        for (int q = 0; q < C * C; ++q) tmx = fmaxf(tmx, fmaxf((float)((double)a.trans[q] * LOG2E), NEG));
+    const float tmax = tmx > NEG_HALF ? tmx : 0.0f;
 #pragma unroll
     for (int i = 0; i < CP; ++i) wreg[i] = exp2_or_zero(treg[i] - tmax);
     __syncthreads();   // ring cleared, SL and dmax visible
@@ -340,6 +361,24 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
         const float r0 = cact ? fmaxf(proj_s(0, cl), NEG) : 0.0f;
         Eh[M - 1] = exp2_or_zero(r0);
         fH[M - 1] = r0;
+    } else if (spec) {
+        // burn-in start: every ring entry of positions t0-K+1 .. t0 equal (0 in log2, 1
+        // linear), a positive state from which the sweep converges to the exact one up to
+        // a constant; bases and normaliser 0
+        if (bact)
+            for (int q = j; q < K && t0 - q >= 0; q += G) {
+                Rrow[slot_of(t0 - q)] = 0.0f;
+                if constexpr (LIN) Erow[slot_of(t0 - q)] = 1.0f;
+            }
+        if (chain) {
+#pragma unroll
+            for (int i = 0; i < M; ++i) {
+                const int q = M - 1 - i;                   // position t0 - q
+                const bool in = q < K && t0 - q >= 0;
+                fH[i] = in ? 0.0f : NEG;
+                Eh[i] = in ? 1.0f : 0.0f;
+            }
+        }
     } else {
         const size_t ck = ckrow + span;
         if (bact)
@@ -361,8 +400,17 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
             }
         }
     }
-    if (cact && a.write_xa)
-        Aout[(outrow + (dir == 0 ? t0 : L - t0)) * C + cl] = (Bc + (double)fH[M - 1]) * LN2;
+    if (cact) {
+        const double a0 = (Bc + (double)fH[M - 1]) * LN2;   // ring value of position t0
+        if (a.write_xa && t0 == tout) Aout[(outrow + (dir == 0 ? t0 : L - t0)) * C + cl] = a0;
+        if (t0 == 0) {
+            // window positions <= 0: position 0's value, nothing before it
+            for (int p = hlo; p <= min(0, tout); ++p)
+                a.head[(winrow + p - hlo) * C + cl] = p == 0 ? a0 : -1.0e300;
+            for (int p = tlo; p <= min(0, t1); ++p)
+                a.tail[(winrow + p - tlo) * C + cl] = p == 0 ? a0 : -1.0e300;
+        }
+    }
 
     // ---------------------------------------------------------------- S staging (bulk lanes)
     const int chunkN = CH * C;
@@ -436,7 +484,8 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     // bulk lanes at the start of round r (rs = its first position - 1): the log ring block
     // of round r-1 from the chain's staging, the chain's rebase of round r-1 applied to the
     // rings, the rings of the checkpoints the chain took in round r-1
-    int next_ckb = ckpt ? a.delta : INT_MAX;   // next checkpoint whose ring is to copy
+    const int ck_first = spec ? t1 : a.delta;    // first checkpoint position
+    int next_ckb = ckpt ? ck_first : INT_MAX;  // next checkpoint whose ring is to copy
     // Sprev: the staged S of round r-1's first position for this lane's label; Fprev: its
     // end-side projection plane (projections only)
     auto ring_round = [&](int r, int rs, const double* Sprev, const float* Fprev) {
@@ -444,17 +493,23 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
             const float* ns = nsh + (((r - 1) & 1) * (CP + 1) + cb) * 2 * M + j;
             const float rl = fast_log2(ns[0]) + ns[M];
             Rrow[round_slot(r - 1, RMASK) + j] = fmaxf(rl, NEG);
-            // per-position outputs of round r-1 (position p = rs - M + 1 + j), natural log
+            // per-position outputs of round r-1 (position p = rs - M + 1 + j), natural log:
+            // X on (tout, t1], A on [tout, t1); ring values of the seam windows
             const int p = rs - M + 1 + j;
             if (XA && p <= t1) {
                 const double Bp = bcsh[((r - 1) & 1) * CP + cb];
-                const float sg = sgsh[(((r - 1) & 1) * CP + cb) * M + j];
-                const float sgl = rpsh[(r - 1) & 1] ? sg : fast_log2(sg) + dmax_b;
-                double Sp = Sprev[j];
-                if constexpr (PROJ) Sp += (double)Fprev[j];
+                const double av = (Bp + (double)rl) * LN2;
                 const size_t o = (outrow + (dir == 0 ? p : L - p)) * C + cb;
-                Xout[o] = (Sp + Bp + (double)sgl) * LN2;
-                if (p < t1) Aout[o] = (Bp + (double)rl) * LN2;
+                if (a.write_xa && p > tout) {
+                    const float sg = sgsh[(((r - 1) & 1) * CP + cb) * M + j];
+                    const float sgl = rpsh[(r - 1) & 1] ? sg : fast_log2(sg) + dmax_b;
+                    double Sp = Sprev[j];
+                    if constexpr (PROJ) Sp += (double)Fprev[j];
+                    Xout[o] = (Sp + Bp + (double)sgl) * LN2;
+                }
+                if (a.write_xa && p >= tout && p < t1) Aout[o] = av;
+                if (p >= hlo && p <= tout) a.head[(winrow + p - hlo) * C + cb] = av;
+                if (p >= tlo) a.tail[(winrow + p - tlo) * C + cb] = av;
             }
         }
         // the chain rebased last round: move the blocks of rounds <= r-2 (reads first).
@@ -464,7 +519,7 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
         if (r >= 3 && (r & 1) == 1) {
             constexpr int BR = BPL + 1;               // covers NR = bmax + 3 <= BPL*G + G blocks
             const float dl = bact ? dlsh[cb] : 0.0f;
-            const float sc = fast_exp2(-dl);
+            const float sc = pow2_neg(dl);
             if constexpr (BR <= 3) {
                 float4 v[BR], e[BR];
 #pragma unroll
@@ -534,7 +589,7 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     // ---------------------------------------------------------------- main loop
     double BH = Bc - H;                                   // B_c - H
     double lz = 0.0;
-    int next_ck = ckpt ? a.delta : INT_MAX;
+    int next_ck = ckpt ? ck_first : INT_MAX;
     float pdl = 0.0f;          // chain: rebase of the last round, still to apply to the
     bool pend = false;         // bulk sums it reads this round
     const int nrounds = (t1 - t0 + M - 1) / M;
@@ -553,7 +608,7 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
             float QL[M] = {ql4.x, ql4.y, ql4.z, ql4.w};
             float QG[M] = {qg4.x, qg4.y, qg4.z, qg4.w};
             if (pend) {                                // summed before the ring was rebased
-                const float sc = fast_exp2(-pdl);
+                const float sc = pow2_neg(pdl);
 #pragma unroll
                 for (int m = 0; m < M; ++m) {
                     QL[m] *= sc;
@@ -565,8 +620,9 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
                 // ---- rebase: this label's values move to a new base
                 const float rn = fmaxf(fast_log2(sH[M - 1]) + fH[M - 1], NEG);
                 const float ref = fmaxf(Mref, rn);
-                const float dl = cact && ref > NEG_HALF ? ref : 0.0f;
-                const float sc = fast_exp2(-dl);
+                // a whole number of octaves: the linear values scale exactly
+                const float dl = cact && ref > NEG_HALF ? floorf(ref) : 0.0f;
+                const float sc = pow2_neg(dl);
                 Bc += (double)dl;
                 BH += (double)dl;
                 Mref -= dl;
@@ -851,7 +907,17 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     }
 
     // ---------------------------------------------------------------- end of sequence
-    if (t1 == L && tid == 0) (dir == 0 ? a.logz : a.logz_b)[b] = bad ? nan_d() : lz * LN2;
+    if (t1 == L && tid == 0) {
+        if (spec) {
+            a.lzloc[dir * a.B + b] = lz * LN2;           // the seam check adds the offsets
+        } else {
+            // a repaired sweep continues in the frame of the span before the failed seam
+            const double base = a.mode == MODE_REPAIR
+                                    ? a.off[((size_t)dir * a.B + b) * a.nspans + span - 1]
+                                    : 0.0;
+            (dir == 0 ? a.logz : a.logz_b)[b] = bad ? nan_d() : lz * LN2 + base;
+        }
+    }
 }
 
 // ------------------------------------------------------------------ launch
@@ -871,24 +937,15 @@ static hipError_t launch_lse_round_inst(const SweepLaunch& a, dim3 grid, const S
 
 #define LSE_ROUND_BPL_CASES(G, CP)                                                   \
     switch (cfg.BPL) {                                                               \
-        case 0: return a.write_xa ? launch_lse_round_inst<G, 0, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
-                             : launch_lse_round_inst<G, 0, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
-        case 1: return a.write_xa ? launch_lse_round_inst<G, 1, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
-                             : launch_lse_round_inst<G, 1, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
-        case 2: return a.write_xa ? launch_lse_round_inst<G, 2, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
-                             : launch_lse_round_inst<G, 2, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
-        case 3: return a.write_xa ? launch_lse_round_inst<G, 3, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
-                             : launch_lse_round_inst<G, 3, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
-        case 4: return a.write_xa ? launch_lse_round_inst<G, 4, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
-                             : launch_lse_round_inst<G, 4, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
-        case 5: return a.write_xa ? launch_lse_round_inst<G, 5, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
-                             : launch_lse_round_inst<G, 5, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
-        case 6: return a.write_xa ? launch_lse_round_inst<G, 6, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
-                             : launch_lse_round_inst<G, 6, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
-        case 7: return a.write_xa ? launch_lse_round_inst<G, 7, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
-                             : launch_lse_round_inst<G, 7, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
-        case 8: return a.write_xa ? launch_lse_round_inst<G, 8, CP, LIN, PROJ, true>(a, grid, cfg, stream) \
-                             : launch_lse_round_inst<G, 8, CP, LIN, PROJ, false>(a, grid, cfg, stream);      \
+        case 0: return launch_lse_round_inst<G, 0, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
+        case 1: return launch_lse_round_inst<G, 1, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
+        case 2: return launch_lse_round_inst<G, 2, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
+        case 3: return launch_lse_round_inst<G, 3, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
+        case 4: return launch_lse_round_inst<G, 4, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
+        case 5: return launch_lse_round_inst<G, 5, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
+        case 6: return launch_lse_round_inst<G, 6, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
+        case 7: return launch_lse_round_inst<G, 7, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
+        case 8: return launch_lse_round_inst<G, 8, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
         default: return hipErrorInvalidValue;                                        \
     }
 
@@ -897,7 +954,12 @@ static hipError_t launch_lse_round_inst(const SweepLaunch& a, dim3 grid, const S
 template <bool LIN, bool PROJ>
 hipError_t launch_lse_round_layout(const SweepCfg& cfg, const SweepLaunch& a, int ndir,
                                    hipStream_t stream) {
-    const dim3 grid = a.mode == MODE_FULL ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);
+    const dim3 grid = (a.mode == MODE_FULL || a.mode == MODE_REPAIR) ? dim3(a.B, ndir)
+                                                                     : dim3(a.nspans, a.B, ndir);
+    // the speculative spans and their repair (the only modes the library launches for
+    // C <= 16) run the instance with per-position staging, which writes the outputs and
+    // the seam windows
+    if (a.mode != MODE_SPEC && a.mode != MODE_REPAIR) return hipErrorInvalidValue;
     if (cfg.G == 64 && cfg.CPr == 4) { LSE_ROUND_BPL_CASES(64, 4) }
     if (cfg.G == 64 && cfg.CPr == 6) { LSE_ROUND_BPL_CASES(64, 6) }
     if (cfg.G == 64 && cfg.CPr == 8) { LSE_ROUND_BPL_CASES(64, 8) }

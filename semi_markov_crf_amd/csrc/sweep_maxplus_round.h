@@ -115,12 +115,42 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
     const bool cact = chain && tid < C;
     const int cl = cact ? tid : 0;
 
-    const int b = blockIdx.x, dir = blockIdx.y;
+    // MODE_FULL: grid (B, 2), the two directions meet in the middle.  MODE_SPEC: grid
+    // (nspans, B), every span of the forward sweep at once from a burn-in; MODE_REPAIR:
+    // grid (B), the forward sweep again from the checkpoint at the first failed seam.
+    const bool full = a.mode == MODE_FULL, spec = a.mode == MODE_SPEC;
+    int b, dir = 0, span = 0;
+    if (full) {
+        b = blockIdx.x; dir = blockIdx.y;
+    } else if (spec) {
+        span = blockIdx.x; b = blockIdx.y;
+    } else {
+        b = blockIdx.x;
+    }
     const int Lr = a.Leff[b];
     const int L = Lr < 0 ? -Lr : Lr;
-    const int mm = min(L, (L + K - 1) / 2);             // meeting window [lo, mm]
-    const int lo = max(0, mm - K + 1);
-    const int t0 = 0, t1 = dir == 0 ? mm : L - lo;
+    int mm = 0, lo = 0, t0 = 0, t1 = L, tout = 0;
+    if (full) {
+        mm = min(L, (L + K - 1) / 2);                   // meeting window [lo, mm]
+        lo = max(0, mm - K + 1);
+        t1 = dir == 0 ? mm : L - lo;
+    } else if (spec) {
+        tout = span * a.delta;
+        if (tout >= L) return;
+        t1 = min(L, tout + a.delta);
+        t0 = max(0, tout - a.warm);
+    } else {
+        span = a.first_bad[b];
+        if (span >= a.nspans) return;
+        tout = span * a.delta;
+        if (tout >= L) return;
+        t0 = tout;
+    }
+    const bool ckpt = spec && t1 < L;                   // checkpoint at the span's end
+    const int hlo = (spec && span > 0) ? tout - K + 1 : INT_MAX;    // seam windows
+    const int tlo = ckpt ? t1 - K + 1 : INT_MAX;
+    const size_t winrow = ((size_t)b * a.nspans + span) * K;
+    const size_t ckrow = (size_t)b * a.nspans;
     const int RMASK = RS - 1;
     const int bmax = (K + M - 1) / M;
     const int NR = bmax + 3;
@@ -219,16 +249,48 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
     };
 
     // ---------------------------------------------------------------- start state
-    // position 0: no transition into it; the ring entry is its start-side projection
-    if (bact && j == 0) Rrow[slot_mp(-1, RMASK) + M - 1] = fmaxf(proj_s(0, cb), NEG);
+    auto slot_of = [&](int pos) { return (pos - t0 - 1) & RMASK; };
     // chain history, i < M: the previous round's positions (round start) - 3 + i; i >= M:
     // this round's (ring entries A - B_c)
     float Rh[2 * M];
 #pragma unroll
     for (int i = 0; i < 2 * M; ++i) Rh[i] = NEG;
-    Rh[M - 1] = cact ? fmaxf(proj_s(0, cl), NEG) : 0.0f;
     double Bc = 0.0, H = 0.0;
     float Mref = 0.0f;
+    if (t0 == 0) {
+        // position 0: no transition into it; the ring entry is its start-side projection
+        if (bact && j == 0) Rrow[slot_of(0)] = fmaxf(proj_s(0, cb), NEG);
+        Rh[M - 1] = cact ? fmaxf(proj_s(0, cl), NEG) : 0.0f;
+    } else if (spec) {
+        // burn-in start: every ring entry of positions t0-K+1 .. t0 equal
+        if (bact)
+            for (int q = j; q < K && t0 - q >= 0; q += G) Rrow[slot_of(t0 - q)] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            const int q = M - 1 - i;
+            Rh[i] = (q < K && t0 - q >= 0) ? 0.0f : NEG;
+        }
+    } else {
+        const size_t ck = ckrow + span;
+        if (bact)
+            for (int q = j; q < K; q += G) Rrow[slot_of(t0 - q)] = a.ck_ring[(ck * K + q) * C + cb];
+        if (chain) {
+            Bc = a.ck_base[ck * C + cl];
+            Mref = a.ck_mprev[ck * C + cl];
+            H = a.ck_href[ck];
+#pragma unroll
+            for (int i = 0; i < M; ++i) {
+                const int q = M - 1 - i;
+                Rh[i] = (q < K && t0 - q >= 0) ? a.ck_ring[(ck * K + q) * C + cl] : NEG;
+            }
+        }
+    }
+    if (cact && t0 == 0) {
+        // seam window positions <= 0: position 0's value, nothing before it
+        const double a0 = Bc + (double)Rh[M - 1];
+        for (int p = hlo; p <= min(0, tout); ++p) a.head[(winrow + p - hlo) * C + cl] = p == 0 ? a0 : -1.0e300;
+        for (int p = tlo; p <= min(0, t1); ++p) a.tail[(winrow + p - tlo) * C + cl] = p == 0 ? a0 : -1.0e300;
+    }
 
     const int chunkN = CH * C;
     auto sidx = [&](int t, int q) -> size_t { return (size_t)(dir == 0 ? t : L - t) * C + q; };
@@ -269,6 +331,31 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
     __builtin_amdgcn_s_waitcnt(0);
     if (!chain) bulk_round(0);
     __syncthreads();
+
+    // bulk lanes: the chain rebased in round r-1: move the blocks of rounds <= r-2 (reads
+    // first)
+    auto rescale = [&](int r) {
+        if (r >= 3 && (r & 1) == 1) {
+            constexpr int BR = BPL + 1;
+            const float dl = bact ? dlsh[cb] : 0.0f;
+            float4 v[BR];
+#pragma unroll
+            for (int i = 0; i < BR; ++i) v[i] = ld4_mp(Rrow + slot_mp(r - 2 - j - i * G, RMASK));
+#pragma unroll
+            for (int i = 0; i < BR; ++i) {
+                const int q = j + i * G;
+                const int rho = r - 2 - q;
+                // blocks outside the live window go to the spare row (read by idle lanes)
+                const bool live = (q < NR) & (t0 + M * rho + M >= 0);
+                float4 rv = v[i];
+                rv.x -= dl;
+                rv.y -= dl;
+                rv.z -= dl;
+                rv.w -= dl;
+                st4_mp((live ? Rrow : R + C * P) + slot_mp(rho, RMASK), rv);
+            }
+        }
+    };
 
     // ---------------------------------------------------------------- main loop
     double BH = Bc - H;
@@ -338,6 +425,7 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
             // the round's last step inside the sweep sets the normaliser
             const int ml = min(M - 1, t1 - rs - 1);
             float me = NEG;
+            float uu[M];
             uint32_t* bpp = a.bp + (size_t)dir * a.B * (T + 1) * C + (outrow + rs + 1) * C + cl;
 #pragma unroll
             for (int m = 0; m < M; ++m) {
@@ -368,8 +456,9 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
                 for (int i = 0; i < CP; ++i) ci[i] = y[i] == mt ? i : INT_MAX;
                 const int cbest = min_tree_i<CP>(ci);
                 Rh[M + m] = mt - hbs[m];
-                if (p <= t1 && cact)   // the label of position L + 1 is never read
+                if (p <= t1 && p > tout && cact)   // the label of position L + 1 is never read
                     bpp[m * C] = (uint32_t)kbest | ((uint32_t)cbest << 16);
+                uu[m] = u;
                 if (m == ml) {
                     float uw[CP];
                     row_bcast_all_mp<CP>(u, uw);
@@ -377,8 +466,22 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
                 }
                 // value at an original position of the meeting window
                 const int tw = dir == 0 ? p : L - p;
-                if (p <= t1 && tw >= lo && tw <= mm && cact)
+                if (full && p <= t1 && tw >= lo && tw <= mm && cact)
                     a.vwin[(((size_t)dir * a.B + b) * K + (tw - lo)) * C + cl] = H0 + (double)u;
+            }
+            if (!full && (rs + M >= min(hlo, tlo) || rs + M >= L)) {
+                // seam windows (ring values, natural log, this sweep's frame) and the final
+                // values V(L, c)
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const int p = rs + 1 + m;
+                    if (cact && p <= t1) {
+                        const double av = Bc + (double)Rh[M + m];
+                        if (p >= hlo && p <= tout) a.head[(winrow + p - hlo) * C + cl] = av;
+                        if (p >= tlo) a.tail[(winrow + p - tlo) * C + cl] = av;
+                        if (p == L) a.vfin[(size_t)b * C + cl] = H0 + (double)uu[m];
+                    }
+                }
             }
             H = H0 + (me > NEG_HALF ? (double)floorf(me) : 0.0);
             BH = Bc - H;
@@ -387,6 +490,15 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
 #pragma unroll
             for (int m = 0; m < M; ++m)
                 if (rs + 1 + m <= t1 && Q[m] > NEG_HALF) Mref = Q[m];
+            if (ckpt && rs < t1 && rs + M >= t1) {
+                // checkpoint at the span's end (its ring is copied after the loop)
+                const size_t ck = ckrow + t1 / a.delta;
+                if (cact) {
+                    a.ck_base[ck * C + cl] = Bc;
+                    a.ck_mprev[ck * C + cl] = Mref;
+                }
+                if (tid == 0) a.ck_href[ck] = H0;
+            }
 #pragma unroll
             for (int i = 0; i < M; ++i) Rh[i] = Rh[i + M];
         } else {
@@ -418,30 +530,19 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
                     }
                 }
             }
-            // the chain rebased last round: move the blocks of rounds <= r-2 (reads first)
-            if (r >= 3 && (r & 1) == 1) {
-                constexpr int BR = BPL + 1;
-                const float dl = bact ? dlsh[cb] : 0.0f;
-                float4 v[BR];
-#pragma unroll
-                for (int i = 0; i < BR; ++i) v[i] = ld4_mp(Rrow + slot_mp(r - 2 - j - i * G, RMASK));
-#pragma unroll
-                for (int i = 0; i < BR; ++i) {
-                    const int q = j + i * G;
-                    const int rho = r - 2 - q;
-                    // blocks outside the live window go to the spare row (read by idle lanes)
-                    const bool live = (q < NR) & (t0 + M * rho + M >= 0);
-                    float4 rv = v[i];
-                    rv.x -= dl;
-                    rv.y -= dl;
-                    rv.z -= dl;
-                    rv.w -= dl;
-                    st4_mp((live ? Rrow : R + C * P) + slot_mp(rho, RMASK), rv);
-                }
-            }
+            rescale(r);
             bulk_round(r + 1);
         }
         __syncthreads();
+    }
+    if (ckpt) {
+        // the ring at the span's end, once the last rebase has reached it
+        if (!chain) rescale(nrounds);
+        __syncthreads();
+        if (bact) {
+            const size_t ck = ckrow + t1 / a.delta;
+            for (int qq = j; qq < K; qq += G) a.ck_ring[(ck * K + qq) * C + cb] = Rrow[slot_of(t1 - qq)];
+        }
     }
 }
 
@@ -453,7 +554,9 @@ static hipError_t launch_maxplus_round_inst(const SweepLaunch& a, const SweepCfg
         cfg.vit.P % 4 != 0 || cfg.RS % ROUND != 0)
         return hipErrorInvalidValue;
     const size_t bytes = maxplus_round_lds_bytes(a.C, CP, cfg.vit.P, cfg.vit.CH, PROJ);
-    hipLaunchKernelGGL((k_maxplus_round<G, BPL, CP, PROJ>), dim3(a.B, 2), dim3(cfg.NT), bytes,
+    const dim3 grid = a.mode == MODE_FULL ? dim3(a.B, 2)
+                      : a.mode == MODE_SPEC ? dim3(a.nspans, a.B) : dim3(a.B);
+    hipLaunchKernelGGL((k_maxplus_round<G, BPL, CP, PROJ>), grid, dim3(cfg.NT), bytes,
                        stream, static_cast<const SweepArgs&>(a), cfg.RS, cfg.vit.P, cfg.vit.CH,
                        a.proj_start, a.proj_end);
     return hipGetLastError();

@@ -127,6 +127,37 @@ __global__ __launch_bounds__(256) void k_vit_combine(const double* __restrict__ 
     }
 }
 
+// one thread per sequence: the best final label of the forward decode over speculative
+// spans (lowest on ties) and its score in the exact frame (the last span's offset)
+__global__ void k_vit_final(const double* __restrict__ vfin, const double* __restrict__ off,
+                            const int* __restrict__ Leff, int B, int C, int delta, int nspans,
+                            double* __restrict__ vscore, int* __restrict__ vcstar) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    const int L = abs(Leff[b]);
+    const int n = (L + delta - 1) / delta;
+    double best = -INFINITY;
+    int bc = 0;
+    for (int c = 0; c < C; ++c) {
+        const double v = vfin[(size_t)b * C + c];
+        if (v > best) {
+            best = v;
+            bc = c;
+        }
+    }
+    vscore[b] = Leff[b] < 0 ? __longlong_as_double(0x7ff8000000000000LL)
+                            : best + off[(size_t)b * nspans + max(n - 1, 0)];
+    vcstar[b] = bc;
+}
+
+hipError_t launch_vit_final(const double* vfin, const double* off, const int* Leff, int B,
+                            int C, int delta, int nspans, double* vscore, int* vcstar,
+                            hipStream_t stream) {
+    hipLaunchKernelGGL(k_vit_final, dim3((B + 255) / 256), dim3(256), 0, stream, vfin, off, Leff,
+                       B, C, delta, nspans, vscore, vcstar);
+    return hipGetLastError();
+}
+
 // grid (nch, B, 2 parts), block BT_THREADS, dynamic LDS (W + K) * C * 4 bytes.
 // tr: [2][B][nch][K*C], the entry node of chunk j+1 reached from each entry node of chunk
 // j, or -1 when the chain ends inside chunk j (or the entry is not a valid end).

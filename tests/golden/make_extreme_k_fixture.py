@@ -4,7 +4,8 @@ Calls only ``oracle/`` (fp64) on inputs from ``workloads.make_custom`` with the 
 shapes listed in CASES; nothing here touches the HIP path.  Output:
 ``tests/golden/oracle_extreme_k.npz`` holding, per case, log Z, mu, grad_em, grad_trans,
 grad_dur, the start / end marginals and boundary probabilities (upstream gradient 1), the
-Viterbi score, margin, labels and segment starts.  Two cases carry boundary projections.
+Viterbi score, margin, labels and segment starts, and the Viterbi paths with the gap of
+every decision along them.  Two cases carry boundary projections.
 The oracle needs minutes for these shapes, so the values are stored instead of being
 recomputed by the GPU tests.
 
@@ -66,6 +67,12 @@ def main():
             out[f"{name}_{k}"] = r[k].astype(np.float32)
         out[f"{name}_labels"] = r["labels"].astype(np.int16)
         out[f"{name}_seg_start"] = r["seg_start"].astype(np.uint8)
+        # the Viterbi paths with the gap of every decision along them
+        segs = [p["segments"] for p in r["paths"]]
+        out[f"{name}_path_off"] = np.cumsum([0] + [len(x) for x in segs]).astype(np.int64)
+        out[f"{name}_path_segs"] = np.concatenate(segs).astype(np.int32)
+        out[f"{name}_path_gaps"] = np.concatenate([p["gaps"] for p in r["paths"]])
+        out[f"{name}_final_gap"] = np.array([p["final_gap"] for p in r["paths"]])
     np.savez_compressed(os.path.join(HERE, "oracle_extreme_k.npz"), **out)
 
 

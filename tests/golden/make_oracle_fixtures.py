@@ -1,12 +1,20 @@
 """Write the oracle's expected values for the five synthetic configurations.
 
-Calls only ``oracle/`` (fp64) on inputs from ``workloads.make(i)``; nothing
-here touches the HIP path.  Output: ``tests/golden/oracle_cfg{i}.npz`` with
-log Z, the batch-summed gradients of trans and dur, the Viterbi score and
-margin for every sequence, and mu / grad_em at a fixed sample of positions
-(every position for the tiny configuration).  Full Viterbi labels are stored
-when the margin exceeds 1e-4 (otherwise several segmentations are optimal
-within the tolerance and only validity and optimality can be checked).
+Calls only ``oracle/`` (fp64) on inputs from ``workloads.make(i)``; nothing here
+touches the HIP path.  Output: ``tests/golden/oracle_cfg{i}.npz`` with
+
+* log Z (forward and backward recursions), the batch-summed gradients of trans and
+  dur, the Viterbi score and margin of every sequence;
+* the Viterbi path of every sequence with the gap of each decision along it
+  (``path_segs`` rows (start, length, label), ``path_gaps``, offsets ``path_off``,
+  ``final_gap``), so a decode can be compared decision by decision;
+* mu and grad_em (float32) on contiguous windows of positions: [j*D - K, j*D + K]
+  around every multiple j*D of the checkpoint interval D = ceil(sqrt(T*K)) counted
+  from either end of the sequence (where the streamed sweeps of the two directions
+  restart), plus the first and last 2K positions (``win_pos`` per sequence with
+  offsets ``win_off``); instead, every position for the tiny and speech
+  configurations and for sequence 0 of the genomic one (``mu_full`` /
+  ``grad_em_full`` with ``full_seqs``).
 
 Usage:  python tests/golden/make_oracle_fixtures.py [cfg ...] [--workers N]
 """
@@ -14,6 +22,7 @@ Usage:  python tests/golden/make_oracle_fixtures.py [cfg ...] [--workers N]
 from __future__ import annotations
 
 import argparse
+import math
 import os
 import sys
 import time
@@ -27,20 +36,23 @@ sys.path.insert(0, ROOT)
 import oracle      # noqa: E402
 import workloads   # noqa: E402
 
-SAMPLES_PER_SEQ = {0: None, 1: 48, 2: 96, 3: 384, 4: 32}
+FULL_SEQS = {0: "all", 1: "all", 2: [0], 3: [], 4: []}
 
 
-def sample_positions(index: int, lengths: np.ndarray) -> np.ndarray:
-    """[B, n] positions: the first and last two, then uniform draws (seed 77)."""
-    n = SAMPLES_PER_SEQ[index]
-    rng = np.random.default_rng(77 + index)
-    out = []
-    for L in lengths:
-        L = int(L)
-        fixed = [0, 1, L - 2, L - 1]
-        draw = rng.integers(0, L, size=n - len(fixed))
-        out.append(np.array(fixed + list(draw), dtype=np.int64))
-    return np.stack(out)
+def window_positions(L: int, T: int, K: int) -> np.ndarray:
+    """Sorted positions in [0, L): windows of half-width K around every multiple of the
+    checkpoint interval from either end, and the first and last 2K positions."""
+    D = math.isqrt(T * K - 1) + 1 if T * K > 1 else 1
+    D = min(D, T)
+    keep = np.zeros(L, dtype=bool)
+    keep[: min(L, 2 * K)] = True
+    keep[max(0, L - 2 * K):] = True
+    for j in range(1, (L + D - 1) // D + 1):
+        for c in (j * D, L - j * D):
+            lo, hi = max(0, c - K), min(L, c + K + 1)
+            if lo < hi:
+                keep[lo:hi] = True
+    return np.nonzero(keep)[0].astype(np.int32)
 
 
 def make_fixture(index: int, workers: int) -> str:
@@ -55,23 +67,31 @@ def make_fixture(index: int, workers: int) -> str:
         "score": res["score"], "margin": res["margin"],
         "oracle_seconds": np.array(dt), "workers": np.array(workers),
     }
-    if SAMPLES_PER_SEQ[index] is None:
-        out["mu"] = res["mu"]
-        out["grad_em"] = res["grad_em"]
-    else:
-        pos = sample_positions(index, w.lengths)
-        b = np.arange(w.B)[:, None]
-        out["positions"] = pos
-        out["mu_sample"] = res["mu"][b, pos].astype(np.float32)
-        out["grad_em_sample"] = res["grad_em"][b, pos].astype(np.float32)
-    keep = res["margin"] > 1e-4
-    out["labels_stored"] = keep
-    if keep.any():
-        out["labels"] = np.where(keep[:, None], res["labels"], -2).astype(np.int16)
-        out["seg_start"] = np.where(keep[:, None], res["seg_start"], 0).astype(np.uint8)
+    # Viterbi paths with their decision gaps
+    segs = [p["segments"] for p in res["paths"]]
+    out["path_off"] = np.cumsum([0] + [len(s) for s in segs]).astype(np.int64)
+    out["path_segs"] = np.concatenate(segs).astype(np.int32)
+    out["path_gaps"] = np.concatenate([p["gaps"] for p in res["paths"]])
+    out["final_gap"] = np.array([p["final_gap"] for p in res["paths"]])
+    # mu / grad_em windows (none where every position is stored)
+    full = list(range(w.B)) if FULL_SEQS[index] == "all" else FULL_SEQS[index]
+    pos = [np.zeros(0, dtype=np.int32) if b in full else window_positions(int(L), w.T, w.K)
+           for b, L in enumerate(w.lengths)]
+    out["win_off"] = np.cumsum([0] + [len(p) for p in pos]).astype(np.int64)
+    out["win_pos"] = np.concatenate(pos)
+    C = w.C
+    out["mu_win"] = np.concatenate([res["mu"][b, p].reshape(-1, C)
+                                    for b, p in enumerate(pos)]).astype(np.float32)
+    out["grad_em_win"] = np.concatenate([res["grad_em"][b, p].reshape(-1, C)
+                                         for b, p in enumerate(pos)]).astype(np.float32)
+    out["full_seqs"] = np.array(full, dtype=np.int32)
+    if full:
+        out["mu_full"] = res["mu"][full].astype(np.float32)
+        out["grad_em_full"] = res["grad_em"][full].astype(np.float32)
     path = os.path.join(HERE, f"oracle_cfg{index}.npz")
     np.savez_compressed(path, **out)
-    print(f"cfg {index} ({w.name}): {dt:.1f} s, logZ {res['logZ']}, margins {res['margin']}",
+    print(f"cfg {index} ({w.name}): {dt:.1f} s, logZ {res['logZ']}, margins {res['margin']}, "
+          f"{len(out['win_pos'])} window positions, {os.path.getsize(path) / 1e6:.1f} MB",
           flush=True)
     return path
 

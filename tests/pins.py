@@ -205,3 +205,50 @@ def linear_chain(unary, trans):
     path.reverse()
     return {"logZ": logZ, "node": np.array(node), "pair": pair, "score": score,
             "path": np.array(path, dtype=np.int32)}
+
+
+def all_segmentations(em_b, L: int, trans, dur, K: int):
+    """Every segmentation of [0, L) as (segments, score), segments a tuple of
+    (start, length, label) in order; the score summed position by position from
+    the centred emissions (no prefix sums), plus durations and transitions."""
+    x = centred_emissions(em_b, L)
+    C = len(x[0])
+    trans = np.asarray(trans, dtype=np.float64)
+    dur = np.asarray(dur, dtype=np.float64)
+    out = []
+    for comp in compositions(L, K):
+        st = [sum(comp[:i]) for i in range(len(comp))]
+        for labs in itertools.product(range(C), repeat=len(comp)):
+            sc = 0.0
+            for i, (s, k) in enumerate(zip(st, comp)):
+                sc += sum(x[u][labs[i]] for u in range(s, s + k)) + dur[k - 1, labs[i]]
+                if i > 0:
+                    sc += trans[labs[i - 1], labs[i]]
+            out.append((tuple(zip(st, comp, labs)), sc))
+    return out
+
+
+def decision_gaps(segmentations, path):
+    """Gaps of the decisions along ``path`` (a tuple of (start, length, label)),
+    from the enumerated segmentations alone.  For segment i of the path, ending at
+    e with label c after label c' (or after nothing when it starts at 0): the best
+    score minus the best score of any segmentation that also has a segment of label
+    c ending at e but a different start or previous label (inf if none).  The
+    final gap: the best score minus the best score with another last label."""
+    best = max(sc for _, sc in segmentations)
+    gaps = []
+    for i, (s, k, c) in enumerate(path):
+        e = s + k
+        prev = path[i - 1][2] if i > 0 else None
+        alt = -math.inf
+        for segs, sc in segmentations:
+            for j, (s2, k2, c2) in enumerate(segs):
+                if s2 + k2 == e and c2 == c:
+                    p2 = segs[j - 1][2] if j > 0 else None
+                    if (s2, p2) != (s, prev):
+                        alt = max(alt, sc)
+                    break
+        gaps.append(best - alt)
+    last = path[-1][2]
+    alt = max((sc for segs, sc in segmentations if segs[-1][2] != last), default=-math.inf)
+    return np.array(gaps), best - alt

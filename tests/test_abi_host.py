@@ -37,6 +37,58 @@ def test_header_declares_the_three_calls():
         assert f in fns
 
 
+def prototype(name):
+    """Parameter types of `name` in the header, e.g. ['const float*', 'int', ...]."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    out = []
+    for p in m.group(1).split(","):
+        typ = re.match(r"(.*?)\b\w+\s*$", " ".join(p.split())).group(1)
+        out.append(re.sub(r"\s*\*", "*", typ).strip())
+    return out
+
+
+# The problem statement's calls: each takes (emissions[B,T,C], lengths, trans[C,C],
+# dur[K,C], K, stream), with B, T, C explicit, a caller workspace and the outputs.
+PROBLEM_STATEMENT = {
+    "semicrf_workspace_bytes": ["semicrf_op", "int", "int", "int", "int", "int"],
+    "semicrf_logz": ["const float*", "const int32_t*", "const float*", "const float*", "int",
+                     "int", "int", "int", "int", "hipStream_t", "void*", "size_t", "float*"],
+    "semicrf_backward": ["const float*", "const int32_t*", "const float*", "const float*",
+                         "int", "int", "int", "int", "int", "hipStream_t", "void*", "size_t",
+                         "const float*", "float*", "float*", "float*", "float*", "float*"],
+    "semicrf_viterbi": ["const float*", "const int32_t*", "const float*", "const float*", "int",
+                        "int", "int", "int", "hipStream_t", "void*", "size_t", "float*",
+                        "int32_t*", "uint8_t*"],
+    "semicrf_status_string": ["int"],
+}
+
+
+@pytest.mark.parametrize("name", sorted(PROBLEM_STATEMENT))
+def test_prototypes_follow_the_problem_statement(name):
+    assert prototype(name) == PROBLEM_STATEMENT[name]
+
+
+def test_status_codes_in_header():
+    text = open(HEADER).read()
+    for i, n in enumerate(["SEMICRF_OK", "SEMICRF_ERR_INVALID", "SEMICRF_ERR_WORKSPACE",
+                           "SEMICRF_ERR_UNSUPPORTED", "SEMICRF_ERR_DEVICE",
+                           "SEMICRF_ERR_UNIMPLEMENTED"]):
+        assert re.search(rf"\b{n}\s*=\s*{i}\b", text), n
+    for i, n in enumerate(["SEMICRF_OP_LOGZ", "SEMICRF_OP_BACKWARD", "SEMICRF_OP_VITERBI"]):
+        assert re.search(rf"\b{n}\s*=\s*{i}\b", text), n
+
+
+def test_options_struct_matches_binding():
+    """The ctypes Options struct lists the header's semicrf_options fields in order."""
+    from semi_markov_crf_amd import _native
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct semicrf_options \{(.*?)\} semicrf_options;", text, re.S)
+    names = re.findall(r"(\w+)\s*;", body.group(1))
+    assert names == [f[0] for f in _native.Options._fields_]
+
+
 def test_every_declared_symbol_is_exported(native):
     out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
                          check=True).stdout
@@ -50,7 +102,7 @@ def test_every_declared_symbol_is_exported(native):
 
 
 def test_status_strings(native):
-    for s in range(5):
+    for s in range(6):
         assert native.status_string(s)
     assert native.status_string(99) == "unknown status"
 
@@ -102,40 +154,39 @@ def test_argument_validation_returns_before_any_launch(native):
     lib = native.load()
     p = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
     n = None
-    # NULL inputs / outputs (projections NULL: absent)
-    assert lib.semicrf_logz(n, p, p, p, n, n, 1, 4, 2, 2, n, p, 1 << 20, p) == 1
-    assert lib.semicrf_logz(p, p, p, p, n, n, 1, 4, 2, 2, n, p, 1 << 20, n) == 1
-    # bad sizes
-    assert lib.semicrf_logz(p, p, p, p, n, n, 0, 4, 2, 2, n, p, 1 << 20, p) == 1
-    assert lib.semicrf_logz(p, p, p, p, n, n, 1, 4, 2, 0, n, p, 1 << 20, p) == 1
+    # NULL inputs / outputs
+    assert lib.semicrf_logz(n, p, p, p, 1, 4, 2, 2, 0, n, p, 1 << 20, p) == 1
+    assert lib.semicrf_logz(p, p, p, p, 1, 4, 2, 2, 0, n, p, 1 << 20, n) == 1
+    # bad sizes, negative delta
+    assert lib.semicrf_logz(p, p, p, p, 0, 4, 2, 2, 0, n, p, 1 << 20, p) == 1
+    assert lib.semicrf_logz(p, p, p, p, 1, 4, 2, 0, 0, n, p, 1 << 20, p) == 1
+    assert lib.semicrf_logz(p, p, p, p, 1, 4, 2, 2, -1, n, p, 1 << 20, p) == 1
     # unsupported label count
-    assert lib.semicrf_logz(p, p, p, p, n, n, 1, 4, 4096, 2, n, p, 1 << 20, p) == 3
+    assert lib.semicrf_logz(p, p, p, p, 1, 4, 4096, 2, 0, n, p, 1 << 20, p) == 3
     # workspace missing, too small, misaligned
     need = lib.semicrf_workspace_bytes(0, 1, 4, 2, 2, 0)
-    assert lib.semicrf_logz(p, p, p, p, p, p, 1, 4, 2, 2, n, n, need, p) == 2
-    assert lib.semicrf_logz(p, p, p, p, p, p, 1, 4, 2, 2, n, p, need - 1, p) == 2
-    assert lib.semicrf_logz(p, p, p, p, n, n, 1, 4, 2, 2, n, ctypes.c_void_p(0x1008), need, p) == 2
+    assert lib.semicrf_logz(p, p, p, p, 1, 4, 2, 2, 0, n, n, need, p) == 2
+    assert lib.semicrf_logz(p, p, p, p, 1, 4, 2, 2, 0, n, p, need - 1, p) == 2
+    assert lib.semicrf_logz(p, p, p, p, 1, 4, 2, 2, 0, n, ctypes.c_void_p(0x1008), need, p) == 2
     # backward: required gradient outputs, negative delta
     need = lib.semicrf_workspace_bytes(1, 1, 4, 2, 2, 0)
-    assert lib.semicrf_backward(p, p, p, p, n, n, 1, 4, 2, 2, 0, n, p, need, n, n, p, p, n, n,
-                                n, n, n) == 1
-    assert lib.semicrf_backward(p, p, p, p, n, n, 1, 4, 2, 2, -1, n, p, need, n, p, p, p, n, n,
-                                p, p, p) == 1
-    assert lib.semicrf_backward(p, p, p, p, p, p, 1, 4, 2, 2, 0, n, p, 16, n, p, p, p, n, n,
-                                n, n, n) == 2
-    # training loss: gold segmentation and loss output required
-    assert lib.semicrf_nll(p, p, p, p, n, n, n, p, 1, 4, 2, 2, 0, n, p, need, n, p, p, p, p,
-                           n, n) == 1
-    assert lib.semicrf_nll(p, p, p, p, n, n, p, p, 1, 4, 2, 2, 0, n, p, need, n, n, p, p, p,
-                           n, n) == 1
-    # viterbi outputs
+    assert lib.semicrf_backward(p, p, p, p, 1, 4, 2, 2, 0, n, p, need, n, n, p, p, n, n) == 1
+    assert lib.semicrf_backward(p, p, p, p, 1, 4, 2, 2, -1, n, p, need, n, p, p, p, n, n) == 1
+    assert lib.semicrf_backward(p, p, p, p, 1, 4, 2, 2, 0, n, p, 16, n, p, p, p, n, n) == 2
+    # training loss: gold segmentation and loss output required; no backward-only options
+    assert lib.semicrf_nll(p, p, p, p, n, p, 1, 4, 2, 2, 0, n, p, need, n, p, p, p, p, n) == 1
+    assert lib.semicrf_nll(p, p, p, p, p, p, 1, 4, 2, 2, 0, n, p, need, n, n, p, p, p, n) == 1
+    opt = native.options(boundary=0x1000)
+    assert lib.semicrf_nll(p, p, p, p, p, p, 1, 4, 2, 2, 0, n, p, need, n, p, p, p, p,
+                           ctypes.byref(opt)) == 1
+    # viterbi outputs; backward-only options refused
     need = lib.semicrf_workspace_bytes(2, 1, 4, 2, 2, 0)
-    assert lib.semicrf_viterbi(p, p, p, p, n, n, 1, 4, 2, 2, n, p, need, p, n, p) == 1
+    assert lib.semicrf_viterbi(p, p, p, p, 1, 4, 2, 2, n, p, need, p, n, p) == 1
+    opt = native.options(node_mass=0x1000)
+    assert lib.semicrf_viterbi_ex(p, p, p, p, 1, 4, 2, 2, n, p, need, p, p, p,
+                                  ctypes.byref(opt)) == 1
     assert lib.semicrf_read_status(n, n) == 2
     need = lib.semicrf_workspace_bytes(3, 1, 4, 2, 1, 0)
     assert lib.semicrf_prefix(p, p, 1, 4, 2, n, p, need, n) == 1
     assert lib.semicrf_prefix(p, p, 1, 4, 2, n, p, need - 1, p) == 2
-    for f in ("semicrf_logz_staged", "semicrf_viterbi_staged"):
-        args = [p, p, p, p, n, n, 1, 4, 2, 2, n, p, 1 << 20, p] + (
-            [n] if f == "semicrf_logz_staged" else [p, p, n])
-        assert getattr(lib, f)(*args) == 1          # events pointer required
+

@@ -149,6 +149,8 @@ def test_nll_at_config_size(crf, cfg):
     fixture (the same values the backward pass is checked against), the gold score and
     the gold feature counts from the oracle's O(L) definitions."""
     ref = _fixture(cfg)
+    if "win_pos" not in ref:
+        pytest.skip("fixture written by an older script")
     w = workloads.make(cfg)
     print(f"\n[nll config {cfg}: {w.name} B={w.B} T={w.T} C={w.C} K={w.K}]", flush=True)
     labels, seg = workloads.gold_segmentation(2000 + cfg, w.lengths, w.T, w.C, w.K)
@@ -166,12 +168,15 @@ def test_nll_at_config_size(crf, cfg):
         tcount += tc
         dcount += dc
         gold = ind - ind.mean(axis=0, keepdims=True)
-        if "grad_em" in ref:
-            close_abs(ge[b, :L], ref["grad_em"][b, :L] - gold, MARG_ATOL, f"grad_em[{b}]")
+        full = list(ref["full_seqs"])
+        if b in full:
+            close_abs(ge[b, :L], ref["grad_em_full"][full.index(b)][:L] - gold, MARG_ATOL,
+                      f"grad_em[{b}]")
         else:
-            pos = ref["positions"][b]
-            close_abs(ge[b, pos], ref["grad_em_sample"][b] - gold[pos], MARG_ATOL,
-                      f"grad_em[{b}] (sampled)")
+            o0, o1 = ref["win_off"][b], ref["win_off"][b + 1]
+            pos = ref["win_pos"][o0:o1]
+            close_abs(ge[b, pos], ref["grad_em_win"][o0:o1] - gold[pos], MARG_ATOL,
+                      f"grad_em[{b}] (seam windows)")
     close_rel(np_(out["grad_trans"]), ref["grad_trans"] - tcount, GRAD_RTOL, ref["grad_trans"],
               "grad_trans")
     close_rel(np_(out["grad_dur"]), ref["grad_dur"] - dcount, GRAD_RTOL, ref["grad_dur"],

@@ -4,9 +4,10 @@ Tolerances (fixed here, derived in the design doc):
   log Z, Viterbi score     |gpu - ref| <= 1e-5 * max(1, |ref|)
   marginals, grad_em       |gpu - ref| <= 1e-4
   grad_trans, grad_dur     |gpu - ref| <= 1e-4 * max(1, |ref|)   (sums over up to B*T positions)
-  Viterbi segmentation     identical wherever the oracle's margin exceeds 1e-4; otherwise the
-                           GPU segmentation must be valid and score (rescored in fp64 by the
-                           oracle) within the score tolerance of the best.
+  Viterbi segmentation     valid, rescored in fp64 by the oracle within 1e-3 of the best,
+                           and equal to the oracle's path at every decision whose gap
+                           exceeds 1e-4 (decode_check.py)
+  node mass                |sum over labels of the unnormalised marginals - 1| <= 1e-4
 """
 
 import os
@@ -14,6 +15,7 @@ import os
 import numpy as np
 import pytest
 
+import decode_check
 import oracle
 import workloads
 
@@ -59,19 +61,18 @@ def assert_abs_close(gpu, ref, atol, what):
     assert err.max() <= atol, f"{what}: max abs err {err.max():.3e} > {atol}"
 
 
-def check_viterbi(w, score, labels, seg, ref):
-    """Exact where the oracle's margin > 1e-4, else validity + optimality by rescoring."""
+def check_viterbi(w, score, labels, seg, ref, paths=None):
+    """Score within 1e-5 relative; every decode valid, its fp64 rescore within 1e-3 of the
+    best, and equal to the oracle's path at every decision whose gap exceeds 1e-4."""
     assert_scalar_close(score, ref["score"], LOGZ_RTOL, "viterbi score")
+    paths = paths if paths is not None else ref.get("paths")
+    checked = 0
     for b in range(w.B):
         L = int(w.lengths[b])
-        assert np.all(labels[b, L:] == -1) and np.all(seg[b, L:] == 0)
-        if ref["margin"][b] > 1e-4 and "labels" in ref:
-            np.testing.assert_array_equal(labels[b, :L], ref["labels"][b, :L])
-            np.testing.assert_array_equal(seg[b, :L], ref["seg_start"][b, :L])
-        _, S = oracle.centered_prefix(w.em[b], L)
-        got = oracle.segmentation_score(S, w.trans, w.dur, w.K, seg[b, :L], labels[b, :L])
-        best = float(ref["score"][b])
-        assert got >= best - LOGZ_RTOL * max(1.0, abs(best)), (b, got, best)
+        checked += decode_check.check_decode(w.em[b], L, w.trans, w.dur, w.K, labels[b],
+                                             seg[b], float(ref["score"][b]),
+                                             None if paths is None else paths[b])
+    return checked
 
 
 SMALL = [
@@ -105,8 +106,12 @@ def test_small_cases_against_oracle(crf, case):
     assert_scalar_close(np_(lz), ref["logZ"], LOGZ_RTOL, "logz")
 
     out = crf.backward(em, lengths, trans, dur, grad_log_z=torch.from_numpy(g).cuda(),
-                       check_status=True)
+                       want_node_mass=True, check_status=True)
     assert_scalar_close(np_(out["log_z"]), ref["logZ"], LOGZ_RTOL, "backward log_z")
+    nm = np_(out["node_mass"])
+    for b in range(B):
+        L = int(w.lengths[b])
+        assert np.abs(nm[b, :L] - 1.0).max() <= 1e-4 and np.all(nm[b, L:] == 0)
     assert_abs_close(np_(out["marginals"]), ref["mu"], MARG_ATOL, "marginals")
     assert_abs_close(np_(out["grad_em"]), ref["grad_em"], MARG_ATOL, "grad_em")
     assert_scalar_close(np_(out["grad_trans"]), ref["grad_trans"], GRAD_RTOL, "grad_trans")
@@ -196,38 +201,54 @@ def _fixture(i):
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_config_against_oracle_fixture(crf, cfg):
     ref = _fixture(cfg)
+    if "win_pos" not in ref:
+        pytest.skip("fixture written by an older script")
     w = workloads.make(cfg)
     em, lengths, trans, dur = dev(w)
     print(f"\n[config {cfg}: {w.name} B={w.B} T={w.T} C={w.C} K={w.K}]", flush=True)
     lz = np_(crf.logz(em, lengths, trans, dur, check_status=True))
     assert_scalar_close(lz, ref["logZ"], LOGZ_RTOL, "logz")
-    out = crf.backward(em, lengths, trans, dur, check_status=True)
+    out = crf.backward(em, lengths, trans, dur, want_node_mass=True, check_status=True)
     assert_scalar_close(np_(out["log_z"]), ref["logZ"], LOGZ_RTOL, "backward log_z")
-    mu, ge = np_(out["marginals"]), np_(out["grad_em"])
-    if "mu" in ref:
-        assert_abs_close(mu, ref["mu"], MARG_ATOL, "marginals")
-        assert_abs_close(ge, ref["grad_em"], MARG_ATOL, "grad_em")
-    else:
-        b = np.arange(w.B)[:, None]
-        pos = ref["positions"]
-        assert_abs_close(mu[b, pos], ref["mu_sample"], MARG_ATOL, "marginals (sampled)")
-        assert_abs_close(ge[b, pos], ref["grad_em_sample"], MARG_ATOL, "grad_em (sampled)")
+    mu, ge, nm = np_(out["marginals"]), np_(out["grad_em"]), np_(out["node_mass"])
+    # every position of the sequences stored in full
+    for i, b in enumerate(ref["full_seqs"]):
+        assert_abs_close(mu[b], ref["mu_full"][i], MARG_ATOL, f"marginals of sequence {b}")
+        assert_abs_close(ge[b], ref["grad_em_full"][i], MARG_ATOL, f"grad_em of sequence {b}")
+    # contiguous windows around every checkpoint seam of both sweep directions and the
+    # first and last 2K positions of the other sequences
+    off, pos = ref["win_off"], ref["win_pos"]
+    for b in range(w.B):
+        p = pos[off[b]:off[b + 1]]
+        if len(p):
+            assert_abs_close(mu[b, p], ref["mu_win"][off[b]:off[b + 1]], MARG_ATOL,
+                             f"marginals, seam windows of sequence {b}")
+            assert_abs_close(ge[b, p], ref["grad_em_win"][off[b]:off[b + 1]], MARG_ATOL,
+                             f"grad_em, seam windows of sequence {b}")
     assert_scalar_close(np_(out["grad_trans"]), ref["grad_trans"], GRAD_RTOL, "grad_trans")
     assert_scalar_close(np_(out["grad_dur"]), ref["grad_dur"], GRAD_RTOL, "grad_dur")
-    # properties that hold at every position
+    # the marginals before normalisation sum to 1 over labels at every position (the
+    # pages' self-consistency check, EN explainer "4. Results and Benchmarks"), and mass
+    # is conserved
     for b in range(w.B):
         L = int(w.lengths[b])
-        assert np.abs(mu[b, :L].sum(axis=1) - 1.0).max() < 1e-5
+        assert np.all(nm[b, L:] == 0)
         assert mu[b, :L].min() > -1e-6 and np.all(mu[b, L:] == 0)
         assert np.abs(ge[b, :L].sum(axis=0)).max() < 1e-3 * max(1, L / 1000)
     k = np.arange(1, w.K + 1)[:, None]
     total = float(w.lengths.astype(np.int64).sum())
     assert abs((k * np_(out["grad_dur"]).astype(np.float64)).sum() - total) < 1e-4 * total
     score, labels, seg = crf.viterbi(em, lengths, trans, dur, check_status=True)
-    vref = {"score": ref["score"], "margin": ref["margin"]}
-    if "labels" in ref:
-        vref["labels"], vref["seg_start"] = ref["labels"], ref["seg_start"]
-    check_viterbi(w, np_(score), np_(labels), np_(seg), vref)
+    paths = [decode_check.fixture_path(ref, b) for b in range(w.B)]
+    n = check_viterbi(w, np_(score), np_(labels), np_(seg), ref, paths)
+    print(f"Viterbi: {n} unique decisions of the oracle's paths compared", flush=True)
+    drift = [float(np.abs(nm[b, :int(w.lengths[b])].astype(np.float64) - 1.0).max())
+             for b in range(w.B)]
+    L0 = int(w.lengths[0])
+    print("node mass - 1 of sequence 0 at t = 0, L/4, L/2, 3L/4, L-1:",
+          [float(nm[0, t]) - 1.0 for t in (0, L0 // 4, L0 // 2, 3 * L0 // 4, L0 - 1)], flush=True)
+    print(f"max |node mass - 1| per sequence: {np.array(drift)}", flush=True)
+    assert max(drift) <= 1e-4
 
 
 # label counts 1..8 take the rows-per-lane kernels (odd T: a partial last lane, lengths

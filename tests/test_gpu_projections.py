@@ -13,6 +13,7 @@ import os
 import numpy as np
 import pytest
 
+import decode_check
 import oracle
 import workloads
 
@@ -109,15 +110,9 @@ def test_projections_against_oracle(crf, case):
     labels, seg = np_(labels), np_(seg)
     for b in range(B):
         L = int(w.lengths[b])
-        assert np.all(labels[b, L:] == -1) and np.all(seg[b, L:] == 0)
-        if ref["margin"][b] > 1e-4:
-            np.testing.assert_array_equal(labels[b, :L], ref["labels"][b, :L])
-            np.testing.assert_array_equal(seg[b, :L], ref["seg_start"][b, :L])
-        _, S = oracle.centered_prefix(w.em[b], L)
-        got = oracle.segmentation_score(S, w.trans, w.dur, K, seg[b, :L], labels[b, :L],
-                                        (ps[b, :L], pe[b, :L]))
-        best = float(ref["score"][b])
-        assert got >= best - LOGZ_RTOL * max(1.0, abs(best)), (b, got, best)
+        decode_check.check_decode(w.em[b], L, w.trans, w.dur, K, labels[b], seg[b],
+                                  float(ref["score"][b]), ref["paths"][b],
+                                  (ps[b, :L], pe[b, :L]))
 
     # the training loss with projections
     glab, gseg = workloads.gold_segmentation(seed + 400, w.lengths, T, C, K)
