@@ -59,6 +59,16 @@ __device__ __forceinline__ bool in_lin_range(float s) {
     return __float_as_uint(s) - lo <= hi - lo;
 }
 __device__ __forceinline__ float exp2_or_zero(float x) { return x > NEG_HALF ? fast_exp2(x) : 0.0f; }
+// 2^x for an fp64 exponent, to about the accuracy of the hardware exp2 (a few 1e-8
+// relative): the exponent is rounded to fp32 for exp2 and the part it dropped, x - fl(x),
+// enters to first order, 2^(x - fl(x)) = 1 + (x - fl(x)) ln 2.  Rounding the exponent alone
+// would cost up to half an ulp of |x|, about 1e-6 for |x| near 16, at every use.
+__device__ __forceinline__ float exp2_d(double x) {
+    const float xf = (float)x;
+    const float lo = (float)(x - (double)xf);
+    const float e = fast_exp2(xf);
+    return fmaf(e, lo * 0.69314718f, e);
+}
 // 2^-n for a whole number n (a rebase shift), exactly (0 below the fp32 range)
 __device__ __forceinline__ float pow2_neg(float n) {
     return __builtin_amdgcn_ldexpf(1.0f, -(int)fminf(fmaxf(n, -1.0e9f), 1.0e9f));
@@ -320,7 +330,7 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
         if (a.write_xa && writer)
             Xout[(outrow + (dir == 0 ? tn : L - tn)) * C + c] = (Sn + Bc + (double)sigma) * LN2;
     };
-    publish(t0 + 1, Sbuf[cc], fast_exp2((float)(Sbuf[cc] + BH) + dmax), Qla, Qga);
+    publish(t0 + 1, Sbuf[cc], exp2_d(Sbuf[cc] + BH + (double)dmax), Qla, Qga);
     bulk(t0 + 2, Qla, Qga);
     double lz = 0.0;
     int next_ck = (a.mode == MODE_FULL && a.write_ckpt) ? a.delta : INT_MAX;
@@ -385,8 +395,8 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
             }
             const double Snx = Srow[(row + 1) * C + cc];      // end side of t+1
             const float h = (float)(Scur + BH);                 // start side of t + B_c - H(t)
-            const float f = fast_exp2(tmax - h);                // E(t) = s * f
-            const float z = fast_exp2((float)(Snx + BH) + dmax);
+            const float f = exp2_d((double)tmax - (Scur + BH)); // E(t) = s * f
+            const float z = exp2_d(Snx + BH + (double)dmax);
 
             // ---- loads: bulk window of t+2 and the messages of t
             float bv[KP];

@@ -444,28 +444,34 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
         dS[1] = make_double2(sv[2], sv[3]);
         float* f = Fst + (size_t)buf * NPL * C * CH + sl * CH + M * sq;
         if constexpr (PROJ) {
-            float ge[M], gs[M], pe2[M];
+            // the scale factors from the fp64 exponents (exp2_d), the fp32 exponents for the
+            // log-space path
+            float ge[M], gs[M], pe2[M], fe[M], fs[M];
 #pragma unroll
             for (int d = 0; d < M; ++d) {
-                const float g = (float)(sv[d] - sv[0]);
-                pe2[d] = base2(pfe[d]);
-                ge[d] = g + pe2[d];
-                gs[d] = g - base2(pfs[d]);
+                const double g = sv[d] - sv[0];
+                const double pe = (double)pfe[d] * LOG2E, ps = (double)pfs[d] * LOG2E;
+                pe2[d] = (float)pe;
+                ge[d] = (float)(g + pe);
+                gs[d] = (float)(g - ps);
+                fe[d] = exp2_d(g + pe);
+                fs[d] = exp2_d(ps - g);
             }
-            st4(f, make_float4(fast_exp2(ge[0]), fast_exp2(ge[1]), fast_exp2(ge[2]),
-                               fast_exp2(ge[3])));
-            st4(f + C * CH, make_float4(fast_exp2(-gs[0]), fast_exp2(-gs[1]), fast_exp2(-gs[2]),
-                                        fast_exp2(-gs[3])));
+            st4(f, make_float4(fe[0], fe[1], fe[2], fe[3]));
+            st4(f + C * CH, make_float4(fs[0], fs[1], fs[2], fs[3]));
             st4(f + 2 * C * CH, make_float4(ge[0], ge[1], ge[2], ge[3]));
             st4(f + 3 * C * CH, make_float4(gs[0], gs[1], gs[2], gs[3]));
             st4(f + 4 * C * CH, make_float4(pe2[0], pe2[1], pe2[2], pe2[3]));
         } else {
             // one side: ge = gs = g
+            // the scale factors from the fp64 differences (exp2_d)
             float g[M];
 #pragma unroll
             for (int d = 0; d < M; ++d) g[d] = (float)(sv[d] - sv[0]);
-            st4(f, make_float4(1.0f, fast_exp2(g[1]), fast_exp2(g[2]), fast_exp2(g[3])));
-            st4(f + C * CH, make_float4(1.0f, fast_exp2(-g[1]), fast_exp2(-g[2]), fast_exp2(-g[3])));
+            st4(f, make_float4(1.0f, exp2_d(sv[1] - sv[0]), exp2_d(sv[2] - sv[0]),
+                               exp2_d(sv[3] - sv[0])));
+            st4(f + C * CH, make_float4(1.0f, exp2_d(sv[0] - sv[1]), exp2_d(sv[0] - sv[2]),
+                                        exp2_d(sv[0] - sv[3])));
             st4(f + 2 * C * CH, make_float4(0.0f, g[1], g[2], g[3]));
         }
     };
@@ -648,10 +654,11 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
                 // 2^(hb + dmax) and 2^(tmax - hb) from one exp2 each and staged factors
                 const float* f = Fst + (size_t)(nch & 1) * NPL * C * CH + cl * CH + row0;
                 const float4 sg4 = ld4(f), is4 = ld4(f + C * CH), g4 = ld4(f + 2 * C * CH);
-                const float hb0 = (float)(Sch[cl * CH + row0] + BH);
-                const float y0 = cact ? fast_exp2(hb0 + dmax) : 0.0f;
+                const double hb64 = Sch[cl * CH + row0] + BH;
+                const float hb0 = (float)hb64;
+                const float y0 = cact ? exp2_d(hb64 + (double)dmax) : 0.0f;
                 const float fo0 = tmax - hb0;
-                const float f0 = fast_exp2(fo0);
+                const float f0 = exp2_d((double)tmax - hb64);
                 const float gs[M] = {g4.x, g4.y, g4.z, g4.w};
                 const float ss[M] = {sg4.x, sg4.y, sg4.z, sg4.w};
                 const float is[M] = {is4.x, is4.y, is4.z, is4.w};
@@ -670,10 +677,11 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
                 const float* f = Fst + (size_t)(nch & 1) * NPL * C * CH + cl * CH + row0;
                 const float4 fe4 = ld4(f), fs4 = ld4(f + C * CH), ge4 = ld4(f + 2 * C * CH);
                 const float4 gs4 = ld4(f + 3 * C * CH);
-                const float hb0 = (float)(Sch[cl * CH + row0] + BH);
-                const float y0 = cact ? fast_exp2(hb0 + dmax) : 0.0f;
+                const double hb64 = Sch[cl * CH + row0] + BH;
+                const float hb0 = (float)hb64;
+                const float y0 = cact ? exp2_d(hb64 + (double)dmax) : 0.0f;
                 const float fo0 = tmax - hb0;
-                const float f0 = fast_exp2(fo0);
+                const float f0 = exp2_d((double)tmax - hb64);
                 const float ge[M] = {ge4.x, ge4.y, ge4.z, ge4.w};
                 const float gs[M] = {gs4.x, gs4.y, gs4.z, gs4.w};
                 const float fe[M] = {fe4.x, fe4.y, fe4.z, fe4.w};
