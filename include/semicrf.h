@@ -245,6 +245,24 @@ int semicrf_nll(const float* emissions, const int32_t* lengths, const float* tra
                 float* grad_emissions, float* grad_trans, float* grad_dur,
                 const semicrf_options* options);
 
+/* ------------------------------------------------------------------ no allocation
+ * For callers that cannot allocate device memory at all: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  semicrf_logz without a
+ * workspace argument: the workspace is a static device array of
+ * SEMICRF_STATIC_SCRATCH_BYTES inside the library, one per GPU, held from the first
+ * call on that GPU until the process ends.  The call allocates nothing (no hipMalloc,
+ * no allocating library routine).  Shapes whose semicrf_workspace_bytes(
+ * SEMICRF_OP_LOGZ, ...) exceeds the array return SEMICRF_ERR_WORKSPACE before any
+ * launch.  Every call on one GPU shares that GPU's array, so calls that overlap on one
+ * GPU (on different streams, or from different threads) race and must be serialised
+ * by the caller.  An invalid length gives NaN in log_z as for semicrf_logz; its status
+ * flag is not readable.  The array lives on the device of `stream` (the current
+ * device for the NULL stream). */
+#define SEMICRF_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+int semicrf_logz_static(const float* emissions, const int32_t* lengths, const float* trans,
+                        const float* dur, int B, int T, int C, int K, int delta,
+                        hipStream_t stream, float* log_z);
+
 /* Synchronously reads the device status flag left in `workspace` by the last call
  * that used it (after waiting for `stream`).  SEMICRF_OK, SEMICRF_ERR_INVALID if a
  * length was outside [1, T], or SEMICRF_ERR_DEVICE if the copy failed. */

@@ -53,7 +53,10 @@ SIGNATURES = {
     "semicrf_nll": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                              _c_int, _vp, _vp, _c_size, _vp, _vp, _vp, _vp, _vp, _opt]),
     "semicrf_read_status": (_c_int, [_vp, _vp]),
+    "semicrf_logz_static": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                     _vp, _vp]),
 }
+STATIC_SCRATCH_BYTES = 32 << 20
 STAGES = {"logz": 2, "backward": 5, "viterbi": 3}
 
 

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/semicrf.h"
@@ -590,6 +592,61 @@ int semicrf_viterbi_ex(const float* em, const int32_t* lengths, const float* tra
     return run_viterbi(em, lengths, trans, dur, Proj{o.proj_start, o.proj_end}, B, T, C, K,
                        stream, workspace, workspace_bytes, best_score, labels, seg_start,
                        spec_opt(o), o.events);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-allocation variant
+namespace {
+
+// The workspace of semicrf_logz_static: one copy per GPU, in the code object's device
+// memory.  Host code never passes `scratch` itself (on the host it only names a
+// stand-in): it passes the device address hipGetSymbolAddress returns for each device.
+static __device__ __align__(256) unsigned char scratch[SEMICRF_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device of `stream`, looked up once per device with
+// that device current.
+int static_scratch(hipStream_t stream, void** out) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return SEMICRF_ERR_DEVICE;
+    int dev = cur;
+    if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return SEMICRF_ERR_DEVICE;
+    if (dev < 0 || dev >= kMaxDevices) return SEMICRF_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return SEMICRF_ERR_DEVICE;
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return SEMICRF_ERR_DEVICE;
+        if (e != hipSuccess || !ptr) return SEMICRF_ERR_DEVICE;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SEMICRF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int semicrf_logz_static(const float* em, const int32_t* lengths, const float* trans,
+                        const float* dur, int B, int T, int C, int K, int delta,
+                        hipStream_t stream, float* log_z) {
+    int rc = common_checks(em, lengths, trans, dur, B, T, C, K);
+    if (rc) return rc;
+    if (!log_z || delta < 0) return SEMICRF_ERR_INVALID;
+    Layout lo;
+    if (!make_layout(SEMICRF_OP_LOGZ, B, T, C, K, delta, lo)) return SEMICRF_ERR_UNSUPPORTED;
+    if (lo.total > SEMICRF_STATIC_SCRATCH_BYTES) return SEMICRF_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((rc = static_scratch(stream, &ws))) return rc;
+    return run_logz(em, lengths, trans, dur, Proj{nullptr, nullptr}, B, T, C, K, delta, stream,
+                    ws, SEMICRF_STATIC_SCRATCH_BYTES, log_z, SpecOpt{SEAM_TOL, nullptr, nullptr},
+                    nullptr);
 }
 
 int semicrf_read_status(const void* workspace, hipStream_t stream) {

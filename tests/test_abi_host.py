@@ -190,3 +190,15 @@ def test_argument_validation_returns_before_any_launch(native):
     assert lib.semicrf_prefix(p, p, 1, 4, 2, n, p, need, n) == 1
     assert lib.semicrf_prefix(p, p, 1, 4, 2, n, p, need - 1, p) == 2
 
+
+def test_static_scratch_limit_is_checked_before_any_launch(native):
+    """semicrf_logz_static: shapes whose log Z workspace exceeds the static array are
+    refused with SEMICRF_ERR_WORKSPACE, before the device is touched."""
+    lib = native.load()
+    p, n = ctypes.c_void_p(0x1000), None
+    assert lib.semicrf_workspace_bytes(0, 1, 1_000_000, 6, 200, 0) > native.STATIC_SCRATCH_BYTES
+    assert lib.semicrf_logz_static(p, p, p, p, 1, 1_000_000, 6, 200, 0, n, p) == 2
+    assert lib.semicrf_logz_static(p, p, p, p, 1, 4, 2, 2, 0, n, n) == 1
+    assert lib.semicrf_logz_static(n, p, p, p, 1, 4, 2, 2, 0, n, p) == 1
+    assert lib.semicrf_logz_static(p, p, p, p, 1, 4, 2, 2, -1, n, p) == 1
+    assert lib.semicrf_workspace_bytes(0, 4, 100_000, 6, 200, 0) <= native.STATIC_SCRATCH_BYTES
