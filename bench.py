@@ -1,24 +1,25 @@
 #!/usr/bin/env python3
 """Throughput of the streaming semi-CRF hot path on one MI355X.
 
-One step = one pass of every hot-path stage over one batch of the genomic
-workload (B=4, T=100,000, K=200, C=6, synthetic, seeded): semicrf_backward
-(centring + prefix scan, forward and backward checkpoint sweeps, span recompute,
-segment posteriors, marginals and gradients, log Z) and semicrf_viterbi (prefix
-scan, max-plus sweep, backtrace), issued on two streams: the two calls are
-independent and their sweeps occupy few compute units, so they run side by side.  Inputs are resident in HBM before the
-timed region; W warm-up steps, then K timed steps between two device
-synchronisations.  Prints one JSON line.
+One step = one pass of every hot-path stage over one batch of the genomic workload
+(B=4, T=100,000, K=200, C=6, synthetic, seeded, checkpoint interval ceil(sqrt(TK)) =
+4,473): semicrf_backward (centring + prefix scan, the checkpoint spans of both directions
+swept at once, seam check, segment posteriors, marginals and gradients, log Z) and
+semicrf_viterbi (prefix scan, max-plus spans, seam check, backtrace), issued on two
+streams: the calls are independent and each keeps part of the chip busy.  Inputs are
+resident in HBM before the timed region; W warm-up steps, then K timed steps between two
+device synchronisations.  Prints one JSON line.
 
-The roofline object describes the dominant kernel (the checkpoint sweep pair,
-timed live with events recorded by the library on the stream it launches on):
-algorithmic transcendental operations per launch / its mean duration, against the
-chip's exp2/log2 issue rate (256 CUs x 32 lanes/clock x 2.4 GHz: transcendentals
-issue at half the 64 lanes/clock of plain fp32 ops on gfx950).  Its HBM traffic comes
-from FETCH_SIZE / WRITE_SIZE counter runs calibrated on a plain copy; it is reported
-only while the kernel source is the one those counters were taken on.  The centring +
-prefix scan is also reported against HBM bandwidth on a shape larger than the
-256 MB last-level cache.
+roofline: the dominant kernel of the fwd+bwd pass is the launch that sweeps every
+checkpoint span of both directions (k_lse_round in span mode), timed live with the events
+the library records on the stream it launches on.  Its algorithmic work is the factored
+recurrence, (K*C + C^2) multiply-adds per position and direction (2 flops each, fp32), over
+every position of both directions; the burn-in positions the spans add are reported beside
+it.  The peak is the chip's fp32 vector rate (157.3 TFLOP/s: 256 CUs x 2.4 GHz x 256
+flop/clock); the plain v_fma_f32 and v_exp_f32 rates measured on the same chip by
+libsemicrf_peak.so are reported with it, and the VALU / transcendental instruction counts of
+the launch from rocprofv3 counter runs (kept while the kernel sources match the ones the
+counters were taken on).  HBM traffic likewise from FETCH_SIZE / WRITE_SIZE runs.
 """
 
 from __future__ import annotations
@@ -36,15 +37,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 CONFIG = 2                       # genomic: B=4, T=1e5, K=200, C=6
-PEAK_TRANS_PER_S = 256 * 32 * 2.4e9     # exp2/log2 issue: half of 64 lanes/clock per CU
+PEAK_FP32_FLOPS = 157.3e12       # MI355X fp32 vector: 256 CUs x 2.4 GHz x 256 flop/clock
 PEAK_HBM_BPS = 8.0e12
-# HBM bytes per checkpoint-sweep launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per
-# dispatch, scaled by 2.0 / 1.0, what the counters read for a 1 GiB copy), valid for the
-# kernel sources with this SHA-256 (of their concatenation, in this order)
+CLOCK_HZ = 2.4e9
+N_CU = 256
+# Counter runs of the span-sweep launch at the bench shape (rocprofv3 --pmc, summarised in
+# profiles/counters_k_lse_round_spans_genomic_B4_T1e5_K200_C6.md): instructions per
+# dispatch, and HBM bytes (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, the factors a 1 GiB device
+# copy reads), valid for the kernel sources with this SHA-256 (of their concatenation, in
+# this order).  Empty until counters are taken on the current sources.
 SWEEP_SRCS = [os.path.join(ROOT, "semi_markov_crf_amd", "csrc", f)
-              for f in ("sweep_lse_round.h", "sweep_lse_kernel.h", "ring.h", "common.h")]
-SWEEP_TRAFFIC = {"sha256": "80e4448cf00fc0a04cf04d3cfa50108d320defcbb64f09c74720172186c70928",
-                 "bytes": (19112.97 * 2.0 + 840.0 * 1.0) * 1024}
+              for f in ("sweep_lse_round.h", "sweep_lse_kernel.h", "ring.h", "common.h",
+                        "internal.h")]
+SWEEP_COUNTERS = {"sha256": "68df8d9b7c75e9ed15071dc9150fc6a5825ad0494f51c6407d985900e98ac0d6",
+                  "delta": 4473, "valu": 174_879_792, "trans": 3_961_632,
+                  "hbm_bytes": (20_993 * 2.0 + 79_163 * 1.0) * 1024}
+
+
+def sources_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def hip_runtime():
@@ -85,18 +100,58 @@ class EventSet:
                 self.hip.hipEventDestroy(a[i])
 
 
-def cpu_baseline(w, sample_positions):
-    """The fp64 oracle (untuned) on one host core: forward, backward, posteriors and
-    Viterbi over the first `sample_positions` positions of sequence 0."""
+def measured_peaks():
+    """Plain v_fma_f32, v_exp_f32 and interleaved rates of this chip (lane operations/s)."""
+    path = os.path.join(ROOT, "semi_markov_crf_amd", "libsemicrf_peak.so")
+    lib = ctypes.CDLL(path)
+    lib.semicrf_peak_rates.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    out = (ctypes.c_double * 3)()
+    if lib.semicrf_peak_rates(4096, 3, out) != 0:
+        raise RuntimeError("semicrf_peak_rates failed")
+    return {"fma_f32_lane_ops_per_s": out[0], "exp_f32_lane_ops_per_s": out[1],
+            "exp_plus_fma_lane_ops_per_s": out[2],
+            "fma_f32_per_cu_clock": out[0] / (N_CU * CLOCK_HZ),
+            "exp_f32_per_cu_clock": out[1] / (N_CU * CLOCK_HZ)}
+
+
+def _oracle_job(args):
     import oracle
+    em_b, n, trans, dur, K = args
     t0 = time.perf_counter()
-    oracle.sequence(w.em[0], sample_positions, w.trans, w.dur, w.K, want_viterbi=True,
-                    want_grads=True)
-    dt = time.perf_counter() - t0
-    return {"value": sample_positions / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+    oracle.sequence(em_b, n, trans, dur, K, want_viterbi=True, want_grads=True)
+    return time.perf_counter() - t0
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, sample_positions):
+    """The fp64 oracle, untuned: forward, backward, posteriors and Viterbi over the first
+    `sample_positions` positions of every sequence, one process per sequence."""
+    import multiprocessing as mp
+    usable = len(os.sched_getaffinity(0))
+    workers = max(1, min(w.B, usable))
+    jobs = [(w.em[b], sample_positions, w.trans, w.dur, w.K) for b in range(w.B)]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        per_seq = pool.map(_oracle_job, jobs)
+    wall = time.perf_counter() - t0
+    pos = w.B * sample_positions
+    return {"value": pos / wall, "unit": "positions/s", "cores": workers, "kind": "oracle",
             "sample": f"fwd+bwd+posteriors+viterbi over positions [0, {sample_positions}) of "
-                      f"sequence 0 of the genomic workload, fp64 NumPy, one process",
-            "seconds": dt}
+                      f"each of the {w.B} genomic sequences, fp64 NumPy, one process per "
+                      f"sequence",
+            "seconds": wall, "seconds_per_sequence": per_seq,
+            "host": {"cpu_model": cpu_model(), "cpu_count": os.cpu_count(),
+                     "usable_cores": usable}}
 
 
 def _time_ms(fn, d, reps):
@@ -114,10 +169,44 @@ def _time_ms(fn, d, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def config_timings(crf, d):
+    """The other configurations: backward (log Z and every gradient), Viterbi and log Z
+    alone, positions/s and nominal edges/s (B*T*K*C^2 per pass)."""
+    import torch
+
+    import workloads
+    out = {}
+    for i in (1, 3, 4):
+        w = workloads.make(i)
+        em, lengths, trans, dur = (torch.from_numpy(a).to(d) for a in
+                                   (w.em, w.lengths, w.trans, w.dur))
+        wsb = torch.empty(crf.workspace_bytes(crf.OP_BACKWARD, w.B, w.T, w.C, w.K),
+                          dtype=torch.uint8, device=d)
+        wsv = torch.empty(crf.workspace_bytes(crf.OP_VITERBI, w.B, w.T, w.C, w.K),
+                          dtype=torch.uint8, device=d)
+        wsl = torch.empty(crf.workspace_bytes(crf.OP_LOGZ, w.B, w.T, w.C, w.K),
+                          dtype=torch.uint8, device=d)
+        reps = 2 if i == 3 else 5
+        mb = _time_ms(lambda: crf.backward(em, lengths, trans, dur, workspace=wsb), d, reps)
+        mv = _time_ms(lambda: crf.viterbi(em, lengths, trans, dur, workspace=wsv), d, reps)
+        ml = _time_ms(lambda: crf.logz(em, lengths, trans, dur, workspace=wsl), d, reps)
+        pos = w.positions()
+        edges = w.B * w.T * w.K * w.C * w.C
+        out[w.name] = {"B": w.B, "T": w.T, "K": w.K, "C": w.C, "positions": pos,
+                       "backward_ms": mb, "viterbi_ms": mv, "logz_ms": ml,
+                       "fwd_bwd_positions_per_s": pos / (mb * 1e-3),
+                       "viterbi_positions_per_s": pos / (mv * 1e-3),
+                       "logz_positions_per_s": pos / (ml * 1e-3),
+                       "fwd_bwd_edges_per_s_nominal": edges / (mb * 1e-3),
+                       "path": "spans swept at once" if w.C <= 16 else "sweeps in order"}
+        del wsb, wsv, wsl
+    return out
+
+
 def extras(crf, w, em, lengths, trans, dur, d):
-    """Timings beyond the step: the training loss of gold segmentations and the backward
-    pass with boundary projections (both at the genomic shape), and the genome-scale
-    long-duration workload (B=1, T=10^6, K=2000, C=6: backward and Viterbi)."""
+    """Timings beyond the step: the training loss of gold segmentations, the backward
+    pass with boundary projections, log Z alone (all at the genomic shape), and the
+    genome-scale long-duration workload (B=1, T=10^6, K=2000, C=6)."""
     import numpy as np
     import torch
 
@@ -132,14 +221,15 @@ def extras(crf, w, em, lengths, trans, dur, d):
     ms0 = _time_ms(lambda: crf.backward(em, lengths, trans, dur, workspace=ws), d, 3)
     out["nll"] = {"ms": ms, "positions_per_s": pos / (ms * 1e-3), "backward_alone_ms": ms0,
                   "what": "semicrf_nll (backward pass + gold-segmentation kernels), genomic shape"}
-    # inference alone, and an autograd-style forward then backward as two calls
-    ml = _time_ms(lambda: crf.logz(em, lengths, trans, dur, workspace=ws), d, 3)
-    mlb = _time_ms(lambda: (crf.logz(em, lengths, trans, dur, workspace=ws),
+    wsl = torch.empty(crf.workspace_bytes(crf.OP_LOGZ, w.B, w.T, w.C, w.K), dtype=torch.uint8,
+                      device=d)
+    ml = _time_ms(lambda: crf.logz(em, lengths, trans, dur, workspace=wsl), d, 3)
+    mlb = _time_ms(lambda: (crf.logz(em, lengths, trans, dur, workspace=wsl),
                             crf.backward(em, lengths, trans, dur, workspace=ws)), d, 3)
     out["logz"] = {"ms": ml, "positions_per_s": pos / (ml * 1e-3),
                    "logz_then_backward_ms": mlb,
-                   "what": "semicrf_logz alone (one forward sweep per sequence), and semicrf_logz "
-                           "followed by semicrf_backward, genomic shape"}
+                   "what": "semicrf_logz alone (inference), and semicrf_logz followed by "
+                           "semicrf_backward, genomic shape"}
     g = torch.Generator(device="cpu").manual_seed(11)
     ps = torch.randn(em.shape, generator=g).to(d)
     pe = torch.randn(em.shape, generator=g).to(d)
@@ -148,7 +238,7 @@ def extras(crf, w, em, lengths, trans, dur, d):
     out["projections"] = {"ms": ms, "positions_per_s": pos / (ms * 1e-3),
                           "what": "semicrf_backward with proj_start / proj_end N(0,1), their "
                                   "gradients and the boundary probabilities, genomic shape"}
-    del ws
+    del ws, wsl
     x = workloads.long_duration()
     xe, xl, xt, xd = (torch.from_numpy(a).to(d) for a in (x.em, x.lengths, x.trans, x.dur))
     wsb = torch.empty(crf.workspace_bytes(crf.OP_BACKWARD, x.B, x.T, x.C, x.K), dtype=torch.uint8,
@@ -165,18 +255,30 @@ def extras(crf, w, em, lengths, trans, dur, d):
     return out
 
 
+def span_positions(lengths, delta, warm):
+    """Positions the span sweeps execute per direction: every span from its burn-in start
+    (or 0) to its end."""
+    n = 0
+    for L in lengths:
+        L = int(L)
+        for t0 in range(0, L, delta):
+            n += min(L, t0 + delta) - max(0, t0 - warm)
+    return n
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--delta", type=int, default=0, help="checkpoint interval (0: ceil(sqrt(TK)))")
-    ap.add_argument("--cpu-sample", type=int, default=40_000)
+    ap.add_argument("--cpu-sample", type=int, default=12_000,
+                    help="positions of every sequence the oracle baseline runs over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-scan-roofline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the timings of the training loss, the projections and the "
-                         "long-duration workload")
+                    help="skip the other configurations, the training loss, the projections "
+                         "and the long-duration workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
@@ -209,28 +311,33 @@ def main():
     score = torch.empty(B, dtype=torch.float32, device=d)
     labels = torch.empty((B, T), dtype=torch.int32, device=d)
     seg = torch.empty((B, T), dtype=torch.uint8, device=d)
-    # semicrf_backward and semicrf_viterbi are independent and each keeps only 2B (resp. B)
-    # compute units busy in its sweeps, so they run on two streams (default priority)
+    rep_b = torch.empty(B, dtype=torch.int32, device=d)
+    rep_v = torch.empty(B, dtype=torch.int32, device=d)
+    bound_b = torch.empty(B, dtype=torch.float32, device=d)
+    # semicrf_backward and semicrf_viterbi are independent: two streams (default priority)
     main = torch.cuda.current_stream(d)
     s_b, s_v = torch.cuda.Stream(d), torch.cuda.Stream(d)
     stream_b, stream_v = s_b.cuda_stream, s_v.cuda_stream
     stream = main.cuda_stream
 
-    def _opt(ev):
-        if ev is None:
-            return None
-        return ctypes.byref(_native.options(events=ctypes.cast(ev, ctypes.c_void_p).value))
+    def _opt(ev, rep, bound=None):
+        o = _native.options(seam_repairs=rep.data_ptr(),
+                            seam_bound=None if bound is None else bound.data_ptr())
+        if ev is not None:
+            o.events = ctypes.cast(ev, ctypes.c_void_p).value
+        return ctypes.byref(o)
 
     def step(ev_b=None, ev_v=None):
         rc = lib.semicrf_backward_ex(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
                                      dur.data_ptr(), B, T, C, K, args.delta, stream_b,
                                      ws_b.data_ptr(), nb, None, g_em.data_ptr(), g_tr.data_ptr(),
-                                     g_du.data_ptr(), mu.data_ptr(), lz.data_ptr(), _opt(ev_b))
+                                     g_du.data_ptr(), mu.data_ptr(), lz.data_ptr(),
+                                     _opt(ev_b, rep_b, bound_b))
         _native.check("semicrf_backward", rc)
         rc = lib.semicrf_viterbi_ex(em.data_ptr(), lengths.data_ptr(), trans.data_ptr(),
                                     dur.data_ptr(), B, T, C, K, stream_v, ws_v.data_ptr(), nv,
                                     score.data_ptr(), labels.data_ptr(), seg.data_ptr(),
-                                    _opt(ev_v))
+                                    _opt(ev_v, rep_v))
         _native.check("semicrf_viterbi", rc)
 
     torch.cuda.synchronize(d)          # inputs are resident before either stream starts
@@ -264,24 +371,34 @@ def main():
     value = positions / (ms_step * 1e-3)
     bwd_ms = float(sb.sum(axis=1).mean())
     vit_ms = float(sv.sum(axis=1).mean())
-    # dominant kernel: both checkpoint sweeps in one launch (stage 1), or the span
-    # recompute when delta >= T
-    nspans = -(-T // delta)
-    dom_stage = 1 if nspans > 1 else 2
-    dom_ms = float(sb[:, dom_stage].mean())
-    trans_per_pos = K * C + C * C + 2 * C          # exp2 of the K*C and C*C terms, 2C log2
-    algo = 2 * positions * trans_per_pos           # both directions
+    # dominant kernel of the fwd+bwd pass: the span sweeps of both directions (stage 1, one
+    # launch)
+    dom_ms = float(sb[:, 1].mean())
+    flop_per_pos = 2 * (K * C + C * C)               # multiply-adds of the factored recurrence
+    algo = 2 * positions * flop_per_pos              # both directions
     achieved = algo / (dom_ms * 1e-3)
-    busy_cus = 2 * B if dom_stage == 1 else min(256, 2 * B * nspans)
-    # algorithmic bytes of the sweep pair: S read once per direction, checkpoints written
-    nck = sum(max(0, (int(L) - 1) // delta) for L in w.lengths)
-    algo_bytes = 2 * B * (T + 1) * C * 8 + 2 * nck * (K * C * 4 + C * 8 + C * 4 + 8)
-    digest = hashlib.sha256()
-    for src in SWEEP_SRCS:
-        with open(src, "rb") as f:
-            digest.update(f.read())
-    same_src = digest.hexdigest() == SWEEP_TRAFFIC["sha256"]
-    traffic = SWEEP_TRAFFIC["bytes"] if (same_src and dom_stage == 1 and delta == 4473) else None
+    warm = max(3 * K, 64)
+    executed_pos = 2 * span_positions(w.lengths, delta, warm)
+    nspans = -(-T // delta)
+    workgroups = 2 * B * nspans
+    busy_cus = min(N_CU, workgroups)
+    peaks = measured_peaks()
+    same_src = sources_sha(SWEEP_SRCS) == SWEEP_COUNTERS.get("sha256")
+    counted = None
+    traffic = None
+    if same_src and delta == SWEEP_COUNTERS.get("delta"):
+        c = SWEEP_COUNTERS
+        t = dom_ms * 1e-3
+        counted = {
+            "valu_insts_per_launch": c["valu"], "trans_f32_insts_per_launch": c["trans"],
+            "valu_lane_ops_per_s": c["valu"] * 64 / t,
+            "trans_lane_ops_per_s": c["trans"] * 64 / t,
+            "valu_frac_of_measured_fma_peak": c["valu"] * 64 / t / peaks["fma_f32_lane_ops_per_s"],
+            "trans_frac_of_measured_exp_peak": c["trans"] * 64 / t / peaks["exp_f32_lane_ops_per_s"],
+            "valu_issue_frac_busy_cus": c["valu"] / t / (busy_cus * CLOCK_HZ *
+                                                          peaks["fma_f32_per_cu_clock"] / 64),
+            "source": "profiles/counters_k_lse_round_spans_genomic_B4_T1e5_K200_C6.md"}
+        traffic = c.get("hbm_bytes")
 
     out = {
         "metric": "fwd+bwd positions/s at T=1e5,K=200,C=6; % of VALU-exp/HBM roofline",
@@ -302,31 +419,36 @@ def main():
                    "B": B, "T": T, "K": K, "C": C, "delta": delta, "parallelism": "none (1 GPU)"},
         "roofline": {
             "bound": "alu",
-            "kernel": "k_lse_round (checkpoint sweeps: forward and backward of every sequence, "
-                      "one workgroup each, one launch)",
+            "kernel": "k_lse_round, span mode: every checkpoint span of both directions of "
+                      "every sequence at once, one workgroup each, one launch",
             "achieved": achieved / 1e12,
-            "peak": PEAK_TRANS_PER_S / 1e12,
-            "unit": "Ttrans/s",
-            "frac": achieved / PEAK_TRANS_PER_S,
+            "peak": PEAK_FP32_FLOPS / 1e12,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_FLOPS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": algo_bytes,
             "algorithmic_per_launch": algo,
+            "algorithmic_unit": f"fp32 flop: 2 directions x positions x 2 x (K*C + C^2) = "
+                                f"2 x {positions} x {flop_per_pos}",
+            "executed_positions_per_launch": executed_pos,
             "launch_ms": dom_ms,
+            "workgroups": workgroups,
             "busy_cus": busy_cus,
-            "frac_of_busy_cus": achieved / (PEAK_TRANS_PER_S * busy_cus / 256),
+            "frac_of_busy_cus": achieved / (PEAK_FP32_FLOPS * busy_cus / N_CU),
+            "measured_peaks": peaks,
+            "counted": counted,
         },
         "stages_ms": {
-            "backward": dict(zip(["prefix", "ckpt_sweeps", "span_recompute", "posteriors",
-                                  "marginals_grads"], sb.mean(axis=0).round(4).tolist())),
-            "viterbi": dict(zip(["prefix", "maxplus_sweep", "backtrace"],
+            "backward": dict(zip(["prefix", "span_sweeps", "seam_check_and_repair",
+                                  "posteriors", "marginals_grads"],
+                                 sb.mean(axis=0).round(4).tolist())),
+            "viterbi": dict(zip(["prefix", "maxplus_spans_seam_repair", "backtrace"],
                                 sv.mean(axis=0).round(4).tolist())),
         },
+        "seam_repairs": {"backward": int(rep_b.sum().item()), "viterbi": int(rep_v.sum().item())},
+        "seam_bound_max": float(bound_b.max().item()),
         "fwd_bwd_positions_per_s": positions / (bwd_ms * 1e-3),
         "viterbi_positions_per_s": positions / (vit_ms * 1e-3),
         "edges_per_s_nominal": positions * K * C * C / (bwd_ms * 1e-3),
-        # recurrence passes over every position in one backward call: the forward and the
-        # mirrored checkpoint sweeps, then the span recompute in both directions
-        "recurrence_passes": 4,
         "wall_s_timed_region": wall,
     }
 
@@ -349,8 +471,8 @@ def main():
             torch.cuda.synchronize(d)
             times.append(e0.elapsed_time(e1))
         ms = min(times[1:])
-        nbytes = Bs * Ts * C * (4 + 4 + 8)        # em read twice (mean, then scan), S written
-        # for scale: a plain device copy of S (read and write 8 B per element)
+        nbytes = Bs * Ts * C * (4 + 4 + 8)        # em read twice (mean, then scan), S written fp64
+        nbytes12 = Bs * Ts * C * 12               # the same with S in fp32
         S_copy = torch.empty_like(S_big)
         ctimes = []
         for _ in range(4):
@@ -364,10 +486,12 @@ def main():
                                 "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": 8000.0,
                                 "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / PEAK_HBM_BPS,
                                 "ms": ms, "algorithmic_bytes": nbytes,
+                                "frac_on_12C_bytes": nbytes12 / (ms * 1e-3) / PEAK_HBM_BPS,
                                 "device_copy_GBps": 2 * S_big.numel() * 8 / (cms * 1e-3) / 1e9}
         del em_big, S_big, S_copy, ws_s
 
     if not args.no_extras:
+        out["configs"] = config_timings(crf, d)
         out["extras"] = extras(crf, w, em, lengths, trans, dur, d)
 
     if not args.no_cpu_baseline:

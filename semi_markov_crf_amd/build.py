@@ -1,7 +1,8 @@
 """Build the gfx950 shared library ``libsemicrf.so`` in-tree with hipcc.
 
 Every call compiles all sources again (object files go to ``_build/``), then links
-``semi_markov_crf_amd/libsemicrf.so``.  Usage: ``python -m semi_markov_crf_amd.build``.
+``semi_markov_crf_amd/libsemicrf.so`` and the peak-rate microbenchmark
+``libsemicrf_peak.so`` that bench.py uses.  Usage: ``python -m semi_markov_crf_amd.build``.
 """
 
 from __future__ import annotations
@@ -17,6 +18,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsemicrf.so")
+# the peak-rate microbenchmark behind bench.py's roofline, a library of its own
+PEAK_LIB = os.path.join(HERE, "libsemicrf_peak.so")
+PEAK_SOURCES = ["peak.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -48,18 +52,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(PEAK_SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES + PEAK_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PEAK_LIB)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+        print(f"built {LIB} and {PEAK_LIB}", file=sys.stderr)
     return LIB
 
 
