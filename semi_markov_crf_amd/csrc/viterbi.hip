@@ -158,45 +158,63 @@ hipError_t launch_vit_final(const double* vfin, const double* off, const int* Le
     return hipGetLastError();
 }
 
-// grid (nch, B, 2 parts), block BT_THREADS, dynamic LDS (W + K) * C * 4 bytes.
+// grid (nch, B, 2 parts), block BT_THREADS, dynamic LDS W * C * 4 bytes.
 // tr: [2][B][nch][K*C], the entry node of chunk j+1 reached from each entry node of chunk
 // j, or -1 when the chain ends inside chunk j (or the entry is not a valid end).
+// Every node (t, c) of the chunk first points at its successor (t - k, c') when that lies
+// in the chunk, else holds where the chain goes next: the entry node of chunk j+1, or the
+// end of the chain.  ceil(log2 W) rounds of pointer jumping (n -> next[next[n]]) then take
+// every node to where its chain leaves the chunk.  The rounds update in place: any value
+// a lane reads is a node further along the same chain, so the result is the same and the
+// distance covered at least doubles per round.
 __global__ __launch_bounds__(BT_THREADS) void k_bt_transfer(const uint32_t* __restrict__ bp,
                                                            const int* __restrict__ split, int B,
                                                            int T, int C, int K, int W, int nch,
                                                            int32_t* __restrict__ tr) {
-    extern __shared__ uint32_t tile[];
-    const int j = blockIdx.x, b = blockIdx.y, part = blockIdx.z;
+    extern __shared__ int nxt[];                         // [W * C]: node n = (t - lo) * C + c
+    const int j = blockIdx.x, b = blockIdx.y, part = blockIdx.z, tid = threadIdx.x;
     int E, c0;
     part_of(split, b, part, &E, &c0);
     const int KC = K * C;
     int32_t* trj = tr + (((size_t)part * B + b) * nch + j) * KC;
     const int hi = E + 1 - j * W;
     if (hi <= 0) {
-        for (int e = threadIdx.x; e < KC; e += BT_THREADS) trj[e] = -1;
+        for (int e = tid; e < KC; e += BT_THREADS) trj[e] = -1;
         return;
     }
     const int lo = max(0, hi - W);
-    const int base = max(0, lo - K);
-    stage_rows(tile, bp + ((size_t)part * B + b) * (T + 1) * C, base, hi, C);
+    const int rows = hi - lo;                            // <= W
+    const uint32_t* bpb = bp + ((size_t)part * B + b) * (T + 1) * C;
+    // successors: >= 0 a node of the chunk; -1 the chain ends; -(x + 2) it enters chunk
+    // j+1 at entry node x
+    for (int n = tid; n < rows * C; n += BT_THREADS) {
+        const int t = lo + n / C, c = n - (n / C) * C;
+        int v = -1;
+        if (t >= 1) {
+            const int k = (int)(bpb[(size_t)t * C + c] & 0xFFFFu);
+            const int s = t - k;
+            if (s > 0 && k >= 1 && k <= K) {
+                const int cp = min((int)(bpb[(size_t)s * C + c] >> 16), C - 1);
+                v = s >= lo ? (s - lo) * C + cp : -((lo - 1 - s) * C + cp + 2);
+            }
+        }
+        nxt[n] = v;
+    }
     __syncthreads();
-    for (int e = threadIdx.x; e < KC; e += BT_THREADS) {
+    for (int span = 1; span < rows; span *= 2) {
+        for (int n = tid; n < rows * C; n += BT_THREADS) {
+            const int v = nxt[n];
+            if (v >= 0) nxt[n] = nxt[v];
+        }
+        __syncthreads();
+    }
+    for (int e = tid; e < KC; e += BT_THREADS) {
         const int r = e / C;
-        int t = hi - 1 - r, c = e - r * C;
+        const int t = hi - 1 - r, c = e - r * C;
         int out = -1;
         if (t >= lo && t >= 1) {
-            while (true) {
-                const int k = (int)(tile[(t - base) * C + c] & 0xFFFFu);
-                const int s = t - k;
-                if (s <= 0 || k < 1 || k > K) break;        // chain ends (or corrupt entry)
-                const int cp = min((int)(tile[(s - base) * C + c] >> 16), C - 1);
-                if (s < lo) {                                // leaves the chunk
-                    out = (lo - 1 - s) * C + cp;
-                    break;
-                }
-                t = s;
-                c = cp;
-            }
+            const int v = nxt[(t - lo) * C + c];
+            out = v <= -2 ? -v - 2 : -1;
         }
         trj[e] = out;
     }
@@ -268,18 +286,26 @@ __global__ __launch_bounds__(BT_THREADS) void k_bt_fill(const uint32_t* __restri
     }
     __syncthreads();
     const int n = s_nseg;
-    for (int i = tid; i < n; i += BT_THREADS) {
-        const int s = segs[3 * i], t = segs[3 * i + 1], c = segs[3 * i + 2];
+    if (n == 0) return;
+    // the chunk's segments cover [segs[n-1].start, segs[0].end) without gaps, in
+    // decreasing order: one lane per position finds its segment by bisection
+    const int u0 = segs[3 * (n - 1)], u1 = segs[1];
+    for (int u = u0 + tid; u < u1; u += BT_THREADS) {
+        int a = 0, z = n - 1;                            // segs[a].start > u >= segs[z].start
+        while (a < z) {
+            const int m = (a + z) >> 1;
+            if (segs[3 * m] <= u) z = m;
+            else a = m + 1;
+        }
+        const int s = segs[3 * a], c = segs[3 * a + 2];
         if (part == 0) {
-            for (int u = s; u < t; ++u) {
-                lab[u] = c;
-                ss[u] = (u == s) ? 1 : 0;
-            }
+            lab[u] = c;
+            ss[u] = (u == s) ? 1 : 0;
         } else {
-            for (int u = L - t; u < L - s; ++u) {
-                lab[u] = c;
-                ss[u] = (u == L - t) ? 1 : 0;
-            }
+            // part 1 walks the mirrored sequence: [s, t) covers original [L - t, L - s)
+            const int t = segs[3 * a + 1];
+            lab[L - 1 - u] = c;
+            ss[L - 1 - u] = (L - 1 - u == L - t) ? 1 : 0;
         }
     }
 }
@@ -307,14 +333,17 @@ hipError_t launch_backtrace(const uint32_t* bp, const int* split, int B, int T, 
                             hipStream_t stream) {
     const int W = backtrace_chunk(C, K);
     const int nch = backtrace_chunks(T, C, K);
-    const size_t lds_t = (size_t)(W + K) * C * sizeof(uint32_t);
-    const size_t lds_f = lds_t + (size_t)3 * W * sizeof(int);
-    if (lds_f > 150 * 1024) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_bt_transfer, dim3(nch, B, 2), dim3(BT_THREADS), lds_t, stream, bp, split,
-                       B, T, C, K, W, nch, tr);
-    hipLaunchKernelGGL(k_bt_compose, dim3(B, 2), dim3(64), 0, stream, tr, split, B, C, K, nch, ent);
-    hipLaunchKernelGGL(k_bt_fill, dim3(nch, B, 2), dim3(BT_THREADS), lds_f, stream, bp, split, ent,
-                       B, T, C, K, W, nch, labels, seg_start);
+    const size_t lds_t = (size_t)W * C * sizeof(int);
+    const size_t lds_f = (size_t)(W + K) * C * sizeof(uint32_t) + (size_t)3 * W * sizeof(int);
+    if (lds_f > 150 * 1024 || lds_t > 150 * 1024) return hipErrorInvalidValue;
+    // the decode ends at (L, final label) in one direction: part 1 is empty
+    const int parts = 1;
+    hipLaunchKernelGGL(k_bt_transfer, dim3(nch, B, parts), dim3(BT_THREADS), lds_t, stream, bp,
+                       split, B, T, C, K, W, nch, tr);
+    hipLaunchKernelGGL(k_bt_compose, dim3(B, parts), dim3(64), 0, stream, tr, split, B, C, K, nch,
+                       ent);
+    hipLaunchKernelGGL(k_bt_fill, dim3(nch, B, parts), dim3(BT_THREADS), lds_f, stream, bp, split,
+                       ent, B, T, C, K, W, nch, labels, seg_start);
     return hipGetLastError();
 }
 
