@@ -198,7 +198,7 @@ def config_timings(crf, d):
                        "viterbi_positions_per_s": pos / (mv * 1e-3),
                        "logz_positions_per_s": pos / (ml * 1e-3),
                        "fwd_bwd_edges_per_s_nominal": edges / (mb * 1e-3),
-                       "path": "spans swept at once" if w.C <= 16 else "sweeps in order"}
+                       "kernel": "round kernel" if w.C <= 16 else "one barrier per position"}
         del wsb, wsv, wsl
     return out
 

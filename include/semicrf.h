@@ -175,9 +175,9 @@ typedef struct semicrf_options {
      *   logz:     0 centring + prefix scan, 1 forward sweep
      *   backward: 0 centring + prefix scan, 1 the checkpoint spans of both directions
      *             with their per-position values, 2 seam check and repair, 3 segment
-     *             posteriors, 4 node marginals and gradient reductions (for C > 16: 1
-     *             checkpoint sweeps, 2 span recompute)
-     *   viterbi:  0 centring + prefix scan, 1 max-plus sweep, 2 combine and backtrace */
+     *             posteriors, 4 node marginals and gradient reductions
+     *   viterbi:  0 centring + prefix scan, 1 max-plus checkpoint spans with the seam
+     *             check, repair and final label, 2 backtrace */
     hipEvent_t* events;
     /* Checkpoint spans swept at once.  The sweeps are sequential in the position; every
      * span of delta positions is swept at the same time instead, starting 3K positions
@@ -187,7 +187,7 @@ typedef struct semicrf_options {
      * before it, takes the constant from them and accepts the seam when every entry is
      * within seam_tolerance of it (natural-log units; 0 = the default, 1e-4).  From the
      * first seam that is not accepted the sequence is swept again in order, exactly as a
-     * single sweep would.  C <= 16; for C > 16 the sweeps run in order.
+     * single sweep would.
      *   seam_bound   [B] float32 or NULL: per sequence, the sum over both directions'
      *                accepted seams of the largest deviation from the constant; no value
      *                of the call moves by more than it (beyond rounding) from the values

@@ -314,17 +314,9 @@ static int run_logz(const float* em, const int32_t* lengths, const float* trans,
     STAGE(1);
     const SweepCfg cfg = choose_sweep(C, K);
     SweepLaunch a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
-    if (cfg.split) {
-        // every checkpoint span at once, then the seam check
-        a.write_xa = 0;
-        if ((rc = run_spans(cfg, a, 1, lo, workspace, so, stream, nullptr, -1))) return rc;
-    } else {
-        a.mode = MODE_FULL;
-        a.delta = T;
-        a.nspans = 1;
-        LAUNCH(launch_lse(cfg, a, 1, stream));
-        LAUNCH(launch_seam_report(nullptr, B, 0, so.bound, so.repairs, stream));
-    }
+    // every checkpoint span at once, then the seam check
+    a.write_xa = 0;
+    if ((rc = run_spans(cfg, a, 1, lo, workspace, so, stream, nullptr, -1))) return rc;
     LAUNCH(launch_write_logz(a.logz, B, log_z, stream));
     STAGE(2);
     return SEMICRF_OK;
@@ -352,26 +344,9 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
     a.XB = at<double>(workspace, lo.XB);
     a.AB = at<double>(workspace, lo.AB);
     a.write_xa = 1;
-    if (cfg.split) {
-        // every checkpoint span of both directions at once with its per-position values,
-        // then the seam check and the repair of failed seams
-        if ((rc = run_spans(cfg, a, 2, lo, workspace, so, stream, events, 2))) return rc;
-    } else {
-        if (lo.nspans > 1) {
-            // streaming sweeps in both directions at once: checkpoints every delta positions
-            a.mode = MODE_FULL;
-            a.write_ckpt = 1;
-            a.write_xa = 0;
-            LAUNCH(launch_lse(cfg, a, 2, stream));
-        }
-        STAGE(2);
-        // recompute every checkpoint span in parallel, writing the per-position values
-        a.mode = MODE_SPAN;
-        a.write_ckpt = 0;
-        a.write_xa = 1;
-        LAUNCH(launch_lse(cfg, a, 2, stream));
-        LAUNCH(launch_seam_report(nullptr, B, 0, so.bound, so.repairs, stream));
-    }
+    // every checkpoint span of both directions at once with its per-position values, then
+    // the seam check and the repair of failed seams
+    if ((rc = run_spans(cfg, a, 2, lo, workspace, so, stream, events, 2))) return rc;
     STAGE(3);
 
     MargArgs m{};
@@ -379,7 +354,7 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
     m.B = B; m.T = T; m.C = C; m.K = K;
     m.tile = lo.tm; m.ntiles = lo.ntm; m.kchunk = marg_kchunk(C, K);
     m.XF = a.XF; m.AF = a.AF; m.XB = a.XB; m.AB = a.AB; m.logz = a.logz;
-    m.off = cfg.split ? a.off : nullptr;
+    m.off = a.off;
     m.delta = lo.delta;
     m.nspans = lo.nspans;
     m.Dn = at<double>(workspace, lo.Dn);
@@ -442,7 +417,7 @@ static int run_viterbi(const float* em, const int32_t* lengths, const float* tra
     a.vcstar = at<int>(workspace, lo.vcstar);
     a.vwin = at<double>(workspace, lo.vwin);
     a.vfin = at<double>(workspace, lo.vfin);
-    if (cfg.split) {
+    {
         // every checkpoint span of the forward decode at once, the seam check (the frame
         // offsets, no log Z), the in-order repair from a failed seam, the final label
         a.mode = MODE_SPEC;
@@ -465,10 +440,6 @@ static int run_viterbi(const float* em, const int32_t* lengths, const float* tra
         LAUNCH(launch_vit_final(a.vfin, sa.off, a.Leff, B, C, a.delta, a.nspans, a.vscore,
                                 a.vcstar, stream));
         LAUNCH(launch_seam_report(sa.diag, B, 1, so.bound, so.repairs, stream));
-    } else {
-        a.mode = MODE_FULL;
-        LAUNCH(launch_maxplus(cfg, a, stream));
-        LAUNCH(launch_seam_report(nullptr, B, 0, so.bound, so.repairs, stream));
     }
     STAGE(2);
     int* split = at<int>(workspace, lo.split);

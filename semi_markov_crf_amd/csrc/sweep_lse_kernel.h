@@ -109,7 +109,7 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
     const bool writer = act && j == 0;       // one lane per label publishes
 
     int b, span, dir;
-    if (a.mode == MODE_FULL) {
+    if (a.mode == MODE_FULL || a.mode == MODE_REPAIR) {
         b = blockIdx.x; dir = blockIdx.y; span = 0;
     } else {
         span = blockIdx.x; b = blockIdx.y; dir = blockIdx.z;
@@ -117,12 +117,31 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
     const int Lr = a.Leff[b];
     const bool bad = Lr < 0;
     const int L = bad ? -Lr : Lr;
-    int t0 = 0, t1 = L;
-    if (a.mode == MODE_SPAN) {
-        t0 = span * a.delta;
-        if (t0 >= L) return;
-        t1 = min(L, t0 + a.delta);
+    // [tout, t1]: the positions this workgroup writes; t0: where its sweep starts (a
+    // speculative span runs a burn-in from t0 = tout - warm, or exactly from 0)
+    int t0 = 0, t1 = L, tout = 0;
+    const bool spec = a.mode == MODE_SPEC;
+    if (a.mode == MODE_SPAN || spec) {
+        tout = span * a.delta;
+        if (tout >= L) return;
+        t1 = min(L, tout + a.delta);
+        t0 = spec ? max(0, tout - a.warm) : tout;
+    } else if (a.mode == MODE_REPAIR) {
+        span = a.first_bad[dir * a.B + b];
+        if (span >= a.nspans) return;
+        tout = span * a.delta;
+        if (tout >= L) return;
+        t0 = tout;
     }
+    // seam windows (MODE_SPEC): head [hlo, tout] of every span but the first, tail [tlo, t1]
+    // of every span but the last
+    const int hlo = (spec && span > 0) ? tout - K + 1 : INT_MAX;
+    const int tlo = (spec && t1 < L) ? t1 - K + 1 : INT_MAX;
+    const size_t winrow = (((size_t)dir * a.B + b) * a.nspans + span) * K;
+    auto window = [&](int t, double av) {                 // writer lanes
+        if (t >= hlo && t <= tout) a.head[(winrow + t - hlo) * C + c] = av;
+        if (t >= tlo && t <= t1) a.tail[(winrow + t - tlo) * C + c] = av;
+    };
     const int RMASK = RS - 1;
     const int rowsN = (CH + 1) * C;           // staged S values per chunk and side
     constexpr bool MIR = LAY & SWEEP_MIRRORED;
@@ -252,6 +271,12 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
         Rn1 = act ? fmaxf((float)proj_s(0, c), NEG) : 0.0f;
         if (writer) put_all(0, Rn1);
         Rn2 = NEG;
+    } else if (spec) {
+        // burn-in start: every ring entry of positions t0-K+1 .. t0 equal (0 in log2)
+        if (act)
+            for (int q = j; q < K && t0 - q >= 0; q += G) put_all(t0 - q, 0.0f);
+        Rn1 = 0.0f;
+        Rn2 = (K >= 2 && t0 >= 1) ? 0.0f : NEG;
     } else {
         const size_t ck = ckrow + span;
         if (act)
@@ -262,8 +287,10 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
         Rn1 = a.ck_ring[(ck * K + 0) * C + cc];
         Rn2 = K >= 2 ? a.ck_ring[(ck * K + 1) * C + cc] : NEG;
     }
-    if (writer && a.write_xa)
+    if (writer && a.write_xa && t0 == tout)
         Aout[(outrow + (dir == 0 ? t0 : L - t0)) * C + c] = (Bc + (double)Rn1) * LN2;
+    if (writer && t0 == 0)   // window positions <= 0: position 0's value, nothing before it
+        for (int p = min(hlo, tlo); p <= 0; ++p) window(p, p == 0 ? (Bc + (double)Rn1) * LN2 : -1.0e300);
     float En1 = exp2_or_zero(Rn1), En2 = exp2_or_zero(Rn2);
 
     // ---------------------------------------------------------------- S staging
@@ -327,13 +354,14 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
         const int o = (tn & 1) * UP + c;
         *(writer ? p_sh + o : dummy + tid) = p;
         *(writer ? u_sh + o : dummy + tid) = hn + sigma;
-        if (a.write_xa && writer)
+        if (a.write_xa && writer && tn > tout)
             Xout[(outrow + (dir == 0 ? tn : L - tn)) * C + c] = (Sn + Bc + (double)sigma) * LN2;
     };
     publish(t0 + 1, Sbuf[cc], exp2_d(Sbuf[cc] + BH + (double)dmax), Qla, Qga);
     bulk(t0 + 2, Qla, Qga);
     double lz = 0.0;
-    int next_ck = (a.mode == MODE_FULL && a.write_ckpt) ? a.delta : INT_MAX;
+    // checkpoints: every delta positions (MODE_FULL), or at the end of a speculative span
+    int next_ck = (a.mode == MODE_FULL && a.write_ckpt) ? a.delta : (spec && t1 < L) ? t1 : INT_MAX;
     __syncthreads();
 
     // ---------------------------------------------------------------- main loop
@@ -471,8 +499,9 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
                     if constexpr (MIR) *(writer ? Erow + s0 + RS : dummy + tid) = Enew;
                 }
             }
-            if (a.write_xa && writer && t < t1)
+            if (a.write_xa && writer && t < t1 && t >= tout)
                 Aout[(outrow + (dir == 0 ? t : L - t)) * C + c] = (Bc + (double)Rnew) * LN2;
+            if (writer && t >= min(hlo, tlo)) window(t, (Bc + (double)Rnew) * LN2);
             Rn2 = Rn1; En2 = En1;
             Rn1 = Rnew; En1 = Enew;
             if (Qgc > NEG_HALF) Mref = Qgc;
@@ -501,7 +530,17 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
     }
 
     // ---------------------------------------------------------------- end of sequence
-    if (t1 == L && tid == 0) (dir == 0 ? a.logz : a.logz_b)[b] = bad ? nan_d() : lz * LN2;
+    if (t1 == L && tid == 0) {
+        if (spec) {
+            a.lzloc[dir * a.B + b] = lz * LN2;           // the seam check adds the offsets
+        } else {
+            // a repaired sweep continues in the frame of the span before the failed seam
+            const double base = a.mode == MODE_REPAIR
+                                    ? a.off[((size_t)dir * a.B + b) * a.nspans + span - 1]
+                                    : 0.0;
+            (dir == 0 ? a.logz : a.logz_b)[b] = bad ? nan_d() : lz * LN2 + base;
+        }
+    }
 }
 
 // ------------------------------------------------------------------ launch
@@ -538,7 +577,8 @@ static hipError_t launch_lse_inst(const SweepLaunch& a, dim3 grid, const SweepCf
 template <int LAY>
 hipError_t launch_lse_layout(const SweepCfg& cfg, const SweepLaunch& a, int ndir,
                              hipStream_t stream) {
-    dim3 grid = a.mode == MODE_FULL ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);
+    dim3 grid = (a.mode == MODE_FULL || a.mode == MODE_REPAIR) ? dim3(a.B, ndir)
+                                                               : dim3(a.nspans, a.B, ndir);
     // C <= 16 (G >= 16) runs the split-role kernel instead
     if (cfg.G == 8 && cfg.CPL == 4) { LSE_KPL_CASES(8, 4, 8, 256) }
     if (cfg.G == 8 && cfg.CPL == 8) { LSE_KPL_CASES(8, 8, 8, 512) }

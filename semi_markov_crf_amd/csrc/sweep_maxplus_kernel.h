@@ -65,10 +65,41 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
     const int cr = act ? c : C;              // inactive lanes use the spare LDS row C
     const int cc = act ? c : 0;
 
-    const int b = blockIdx.x;
+    // MODE_FULL: grid (B), the whole sequence.  MODE_SPEC: grid (nspans, B), every span at
+    // once from a burn-in; MODE_REPAIR: grid (B), from the checkpoint at the first failed
+    // seam to the end.
+    const bool spec = a.mode == MODE_SPEC;
+    int b, span = 0;
+    if (spec) {
+        span = blockIdx.x; b = blockIdx.y;
+    } else {
+        b = blockIdx.x;
+    }
     const int Lr = a.Leff[b];
     const bool bad = Lr < 0;
     const int L = bad ? -Lr : Lr;
+    int t0 = 0, t1 = L, tout = 0;
+    if (spec) {
+        tout = span * a.delta;
+        if (tout >= L) return;
+        t1 = min(L, tout + a.delta);
+        t0 = max(0, tout - a.warm);
+    } else if (a.mode == MODE_REPAIR) {
+        span = a.first_bad[b];
+        if (span >= a.nspans) return;
+        tout = span * a.delta;
+        if (tout >= L) return;
+        t0 = tout;
+    }
+    const bool ckpt = spec && t1 < L;                    // checkpoint at the span's end
+    const int hlo = (spec && span > 0) ? tout - K + 1 : INT_MAX;    // seam windows
+    const int tlo = ckpt ? t1 - K + 1 : INT_MAX;
+    const size_t winrow = ((size_t)b * a.nspans + span) * K;
+    const size_t ckrow = (size_t)b * a.nspans;
+    auto window = [&](int t, double av) {                // writer lanes
+        if (t >= hlo && t <= tout) a.head[(winrow + t - hlo) * C + c] = av;
+        if (t >= tlo && t <= t1) a.tail[(winrow + t - tlo) * C + c] = av;
+    };
     const int RMASK = RS - 1;
     const int chunkN = CH * C;
 
@@ -110,22 +141,42 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
     auto put = [&](int pos, float r) { ring_put<MIR>(Rrow, pos, RS, r); };
 
     double Bc = 0.0, H = 0.0;
-    // position 0: no transition into it; the ring entry is its start-side projection
-    float Mref = 0.0f, Rn1 = act ? fmaxf(proj_s(0, cc), NEG) : 0.0f, Rn2 = NEG;
-    if (act && j == 0) put(0, Rn1);
+    float Mref = 0.0f, Rn1 = NEG, Rn2 = NEG;
+    if (t0 == 0) {
+        // position 0: no transition into it; the ring entry is its start-side projection
+        Rn1 = act ? fmaxf(proj_s(0, cc), NEG) : 0.0f;
+        if (act && j == 0) put(0, Rn1);
+        if (act && j == 0)
+            for (int p = min(hlo, tlo); p <= 0; ++p) window(p, p == 0 ? (double)Rn1 : -1.0e300);
+    } else if (spec) {
+        // burn-in start: every ring entry of positions t0-K+1 .. t0 equal
+        if (act)
+            for (int q = j; q < K && t0 - q >= 0; q += G) put(t0 - q, 0.0f);
+        Rn1 = 0.0f;
+        Rn2 = (K >= 2 && t0 >= 1) ? 0.0f : NEG;
+    } else {
+        const size_t ck = ckrow + span;
+        if (act)
+            for (int q = j; q < K; q += G) put(t0 - q, a.ck_ring[(ck * K + q) * C + c]);
+        Bc = a.ck_base[ck * C + cc];
+        Mref = a.ck_mprev[ck * C + cc];
+        H = a.ck_href[ck];
+        Rn1 = a.ck_ring[(ck * K + 0) * C + cc];
+        Rn2 = K >= 2 ? a.ck_ring[(ck * K + 1) * C + cc] : NEG;
+    }
     __syncthreads();
 
     int kQa = 0, kQb = 0, kb_prev = 0;
-    float Qa = bulk_max<G, KPL, MIR>(Rrow, 1, j, RS, dreg, &kQa);
-    float Qb = bulk_max<G, KPL, MIR>(Rrow, 2, j, RS, dreg, &kQb);
+    float Qa = bulk_max<G, KPL, MIR>(Rrow, t0 + 1, j, RS, dreg, &kQa);
+    float Qb = bulk_max<G, KPL, MIR>(Rrow, t0 + 2, j, RS, dreg, &kQb);
 
     // ---------------------------------------------------------------- S staging
     for (int q = tid; q < chunkN; q += NT) {
-        const int t = 1 + q / C;
-        const size_t gq = (size_t)C + q;
-        const double sv = (t <= L) ? Sb[gq] : 0.0;
-        Sbuf[q] = (t <= L) ? sv + (double)proj_e(t, gq) : 0.0;
-        Sbuf[chunkN + q] = (t <= L) ? sv - (double)proj_s(t, gq) : 0.0;
+        const int t = t0 + 1 + q / C;
+        const size_t gq = (size_t)(t0 + 1) * C + q;
+        const double sv = (t <= t1) ? Sb[gq] : 0.0;
+        Sbuf[q] = (t <= t1) ? sv + (double)proj_e(t, gq) : 0.0;
+        Sbuf[chunkN + q] = (t <= t1) ? sv - (double)proj_s(t, gq) : 0.0;
     }
     // the chunk after: values in registers, published CH positions later
     double pf[PF], pfs[PF];
@@ -133,9 +184,9 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
     for (int i = 0; i < PF; ++i) {
         const int q = tid + i * NT;
         pf[i] = pfs[i] = 0.0;
-        const int t = 1 + CH + q / C;
-        if (q < chunkN && t <= L) {
-            const size_t gq = (size_t)(1 + CH) * C + q;
+        const int t = t0 + 1 + CH + q / C;
+        if (q < chunkN && t <= t1) {
+            const size_t gq = (size_t)(t0 + 1 + CH) * C + q;
             pf[i] = Sb[gq] + (double)proj_e(t, gq);
             pfs[i] = Sb[gq] - (double)proj_s(t, gq);
         }
@@ -147,43 +198,46 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
     const size_t outrow = (size_t)b * (T + 1);
 
     // ---------------------------------------------------------------- main loop
-    for (int tc = 1, nch = 0; tc <= L; tc += CH, ++nch) {
+    // the transition step [B] of position t-1, at iteration t (and once more after the loop
+    // for a span's last position)
+    auto transition = [&](int tp) {
+        const float* us = u_sh + (tp & 1) * UP;
+        float y[CPL], uv[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            uv[i] = us[jt + i * GT];
+            y[i] = uv[i] + treg[i];
+        }
+        float mt = y[0], mu = uv[0];
+#pragma unroll
+        for (int i = 1; i < CPL; ++i) {
+            mt = fmaxf(mt, y[i]);
+            mu = fmaxf(mu, uv[i]);
+        }
+        mt = group_reduce<GT>(mt, OpMax());
+        mu = group_reduce<GT>(mu, OpMax());
+        int cb = INT_MAX;
+#pragma unroll
+        for (int i = CPL - 1; i >= 0; --i)
+            if (y[i] == mt) cb = jt + i * GT;
+        const int cbest = group_min_int<GT>(cb);
+        const float Rnew = mt - h_prev;
+        H += (double)mu;
+        Rn2 = Rn1;
+        Rn1 = Rnew;
+        if (j == 0) {
+            put(tp, Rnew);
+            if (act && tp > tout)
+                a.bp[(outrow + tp) * C + c] = (uint32_t)kb_prev | ((uint32_t)cbest << 16);
+            if (act && tp >= min(hlo, tlo)) window(tp, Bc + (double)Rnew);
+        }
+    };
+    for (int tc = t0 + 1, nch = 0; tc <= t1; tc += CH, ++nch) {
         const double* Srow = Sbuf + (nch & 1) * 2 * chunkN;   // end side; start side at +chunkN
-        const int rows = min(CH, L - tc + 1);
+        const int rows = min(CH, t1 - tc + 1);
         for (int row = 0; row < rows; ++row) {
             const int t = tc + row;
-            if (t > 1) {
-                // ---- [B] A(t-1) = max_{c'} (u(t-1)[c'] + T[c'][c]) - h(t-1); H(t)
-                const float* us = u_sh + ((t - 1) & 1) * UP;
-                float y[CPL], uv[CPL];
-#pragma unroll
-                for (int i = 0; i < CPL; ++i) {
-                    uv[i] = us[jt + i * GT];
-                    y[i] = uv[i] + treg[i];
-                }
-                float mt = y[0], mu = uv[0];
-#pragma unroll
-                for (int i = 1; i < CPL; ++i) {
-                    mt = fmaxf(mt, y[i]);
-                    mu = fmaxf(mu, uv[i]);
-                }
-                mt = group_reduce<GT>(mt, OpMax());
-                mu = group_reduce<GT>(mu, OpMax());
-                int cb = INT_MAX;
-#pragma unroll
-                for (int i = CPL - 1; i >= 0; --i)
-                    if (y[i] == mt) cb = jt + i * GT;
-                const int cbest = group_min_int<GT>(cb);
-                const float Rnew = mt - h_prev;
-                H += (double)mu;
-                Rn2 = Rn1;
-                Rn1 = Rnew;
-                if (j == 0) {
-                    put(t - 1, Rnew);
-                    if (act) a.bp[(outrow + t - 1) * C + c] = (uint32_t)kb_prev | ((uint32_t)cbest << 16);
-                }
-            }
-
+            if (t > t0 + 1) transition(t - 1);
             // ---- [C] V(t): k = 1, 2 from registers, k >= 3 from the bulk value
             const float e1 = Rn1 + d0, e2 = Rn2 + d1;
             const float sig = fmaxf(fmaxf(Qa, e1), e2);
@@ -221,7 +275,7 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
             __syncthreads();
         }
         // ---- S staging: publish the next chunk, fetch the one after
-        if (tc + CH <= L) {
+        if (tc + CH <= t1) {
             double* dst = Sbuf + ((nch + 1) & 1) * 2 * chunkN;
 #pragma unroll
             for (int i = 0; i < PF; ++i) {
@@ -237,17 +291,40 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
                 if (q < chunkN) {
                     const int tt = tc + 2 * CH + q / C;
                     const size_t gq = (size_t)(tc + 2 * CH) * C + q;
-                    pf[i] = (tt <= L) ? Sb[gq] + (double)proj_e(tt, gq) : 0.0;
-                    pfs[i] = (tt <= L) ? Sb[gq] - (double)proj_s(tt, gq) : 0.0;
+                    pf[i] = (tt <= t1) ? Sb[gq] + (double)proj_e(tt, gq) : 0.0;
+                    pfs[i] = (tt <= t1) ? Sb[gq] - (double)proj_s(tt, gq) : 0.0;
                 }
             }
             __syncthreads();
         }
     }
 
+    if (t1 < L) {
+        // a span's last position: its transition step (the previous-label field of its
+        // backpointer, its ring entry, the tail window), then the checkpoint at it
+        transition(t1);
+        if (ckpt) {
+            __syncthreads();                                // every label's ring entry of t1
+            const size_t ck = ckrow + t1 / a.delta;
+            if (act)
+                for (int qq = j; qq < K; qq += G)
+                    a.ck_ring[(ck * K + qq) * C + c] = Rrow[(t1 - qq) & RMASK];
+            if (act && j == 0) {
+                a.ck_base[ck * C + c] = Bc;
+                a.ck_mprev[ck * C + c] = Mref;
+            }
+            if (tid == 0) a.ck_href[ck] = H;
+        }
+        return;
+    }
     // ---------------------------------------------------------------- end of sequence
     const float* us = u_sh + (L & 1) * UP;
     if (act && j == 0) a.bp[(outrow + L) * C + c] = (uint32_t)kb_prev;
+    if (a.mode != MODE_FULL) {
+        // the values V(L, c) in this sweep's frame; the final label is chosen afterwards
+        if (act && j == 0) a.vfin[(size_t)b * C + c] = H + (double)us[c];
+        return;
+    }
     if (c == 0) {
         float mu = NEG;
 #pragma unroll
@@ -270,7 +347,8 @@ template <int G, int KPL, int CPL, int GT, int NTMAX, bool MIR>
 static hipError_t launch_maxplus_inst(const SweepLaunch& a, const SweepCfg& cfg,
                                       hipStream_t stream) {
     if (cfg.NTv > NTMAX || cfg.vit.CH > MAXPLUS_CHUNK_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_maxplus<G, KPL, CPL, GT, NTMAX, MIR>), dim3(a.B), dim3(cfg.NTv),
+    const dim3 grid = a.mode == MODE_SPEC ? dim3(a.nspans, a.B) : dim3(a.B);
+    hipLaunchKernelGGL((k_maxplus<G, KPL, CPL, GT, NTMAX, MIR>), grid, dim3(cfg.NTv),
                        cfg.vit.bytes, stream, static_cast<const SweepArgs&>(a), cfg.RS,
                        cfg.vit.P, cfg.vit.CH, a.proj_start, a.proj_end);
     return hipGetLastError();

@@ -1,4 +1,4 @@
-"""The checkpoint spans swept at once (C <= 16) against the in-order sweeps and the oracle.
+"""The checkpoint spans swept at once against the in-order sweeps and the oracle.
 
 Every span of delta positions starts a burn-in of 3K positions early from a uniform ring;
 a seam check at each checkpoint proves that the two spans' states agree up to a constant
@@ -57,6 +57,9 @@ CASES = [
     (203, 2, 1500, 16, 12, 1.0, 100),    # 16 labels
     (204, 2, 2500, 8, 150, 2.0, 0),      # 32 lanes per label, long burn-in
     (205, 3, 700, 5, 6, 1.0, 7),         # spans shorter than the burn-in
+    (206, 2, 1200, 24, 10, 1.0, 90),     # 24 labels: one barrier per position
+    (207, 2, 1000, 40, 16, 1.0, 0),      # 40 labels
+    (208, 2, 600, 64, 8, 1.5, 50),       # 64 labels, 4 lanes per label
 ]
 
 
@@ -126,6 +129,8 @@ VIT_CASES = [
     (221, 3, 3000, 6, 40, 2.0),
     (222, 2, 4000, 4, 100, 1.5),
     (223, 2, 2000, 16, 20, 1.0),
+    (224, 2, 1500, 24, 16, 1.5),
+    (225, 2, 1000, 64, 8, 1.5),
 ]
 
 
