@@ -25,7 +25,7 @@ struct Layout {
     size_t ckR = 0, ckB = 0, ckM = 0, ckH = 0, XF = 0, AF = 0, XB = 0, AB = 0;
     size_t Dn = 0, dnt = 0, dno = 0, mu = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0, rps = 0;
     size_t gcnt = 0, gpart = 0, pst = 0, pen = 0;
-    size_t bp = 0, vscore = 0, vcstar = 0, vwin = 0, vfin = 0, split = 0, btr = 0, bent = 0;
+    size_t bp = 0, vfin = 0, vend = 0, btr = 0, bent = 0, btg = 0;
     size_t total = 0;
 };
 
@@ -119,15 +119,13 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         lo.total = lo.S;
         return true;
     } else if (op == SEMICRF_OP_VITERBI) {
-        lo.bp = m.take(sizeof(uint32_t) * 2 * BT1C);
-        lo.vscore = m.take(sizeof(double) * B);
-        lo.vcstar = m.take(sizeof(int) * B);
-        lo.vwin = m.take(sizeof(double) * 2 * B * K * C);
+        lo.bp = m.take(sizeof(uint32_t) * BT1C);
         lo.vfin = m.take(sizeof(double) * B * C);
-        lo.split = m.take(sizeof(int) * 4 * B);
+        lo.vend = m.take(sizeof(int) * 2 * B);
         const size_t nch = (size_t)backtrace_chunks(T, C, K);
-        lo.btr = m.take(sizeof(int32_t) * 2 * B * nch * K * C);
-        lo.bent = m.take(sizeof(int32_t) * 2 * B * nch);
+        lo.btr = m.take(sizeof(int32_t) * B * nch * K * C);
+        lo.bent = m.take(sizeof(int32_t) * B * nch);
+        lo.btg = m.take(sizeof(int32_t) * backtrace_scratch_ints(B, T, C, K));
     } else {
         return false;
     }
@@ -227,7 +225,6 @@ SweepLaunch base_args(const float* trans, const float* dur, const Proj& pj, int 
 int run_spans(const SweepCfg& cfg, SweepLaunch a, int ndir, const Layout& lo, void* ws,
               const SpecOpt& so, hipStream_t stream, hipEvent_t* events, int stage) {
     a.mode = MODE_SPEC;
-    a.write_ckpt = 0;
     LAUNCH(launch_lse(cfg, a, ndir, stream));
     if (events && stage >= 0 && hipEventRecord(events[stage], stream) != hipSuccess)
         return SEMICRF_ERR_DEVICE;
@@ -413,40 +410,35 @@ static int run_viterbi(const float* em, const int32_t* lengths, const float* tra
     const SweepCfg cfg = choose_sweep(C, K);
     SweepLaunch a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
     a.bp = at<uint32_t>(workspace, lo.bp);
-    a.vscore = at<double>(workspace, lo.vscore);
-    a.vcstar = at<int>(workspace, lo.vcstar);
-    a.vwin = at<double>(workspace, lo.vwin);
     a.vfin = at<double>(workspace, lo.vfin);
-    {
-        // every checkpoint span of the forward decode at once, the seam check (the frame
-        // offsets, no log Z), the in-order repair from a failed seam, the final label
-        a.mode = MODE_SPEC;
-        LAUNCH(launch_maxplus(cfg, a, stream));
-        SeamArgs sa{};
-        sa.head = a.head;
-        sa.tail = a.tail;
-        sa.lzloc = a.lzloc;
-        sa.Leff = a.Leff;
-        sa.B = B; sa.C = C; sa.K = K; sa.delta = a.delta; sa.nspans = a.nspans;
-        sa.tol = so.tol;
-        sa.off = at<double>(workspace, lo.soff);
-        sa.first_bad = at<int>(workspace, lo.fbad);
-        sa.logz = a.logz;
-        sa.logz_b = a.logz_b;
-        sa.diag = at<double>(workspace, lo.diag);
-        LAUNCH(launch_seam(sa, 1, stream));
-        a.mode = MODE_REPAIR;
-        LAUNCH(launch_maxplus(cfg, a, stream));
-        LAUNCH(launch_vit_final(a.vfin, sa.off, a.Leff, B, C, a.delta, a.nspans, a.vscore,
-                                a.vcstar, stream));
-        LAUNCH(launch_seam_report(sa.diag, B, 1, so.bound, so.repairs, stream));
-    }
+    // every checkpoint span of the forward decode at once, the seam check (the frame
+    // offsets, no log Z), the in-order repair from a failed seam, the final label
+    a.mode = MODE_SPEC;
+    LAUNCH(launch_maxplus(cfg, a, stream));
+    SeamArgs sa{};
+    sa.head = a.head;
+    sa.tail = a.tail;
+    sa.lzloc = a.lzloc;
+    sa.Leff = a.Leff;
+    sa.B = B; sa.C = C; sa.K = K; sa.delta = a.delta; sa.nspans = a.nspans;
+    sa.tol = so.tol;
+    sa.off = at<double>(workspace, lo.soff);
+    sa.first_bad = at<int>(workspace, lo.fbad);
+    sa.logz = a.logz;
+    sa.logz_b = a.logz_b;
+    sa.diag = at<double>(workspace, lo.diag);
+    LAUNCH(launch_seam(sa, 1, stream));
+    a.mode = MODE_REPAIR;
+    LAUNCH(launch_maxplus(cfg, a, stream));
+    int* vend = at<int>(workspace, lo.vend);
+    LAUNCH(launch_vit_final(a.vfin, sa.off, a.Leff, B, C, a.delta, a.nspans, vend, best_score,
+                            stream));
+    LAUNCH(launch_seam_report(sa.diag, B, 1, so.bound, so.repairs, stream));
     STAGE(2);
-    int* split = at<int>(workspace, lo.split);
-    LAUNCH(launch_vit_combine(a.vwin, trans, a.Leff, B, C, K, false, a.vscore, a.vcstar,
-                              split, best_score, stream));
-    LAUNCH(launch_backtrace(a.bp, split, B, T, C, K, at<int32_t>(workspace, lo.btr),
-                            at<int32_t>(workspace, lo.bent), labels, seg_start, stream));
+    LAUNCH(launch_backtrace(a.bp, vend, B, T, C, K, at<int32_t>(workspace, lo.btr),
+                            at<int32_t>(workspace, lo.bent),
+                            backtrace_global(C, K) ? at<int>(workspace, lo.btg) : nullptr, labels,
+                            seg_start, stream));
     STAGE(3);
     return SEMICRF_OK;
 }

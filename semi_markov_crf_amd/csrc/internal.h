@@ -73,13 +73,13 @@ inline size_t lse_round_lds_bytes(int C, int CP, int P, int CH, bool lin, bool p
                     4 * (CP + 1) * ROUND + 2 * cp4 + 16 + 2 * CP * ROUND + 4) * 4 +
            (size_t)2 * CP * 8;
 }
-// Dynamic LDS of the max-plus round kernel (C <= 16): S chunks [2][C][CH] and S(L) (fp64),
+// Dynamic LDS of the max-plus round kernel (C <= 16): S chunks [2][C][CH] (fp64),
 // with projections the chunks' end-side and start-side projections [2][2][C][CH], the
 // ring [C+1][P], bulk maxima and their k [2][CP][2][ROUND], rebase shifts [CP rounded to
 // 4], a sink and a constant block [12] (fp32).
 inline size_t maxplus_round_lds_bytes(int C, int CP, int P, int CH, bool proj) {
     const int cp4 = (CP + 3) / 4 * 4;
-    return (size_t)(2 * CH * C + (C + 1) / 2 * 2) * 8 +
+    return (size_t)(2 * CH * C) * 8 +
            (size_t)((proj ? 4 : 0) * C * CH + (C + 1) * P + 4 * CP * ROUND + cp4 + 12) * 4;
 }
 // Dynamic LDS of the max-plus sweep: end-side and start-side S chunks [2][2][CH][C]
@@ -88,10 +88,7 @@ inline size_t maxplus_lds_bytes(int C, int UP, int P, int CH) {
     return (size_t)(4 * CH * C) * 8 + (size_t)((C + 1) * P + 2 * UP) * 4;
 }
 
-// MODE_FULL: one workgroup per (sequence, direction) from position 0 to L.
-// MODE_SPAN: one per (checkpoint span, sequence, direction), restored from the checkpoint
-//            at the span's start.
-// MODE_SPEC: one per (span, sequence, direction), all at once: a span other than the first
+// MODE_SPEC: one workgroup per (span, sequence, direction), all at once: a span other than the first
 //            starts `warm` positions early from a uniform ring (every entry equal) instead
 //            of a checkpoint; its values then equal the exact ones up to a constant, to
 //            within the rounding of the sweep, which the seam check verifies.  It writes its
@@ -99,7 +96,7 @@ inline size_t maxplus_lds_bytes(int C, int UP, int P, int CH) {
 //            burn-in (head) and its span (tail), and a checkpoint at its end.
 // MODE_REPAIR: one per (sequence, direction): where a seam check failed, the sequence is
 //            swept again from the checkpoint at the first failed seam to its end.
-enum SweepMode { MODE_FULL = 0, MODE_SPAN = 1, MODE_SPEC = 2, MODE_REPAIR = 3 };
+enum SweepMode { MODE_SPEC = 2, MODE_REPAIR = 3 };
 
 struct SweepArgs {
     const double* S;        // [B][T+1][C] centred prefix sums
@@ -107,12 +104,11 @@ struct SweepArgs {
     const float* trans;     // [C][C]
     const float* dur;       // [K][C]
     int B, T, C, K;
-    int mode;               // MODE_FULL: grid (B, ndir); MODE_SPAN: grid (nspans, B, ndir)
+    int mode;               // MODE_SPEC: grid (nspans, B, ndir); MODE_REPAIR: grid (B, ndir)
     int delta;              // checkpoint interval
     int nspans;             // max spans per sequence (ceil(T / delta))
-    int write_ckpt;         // FULL mode: write checkpoints at multiples of delta
-    int write_xa;           // write per-position X / A (SPAN mode, or FULL with one span)
-    // checkpoints [2 dirs][B][nspans][...]; index 0 of the span axis is unused
+    int write_xa;           // write the per-position values X / A
+    // checkpoints at span ends [2 dirs][B][nspans][...]; index 0 of the span axis is unused
     float* ck_ring;         // [..][K][C]
     double* ck_base;        // [..][C]
     float* ck_mprev;        // [..][C]
@@ -132,10 +128,7 @@ struct SweepArgs {
     const int* first_bad;   // [2 dirs][B] first span whose seam failed (nspans: none)
     const double* off;      // [2 dirs][B][nspans] frame offsets (natural log)
     // Viterbi
-    uint32_t* bp;           // [2 dirs][B][T+1][C]: (k) | (previous label << 16)
-    double* vscore;         // [B] (one-direction sweep)
-    int* vcstar;            // [B] final label (one-direction sweep)
-    double* vwin;           // [2 dirs][B][K][C] values over the meeting window (round kernel)
+    uint32_t* bp;           // [B][T+1][C]: (k) | (previous label << 16)
     double* vfin;           // [B][C] values V(L, c) of the span that holds L, in its frame
 };
 
@@ -150,7 +143,7 @@ struct SweepLaunch : SweepArgs {
     const float* proj_end = nullptr;
 };
 
-// log-semiring sweep: grid (B, ndir) in MODE_FULL, (nspans, B, ndir) in MODE_SPAN;
+// log-semiring sweep: grid (nspans, B, ndir) in MODE_SPEC, (B, ndir) in MODE_REPAIR;
 // dispatches on cfg.lse.layout to the per-layout translation units
 hipError_t launch_lse(const SweepCfg& cfg, const SweepLaunch& a, int ndir, hipStream_t stream);
 hipError_t launch_lse_mirror(const SweepCfg& cfg, const SweepLaunch& a, int ndir, hipStream_t stream);
@@ -160,7 +153,8 @@ hipError_t launch_lse_log(const SweepCfg& cfg, const SweepLaunch& a, int ndir, h
 hipError_t launch_lse_round_proj(const SweepCfg& cfg, const SweepLaunch& a, int ndir, bool lin,
                                  hipStream_t stream);
 hipError_t launch_maxplus_round_proj(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream);
-// max-plus sweep (Viterbi): MODE_FULL, forward only, grid (B); dispatches on cfg.vit.layout
+// max-plus sweep (Viterbi), forward only: grid (nspans, B) in MODE_SPEC, (B) in
+// MODE_REPAIR; dispatches on cfg.vit.layout
 hipError_t launch_maxplus(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream);
 hipError_t launch_maxplus_mirror(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream);
 hipError_t launch_maxplus_plain(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream);
@@ -288,21 +282,20 @@ hipError_t launch_gold(const GoldArgs& g, hipStream_t stream);
 // chunk length and chunk count of the parallel backtrace
 int backtrace_chunk(int C, int K);
 int backtrace_chunks(int T, int C, int K);
-// split[b] = {t*, c_left, c_right, L}: the best segmentation's boundary in the meeting
-// window of the two-direction sweep (bidir), or t* = L and the one-direction sweep's final
-// label; best_score[b] its score (NaN for an invalid length)
-// vscore[b] = max_c vfin[b][c] + off[b][last span], vcstar[b] the lowest maximising c (NaN
-// for an invalid length): the end of the one-direction decode over speculative spans
+// the backtrace's chunk tables live in global memory (the chunks' LDS would not hold them)
+bool backtrace_global(int C, int K);
+// int32 words of that global scratch (0 when the tables fit LDS)
+size_t backtrace_scratch_ints(int B, int T, int C, int K);
+// vend[b] = {L, c*}: c* the lowest label maximising vfin[b][c] (the values V(L, c) of the
+// span that holds L, in its frame); best_score[b] = V(L, c*) + off[b][that span] (NaN for
+// an invalid length)
 hipError_t launch_vit_final(const double* vfin, const double* off, const int* Leff, int B,
-                            int C, int delta, int nspans, double* vscore, int* vcstar,
+                            int C, int delta, int nspans, int* vend, float* best_score,
                             hipStream_t stream);
-hipError_t launch_vit_combine(const double* vwin, const float* trans, const int* Leff, int B,
-                              int C, int K, bool bidir, const double* vscore, const int* vcstar,
-                              int* split, float* best_score, hipStream_t stream);
-// bp: [2][B][T+1][C] (part 1: the mirrored sequence); tr: [2][B][nch][K*C] and ent:
-// [2][B][nch] int32 scratch
-hipError_t launch_backtrace(const uint32_t* bp, const int* split, int B, int T, int C, int K,
-                            int32_t* tr, int32_t* ent, int32_t* labels, uint8_t* seg_start,
-                            hipStream_t stream);
+// bp: [B][T+1][C]; tr: [B][nch][K*C] and ent: [B][nch] int32 scratch; gscratch: the global
+// chunk tables (backtrace_scratch_ints words) or NULL when they fit LDS
+hipError_t launch_backtrace(const uint32_t* bp, const int* vend, int B, int T, int C, int K,
+                            int32_t* tr, int32_t* ent, int* gscratch, int32_t* labels,
+                            uint8_t* seg_start, hipStream_t stream);
 
 }  // namespace semicrf

@@ -108,11 +108,13 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
     const int cc = act ? c : 0;
     const bool writer = act && j == 0;       // one lane per label publishes
 
+    // MODE_SPEC: grid (nspans, B, ndir); MODE_REPAIR: grid (B, ndir)
+    const bool spec = a.mode == MODE_SPEC;
     int b, span, dir;
-    if (a.mode == MODE_FULL || a.mode == MODE_REPAIR) {
-        b = blockIdx.x; dir = blockIdx.y; span = 0;
-    } else {
+    if (spec) {
         span = blockIdx.x; b = blockIdx.y; dir = blockIdx.z;
+    } else {
+        b = blockIdx.x; dir = blockIdx.y; span = 0;
     }
     const int Lr = a.Leff[b];
     const bool bad = Lr < 0;
@@ -120,13 +122,12 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
     // [tout, t1]: the positions this workgroup writes; t0: where its sweep starts (a
     // speculative span runs a burn-in from t0 = tout - warm, or exactly from 0)
     int t0 = 0, t1 = L, tout = 0;
-    const bool spec = a.mode == MODE_SPEC;
-    if (a.mode == MODE_SPAN || spec) {
+    if (spec) {
         tout = span * a.delta;
         if (tout >= L) return;
         t1 = min(L, tout + a.delta);
-        t0 = spec ? max(0, tout - a.warm) : tout;
-    } else if (a.mode == MODE_REPAIR) {
+        t0 = max(0, tout - a.warm);
+    } else {
         span = a.first_bad[dir * a.B + b];
         if (span >= a.nspans) return;
         tout = span * a.delta;
@@ -360,8 +361,8 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
     publish(t0 + 1, Sbuf[cc], exp2_d(Sbuf[cc] + BH + (double)dmax), Qla, Qga);
     bulk(t0 + 2, Qla, Qga);
     double lz = 0.0;
-    // checkpoints: every delta positions (MODE_FULL), or at the end of a speculative span
-    int next_ck = (a.mode == MODE_FULL && a.write_ckpt) ? a.delta : (spec && t1 < L) ? t1 : INT_MAX;
+    // checkpoint at the end of a speculative span (the start of a repair)
+    const int ck_at = (spec && t1 < L) ? t1 : INT_MAX;
     __syncthreads();
 
     // ---------------------------------------------------------------- main loop
@@ -506,19 +507,16 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
             Rn1 = Rnew; En1 = Enew;
             if (Qgc > NEG_HALF) Mref = Qgc;
             // ---- checkpoint: state right after the transition step of position t
-            if (t == next_ck) {
-                if (t < L) {
-                    const size_t ck = ckrow + t / a.delta;
-                    if (act)
-                        for (int qq = j; qq < K; qq += G)
-                            a.ck_ring[(ck * K + qq) * C + c] = Rrow[(t - qq) & RMASK];
-                    if (writer) {
-                        a.ck_base[ck * C + c] = Bc;
-                        a.ck_mprev[ck * C + c] = Mref;
-                    }
-                    if (tid == 0) a.ck_href[ck] = H;
+            if (t == ck_at) {
+                const size_t ck = ckrow + t / a.delta;
+                if (act)
+                    for (int qq = j; qq < K; qq += G)
+                        a.ck_ring[(ck * K + qq) * C + c] = Rrow[(t - qq) & RMASK];
+                if (writer) {
+                    a.ck_base[ck * C + c] = Bc;
+                    a.ck_mprev[ck * C + c] = Mref;
                 }
-                next_ck += a.delta;
+                if (tid == 0) a.ck_href[ck] = H;
             }
             // ---- [C] message of t+1
             if (t < t1) publish(t + 1, Snx, z, Qla, Qga);
@@ -535,9 +533,7 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
             a.lzloc[dir * a.B + b] = lz * LN2;           // the seam check adds the offsets
         } else {
             // a repaired sweep continues in the frame of the span before the failed seam
-            const double base = a.mode == MODE_REPAIR
-                                    ? a.off[((size_t)dir * a.B + b) * a.nspans + span - 1]
-                                    : 0.0;
+            const double base = a.off[((size_t)dir * a.B + b) * a.nspans + span - 1];
             (dir == 0 ? a.logz : a.logz_b)[b] = bad ? nan_d() : lz * LN2 + base;
         }
     }
@@ -577,8 +573,8 @@ static hipError_t launch_lse_inst(const SweepLaunch& a, dim3 grid, const SweepCf
 template <int LAY>
 hipError_t launch_lse_layout(const SweepCfg& cfg, const SweepLaunch& a, int ndir,
                              hipStream_t stream) {
-    dim3 grid = (a.mode == MODE_FULL || a.mode == MODE_REPAIR) ? dim3(a.B, ndir)
-                                                               : dim3(a.nspans, a.B, ndir);
+    if (a.mode != MODE_SPEC && a.mode != MODE_REPAIR) return hipErrorInvalidValue;
+    const dim3 grid = a.mode == MODE_REPAIR ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);
     // C <= 16 (G >= 16) runs the split-role kernel instead
     if (cfg.G == 8 && cfg.CPL == 4) { LSE_KPL_CASES(8, 4, 8, 256) }
     if (cfg.G == 8 && cfg.CPL == 8) { LSE_KPL_CASES(8, 8, 8, 512) }

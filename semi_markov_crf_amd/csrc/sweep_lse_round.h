@@ -126,11 +126,13 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     constexpr bool QLANE = CP < 16;
     const bool qlane = QLANE && chain && tid == 15;
 
+    // MODE_SPEC: grid (nspans, B, ndir); MODE_REPAIR: grid (B, ndir)
+    const bool spec = a.mode == MODE_SPEC;
     int b, span, dir;
-    if (a.mode == MODE_FULL || a.mode == MODE_REPAIR) {
-        b = blockIdx.x; dir = blockIdx.y; span = 0;
-    } else {
+    if (spec) {
         span = blockIdx.x; b = blockIdx.y; dir = blockIdx.z;
+    } else {
+        b = blockIdx.x; dir = blockIdx.y; span = 0;
     }
     const int Lr = a.Leff[b];
     const bool bad = Lr < 0;
@@ -138,13 +140,12 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     // [tout, t1]: the positions this workgroup writes; t0: where its sweep starts (a
     // speculative span runs a burn-in from t0 = tout - warm, or exactly from 0)
     int t0 = 0, t1 = L, tout = 0;
-    const bool spec = a.mode == MODE_SPEC;
-    if (a.mode == MODE_SPAN || spec) {
+    if (spec) {
         tout = span * a.delta;
         if (tout >= L) return;
         t1 = min(L, tout + a.delta);
-        t0 = spec ? max(0, tout - a.warm) : tout;
-    } else if (a.mode == MODE_REPAIR) {
+        t0 = max(0, tout - a.warm);
+    } else {
         span = a.first_bad[dir * a.B + b];
         if (span >= a.nspans) return;
         tout = span * a.delta;
@@ -152,8 +153,8 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
         t0 = tout;
     }
     const int RMASK = RS - 1;
-    // checkpoints: every delta positions (MODE_FULL), or at the end of a speculative span
-    const bool ckpt = (a.mode == MODE_FULL && a.write_ckpt) || (spec && t1 < L);
+    // checkpoint at the end of a speculative span (the start of a repair)
+    const bool ckpt = spec && t1 < L;
     // ring values of the windows the seam check compares (MODE_SPEC): head [hlo, tout] of
     // every span but the first, tail [tlo, t1] of every span but the last
     const int hlo = (spec && span > 0) ? tout - K + 1 : INT_MAX;
@@ -490,8 +491,7 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     // bulk lanes at the start of round r (rs = its first position - 1): the log ring block
     // of round r-1 from the chain's staging, the chain's rebase of round r-1 applied to the
     // rings, the rings of the checkpoints the chain took in round r-1
-    const int ck_first = spec ? t1 : a.delta;    // first checkpoint position
-    int next_ckb = ckpt ? ck_first : INT_MAX;  // next checkpoint whose ring is to copy
+    int next_ckb = ckpt ? t1 : INT_MAX;        // next checkpoint whose ring is to copy
     // Sprev: the staged S of round r-1's first position for this lane's label; Fprev: its
     // end-side projection plane (projections only)
     auto ring_round = [&](int r, int rs, const double* Sprev, const float* Fprev) {
@@ -595,7 +595,7 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     // ---------------------------------------------------------------- main loop
     double BH = Bc - H;                                   // B_c - H
     double lz = 0.0;
-    int next_ck = ckpt ? ck_first : INT_MAX;
+    int next_ck = ckpt ? t1 : INT_MAX;
     float pdl = 0.0f;          // chain: rebase of the last round, still to apply to the
     bool pend = false;         // bulk sums it reads this round
     const int nrounds = (t1 - t0 + M - 1) / M;
@@ -920,9 +920,7 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
             a.lzloc[dir * a.B + b] = lz * LN2;           // the seam check adds the offsets
         } else {
             // a repaired sweep continues in the frame of the span before the failed seam
-            const double base = a.mode == MODE_REPAIR
-                                    ? a.off[((size_t)dir * a.B + b) * a.nspans + span - 1]
-                                    : 0.0;
+            const double base = a.off[((size_t)dir * a.B + b) * a.nspans + span - 1];
             (dir == 0 ? a.logz : a.logz_b)[b] = bad ? nan_d() : lz * LN2 + base;
         }
     }
@@ -962,12 +960,8 @@ static hipError_t launch_lse_round_inst(const SweepLaunch& a, dim3 grid, const S
 template <bool LIN, bool PROJ>
 hipError_t launch_lse_round_layout(const SweepCfg& cfg, const SweepLaunch& a, int ndir,
                                    hipStream_t stream) {
-    const dim3 grid = (a.mode == MODE_FULL || a.mode == MODE_REPAIR) ? dim3(a.B, ndir)
-                                                                     : dim3(a.nspans, a.B, ndir);
-    // the speculative spans and their repair (the only modes the library launches for
-    // C <= 16) run the instance with per-position staging, which writes the outputs and
-    // the seam windows
     if (a.mode != MODE_SPEC && a.mode != MODE_REPAIR) return hipErrorInvalidValue;
+    const dim3 grid = a.mode == MODE_REPAIR ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);
     if (cfg.G == 64 && cfg.CPr == 4) { LSE_ROUND_BPL_CASES(64, 4) }
     if (cfg.G == 64 && cfg.CPr == 6) { LSE_ROUND_BPL_CASES(64, 6) }
     if (cfg.G == 64 && cfg.CPr == 8) { LSE_ROUND_BPL_CASES(64, 8) }

@@ -10,8 +10,8 @@
 // and, for the segment start s = t - k, the lowest c' attaining abar[s, c]; packed as
 // k | c' << 16 (c' stored at the start position s).
 //
-// Work layout as in the log-semiring sweep: one workgroup per sequence, lanes in groups
-// of G per label, the label's ring of A = abar - S (relative to a per-label fp64 base,
+// Work layout as in the log-semiring sweep: one workgroup per checkpoint span (or per
+// sequence for a repair), lanes in groups of G per label, the label's ring of A = abar - S (relative to a per-label fp64 base,
 // moved every REBASE positions) in LDS, one barrier per position.  Iteration t runs
 //   [B] transition step of position t-1: max over u(t-1)[c'] + T[c', c] (DPP) -> A[t-1, c]
 //   [C] V(t): three-term max of the k = 1, 2 terms and the bulk value of t -> u(t) to LDS
@@ -25,8 +25,6 @@
 namespace semicrf {
 
 namespace {
-
-__device__ __forceinline__ double nan_d() { return __longlong_as_double(0x7ff8000000000000LL); }
 
 // Bulk value of position tq (terms k >= 3): max over the group and the lowest k attaining it.
 template <int G, int KPL, bool MIR>
@@ -47,7 +45,7 @@ __device__ __forceinline__ float bulk_max(const float* Rrow, int tq, int j, int 
 // G: lanes per label; KPL: durations k >= 3 per lane (k = 3 + j + i*G, i < KPL, covering
 // k <= K + 1); CPL, GT: previous labels per lane and the lane count of the transition
 // reduction (GT * CPL >= C, GT <= G); NTMAX: largest workgroup routed here.
-// Grid: one workgroup per sequence.  Natural-log units (max-plus needs no base change).
+// Natural-log units (max-plus needs no base change).
 template <int G, int KPL, int CPL, int GT, int NTMAX, bool MIR>
 __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int RS, const int P,
                                                   const int CH,
@@ -65,9 +63,8 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
     const int cr = act ? c : C;              // inactive lanes use the spare LDS row C
     const int cc = act ? c : 0;
 
-    // MODE_FULL: grid (B), the whole sequence.  MODE_SPEC: grid (nspans, B), every span at
-    // once from a burn-in; MODE_REPAIR: grid (B), from the checkpoint at the first failed
-    // seam to the end.
+    // MODE_SPEC: grid (nspans, B), every span at once from a burn-in; MODE_REPAIR: grid
+    // (B), from the checkpoint at the first failed seam to the end.
     const bool spec = a.mode == MODE_SPEC;
     int b, span = 0;
     if (spec) {
@@ -76,15 +73,14 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
         b = blockIdx.x;
     }
     const int Lr = a.Leff[b];
-    const bool bad = Lr < 0;
-    const int L = bad ? -Lr : Lr;
+    const int L = Lr < 0 ? -Lr : Lr;
     int t0 = 0, t1 = L, tout = 0;
     if (spec) {
         tout = span * a.delta;
         if (tout >= L) return;
         t1 = min(L, tout + a.delta);
         t0 = max(0, tout - a.warm);
-    } else if (a.mode == MODE_REPAIR) {
+    } else {
         span = a.first_bad[b];
         if (span >= a.nspans) return;
         tout = span * a.delta;
@@ -320,26 +316,8 @@ __global__ __launch_bounds__(NTMAX) void k_maxplus(const SweepArgs a, const int 
     // ---------------------------------------------------------------- end of sequence
     const float* us = u_sh + (L & 1) * UP;
     if (act && j == 0) a.bp[(outrow + L) * C + c] = (uint32_t)kb_prev;
-    if (a.mode != MODE_FULL) {
-        // the values V(L, c) in this sweep's frame; the final label is chosen afterwards
-        if (act && j == 0) a.vfin[(size_t)b * C + c] = H + (double)us[c];
-        return;
-    }
-    if (c == 0) {
-        float mu = NEG;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) mu = fmaxf(mu, us[jt + i * GT]);
-        mu = group_reduce<GT>(mu, OpMax());
-        int cb = INT_MAX;
-#pragma unroll
-        for (int i = CPL - 1; i >= 0; --i)
-            if (us[jt + i * GT] == mu) cb = jt + i * GT;
-        cb = group_min_int<GT>(cb);
-        if (j == 0) {
-            a.vscore[b] = bad ? nan_d() : H + (double)mu;
-            a.vcstar[b] = cb;
-        }
-    }
+    // the values V(L, c) in this sweep's frame; the final label is chosen afterwards
+    if (act && j == 0) a.vfin[(size_t)b * C + c] = H + (double)us[c];
 }
 
 // ------------------------------------------------------------------ launch
@@ -347,6 +325,7 @@ template <int G, int KPL, int CPL, int GT, int NTMAX, bool MIR>
 static hipError_t launch_maxplus_inst(const SweepLaunch& a, const SweepCfg& cfg,
                                       hipStream_t stream) {
     if (cfg.NTv > NTMAX || cfg.vit.CH > MAXPLUS_CHUNK_MAX) return hipErrorInvalidValue;
+    if (a.mode != MODE_SPEC && a.mode != MODE_REPAIR) return hipErrorInvalidValue;
     const dim3 grid = a.mode == MODE_SPEC ? dim3(a.nspans, a.B) : dim3(a.B);
     hipLaunchKernelGGL((k_maxplus<G, KPL, CPL, GT, NTMAX, MIR>), grid, dim3(cfg.NTv),
                        cfg.vit.bytes, stream, static_cast<const SweepArgs&>(a), cfg.RS,

@@ -15,13 +15,8 @@
 //    S, label-major.
 // Values are natural-log scores relative to a per-label fp64 base (moved every second
 // round) and a common fp64 reference H that advances by whole units once per round.
-//
-// The two directions meet in the middle: direction 0 runs forward over [0, mm], direction
-// 1 runs the same recurrence on the mirrored sequence (S'(t) = S(L) - S(L - t), trans
-// transposed) over original positions [lo, L], lo = max(0, mm - K + 1).  Every
-// segmentation has a segment boundary in [lo, mm], so the best one is the best of
-// V(t, c) + trans[c][c'] + W(t, c') over that window, V the forward and W the backward
-// value; both are written for the window in fp64 and combined afterwards.
+// Forward only: every checkpoint span at once from a burn-in (MODE_SPEC), then the repair
+// of a failed seam (MODE_REPAIR); the backtrace follows the backpointers afterwards.
 #pragma once
 
 #include "internal.h"
@@ -88,8 +83,8 @@ __device__ __forceinline__ int min_tree_i(const int* x) {
 }  // namespace
 
 // G: bulk lanes per label (C <= 256/G); BPL: ring blocks per bulk lane; CP: labels the
-// chain broadcasts (>= C); PROJ: boundary projections present.  Grid (B, 2 directions),
-// block 64 + ceil(C*G/64)*64 threads.
+// chain broadcasts (>= C); PROJ: boundary projections present.  Grid (nspans, B) in
+// MODE_SPEC, (B) in MODE_REPAIR; block 64 + ceil(C*G/64)*64 threads.
 template <int G, int BPL, int CP, bool PROJ>
 __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const int RS,
                                                       const int P, const int CH,
@@ -115,26 +110,20 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
     const bool cact = chain && tid < C;
     const int cl = cact ? tid : 0;
 
-    // MODE_FULL: grid (B, 2), the two directions meet in the middle.  MODE_SPEC: grid
-    // (nspans, B), every span of the forward sweep at once from a burn-in; MODE_REPAIR:
-    // grid (B), the forward sweep again from the checkpoint at the first failed seam.
-    const bool full = a.mode == MODE_FULL, spec = a.mode == MODE_SPEC;
-    int b, dir = 0, span = 0;
-    if (full) {
-        b = blockIdx.x; dir = blockIdx.y;
-    } else if (spec) {
+    // MODE_SPEC: grid (nspans, B), every span of the forward sweep at once from a burn-in;
+    // MODE_REPAIR: grid (B), the forward sweep again from the checkpoint at the first
+    // failed seam.
+    const bool spec = a.mode == MODE_SPEC;
+    int b, span = 0;
+    if (spec) {
         span = blockIdx.x; b = blockIdx.y;
     } else {
         b = blockIdx.x;
     }
     const int Lr = a.Leff[b];
     const int L = Lr < 0 ? -Lr : Lr;
-    int mm = 0, lo = 0, t0 = 0, t1 = L, tout = 0;
-    if (full) {
-        mm = min(L, (L + K - 1) / 2);                   // meeting window [lo, mm]
-        lo = max(0, mm - K + 1);
-        t1 = dir == 0 ? mm : L - lo;
-    } else if (spec) {
+    int t0 = 0, t1 = L, tout = 0;
+    if (spec) {
         tout = span * a.delta;
         if (tout >= L) return;
         t1 = min(L, tout + a.delta);
@@ -156,8 +145,7 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
     const int NR = bmax + 3;
 
     double* Sbuf = lds;                                    // [2][C][CH] label-major
-    double* SL = Sbuf + 2 * C * CH;                        // [C] (padded to 16 bytes)
-    float* Pst = (float*)(SL + (C + 1) / 2 * 2);           // [2][end, start][C][CH] projections
+    float* Pst = (float*)(Sbuf + 2 * C * CH);              // [2][end, start][C][CH] projections
     float* R = Pst + (PROJ ? 4 * C * CH : 0);              // [C+1][P]
     float* qsh = R + (C + 1) * P;                          // [2 rounds][CP][max, k][M]
     float* dlsh = qsh + 2 * CP * 2 * M;                    // [CP4] rebase shift per label
@@ -166,22 +154,17 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
     float* Rrow = R + cr * P;
 
     const double* Sb = a.S + (size_t)b * (T + 1) * C;
-    for (int q = tid; q < C; q += NT) SL[q] = Sb[(size_t)L * C + q];
-    // projections of sweep position p: end side (segments ending at p) and start side
+    // projections of position p: end side (segments ending at p) and start side
     // (segments starting at p); 0 without projections or outside [1, L] / [0, L-1]
     const float* PSb = proj_start ? proj_start + (size_t)b * T * C : nullptr;
     const float* PEb = proj_end ? proj_end + (size_t)b * T * C : nullptr;
     auto proj_e = [&](int p, int q) -> float {
         if constexpr (!PROJ) return 0.0f;
-        const float* src = dir == 0 ? PEb : PSb;
-        const int t = dir == 0 ? p - 1 : L - p;
-        return (src && p >= 1 && p <= L) ? src[(size_t)t * C + q] : 0.0f;
+        return (PEb && p >= 1 && p <= L) ? PEb[(size_t)(p - 1) * C + q] : 0.0f;
     };
     auto proj_s = [&](int p, int q) -> float {
         if constexpr (!PROJ) return 0.0f;
-        const float* src = dir == 0 ? PSb : PEb;
-        const int t = dir == 0 ? p : L - 1 - p;
-        return (src && p >= 0 && p < L) ? src[(size_t)t * C + q] : 0.0f;
+        return (PSb && p >= 0 && p < L) ? PSb[(size_t)p * C + q] : 0.0f;
     };
     for (int q = tid; q < (C + 1) * P; q += NT) R[q] = NEG;
     for (int q = tid; q < 2 * CP * 2 * M; q += NT) qsh[q] = ((q / M) & 1) ? __int_as_float(INT_MAX) : NEG;
@@ -204,8 +187,8 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
     float treg[CP];
 #pragma unroll
     for (int i = 0; i < CP; ++i)
-        treg[i] = (cact && i < C) ? fmaxf(dir == 0 ? a.trans[i * C + cl] : a.trans[cl * C + i], NEG) : NEG;
-    __syncthreads();   // ring cleared, SL visible
+        treg[i] = (cact && i < C) ? fmaxf(a.trans[i * C + cl], NEG) : NEG;
+    __syncthreads();   // ring cleared
 
     // bulk best (durations k >= m + 5) of the positions of round rr and its lowest k
     auto bulk_round = [&](int rr) {
@@ -293,8 +276,7 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
     }
 
     const int chunkN = CH * C;
-    auto sidx = [&](int t, int q) -> size_t { return (size_t)(dir == 0 ? t : L - t) * C + q; };
-    auto spub = [&](double raw, int q) -> double { return dir == 0 ? raw : SL[q] - raw; };
+    auto sidx = [&](int t, int q) -> size_t { return (size_t)t * C + q; };
     double pf[PF];
     float pfe[PF], pfs[PF];
 #pragma unroll
@@ -307,7 +289,7 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
             const int row = q / C, l = q - row * C;
             const int t = t0 + 1 + row;
             const bool in = t <= t1;
-            Sbuf[l * CH + row] = in ? spub(Sb[sidx(t, l)], l) : 0.0;
+            Sbuf[l * CH + row] = in ? Sb[sidx(t, l)] : 0.0;
             if constexpr (PROJ) {
                 Pst[l * CH + row] = in ? proj_e(t, l) : 0.0f;
                 Pst[C * CH + l * CH + row] = in ? proj_s(t, l) : 0.0f;
@@ -426,7 +408,7 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
             const int ml = min(M - 1, t1 - rs - 1);
             float me = NEG;
             float uu[M];
-            uint32_t* bpp = a.bp + (size_t)dir * a.B * (T + 1) * C + (outrow + rs + 1) * C + cl;
+            uint32_t* bpp = a.bp + (outrow + rs + 1) * C + cl;
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 const int p = rs + 1 + m;
@@ -464,12 +446,8 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
                     row_bcast_all_mp<CP>(u, uw);
                     me = max_tree<CP>(uw);
                 }
-                // value at an original position of the meeting window
-                const int tw = dir == 0 ? p : L - p;
-                if (full && p <= t1 && tw >= lo && tw <= mm && cact)
-                    a.vwin[(((size_t)dir * a.B + b) * K + (tw - lo)) * C + cl] = H0 + (double)u;
             }
-            if (!full && (rs + M >= min(hlo, tlo) || rs + M >= L)) {
+            if (rs + M >= min(hlo, tlo) || rs + M >= L) {
                 // seam windows (ring values, natural log, this sweep's frame) and the final
                 // values V(L, c)
 #pragma unroll
@@ -510,7 +488,7 @@ __global__ __launch_bounds__(512) void k_maxplus_round(const SweepArgs a, const 
                     const int q = bt + i * NB;
                     if (q < chunkN) {
                         const int row = q / C, l = q - row * C;
-                        dst[l * CH + row] = spub(pf[i], l);
+                        dst[l * CH + row] = pf[i];
                         if constexpr (PROJ) {
                             dp[l * CH + row] = pfe[i];
                             dp[C * CH + l * CH + row] = pfs[i];
@@ -554,8 +532,8 @@ static hipError_t launch_maxplus_round_inst(const SweepLaunch& a, const SweepCfg
         cfg.vit.P % 4 != 0 || cfg.RS % ROUND != 0)
         return hipErrorInvalidValue;
     const size_t bytes = maxplus_round_lds_bytes(a.C, CP, cfg.vit.P, cfg.vit.CH, PROJ);
-    const dim3 grid = a.mode == MODE_FULL ? dim3(a.B, 2)
-                      : a.mode == MODE_SPEC ? dim3(a.nspans, a.B) : dim3(a.B);
+    if (a.mode != MODE_SPEC && a.mode != MODE_REPAIR) return hipErrorInvalidValue;
+    const dim3 grid = a.mode == MODE_SPEC ? dim3(a.nspans, a.B) : dim3(a.B);
     hipLaunchKernelGGL((k_maxplus_round<G, BPL, CP, PROJ>), grid, dim3(cfg.NT), bytes,
                        stream, static_cast<const SweepArgs&>(a), cfg.RS, cfg.vit.P, cfg.vit.CH,
                        a.proj_start, a.proj_end);
