@@ -39,7 +39,8 @@ FLAGS = [
 
 SOURCES = ["api.cpp", "sweep_cfg.cpp", "scan.hip", "sweep_lse_mirror.hip", "sweep_lse_plain.hip",
            "sweep_lse_log.hip", "sweep_maxplus_mirror.hip", "sweep_maxplus_plain.hip",
-           "sweep_round_proj.hip", "sweep_round_proj_log.hip", "marginals.hip", "gold.hip", "viterbi.hip", "seam.hip"]
+           "sweep_round_proj.hip", "sweep_round_proj_log.hip", "marginals.hip", "gold.hip", "viterbi.hip", "seam.hip",
+           "sweep_xk_lse.hip", "sweep_xk_maxplus.hip"]
 
 
 def _compile(src: str) -> str:

@@ -26,6 +26,8 @@ struct Layout {
     size_t Dn = 0, dnt = 0, dno = 0, mu = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0, rps = 0;
     size_t gcnt = 0, gpart = 0, pst = 0, pen = 0;
     size_t bp = 0, vfin = 0, vend = 0, btr = 0, bent = 0, btg = 0;
+    size_t xkr = 0;                 // long-duration sweeps: the global ring scratch
+    bool has_xkr = false;
     size_t total = 0;
 };
 
@@ -58,7 +60,8 @@ bool shape_ok(int B, int T, int C, int K) {
 
 bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
     if (!shape_ok(B, T, C, K)) return false;
-    if (!choose_sweep(C, K).ok) return false;
+    const SweepCfg cfg = choose_sweep(C, K);
+    if (!cfg.ok) return false;
     const size_t BT1C = (size_t)B * (T + 1) * C;
     const int TS = scan_tile(C);
     lo.nts = (T + TS - 1) / TS;
@@ -89,6 +92,16 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         lo.soff = m.take(sizeof(double) * nck);
         lo.fbad = m.take(sizeof(int) * lo.ndir * B);
         lo.diag = m.take(sizeof(double) * lo.ndir * B * 4);
+        if (cfg.xk) {
+            // one ring slice per workgroup of the span sweeps (a repair reuses its span's)
+            const bool vit = op == SEMICRF_OP_VITERBI;
+            const size_t nf = xk_ring_floats(vit ? cfg.xk_vit : cfg.xk_lse, C,
+                                             lo.ndir * B * lo.nspans, vit);
+            if (nf > 0) {
+                lo.xkr = m.take(sizeof(float) * nf);
+                lo.has_xkr = true;
+            }
+        }
     }
     if (op == SEMICRF_OP_LOGZ) {
     } else if (op == SEMICRF_OP_BACKWARD) {
@@ -214,6 +227,7 @@ SweepLaunch base_args(const float* trans, const float* dur, const Proj& pj, int 
         a.lzloc = at<double>(ws, lo.lzloc);
         a.first_bad = at<int>(ws, lo.fbad);
         a.off = at<double>(ws, lo.soff);
+        if (lo.has_xkr) a.xk_ring = at<float>(ws, lo.xkr);
     }
     return a;
 }

@@ -32,6 +32,29 @@ struct SweepLds {
     size_t bytes;        // dynamic LDS per workgroup (0: does not fit)
 };
 
+// Long-duration sweeps (sweep_xk.h): one chain wavefront and G bulk lanes per label, each
+// lane holding kpl duration weights (a multiple of XK_UNROLL, at most the instance's
+// kplmax), the ring of RS >= K + 2 slots per label in LDS or (gring) in a global scratch
+// slice per workgroup.
+constexpr int XK_UNROLL = 8;
+constexpr int XK_REBASE = 16;      // positions between base moves (a power of two)
+constexpr int XK_PF = 2;           // staged S values per bulk lane and chunk
+constexpr int XK_FROM = 1026;      // durations from which the long-duration sweeps run
+
+struct XkCfg {
+    bool ok;
+    int G, kplmax, NT, kpl, RS, CH;
+    bool gring;          // ring in global memory
+    size_t lds;          // dynamic LDS per workgroup
+};
+// per-launch parameters of the long-duration sweeps
+struct XkParams {
+    float* ring;         // gring: [workgroups][rings][C][RS] scratch, else NULL
+    int RS, CH, kpl;
+};
+// maxp: the max-plus sweep (one ring) instead of the log-semiring sweep (two)
+XkCfg choose_xk(int C, int K, bool maxp);
+
 struct SweepCfg {
     int G, KPL, CPL, GT; // instantiated kernel shape (KPL: register capacity per lane)
     int kpl;             // durations k >= 3 per lane actually used
@@ -43,6 +66,8 @@ struct SweepCfg {
     int RS;              // ring slots per copy (power of two)
     SweepLds lse;        // log-semiring sweep
     SweepLds vit;        // max-plus sweep
+    bool xk;             // the long-duration sweeps run (xk_lse, xk_vit) instead
+    XkCfg xk_lse, xk_vit;
     bool ok;
 };
 SweepCfg choose_sweep(int C, int K);
@@ -141,6 +166,7 @@ struct SweepArgs {
 struct SweepLaunch : SweepArgs {
     const float* proj_start = nullptr;
     const float* proj_end = nullptr;
+    float* xk_ring = nullptr;       // long-duration sweeps: the global ring scratch
 };
 
 // log-semiring sweep: grid (nspans, B, ndir) in MODE_SPEC, (B, ndir) in MODE_REPAIR;
@@ -158,6 +184,11 @@ hipError_t launch_maxplus_round_proj(const SweepCfg& cfg, const SweepLaunch& a, 
 hipError_t launch_maxplus(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream);
 hipError_t launch_maxplus_mirror(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream);
 hipError_t launch_maxplus_plain(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream);
+// long-duration sweeps (cfg.xk): same grids and modes
+hipError_t launch_xk_lse(const XkCfg& xc, const SweepLaunch& a, int ndir, hipStream_t stream);
+hipError_t launch_xk_maxplus(const XkCfg& xc, const SweepLaunch& a, hipStream_t stream);
+// float words of the global ring scratch of the long-duration sweeps (0 in LDS)
+size_t xk_ring_floats(const XkCfg& xc, int C, int workgroups, bool maxp);
 
 // ------------------------------------------------------------------ seam check
 struct SeamArgs {

@@ -16,9 +16,8 @@ int pow2_at_least(int v) {
     return p;
 }
 
-}  // namespace
-
-SweepCfg choose_sweep(int C, int K) {
+// The ring sweeps with every duration weight in registers (short and moderate K).
+SweepCfg choose_ring_sweeps(int C, int K) {
     SweepCfg s{};
     s.ok = false;
     if (C < 1 || K < 1) return s;
@@ -94,12 +93,65 @@ SweepCfg choose_sweep(int C, int K) {
     return s;
 }
 
+}  // namespace
+
+XkCfg choose_xk(int C, int K, bool maxp) {
+    XkCfg x{};
+    x.ok = false;
+    if (C < 1 || K < 2) return x;
+    // lanes per label and duration weights per lane: a whole wavefront per label with 128
+    // weights (512 threads, 256 VGPRs a lane) up to 7 labels, else 64 weights (at most 576
+    // threads, 168 VGPRs a lane)
+    const int G = C <= 7 ? 64 : C <= 16 ? 32 : C <= 64 ? 8 : 0;
+    if (G == 0) return x;
+    const int kplmax = G == 64 ? 128 : 64;
+    int kpl = (K - 1 + G - 1) / G;                       // durations k = 2 .. K
+    kpl = (kpl + XK_UNROLL - 1) / XK_UNROLL * XK_UNROLL;
+    if (kpl > kplmax) return x;
+    x.G = G;
+    x.kplmax = kplmax;
+    x.kpl = kpl;
+    x.NT = 64 + (C * G + 63) / 64 * 64;
+    x.RS = pow2_at_least(K + 2);
+    const int NB = x.NT - 64;
+    // S chunk: every bulk lane stages at most XK_PF values of it
+    x.CH = std::min(64, XK_PF * NB / C);
+    if (x.CH < 1) return x;
+    const size_t base = (size_t)8 * (4 * x.CH * C + C) + (size_t)4 * (C * C + 4 * C + C + 1);
+    const size_t ring = (size_t)4 * (maxp ? 1 : 2) * C * x.RS;
+    x.gring = base + ring > LDS_BUDGET;
+    x.lds = x.gring ? base : base + ring;
+    x.ok = x.lds <= LDS_BUDGET;
+    return x;
+}
+
+size_t xk_ring_floats(const XkCfg& xc, int C, int workgroups, bool maxp) {
+    if (!xc.ok || !xc.gring) return 0;
+    return (size_t)workgroups * (maxp ? 1 : 2) * C * xc.RS;
+}
+
+SweepCfg choose_sweep(int C, int K) {
+    SweepCfg s = choose_ring_sweeps(C, K);
+    s.xk = false;
+    if (K >= XK_FROM || !s.ok) {
+        // long durations: the duration weights no longer fit the lanes' registers
+        s.xk_lse = choose_xk(C, K, false);
+        s.xk_vit = choose_xk(C, K, true);
+        if (s.xk_lse.ok && s.xk_vit.ok) {
+            s.xk = true;
+            s.ok = true;
+        }
+    }
+    return s;
+}
+
 // A span's state converges to the exact one (up to a constant) within about 1.25 K
 // positions on every workload tried; the seam compares the K positions before the span, so
 // the burn-in is 3 K (at least 64 positions for small K).
 int spec_warm(int K) { return std::max(3 * K, 64); }
 
 hipError_t launch_lse(const SweepCfg& cfg, const SweepLaunch& a, int ndir, hipStream_t stream) {
+    if (cfg.xk) return launch_xk_lse(cfg.xk_lse, a, ndir, stream);
     switch (cfg.lse.layout) {
         case SWEEP_MIRRORED | SWEEP_LINEAR: return launch_lse_mirror(cfg, a, ndir, stream);
         case SWEEP_LINEAR: return launch_lse_plain(cfg, a, ndir, stream);
@@ -109,6 +161,7 @@ hipError_t launch_lse(const SweepCfg& cfg, const SweepLaunch& a, int ndir, hipSt
 }
 
 hipError_t launch_maxplus(const SweepCfg& cfg, const SweepLaunch& a, hipStream_t stream) {
+    if (cfg.xk) return launch_xk_maxplus(cfg.xk_vit, a, stream);
     switch (cfg.vit.layout) {
         case SWEEP_MIRRORED: return launch_maxplus_mirror(cfg, a, stream);
         case 0: return launch_maxplus_plain(cfg, a, stream);

@@ -1,0 +1,547 @@
+// Streaming sweeps for long maximum durations (K up to 8193) on gfx950: the log-semiring
+// sweep (forward and mirrored backward) and the max-plus sweep (Viterbi) in one template.
+//
+// Method ("Streaming Structured Inference with Flash-SemiCRF", gist.science EN explainer,
+// "2. Methodology", and the genome-scale regime of "4. Results and Benchmarks", where the
+// maximum duration reaches thousands of positions).  The factored recurrence
+//     abar[s, c]  = (+)_{c'} (alpha[s, c'] + trans[c', c])
+//     alpha[t, c] = S[t, c] + (+)_k (abar[t-k, c] - S[t-k, c] + dur[k-1, c])
+// with (+) the log-sum-exp (log semiring) or max (max-plus), keeps per label a ring of
+// A[s, c] = abar[s, c] - S[s, c] for the last K positions.  For large K the ring is the
+// only large state: K*C floats per ring, 192 KB at K = 8000, C = 6, more than the LDS of
+// a compute unit.  Where it fits, the ring sits in LDS; otherwise in a per-workgroup slice
+// of global memory, read through the L2 cache (the pages' fused kernel keeps its ring in
+// on-chip memory, which caps K there).
+//
+// Work layout: one workgroup per (checkpoint span, sequence, direction), as the other
+// sweeps (burn-in, seam windows, end checkpoint, in-order repair).
+//  * chain wavefront (threads 0..63): lane c holds label c.  At position t it combines
+//    the bulk value of t (durations k >= 2, from the bulk wavefronts) with the k = 1 term
+//    from its own register, forms alpha(t, c), runs the transition step over every label
+//    (lane broadcasts) and writes the ring entry A(t, c).
+//  * bulk wavefronts (threads 64..): G lanes per label (G <= 64, inside one wavefront).
+//    At position t they form the bulk value of t+1 over the ring entries of positions
+//    <= t-1: lane j owns durations k = 2 + j + i*G, i < KPL, with the duration weights in
+//    registers (up to 128 per lane: 512 threads, two wavefronts per SIMD, 256 VGPRs).
+//    One workgroup barrier per position.
+// Log semiring: the bulk sum is linear in fp32 (E = 2^(A - B_c), weights 2^(dur - dmax)),
+// range-checked per wavefront and, outside range, recomputed exactly in log space from the
+// log ring; the chain works in log space throughout (a few exponentials per position).
+// Max-plus: the bulk is a max with the lowest k on ties, the chain's k = 1 term wins ties.
+// Values are fp32 relative to per-label fp64 bases B_c (moved every XK_REBASE positions)
+// and a common fp64 reference H; outputs fp64, natural-log units.
+#pragma once
+
+#include "common.h"
+#include "internal.h"
+
+namespace semicrf {
+
+namespace {
+
+constexpr float XK_LIN_LO = 0x1p-60f;   // linear partial sums trusted inside this range
+constexpr float XK_LIN_HI = 0x1p+60f;
+
+__device__ __forceinline__ bool xk_in_range(float s) {
+    constexpr uint32_t lo = __builtin_bit_cast(uint32_t, XK_LIN_LO);
+    constexpr uint32_t hi = __builtin_bit_cast(uint32_t, XK_LIN_HI);
+    return __float_as_uint(s) - lo <= hi - lo;
+}
+
+// some lane of the wavefront
+__device__ __forceinline__ bool xk_wave_any(bool v) { return __builtin_amdgcn_ballot_w64(v) != 0; }
+
+__device__ __forceinline__ double xk_nan() { return __longlong_as_double(0x7ff8000000000000LL); }
+
+// 2^x, 0 for x <= -126 (NEG included); +inf past the fp32 range (a linear sum holding it
+// fails the range check and is redone in log space)
+__device__ __forceinline__ float xk_exp2(float x) { return x > -126.0f ? fast_exp2(x) : 0.0f; }
+
+// log2(2^a + 2^b), NEG when both are NEG
+__device__ __forceinline__ float xk_lse2(float a, float b) {
+    const float m = fmaxf(a, b);
+    if (m <= NEG_HALF) return NEG;
+    return m + fast_log2(xk_exp2(a - m) + xk_exp2(b - m));
+}
+
+// exact 2^-n for a whole number n (the scale of a whole-octave rebase)
+__device__ __forceinline__ float xk_pow2_neg(float n) {
+    return __builtin_amdgcn_ldexpf(1.0f, -(int)n);
+}
+
+}  // namespace
+
+// MAXP: max-plus (Viterbi) instead of the log semiring.  GRING: the ring in global memory
+// (XkParams::ring) instead of LDS.  G: bulk lanes per label (<= 64); KPLMAX: duration
+// weights per lane (registers); NTMAX: the largest block.
+// Block: 64 + ceil(C*G/64)*64 threads.  Grid: (nspans, B, ndir) in MODE_SPEC, (B, ndir) in
+// MODE_REPAIR (ndir = 1 for max-plus).
+template <bool MAXP, bool GRING, int G, int KPLMAX, int NTMAX>
+__global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkParams x,
+                                                   const float* __restrict__ proj_start,
+                                                   const float* __restrict__ proj_end) {
+    static_assert(G <= 64, "a label's lanes share one wavefront");
+    constexpr int U = XK_UNROLL;
+    constexpr double SC = MAXP ? 1.0 : LOG2E;      // working units: natural (max) or base 2
+    constexpr double OUT = MAXP ? 1.0 : LN2;       // back to natural-log units
+    extern __shared__ double lds[];
+    const int C = a.C, K = a.K, T = a.T;
+    const int tid = threadIdx.x, NT = blockDim.x, NB = NT - 64;
+    const bool chain = __builtin_amdgcn_readfirstlane(tid >> 6) == 0;
+    const int bt = tid - 64;
+    const int cb = chain ? C : bt / G;
+    const int j = chain ? 0 : bt - cb * G;
+    const bool bact = !chain && cb < C;
+    const bool cact = chain && tid < C;
+    const int cl = cact ? tid : 0;
+    const int RS = x.RS, RMASK = RS - 1, CH = x.CH, kplr = x.kpl;
+
+    const bool spec = a.mode == MODE_SPEC;
+    int b, span, dir;
+    if (spec) {
+        span = blockIdx.x; b = blockIdx.y; dir = blockIdx.z;
+    } else {
+        b = blockIdx.x; dir = blockIdx.y; span = 0;
+    }
+    const int Lr = a.Leff[b];
+    const bool bad = Lr < 0;
+    const int L = bad ? -Lr : Lr;
+    int t0 = 0, t1 = L, tout = 0;
+    if (spec) {
+        tout = span * a.delta;
+        if (tout >= L) return;
+        t1 = min(L, tout + a.delta);
+        t0 = max(0, tout - a.warm);
+    } else {
+        span = a.first_bad[dir * a.B + b];
+        if (span >= a.nspans) return;
+        tout = span * a.delta;
+        if (tout >= L) return;
+        t0 = tout;
+    }
+    const bool ckpt = spec && t1 < L;
+    const int hlo = (spec && span > 0) ? tout - K + 1 : INT_MAX;    // seam windows
+    const int tlo = ckpt ? t1 - K + 1 : INT_MAX;
+    const size_t drow = (size_t)dir * a.B + b;   // (direction, sequence) row
+    const size_t winrow = (drow * a.nspans + span) * K;
+    const size_t ckrow = drow * a.nspans;
+    auto window = [&](int t, double av) {                 // chain lanes
+        if (t >= hlo && t <= tout) a.head[(winrow + t - hlo) * C + cl] = av;
+        if (t >= tlo && t <= t1) a.tail[(winrow + t - tlo) * C + cl] = av;
+    };
+
+    // ---------------------------------------------------------------- LDS
+    const int rowsN = CH * C;
+    double* Sbuf = lds;                                   // [2 chunks][end, start][CH][C]
+    double* SL = Sbuf + 4 * rowsN;                        // [C]
+    float* trl = (float*)(SL + C);                        // [C][C]: trl[c' * C + c]
+    float* part = trl + C * C;                            // [2][C][2] bulk values
+    float* dlsh = part + 4 * C;                           // [C] rebase shift
+    int* rebsh = (int*)(dlsh + C);                        // [1] position of the last rebase
+    float* Rl = (float*)(rebsh + 1);                      // [C][RS] log ring (LDS form)
+    float* El = Rl + (size_t)C * RS;                      // [C][RS] linear ring (LDS form)
+    // ring rows of this workgroup's label (bulk lanes) or of any label (chain lanes)
+    float* Rbase;
+    float* Ebase;
+    if constexpr (GRING) {
+        const size_t wg = drow * a.nspans + span;        // a repair reuses its span's slice
+        Rbase = x.ring + wg * (size_t)(MAXP ? 1 : 2) * C * RS;
+        Ebase = Rbase + (size_t)C * RS;
+    } else {
+        Rbase = Rl;
+        Ebase = El;
+    }
+    const int crow = bact ? cb : 0;
+    float* Rrow = Rbase + (size_t)crow * RS;
+    float* Erow = Ebase + (size_t)crow * RS;
+
+    const double* Sb = a.S + (size_t)b * (T + 1) * C;
+    for (int q = tid; q < C; q += NT) SL[q] = Sb[(size_t)L * C + q];
+    const float* PSb = proj_start ? proj_start + (size_t)b * T * C : nullptr;
+    const float* PEb = proj_end ? proj_end + (size_t)b * T * C : nullptr;
+    // projections of sweep position p in working units: end side (segments ending at p)
+    // and start side (segments starting at p); 0 without projections or outside the
+    // sequence.  The mirrored direction swaps their roles.
+    auto proj_e = [&](int p, int q) -> double {
+        const float* src = dir == 0 ? PEb : PSb;
+        const int t = dir == 0 ? p - 1 : L - p;
+        return (src && p >= 1 && p <= L) ? (double)src[(size_t)t * C + q] * SC : 0.0;
+    };
+    auto proj_s = [&](int p, int q) -> double {
+        const float* src = dir == 0 ? PSb : PEb;
+        const int t = dir == 0 ? p : L - 1 - p;
+        return (src && p >= 0 && p < L) ? (double)src[(size_t)t * C + q] * SC : 0.0;
+    };
+    // transitions into each label (transposed for the mirrored direction)
+    for (int q = tid; q < C * C; q += NT) {
+        const int cp = q / C, c = q - cp * C;
+        const float tv = dir == 0 ? a.trans[cp * C + c] : a.trans[c * C + cp];
+        trl[q] = fmaxf((float)((double)tv * SC), NEG);
+    }
+    // ring: every slot cleared (log NEG, linear 0)
+    for (size_t q = tid; q < (size_t)C * RS; q += NT) {
+        Rbase[q] = NEG;
+        if constexpr (!MAXP) Ebase[q] = 0.0f;
+    }
+    if (tid == 0) *rebsh = INT_MIN;
+
+    // ---------------------------------------------------------------- durations
+    auto durv = [&](int c, int k) -> float {
+        return (k >= 1 && k <= K) ? fmaxf((float)((double)a.dur[(k - 1) * C + c] * SC), NEG) : NEG;
+    };
+    // bulk lanes: weights of durations k = 2 + j + i*G (linear, relative to the label's
+    // largest duration score dmax, or log for max-plus); NEG / 0 past K
+    float Dw[KPLMAX];
+    float dmx = NEG;
+#pragma unroll
+    for (int i = 0; i < KPLMAX; ++i) {
+        Dw[i] = (bact && i < kplr) ? durv(cb, 2 + j + i * G) : NEG;
+        dmx = fmaxf(dmx, Dw[i]);
+    }
+    if (!chain) dmx = group_reduce<G>(dmx, OpMax());
+    const float dmax = dmx > NEG_HALF ? dmx : 0.0f;
+    if constexpr (!MAXP) {
+#pragma unroll
+        for (int i = 0; i < KPLMAX; ++i) Dw[i] = xk_exp2(Dw[i] - dmax);
+    }
+    const float d1 = cact ? durv(cl, 1) : NEG;            // chain: the k = 1 term
+
+    // ---------------------------------------------------------------- start state
+    auto slot = [&](int p) { return p & RMASK; };
+    double Bc = 0.0, H = 0.0;
+    float Rn1 = NEG;                                      // chain: A(t-1) - B_c
+    float Mref = 0.0f;                                    // chain: last bulk value (rebase)
+    if (t0 == 0) {
+        // position 0: no transition into it; its ring entry is its start-side projection
+        if (bact && j == 0) {
+            const float r0 = fmaxf((float)proj_s(0, cb), NEG);
+            Rrow[slot(0)] = r0;
+            if constexpr (!MAXP) Erow[slot(0)] = xk_exp2(r0);
+        }
+        Rn1 = cact ? fmaxf((float)proj_s(0, cl), NEG) : NEG;
+    } else if (spec) {
+        // burn-in start: every ring entry of positions t0-K+1 .. t0 equal (0)
+        if (bact)
+            for (int q = j; q < K && t0 - q >= 0; q += G) {
+                Rrow[slot(t0 - q)] = 0.0f;
+                if constexpr (!MAXP) Erow[slot(t0 - q)] = 1.0f;
+            }
+        Rn1 = cact ? 0.0f : NEG;
+    } else {
+        const size_t ck = ckrow + span;
+        if (bact)
+            for (int q = j; q < K && t0 - q >= 0; q += G) {
+                const float rv = a.ck_ring[(ck * K + q) * C + cb];
+                Rrow[slot(t0 - q)] = rv;
+                if constexpr (!MAXP) Erow[slot(t0 - q)] = xk_exp2(rv);
+            }
+        if (chain) {
+            Bc = a.ck_base[ck * C + cl];
+            H = a.ck_href[ck];
+            Mref = a.ck_mprev[ck * C + cl];
+            Rn1 = cact ? a.ck_ring[(ck * K + 0) * C + cl] : NEG;
+        }
+    }
+    const size_t outrow = (size_t)b * (T + 1);
+    double* Xout = dir == 0 ? a.XF : a.XB;
+    double* Aout = dir == 0 ? a.AF : a.AB;
+    if (cact) {
+        const double a0 = (Bc + (double)Rn1) * OUT;
+        if (!MAXP && a.write_xa && t0 == tout) Aout[(outrow + (dir == 0 ? t0 : L - t0)) * C + cl] = a0;
+        if (t0 == 0)   // window positions <= 0: position 0's value, nothing before it
+            for (int p = min(hlo, tlo); p <= 0; ++p) window(p, p == 0 ? a0 : -1.0e300);
+    }
+
+    // ---------------------------------------------------------------- S staging
+    // chunk n holds rows t = t0 + 1 + n*CH + r, r < CH: end side S(t) + pe(t) and start
+    // side S(t) - ps(t), working units; staged by the bulk lanes one chunk ahead
+    auto sidx = [&](int t, int q) -> size_t { return (size_t)(dir == 0 ? t : L - t) * C + q; };
+    auto spub = [&](double raw, int q) -> double { return dir == 0 ? raw * SC : (SL[q] - raw) * SC; };
+    __syncthreads();                                      // SL visible
+    const int pfn = (rowsN + NB - 1) / NB;                // staged values per bulk lane
+    if (!chain)
+        for (int q = bt; q < rowsN; q += NB) {
+            const int row = q / C, l = q - row * C;
+            const int t = t0 + 1 + row;
+            const bool in = t <= t1;
+            const double sv = in ? spub(Sb[sidx(t, l)], l) : 0.0;
+            Sbuf[q] = in ? sv + proj_e(t, l) : 0.0;
+            Sbuf[rowsN + q] = in ? sv - proj_s(t, l) : 0.0;
+        }
+    // the chunk after next is fetched into registers (at most XK_PF per lane)
+    double pf[XK_PF], pfe[XK_PF], pfs[XK_PF];
+    auto stage_fetch = [&](int tcs) {
+#pragma unroll
+        for (int i = 0; i < XK_PF; ++i) {
+            const int q = bt + i * NB;
+            pf[i] = pfe[i] = pfs[i] = 0.0;
+            if (!chain && i < pfn && q < rowsN) {
+                const int row = q / C, l = q - row * C;
+                const int t = tcs + row;
+                if (t <= t1) {
+                    pf[i] = Sb[sidx(t, l)];
+                    pfe[i] = proj_e(t, l);
+                    pfs[i] = proj_s(t, l);
+                }
+            }
+        }
+    };
+    auto stage_store = [&](int buf) {
+        double* dst = Sbuf + buf * 2 * rowsN;
+#pragma unroll
+        for (int i = 0; i < XK_PF; ++i) {
+            const int q = bt + i * NB;
+            if (!chain && i < pfn && q < rowsN) {
+                const double sv = spub(pf[i], q - (q / C) * C);
+                dst[q] = sv + pfe[i];
+                dst[rowsN + q] = sv - pfs[i];
+            }
+        }
+    };
+    stage_fetch(t0 + 1 + CH);
+    __syncthreads();                                      // ring, chunk 0 visible
+
+    // ---------------------------------------------------------------- bulk value
+    // of position tq over durations k >= 2 (ring entries of positions <= tq - 2): log value
+    // (both semirings) and, for max-plus, the lowest k attaining it; written to
+    // part[tq & 1][label]
+    auto bulk = [&](int tq) {
+        const int p0 = tq - 2 - j;                        // position of k = 2 + j (i = 0)
+        float qv = NEG;
+        int kq = INT_MAX;
+        if constexpr (MAXP) {
+            float best = NEG;
+            int kb = INT_MAX;
+#pragma unroll
+            for (int i0 = 0; i0 < KPLMAX; i0 += U) {
+                if (i0 < kplr) {
+                    float v[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) v[u] = Rrow[slot(p0 - (i0 + u) * G)];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const float y = v[u] + Dw[i0 + u];
+                        if (y > best) {                   // ascending k: the lowest wins ties
+                            best = y;
+                            kb = 2 + j + (i0 + u) * G;
+                        }
+                    }
+                }
+            }
+            qv = group_reduce<G>(best, OpMax());
+            kq = group_min_int<G>(best == qv && qv > NEG_HALF ? kb : INT_MAX);
+        } else {
+            float acc = 0.0f;
+#pragma unroll
+            for (int i0 = 0; i0 < KPLMAX; i0 += U) {
+                if (i0 < kplr) {
+                    float v[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) v[u] = Erow[slot(p0 - (i0 + u) * G)];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) acc = fmaf(v[u], Dw[i0 + u], acc);
+                }
+            }
+            acc = group_reduce<G>(acc, OpSum());
+            const bool ok = xk_in_range(acc) || !bact;   // per label group
+            qv = fast_log2(acc) + dmax;
+            if (xk_wave_any(!ok)) {
+                // exact log-space sum (log ring, the duration scores from global memory)
+                float m = NEG, s = 0.0f;
+                for (int i0 = 0; i0 < kplr; i0 += U) {
+                    {
+                        float y[U];
+#pragma unroll
+                        for (int u = 0; u < U; ++u) {
+                            const int k = 2 + j + (i0 + u) * G;
+                            y[u] = Rrow[slot(p0 - (i0 + u) * G)] + (bact ? durv(cb, k) : NEG);
+                        }
+                        float mc = y[0];
+#pragma unroll
+                        for (int u = 1; u < U; ++u) mc = fmaxf(mc, y[u]);
+                        const float mn = fmaxf(m, mc);
+                        if (mn > NEG_HALF) {
+                            s *= xk_exp2(m - mn);
+#pragma unroll
+                            for (int u = 0; u < U; ++u) s += xk_exp2(y[u] - mn);
+                            m = mn;
+                        }
+                    }
+                }
+                const float gm = group_reduce<G>(m, OpMax());
+                float sg = gm > NEG_HALF ? s * xk_exp2(m - gm) : 0.0f;
+                sg = group_reduce<G>(sg, OpSum());
+                const float lg = gm > NEG_HALF ? gm + fast_log2(sg) : NEG;
+                if (!ok) qv = lg;
+            }
+        }
+        if (bact && j == 0) {
+            float* pp = part + ((tq & 1) * C + cb) * 2;
+            pp[0] = qv;
+            pp[1] = __int_as_float(kq);
+        }
+    };
+    // bulk lanes, one position after a rebase at position tr: the live entries of
+    // positions tr-K+1 .. tr-1 this lane reads for the bulk of tr + 2 move to the new base
+    // (the entry of tr was written in it; older ones are never weighted again, and the
+    // ring holds RS >= K + 2 positions, so every live slot is moved exactly once)
+    auto rebase_ring = [&](int tq) {
+        const int trb = *rebsh;
+        if (trb != tq - 2 || !bact) return;
+        const float dl = dlsh[cb];
+        const float sc = MAXP ? 1.0f : xk_pow2_neg(dl);
+        const int p0 = tq - 2 - j;
+        for (int i0 = 0; i0 < kplr; i0 += U) {
+            {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int p = p0 - (i0 + u) * G;
+                    if (p <= trb - 1 && p >= trb - K + 1) {
+                        Rrow[slot(p)] -= dl;
+                        if constexpr (!MAXP) Erow[slot(p)] *= sc;
+                    }
+                }
+            }
+        }
+    };
+    if (bact) bulk(t0 + 1);
+    __syncthreads();
+
+    // ---------------------------------------------------------------- main loop
+    double lz = 0.0;
+    float pdl = 0.0f;
+    bool pend = false;
+    for (int tc = t0 + 1, nch = 0; tc <= t1; tc += CH, ++nch) {
+        const double* Sch = Sbuf + (nch & 1) * 2 * rowsN;
+        const int rows = min(CH, t1 - tc + 1);
+        for (int row = 0; row < rows; ++row) {
+            const int t = tc + row;
+            if (chain) {
+                // ---- bulk value of t (and its lowest k for max-plus)
+                const float* pp = part + ((t & 1) * C + cl) * 2;
+                float Q = pp[0];
+                const int kQ = __float_as_int(pp[1]);
+                if (pend) {                               // summed before the last rebase
+                    Q -= pdl;
+                    pend = false;
+                }
+                // ---- rebase: this label's values move to a new base (never at the span's
+                // end, so that the ring is in one base when the checkpoint copies it)
+                if ((t & (XK_REBASE - 1)) == 0 && t < t1) {
+                    const float ref = fmaxf(Mref, Rn1);
+                    float dl = cact && ref > NEG_HALF ? ref : 0.0f;
+                    if constexpr (!MAXP) dl = floorf(dl);  // whole octaves: exact linear scale
+                    Bc += (double)dl;
+                    Rn1 -= dl;
+                    Mref -= dl;
+                    Q -= dl;
+                    if (cact) dlsh[cl] = dl;
+                    if (tid == 0) *rebsh = t;
+                    pdl = dl;
+                    pend = true;
+                }
+                // ---- alpha(t): the k = 1 term and the bulk
+                const double Se = Sch[row * C + cl];                  // end side of t
+                const double Ss = Sch[rowsN + row * C + cl];          // start side of t
+                const float e1 = Rn1 + d1;
+                float sig;
+                int kb = 1;
+                if constexpr (MAXP) {
+                    sig = fmaxf(e1, Q);
+                    kb = (e1 >= Q) ? 1 : kQ;
+                } else {
+                    sig = xk_lse2(e1, Q);
+                }
+                const float u = cact ? (float)(Se + Bc - H) + sig : NEG;  // alpha(t) - H
+                if (!MAXP && cact && a.write_xa && t > tout)
+                    Xout[(outrow + (dir == 0 ? t : L - t)) * C + cl] = (Se + Bc + (double)sig) * OUT;
+                // ---- transition step of t over every label's alpha (lane broadcasts)
+                float mu = NEG;                                        // max_c' u(c')
+                float mt = NEG;                                        // max_c' u + trans
+                int cbest = 0;
+                for (int cp = 0; cp < C; ++cp) {
+                    const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), cp));
+                    const float y = uv + trl[cp * C + cl];
+                    mu = fmaxf(mu, uv);
+                    if (y > mt) {
+                        mt = y;
+                        cbest = cp;
+                    }
+                }
+                float abar = mt;                                       // abar(t) - H
+                if constexpr (!MAXP) {
+                    if (mt > NEG_HALF) {
+                        float s = 0.0f;
+                        for (int cp = 0; cp < C; ++cp) {
+                            const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), cp));
+                            s += xk_exp2(uv + trl[cp * C + cl] - mt);
+                        }
+                        abar = mt + fast_log2(s);
+                    }
+                    if (t == L && mu > NEG_HALF) {                     // log2 Z
+                        float s = 0.0f;
+                        for (int cp = 0; cp < C; ++cp) {
+                            const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), cp));
+                            s += xk_exp2(uv - mu);
+                        }
+                        lz = H + (double)mu + (double)fast_log2(s);
+                    }
+                } else {
+                    if (t == L && cact) a.vfin[(size_t)b * C + cl] = H + (double)u;
+                }
+                const float Rnew = cact ? fmaxf(abar - (float)(Ss + Bc - H), NEG) : NEG;
+                if (MAXP && cact && t > tout)
+                    a.bp[(outrow + t) * C + cl] =
+                        (uint32_t)kb | (t < L ? ((uint32_t)cbest << 16) : 0u);
+                if (mu > NEG_HALF) H += (double)mu;
+                if (cact) {
+                    Rbase[(size_t)cl * RS + slot(t)] = Rnew;
+                    if constexpr (!MAXP)
+                        Ebase[(size_t)cl * RS + slot(t)] = xk_exp2(Rnew);
+                    const double av = (Bc + (double)Rnew) * OUT;
+                    if (!MAXP && a.write_xa && t >= tout && t < t1)
+                        Aout[(outrow + (dir == 0 ? t : L - t)) * C + cl] = av;
+                    if (t >= min(hlo, tlo)) window(t, av);
+                }
+                Rn1 = Rnew;
+                if (Q > NEG_HALF) Mref = Q;
+            } else {
+                // ---- S staging: publish the next chunk, fetch the one after
+                if (row == 0 && tc + CH <= t1) {
+                    stage_store((nch + 1) & 1);
+                    stage_fetch(tc + 2 * CH);
+                }
+                rebase_ring(t + 1);
+                if (t + 1 <= t1 && bact) bulk(t + 1);
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---------------------------------------------------------------- span end
+    if (ckpt) {
+        // the ring in its final base (no rebase at t1; the one before it was applied
+        // during t1) and the chain's state: the checkpoint a repair restarts from
+        const size_t ck = ckrow + t1 / a.delta;
+        if (bact)
+            for (int q = j; q < K; q += G) a.ck_ring[(ck * K + q) * C + cb] = Rrow[slot(t1 - q)];
+        if (cact) {
+            a.ck_base[ck * C + cl] = Bc;
+            a.ck_mprev[ck * C + cl] = Mref;
+        }
+        if (tid == 0) a.ck_href[ck] = H;
+    }
+    if constexpr (!MAXP) {
+        if (t1 == L && tid == 0) {
+            if (spec) {
+                a.lzloc[dir * a.B + b] = lz * LN2;       // the seam check adds the offsets
+            } else {
+                // a repaired sweep continues in the frame of the span before the failed seam
+                const double base = a.off[drow * a.nspans + span - 1];
+                (dir == 0 ? a.logz : a.logz_b)[b] = bad ? xk_nan() : lz * LN2 + base;
+            }
+        }
+    }
+}
+
+}  // namespace semicrf

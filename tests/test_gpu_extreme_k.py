@@ -1,4 +1,4 @@
-"""Long maximum durations (K up to 2049): parity with stored fp64 oracle values, and the
+"""Long maximum durations (K up to 8000): parity with stored fp64 oracle values, and the
 pages' genome-scale case T = 10^6, K = 2000 by properties that hold at any size.
 
 Tolerances as for the rest of the path (log Z and Viterbi score 1e-5 relative; mu,
@@ -63,11 +63,13 @@ def _projections(seed, B, T, C, sd):
             rng.normal(0, sd, (B, T, C)).astype(np.float32))
 
 
-@pytest.mark.parametrize("name", ["x1", "x2", "x3", "x4", "x5"])
+@pytest.mark.parametrize("name", [f"x{i}" for i in range(1, 11)])
 def test_long_durations_against_oracle(crf, name):
     if not os.path.exists(FIXTURE):
         pytest.skip(f"{FIXTURE} not generated")
     f = np.load(FIXTURE, allow_pickle=False)
+    if f"{name}_case" not in f.files:
+        pytest.skip(f"{name} not in {FIXTURE}")
     seed, B, T, C, K, scale, ragged, sd = f[f"{name}_case"]
     seed, B, T, C, K = int(seed), int(B), int(T), int(C), int(K)
     print(f"\n[long durations {name}: B={B} T={T} C={C} K={K} projections sd={sd}]", flush=True)

@@ -60,6 +60,7 @@ CASES = [
     (206, 2, 1200, 24, 10, 1.0, 90),     # 24 labels: one barrier per position
     (207, 2, 1000, 40, 16, 1.0, 0),      # 40 labels
     (208, 2, 600, 64, 8, 1.5, 50),       # 64 labels, 4 lanes per label
+    (209, 1, 6000, 3, 1030, 1.5, 1500),  # long durations: burn-in of 3K from a uniform ring
 ]
 
 
@@ -131,6 +132,7 @@ VIT_CASES = [
     (223, 2, 2000, 16, 20, 1.0),
     (224, 2, 1500, 24, 16, 1.5),
     (225, 2, 1000, 64, 8, 1.5),
+    (226, 1, 5000, 3, 1030, 2.0),        # long durations
 ]
 
 
