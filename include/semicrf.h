@@ -33,10 +33,10 @@
  *    reductions, no floating-point atomics).
  *  - Errors: every call returns a semicrf_status and never aborts.  Host-side
  *    checks: B, T, C, K >= 1, required pointers non-NULL, workspace large enough,
- *    shape supported (SEMICRF_ERR_UNSUPPORTED: C > 128; K above 2049 when C <= 7,
- *    1025 when C = 8, 513 when C <= 16, 257 when C <= 64, and for 64 < C <= 128
- *    whatever the 160 KB of LDS of a compute unit holds: 129 down to 97 at C = 128;
- *    semicrf_workspace_bytes returns 0 for such shapes).  A failed
+ *    shape supported (SEMICRF_ERR_UNSUPPORTED: C > 128; K above 8193 when C <= 7,
+ *    2049 when C <= 16, 513 when C <= 64, and for 64 < C <= 128 whatever the 160 KB
+ *    of LDS of a compute unit holds: 129 down to 97 at C = 128; semicrf_workspace_bytes
+ *    returns 0 for such shapes).  A failed
  *    kernel launch returns SEMICRF_ERR_DEVICE.  A length outside [1, T] is only
  *    visible on the device: that sequence is processed as if clamped to [1, T],
  *    its log Z / Viterbi score is set to NaN, and a flag is raised in the
@@ -79,6 +79,12 @@ const char* semicrf_status_string(int status);
  * else ceil(sqrt(T*K)) (EN explainer, "2. Methodology", "Checkpointing": an interval of
  * about sqrt(TK)); clamped to [1, T].  0 on bad input. */
 int semicrf_checkpoint_interval(int T, int K, int delta);
+
+/* Checkpoint interval of semicrf_viterbi (which takes none) for a batch of B sequences of
+ * padded length T: semicrf_checkpoint_interval(T, K, 0), halved when the batch holds at
+ * most 128 spans of that length and each is at least four burn-ins (12 K) long, so that
+ * the spans swept at once occupy more compute units.  0 on bad input. */
+int semicrf_viterbi_interval(int B, int T, int K);
 
 /* Bytes of workspace that `op` needs for these shapes (delta as above).  0 if the
  * arguments are invalid or unsupported. */

@@ -238,6 +238,7 @@ struct MargArgs {
     int tile;               // positions per tile
     int kchunk;             // durations per staged chunk
     int ntiles;             // ceil((T+1) / tile)
+    int tpg, ngroups;       // tiles per group of the duration / transition partials
     const double* XF; const double* AF; const double* XB; const double* AB;
     const double* logz;
     // frame offsets of the speculative spans, [2 dirs][B][nspans] (NULL: none): added to
@@ -247,12 +248,15 @@ struct MargArgs {
     int delta, nspans;
     double* Dn;             // [B][T+1][C]: start mass - end mass of segments at each position
     double* dn_tile;        // [B][ntiles][C]: tile sums of Dn
-    double* part_dur;       // [B][ntiles][K][C]
-    double* part_trans;     // [B][ntiles][C][C]
+    double* part_dur;       // [B][ngroups][K][C]: sums over a group's tiles
+    double* part_trans;     // [B][ngroups][C][C]
     float* pstart;          // [B][T][C] or NULL: start mass of segments at each position
     float* pend;            // [B][T][C] or NULL: mass of segments whose last position it is
 };
 hipError_t launch_marginals(const MargArgs& a, hipStream_t stream);
+// tiles per group of the posterior partials: enough groups to fill the device, the
+// partials (B * groups * (K + C) * C doubles) within a fixed budget
+int marg_tiles_per_group(int B, int ntiles, int C, int K);
 
 // mu = prefix sum of Dn, normalised per position; writes marginals, per-tile sums of
 // mu and the per-tile mean normaliser.  With pstart / pend (the raw start and end masses
@@ -278,7 +282,7 @@ hipError_t launch_grad_em(const float* mu, const double* mu_tot, const int* Leff
 size_t reduce_scratch_doubles(int C, int K);
 hipError_t launch_reduce_partials(const double* part_dur, const double* part_trans,
                                   const double* z_tile, const int* Leff, const float* grad_log_z,
-                                  int B, int T, int C, int K, int tile, int ntiles,
+                                  int B, int C, int K, int tile, int ntiles, int tpg,
                                   double* scratch, float* grad_dur, float* grad_trans,
                                   hipStream_t stream);
 hipError_t launch_write_logz(const double* logz, int B, float* out, hipStream_t stream);

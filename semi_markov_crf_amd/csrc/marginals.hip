@@ -87,15 +87,16 @@ int marg_kchunk(int C, int K) {
 
 constexpr double DNEG = -1.0e300;
 
-// grid (ntiles, B), block 256.  Durations are taken in chunks [kc0, kc1] of at most KC:
-// per chunk the starts [p0 - kc1, p0 + TM - 1 - kc0] and the ends [p0 + kc0,
-// p0 + TM - 1 + kc1] are staged beside the tile's own starts and ends.
+// grid (ngroups, B), block 256: the tiles g*tpg .. (g+1)*tpg - 1 of sequence b in order.
+// Durations are taken in chunks [kc0, kc1] of at most KC: per chunk the starts
+// [p0 - kc1, p0 + TM - 1 - kc0] and the ends [p0 + kc0, p0 + TM - 1 + kc1] are staged
+// beside the tile's own starts and ends.  The duration and transition partials of the
+// group's tiles are summed in tile order (each lane owns the same entries in every tile).
 __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
     extern __shared__ double lds[];
     const int C = a.C, K = a.K, T = a.T, TM = a.tile, KC = a.kchunk;
-    const int tile = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int L = abs(a.Leff[b]);
-    const int p0 = tile * TM;
     const size_t rowC = (size_t)(T + 1) * C;
 
     double* AFt = lds;                               // [TM][C]: starts p0 .. p0+TM-1
@@ -109,137 +110,156 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
     float* dur2 = (float*)(Den + (size_t)TM * C);    // [KC][C]
     float* tr2 = dur2 + (size_t)KC * C;              // [C][C]
 
-    double* part_dur = a.part_dur + ((size_t)b * a.ntiles + tile) * K * C;
-    double* part_trans = a.part_trans + ((size_t)b * a.ntiles + tile) * C * C;
-    double* dn_tile = a.dn_tile + ((size_t)b * a.ntiles + tile) * C;
+    double* part_dur = a.part_dur + ((size_t)b * a.ngroups + g) * K * C;
+    double* part_trans = a.part_trans + ((size_t)b * a.ngroups + g) * C * C;
     double* Dn = a.Dn + (size_t)b * rowC;
-
-    if (p0 > L) {   // nothing of this sequence here
-        for (int q = tid; q < K * C; q += 256) part_dur[q] = 0.0;
-        for (int q = tid; q < C * C; q += 256) part_trans[q] = 0.0;
-        for (int q = tid; q < C; q += 256) dn_tile[q] = 0.0;
-        for (int q = tid; q < TM * C; q += 256)
-            if (p0 + q / C <= T) Dn[(size_t)p0 * C + q] = 0.0;
-        return;
-    }
-    const double logZ = a.logz[b];
-    const double* Sb = a.S + (size_t)b * rowC;
-    const double* XF = a.XF + (size_t)b * rowC;
-    const double* AF = a.AF + (size_t)b * rowC;
-    const double* XB = a.XB + (size_t)b * rowC;
-    const double* AB = a.AB + (size_t)b * rowC;
-    // frame offsets of the spans that wrote each value (0 without speculative spans):
-    // forward X / A of position s from span floor((s-1)/delta) / floor(s/delta), backward
-    // ones of s from the mirrored position L - s
-    const double* offF = a.off ? a.off + (size_t)b * a.nspans : nullptr;
-    const double* offB = a.off ? a.off + ((size_t)a.B + b) * a.nspans : nullptr;
-    auto oAF = [&](int s) { return offF ? offF[s / a.delta] : 0.0; };
-    auto oXF = [&](int s) { return offF ? offF[(s - 1) / a.delta] : 0.0; };
-    auto oAB = [&](int u) { return offB ? offB[(L - u) / a.delta] : 0.0; };
-    auto oXB = [&](int s) { return offB ? offB[(L - s - 1) / a.delta] : 0.0; };
-    // staged in base 2 (times log2 e); invalid starts / ends get DNEG so that their
-    // exponentials vanish
-    auto af = [&](int s, int c) -> double {
-        return (s >= 0 && s <= L - 1)
-                   ? (AF[(size_t)s * C + c] + oAF(s) + Sb[(size_t)L * C + c] - logZ) * LOG2E
-                   : DNEG;
-    };
-    auto ab = [&](int u, int c) -> double {
-        return (u >= 1 && u <= L) ? (AB[(size_t)u * C + c] + oAB(u)) * LOG2E : DNEG;
-    };
-
-    for (int q = tid; q < TM * C; q += 256) {
-        const int r = q / C, c = q - r * C;
-        const int s = p0 + r;
-        AFt[q] = af(s, c);
-        ABt[q] = ab(s, c);
-        XFs[q] = (s >= 1 && s <= L - 1) ? (XF[(size_t)s * C + c] + oXF(s)) * LOG2E : DNEG;
-        XBs[q] = (s >= 1 && s <= L - 1) ? (XB[(size_t)s * C + c] + oXB(s) - logZ) * LOG2E
-                                        : DNEG;
-        Dst[q] = 0.0;
-        Den[q] = 0.0;
-    }
+    for (int q = tid; q < K * C; q += 256) part_dur[q] = 0.0;
+    for (int q = tid; q < C * C; q += 256) part_trans[q] = 0.0;
     for (int q = tid; q < C * C; q += 256) tr2[q] = fmaxf((float)((double)a.trans[q] * LOG2E), NEG);
-
-    auto seg = [&](double v, float d) -> float { return fast_exp2((float)v + d); };
-
-    for (int kc0 = 1; kc0 <= K; kc0 += KC) {
-        const int kc1 = min(K, kc0 + KC - 1);
-        const int nk = kc1 - kc0 + 1;
-        __syncthreads();   // the previous chunk's windows are no longer read
-        for (int q = tid; q < (TM + nk - 1) * C; q += 256) {
-            const int r = q / C, c = q - r * C;
-            AFw[q] = af(p0 - kc1 + r, c);
-            ABw[q] = ab(p0 + kc0 + r, c);
+    const int tile_end = min(a.ntiles, (g + 1) * a.tpg);
+    for (int tile = g * a.tpg; tile < tile_end; ++tile) {
+        const int p0 = tile * TM;
+        double* dn_tile = a.dn_tile + ((size_t)b * a.ntiles + tile) * C;
+        if (p0 > L) {   // nothing of this sequence here
+            for (int q = tid; q < C; q += 256) dn_tile[q] = 0.0;
+            for (int q = tid; q < TM * C; q += 256)
+                if (p0 + q / C <= T) Dn[(size_t)p0 * C + q] = 0.0;
+            continue;
         }
-        for (int q = tid; q < nk * C; q += 256)
-            dur2[q] = fmaxf((float)((double)a.dur[(size_t)(kc0 - 1) * C + q] * LOG2E), NEG);
-        __syncthreads();
+        const double logZ = a.logz[b];
+        const double* Sb = a.S + (size_t)b * rowC;
+        const double* XF = a.XF + (size_t)b * rowC;
+        const double* AF = a.AF + (size_t)b * rowC;
+        const double* XB = a.XB + (size_t)b * rowC;
+        const double* AB = a.AB + (size_t)b * rowC;
+        // frame offsets of the spans that wrote each value (0 without speculative spans):
+        // forward X / A of position s from span floor((s-1)/delta) / floor(s/delta), backward
+        // ones of s from the mirrored position L - s
+        const double* offF = a.off ? a.off + (size_t)b * a.nspans : nullptr;
+        const double* offB = a.off ? a.off + ((size_t)a.B + b) * a.nspans : nullptr;
+        auto oAF = [&](int s) { return offF ? offF[s / a.delta] : 0.0; };
+        auto oXF = [&](int s) { return offF ? offF[(s - 1) / a.delta] : 0.0; };
+        auto oAB = [&](int u) { return offB ? offB[(L - u) / a.delta] : 0.0; };
+        auto oXB = [&](int s) { return offB ? offB[(L - s - 1) / a.delta] : 0.0; };
+        // staged in base 2 (times log2 e); invalid starts / ends get DNEG so that their
+        // exponentials vanish
+        auto af = [&](int s, int c) -> double {
+            return (s >= 0 && s <= L - 1)
+                       ? (AF[(size_t)s * C + c] + oAF(s) + Sb[(size_t)L * C + c] - logZ) * LOG2E
+                       : DNEG;
+        };
+        auto ab = [&](int u, int c) -> double {
+            return (u >= 1 && u <= L) ? (AB[(size_t)u * C + c] + oAB(u)) * LOG2E : DNEG;
+        };
 
-        // ---- phase 1: per position, start and end mass of the chunk's segments
         for (int q = tid; q < TM * C; q += 256) {
             const int r = q / C, c = q - r * C;
-            if (p0 + r > L) continue;
-            double st = Dst[q], en = Den[q];
-            const double a0 = AFt[q], b0 = ABt[q];
-#pragma unroll 4
-            for (int k = kc0; k <= kc1; ++k) {
-                const float d = dur2[(k - kc0) * C + c];
-                st += (double)seg(a0 + ABw[(size_t)(r + k - kc0) * C + c], d);   // [t, t+k)
-                en += (double)seg(AFw[(size_t)(r + kc1 - k) * C + c] + b0, d);   // [t-k, t)
+            const int s = p0 + r;
+            AFt[q] = af(s, c);
+            ABt[q] = ab(s, c);
+            XFs[q] = (s >= 1 && s <= L - 1) ? (XF[(size_t)s * C + c] + oXF(s)) * LOG2E : DNEG;
+            XBs[q] = (s >= 1 && s <= L - 1) ? (XB[(size_t)s * C + c] + oXB(s) - logZ) * LOG2E
+                                            : DNEG;
+            Dst[q] = 0.0;
+            Den[q] = 0.0;
+        }
+
+        auto seg = [&](double v, float d) -> float { return fast_exp2((float)v + d); };
+
+        for (int kc0 = 1; kc0 <= K; kc0 += KC) {
+            const int kc1 = min(K, kc0 + KC - 1);
+            const int nk = kc1 - kc0 + 1;
+            __syncthreads();   // the previous chunk's windows are no longer read
+            for (int q = tid; q < (TM + nk - 1) * C; q += 256) {
+                const int r = q / C, c = q - r * C;
+                AFw[q] = af(p0 - kc1 + r, c);
+                ABw[q] = ab(p0 + kc0 + r, c);
             }
-            Dst[q] = st;
-            Den[q] = en;
-        }
+            for (int q = tid; q < nk * C; q += 256)
+                dur2[q] = fmaxf((float)((double)a.dur[(size_t)(kc0 - 1) * C + q] * LOG2E), NEG);
+            __syncthreads();
 
-        // ---- phase 2: duration partials, lanes over (k, c), segments starting in the tile
-        for (int q = tid; q < nk * C; q += 256) {
-            const int kk = q / C, c = q - kk * C;
-            const float d = dur2[q];
-            double acc = 0.0;
+            // ---- phase 1: per position, start and end mass of the chunk's segments
+            for (int q = tid; q < TM * C; q += 256) {
+                const int r = q / C, c = q - r * C;
+                if (p0 + r > L) continue;
+                double st = Dst[q], en = Den[q];
+                const double a0 = AFt[q], b0 = ABt[q];
 #pragma unroll 4
-            for (int r = 0; r < TM; ++r)
-                acc += (double)seg(AFt[(size_t)r * C + c] + ABw[(size_t)(r + kk) * C + c], d);
-            part_dur[(size_t)(kc0 - 1) * C + q] = acc;
-        }
-    }
-    __syncthreads();
+                for (int k = kc0; k <= kc1; ++k) {
+                    const float d = dur2[(k - kc0) * C + c];
+                    st += (double)seg(a0 + ABw[(size_t)(r + k - kc0) * C + c], d);   // [t, t+k)
+                    en += (double)seg(AFw[(size_t)(r + kc1 - k) * C + c] + b0, d);   // [t-k, t)
+                }
+                Dst[q] = st;
+                Den[q] = en;
+            }
 
-    // ---- start mass - end mass per position, the tile's sums, boundary masses
-    for (int q = tid; q < TM * C; q += 256) {
-        const int r = q / C, c = q - r * C;
-        const int t = p0 + r;
-        const double st = Dst[q], en = Den[q];
-        const double d = st - en;
-        Dst[q] = d;
-        if (t <= T) Dn[(size_t)t * C + c] = d;
-        if (a.pstart && t < L) a.pstart[((size_t)b * T + t) * C + c] = (float)st;
-        if (a.pend && t >= 1 && t <= L) a.pend[((size_t)b * T + t - 1) * C + c] = (float)en;
-    }
-    __syncthreads();
-    for (int c = tid; c < C; c += 256) {
-        double s = 0.0;
-        for (int r = 0; r < TM; ++r) s += Dst[(size_t)r * C + c];
-        dn_tile[c] = s;
-    }
-
-    // ---- phase 3: transition partials, lanes over (c', c)
-    for (int q = tid; q < C * C; q += 256) {
-        const int cp = q / C, c = q - cp * C;
-        const float tv = tr2[q];
-        double acc = 0.0;
-        for (int r = 0; r < TM; ++r) {
-            const double v = XFs[(size_t)r * C + cp] + XBs[(size_t)r * C + c];
-            acc += (double)fast_exp2((float)v + tv);
+            // ---- phase 2: duration partials, lanes over (k, c), segments starting in the tile
+            for (int q = tid; q < nk * C; q += 256) {
+                const int kk = q / C, c = q - kk * C;
+                const float d = dur2[q];
+                double acc = 0.0;
+#pragma unroll 4
+                for (int r = 0; r < TM; ++r)
+                    acc += (double)seg(AFt[(size_t)r * C + c] + ABw[(size_t)(r + kk) * C + c], d);
+                part_dur[(size_t)(kc0 - 1) * C + q] += acc;
+            }
         }
-        part_trans[q] = acc;
+        __syncthreads();
+
+        // ---- start mass - end mass per position, the tile's sums, boundary masses
+        for (int q = tid; q < TM * C; q += 256) {
+            const int r = q / C, c = q - r * C;
+            const int t = p0 + r;
+            const double st = Dst[q], en = Den[q];
+            const double d = st - en;
+            Dst[q] = d;
+            if (t <= T) Dn[(size_t)t * C + c] = d;
+            if (a.pstart && t < L) a.pstart[((size_t)b * T + t) * C + c] = (float)st;
+            if (a.pend && t >= 1 && t <= L) a.pend[((size_t)b * T + t - 1) * C + c] = (float)en;
+        }
+        __syncthreads();
+        for (int c = tid; c < C; c += 256) {
+            double s = 0.0;
+            for (int r = 0; r < TM; ++r) s += Dst[(size_t)r * C + c];
+            dn_tile[c] = s;
+        }
+
+        // ---- phase 3: transition partials, lanes over (c', c)
+        for (int q = tid; q < C * C; q += 256) {
+            const int cp = q / C, c = q - cp * C;
+            const float tv = tr2[q];
+            double acc = 0.0;
+            for (int r = 0; r < TM; ++r) {
+                const double v = XFs[(size_t)r * C + cp] + XBs[(size_t)r * C + c];
+                acc += (double)fast_exp2((float)v + tv);
+            }
+            part_trans[q] += acc;
+        }
+        __syncthreads();   // the tile's LDS is read no more
     }
 }
 
 hipError_t launch_marginals(const MargArgs& a, hipStream_t stream) {
     const size_t lds = marg_lds(a.C, a.tile, a.kchunk);
-    hipLaunchKernelGGL(k_marginals, dim3(a.ntiles, a.B), dim3(256), lds, stream, a);
+    if (a.tpg < 1 || a.ngroups != (a.ntiles + a.tpg - 1) / a.tpg) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_marginals, dim3(a.ngroups, a.B), dim3(256), lds, stream, a);
     return hipGetLastError();
+}
+
+int marg_tiles_per_group(int B, int ntiles, int C, int K) {
+    // a group per tile while the partials stay within the budget (longer workgroups leave
+    // the device's last pass over them mostly idle: four tiles a group cost 45 % more time
+    // at B = 4, T = 10^5, K = 200), else the fewest tiles a group that meet it
+    constexpr size_t BUDGET = (size_t)64 << 20;          // bytes of partials
+    constexpr long long TARGET = 8192;                   // workgroups
+    int tpg = (int)std::max<long long>(1, ((long long)B * ntiles + TARGET - 1) / TARGET);
+    auto bytes = [&](int t) {
+        return (size_t)B * ((ntiles + t - 1) / t) * (size_t)(K + C) * C * sizeof(double);
+    };
+    while (tpg < ntiles && bytes(tpg) > BUDGET) tpg *= 2;
+    return std::min(tpg, std::max(ntiles, 1));
 }
 
 // grid (ntiles, B), block 256: mu over positions [p0, p0+TM) of the prefix sum of Dn,
@@ -385,18 +405,21 @@ hipError_t launch_grad_em(const float* mu, const double* mu_tot, const int* Leff
 }
 
 // one thread per output element of grad_dur [K*C] followed by grad_trans [C*C]
-// grad_dur / grad_trans = sum over sequences b of g_b * sum over tiles j of
-// part[b][j] / z_tile[b][j].  Pass 1: grid (ceil(n / 64), RP_SLICES / 4), block 256; lane
-// (e, slice) sums the tiles j = slice, slice + RP_SLICES, ... of every sequence into
-// scratch[slice][e].  Pass 2: one lane per output adds the slices in order.  Fixed order
-// throughout: bitwise reproducible.
+// grad_dur / grad_trans = sum over sequences b of g_b * sum over tile groups j of
+// part[b][j] / z_j, z_j the mean per-position normaliser over the group's valid positions
+// (it drifts by far less than 1e-6 across a group).  Pass 1: grid (ceil(n / 64),
+// RP_SLICES / 4), block 256; lane (e, slice) sums the groups j = slice, slice + RP_SLICES,
+// ... of every sequence into scratch[slice][e].  Pass 2: one lane per output adds the
+// slices in order.  Fixed order throughout: bitwise reproducible.
 constexpr int RP_SLICES = 128;
 
 __global__ __launch_bounds__(256) void k_reduce_partials(const double* __restrict__ part_dur,
                                                          const double* __restrict__ part_trans,
                                                          const double* __restrict__ z_tile,
+                                                         const int* __restrict__ Leff,
                                                          const float* __restrict__ grad_log_z,
-                                                         int B, int C, int K, int ntiles,
+                                                         int B, int C, int K, int TM, int ntiles,
+                                                         int tpg, int ngroups,
                                                          double* __restrict__ scratch) {
     const int n = K * C + C * C;
     const int e = blockIdx.x * 64 + (threadIdx.x & 63);
@@ -409,9 +432,17 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const double* __restric
     const double* src = isd ? part_dur : part_trans;
     double total = 0.0;
     for (int b = 0; b < B; ++b) {
+        const int L = abs(Leff[b]);
         double s = 0.0;
-        for (int j = slice; j < ntiles; j += RP_SLICES)
-            s += src[((size_t)b * ntiles + j) * stride + ee] / z_tile[(size_t)b * ntiles + j];
+        for (int j = slice; j < ngroups; j += RP_SLICES) {
+            double zs = 0.0, ns = 0.0;
+            for (int tl = j * tpg; tl < min(ntiles, (j + 1) * tpg); ++tl) {
+                const int rows = max(0, min(TM, L - tl * TM));
+                zs += (double)rows * z_tile[(size_t)b * ntiles + tl];
+                ns += (double)rows;
+            }
+            s += src[((size_t)b * ngroups + j) * stride + ee] / (ns > 0.0 ? zs / ns : 1.0);
+        }
         total += (grad_log_z ? (double)grad_log_z[b] : 1.0) * s;
     }
     scratch[(size_t)slice * n + e] = total;
@@ -433,13 +464,14 @@ size_t reduce_scratch_doubles(int C, int K) { return (size_t)RP_SLICES * (K * C 
 
 hipError_t launch_reduce_partials(const double* part_dur, const double* part_trans,
                                   const double* z_tile, const int* Leff, const float* grad_log_z,
-                                  int B, int T, int C, int K, int tile, int ntiles,
+                                  int B, int C, int K, int tile, int ntiles, int tpg,
                                   double* scratch, float* grad_dur, float* grad_trans,
                                   hipStream_t stream) {
-    (void)Leff; (void)T; (void)tile;
     const int n = K * C + C * C;
+    const int ngroups = (ntiles + tpg - 1) / tpg;
     hipLaunchKernelGGL(k_reduce_partials, dim3((n + 63) / 64, RP_SLICES / 4), dim3(256), 0, stream,
-                       part_dur, part_trans, z_tile, grad_log_z, B, C, K, ntiles, scratch);
+                       part_dur, part_trans, z_tile, Leff, grad_log_z, B, C, K, tile, ntiles,
+                       tpg, ngroups, scratch);
     hipLaunchKernelGGL(k_reduce_slices, dim3((n + 255) / 256), dim3(256), 0, stream, scratch, C, K,
                        grad_dur, grad_trans);
     return hipGetLastError();

@@ -121,6 +121,18 @@ def test_checkpoint_interval(native):
     assert f(0, 5, 0) == 0 and f(10, 0, 0) == 0 and f(10, 5, -1) == 0
 
 
+def test_viterbi_interval(native):
+    lib = native.load()
+    f = lib.semicrf_viterbi_interval
+    assert f(4, 100_000, 200) == 2237          # 92 spans of 4473 >= 12 K: halved
+    assert f(1, 1_000_000, 200) == 7072        # 71 spans of 14143: halved
+    assert f(8, 10_000, 64) == 400             # 104 spans of 800 >= 768: halved
+    assert f(32, 800, 30) == 155               # 192 spans: the batch fills the device
+    assert f(64, 100_000, 200) == 4473         # 1472 spans
+    assert f(1, 1000, 200) == 448              # a span shorter than 12 K: kept
+    assert f(0, 100, 5) == 0 and f(1, 0, 5) == 0 and f(1, 10, 0) == 0
+
+
 def test_workspace_bytes(native):
     lib = native.load()
     ws = lib.semicrf_workspace_bytes
@@ -138,8 +150,8 @@ def test_workspace_bytes(native):
     assert ws(0, 1, 10, 2, 70000, 0) == 0              # K beyond 65535
 
 
-@pytest.mark.parametrize("C,kmax", [(1, 2049), (4, 2049), (5, 2049), (7, 2049), (8, 1025), (9, 513), (16, 513),
-                                    (17, 257), (39, 257), (64, 257), (128, 97)])
+@pytest.mark.parametrize("C,kmax", [(1, 8193), (4, 8193), (6, 8193), (7, 8193), (8, 2049), (9, 2049),
+                                    (16, 2049), (17, 513), (39, 513), (64, 513), (128, 97)])
 def test_supported_duration_range(native, C, kmax):
     """The largest K each label count supports, as the header states it."""
     lib = native.load()
