@@ -34,22 +34,25 @@ struct SweepLds {
 
 // Long-duration sweeps (sweep_xk.h): one chain wavefront and G bulk lanes per label, each
 // lane holding kpl duration weights (a multiple of XK_UNROLL, at most the instance's
-// kplmax), the ring of RS >= K + 2 slots per label in LDS or (gring) in a global scratch
-// slice per workgroup.
+// kplmax), the rings of RS >= K + 2 slots per label in LDS, mirrored in LDS, or in a global
+// scratch slice per workgroup (XK_RING_*).
 constexpr int XK_UNROLL = 8;
 constexpr int XK_REBASE = 16;      // positions between base moves (a power of two)
 constexpr int XK_PF = 2;           // staged S values per bulk lane and chunk
 constexpr int XK_FROM = 1026;      // durations from which the long-duration sweeps run
 
+// where the rings of the long-duration sweeps live (sweep_xk.h)
+enum { XK_RING_LDS = 0, XK_RING_MIRRORED = 1, XK_RING_GLOBAL = 2 };
+
 struct XkCfg {
     bool ok;
     int G, kplmax, NT, kpl, RS, CH;
-    bool gring;          // ring in global memory
+    int ring;            // XK_RING_*
     size_t lds;          // dynamic LDS per workgroup
 };
 // per-launch parameters of the long-duration sweeps
 struct XkParams {
-    float* ring;         // gring: [workgroups][rings][C][RS] scratch, else NULL
+    float* ring;         // [workgroups][rings held in global memory][C][RS], or NULL
     int RS, CH, kpl;
 };
 // maxp: the max-plus sweep (one ring) instead of the log-semiring sweep (two)

@@ -104,9 +104,10 @@ XkCfg choose_xk(int C, int K, bool maxp) {
     // threads, 168 VGPRs a lane)
     const int G = C <= 7 ? 64 : C <= 16 ? 32 : C <= 64 ? 8 : 0;
     if (G == 0) return x;
-    const int kplmax = G == 64 ? 128 : 64;
     int kpl = (K - 1 + G - 1) / G;                       // durations k = 2 .. K
     kpl = (kpl + XK_UNROLL - 1) / XK_UNROLL * XK_UNROLL;
+    // the instance's register capacity: 32 or 128 weights at G = 64, else 64
+    const int kplmax = G == 64 ? (kpl <= 32 ? 32 : 128) : 64;
     if (kpl > kplmax) return x;
     x.G = G;
     x.kplmax = kplmax;
@@ -117,17 +118,34 @@ XkCfg choose_xk(int C, int K, bool maxp) {
     // S chunk: every bulk lane stages at most XK_PF values of it
     x.CH = std::min(64, XK_PF * NB / C);
     if (x.CH < 1) return x;
-    const size_t base = (size_t)8 * (4 * x.CH * C + C) + (size_t)4 * (C * C + 4 * C + C + 1);
-    const size_t ring = (size_t)4 * (maxp ? 1 : 2) * C * x.RS;
-    x.gring = base + ring > LDS_BUDGET;
-    x.lds = x.gring ? base : base + ring;
+    // S chunks, S(L) and the staged outputs (fp64); transitions, bulk values, rebase
+    // shifts, staged ring entries and backpointers, the rebase position (32-bit)
+    const size_t base = (size_t)8 * (4 * x.CH * C + C + 4 * C) +
+                        (size_t)4 * (C * C + 4 * C + C + 2 * C + 2 * C + 1);
+    // rings: the one the bulk sums read mirrored in LDS (its log twin, for the log
+    // semiring, in global memory) when the window addressing allows it and it fits, else
+    // every ring plain in LDS, else every ring in global memory
+    const size_t row = (size_t)4 * C * x.RS;
+    const bool mir_ok = (size_t)(kplmax - 1) * G <= (size_t)x.RS;
+    if (mir_ok && base + 2 * row <= LDS_BUDGET) {
+        x.ring = XK_RING_MIRRORED;
+        x.lds = base + 2 * row;
+    } else if (base + (maxp ? 1 : 2) * row <= LDS_BUDGET) {
+        x.ring = XK_RING_LDS;
+        x.lds = base + (maxp ? 1 : 2) * row;
+    } else {
+        x.ring = XK_RING_GLOBAL;
+        x.lds = base;
+    }
     x.ok = x.lds <= LDS_BUDGET;
     return x;
 }
 
 size_t xk_ring_floats(const XkCfg& xc, int C, int workgroups, bool maxp) {
-    if (!xc.ok || !xc.gring) return 0;
-    return (size_t)workgroups * (maxp ? 1 : 2) * C * xc.RS;
+    if (!xc.ok) return 0;
+    const int rings = xc.ring == XK_RING_GLOBAL ? (maxp ? 1 : 2)
+                      : xc.ring == XK_RING_MIRRORED ? (maxp ? 0 : 1) : 0;
+    return (size_t)workgroups * rings * C * xc.RS;
 }
 
 SweepCfg choose_sweep(int C, int K) {

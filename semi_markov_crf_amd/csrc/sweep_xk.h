@@ -71,12 +71,15 @@ __device__ __forceinline__ float xk_pow2_neg(float n) {
 
 }  // namespace
 
-// MAXP: max-plus (Viterbi) instead of the log semiring.  GRING: the ring in global memory
-// (XkParams::ring) instead of LDS.  G: bulk lanes per label (<= 64); KPLMAX: duration
-// weights per lane (registers); NTMAX: the largest block.
+// MAXP: max-plus (Viterbi) instead of the log semiring.  RM: where the rings live
+// (XK_RING_LDS: plain rows in LDS; XK_RING_MIRRORED: the ring the bulk sums read, mirrored
+// in LDS (every position in two slots RS apart, so a lane's window is contiguous and its
+// reads take compile-time offsets), with the log ring of the log semiring in global
+// memory; XK_RING_GLOBAL: plain rows in global memory).  G: bulk lanes per label (<= 64);
+// KPLMAX: duration weights per lane (registers); NTMAX: the largest block.
 // Block: 64 + ceil(C*G/64)*64 threads.  Grid: (nspans, B, ndir) in MODE_SPEC, (B, ndir) in
 // MODE_REPAIR (ndir = 1 for max-plus).
-template <bool MAXP, bool GRING, int G, int KPLMAX, int NTMAX>
+template <bool MAXP, int RM, int G, int KPLMAX, int NTMAX>
 __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkParams x,
                                                    const float* __restrict__ proj_start,
                                                    const float* __restrict__ proj_end) {
@@ -125,35 +128,52 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
     const size_t drow = (size_t)dir * a.B + b;   // (direction, sequence) row
     const size_t winrow = (drow * a.nspans + span) * K;
     const size_t ckrow = drow * a.nspans;
-    auto window = [&](int t, double av) {                 // chain lanes
-        if (t >= hlo && t <= tout) a.head[(winrow + t - hlo) * C + cl] = av;
-        if (t >= tlo && t <= t1) a.tail[(winrow + t - tlo) * C + cl] = av;
+    auto window = [&](int t, int c, double av) {
+        if (t >= hlo && t <= tout) a.head[(winrow + t - hlo) * C + c] = av;
+        if (t >= tlo && t <= t1) a.tail[(winrow + t - tlo) * C + c] = av;
     };
 
     // ---------------------------------------------------------------- LDS
     const int rowsN = CH * C;
     double* Sbuf = lds;                                   // [2 chunks][end, start][CH][C]
     double* SL = Sbuf + 4 * rowsN;                        // [C]
-    float* trl = (float*)(SL + C);                        // [C][C]: trl[c' * C + c]
+    // a position's outputs, staged by the chain for the bulk lanes to write one position
+    // later (the chain issues no global memory operation inside the loop, so nothing it
+    // waits on there includes its own stores): [2][X, A][C] (working units)
+    double* oXA = SL + C;
+    float* trl = (float*)(oXA + 4 * C);                   // [C][C]: trl[c' * C + c]
     float* part = trl + C * C;                            // [2][C][2] bulk values
     float* dlsh = part + 4 * C;                           // [C] rebase shift
-    int* rebsh = (int*)(dlsh + C);                        // [1] position of the last rebase
-    float* Rl = (float*)(rebsh + 1);                      // [C][RS] log ring (LDS form)
-    float* El = Rl + (size_t)C * RS;                      // [C][RS] linear ring (LDS form)
-    // ring rows of this workgroup's label (bulk lanes) or of any label (chain lanes)
-    float* Rbase;
-    float* Ebase;
-    if constexpr (GRING) {
-        const size_t wg = drow * a.nspans + span;        // a repair reuses its span's slice
-        Rbase = x.ring + wg * (size_t)(MAXP ? 1 : 2) * C * RS;
-        Ebase = Rbase + (size_t)C * RS;
-    } else {
-        Rbase = Rl;
-        Ebase = El;
-    }
+    float* oR = dlsh + C;                                 // [2][C] ring entry (staged)
+    uint32_t* oBP = (uint32_t*)(oR + 2 * C);              // [2][C] backpointer (staged)
+    int* rebsh = (int*)(oBP + 2 * C);                     // [1] position of the last rebase
+    float* ringl = (float*)(rebsh + 1);                   // the rings held in LDS
+    // log ring R (both semirings) and linear ring E (log semiring): base, row pitch, and
+    // whether a row is mirrored; a repair reuses its span's global slice
+    constexpr bool RMIR = MAXP && RM == XK_RING_MIRRORED;
+    constexpr bool EMIR = !MAXP && RM == XK_RING_MIRRORED;
+    constexpr bool RGLB = RM == XK_RING_GLOBAL || (!MAXP && RM == XK_RING_MIRRORED);
+    constexpr bool EGLB = RM == XK_RING_GLOBAL;
+    constexpr int NGR = (RGLB ? 1 : 0) + (EGLB ? 1 : 0);   // rings in global memory
+    const int RP = RMIR ? 2 * RS : RS, EP = EMIR ? 2 * RS : RS;
+    float* gslice = x.ring ? x.ring + (drow * a.nspans + span) * (size_t)NGR * C * RS : nullptr;
+    float* Rbase = RGLB ? gslice : ringl;
+    float* Ebase = EGLB ? gslice + (RGLB ? (size_t)C * RS : 0) : RGLB ? ringl : ringl + (size_t)C * RP;
     const int crow = bact ? cb : 0;
-    float* Rrow = Rbase + (size_t)crow * RS;
-    float* Erow = Ebase + (size_t)crow * RS;
+    float* Rrow = Rbase + (size_t)crow * RP;
+    float* Erow = Ebase + (size_t)crow * EP;
+    auto slot = [&](int p) { return p & RMASK; };
+    // ring entries of position p of label c (every copy)
+    auto putR = [&](int c, int p, float v) {
+        float* row = Rbase + (size_t)c * RP;
+        row[slot(p)] = v;
+        if constexpr (RMIR) row[slot(p) + RS] = v;
+    };
+    auto putE = [&](int c, int p, float v) {
+        float* row = Ebase + (size_t)c * EP;
+        row[slot(p)] = v;
+        if constexpr (EMIR) row[slot(p) + RS] = v;
+    };
 
     const double* Sb = a.S + (size_t)b * (T + 1) * C;
     for (int q = tid; q < C; q += NT) SL[q] = Sb[(size_t)L * C + q];
@@ -178,11 +198,10 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
         const float tv = dir == 0 ? a.trans[cp * C + c] : a.trans[c * C + cp];
         trl[q] = fmaxf((float)((double)tv * SC), NEG);
     }
-    // ring: every slot cleared (log NEG, linear 0)
-    for (size_t q = tid; q < (size_t)C * RS; q += NT) {
-        Rbase[q] = NEG;
-        if constexpr (!MAXP) Ebase[q] = 0.0f;
-    }
+    // rings: every slot cleared (log NEG, linear 0)
+    for (size_t q = tid; q < (size_t)C * RP; q += NT) Rbase[q] = NEG;
+    if constexpr (!MAXP)
+        for (size_t q = tid; q < (size_t)C * EP; q += NT) Ebase[q] = 0.0f;
     if (tid == 0) *rebsh = INT_MIN;
 
     // ---------------------------------------------------------------- durations
@@ -205,9 +224,19 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
         for (int i = 0; i < KPLMAX; ++i) Dw[i] = xk_exp2(Dw[i] - dmax);
     }
     const float d1 = cact ? durv(cl, 1) : NEG;            // chain: the k = 1 term
+    // chain: the transitions into this lane's label in registers (C <= CT = 8), so the
+    // transition step is an unrolled run of lane broadcasts and adds; larger C reads them
+    // from LDS
+    constexpr int CT = G == 64 ? 8 : 0;
+    float trv[CT > 0 ? CT : 1];
+    __syncthreads();   // ring cleared (the start state below overwrites slots other
+                       // threads cleared) and trl visible
+    if constexpr (CT > 0) {
+#pragma unroll
+        for (int i = 0; i < CT; ++i) trv[i] = (cact && i < C) ? trl[i * C + cl] : NEG;
+    }
 
     // ---------------------------------------------------------------- start state
-    auto slot = [&](int p) { return p & RMASK; };
     double Bc = 0.0, H = 0.0;
     float Rn1 = NEG;                                      // chain: A(t-1) - B_c
     float Mref = 0.0f;                                    // chain: last bulk value (rebase)
@@ -215,16 +244,16 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
         // position 0: no transition into it; its ring entry is its start-side projection
         if (bact && j == 0) {
             const float r0 = fmaxf((float)proj_s(0, cb), NEG);
-            Rrow[slot(0)] = r0;
-            if constexpr (!MAXP) Erow[slot(0)] = xk_exp2(r0);
+            putR(cb, 0, r0);
+            if constexpr (!MAXP) putE(cb, 0, xk_exp2(r0));
         }
         Rn1 = cact ? fmaxf((float)proj_s(0, cl), NEG) : NEG;
     } else if (spec) {
         // burn-in start: every ring entry of positions t0-K+1 .. t0 equal (0)
         if (bact)
             for (int q = j; q < K && t0 - q >= 0; q += G) {
-                Rrow[slot(t0 - q)] = 0.0f;
-                if constexpr (!MAXP) Erow[slot(t0 - q)] = 1.0f;
+                putR(cb, t0 - q, 0.0f);
+                if constexpr (!MAXP) putE(cb, t0 - q, 1.0f);
             }
         Rn1 = cact ? 0.0f : NEG;
     } else {
@@ -232,8 +261,8 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
         if (bact)
             for (int q = j; q < K && t0 - q >= 0; q += G) {
                 const float rv = a.ck_ring[(ck * K + q) * C + cb];
-                Rrow[slot(t0 - q)] = rv;
-                if constexpr (!MAXP) Erow[slot(t0 - q)] = xk_exp2(rv);
+                putR(cb, t0 - q, rv);
+                if constexpr (!MAXP) putE(cb, t0 - q, xk_exp2(rv));
             }
         if (chain) {
             Bc = a.ck_base[ck * C + cl];
@@ -249,8 +278,26 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
         const double a0 = (Bc + (double)Rn1) * OUT;
         if (!MAXP && a.write_xa && t0 == tout) Aout[(outrow + (dir == 0 ? t0 : L - t0)) * C + cl] = a0;
         if (t0 == 0)   // window positions <= 0: position 0's value, nothing before it
-            for (int p = min(hlo, tlo); p <= 0; ++p) window(p, p == 0 ? a0 : -1.0e300);
+            for (int p = min(hlo, tlo); p <= 0; ++p) window(p, cl, p == 0 ? a0 : -1.0e300);
     }
+    // bulk lanes, first lane of a label: the staged outputs of position p (the ring entry
+    // too when the ring is in global memory; the same lane reads it back first)
+    auto flush = [&](int p) {
+        if (!(bact && j == 0)) return;
+        const int s2 = p & 1;
+        const double av = oXA[(s2 * 2 + 1) * C + cb];
+        const size_t o = (outrow + (dir == 0 ? p : L - p)) * C + cb;
+        if constexpr (MAXP) {
+            if (p > tout) a.bp[(outrow + p) * C + cb] = oBP[s2 * C + cb];
+        } else if (a.write_xa) {
+            if (p > tout) Xout[o] = oXA[(s2 * 2) * C + cb] * OUT;
+            if (p >= tout && p < t1) Aout[o] = av * OUT;
+        }
+        if (p >= min(hlo, tlo)) window(p, cb, av * OUT);
+        // the rings held in global memory get their entry here, the LDS ones from the chain
+        if constexpr (RGLB) putR(cb, p, oR[s2 * C + cb]);
+        if constexpr (EGLB) putE(cb, p, xk_exp2(oR[s2 * C + cb]));
+    };
 
     // ---------------------------------------------------------------- S staging
     // chunk n holds rows t = t0 + 1 + n*CH + r, r < CH: end side S(t) + pe(t) and start
@@ -268,22 +315,24 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
             Sbuf[q] = in ? sv + proj_e(t, l) : 0.0;
             Sbuf[rowsN + q] = in ? sv - proj_s(t, l) : 0.0;
         }
-    // the chunk after next is fetched into registers (at most XK_PF per lane)
-    double pf[XK_PF], pfe[XK_PF], pfs[XK_PF];
+    // the chunk after next is fetched into registers (at most XK_PF per lane), raw: the
+    // values are converted when stored, so no load is waited on before then
+    const float* PEd = dir == 0 ? PEb : PSb;              // end-side projection source
+    const float* PSd = dir == 0 ? PSb : PEb;              // start-side projection source
+    double pf[XK_PF];
+    float pfe[XK_PF], pfs[XK_PF];
     auto stage_fetch = [&](int tcs) {
 #pragma unroll
         for (int i = 0; i < XK_PF; ++i) {
             const int q = bt + i * NB;
-            pf[i] = pfe[i] = pfs[i] = 0.0;
-            if (!chain && i < pfn && q < rowsN) {
-                const int row = q / C, l = q - row * C;
-                const int t = tcs + row;
-                if (t <= t1) {
-                    pf[i] = Sb[sidx(t, l)];
-                    pfe[i] = proj_e(t, l);
-                    pfs[i] = proj_s(t, l);
-                }
-            }
+            const int row = q / C, l = q - row * C;
+            const int t = tcs + row;
+            const bool in = !chain && i < pfn && q < rowsN && t <= t1;
+            const int te = dir == 0 ? t - 1 : L - t;       // end side: valid for 1 <= t <= L
+            const int ts = dir == 0 ? t : L - 1 - t;       // start side: valid for t <= L-1
+            pf[i] = in ? Sb[sidx(t, l)] : 0.0;
+            pfe[i] = (in && PEd && t >= 1) ? PEd[(size_t)te * C + l] : 0.0f;
+            pfs[i] = (in && PSd && t < L) ? PSd[(size_t)ts * C + l] : 0.0f;
         }
     };
     auto stage_store = [&](int buf) {
@@ -293,8 +342,8 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
             const int q = bt + i * NB;
             if (!chain && i < pfn && q < rowsN) {
                 const double sv = spub(pf[i], q - (q / C) * C);
-                dst[q] = sv + pfe[i];
-                dst[rowsN + q] = sv - pfs[i];
+                dst[q] = sv + (double)pfe[i] * SC;
+                dst[rowsN + q] = sv - (double)pfs[i] * SC;
             }
         }
     };
@@ -307,6 +356,17 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
     // part[tq & 1][label]
     auto bulk = [&](int tq) {
         const int p0 = tq - 2 - j;                        // position of k = 2 + j (i = 0)
+        // ring value of position p0 - i*G of the ring the sums read: on a mirrored row the
+        // lane's window is one contiguous stretch below slot(p0) + RS (RS >= (KPLMAX-1)*G,
+        // checked on the host), read at compile-time offsets from its lowest slot
+        int lo = slot(p0) + RS - (KPLMAX - 1) * G;
+        // opaque to the compiler, so the offsets stay positive (the LDS offset field is
+        // unsigned) instead of being rewritten from the top of the window
+        asm volatile("" : "+v"(lo));
+        auto bulk_at = [&](const float* row, int i) -> float {
+            if constexpr (RM == XK_RING_MIRRORED) return row[lo + (KPLMAX - 1 - i) * G];
+            else return row[slot(p0 - i * G)];
+        };
         float qv = NEG;
         int kq = INT_MAX;
         if constexpr (MAXP) {
@@ -317,7 +377,7 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
                 if (i0 < kplr) {
                     float v[U];
 #pragma unroll
-                    for (int u = 0; u < U; ++u) v[u] = Rrow[slot(p0 - (i0 + u) * G)];
+                    for (int u = 0; u < U; ++u) v[u] = bulk_at(Rrow, i0 + u);
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const float y = v[u] + Dw[i0 + u];
@@ -337,7 +397,7 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
                 if (i0 < kplr) {
                     float v[U];
 #pragma unroll
-                    for (int u = 0; u < U; ++u) v[u] = Erow[slot(p0 - (i0 + u) * G)];
+                    for (int u = 0; u < U; ++u) v[u] = bulk_at(Erow, i0 + u);
 #pragma unroll
                     for (int u = 0; u < U; ++u) acc = fmaf(v[u], Dw[i0 + u], acc);
                 }
@@ -392,14 +452,19 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
         const float sc = MAXP ? 1.0f : xk_pow2_neg(dl);
         const int p0 = tq - 2 - j;
         for (int i0 = 0; i0 < kplr; i0 += U) {
-            {
+            // a chunk's loads first, then its stores (each slot belongs to one lane)
+            float rv[U], ev[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int p = p0 - (i0 + u) * G;
-                    if (p <= trb - 1 && p >= trb - K + 1) {
-                        Rrow[slot(p)] -= dl;
-                        if constexpr (!MAXP) Erow[slot(p)] *= sc;
-                    }
+            for (int u = 0; u < U; ++u) {
+                rv[u] = Rrow[slot(p0 - (i0 + u) * G)];
+                if constexpr (!MAXP) ev[u] = Erow[slot(p0 - (i0 + u) * G)];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int p = p0 - (i0 + u) * G;
+                if (p <= trb - 1 && p >= trb - K + 1) {
+                    putR(cb, p, rv[u] - dl);
+                    if constexpr (!MAXP) putE(cb, p, ev[u] * sc);
                 }
             }
         }
@@ -453,60 +518,89 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
                     sig = xk_lse2(e1, Q);
                 }
                 const float u = cact ? (float)(Se + Bc - H) + sig : NEG;  // alpha(t) - H
-                if (!MAXP && cact && a.write_xa && t > tout)
-                    Xout[(outrow + (dir == 0 ? t : L - t)) * C + cl] = (Se + Bc + (double)sig) * OUT;
-                // ---- transition step of t over every label's alpha (lane broadcasts)
+                if (!MAXP && cact) oXA[((t & 1) * 2) * C + cl] = Se + Bc + (double)sig;
+                // ---- transition step of t over every label's alpha (lane broadcasts; the
+                // lowest c' on ties)
                 float mu = NEG;                                        // max_c' u(c')
                 float mt = NEG;                                        // max_c' u + trans
                 int cbest = 0;
-                for (int cp = 0; cp < C; ++cp) {
-                    const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), cp));
-                    const float y = uv + trl[cp * C + cl];
-                    mu = fmaxf(mu, uv);
-                    if (y > mt) {
-                        mt = y;
-                        cbest = cp;
+                float abar;                                            // abar(t) - H
+                float zs = 0.0f;                                       // sum_c' 2^(u - mu)
+                if constexpr (CT > 0) {
+                    float uv[CT], y[CT];
+#pragma unroll
+                    for (int i = 0; i < CT; ++i) {
+                        uv[i] = i < C ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), i)) : NEG;
+                        y[i] = uv[i] + trv[i];
+                        mu = fmaxf(mu, uv[i]);
+                        if (y[i] > mt) {
+                            mt = y[i];
+                            cbest = i;
+                        }
+                    }
+                    abar = mt;
+                    if constexpr (!MAXP) {
+                        if (mt > NEG_HALF) {
+                            float s = 0.0f;
+#pragma unroll
+                            for (int i = 0; i < CT; ++i) s += xk_exp2(y[i] - mt);
+                            abar = mt + fast_log2(s);
+                        }
+                        if (t == L && mu > NEG_HALF)
+#pragma unroll
+                            for (int i = 0; i < CT; ++i) zs += xk_exp2(uv[i] - mu);
+                    }
+                } else {
+#pragma unroll 8
+                    for (int cp = 0; cp < C; ++cp) {
+                        const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), cp));
+                        const float y = uv + trl[cp * C + cl];
+                        mu = fmaxf(mu, uv);
+                        if (y > mt) {
+                            mt = y;
+                            cbest = cp;
+                        }
+                    }
+                    abar = mt;
+                    if constexpr (!MAXP) {
+                        if (mt > NEG_HALF) {
+                            float s = 0.0f;
+#pragma unroll 8
+                            for (int cp = 0; cp < C; ++cp) {
+                                const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), cp));
+                                s += xk_exp2(uv + trl[cp * C + cl] - mt);
+                            }
+                            abar = mt + fast_log2(s);
+                        }
+                        if (t == L && mu > NEG_HALF)
+                            for (int cp = 0; cp < C; ++cp) {
+                                const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), cp));
+                                zs += xk_exp2(uv - mu);
+                            }
                     }
                 }
-                float abar = mt;                                       // abar(t) - H
                 if constexpr (!MAXP) {
-                    if (mt > NEG_HALF) {
-                        float s = 0.0f;
-                        for (int cp = 0; cp < C; ++cp) {
-                            const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), cp));
-                            s += xk_exp2(uv + trl[cp * C + cl] - mt);
-                        }
-                        abar = mt + fast_log2(s);
-                    }
-                    if (t == L && mu > NEG_HALF) {                     // log2 Z
-                        float s = 0.0f;
-                        for (int cp = 0; cp < C; ++cp) {
-                            const float uv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), cp));
-                            s += xk_exp2(uv - mu);
-                        }
-                        lz = H + (double)mu + (double)fast_log2(s);
-                    }
+                    if (t == L && mu > NEG_HALF) lz = H + (double)mu + (double)fast_log2(zs);   // log2 Z
                 } else {
                     if (t == L && cact) a.vfin[(size_t)b * C + cl] = H + (double)u;
                 }
                 const float Rnew = cact ? fmaxf(abar - (float)(Ss + Bc - H), NEG) : NEG;
-                if (MAXP && cact && t > tout)
-                    a.bp[(outrow + t) * C + cl] =
-                        (uint32_t)kb | (t < L ? ((uint32_t)cbest << 16) : 0u);
                 if (mu > NEG_HALF) H += (double)mu;
                 if (cact) {
-                    Rbase[(size_t)cl * RS + slot(t)] = Rnew;
-                    if constexpr (!MAXP)
-                        Ebase[(size_t)cl * RS + slot(t)] = xk_exp2(Rnew);
-                    const double av = (Bc + (double)Rnew) * OUT;
-                    if (!MAXP && a.write_xa && t >= tout && t < t1)
-                        Aout[(outrow + (dir == 0 ? t : L - t)) * C + cl] = av;
-                    if (t >= min(hlo, tlo)) window(t, av);
+                    // outputs of t, staged; the ring entry goes straight to an LDS ring
+                    if constexpr (MAXP)
+                        oBP[(t & 1) * C + cl] = (uint32_t)kb | (t < L ? ((uint32_t)cbest << 16) : 0u);
+                    oXA[((t & 1) * 2 + 1) * C + cl] = Bc + (double)Rnew;
+                    oR[(t & 1) * C + cl] = Rnew;
+                    if constexpr (!RGLB) putR(cl, t, Rnew);
+                    if constexpr (!MAXP && !EGLB) putE(cl, t, xk_exp2(Rnew));
                 }
                 Rn1 = Rnew;
                 if (Q > NEG_HALF) Mref = Q;
             } else {
-                // ---- S staging: publish the next chunk, fetch the one after
+                // ---- the outputs of t-1, S staging (publish the next chunk, fetch the one
+                // after), the rebase of the ring, the bulk value of t+1
+                if (t - 1 > t0) flush(t - 1);
                 if (row == 0 && tc + CH <= t1) {
                     stage_store((nch + 1) & 1);
                     stage_fetch(tc + 2 * CH);
@@ -517,6 +611,8 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
             __syncthreads();
         }
     }
+    if (!chain) flush(t1);
+    __syncthreads();                                      // the ring entry of t1 (global form)
 
     // ---------------------------------------------------------------- span end
     if (ckpt) {

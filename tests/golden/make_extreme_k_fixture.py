@@ -35,7 +35,7 @@ CASES = {
     "x3": (603, 1, 2100, 4, 2049, 2.0, False, 0.0),   # the largest K, log-space ring only
     "x4": (604, 1, 1400, 6, 1200, 1.5, False, 1.0),   # boundary projections, 64 lanes
     "x5": (605, 3, 60, 5, 1500, 1.0, True, 0.5),      # K > T on the 64-lane path
-    "x6": (606, 1, 8600, 6, 8000, 2.0, False, 0.0),   # K = 8000: rings in global memory
+    "x6": (606, 1, 8100, 3, 8000, 2.0, False, 0.0),   # K = 8000: log-semiring rings in global memory
     "x7": (607, 2, 4500, 3, 4000, 1.5, True, 0.5),    # K = 4000 with projections
     "x8": (608, 1, 5000, 6, 4000, 2.0, False, 0.0),   # log rings global, max-plus ring LDS
     "x9": (609, 1, 2600, 12, 2049, 1.5, False, 0.0),  # 12 labels at K = 2049
