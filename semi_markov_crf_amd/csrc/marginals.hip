@@ -113,17 +113,20 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
     double* part_dur = a.part_dur + ((size_t)b * a.ngroups + g) * K * C;
     double* part_trans = a.part_trans + ((size_t)b * a.ngroups + g) * C * C;
     double* Dn = a.Dn + (size_t)b * rowC;
-    for (int q = tid; q < K * C; q += 256) part_dur[q] = 0.0;
-    for (int q = tid; q < C * C; q += 256) part_trans[q] = 0.0;
     for (int q = tid; q < C * C; q += 256) tr2[q] = fmaxf((float)((double)a.trans[q] * LOG2E), NEG);
     const int tile_end = min(a.ntiles, (g + 1) * a.tpg);
     for (int tile = g * a.tpg; tile < tile_end; ++tile) {
         const int p0 = tile * TM;
+        const bool first = tile == g * a.tpg;    // stores the group's partials, later tiles add
         double* dn_tile = a.dn_tile + ((size_t)b * a.ntiles + tile) * C;
         if (p0 > L) {   // nothing of this sequence here
             for (int q = tid; q < C; q += 256) dn_tile[q] = 0.0;
             for (int q = tid; q < TM * C; q += 256)
                 if (p0 + q / C <= T) Dn[(size_t)p0 * C + q] = 0.0;
+            if (first) {
+                for (int q = tid; q < K * C; q += 256) part_dur[q] = 0.0;
+                for (int q = tid; q < C * C; q += 256) part_trans[q] = 0.0;
+            }
             continue;
         }
         const double logZ = a.logz[b];
@@ -203,7 +206,8 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
 #pragma unroll 4
                 for (int r = 0; r < TM; ++r)
                     acc += (double)seg(AFt[(size_t)r * C + c] + ABw[(size_t)(r + kk) * C + c], d);
-                part_dur[(size_t)(kc0 - 1) * C + q] += acc;
+                double* pd = part_dur + (size_t)(kc0 - 1) * C + q;
+            *pd = first ? acc : *pd + acc;
             }
         }
         __syncthreads();
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
                 const double v = XFs[(size_t)r * C + cp] + XBs[(size_t)r * C + c];
                 acc += (double)fast_exp2((float)v + tv);
             }
-            part_trans[q] += acc;
+            part_trans[q] = first ? acc : part_trans[q] + acc;
         }
         __syncthreads();   // the tile's LDS is read no more
     }
