@@ -37,7 +37,12 @@ struct SweepLds {
 // kplmax), the rings of RS >= K + 2 slots per label in LDS, mirrored in LDS, or in a global
 // scratch slice per workgroup (XK_RING_*).
 constexpr int XK_UNROLL = 8;
-constexpr int XK_REBASE = 16;      // positions between base moves (a power of two)
+// positions between base moves: entries written between two moves drift from their base
+// by up to XK_REBASE times the per-position growth of the log partition function, and
+// their fp32 rounding grows with that offset (8 positions: node-mass deviation about 3e-5
+// at T = 6000, K = 1030, three times that with 16)
+constexpr int XK_LOG_REBASE = 3;
+constexpr int XK_REBASE = 1 << XK_LOG_REBASE;
 constexpr int XK_PF = 2;           // staged S values per bulk lane and chunk
 constexpr int XK_FROM = 1026;      // durations from which the long-duration sweeps run
 
@@ -47,13 +52,14 @@ enum { XK_RING_LDS = 0, XK_RING_MIRRORED = 1, XK_RING_GLOBAL = 2 };
 struct XkCfg {
     bool ok;
     int G, kplmax, NT, kpl, RS, CH;
+    int NE;              // log semiring: epochs of XK_REBASE positions in the shift table
     int ring;            // XK_RING_*
     size_t lds;          // dynamic LDS per workgroup
 };
 // per-launch parameters of the long-duration sweeps
 struct XkParams {
     float* ring;         // [workgroups][rings held in global memory][C][RS], or NULL
-    int RS, CH, kpl;
+    int RS, CH, kpl, NE;
 };
 // maxp: the max-plus sweep (one ring) instead of the log-semiring sweep (two)
 XkCfg choose_xk(int C, int K, bool maxp);

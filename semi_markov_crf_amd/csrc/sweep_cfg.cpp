@@ -118,10 +118,14 @@ XkCfg choose_xk(int C, int K, bool maxp) {
     // S chunk: every bulk lane stages at most XK_PF values of it
     x.CH = std::min(64, XK_PF * NB / C);
     if (x.CH < 1) return x;
+    // log semiring: a table of each label's total base shift per epoch of XK_REBASE
+    // positions, covering more than the K + 2 positions a ring holds
+    x.NE = maxp ? 0 : pow2_at_least((K + 2 + 3 * XK_REBASE - 1) / XK_REBASE);
     // S chunks, S(L) and the staged outputs (fp64); transitions, bulk values, rebase
-    // shifts, staged ring entries and backpointers, the rebase position (32-bit)
+    // shifts, staged ring entries and backpointers, the rebase position, the shift table
+    // (32-bit)
     const size_t base = (size_t)8 * (4 * x.CH * C + C + 4 * C) +
-                        (size_t)4 * (C * C + 4 * C + C + 2 * C + 2 * C + 1);
+                        (size_t)4 * (C * C + 4 * C + C + 2 * C + 2 * C + 1 + (size_t)C * x.NE);
     // rings: the one the bulk sums read mirrored in LDS (its log twin, for the log
     // semiring, in global memory) when the window addressing allows it and it fits, else
     // every ring plain in LDS, else every ring in global memory

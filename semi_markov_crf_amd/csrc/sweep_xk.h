@@ -39,7 +39,13 @@ namespace semicrf {
 
 namespace {
 
-constexpr float XK_LIN_LO = 0x1p-60f;   // linear partial sums trusted inside this range
+// Linear bulk sums are trusted inside [2^-60, 2^60]: a term lost to fp32 underflow (an
+// entry or a weight below 2^-126, the weights relative to the label's largest duration
+// score) is far under 2^-23 of such a sum, and nothing overflowed.  With a rebase every
+// XK_REBASE positions the newest ring entries stay within that range unless the log
+// partition function grows by more than about 60 / XK_REBASE octaves a position; outside
+// it (inf and NaN included) the sum is redone exactly in log space.
+constexpr float XK_LIN_LO = 0x1p-60f;
 constexpr float XK_LIN_HI = 0x1p+60f;
 
 __device__ __forceinline__ bool xk_in_range(float s) {
@@ -147,7 +153,13 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
     float* oR = dlsh + C;                                 // [2][C] ring entry (staged)
     uint32_t* oBP = (uint32_t*)(oR + 2 * C);              // [2][C] backpointer (staged)
     int* rebsh = (int*)(oBP + 2 * C);                     // [1] position of the last rebase
-    float* ringl = (float*)(rebsh + 1);                   // the rings held in LDS
+    // log semiring: [C][NE] each label's total base shift (whole octaves) in force at the
+    // epochs of XK_REBASE positions, by epoch mod NE.  A log ring entry keeps the base of
+    // its epoch (only the linear ring is moved at a rebase); the table takes it to any
+    // later base.
+    const int NE = MAXP ? 0 : x.NE, NEM = NE - 1;
+    int* cumt = rebsh + 1;
+    float* ringl = (float*)(cumt + (MAXP ? 0 : C * NE));  // the rings held in LDS
     // log ring R (both semirings) and linear ring E (log semiring): base, row pitch, and
     // whether a row is mirrored; a repair reuses its span's global slice
     constexpr bool RMIR = MAXP && RM == XK_RING_MIRRORED;
@@ -203,6 +215,9 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
     if constexpr (!MAXP)
         for (size_t q = tid; q < (size_t)C * EP; q += NT) Ebase[q] = 0.0f;
     if (tid == 0) *rebsh = INT_MIN;
+    if constexpr (!MAXP)
+        for (int q = tid; q < C * NE; q += NT) cumt[q] = 0;   // positions <= t0: base 0
+    auto epoch = [&](int p) { return (p >> XK_LOG_REBASE) & NEM; };
 
     // ---------------------------------------------------------------- durations
     auto durv = [&](int c, int k) -> float {
@@ -406,7 +421,11 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
             const bool ok = xk_in_range(acc) || !bact;   // per label group
             qv = fast_log2(acc) + dmax;
             if (xk_wave_any(!ok)) {
-                // exact log-space sum (log ring, the duration scores from global memory)
+                // exact log-space sum (log ring, each entry taken from the base of its
+                // epoch to that of the linear ring, the one of position tq - 2; the
+                // duration scores from global memory)
+                const int* cum = cumt + crow * NE;
+                const int cnow = cum[epoch(tq - 2)];
                 float m = NEG, s = 0.0f;
                 for (int i0 = 0; i0 < kplr; i0 += U) {
                     {
@@ -414,7 +433,9 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
 #pragma unroll
                         for (int u = 0; u < U; ++u) {
                             const int k = 2 + j + (i0 + u) * G;
-                            y[u] = Rrow[slot(p0 - (i0 + u) * G)] + (bact ? durv(cb, k) : NEG);
+                            const int p = p0 - (i0 + u) * G;
+                            y[u] = Rrow[slot(p)] - (float)(cnow - cum[epoch(p)]) +
+                                   (bact ? durv(cb, k) : NEG);
                         }
                         float mc = y[0];
 #pragma unroll
@@ -444,7 +465,9 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
     // bulk lanes, one position after a rebase at position tr: the live entries of
     // positions tr-K+1 .. tr-1 this lane reads for the bulk of tr + 2 move to the new base
     // (the entry of tr was written in it; older ones are never weighted again, and the
-    // ring holds RS >= K + 2 positions, so every live slot is moved exactly once)
+    // ring holds RS >= K + 2 positions, so every live slot is moved exactly once).  The
+    // ring the bulk sums read moves: the log ring of max-plus, the linear ring of the log
+    // semiring (its log ring keeps its epochs' bases).
     auto rebase_ring = [&](int tq) {
         const int trb = *rebsh;
         if (trb != tq - 2 || !bact) return;
@@ -453,18 +476,15 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
         const int p0 = tq - 2 - j;
         for (int i0 = 0; i0 < kplr; i0 += U) {
             // a chunk's loads first, then its stores (each slot belongs to one lane)
-            float rv[U], ev[U];
+            float v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                rv[u] = Rrow[slot(p0 - (i0 + u) * G)];
-                if constexpr (!MAXP) ev[u] = Erow[slot(p0 - (i0 + u) * G)];
-            }
+            for (int u = 0; u < U; ++u) v[u] = (MAXP ? Rrow : Erow)[slot(p0 - (i0 + u) * G)];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int p = p0 - (i0 + u) * G;
                 if (p <= trb - 1 && p >= trb - K + 1) {
-                    putR(cb, p, rv[u] - dl);
-                    if constexpr (!MAXP) putE(cb, p, ev[u] * sc);
+                    if constexpr (MAXP) putR(cb, p, v[u] - dl);
+                    else putE(cb, p, v[u] * sc);
                 }
             }
         }
@@ -476,6 +496,7 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
     double lz = 0.0;
     float pdl = 0.0f;
     bool pend = false;
+    int ocum = 0;                                         // chain: total shift (octaves)
     for (int tc = t0 + 1, nch = 0; tc <= t1; tc += CH, ++nch) {
         const double* Sch = Sbuf + (nch & 1) * 2 * rowsN;
         const int rows = min(CH, t1 - tc + 1);
@@ -504,7 +525,11 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
                     if (tid == 0) *rebsh = t;
                     pdl = dl;
                     pend = true;
+                    if constexpr (!MAXP) ocum += (int)dl;
                 }
+                // the shift in force from here to the next epoch (none at the span's end)
+                if constexpr (!MAXP)
+                    if ((t & (XK_REBASE - 1)) == 0 && cact) cumt[cl * NE + epoch(t)] = ocum;
                 // ---- alpha(t): the k = 1 term and the bulk
                 const double Se = Sch[row * C + cl];                  // end side of t
                 const double Ss = Sch[rowsN + row * C + cl];          // start side of t
@@ -619,8 +644,18 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
         // the ring in its final base (no rebase at t1; the one before it was applied
         // during t1) and the chain's state: the checkpoint a repair restarts from
         const size_t ck = ckrow + t1 / a.delta;
-        if (bact)
-            for (int q = j; q < K; q += G) a.ck_ring[(ck * K + q) * C + cb] = Rrow[slot(t1 - q)];
+        if (bact) {
+            if constexpr (MAXP) {
+                for (int q = j; q < K; q += G) a.ck_ring[(ck * K + q) * C + cb] = Rrow[slot(t1 - q)];
+            } else {
+                // log ring entries in the final base
+                const int* cum = cumt + cb * NE;
+                const int cnow = cum[epoch(t1)];
+                for (int q = j; q < K; q += G)
+                    a.ck_ring[(ck * K + q) * C + cb] =
+                        Rrow[slot(t1 - q)] - (float)(cnow - cum[epoch(t1 - q)]);
+            }
+        }
         if (cact) {
             a.ck_base[ck * C + cl] = Bc;
             a.ck_mprev[ck * C + cl] = Mref;

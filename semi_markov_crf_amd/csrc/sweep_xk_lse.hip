@@ -10,11 +10,12 @@ hipError_t launch_inst(const XkCfg& xc, const SweepLaunch& a, int ndir, hipStrea
     if (xk_ring_floats(xc, a.C, 1, false) > 0 && !a.xk_ring) return hipErrorInvalidValue;
     if (xc.NT > NTMAX || xc.NT < 64 + a.C * G || xc.kpl > KPLMAX || xc.kpl % XK_UNROLL != 0 ||
         (RM == XK_RING_MIRRORED && (KPLMAX - 1) * G > xc.RS) ||
-        (xc.RS & (xc.RS - 1)) != 0 || xc.RS < a.K + 2 || xc.CH * a.C > XK_PF * (xc.NT - 64))
+        (xc.RS & (xc.RS - 1)) != 0 || xc.RS < a.K + 2 || xc.CH * a.C > XK_PF * (xc.NT - 64) ||
+        (xc.NE & (xc.NE - 1)) != 0 || (size_t)xc.NE * XK_REBASE < (size_t)a.K + 2 + 2 * XK_REBASE)
         return hipErrorInvalidValue;
     if (a.mode != MODE_SPEC && a.mode != MODE_REPAIR) return hipErrorInvalidValue;
     const dim3 grid = a.mode == MODE_REPAIR ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);
-    const XkParams p{a.xk_ring, xc.RS, xc.CH, xc.kpl};
+    const XkParams p{a.xk_ring, xc.RS, xc.CH, xc.kpl, xc.NE};
     hipLaunchKernelGGL((k_sweep_xk<false, RM, G, KPLMAX, NTMAX>), grid, dim3(xc.NT), xc.lds, stream,
                        static_cast<const SweepArgs&>(a), p, a.proj_start, a.proj_end);
     return hipGetLastError();

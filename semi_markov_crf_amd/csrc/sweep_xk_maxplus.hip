@@ -14,7 +14,7 @@ hipError_t launch_inst(const XkCfg& xc, const SweepLaunch& a, int ndir, hipStrea
         return hipErrorInvalidValue;
     if (a.mode != MODE_SPEC && a.mode != MODE_REPAIR) return hipErrorInvalidValue;
     const dim3 grid = a.mode == MODE_REPAIR ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);
-    const XkParams p{a.xk_ring, xc.RS, xc.CH, xc.kpl};
+    const XkParams p{a.xk_ring, xc.RS, xc.CH, xc.kpl, xc.NE};
     hipLaunchKernelGGL((k_sweep_xk<true, RM, G, KPLMAX, NTMAX>), grid, dim3(xc.NT), xc.lds, stream,
                        static_cast<const SweepArgs&>(a), p, a.proj_start, a.proj_end);
     return hipGetLastError();

@@ -100,6 +100,7 @@ def test_spans_at_once_match_in_order_sweeps_and_oracle(crf, case):
     nm = np_(out["node_mass"])
     for i in range(B):
         L = int(w.lengths[i])
+        print(f"node mass deviation {np.abs(nm[i, :L] - 1.0).max():.2e}", flush=True)
         assert np.abs(nm[i, :L] - 1.0).max() <= 1e-4
     # the two agree far closer than the oracle tolerance
     close_abs(np_(out["marginals"]), np_(seq["marginals"]), 1e-5, "at once vs in order")
