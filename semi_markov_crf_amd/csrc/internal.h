@@ -48,6 +48,11 @@ constexpr int XK_FROM = 1026;      // durations from which the long-duration swe
 
 // where the rings of the long-duration sweeps live (sweep_xk.h)
 enum { XK_RING_LDS = 0, XK_RING_MIRRORED = 1, XK_RING_GLOBAL = 2 };
+// rings of C * RS floats a workgroup keeps in global memory: the log ring (both semirings)
+// unless it is in LDS, and the linear ring of the log semiring in the plain global layout
+constexpr int xk_global_rings(bool maxp, int ring) {
+    return ring == XK_RING_GLOBAL ? (maxp ? 1 : 2) : ring == XK_RING_MIRRORED ? (maxp ? 0 : 1) : 0;
+}
 
 struct XkCfg {
     bool ok;

@@ -121,25 +121,28 @@ XkCfg choose_xk(int C, int K, bool maxp) {
     // log semiring: a table of each label's total base shift per epoch of XK_REBASE
     // positions, covering more than the K + 2 positions a ring holds
     x.NE = maxp ? 0 : pow2_at_least((K + 2 + 3 * XK_REBASE - 1) / XK_REBASE);
-    // S chunks, S(L) and the staged outputs (fp64); transitions, bulk values, rebase
-    // shifts, staged ring entries and backpointers, the rebase position, the shift table
-    // (32-bit)
-    const size_t base = (size_t)8 * (4 * x.CH * C + C + 4 * C) +
-                        (size_t)4 * (C * C + 4 * C + C + 2 * C + 2 * C + 1 + (size_t)C * x.NE);
+    // S chunks, S(L) and the output history (fp64); transitions, bulk values, rebase
+    // shifts, the output history and the shift table (32-bit).  The history holds two
+    // chunks of positions, or two positions when the rings are in global memory.
+    auto base = [&](int HD) {
+        return (size_t)8 * (4 * x.CH * C + C + (maxp ? 1 : 2) * (size_t)HD * C) +
+               (size_t)4 * (C * C + 4 * C + C + (maxp ? 2 : 1) * (size_t)HD * C + (size_t)C * x.NE);
+    };
     // rings: the one the bulk sums read mirrored in LDS (its log twin, for the log
     // semiring, in global memory) when the window addressing allows it and it fits, else
     // every ring plain in LDS, else every ring in global memory
     const size_t row = (size_t)4 * C * x.RS;
     const bool mir_ok = (size_t)(kplmax - 1) * G <= (size_t)x.RS;
-    if (mir_ok && base + 2 * row <= LDS_BUDGET) {
+    const size_t bch = base(2 * x.CH);
+    if (mir_ok && bch + 2 * row <= LDS_BUDGET) {
         x.ring = XK_RING_MIRRORED;
-        x.lds = base + 2 * row;
-    } else if (base + (maxp ? 1 : 2) * row <= LDS_BUDGET) {
+        x.lds = bch + 2 * row;
+    } else if (bch + (maxp ? 1 : 2) * row <= LDS_BUDGET) {
         x.ring = XK_RING_LDS;
-        x.lds = base + (maxp ? 1 : 2) * row;
+        x.lds = bch + (maxp ? 1 : 2) * row;
     } else {
         x.ring = XK_RING_GLOBAL;
-        x.lds = base;
+        x.lds = base(2);
     }
     x.ok = x.lds <= LDS_BUDGET;
     return x;
@@ -147,9 +150,7 @@ XkCfg choose_xk(int C, int K, bool maxp) {
 
 size_t xk_ring_floats(const XkCfg& xc, int C, int workgroups, bool maxp) {
     if (!xc.ok) return 0;
-    const int rings = xc.ring == XK_RING_GLOBAL ? (maxp ? 1 : 2)
-                      : xc.ring == XK_RING_MIRRORED ? (maxp ? 0 : 1) : 0;
-    return (size_t)workgroups * rings * C * xc.RS;
+    return (size_t)workgroups * xk_global_rings(maxp, xc.ring) * C * xc.RS;
 }
 
 SweepCfg choose_sweep(int C, int K) {

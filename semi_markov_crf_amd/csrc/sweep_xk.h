@@ -91,6 +91,9 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
                                                    const float* __restrict__ proj_end) {
     static_assert(G <= 64, "a label's lanes share one wavefront");
     constexpr int U = XK_UNROLL;
+    // ring reads of a bulk value in flight at once: the whole window of a lane when the
+    // ring is in LDS and the window is short (one LDS round trip a position), else U
+    constexpr int UB = (RM != XK_RING_GLOBAL && KPLMAX <= 32) ? KPLMAX : U;
     constexpr double SC = MAXP ? 1.0 : LOG2E;      // working units: natural (max) or base 2
     constexpr double OUT = MAXP ? 1.0 : LN2;       // back to natural-log units
     extern __shared__ double lds[];
@@ -140,33 +143,43 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
     };
 
     // ---------------------------------------------------------------- LDS
+    // log ring R (both semirings) and linear ring E (log semiring): where they live, and
+    // whether a row is mirrored
+    constexpr bool RMIR = MAXP && RM == XK_RING_MIRRORED;
+    constexpr bool EMIR = !MAXP && RM == XK_RING_MIRRORED;
+    constexpr bool RGLB = RM == XK_RING_GLOBAL || (!MAXP && RM == XK_RING_MIRRORED);
+    constexpr bool EGLB = !MAXP && RM == XK_RING_GLOBAL;
+    constexpr int NGR = (RGLB ? 1 : 0) + (EGLB ? 1 : 0);   // rings in global memory
+    static_assert(NGR == xk_global_rings(MAXP, RM), "the host sizes the global rings");
+    // The chain stages every position's outputs in LDS (it issues no global memory
+    // operation inside the loop); the bulk lanes write them out.  With plain global rings
+    // the bulk sum of the next position reads the newest entry from global memory, so a
+    // position's outputs are written one position later (history of 2 positions); else a
+    // whole chunk of CH positions at the next chunk's first row (history of two chunks),
+    // so that the lanes, whose global stores share the vector memory counter with their
+    // loads, wait on stores once a chunk.
+    constexpr bool FLUSH_FIRST = RM == XK_RING_GLOBAL;
     const int rowsN = CH * C;
+    const int HD = FLUSH_FIRST ? 2 : 2 * CH;              // history depth (positions)
     double* Sbuf = lds;                                   // [2 chunks][end, start][CH][C]
     double* SL = Sbuf + 4 * rowsN;                        // [C]
-    // a position's outputs, staged by the chain for the bulk lanes to write one position
-    // later (the chain issues no global memory operation inside the loop, so nothing it
-    // waits on there includes its own stores): [2][X, A][C] (working units)
-    double* oXA = SL + C;
-    float* trl = (float*)(oXA + 4 * C);                   // [C][C]: trl[c' * C + c]
+    double* hA = SL + C;                                  // [HD][C] A (working units)
+    double* hX = hA + HD * C;                             // [HD][C] X (log semiring)
+    float* trl = (float*)(hX + (MAXP ? 0 : HD * C));      // [C][C]: trl[c' * C + c]
     float* part = trl + C * C;                            // [2][C][2] bulk values
     float* dlsh = part + 4 * C;                           // [C] rebase shift
-    float* oR = dlsh + C;                                 // [2][C] ring entry (staged)
-    uint32_t* oBP = (uint32_t*)(oR + 2 * C);              // [2][C] backpointer (staged)
-    int* rebsh = (int*)(oBP + 2 * C);                     // [1] position of the last rebase
+    float* hR = dlsh + C;                                 // [HD][C] ring entry
+    uint32_t* hB = (uint32_t*)(hR + HD * C);              // [HD][C] backpointer (max-plus)
+    // history row of position p >= t0 + 1
+    auto hrow = [&](int p) { return FLUSH_FIRST ? (p & 1) : (p - t0 - 1) % HD; };
     // log semiring: [C][NE] each label's total base shift (whole octaves) in force at the
     // epochs of XK_REBASE positions, by epoch mod NE.  A log ring entry keeps the base of
     // its epoch (only the linear ring is moved at a rebase); the table takes it to any
     // later base.
     const int NE = MAXP ? 0 : x.NE, NEM = NE - 1;
-    int* cumt = rebsh + 1;
+    int* cumt = (int*)(hB + (MAXP ? HD * C : 0));
     float* ringl = (float*)(cumt + (MAXP ? 0 : C * NE));  // the rings held in LDS
-    // log ring R (both semirings) and linear ring E (log semiring): base, row pitch, and
-    // whether a row is mirrored; a repair reuses its span's global slice
-    constexpr bool RMIR = MAXP && RM == XK_RING_MIRRORED;
-    constexpr bool EMIR = !MAXP && RM == XK_RING_MIRRORED;
-    constexpr bool RGLB = RM == XK_RING_GLOBAL || (!MAXP && RM == XK_RING_MIRRORED);
-    constexpr bool EGLB = RM == XK_RING_GLOBAL;
-    constexpr int NGR = (RGLB ? 1 : 0) + (EGLB ? 1 : 0);   // rings in global memory
+    // rings: base and row pitch; a repair reuses its span's global slice
     const int RP = RMIR ? 2 * RS : RS, EP = EMIR ? 2 * RS : RS;
     float* gslice = x.ring ? x.ring + (drow * a.nspans + span) * (size_t)NGR * C * RS : nullptr;
     float* Rbase = RGLB ? gslice : ringl;
@@ -214,7 +227,6 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
     for (size_t q = tid; q < (size_t)C * RP; q += NT) Rbase[q] = NEG;
     if constexpr (!MAXP)
         for (size_t q = tid; q < (size_t)C * EP; q += NT) Ebase[q] = 0.0f;
-    if (tid == 0) *rebsh = INT_MIN;
     if constexpr (!MAXP)
         for (int q = tid; q < C * NE; q += NT) cumt[q] = 0;   // positions <= t0: base 0
     auto epoch = [&](int p) { return (p >> XK_LOG_REBASE) & NEM; };
@@ -295,28 +307,37 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
         if (t0 == 0)   // window positions <= 0: position 0's value, nothing before it
             for (int p = min(hlo, tlo); p <= 0; ++p) window(p, cl, p == 0 ? a0 : -1.0e300);
     }
-    // bulk lanes, first lane of a label: the staged outputs of position p (the ring entry
-    // too when the ring is in global memory; the same lane reads it back first)
-    auto flush = [&](int p) {
-        if (!(bact && j == 0)) return;
-        const int s2 = p & 1;
-        const double av = oXA[(s2 * 2 + 1) * C + cb];
-        const size_t o = (outrow + (dir == 0 ? p : L - p)) * C + cb;
+    // the staged outputs of position p, label c (bulk lanes of label c, so that a label's
+    // global ring entries are written and read back by one wavefront): X, A, backpointer,
+    // seam windows, and the ring entries held in global memory (the LDS ones come from the
+    // chain)
+    auto emit = [&](int p, int c) {
+        const int h = hrow(p) * C + c;
+        const double av = hA[h];
+        const size_t o = (outrow + (dir == 0 ? p : L - p)) * C + c;
         if constexpr (MAXP) {
-            if (p > tout) a.bp[(outrow + p) * C + cb] = oBP[s2 * C + cb];
+            if (p > tout) a.bp[(outrow + p) * C + c] = hB[h];
         } else if (a.write_xa) {
-            if (p > tout) Xout[o] = oXA[(s2 * 2) * C + cb] * OUT;
+            if (p > tout) Xout[o] = hX[h] * OUT;
             if (p >= tout && p < t1) Aout[o] = av * OUT;
         }
-        if (p >= min(hlo, tlo)) window(p, cb, av * OUT);
-        // the rings held in global memory get their entry here, the LDS ones from the chain
-        if constexpr (RGLB) putR(cb, p, oR[s2 * C + cb]);
-        if constexpr (EGLB) putE(cb, p, xk_exp2(oR[s2 * C + cb]));
+        if (p >= min(hlo, tlo)) window(p, c, av * OUT);
+        if constexpr (RGLB) putR(c, p, hR[h]);
+        if constexpr (EGLB) putE(c, p, xk_exp2(hR[h]));
+    };
+    // one position (FLUSH_FIRST), or positions p0 .. p1 (a chunk)
+    auto flush = [&](int p0, int p1) {
+        if (!bact) return;
+        if constexpr (FLUSH_FIRST) {
+            if (j == 0) emit(p0, cb);
+        } else {
+            for (int p = p0 + j; p <= p1; p += G) emit(p, cb);
+        }
     };
 
     // ---------------------------------------------------------------- S staging
     // chunk n holds rows t = t0 + 1 + n*CH + r, r < CH: end side S(t) + pe(t) and start
-    // side S(t) - ps(t), working units; staged by the bulk lanes one chunk ahead
+    // side S(t) - ps(t), working units; staged by the bulk lanes a chunk ahead
     auto sidx = [&](int t, int q) -> size_t { return (size_t)(dir == 0 ? t : L - t) * C + q; };
     auto spub = [&](double raw, int q) -> double { return dir == 0 ? raw * SC : (SL[q] - raw) * SC; };
     __syncthreads();                                      // SL visible
@@ -330,13 +351,14 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
             Sbuf[q] = in ? sv + proj_e(t, l) : 0.0;
             Sbuf[rowsN + q] = in ? sv - proj_s(t, l) : 0.0;
         }
-    // the chunk after next is fetched into registers (at most XK_PF per lane), raw: the
-    // values are converted when stored, so no load is waited on before then
+    // the next chunk, loaded and stored at once (at most XK_PF values per lane): no global
+    // load stays in flight across positions, so the lanes never wait on their own output
+    // stores (they share the vector memory counter) except at the chunk's first row
     const float* PEd = dir == 0 ? PEb : PSb;              // end-side projection source
     const float* PSd = dir == 0 ? PSb : PEb;              // start-side projection source
-    double pf[XK_PF];
-    float pfe[XK_PF], pfs[XK_PF];
-    auto stage_fetch = [&](int tcs) {
+    auto stage = [&](int tcs, int buf) {
+        double pf[XK_PF];
+        float pfe[XK_PF], pfs[XK_PF];
 #pragma unroll
         for (int i = 0; i < XK_PF; ++i) {
             const int q = bt + i * NB;
@@ -349,8 +371,6 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
             pfe[i] = (in && PEd && t >= 1) ? PEd[(size_t)te * C + l] : 0.0f;
             pfs[i] = (in && PSd && t < L) ? PSd[(size_t)ts * C + l] : 0.0f;
         }
-    };
-    auto stage_store = [&](int buf) {
         double* dst = Sbuf + buf * 2 * rowsN;
 #pragma unroll
         for (int i = 0; i < XK_PF; ++i) {
@@ -362,7 +382,6 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
             }
         }
     };
-    stage_fetch(t0 + 1 + CH);
     __syncthreads();                                      // ring, chunk 0 visible
 
     // ---------------------------------------------------------------- bulk value
@@ -388,13 +407,13 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
             float best = NEG;
             int kb = INT_MAX;
 #pragma unroll
-            for (int i0 = 0; i0 < KPLMAX; i0 += U) {
+            for (int i0 = 0; i0 < KPLMAX; i0 += UB) {
                 if (i0 < kplr) {
-                    float v[U];
+                    float v[UB];
 #pragma unroll
-                    for (int u = 0; u < U; ++u) v[u] = bulk_at(Rrow, i0 + u);
+                    for (int u = 0; u < UB; ++u) v[u] = bulk_at(Rrow, i0 + u);
 #pragma unroll
-                    for (int u = 0; u < U; ++u) {
+                    for (int u = 0; u < UB; ++u) {
                         const float y = v[u] + Dw[i0 + u];
                         if (y > best) {                   // ascending k: the lowest wins ties
                             best = y;
@@ -408,13 +427,13 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
         } else {
             float acc = 0.0f;
 #pragma unroll
-            for (int i0 = 0; i0 < KPLMAX; i0 += U) {
+            for (int i0 = 0; i0 < KPLMAX; i0 += UB) {
                 if (i0 < kplr) {
-                    float v[U];
+                    float v[UB];
 #pragma unroll
-                    for (int u = 0; u < U; ++u) v[u] = bulk_at(Erow, i0 + u);
+                    for (int u = 0; u < UB; ++u) v[u] = bulk_at(Erow, i0 + u);
 #pragma unroll
-                    for (int u = 0; u < U; ++u) acc = fmaf(v[u], Dw[i0 + u], acc);
+                    for (int u = 0; u < UB; ++u) acc = fmaf(v[u], Dw[i0 + u], acc);
                 }
             }
             acc = group_reduce<G>(acc, OpSum());
@@ -426,6 +445,8 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
                 // duration scores from global memory)
                 const int* cum = cumt + crow * NE;
                 const int cnow = cum[epoch(tq - 2)];
+                // positions of the chunk of tq - 1 and the one before it are only staged
+                const int hlo_pos = t0 + 1 + max(0, (tq - 2 - t0) / CH - 1) * CH;
                 float m = NEG, s = 0.0f;
                 for (int i0 = 0; i0 < kplr; i0 += U) {
                     {
@@ -434,8 +455,12 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
                         for (int u = 0; u < U; ++u) {
                             const int k = 2 + j + (i0 + u) * G;
                             const int p = p0 - (i0 + u) * G;
-                            y[u] = Rrow[slot(p)] - (float)(cnow - cum[epoch(p)]) +
-                                   (bact ? durv(cb, k) : NEG);
+                            float rv;
+                            if constexpr (RGLB && !FLUSH_FIRST)   // chunks not yet written
+                                rv = p >= hlo_pos ? hR[hrow(p) * C + crow] : Rrow[slot(p)];
+                            else
+                                rv = Rrow[slot(p)];
+                            y[u] = rv - (float)(cnow - cum[epoch(p)]) + (bact ? durv(cb, k) : NEG);
                         }
                         float mc = y[0];
 #pragma unroll
@@ -469,18 +494,19 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
     // ring the bulk sums read moves: the log ring of max-plus, the linear ring of the log
     // semiring (its log ring keeps its epochs' bases).
     auto rebase_ring = [&](int tq) {
-        const int trb = *rebsh;
-        if (trb != tq - 2 || !bact) return;
-        const float dl = dlsh[cb];
-        const float sc = MAXP ? 1.0f : xk_pow2_neg(dl);
+        const int trb = tq - 2;                           // the chain's rebase positions
+        if (!bact || (trb & (XK_REBASE - 1)) != 0 || trb <= t0 || trb >= t1) return;
         const int p0 = tq - 2 - j;
-        for (int i0 = 0; i0 < kplr; i0 += U) {
-            // a chunk's loads first, then its stores (each slot belongs to one lane)
-            float v[U];
+        for (int i0 = 0; i0 < kplr; i0 += UB) {
+            // a chunk's loads (the whole window when it is short) and the shift first, then
+            // its stores (each slot belongs to one lane): one LDS round trip
+            float v[UB];
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = (MAXP ? Rrow : Erow)[slot(p0 - (i0 + u) * G)];
+            for (int u = 0; u < UB; ++u) v[u] = (MAXP ? Rrow : Erow)[slot(p0 - (i0 + u) * G)];
+            const float dl = dlsh[cb];
+            const float sc = MAXP ? 1.0f : xk_pow2_neg(dl);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
+            for (int u = 0; u < UB; ++u) {
                 const int p = p0 - (i0 + u) * G;
                 if (p <= trb - 1 && p >= trb - K + 1) {
                     if constexpr (MAXP) putR(cb, p, v[u] - dl);
@@ -522,7 +548,6 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
                     Mref -= dl;
                     Q -= dl;
                     if (cact) dlsh[cl] = dl;
-                    if (tid == 0) *rebsh = t;
                     pdl = dl;
                     pend = true;
                     if constexpr (!MAXP) ocum += (int)dl;
@@ -543,7 +568,8 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
                     sig = xk_lse2(e1, Q);
                 }
                 const float u = cact ? (float)(Se + Bc - H) + sig : NEG;  // alpha(t) - H
-                if (!MAXP && cact) oXA[((t & 1) * 2) * C + cl] = Se + Bc + (double)sig;
+                const int hr = (FLUSH_FIRST ? (t & 1) : (nch & 1) * CH + row) * C + cl;
+                if (!MAXP && cact) hX[hr] = Se + Bc + (double)sig;
                 // ---- transition step of t over every label's alpha (lane broadcasts; the
                 // lowest c' on ties)
                 float mu = NEG;                                        // max_c' u(c')
@@ -614,29 +640,32 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
                 if (cact) {
                     // outputs of t, staged; the ring entry goes straight to an LDS ring
                     if constexpr (MAXP)
-                        oBP[(t & 1) * C + cl] = (uint32_t)kb | (t < L ? ((uint32_t)cbest << 16) : 0u);
-                    oXA[((t & 1) * 2 + 1) * C + cl] = Bc + (double)Rnew;
-                    oR[(t & 1) * C + cl] = Rnew;
+                        hB[hr] = (uint32_t)kb | (t < L ? ((uint32_t)cbest << 16) : 0u);
+                    hA[hr] = Bc + (double)Rnew;
+                    hR[hr] = Rnew;
                     if constexpr (!RGLB) putR(cl, t, Rnew);
                     if constexpr (!MAXP && !EGLB) putE(cl, t, xk_exp2(Rnew));
                 }
                 Rn1 = Rnew;
                 if (Q > NEG_HALF) Mref = Q;
             } else {
-                // ---- the outputs of t-1, S staging (publish the next chunk, fetch the one
-                // after), the rebase of the ring, the bulk value of t+1
-                if (t - 1 > t0) flush(t - 1);
-                if (row == 0 && tc + CH <= t1) {
-                    stage_store((nch + 1) & 1);
-                    stage_fetch(tc + 2 * CH);
-                }
+                // ---- S staging (the next chunk, into the buffer the chain left at the last
+                // barrier), the rebase of the ring, the bulk value of t+1, and the staged
+                // outputs: of t-1 before the bulk value (plain global rings), or of the
+                // previous chunk after it, at a chunk's first row
+                if constexpr (FLUSH_FIRST)
+                    if (t - 1 > t0) flush(t - 1, t - 1);
+                if (row == 0 && tc + CH <= t1) stage(tc + CH, (nch + 1) & 1);
                 rebase_ring(t + 1);
                 if (t + 1 <= t1 && bact) bulk(t + 1);
+                if constexpr (!FLUSH_FIRST)
+                    if (row == 0 && nch > 0) flush(tc - CH, tc - 1);
             }
             __syncthreads();
         }
     }
-    if (!chain) flush(t1);
+    if constexpr (FLUSH_FIRST) flush(t1, t1);
+    else flush(t0 + 1 + (t1 - t0 - 1) / CH * CH, t1);    // the last chunk
     __syncthreads();                                      // the ring entry of t1 (global form)
 
     // ---------------------------------------------------------------- span end
