@@ -23,9 +23,9 @@ struct Layout {
     size_t status = 0, Leff = 0, tsum = 0, toff = 0, ttot = 0, S = 0;
     size_t logz = 0, logzb = 0;
     size_t head = 0, tail = 0, lzloc = 0, soff = 0, fbad = 0, diag = 0;
-    size_t ckR = 0, ckB = 0, ckM = 0, ckH = 0, XF = 0, AF = 0, XB = 0, AB = 0;
-    size_t Dn = 0, dnt = 0, dno = 0, mu = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0, rps = 0;
-    size_t gcnt = 0, gpart = 0, pst = 0, pen = 0;
+    size_t ckR = 0, ckB = 0, ckM = 0, ckH = 0, XF = 0, XB = 0;
+    size_t Dn = 0, dnt = 0, dno = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0, rps = 0;
+    size_t gcnt = 0, gpart = 0;
     size_t bp = 0, vfin = 0, vend = 0, btr = 0, bent = 0, btg = 0;
     size_t xkr = 0;                 // long-duration sweeps: the global ring scratch
     bool has_xkr = false;
@@ -121,14 +121,15 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
     } else if (op == SEMICRF_OP_BACKWARD) {
         lo.tm = marg_tile(C, K);
         lo.ntm = (T + 1 + lo.tm - 1) / lo.tm;
+        // the messages before the transition step of both directions (k_trans_step turns
+        // them into the values after it, in place)
         lo.XF = m.take(sizeof(double) * BT1C);
-        lo.AF = m.take(sizeof(double) * BT1C);
         lo.XB = m.take(sizeof(double) * BT1C);
-        lo.AB = m.take(sizeof(double) * BT1C);
-        lo.Dn = m.take(sizeof(double) * BT1C);
+        // in-tile prefix of (start - end mass), fp32; mu goes to the caller's marginals or
+        // grad_emissions, the raw boundary masses to the boundary outputs themselves
+        lo.Dn = m.take(sizeof(float) * BT1C);
         lo.dnt = m.take(sizeof(double) * B * lo.ntm * C);
         lo.dno = m.take(sizeof(double) * B * lo.ntm * C);
-        lo.mu = m.take(sizeof(float) * B * T * C);
         lo.mut = m.take(sizeof(double) * B * lo.ntm * C);
         lo.mutot = m.take(sizeof(double) * B * C);
         lo.zt = m.take(sizeof(double) * B * lo.ntm);
@@ -137,9 +138,6 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         lo.pd = m.take(sizeof(double) * B * lo.ngm * K * C);
         lo.pt = m.take(sizeof(double) * B * lo.ngm * C * C);
         lo.rps = m.take(sizeof(double) * reduce_scratch_doubles(C, K));
-        // raw start / end masses for the boundary outputs
-        lo.pst = m.take(sizeof(float) * (size_t)B * T * C);
-        lo.pen = m.take(sizeof(float) * (size_t)B * T * C);
         // gold-segmentation loss (semicrf_nll): counters and block sums
         lo.gcnt = m.take(sizeof(int) * (size_t)B * (K * C + C * C + C + 1));
         lo.gpart = m.take(sizeof(double) * (size_t)B * gold_blocks(T));
@@ -372,56 +370,58 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
     const SweepCfg cfg = choose_sweep(C, K);
     SweepLaunch a = base_args(trans, dur, pj, B, T, C, K, workspace, lo);
     a.XF = at<double>(workspace, lo.XF);
-    a.AF = at<double>(workspace, lo.AF);
     a.XB = at<double>(workspace, lo.XB);
-    a.AB = at<double>(workspace, lo.AB);
     a.write_xa = 1;
     // every checkpoint span of both directions at once with its per-position values, then
     // the seam check and the repair of failed seams
     if ((rc = run_spans(cfg, a, 2, lo, workspace, so, stream, events, 2))) return rc;
     STAGE(3);
 
+    TransStepArgs ts{};
+    ts.S = a.S; ts.Leff = a.Leff; ts.trans = trans;
+    ts.B = B; ts.T = T; ts.C = C;
+    ts.tile = lo.tm; ts.ntiles = lo.ntm; ts.tpg = lo.tpg; ts.ngroups = lo.ngm;
+    ts.XF = a.XF; ts.XB = a.XB;
+    ts.proj_start = pj.start; ts.proj_end = pj.end;
+    ts.logz = a.logz;
+    ts.off = a.off; ts.delta = lo.delta; ts.nspans = lo.nspans;
+    ts.part_trans = at<double>(workspace, lo.pt);
+    LAUNCH(launch_trans_step(ts, stream));
+
     MargArgs m{};
-    m.S = a.S; m.Leff = a.Leff; m.trans = trans; m.dur = dur;
+    m.S = a.S; m.Leff = a.Leff; m.dur = dur;
     m.B = B; m.T = T; m.C = C; m.K = K;
     m.tile = lo.tm; m.ntiles = lo.ntm; m.kchunk = marg_kchunk(C, K);
     m.tpg = lo.tpg; m.ngroups = lo.ngm;
-    m.XF = a.XF; m.AF = a.AF; m.XB = a.XB; m.AB = a.AB; m.logz = a.logz;
-    m.off = a.off;
-    m.delta = lo.delta;
-    m.nspans = lo.nspans;
-    m.Dn = at<double>(workspace, lo.Dn);
+    m.AF = a.XF; m.AB = a.XB;
+    m.Dloc = at<float>(workspace, lo.Dn);
     m.dn_tile = at<double>(workspace, lo.dnt);
     m.part_dur = at<double>(workspace, lo.pd);
-    m.part_trans = at<double>(workspace, lo.pt);
-    const bool want_b = br.grad_start || br.grad_end || br.prob;
-    if (want_b) {
-        m.pstart = at<float>(workspace, lo.pst);
-        m.pend = at<float>(workspace, lo.pen);
-    }
+    // raw boundary masses straight into the outputs that k_node_marginals rescales in place
+    m.pstart = br.grad_start;
+    m.pend = br.grad_end;
+    m.pbsum = br.prob;
     LAUNCH(launch_marginals(m, stream));
     STAGE(4);
     LAUNCH(launch_tile_scan(m.dn_tile, B, lo.ntm, C, false, at<double>(workspace, lo.dno), nullptr,
                             stream));
-    float* mu = marginals ? marginals : at<float>(workspace, lo.mu);
+    // mu lives in the caller's marginals, else in grad_emissions (k_grad_em then works in
+    // place)
+    float* mu = marginals ? marginals : grad_em;
     BoundaryOut bo{};
-    if (want_b) {
-        bo.pstart = m.pstart;
-        bo.pend = m.pend;
-        bo.grad_log_z = grad_log_z;
-        bo.grad_proj_start = br.grad_start;
-        bo.grad_proj_end = br.grad_end;
-        bo.boundary = br.prob;
-    }
+    bo.grad_log_z = grad_log_z;
+    bo.grad_proj_start = br.grad_start;
+    bo.grad_proj_end = br.grad_end;
+    bo.boundary = br.prob;
     bo.node_mass = br.node_mass;
-    LAUNCH(launch_node_marginals(m.Dn, at<double>(workspace, lo.dno), a.Leff, B, T, C, lo.tm,
+    LAUNCH(launch_node_marginals(m.Dloc, at<double>(workspace, lo.dno), a.Leff, B, T, C, lo.tm,
                                  lo.ntm, mu, at<double>(workspace, lo.mut),
                                  at<double>(workspace, lo.zt), bo, stream));
     LAUNCH(launch_tile_scan(at<double>(workspace, lo.mut), B, lo.ntm, C, false, nullptr,
                             at<double>(workspace, lo.mutot), stream));
     LAUNCH(launch_grad_em(mu, at<double>(workspace, lo.mutot), a.Leff, grad_log_z, B, T, C, grad_em,
                           stream));
-    LAUNCH(launch_reduce_partials(m.part_dur, m.part_trans, at<double>(workspace, lo.zt), a.Leff,
+    LAUNCH(launch_reduce_partials(m.part_dur, ts.part_trans, at<double>(workspace, lo.zt), a.Leff,
                                   grad_log_z, B, C, K, lo.tm, lo.ntm, lo.tpg,
                                   at<double>(workspace, lo.rps), grad_dur, grad_trans, stream));
     if (log_z) LAUNCH(launch_write_logz(a.logz, B, log_z, stream));

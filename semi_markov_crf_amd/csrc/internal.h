@@ -146,17 +146,16 @@ struct SweepArgs {
     int mode;               // MODE_SPEC: grid (nspans, B, ndir); MODE_REPAIR: grid (B, ndir)
     int delta;              // checkpoint interval
     int nspans;             // max spans per sequence (ceil(T / delta))
-    int write_xa;           // write the per-position values X / A
+    int write_xa;           // write the per-position values X
     // checkpoints at span ends [2 dirs][B][nspans][...]; index 0 of the span axis is unused
     float* ck_ring;         // [..][K][C]
     double* ck_base;        // [..][C]
     float* ck_mprev;        // [..][C]
     double* ck_href;        // [..]
-    // per-position outputs, natural-log units, [B][T+1][C]
+    // per-position outputs, natural-log units, [B][T+1][C]: the messages before the
+    // transition step (X on (tout, t1] of a span)
     double* XF;             // forward: alpha[t, c]
-    double* AF;             // forward: alpha_bar[t, c] - S[t, c]
     double* XB;             // backward: beta_bar[s, c]
-    double* AB;             // backward: beta[u, c] + S[u, c] - S[L, c]
     double* logz;           // [B] forward log Z
     double* logz_b;         // [B] log Z from the backward sweep (consistency check)
     // speculative spans (MODE_SPEC) and their repair (MODE_REPAIR)
@@ -243,49 +242,66 @@ hipError_t launch_prefix(const float* em, const int* Leff, int B, int T, int C,
                          hipStream_t stream);
 
 // ------------------------------------------------------------------ marginals / gradients
-struct MargArgs {
+// The transition step of every position, in place: XF / XB (the sweeps' messages before
+// it) become AF / AB in base 2 (frame offsets added, log Z and S[L] folded in; see
+// marginals.hip), and the transition posteriors are summed per tile group.
+struct TransStepArgs {
     const double* S;
     const int* Leff;
     const float* trans;
+    int B, T, C;
+    int tile, ntiles, tpg, ngroups;   // as k_marginals
+    double* XF;                       // [B][T+1][C], in: alpha, out: AF
+    double* XB;                       // [B][T+1][C], in: beta_bar, out: AB
+    const float* proj_start;          // [B][T][C] or NULL
+    const float* proj_end;            // [B][T][C] or NULL
+    const double* logz;
+    // frame offsets of the speculative spans, [2 dirs][B][nspans] (NULL: none): added to
+    // XF of forward span floor((s-1)/delta) and to XB of the mirrored span of L - s - 1
+    const double* off;
+    int delta, nspans;
+    double* part_trans;               // [B][ngroups][C][C]
+};
+hipError_t launch_trans_step(const TransStepArgs& a, hipStream_t stream);
+
+struct MargArgs {
+    const double* S;
+    const int* Leff;
     const float* dur;
     int B, T, C, K;
     int tile;               // positions per tile
     int kchunk;             // durations per staged chunk
     int ntiles;             // ceil((T+1) / tile)
     int tpg, ngroups;       // tiles per group of the duration / transition partials
-    const double* XF; const double* AF; const double* XB; const double* AB;
-    const double* logz;
-    // frame offsets of the speculative spans, [2 dirs][B][nspans] (NULL: none): added to
-    // XF / AF of forward span floor((s-1)/delta) / floor(s/delta) and to XB / AB of the
-    // mirrored span of L - s likewise
-    const double* off;
-    int delta, nspans;
-    double* Dn;             // [B][T+1][C]: start mass - end mass of segments at each position
-    double* dn_tile;        // [B][ntiles][C]: tile sums of Dn
+    const double* AF;       // [B][T+1][C] from k_trans_step
+    const double* AB;       // [B][T+1][C] from k_trans_step
+    // [B][T+1][C]: inclusive prefix sum, inside each tile, of (start mass - end mass) of
+    // the segments at each position (fp64 sums rounded once)
+    float* Dloc;
+    double* dn_tile;        // [B][ntiles][C]: tile sums of (start mass - end mass)
     double* part_dur;       // [B][ngroups][K][C]: sums over a group's tiles
-    double* part_trans;     // [B][ngroups][C][C]
-    float* pstart;          // [B][T][C] or NULL: start mass of segments at each position
-    float* pend;            // [B][T][C] or NULL: mass of segments whose last position it is
+    float* pstart;          // [B][T][C] or NULL: raw start mass of segments at each position
+    float* pend;            // [B][T][C] or NULL: raw mass of segments whose last position it is
+    float* pbsum;           // [B][T] or NULL: raw start mass summed over labels
 };
 hipError_t launch_marginals(const MargArgs& a, hipStream_t stream);
 // tiles per group of the posterior partials: enough groups to fill the device, the
 // partials (B * groups * (K + C) * C doubles) within a fixed budget
 int marg_tiles_per_group(int B, int ntiles, int C, int K);
 
-// mu = prefix sum of Dn, normalised per position; writes marginals, per-tile sums of
-// mu and the per-tile mean normaliser.  With pstart / pend (the raw start and end masses
-// of k_marginals) also the boundary probability [B][T] and g times the normalised start
-// and end marginals [B][T][C] (any of the three outputs may be NULL).
+// mu = tile offset + in-tile prefix Dloc, normalised per position; writes marginals, per-tile
+// sums of mu and the per-tile mean normaliser.  The three boundary outputs hold the raw
+// masses k_marginals wrote into them (start [B][T][C], end [B][T][C], start summed over
+// labels [B][T]) and are rescaled in place: the boundary probability, and g times the
+// normalised start and end marginals (any of them may be NULL).
 struct BoundaryOut {
-    const float* pstart;
-    const float* pend;
     const float* grad_log_z;
     float* grad_proj_start;
     float* grad_proj_end;
     float* boundary;
     float* node_mass;           // [B][T] or NULL: the per-position normaliser itself
 };
-hipError_t launch_node_marginals(const double* Dn, const double* dn_off, const int* Leff,
+hipError_t launch_node_marginals(const float* Dloc, const double* dn_off, const int* Leff,
                                  int B, int T, int C, int tile, int ntiles, float* mu,
                                  double* mu_tile, double* z_tile, const BoundaryOut& bo,
                                  hipStream_t stream);

@@ -1,29 +1,37 @@
 // Posterior marginals and gradients of log Z on gfx950.
 //
-// From the per-position forward / backward quantities written by the span recompute
-//   XF[s,c] = alpha[s,c]        AF[s,c] = abar[s,c] - S[s,c] + P_start[s,c]
-//   XB[s,c] = beta_bar[s,c]     AB[u,c] = beta[u,c] + S[u,c] + P_end[u-1,c] - S[L,c]
-// (the boundary projections P_start / P_end are zero when absent) the posterior of one
-// segment [s, s+k) of label c is
-//   p(s,k,c) = exp(AF[s,c] + AB[s+k,c] + S[L,c] + dur[k-1,c] - logZ)
-// and that of a transition c' -> c at s is exp(XF[s,c'] + trans[c',c] + XB[s,c] - logZ).
-// Their sums are the gradients of log Z with respect to dur and trans, and the
-// position marginal mu[t,c] (the probability that t lies in a segment of label c) is the
-// mass of the segments covering t.  The pages validate exactly these quantities
-// ("Streaming Structured Inference with Flash-SemiCRF", gist.science EN explainer,
-// "4. Results and Benchmarks": marginals sum to 1, exact gradients).
+// The sweeps write, per position, the forward and backward messages before the
+// transition step (natural log, each span in its own frame):
+//   XF[s,c] = alpha[s,c]       (segments of label c ending at s, their end projection included)
+//   XB[s,c] = beta_bar[s,c]    (suffixes whose first segment, label c, starts at s)
+// k_trans_step takes the transition step once per position, in place, and leaves the
+// start-side and end-side values in base 2, frame offsets added, shifted so that a
+// segment's posterior is one exponential:
+//   AF[s,c] = log2 e (log sum_c' exp(XF[s,c'] + trans[c',c]) - S[s,c] + P_start[s,c] + S[L,c] - logZ)
+//             (s = 0: log2 e (P_start[0,c] + S[L,c] - logZ))
+//   AB[u,c] = log2 e (log sum_c'' exp(XB[u,c''] + trans[c,c'']) + S[u,c] - S[L,c] + P_end[u-1,c])
+//             (u = L: log2 e P_end[L-1,c])
+//   p(s,k,c) = 2^(AF[s,c] + AB[s+k,c] + log2 e dur[k-1,c])
+// and, from the messages before it, the transition posteriors
+// exp(XF[s,c'] + trans[c',c] + XB[s,c] - logZ), summed per tile group.  Their sums are the
+// gradients of log Z with respect to dur and trans, and the position marginal mu[t,c] (the
+// probability that t lies in a segment of label c) is the mass of the segments covering
+// t.  The pages validate exactly these quantities ("Streaming Structured Inference with
+// Flash-SemiCRF", gist.science EN explainer, "4. Results and Benchmarks": marginals sum
+// to 1, exact gradients).
 //
 // mu is formed as a prefix sum over positions of (start mass - end mass), where both
-// masses are sums of the same per-segment values, so each segment's contribution
-// cancels exactly once it has ended.  mu is then divided by its sum over labels at each
-// position (1 in exact arithmetic).  This per-position normalisation removes the slow
-// drift between the forward and backward sweeps' rounding over 10^5..10^6 positions;
-// the dur / trans partial sums of a tile are divided by the tile's mean normaliser.
-// The start and end masses at each position, divided by the same per-position
-// normaliser, are the gradients with respect to the projections; their sum over labels
-// at t is the probability that a segment boundary (a segment start) lies at t (the pages
-// check that these boundary probabilities are valid at genome scale, "4. Results and
-// Benchmarks").
+// masses are fp64 sums of the same per-segment values, so each segment's contribution
+// cancels exactly once it has ended.  The prefix is kept as an fp32 prefix inside each
+// tile plus an fp64 prefix of the tile totals.  mu is then divided by its sum over labels
+// at each position (1 in exact arithmetic; the tests bound its distance from 1), which
+// removes the slow drift between the forward and backward sweeps' rounding over
+// 10^5..10^6 positions; the dur / trans partial sums of a tile are divided by the tile's
+// mean normaliser.  The start and end masses at each position, divided by the same
+// per-position normaliser, are the gradients with respect to the projections; their sum
+// over labels at t is the probability that a segment boundary (a segment start) lies at t
+// (the pages check that these boundary probabilities are valid at genome scale,
+// "4. Results and Benchmarks").
 #include <algorithm>
 
 #include "common.h"
@@ -32,15 +40,15 @@
 namespace semicrf {
 
 // LDS of k_marginals for tile TM and duration chunk KC: the tile's own start / end values,
-// the two shifted windows of a chunk, XF / XB, start / end mass accumulators (fp64), the
-// chunk's durations and the transitions (fp32).
+// the two shifted windows of a chunk, start / end mass accumulators (fp64), the prefix
+// scratch (256 doubles) and the chunk's durations (fp32).
 static size_t marg_lds(int C, int TM, int KC) {
-    return (size_t)8 * C * (8 * TM + 2 * KC) + (size_t)4 * ((size_t)KC * C + (size_t)C * C);
+    return (size_t)8 * C * (6 * TM + 2 * KC) + (size_t)8 * 256 + (size_t)4 * KC * C;
 }
 
 // Tile and duration chunk.  First choice: the largest tile of at least max(32, K/4)
 // positions (the per-tile duration partials, K*C doubles, then take at most as much memory
-// as the four per-position input arrays) whose LDS, with a chunk of at least min(K, 64) durations, lets
+// as the per-position input arrays) whose LDS, with a chunk of at least min(K, 64) durations, lets
 // three workgroups share a CU (12 wavefronts to hide the latency of the exponentials and
 // the fp64 sums).  Otherwise the largest tile that fits one workgroup per CU with such a
 // chunk; the smallest tile takes any chunk.
@@ -87,11 +95,166 @@ int marg_kchunk(int C, int K) {
 
 constexpr double DNEG = -1.0e300;
 
+// LDS of k_trans_step for tile TM: both directions' messages (fp64) and their
+// exponentials relative to the row maximum (fp32), the row maxima, the transitions in
+// base 2 and as linear weights.
+static size_t step_lds(int C, int TM) {
+    return (size_t)TM * C * (2 * 8 + 2 * 4) + (size_t)2 * 8 * TM + (size_t)2 * 4 * C * C;
+}
+
+// grid (ngroups, B), block 256: the tiles g*tpg .. (g+1)*tpg - 1 of sequence b in order.
+// Per tile: stage the messages of both directions (frame offsets added, base 2); the
+// transition partials, lanes over (c', c) (an fp32 sum over the tile's rows, then fp64
+// across the group's tiles); then the transition step of every row and direction, lanes
+// over (row, label), as a linear sum of the row's exponentials (relative to the row
+// maximum) against 2^(trans - max trans), redone exactly in log space where that sum
+// leaves [2^-100, inf); written back over the messages.
+__global__ __launch_bounds__(256) void k_trans_step(const TransStepArgs a) {
+    extern __shared__ double lds[];
+    const int C = a.C, T = a.T, TM = a.tile;
+    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int L = abs(a.Leff[b]);
+    const size_t rowC = (size_t)(T + 1) * C;
+    double* X1 = lds;                                // [TM][C] forward messages
+    double* X2 = X1 + (size_t)TM * C;                // [TM][C] backward messages
+    double* m1 = X2 + (size_t)TM * C;                // [TM] row maxima
+    double* m2 = m1 + TM;
+    float* E1 = (float*)(m2 + TM);                   // [TM][C] 2^(X - row max)
+    float* E2 = E1 + (size_t)TM * C;
+    float* tr2 = E2 + (size_t)TM * C;                // [C][C] trans * log2 e
+    float* trw = tr2 + (size_t)C * C;                // [C][C] 2^(tr2 - max tr2)
+
+    for (int q = tid; q < C * C; q += 256) tr2[q] = fmaxf((float)((double)a.trans[q] * LOG2E), NEG);
+    __syncthreads();
+    float tmax = NEG;
+    for (int q = 0; q < C * C; ++q) tmax = fmaxf(tmax, tr2[q]);
+    for (int q = tid; q < C * C; q += 256) trw[q] = fast_exp2(tr2[q] - tmax);
+
+    double* XF = a.XF + (size_t)b * rowC;
+    double* XB = a.XB + (size_t)b * rowC;
+    const double* Sb = a.S + (size_t)b * rowC;
+    const float* Ps = a.proj_start ? a.proj_start + (size_t)b * T * C : nullptr;
+    const float* Pe = a.proj_end ? a.proj_end + (size_t)b * T * C : nullptr;
+    const double logZ = a.logz[b];
+    // frame offsets of the spans that wrote each value (0 without speculative spans):
+    // forward X of position s from span floor((s-1)/delta), backward X of s from the span
+    // of the mirrored position L - s - 1
+    const double* offF = a.off ? a.off + (size_t)b * a.nspans : nullptr;
+    const double* offB = a.off ? a.off + ((size_t)a.B + b) * a.nspans : nullptr;
+    auto oXF = [&](int s) { return offF ? offF[(s - 1) / a.delta] : 0.0; };
+    auto oXB = [&](int s) { return offB ? offB[(L - s - 1) / a.delta] : 0.0; };
+    double* part_trans = a.part_trans + ((size_t)b * a.ngroups + g) * C * C;
+
+    const int tile_end = min(a.ntiles, (g + 1) * a.tpg);
+    for (int tile = g * a.tpg; tile < tile_end; ++tile) {
+        const int p0 = tile * TM;
+        const bool first = tile == g * a.tpg;
+        __syncthreads();   // the previous tile's LDS is read no more
+        for (int q = tid; q < TM * C; q += 256) {
+            const int r = q / C, c = q - r * C;
+            const int s = p0 + r;
+            const bool in = s >= 1 && s <= L - 1;
+            X1[q] = in ? (XF[(size_t)s * C + c] + oXF(s)) * LOG2E : DNEG;
+            X2[q] = in ? (XB[(size_t)s * C + c] + oXB(s)) * LOG2E : DNEG;
+        }
+        __syncthreads();
+        // transition partials
+        const double lz2 = logZ * LOG2E;
+        for (int q = tid; q < C * C; q += 256) {
+            const int cp = q / C, c = q - cp * C;
+            const float tv = tr2[q];
+            float acc = 0.0f;
+            for (int r = 0; r < TM; ++r) {
+                const double v = X1[(size_t)r * C + cp] + X2[(size_t)r * C + c] - lz2;
+                acc += fast_exp2((float)v + tv);
+            }
+            part_trans[q] = first ? (double)acc : part_trans[q] + (double)acc;
+        }
+        // row maxima, then the exponentials relative to them
+        for (int r = tid; r < 2 * TM; r += 256) {
+            const double* x = (r < TM ? X1 : X2) + (size_t)(r % TM) * C;
+            double m = DNEG;
+            for (int c = 0; c < C; ++c) m = fmax(m, x[c]);
+            (r < TM ? m1 : m2)[r % TM] = m;
+        }
+        __syncthreads();
+        for (int q = tid; q < 2 * TM * C; q += 256) {
+            const bool fw = q < TM * C;
+            const int qq = fw ? q : q - TM * C;
+            const int r = qq / C;
+            (fw ? E1 : E2)[qq] = fast_exp2((float)((fw ? X1 : X2)[qq] - (fw ? m1 : m2)[r]));
+        }
+        __syncthreads();
+        // the transition step; rows outside the sequence (and the unwritten message rows
+        // 0 of XF and L of XB) take their boundary values
+        for (int q = tid; q < 2 * TM * C; q += 256) {
+            const bool fw = q < TM * C;
+            const int qq = fw ? q : q - TM * C;
+            const int r = qq / C, c = qq - r * C;
+            const int s = p0 + r;
+            if (s > T) continue;
+            double out;
+            if (fw) {
+                if (s == 0) out = ((Ps ? (double)Ps[c] : 0.0) + (offF ? offF[0] : 0.0) +
+                                   Sb[(size_t)L * C + c] - logZ) * LOG2E;
+                else if (s > L - 1) out = DNEG;
+                else {
+                    const float* e = E1 + (size_t)r * C;
+                    float acc = 0.0f;
+                    for (int j = 0; j < C; ++j) acc = fmaf(e[j], trw[j * C + c], acc);
+                    float lv = fast_log2(acc) + tmax;
+                    if (!(acc >= 0x1p-100f)) {
+                        const double* x = X1 + (size_t)r * C;
+                        float m = NEG;
+                        for (int j = 0; j < C; ++j) m = fmaxf(m, (float)(x[j] - m1[r]) + tr2[j * C + c]);
+                        float z = 0.0f;
+                        for (int j = 0; j < C; ++j) z += fast_exp2((float)(x[j] - m1[r]) + tr2[j * C + c] - m);
+                        lv = m + fast_log2(z);
+                    }
+                    out = m1[r] + (double)lv +
+                          ((Ps ? (double)Ps[(size_t)s * C + c] : 0.0) - Sb[(size_t)s * C + c] +
+                           Sb[(size_t)L * C + c] - logZ) * LOG2E;
+                }
+                XF[(size_t)s * C + c] = out;
+            } else {
+                if (s == L) out = ((Pe ? (double)Pe[(size_t)(L - 1) * C + c] : 0.0) +
+                                   (offB ? offB[0] : 0.0)) * LOG2E;
+                else if (s < 1 || s > L) out = DNEG;
+                else {
+                    const float* e = E2 + (size_t)r * C;
+                    float acc = 0.0f;
+                    for (int j = 0; j < C; ++j) acc = fmaf(e[j], trw[c * C + j], acc);
+                    float lv = fast_log2(acc) + tmax;
+                    if (!(acc >= 0x1p-100f)) {
+                        const double* x = X2 + (size_t)r * C;
+                        float m = NEG;
+                        for (int j = 0; j < C; ++j) m = fmaxf(m, (float)(x[j] - m2[r]) + tr2[c * C + j]);
+                        float z = 0.0f;
+                        for (int j = 0; j < C; ++j) z += fast_exp2((float)(x[j] - m2[r]) + tr2[c * C + j] - m);
+                        lv = m + fast_log2(z);
+                    }
+                    out = m2[r] + (double)lv +
+                          ((Pe ? (double)Pe[(size_t)(s - 1) * C + c] : 0.0) + Sb[(size_t)s * C + c] -
+                           Sb[(size_t)L * C + c]) * LOG2E;
+                }
+                XB[(size_t)s * C + c] = out;
+            }
+        }
+    }
+}
+
+hipError_t launch_trans_step(const TransStepArgs& a, hipStream_t stream) {
+    if (a.tpg < 1 || a.ngroups != (a.ntiles + a.tpg - 1) / a.tpg) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_trans_step, dim3(a.ngroups, a.B), dim3(256), step_lds(a.C, a.tile), stream,
+                       a);
+    return hipGetLastError();
+}
+
 // grid (ngroups, B), block 256: the tiles g*tpg .. (g+1)*tpg - 1 of sequence b in order.
 // Durations are taken in chunks [kc0, kc1] of at most KC: per chunk the starts
 // [p0 - kc1, p0 + TM - 1 - kc0] and the ends [p0 + kc0, p0 + TM - 1 + kc1] are staged
-// beside the tile's own starts and ends.  The duration and transition partials of the
-// group's tiles are summed in tile order (each lane owns the same entries in every tile).
+// beside the tile's own starts and ends.  The duration partials of the group's tiles are
+// summed in tile order (each lane owns the same entries in every tile).
 __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
     extern __shared__ double lds[];
     const int C = a.C, K = a.K, T = a.T, TM = a.tile, KC = a.kchunk;
@@ -103,17 +266,15 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
     double* ABt = AFt + (size_t)TM * C;              // [TM][C]: ends p0 .. p0+TM-1
     double* AFw = ABt + (size_t)TM * C;              // [TM+KC][C]: starts of the chunk's ends
     double* ABw = AFw + (size_t)(TM + KC) * C;       // [TM+KC][C]: ends of the chunk's starts
-    double* XFs = ABw + (size_t)(TM + KC) * C;       // [TM][C]
-    double* XBs = XFs + (size_t)TM * C;              // [TM][C]
-    double* Dst = XBs + (size_t)TM * C;              // [TM][C] start mass
+    double* Dst = ABw + (size_t)(TM + KC) * C;       // [TM][C] start mass
     double* Den = Dst + (size_t)TM * C;              // [TM][C] end mass
-    float* dur2 = (float*)(Den + (size_t)TM * C);    // [KC][C]
-    float* tr2 = dur2 + (size_t)KC * C;              // [C][C]
+    double* csum = Den + (size_t)TM * C;             // [256] prefix scratch
+    float* dur2 = (float*)(csum + 256);              // [KC][C]
 
     double* part_dur = a.part_dur + ((size_t)b * a.ngroups + g) * K * C;
-    double* part_trans = a.part_trans + ((size_t)b * a.ngroups + g) * C * C;
-    double* Dn = a.Dn + (size_t)b * rowC;
-    for (int q = tid; q < C * C; q += 256) tr2[q] = fmaxf((float)((double)a.trans[q] * LOG2E), NEG);
+    float* Dloc = a.Dloc + (size_t)b * rowC;
+    const double* AF = a.AF + (size_t)b * rowC;
+    const double* AB = a.AB + (size_t)b * rowC;
     const int tile_end = min(a.ntiles, (g + 1) * a.tpg);
     for (int tile = g * a.tpg; tile < tile_end; ++tile) {
         const int p0 = tile * TM;
@@ -122,37 +283,17 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
         if (p0 > L) {   // nothing of this sequence here
             for (int q = tid; q < C; q += 256) dn_tile[q] = 0.0;
             for (int q = tid; q < TM * C; q += 256)
-                if (p0 + q / C <= T) Dn[(size_t)p0 * C + q] = 0.0;
-            if (first) {
+                if (p0 + q / C <= T) Dloc[(size_t)p0 * C + q] = 0.0f;
+            if (first)
                 for (int q = tid; q < K * C; q += 256) part_dur[q] = 0.0;
-                for (int q = tid; q < C * C; q += 256) part_trans[q] = 0.0;
-            }
             continue;
         }
-        const double logZ = a.logz[b];
-        const double* Sb = a.S + (size_t)b * rowC;
-        const double* XF = a.XF + (size_t)b * rowC;
-        const double* AF = a.AF + (size_t)b * rowC;
-        const double* XB = a.XB + (size_t)b * rowC;
-        const double* AB = a.AB + (size_t)b * rowC;
-        // frame offsets of the spans that wrote each value (0 without speculative spans):
-        // forward X / A of position s from span floor((s-1)/delta) / floor(s/delta), backward
-        // ones of s from the mirrored position L - s
-        const double* offF = a.off ? a.off + (size_t)b * a.nspans : nullptr;
-        const double* offB = a.off ? a.off + ((size_t)a.B + b) * a.nspans : nullptr;
-        auto oAF = [&](int s) { return offF ? offF[s / a.delta] : 0.0; };
-        auto oXF = [&](int s) { return offF ? offF[(s - 1) / a.delta] : 0.0; };
-        auto oAB = [&](int u) { return offB ? offB[(L - u) / a.delta] : 0.0; };
-        auto oXB = [&](int s) { return offB ? offB[(L - s - 1) / a.delta] : 0.0; };
-        // staged in base 2 (times log2 e); invalid starts / ends get DNEG so that their
-        // exponentials vanish
+        // base 2; invalid starts / ends get DNEG so that their exponentials vanish
         auto af = [&](int s, int c) -> double {
-            return (s >= 0 && s <= L - 1)
-                       ? (AF[(size_t)s * C + c] + oAF(s) + Sb[(size_t)L * C + c] - logZ) * LOG2E
-                       : DNEG;
+            return (s >= 0 && s <= L - 1) ? AF[(size_t)s * C + c] : DNEG;
         };
         auto ab = [&](int u, int c) -> double {
-            return (u >= 1 && u <= L) ? (AB[(size_t)u * C + c] + oAB(u)) * LOG2E : DNEG;
+            return (u >= 1 && u <= L) ? AB[(size_t)u * C + c] : DNEG;
         };
 
         for (int q = tid; q < TM * C; q += 256) {
@@ -160,9 +301,6 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
             const int s = p0 + r;
             AFt[q] = af(s, c);
             ABt[q] = ab(s, c);
-            XFs[q] = (s >= 1 && s <= L - 1) ? (XF[(size_t)s * C + c] + oXF(s)) * LOG2E : DNEG;
-            XBs[q] = (s >= 1 && s <= L - 1) ? (XB[(size_t)s * C + c] + oXB(s) - logZ) * LOG2E
-                                            : DNEG;
             Dst[q] = 0.0;
             Den[q] = 0.0;
         }
@@ -182,7 +320,8 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
                 dur2[q] = fmaxf((float)((double)a.dur[(size_t)(kc0 - 1) * C + q] * LOG2E), NEG);
             __syncthreads();
 
-            // ---- phase 1: per position, start and end mass of the chunk's segments
+            // ---- phase 1: per position, start and end mass of the chunk's segments (fp64
+            // sums of the same per-segment values: they cancel exactly in mu's prefix)
             for (int q = tid; q < TM * C; q += 256) {
                 const int r = q / C, c = q - r * C;
                 if (p0 + r > L) continue;
@@ -198,50 +337,64 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
                 Den[q] = en;
             }
 
-            // ---- phase 2: duration partials, lanes over (k, c), segments starting in the tile
+            // ---- phase 2: duration partials, lanes over (k, c), segments starting in the
+            // tile (an fp32 sum over the tile's rows, then fp64 across tiles)
             for (int q = tid; q < nk * C; q += 256) {
                 const int kk = q / C, c = q - kk * C;
                 const float d = dur2[q];
-                double acc = 0.0;
+                float acc = 0.0f;
 #pragma unroll 4
                 for (int r = 0; r < TM; ++r)
-                    acc += (double)seg(AFt[(size_t)r * C + c] + ABw[(size_t)(r + kk) * C + c], d);
+                    acc += seg(AFt[(size_t)r * C + c] + ABw[(size_t)(r + kk) * C + c], d);
                 double* pd = part_dur + (size_t)(kc0 - 1) * C + q;
-            *pd = first ? acc : *pd + acc;
+                *pd = first ? (double)acc : *pd + (double)acc;
             }
         }
         __syncthreads();
 
-        // ---- start mass - end mass per position, the tile's sums, boundary masses
-        for (int q = tid; q < TM * C; q += 256) {
-            const int r = q / C, c = q - r * C;
-            const int t = p0 + r;
-            const double st = Dst[q], en = Den[q];
-            const double d = st - en;
-            Dst[q] = d;
-            if (t <= T) Dn[(size_t)t * C + c] = d;
-            if (a.pstart && t < L) a.pstart[((size_t)b * T + t) * C + c] = (float)st;
-            if (a.pend && t >= 1 && t <= L) a.pend[((size_t)b * T + t - 1) * C + c] = (float)en;
-        }
+        // ---- raw boundary masses, then start mass - end mass per position
+        if (a.pstart || a.pend)
+            for (int q = tid; q < TM * C; q += 256) {
+                const int r = q / C, c = q - r * C;
+                const int t = p0 + r;
+                if (a.pstart && t < L) a.pstart[((size_t)b * T + t) * C + c] = (float)Dst[q];
+                if (a.pend && t >= 1 && t <= L) a.pend[((size_t)b * T + t - 1) * C + c] = (float)Den[q];
+            }
+        if (a.pbsum)
+            for (int r = tid; r < TM; r += 256) {
+                const int t = p0 + r;
+                if (t >= L) continue;
+                double s = 0.0;
+                for (int c = 0; c < C; ++c) s += Dst[(size_t)r * C + c];
+                a.pbsum[(size_t)b * T + t] = (float)s;
+            }
         __syncthreads();
-        for (int c = tid; c < C; c += 256) {
-            double s = 0.0;
-            for (int r = 0; r < TM; ++r) s += Dst[(size_t)r * C + c];
-            dn_tile[c] = s;
-        }
-
-        // ---- phase 3: transition partials, lanes over (c', c)
-        for (int q = tid; q < C * C; q += 256) {
-            const int cp = q / C, c = q - cp * C;
-            const float tv = tr2[q];
+        for (int q = tid; q < TM * C; q += 256) Dst[q] -= Den[q];
+        __syncthreads();
+        // in-tile inclusive prefix per label: lanes over (label, row chunk), fixed order;
+        // the last row's value is the tile total
+        for (int c0 = 0; c0 < C; c0 += 256) {
+            const int CW = min(256, C - c0);
+            const int R = 256 / CW;
+            const int chunk = (TM + R - 1) / R;
+            const int cw = tid % CW, r = tid / CW, c = c0 + cw;
+            const bool act = r < R;
             double acc = 0.0;
-            for (int r = 0; r < TM; ++r) {
-                const double v = XFs[(size_t)r * C + cp] + XBs[(size_t)r * C + c];
-                acc += (double)fast_exp2((float)v + tv);
+            if (act)
+                for (int i = r * chunk; i < min(TM, (r + 1) * chunk); ++i) acc += Dst[(size_t)i * C + c];
+            csum[tid] = acc;
+            __syncthreads();
+            if (act) {
+                double run = 0.0;
+                for (int qq = 0; qq < r; ++qq) run += csum[qq * CW + cw];
+                for (int i = r * chunk; i < min(TM, (r + 1) * chunk); ++i) {
+                    run += Dst[(size_t)i * C + c];
+                    if (p0 + i <= T) Dloc[(size_t)(p0 + i) * C + c] = (float)run;
+                    if (i == TM - 1) dn_tile[c] = run;
+                }
             }
-            part_trans[q] = first ? acc : part_trans[q] + acc;
+            __syncthreads();
         }
-        __syncthreads();   // the tile's LDS is read no more
     }
 }
 
@@ -266,9 +419,10 @@ int marg_tiles_per_group(int B, int ntiles, int C, int K) {
     return std::min(tpg, std::max(ntiles, 1));
 }
 
-// grid (ntiles, B), block 256: mu over positions [p0, p0+TM) of the prefix sum of Dn,
-// normalised per position; tile sums of mu and the tile's mean normaliser.
-__global__ __launch_bounds__(256) void k_node_marginals(const double* __restrict__ Dn,
+// grid (ntiles, B), block 256: mu over positions [p0, p0+TM) = the tile's offset (fp64
+// prefix of the tile totals) + the in-tile prefix, normalised per position; tile sums of
+// mu and the tile's mean normaliser; the boundary outputs rescaled in place.
+__global__ __launch_bounds__(256) void k_node_marginals(const float* __restrict__ Dloc,
                                                         const double* __restrict__ dn_off,
                                                         const int* __restrict__ Leff, int T, int C,
                                                         int TM, float* __restrict__ mu,
@@ -280,34 +434,12 @@ __global__ __launch_bounds__(256) void k_node_marginals(const double* __restrict
     const int L = abs(Leff[b]);
     const int p0 = tile * TM;
     double* v = lds;                       // [TM][C]
-    double* csum = v + (size_t)TM * C;     // [256]
-    double* zrow = csum + 256;             // [TM]
-    const double* D = Dn + (size_t)b * (T + 1) * C;
+    double* zrow = v + (size_t)TM * C;     // [TM]
+    const float* D = Dloc + (size_t)b * (T + 1) * C;
     const int rows = max(0, min(TM, L - p0));   // positions p0 .. p0+rows-1 are < L
-    for (int q = tid; q < rows * C; q += 256) v[q] = D[(size_t)p0 * C + q];
-    __syncthreads();
     const double* off = dn_off + ((size_t)b * ntiles + tile) * C;
-    for (int c0 = 0; c0 < C; c0 += 256) {
-        const int CW = min(256, C - c0);
-        const int R = 256 / CW;
-        const int chunk = (rows + R - 1) / R;
-        const int cw = tid % CW, r = tid / CW, c = c0 + cw;
-        const bool act = r < R;
-        double acc = 0.0;
-        if (act)
-            for (int i = r * chunk; i < min(rows, (r + 1) * chunk); ++i) acc += v[(size_t)i * C + c];
-        csum[tid] = acc;
-        __syncthreads();
-        if (act) {
-            double run = off[c];
-            for (int qq = 0; qq < r; ++qq) run += csum[qq * CW + cw];
-            for (int i = r * chunk; i < min(rows, (r + 1) * chunk); ++i) {
-                run += v[(size_t)i * C + c];
-                v[(size_t)i * C + c] = run;
-            }
-        }
-        __syncthreads();
-    }
+    for (int q = tid; q < rows * C; q += 256) v[q] = off[q % C] + (double)D[(size_t)p0 * C + q];
+    __syncthreads();
     for (int r = tid; r < rows; r += 256) {
         double z = 0.0;
         for (int c = 0; c < C; ++c) z += v[(size_t)r * C + c];
@@ -319,30 +451,31 @@ __global__ __launch_bounds__(256) void k_node_marginals(const double* __restrict
             const int t = p0 + r;
             if (t < T) bo.node_mass[(size_t)b * T + t] = r < rows ? (float)zrow[r] : 0.0f;
         }
-    if (bo.pstart) {
+    {
         // boundary probabilities and the projections' gradients: the raw start / end
         // masses over the same per-position normaliser (0 at padding)
-        const size_t base = (size_t)b * T * C;
         const double g = bo.grad_log_z ? (double)bo.grad_log_z[b] : 1.0;
-        for (int r = tid; r < TM; r += 256) {
-            const int t = p0 + r;
-            if (t >= T || !bo.boundary) continue;
-            double s = 0.0;
-            if (r < rows)
-                for (int c = 0; c < C; ++c) s += (double)bo.pstart[base + (size_t)t * C + c];
-            bo.boundary[(size_t)b * T + t] = r < rows ? (float)(s / zrow[r]) : 0.0f;
-        }
-        for (int q = tid; q < TM * C; q += 256) {
-            const int r = q / C;
-            const int t = p0 + r;
-            if (t >= T) continue;
-            const size_t idx = base + (size_t)p0 * C + q;
-            const bool in = r < rows;
-            if (bo.grad_proj_start)
-                bo.grad_proj_start[idx] = in ? (float)(g * (double)bo.pstart[idx] / zrow[r]) : 0.0f;
-            if (bo.grad_proj_end)
-                bo.grad_proj_end[idx] = in ? (float)(g * (double)bo.pend[idx] / zrow[r]) : 0.0f;
-        }
+        if (bo.boundary)
+            for (int r = tid; r < TM; r += 256) {
+                const int t = p0 + r;
+                if (t >= T) continue;
+                float* o = bo.boundary + (size_t)b * T + t;
+                *o = r < rows ? (float)((double)*o / zrow[r]) : 0.0f;
+            }
+        if (bo.grad_proj_start || bo.grad_proj_end)
+            for (int q = tid; q < TM * C; q += 256) {
+                const int r = q / C;
+                const int t = p0 + r;
+                if (t >= T) continue;
+                const size_t idx = (size_t)b * T * C + (size_t)p0 * C + q;
+                const bool in = r < rows;
+                if (bo.grad_proj_start)
+                    bo.grad_proj_start[idx] =
+                        in ? (float)(g * (double)bo.grad_proj_start[idx] / zrow[r]) : 0.0f;
+                if (bo.grad_proj_end)
+                    bo.grad_proj_end[idx] =
+                        in ? (float)(g * (double)bo.grad_proj_end[idx] / zrow[r]) : 0.0f;
+            }
     }
     float* mub = mu + (size_t)b * T * C;
     for (int q = tid; q < TM * C; q += 256) {
@@ -370,21 +503,21 @@ __global__ __launch_bounds__(256) void k_node_marginals(const double* __restrict
     }
 }
 
-hipError_t launch_node_marginals(const double* Dn, const double* dn_off, const int* Leff, int B,
+hipError_t launch_node_marginals(const float* Dloc, const double* dn_off, const int* Leff, int B,
                                  int T, int C, int tile, int ntiles, float* mu, double* mu_tile,
                                  double* z_tile, const BoundaryOut& bo, hipStream_t stream) {
-    const size_t lds = (size_t)8 * ((size_t)tile * C + 256 + tile);
-    hipLaunchKernelGGL(k_node_marginals, dim3(ntiles, B), dim3(256), lds, stream, Dn, dn_off, Leff,
+    const size_t lds = (size_t)8 * ((size_t)tile * C + tile);
+    hipLaunchKernelGGL(k_node_marginals, dim3(ntiles, B), dim3(256), lds, stream, Dloc, dn_off, Leff,
                        T, C, tile, mu, mu_tile, z_tile, bo);
     return hipGetLastError();
 }
 
 // grid (ceil(T*C/256), B): grad_em = g * (mu - mean over the valid positions of mu)
-__global__ __launch_bounds__(256) void k_grad_em(const float* __restrict__ mu,
+__global__ __launch_bounds__(256) void k_grad_em(const float* mu,
                                                  const double* __restrict__ mu_tot,
                                                  const int* __restrict__ Leff,
                                                  const float* __restrict__ grad_log_z, int T,
-                                                 int C, float* __restrict__ grad_em) {
+                                                 int C, float* grad_em) {
     const int b = blockIdx.y;
     const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (q >= (size_t)T * C) return;

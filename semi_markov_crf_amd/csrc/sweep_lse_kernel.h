@@ -260,7 +260,6 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
     const size_t ckrow = ((size_t)dir * a.B + b) * a.nspans;
     const size_t outrow = (size_t)b * (T + 1);
     double* Xout = dir == 0 ? a.XF : a.XB;
-    double* Aout = dir == 0 ? a.AF : a.AB;
     auto put_all = [&](int pos, float r) {   // every ring copy of one position
         ring_put<MIR>(Rrow, pos, RS, r);
         if constexpr (LIN) ring_put<MIR>(Erow, pos, RS, exp2_or_zero(r));
@@ -288,8 +287,6 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
         Rn1 = a.ck_ring[(ck * K + 0) * C + cc];
         Rn2 = K >= 2 ? a.ck_ring[(ck * K + 1) * C + cc] : NEG;
     }
-    if (writer && a.write_xa && t0 == tout)
-        Aout[(outrow + (dir == 0 ? t0 : L - t0)) * C + c] = (Bc + (double)Rn1) * LN2;
     if (writer && t0 == 0)   // window positions <= 0: position 0's value, nothing before it
         for (int p = min(hlo, tlo); p <= 0; ++p) window(p, p == 0 ? (Bc + (double)Rn1) * LN2 : -1.0e300);
     float En1 = exp2_or_zero(Rn1), En2 = exp2_or_zero(Rn2);
@@ -500,8 +497,6 @@ __global__ __launch_bounds__(NTMAX) void k_lse(const SweepArgs a, const int RS, 
                     if constexpr (MIR) *(writer ? Erow + s0 + RS : dummy + tid) = Enew;
                 }
             }
-            if (a.write_xa && writer && t < t1 && t >= tout)
-                Aout[(outrow + (dir == 0 ? t : L - t)) * C + c] = (Bc + (double)Rnew) * LN2;
             if (writer && t >= min(hlo, tlo)) window(t, (Bc + (double)Rnew) * LN2);
             Rn2 = Rn1; En2 = En1;
             Rn1 = Rnew; En1 = Enew;

@@ -339,7 +339,6 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     const size_t ckrow = ((size_t)dir * a.B + b) * a.nspans;
     const size_t outrow = (size_t)b * (T + 1);
     double* Xout = dir == 0 ? a.XF : a.XB;
-    double* Aout = dir == 0 ? a.AF : a.AB;
     auto slot_of = [&](int pos) { return (pos - t0 - 1) & RMASK; };
     double Bc = 0.0, H = 0.0;
     float Mref = 0.0f;
@@ -403,7 +402,6 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     }
     if (cact) {
         const double a0 = (Bc + (double)fH[M - 1]) * LN2;   // ring value of position t0
-        if (a.write_xa && t0 == tout) Aout[(outrow + (dir == 0 ? t0 : L - t0)) * C + cl] = a0;
         if (t0 == 0) {
             // window positions <= 0: position 0's value, nothing before it
             for (int p = hlo; p <= min(0, tout); ++p)
@@ -513,7 +511,6 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
                     if constexpr (PROJ) Sp += (double)Fprev[j];
                     Xout[o] = (Sp + Bp + (double)sgl) * LN2;
                 }
-                if (a.write_xa && p >= tout && p < t1) Aout[o] = av;
                 if (p >= hlo && p <= tout) a.head[(winrow + p - hlo) * C + cb] = av;
                 if (p >= tlo) a.tail[(winrow + p - tlo) * C + cb] = av;
             }
@@ -835,10 +832,6 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
                         if constexpr (PROJ) Sp += (double)fpe[m];
                         const float sgl = replayed ? sig[m] : fast_log2(sig[m]) + dmax;
                         Xout[(outrow + (dir == 0 ? p : L - p)) * C + cl] = (Sp + Bc + (double)sgl) * LN2;
-                        if (p < t1) {
-                            const float rl = replayed ? fH[M + m] : fast_log2(sH[M + m]) + fH[M + m];
-                            Aout[(outrow + (dir == 0 ? p : L - p)) * C + cl] = (Bc + (double)rl) * LN2;
-                        }
                     }
                 }
             }

@@ -300,10 +300,8 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
     }
     const size_t outrow = (size_t)b * (T + 1);
     double* Xout = dir == 0 ? a.XF : a.XB;
-    double* Aout = dir == 0 ? a.AF : a.AB;
     if (cact) {
         const double a0 = (Bc + (double)Rn1) * OUT;
-        if (!MAXP && a.write_xa && t0 == tout) Aout[(outrow + (dir == 0 ? t0 : L - t0)) * C + cl] = a0;
         if (t0 == 0)   // window positions <= 0: position 0's value, nothing before it
             for (int p = min(hlo, tlo); p <= 0; ++p) window(p, cl, p == 0 ? a0 : -1.0e300);
     }
@@ -319,7 +317,6 @@ __global__ __launch_bounds__(NTMAX) void k_sweep_xk(const SweepArgs a, const XkP
             if (p > tout) a.bp[(outrow + p) * C + c] = hB[h];
         } else if (a.write_xa) {
             if (p > tout) Xout[o] = hX[h] * OUT;
-            if (p >= tout && p < t1) Aout[o] = av * OUT;
         }
         if (p >= min(hlo, tlo)) window(p, c, av * OUT);
         if constexpr (RGLB) putR(c, p, hR[h]);

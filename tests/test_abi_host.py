@@ -141,8 +141,11 @@ def test_workspace_bytes(native):
         assert a > 0 and a % 256 == 0
         assert ws(op, 8, 1000, 6, 20, 0) > a           # grows with B
         assert ws(op, 4, 2000, 6, 20, 0) > a           # and with T
-    # backward holds O(B*T*C) per-position values plus checkpoints
-    assert ws(1, 1, 10_000, 6, 200, 0) > 5 * 8 * 10_001 * 6
+    # backward holds O(B*T*C) per-position values (S and the messages of both directions,
+    # fp64) plus checkpoints; with more than 16 labels also the values after the transition
+    assert ws(1, 1, 10_000, 6, 200, 0) > 3 * 8 * 10_001 * 6
+    assert ws(1, 1, 10_000, 6, 200, 0) < 4 * 8 * 10_001 * 6 + (64 << 20)
+    assert ws(1, 1, 10_000, 17, 200, 0) > 5 * 8 * 10_001 * 17
     assert ws(4, 1, 10, 2, 2, 0) == 0                  # unknown op
     assert 0 < ws(3, 1, 10, 2, 2, 0) < ws(0, 1, 10, 2, 2, 0)   # prefix: S goes to the caller
     assert ws(0, 0, 10, 2, 2, 0) == 0 and ws(0, 1, 0, 2, 2, 0) == 0
