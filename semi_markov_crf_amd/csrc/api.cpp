@@ -24,7 +24,7 @@ struct Layout {
     size_t logz = 0, logzb = 0;
     size_t head = 0, tail = 0, lzloc = 0, soff = 0, fbad = 0, diag = 0;
     size_t ckR = 0, ckB = 0, ckM = 0, ckH = 0, XF = 0, XB = 0;
-    size_t Dn = 0, dnt = 0, dno = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0, rps = 0;
+    size_t dnt = 0, dno = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0, rps = 0;
     size_t gcnt = 0, gpart = 0;
     size_t bp = 0, vfin = 0, vend = 0, btr = 0, bent = 0, btg = 0;
     size_t xkr = 0;                 // long-duration sweeps: the global ring scratch
@@ -125,9 +125,9 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         // them into the values after it, in place)
         lo.XF = m.take(sizeof(double) * BT1C);
         lo.XB = m.take(sizeof(double) * BT1C);
-        // in-tile prefix of (start - end mass), fp32; mu goes to the caller's marginals or
-        // grad_emissions, the raw boundary masses to the boundary outputs themselves
-        lo.Dn = m.take(sizeof(float) * BT1C);
+        // mu (and before it the in-tile prefix of start - end mass) goes to the caller's
+        // marginals or grad_emissions, the raw boundary masses to the boundary outputs
+        // themselves
         lo.dnt = m.take(sizeof(double) * B * lo.ntm * C);
         lo.dno = m.take(sizeof(double) * B * lo.ntm * C);
         lo.mut = m.take(sizeof(double) * B * lo.ntm * C);
@@ -394,20 +394,20 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
     m.tile = lo.tm; m.ntiles = lo.ntm; m.kchunk = marg_kchunk(C, K);
     m.tpg = lo.tpg; m.ngroups = lo.ngm;
     m.AF = a.XF; m.AB = a.XB;
-    m.Dloc = at<float>(workspace, lo.Dn);
     m.dn_tile = at<double>(workspace, lo.dnt);
     m.part_dur = at<double>(workspace, lo.pd);
     // raw boundary masses straight into the outputs that k_node_marginals rescales in place
     m.pstart = br.grad_start;
     m.pend = br.grad_end;
     m.pbsum = br.prob;
+    // mu lives in the caller's marginals, else in grad_emissions (k_grad_em then works in
+    // place); k_marginals leaves the in-tile prefix there first
+    float* mu = marginals ? marginals : grad_em;
+    m.Dloc = mu;
     LAUNCH(launch_marginals(m, stream));
     STAGE(4);
     LAUNCH(launch_tile_scan(m.dn_tile, B, lo.ntm, C, false, at<double>(workspace, lo.dno), nullptr,
                             stream));
-    // mu lives in the caller's marginals, else in grad_emissions (k_grad_em then works in
-    // place)
-    float* mu = marginals ? marginals : grad_em;
     BoundaryOut bo{};
     bo.grad_log_z = grad_log_z;
     bo.grad_proj_start = br.grad_start;

@@ -275,8 +275,9 @@ struct MargArgs {
     int tpg, ngroups;       // tiles per group of the duration / transition partials
     const double* AF;       // [B][T+1][C] from k_trans_step
     const double* AB;       // [B][T+1][C] from k_trans_step
-    // [B][T+1][C]: inclusive prefix sum, inside each tile, of (start mass - end mass) of
-    // the segments at each position (fp64 sums rounded once)
+    // [B][T][C]: inclusive prefix sum, inside each tile, of (start mass - end mass) of
+    // the segments at each position (fp64 sums rounded once); the marginals' buffer, which
+    // k_node_marginals turns into mu in place
     float* Dloc;
     double* dn_tile;        // [B][ntiles][C]: tile sums of (start mass - end mass)
     double* part_dur;       // [B][ngroups][K][C]: sums over a group's tiles

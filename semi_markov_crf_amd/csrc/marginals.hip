@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
     float* dur2 = (float*)(csum + 256);              // [KC][C]
 
     double* part_dur = a.part_dur + ((size_t)b * a.ngroups + g) * K * C;
-    float* Dloc = a.Dloc + (size_t)b * rowC;
+    float* Dloc = a.Dloc + (size_t)b * T * C;
     const double* AF = a.AF + (size_t)b * rowC;
     const double* AB = a.AB + (size_t)b * rowC;
     const int tile_end = min(a.ntiles, (g + 1) * a.tpg);
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
         if (p0 > L) {   // nothing of this sequence here
             for (int q = tid; q < C; q += 256) dn_tile[q] = 0.0;
             for (int q = tid; q < TM * C; q += 256)
-                if (p0 + q / C <= T) Dloc[(size_t)p0 * C + q] = 0.0f;
+                if (p0 + q / C < T) Dloc[(size_t)p0 * C + q] = 0.0f;
             if (first)
                 for (int q = tid; q < K * C; q += 256) part_dur[q] = 0.0;
             continue;
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
                 for (int qq = 0; qq < r; ++qq) run += csum[qq * CW + cw];
                 for (int i = r * chunk; i < min(TM, (r + 1) * chunk); ++i) {
                     run += Dst[(size_t)i * C + c];
-                    if (p0 + i <= T) Dloc[(size_t)(p0 + i) * C + c] = (float)run;
+                    if (p0 + i < T) Dloc[(size_t)(p0 + i) * C + c] = (float)run;
                     if (i == TM - 1) dn_tile[c] = run;
                 }
             }
@@ -413,7 +413,7 @@ int marg_tiles_per_group(int B, int ntiles, int C, int K) {
     constexpr long long TARGET = 8192;                   // workgroups
     int tpg = (int)std::max<long long>(1, ((long long)B * ntiles + TARGET - 1) / TARGET);
     auto bytes = [&](int t) {
-        return (size_t)B * ((ntiles + t - 1) / t) * (size_t)(K + C) * C * sizeof(double);
+        return (size_t)B * ((ntiles + t - 1) / t) * (size_t)(8 * K + 8 * C) * C;
     };
     while (tpg < ntiles && bytes(tpg) > BUDGET) tpg *= 2;
     return std::min(tpg, std::max(ntiles, 1));
@@ -422,10 +422,10 @@ int marg_tiles_per_group(int B, int ntiles, int C, int K) {
 // grid (ntiles, B), block 256: mu over positions [p0, p0+TM) = the tile's offset (fp64
 // prefix of the tile totals) + the in-tile prefix, normalised per position; tile sums of
 // mu and the tile's mean normaliser; the boundary outputs rescaled in place.
-__global__ __launch_bounds__(256) void k_node_marginals(const float* __restrict__ Dloc,
+__global__ __launch_bounds__(256) void k_node_marginals(const float* Dloc,
                                                         const double* __restrict__ dn_off,
                                                         const int* __restrict__ Leff, int T, int C,
-                                                        int TM, float* __restrict__ mu,
+                                                        int TM, float* mu,
                                                         double* __restrict__ mu_tile,
                                                         double* __restrict__ z_tile,
                                                         const BoundaryOut bo) {
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(256) void k_node_marginals(const float* __restrict_
     const int p0 = tile * TM;
     double* v = lds;                       // [TM][C]
     double* zrow = v + (size_t)TM * C;     // [TM]
-    const float* D = Dloc + (size_t)b * (T + 1) * C;
+    const float* D = Dloc + (size_t)b * T * C;
     const int rows = max(0, min(TM, L - p0));   // positions p0 .. p0+rows-1 are < L
     const double* off = dn_off + ((size_t)b * ntiles + tile) * C;
     for (int q = tid; q < rows * C; q += 256) v[q] = off[q % C] + (double)D[(size_t)p0 * C + q];
@@ -566,7 +566,6 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const double* __restric
     const bool isd = e < nd;
     const int ee = isd ? e : e - nd;
     const int stride = isd ? nd : C * C;
-    const double* src = isd ? part_dur : part_trans;
     double total = 0.0;
     for (int b = 0; b < B; ++b) {
         const int L = abs(Leff[b]);
@@ -578,7 +577,8 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const double* __restric
                 zs += (double)rows * z_tile[(size_t)b * ntiles + tl];
                 ns += (double)rows;
             }
-            s += src[((size_t)b * ngroups + j) * stride + ee] / (ns > 0.0 ? zs / ns : 1.0);
+            const size_t at = ((size_t)b * ngroups + j) * stride + ee;
+            s += (isd ? (double)part_dur[at] : part_trans[at]) / (ns > 0.0 ? zs / ns : 1.0);
         }
         total += (grad_log_z ? (double)grad_log_z[b] : 1.0) * s;
     }
