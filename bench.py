@@ -301,7 +301,7 @@ def main():
     trans = torch.from_numpy(w.trans).to(d)
     dur = torch.from_numpy(w.dur).to(d)
     B, T, C, K = w.B, w.T, w.C, w.K
-    delta = crf.checkpoint_interval(T, K, args.delta)
+    delta = crf.checkpoint_interval(T, K, args.delta) if args.delta else crf.viterbi_interval(B, T, K)
     nb = crf.workspace_bytes(crf.OP_BACKWARD, B, T, C, K, args.delta)
     nv = crf.workspace_bytes(crf.OP_VITERBI, B, T, C, K)
     ws_b = torch.empty(nb, dtype=torch.uint8, device=d)

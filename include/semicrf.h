@@ -80,14 +80,16 @@ const char* semicrf_status_string(int status);
  * about sqrt(TK)); clamped to [1, T].  0 on bad input. */
 int semicrf_checkpoint_interval(int T, int K, int delta);
 
-/* Checkpoint interval of semicrf_viterbi (which takes none) for a batch of B sequences of
- * padded length T: semicrf_checkpoint_interval(T, K, 0), halved when the batch holds at
- * most 128 spans of that length and each is at least four burn-ins (12 K) long, so that
- * the spans swept at once occupy more compute units.  0 on bad input. */
+/* The default checkpoint interval for a batch of B sequences of padded length T: the one
+ * semicrf_viterbi uses (it takes none) and the one semicrf_logz / semicrf_backward use for
+ * delta = 0.  semicrf_checkpoint_interval(T, K, 0), halved when the batch holds at most
+ * 128 spans of that length and each is at least four burn-ins (12 K) long, so that the
+ * spans swept at once occupy more compute units.  0 on bad input. */
 int semicrf_viterbi_interval(int B, int T, int K);
 
-/* Bytes of workspace that `op` needs for these shapes (delta as above).  0 if the
- * arguments are invalid or unsupported. */
+/* Bytes of workspace that `op` needs for these shapes (delta as the call takes it: > 0 an
+ * explicit interval, 0 the default above).  0 if the arguments are invalid or
+ * unsupported. */
 size_t semicrf_workspace_bytes(semicrf_op op, int B, int T, int C, int K, int delta);
 
 /* Centred prefix sums alone (EN explainer, "2. Methodology": "Emission Baseline
@@ -105,8 +107,8 @@ int semicrf_prefix(const float* emissions, const int32_t* lengths, int B, int T,
 
 /* log Z for every sequence: the log-sum-exp of the scores of all segmentations
  * (EN explainer, "2. Methodology", "Streaming Forward-Backward with Ring Buffers",
- * forward pass).  delta: checkpoint interval (0 = ceil(sqrt(T*K))), the same value as
- * given to semicrf_workspace_bytes.  Output: log_z [B] float32. */
+ * forward pass).  delta: checkpoint interval (0 = semicrf_viterbi_interval(B, T, K)), the
+ * same value as given to semicrf_workspace_bytes.  Output: log_z [B] float32. */
 int semicrf_logz(const float* emissions, const int32_t* lengths, const float* trans,
                  const float* dur, int B, int T, int C, int K, int delta, hipStream_t stream,
                  void* workspace, size_t workspace_bytes, float* log_z);
@@ -122,8 +124,8 @@ int semicrf_logz(const float* emissions, const int32_t* lengths, const float* tr
  *   marginals      [B, T, C] float32  or NULL: posterior probability that position t
  *                                     lies in a segment of label c (sums to 1 over c)
  *   log_z          [B]       float32  or NULL
- * delta: checkpoint interval (0 = ceil(sqrt(T*K))); results do not depend on it
- * beyond rounding. */
+ * delta: checkpoint interval (0 = semicrf_viterbi_interval(B, T, K)); results do not
+ * depend on it beyond rounding. */
 int semicrf_backward(const float* emissions, const int32_t* lengths, const float* trans,
                      const float* dur, int B, int T, int C, int K, int delta,
                      hipStream_t stream, void* workspace, size_t workspace_bytes,

@@ -55,12 +55,13 @@ int resolve_delta(int T, int K, int delta) {
     return (int)d;
 }
 
-// The decode takes no checkpoint interval.  It starts from the log-semiring default and
-// halves it when the batch's spans (one workgroup each) would leave most compute units idle
-// and a span stays long next to its burn-in: at B = 4, T = 10^5, K = 200 the decode drops
-// from 1.78 to 1.18 ms; with 32 speech-length sequences the halving costs more burn-in
-// than it gains (0.53 -> 0.61 ms), so it is not taken there.
-int viterbi_delta(int B, int T, int K) {
+// The default checkpoint interval (delta = 0, and always for the decode, which takes
+// none).  It starts from ceil(sqrt(T*K)) and halves it when the batch's spans (one
+// workgroup each, both directions of a span in one for the backward) would leave most
+// compute units idle and a span stays long next to its burn-in: at B = 4, T = 10^5, K = 200
+// the decode drops from 1.78 to 1.18 ms; with 32 speech-length sequences the halving costs
+// more burn-in than it gains (0.53 -> 0.61 ms), so it is not taken there.
+int default_delta(int B, int T, int K) {
     const int d = resolve_delta(T, K, 0);
     if (d < 1) return 0;
     const long long spans = (long long)B * ((T + d - 1) / d);
@@ -89,7 +90,9 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
     if (op == SEMICRF_OP_LOGZ || op == SEMICRF_OP_BACKWARD || op == SEMICRF_OP_VITERBI) {
         // checkpoint spans: checkpoints, seam windows and frame offsets per direction (the
         // decode runs forward only, with the default interval)
-        lo.delta = op == SEMICRF_OP_VITERBI ? viterbi_delta(B, T, K) : resolve_delta(T, K, delta);
+        // delta = 0 (and always for the decode): the batch-aware default interval
+        lo.delta = (op == SEMICRF_OP_VITERBI || delta == 0) ? default_delta(B, T, K)
+                                                            : resolve_delta(T, K, delta);
         if (lo.delta < 1) return false;
         lo.nspans = (T + lo.delta - 1) / lo.delta;
         lo.ndir = op == SEMICRF_OP_BACKWARD ? 2 : 1;
@@ -295,7 +298,7 @@ int semicrf_checkpoint_interval(int T, int K, int delta) { return resolve_delta(
 
 int semicrf_viterbi_interval(int B, int T, int K) {
     if (!shape_ok(B, T, 1, K)) return 0;
-    return viterbi_delta(B, T, K);
+    return default_delta(B, T, K);
 }
 
 int semicrf_prefix(const float* em, const int32_t* lengths, int B, int T, int C,

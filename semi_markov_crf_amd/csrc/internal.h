@@ -105,12 +105,19 @@ constexpr int ROUND = 4;
 // (two when linear), bulk sums [2][CP][2][ROUND], staged ring entries [2][CP+1][2][ROUND],
 // rebase shifts and dmax [CP rounded to 4], a sink and two constant blocks [16], staged
 // message sums [2][CP][ROUND] and replay flags [4] (fp32), staged bases [2][CP] (fp64).
-inline size_t lse_round_lds_bytes(int C, int CP, int P, int CH, bool lin, bool proj) {
+__host__ __device__ inline size_t lse_round_lds_bytes(int C, int CP, int P, int CH, bool lin,
+                                                      bool proj) {
     const int cp4 = (CP + 3) / 4 * 4;
     return (size_t)(2 * CH * C + (C + 1) / 2 * 2) * 8 +
            (size_t)((proj ? 10 : 6) * C * CH + (lin ? 2 : 1) * (C + 1) * P + 4 * CP * ROUND +
                     4 * (CP + 1) * ROUND + 2 * cp4 + 16 + 2 * CP * ROUND + 4) * 4 +
            (size_t)2 * CP * 8;
+}
+// One direction's LDS region of the round kernel (16-byte aligned, so that the region of
+// the second direction, when both share a workgroup, keeps every alignment).
+__host__ __device__ inline size_t lse_round_region_bytes(int C, int CP, int P, int CH, bool lin,
+                                                         bool proj) {
+    return (lse_round_lds_bytes(C, CP, P, CH, lin, proj) + 15) / 16 * 16;
 }
 // Dynamic LDS of the max-plus round kernel (C <= 16): S chunks [2][C][CH] (fp64),
 // with projections the chunks' end-side and start-side projections [2][2][C][CH], the

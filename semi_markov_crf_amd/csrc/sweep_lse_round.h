@@ -95,17 +95,22 @@ __device__ __forceinline__ float at4(const float4& v, int d) {
 // G: bulk lanes per label (C <= 256/G); BPL: ring blocks per bulk lane; CP: labels the
 // chain broadcasts (>= C); LIN: linear ring and sums (else log-space bulk sums only);
 // PROJ: boundary projections present (else the end and start sides coincide); XA: write
-// the per-position outputs X / A (the span recompute; the checkpoint sweep writes none).
-// Block: 64 + ceil(C*G/64)*64 threads.
-template <int G, int BPL, int CP, bool LIN, bool PROJ, bool XA>
-__global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int RS, const int P,
-                                                  const int CH,
-                                                  const float* __restrict__ proj_start,
-                                                  const float* __restrict__ proj_end) {
+// the per-position outputs X; ND: directions per workgroup.  With ND = 2 (MODE_SPEC of both
+// directions) the forward and the backward sweep of the same span share a workgroup: their
+// positions, rounds and chunks coincide, so every branch stays wave-uniform; chain lane
+// 16 d + c holds label c of direction d (one DPP row per direction), the bulk wavefronts
+// of direction d follow those of direction d - 1, and each direction has its own LDS
+// region.  Block: 64 + ND * ceil(C*G/64)*64 threads.
+template <int G, int BPL, int CP, bool LIN, bool PROJ, bool XA, int ND>
+__global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int RS,
+                                                                   const int P, const int CH,
+                                                                   const float* __restrict__ proj_start,
+                                                                   const float* __restrict__ proj_end) {
     constexpr int M = ROUND;
     static_assert(M == 4, "ring blocks are float4");
     static_assert(CP <= 16, "the labels of the chain wavefront share one DPP row");
     static_assert(CP * G <= 512, "at most 7 bulk wavefronts beside the chain");
+    static_assert(ND == 1 || ND == 2, "one or both directions");   // <= 512 threads either way
     constexpr int BP = BPL > 0 ? BPL : 1;
     constexpr int KD = 2 * M - 1;                              // chain durations, last step
     constexpr int CP4 = (CP + 3) / 4 * 4;
@@ -114,23 +119,30 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     const int tid = threadIdx.x, NT = blockDim.x;
     // the role is a property of the wavefront: a wave-uniform value, scalar branches
     const bool chain = __builtin_amdgcn_readfirstlane(tid >> 6) == 0;
-    const int bt = tid - 64;
+    const int NTV = (NT - 64) / ND;                // bulk threads of a direction (waves)
+    const int bdir = chain ? 0 : (tid - 64) / NTV;   // wave-uniform
+    const int bt = chain ? 0 : tid - 64 - bdir * NTV;
     const int cb = chain ? C : bt / G;
     const int j = chain ? 0 : bt - cb * G;
     const bool bact = !chain && cb < C;
     const int cr = bact ? cb : C;                 // inactive lanes use the spare ring row C
-    const bool cact = chain && tid < C;
-    const int cl = cact ? tid : 0;
-    // CP < 16: chain lane 15 is no label; with unit transition weights from every label
-    // its transition sum is the message total q of the step
+    const int crow = chain ? (tid >> 4) : 0;      // chain lanes: DPP row = direction
+    const bool crow_ok = chain && crow < ND;
+    const bool cact = crow_ok && (tid & 15) < C;
+    const int cl = cact ? (tid & 15) : 0;
+    // the lane that writes a direction's scalars (checkpoint reference, replay flag, log Z)
+    const bool clead = crow_ok && (tid & 15) == 0;
+    // CP < 16: chain lane 15 of a row is no label; with unit transition weights from every
+    // label its transition sum is the message total q of the step
     constexpr bool QLANE = CP < 16;
-    const bool qlane = QLANE && chain && tid == 15;
+    const bool qlane = QLANE && crow_ok && (tid & 15) == 15;
 
     // MODE_SPEC: grid (nspans, B, ndir); MODE_REPAIR: grid (B, ndir)
     const bool spec = a.mode == MODE_SPEC;
     int b, span, dir;
     if (spec) {
-        span = blockIdx.x; b = blockIdx.y; dir = blockIdx.z;
+        span = blockIdx.x; b = blockIdx.y;
+        dir = ND == 1 ? (int)blockIdx.z : (chain ? min(crow, ND - 1) : bdir);
     } else {
         b = blockIdx.x; dir = blockIdx.y; span = 0;
     }
@@ -163,7 +175,11 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     const int bmax = (K + M - 1) / M;             // oldest block a bulk sum reaches
     const int NR = bmax + 3;                      // live blocks behind a round (rescale)
 
-    double* Sbuf = lds;                                    // [2][C][CH] label-major
+    // this lane's direction's LDS region (ND = 2: two regions of equal layout; ND = 1: the
+    // only one, whichever direction the workgroup sweeps)
+    const size_t region = lse_round_region_bytes(C, CP, P, CH, LIN, PROJ);
+    const int rdir = ND == 1 ? 0 : dir;
+    double* Sbuf = reinterpret_cast<double*>(reinterpret_cast<char*>(lds) + rdir * region);   // [2][C][CH] label-major
     double* SL = Sbuf + 2 * C * CH;                        // [C] (padded to 16 bytes)
     // per position p of a staged chunk, relative to S(p0), p0 the first position of its
     // round: ge = S(p) + pe(p) - S(p0) and gs = S(p) - ps(p) - S(p0), with pe / ps the
@@ -187,9 +203,15 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     double* bcsh = (double*)(rpsh + 4);                    // [2 rounds][CP]
     float* Rrow = R + cr * P;
     float* Erow = E + cr * P;
+    // a pointer of this lane's region moved to region d (initialisation covers both)
+    auto in_region = [&](auto* ptr, int d) {
+        return reinterpret_cast<decltype(ptr)>(reinterpret_cast<char*>(ptr) +
+                                               (ptrdiff_t)(d - rdir) * (ptrdiff_t)region);
+    };
 
     const double* Sb = a.S + (size_t)b * (T + 1) * C;
-    for (int q = tid; q < C; q += NT) SL[q] = Sb[(size_t)L * C + q];
+    for (int d = 0; d < ND; ++d)
+        for (int q = tid; q < C; q += NT) in_region(SL, d)[q] = Sb[(size_t)L * C + q];
     // projections of sweep position p, base 2: end side (segments ending at p) and start
     // side (segments starting at p); 0 without projections or outside [1, L] / [0, L-1]
     const float* PSb = proj_start ? proj_start + (size_t)b * T * C : nullptr;
@@ -210,14 +232,16 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     };
     auto base2 = [](float raw) -> float { return (float)((double)raw * LOG2E); };
     auto proj_s = [&](int p, int q) -> float { return base2(proj_s_raw(p, q)); };
-    for (int q = tid; q < (C + 1) * P; q += NT) {
-        R[q] = NEG;
-        if constexpr (LIN) E[q] = 0.0f;
-    }
-    for (int q = tid; q < 2 * CP * 2 * M; q += NT) qsh[q] = ((q / M) & 1) ? NEG : 0.0f;
-    if (tid < M) {
-        zblk[tid] = 0.0f;
-        nblk[tid] = NEG;
+    for (int d = 0; d < ND; ++d) {
+        for (int q = tid; q < (C + 1) * P; q += NT) {
+            in_region(R, d)[q] = NEG;
+            if constexpr (LIN) in_region(E, d)[q] = 0.0f;
+        }
+        for (int q = tid; q < 2 * CP * 2 * M; q += NT) in_region(qsh, d)[q] = ((q / M) & 1) ? NEG : 0.0f;
+        if (tid < M) {
+            in_region(zblk, d)[tid] = 0.0f;
+            in_region(nblk, d)[tid] = NEG;
+        }
     }
 
     // ---------------------------------------------------------------- constants, base 2
@@ -742,7 +766,8 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
             }
             // label lanes only (lanes outside row 0 broadcast their own, empty row); a
             // round past the sweep end may replay for nothing
-            const uint64_t lanes = ((1ull << C) - 1) | (QLANE ? (1ull << 15) : 0ull);
+            const uint64_t row_lanes = ((1ull << C) - 1) | (QLANE ? (1ull << 15) : 0ull);
+            const uint64_t lanes = ND == 1 ? row_lanes : row_lanes | (row_lanes << 16);
             bool replayed = false;
             if (__builtin_amdgcn_ballot_w64(any_out_of_lin_range<3 * M>(chk)) & lanes) {
                 // ---- exact replay of the round in log space
@@ -765,9 +790,7 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
                     sig[m] = sigma;
                     const float u = cact ? hbe[m] + sigma : NEG;
                     float uv[CP];
-#pragma unroll
-                    for (int i = 0; i < CP; ++i)
-                        uv[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), i));
+                    row_bcast_all<CP>(u, uv);
                     const float rn = group_lse<1, CP>(uv, treg) - hbs[m];
                     const float lq = group_lse<1, CP>(uv, zero);
                     Rl[M + m] = rn;
@@ -819,7 +842,7 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
                     st4(sgsh + ((r & 1) * CP + cl) * M, make_float4(sig[0], sig[1], sig[2], sig[3]));
                     bcsh[(r & 1) * CP + cl] = Bc;
                 }
-                if (tid == 0) rpsh[r & 1] = replayed ? 1 : 0;
+                if (clead) rpsh[r & 1] = replayed ? 1 : 0;
             } else if (a.write_xa) {
                 // never taken (the launch picks XA when writing outputs); kept because the
                 // register allocation of this instance is the faster one with it
@@ -850,7 +873,7 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
                                 a.ck_base[ck * C + cl] = Bc;
                                 a.ck_mprev[ck * C + cl] = mr;
                             }
-                            if (tid == 0) a.ck_href[ck] = H0;
+                            if (clead) a.ck_href[ck] = H0;
                         }
                         next_ck += a.delta;
                     }
@@ -908,7 +931,7 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
     }
 
     // ---------------------------------------------------------------- end of sequence
-    if (t1 == L && tid == 0) {
+    if (t1 == L && clead) {
         if (spec) {
             a.lzloc[dir * a.B + b] = lz * LN2;           // the seam check adds the offsets
         } else {
@@ -920,31 +943,35 @@ __global__ __launch_bounds__(512) void k_lse_round(const SweepArgs a, const int 
 }
 
 // ------------------------------------------------------------------ launch
-template <int G, int BPL, int CP, bool LIN, bool PROJ, bool XA>
+template <int G, int BPL, int CP, bool LIN, bool PROJ, bool XA, int ND>
 static hipError_t launch_lse_round_inst(const SweepLaunch& a, dim3 grid, const SweepCfg& cfg,
                                         hipStream_t stream) {
-    if (cfg.NT > 512 || cfg.NT < 64 + cfg.G * a.C || cfg.lse.CH > lse_chunk_max(G) ||
-        cfg.lse.CH % ROUND != 0 || cfg.lse.CH < 2 * ROUND ||
+    const int nt = 64 + ND * cfg.NTv;
+    if (cfg.NT > 512 || cfg.NT != 64 + cfg.NTv || cfg.NTv % 64 != 0 || cfg.NT < 64 + cfg.G * a.C ||
+        cfg.lse.CH > lse_chunk_max(G) || cfg.lse.CH % ROUND != 0 || cfg.lse.CH < 2 * ROUND ||
         cfg.lse.P % 4 != 0 || cfg.RS % ROUND != 0)
         return hipErrorInvalidValue;
-    const size_t bytes = lse_round_lds_bytes(a.C, CP, cfg.lse.P, cfg.lse.CH, LIN, PROJ);
-    hipLaunchKernelGGL((k_lse_round<G, BPL, CP, LIN, PROJ, XA>), grid, dim3(cfg.NT), bytes, stream,
+    const size_t bytes = ND * lse_round_region_bytes(a.C, CP, cfg.lse.P, cfg.lse.CH, LIN, PROJ);
+    hipLaunchKernelGGL((k_lse_round<G, BPL, CP, LIN, PROJ, XA, ND>), grid, dim3(nt), bytes, stream,
                        static_cast<const SweepArgs&>(a), cfg.RS, cfg.lse.P, cfg.lse.CH,
                        a.proj_start, a.proj_end);
     return hipGetLastError();
 }
 
+#define LSE_ROUND_BPL_ND(G, CP, B_)                                                            \
+    return nd == 2 ? launch_lse_round_inst<G, B_, CP, LIN, PROJ, true, 2>(a, grid, cfg, stream) \
+                   : launch_lse_round_inst<G, B_, CP, LIN, PROJ, true, 1>(a, grid, cfg, stream);
 #define LSE_ROUND_BPL_CASES(G, CP)                                                   \
     switch (cfg.BPL) {                                                               \
-        case 0: return launch_lse_round_inst<G, 0, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
-        case 1: return launch_lse_round_inst<G, 1, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
-        case 2: return launch_lse_round_inst<G, 2, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
-        case 3: return launch_lse_round_inst<G, 3, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
-        case 4: return launch_lse_round_inst<G, 4, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
-        case 5: return launch_lse_round_inst<G, 5, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
-        case 6: return launch_lse_round_inst<G, 6, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
-        case 7: return launch_lse_round_inst<G, 7, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
-        case 8: return launch_lse_round_inst<G, 8, CP, LIN, PROJ, true>(a, grid, cfg, stream); \
+        case 0: LSE_ROUND_BPL_ND(G, CP, 0)                                           \
+        case 1: LSE_ROUND_BPL_ND(G, CP, 1)                                           \
+        case 2: LSE_ROUND_BPL_ND(G, CP, 2)                                           \
+        case 3: LSE_ROUND_BPL_ND(G, CP, 3)                                           \
+        case 4: LSE_ROUND_BPL_ND(G, CP, 4)                                           \
+        case 5: LSE_ROUND_BPL_ND(G, CP, 5)                                           \
+        case 6: LSE_ROUND_BPL_ND(G, CP, 6)                                           \
+        case 7: LSE_ROUND_BPL_ND(G, CP, 7)                                           \
+        case 8: LSE_ROUND_BPL_ND(G, CP, 8)                                           \
         default: return hipErrorInvalidValue;                                        \
     }
 
@@ -954,7 +981,13 @@ template <bool LIN, bool PROJ>
 hipError_t launch_lse_round_layout(const SweepCfg& cfg, const SweepLaunch& a, int ndir,
                                    hipStream_t stream) {
     if (a.mode != MODE_SPEC && a.mode != MODE_REPAIR) return hipErrorInvalidValue;
-    const dim3 grid = a.mode == MODE_REPAIR ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir);
+    // both directions of a span in one workgroup where they fit (MODE_SPEC only: a repair
+    // of each direction starts at its own failed seam)
+    const bool fits = 64 + 2 * cfg.NTv <= 512 &&
+                      2 * lse_round_region_bytes(a.C, cfg.CPr, cfg.lse.P, cfg.lse.CH, LIN, PROJ) <=
+                          150 * 1024;
+    const int nd = (a.mode == MODE_SPEC && ndir == 2 && fits) ? 2 : 1;
+    const dim3 grid = a.mode == MODE_REPAIR ? dim3(a.B, ndir) : dim3(a.nspans, a.B, ndir / nd);
     if (cfg.G == 64 && cfg.CPr == 4) { LSE_ROUND_BPL_CASES(64, 4) }
     if (cfg.G == 64 && cfg.CPr == 6) { LSE_ROUND_BPL_CASES(64, 6) }
     if (cfg.G == 64 && cfg.CPr == 8) { LSE_ROUND_BPL_CASES(64, 8) }
@@ -966,5 +999,6 @@ hipError_t launch_lse_round_layout(const SweepCfg& cfg, const SweepLaunch& a, in
 }
 
 #undef LSE_ROUND_BPL_CASES
+#undef LSE_ROUND_BPL_ND
 
 }  // namespace semicrf
