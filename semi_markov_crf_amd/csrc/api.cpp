@@ -22,7 +22,7 @@ struct Layout {
     int nts = 0, ntm = 0, tm = 0, tpg = 0, ngm = 0, delta = 0, nspans = 0, ndir = 0;
     size_t status = 0, Leff = 0, tsum = 0, toff = 0, ttot = 0, S = 0;
     size_t logz = 0, logzb = 0;
-    size_t head = 0, tail = 0, lzloc = 0, soff = 0, fbad = 0, diag = 0;
+    size_t head = 0, tail = 0, lzloc = 0, soff = 0, fbad = 0, diag = 0, sstat = 0;
     size_t ckR = 0, ckB = 0, ckM = 0, ckH = 0, XF = 0, XB = 0;
     size_t dnt = 0, dno = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0, rps = 0;
     size_t gcnt = 0, gpart = 0;
@@ -109,6 +109,7 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         lo.soff = m.take(sizeof(double) * nck);
         lo.fbad = m.take(sizeof(int) * lo.ndir * B);
         lo.diag = m.take(sizeof(double) * lo.ndir * B * 4);
+        lo.sstat = m.take(sizeof(double) * nck * 3);
         if (cfg.xk) {
             // one ring slice per workgroup of the span sweeps (a repair reuses its span's)
             const bool vit = op == SEMICRF_OP_VITERBI;
@@ -271,6 +272,7 @@ int run_spans(const SweepCfg& cfg, SweepLaunch a, int ndir, const Layout& lo, vo
     sa.logz = a.logz;
     sa.logz_b = a.logz_b;
     sa.diag = at<double>(ws, lo.diag);
+    sa.stats = at<double>(ws, lo.sstat);
     LAUNCH(launch_seam(sa, ndir, stream));
     a.mode = MODE_REPAIR;
     LAUNCH(launch_lse(cfg, a, ndir, stream));
@@ -466,6 +468,7 @@ static int run_viterbi(const float* em, const int32_t* lengths, const float* tra
     sa.logz = a.logz;
     sa.logz_b = a.logz_b;
     sa.diag = at<double>(workspace, lo.diag);
+    sa.stats = at<double>(workspace, lo.sstat);
     LAUNCH(launch_seam(sa, 1, stream));
     a.mode = MODE_REPAIR;
     LAUNCH(launch_maxplus(cfg, a, stream));

@@ -224,6 +224,7 @@ struct SeamArgs {
     double* logz_b;         // [B] direction 1 (out, where no seam failed)
     double* diag;           // [ndir][B][4]: sum and max of the accepted half-ranges, first
                             //   failed seam (-1: none), number of seams (out)
+    double* stats;          // [ndir][B][nspans][3] scratch: max d, min d, finiteness mismatch
 };
 hipError_t launch_seam(const SeamArgs& s, int ndir, hipStream_t stream);
 // bound [B] / repairs [B] (either may be NULL) from the seam check's diag

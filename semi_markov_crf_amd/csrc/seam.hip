@@ -22,61 +22,91 @@
 // The first seam that fails stops the chain: the spans from there on are swept again in
 // order (MODE_REPAIR) from the checkpoint span j-1 left at its end, in span j-1's frame.
 //
-// Per (sequence, direction) the kernel also records the sum and maximum of the accepted
-// half-ranges (a bound on the error the speculation adds, in natural-log units) and the
-// first failed seam.
+// k_seam_stats reduces every seam's window at once; k_seam then walks the seams of each
+// sequence and direction in order.  Per (sequence, direction) it also records the sum and
+// maximum of the accepted half-ranges (a bound on the error the speculation adds, in
+// natural-log units) and the first failed seam.
 #include "common.h"
 #include "internal.h"
 
 namespace semicrf {
 
-__global__ __launch_bounds__(256) void k_seam(const SeamArgs s) {
-    __shared__ double smax[256], smin[256];
-    __shared__ int smis[256];
+// grid (nspans - 1, B, ndir), block 256: the statistics of seam j = blockIdx.x + 1 of one
+// sequence and direction: max and min of d = tail - head over the finite entries (both
+// finite), and whether the two sides disagree on finiteness anywhere.  Fixed reduction
+// order (lanes, then the four wavefronts in order): bitwise reproducible.
+__global__ __launch_bounds__(256) void k_seam_stats(const SeamArgs s) {
+    __shared__ double wmax[4], wmin[4];
+    __shared__ int wmis[4];
+    const int j = blockIdx.x + 1, b = blockIdx.y, dir = blockIdx.z, tid = threadIdx.x;
+    const int L = abs(s.Leff[b]);
+    const int n = (L + s.delta - 1) / s.delta;                    // spans that hold positions
+    if (j >= n) return;
+    const size_t row = (size_t)dir * s.B + b;
+    const int KC = s.K * s.C;
+    const double* tl = s.tail + (row * s.nspans + j - 1) * KC;
+    const double* hd = s.head + (row * s.nspans + j) * KC;
+    double lmax = -1.0e300, lmin = 1.0e300;
+    int mis = 0;
+    for (int q = tid; q < KC; q += 256) {
+        const double tv = tl[q], hv = hd[q];
+        const bool vt = tv > -1.0e29, vh = hv > -1.0e29;
+        if (vt != vh) {
+            mis = 1;
+        } else if (vt) {
+            const double d = tv - hv;
+            lmax = fmax(lmax, d);
+            lmin = fmin(lmin, d);
+        }
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+        lmax = fmax(lmax, __shfl_xor(lmax, o, 64));
+        lmin = fmin(lmin, __shfl_xor(lmin, o, 64));
+        mis |= __shfl_xor(mis, o, 64);
+    }
+    if ((tid & 63) == 0) {
+        wmax[tid >> 6] = lmax;
+        wmin[tid >> 6] = lmin;
+        wmis[tid >> 6] = mis;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double gmax = wmax[0], gmin = wmin[0];
+        int gm = wmis[0];
+        for (int w = 1; w < 4; ++w) {
+            gmax = fmax(gmax, wmax[w]);
+            gmin = fmin(gmin, wmin[w]);
+            gm |= wmis[w];
+        }
+        double* st = s.stats + (row * s.nspans + j) * 3;
+        st[0] = gmax;
+        st[1] = gmin;
+        st[2] = (double)gm;
+    }
+}
+
+// grid (B, ndir), one wavefront: the seams of one sequence and direction in order.  If
+// every finite entry of one side agrees with the other's finiteness and max d - min d <= 2 tol,
+// the spans' states are the same up to c_j = (max d + min d) / 2; the frame offsets chain
+// the c_j; the first seam that fails stops the chain.
+__global__ __launch_bounds__(64) void k_seam(const SeamArgs s) {
     const int b = blockIdx.x, dir = blockIdx.y, tid = threadIdx.x;
+    if (tid != 0) return;
     const int Lr = s.Leff[b];
     const bool bad = Lr < 0;
     const int L = bad ? -Lr : Lr;
     const int n = (L + s.delta - 1) / s.delta;                    // spans that hold positions
     const size_t row = (size_t)dir * s.B + b;
-    const int KC = s.K * s.C;
     double* off = s.off + row * s.nspans;
     double cur = 0.0, sum = 0.0, mx = 0.0;
     int fb = s.nspans;
-    if (tid == 0) off[0] = 0.0;
+    off[0] = 0.0;
     for (int j = 1; j < n; ++j) {
-        const double* tl = s.tail + (row * s.nspans + j - 1) * KC;
-        const double* hd = s.head + (row * s.nspans + j) * KC;
-        double lmax = -1.0e300, lmin = 1.0e300;
-        int mis = 0;
-        for (int q = tid; q < KC; q += 256) {
-            const double tv = tl[q], hv = hd[q];
-            const bool vt = tv > -1.0e29, vh = hv > -1.0e29;
-            if (vt != vh) {
-                mis = 1;
-            } else if (vt) {
-                const double d = tv - hv;
-                lmax = fmax(lmax, d);
-                lmin = fmin(lmin, d);
-            }
-        }
-        smax[tid] = lmax;
-        smin[tid] = lmin;
-        smis[tid] = mis;
-        __syncthreads();
-        for (int w = 128; w >= 1; w >>= 1) {
-            if (tid < w) {
-                smax[tid] = fmax(smax[tid], smax[tid + w]);
-                smin[tid] = fmin(smin[tid], smin[tid + w]);
-                smis[tid] |= smis[tid + w];
-            }
-            __syncthreads();
-        }
-        const double gmax = smax[0], gmin = smin[0];
+        const double* st = s.stats + (row * s.nspans + j) * 3;
+        const double gmax = st[0], gmin = st[1];
         const bool any = gmax >= gmin;                             // some finite entry
         const double tau = any ? 0.5 * (gmax - gmin) : 0.0;
-        const bool ok = !smis[0] && tau <= s.tol;
-        __syncthreads();                                           // smax / smin reused
+        const bool ok = st[2] == 0.0 && tau <= s.tol;
         if (!ok) {
             fb = j;
             break;
@@ -84,27 +114,26 @@ __global__ __launch_bounds__(256) void k_seam(const SeamArgs s) {
         cur += any ? 0.5 * (gmax + gmin) : 0.0;
         sum += tau;
         mx = fmax(mx, tau);
-        if (tid == 0) off[j] = cur;
+        off[j] = cur;
     }
-    if (tid == 0) {
-        // a repaired sweep continues in the frame of span fb-1
-        for (int j = fb; j < n; ++j) off[j] = cur;
-        s.first_bad[row] = fb;
-        if (fb >= s.nspans) {
-            const double lz = bad ? __longlong_as_double(0x7ff8000000000000LL)
-                                  : s.lzloc[row] + cur;
-            (dir == 0 ? s.logz : s.logz_b)[b] = lz;
-        }
-        double* dg = s.diag + row * 4;
-        dg[0] = sum;
-        dg[1] = mx;
-        dg[2] = fb < s.nspans ? (double)fb : -1.0;
-        dg[3] = (double)(n > 0 ? n - 1 : 0);
+    // a repaired sweep continues in the frame of span fb-1
+    for (int j = fb; j < n; ++j) off[j] = cur;
+    s.first_bad[row] = fb;
+    if (fb >= s.nspans) {
+        const double lz = bad ? __longlong_as_double(0x7ff8000000000000LL) : s.lzloc[row] + cur;
+        (dir == 0 ? s.logz : s.logz_b)[b] = lz;
     }
+    double* dg = s.diag + row * 4;
+    dg[0] = sum;
+    dg[1] = mx;
+    dg[2] = fb < s.nspans ? (double)fb : -1.0;
+    dg[3] = (double)(n > 0 ? n - 1 : 0);
 }
 
 hipError_t launch_seam(const SeamArgs& s, int ndir, hipStream_t stream) {
-    hipLaunchKernelGGL(k_seam, dim3(s.B, ndir), dim3(256), 0, stream, s);
+    if (s.nspans > 1)
+        hipLaunchKernelGGL(k_seam_stats, dim3(s.nspans - 1, s.B, ndir), dim3(256), 0, stream, s);
+    hipLaunchKernelGGL(k_seam, dim3(s.B, ndir), dim3(64), 0, stream, s);
     return hipGetLastError();
 }
 
