@@ -203,6 +203,28 @@ def config_timings(crf, d):
     return out
 
 
+def only_config(crf, d, name, reps):
+    """One other configuration alone: backward, Viterbi and log Z, each timed over reps
+    calls after one untimed call."""
+    import torch
+
+    import workloads
+    w = workloads.long_duration() if name == "long_duration" else \
+        workloads.make({"speech": 1, "long": 3, "large_c": 4}[name])
+    em, lengths, trans, dur = (torch.from_numpy(a).to(d) for a in (w.em, w.lengths, w.trans, w.dur))
+    ws = {op: torch.empty(crf.workspace_bytes(op, w.B, w.T, w.C, w.K), dtype=torch.uint8, device=d)
+          for op in (crf.OP_BACKWARD, crf.OP_VITERBI, crf.OP_LOGZ)}
+    mb = _time_ms(lambda: crf.backward(em, lengths, trans, dur, workspace=ws[crf.OP_BACKWARD]), d,
+                  reps)
+    mv = _time_ms(lambda: crf.viterbi(em, lengths, trans, dur, workspace=ws[crf.OP_VITERBI]), d,
+                  reps)
+    ml = _time_ms(lambda: crf.logz(em, lengths, trans, dur, workspace=ws[crf.OP_LOGZ]), d, reps)
+    pos = w.positions()
+    return {"config": name, "B": w.B, "T": w.T, "K": w.K, "C": w.C, "positions": pos,
+            "reps": reps, "backward_ms": mb, "viterbi_ms": mv, "logz_ms": ml,
+            "fwd_bwd_positions_per_s": pos / (mb * 1e-3)}
+
+
 def extras(crf, w, em, lengths, trans, dur, d):
     """Timings beyond the step: the training loss of gold segmentations, the backward
     pass with boundary projections, log Z alone (all at the genomic shape), and the
@@ -271,7 +293,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--delta", type=int, default=0, help="checkpoint interval (0: ceil(sqrt(TK)))")
+    ap.add_argument("--delta", type=int, default=0,
+                    help="checkpoint interval of the backward (0: the library default)")
     ap.add_argument("--cpu-sample", type=int, default=12_000,
                     help="positions of every sequence the oracle baseline runs over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -279,6 +302,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other configurations, the training loss, the projections "
                          "and the long-duration workload")
+    ap.add_argument("--only-config", choices=("speech", "long", "large_c", "long_duration"),
+                    help="time one other configuration alone (backward, Viterbi, log Z; for "
+                         "profiling it) and print its timings instead of the step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
@@ -293,6 +319,10 @@ def main():
     from semi_markov_crf_amd import _native
 
     lib = _native.load()
+    if args.only_config:
+        print(json.dumps(only_config(crf, torch.device("cuda:0"), args.only_config,
+                                     max(1, args.steps))), flush=True)
+        return
     hip = hip_runtime()
     w = workloads.make(CONFIG)
     d = torch.device("cuda:0")
@@ -301,7 +331,8 @@ def main():
     trans = torch.from_numpy(w.trans).to(d)
     dur = torch.from_numpy(w.dur).to(d)
     B, T, C, K = w.B, w.T, w.C, w.K
-    delta = crf.checkpoint_interval(T, K, args.delta) if args.delta else crf.viterbi_interval(B, T, K)
+    delta = crf.checkpoint_interval(T, K, args.delta) if args.delta else crf.default_interval(B, T, K)
+    vdelta = crf.viterbi_interval(B, T, K)
     nb = crf.workspace_bytes(crf.OP_BACKWARD, B, T, C, K, args.delta)
     nv = crf.workspace_bytes(crf.OP_VITERBI, B, T, C, K)
     ws_b = torch.empty(nb, dtype=torch.uint8, device=d)
@@ -414,9 +445,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"genomic semi-CRF B={B} T={T} K={K} C={C}, delta={delta} "
-                               f"({nspans} checkpoint spans); step = semicrf_backward + "
-                               f"semicrf_viterbi",
-                   "B": B, "T": T, "K": K, "C": C, "delta": delta, "parallelism": "none (1 GPU)"},
+                               f"({nspans} checkpoint spans; decode {vdelta}); step = "
+                               f"semicrf_backward + semicrf_viterbi",
+                   "B": B, "T": T, "K": K, "C": C, "delta": delta, "viterbi_delta": vdelta,
+                   "parallelism": "none (1 GPU)"},
         "roofline": {
             "bound": "alu",
             "kernel": "k_lse_round, span mode: every checkpoint span of both directions of "

@@ -80,12 +80,17 @@ const char* semicrf_status_string(int status);
  * about sqrt(TK)); clamped to [1, T].  0 on bad input. */
 int semicrf_checkpoint_interval(int T, int K, int delta);
 
-/* The default checkpoint interval for a batch of B sequences of padded length T: the one
- * semicrf_viterbi uses (it takes none) and the one semicrf_logz / semicrf_backward use for
- * delta = 0.  semicrf_checkpoint_interval(T, K, 0), halved when the batch holds at most
- * 128 spans of that length and each is at least four burn-ins (12 K) long, so that the
- * spans swept at once occupy more compute units.  0 on bad input. */
+/* The decode's checkpoint interval for a batch of B sequences of padded length T
+ * (semicrf_viterbi takes none): semicrf_checkpoint_interval(T, K, 0), halved when the
+ * batch holds at most 128 spans of that length and each is at least four burn-ins (12 K)
+ * long, so that the spans swept at once occupy more compute units.  0 on bad input. */
 int semicrf_viterbi_interval(int B, int T, int K);
+
+/* The checkpoint interval semicrf_logz and semicrf_backward use for delta = 0:
+ * semicrf_checkpoint_interval(T, K, 0) while the batch has at least 224 spans of that
+ * length (7/8 of the MI355X's 256 compute units), else shortened until it has about 224,
+ * but not below two burn-ins (6 K) nor above ceil(sqrt(T*K)).  0 on bad input. */
+int semicrf_default_interval(int B, int T, int K);
 
 /* Bytes of workspace that `op` needs for these shapes (delta as the call takes it: > 0 an
  * explicit interval, 0 the default above).  0 if the arguments are invalid or
@@ -107,7 +112,7 @@ int semicrf_prefix(const float* emissions, const int32_t* lengths, int B, int T,
 
 /* log Z for every sequence: the log-sum-exp of the scores of all segmentations
  * (EN explainer, "2. Methodology", "Streaming Forward-Backward with Ring Buffers",
- * forward pass).  delta: checkpoint interval (0 = semicrf_viterbi_interval(B, T, K)), the
+ * forward pass).  delta: checkpoint interval (0 = semicrf_default_interval(B, T, K)), the
  * same value as given to semicrf_workspace_bytes.  Output: log_z [B] float32. */
 int semicrf_logz(const float* emissions, const int32_t* lengths, const float* trans,
                  const float* dur, int B, int T, int C, int K, int delta, hipStream_t stream,
@@ -124,7 +129,7 @@ int semicrf_logz(const float* emissions, const int32_t* lengths, const float* tr
  *   marginals      [B, T, C] float32  or NULL: posterior probability that position t
  *                                     lies in a segment of label c (sums to 1 over c)
  *   log_z          [B]       float32  or NULL
- * delta: checkpoint interval (0 = semicrf_viterbi_interval(B, T, K)); results do not
+ * delta: checkpoint interval (0 = semicrf_default_interval(B, T, K)); results do not
  * depend on it beyond rounding. */
 int semicrf_backward(const float* emissions, const int32_t* lengths, const float* trans,
                      const float* dur, int B, int T, int C, int K, int delta,

@@ -55,18 +55,36 @@ int resolve_delta(int T, int K, int delta) {
     return (int)d;
 }
 
-// The default checkpoint interval (delta = 0, and always for the decode, which takes
-// none).  It starts from ceil(sqrt(T*K)) and halves it when the batch's spans (one
-// workgroup each, both directions of a span in one for the backward) would leave most
-// compute units idle and a span stays long next to its burn-in: at B = 4, T = 10^5, K = 200
-// the decode drops from 1.78 to 1.18 ms; with 32 speech-length sequences the halving costs
-// more burn-in than it gains (0.53 -> 0.61 ms), so it is not taken there.
+// The decode's checkpoint interval (it takes none).  It starts from ceil(sqrt(T*K)) and
+// halves it when the batch's spans (one workgroup each) would leave most compute units
+// idle and a span stays long next to its burn-in: at B = 4, T = 10^5, K = 200 the decode
+// drops from 1.78 to 1.18 ms; with 32 speech-length sequences the halving costs more
+// burn-in than it gains (0.53 -> 0.61 ms), so it is not taken there.
 int default_delta(int B, int T, int K) {
     const int d = resolve_delta(T, K, 0);
     if (d < 1) return 0;
     const long long spans = (long long)B * ((T + d - 1) / d);
     if (spans <= 128 && d >= 4 * spec_warm(K)) return (d + 1) / 2;
     return d;
+}
+
+// The default interval of log Z and the backward (delta = 0).  A span's sweep takes time
+// in proportion to its length plus its burn-in while every span has a compute unit of its
+// own, and a second round of workgroups doubles it.  So when ceil(sqrt(T*K)) gives fewer
+// spans than 7/8 of the MI355X's 256 compute units hold (the rest is left to a concurrent
+// call, such as a decode on another stream), the interval shrinks until the batch's spans
+// reach that count, but not below two burn-ins.  At B = 4, T = 10^5, K = 200 (224 spans of
+// 1,786 instead of 180 of 2,237) a backward pass beside a decode drops from 1.96 to
+// 1.74 ms per pair of calls.
+int fill_delta(int B, int T, int K) {
+    constexpr long long TARGET = 256 * 7 / 8;
+    const int d0 = resolve_delta(T, K, 0);
+    if (d0 < 1) return 0;
+    if ((long long)B * ((T + d0 - 1) / d0) >= TARGET) return d0;
+    const long long per = std::max<long long>(1, TARGET / B);   // spans per sequence
+    long long d = (T + per - 1) / per;
+    d = std::max<long long>(d, 2LL * spec_warm(K));
+    return (int)std::min<long long>(d, d0);
 }
 
 bool shape_ok(int B, int T, int C, int K) {
@@ -91,8 +109,9 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         // checkpoint spans: checkpoints, seam windows and frame offsets per direction (the
         // decode runs forward only, with the default interval)
         // delta = 0 (and always for the decode): the batch-aware default interval
-        lo.delta = (op == SEMICRF_OP_VITERBI || delta == 0) ? default_delta(B, T, K)
-                                                            : resolve_delta(T, K, delta);
+        lo.delta = op == SEMICRF_OP_VITERBI ? default_delta(B, T, K)
+                   : delta == 0             ? fill_delta(B, T, K)
+                                            : resolve_delta(T, K, delta);
         if (lo.delta < 1) return false;
         lo.nspans = (T + lo.delta - 1) / lo.delta;
         lo.ndir = op == SEMICRF_OP_BACKWARD ? 2 : 1;
@@ -301,6 +320,11 @@ int semicrf_checkpoint_interval(int T, int K, int delta) { return resolve_delta(
 int semicrf_viterbi_interval(int B, int T, int K) {
     if (!shape_ok(B, T, 1, K)) return 0;
     return default_delta(B, T, K);
+}
+
+int semicrf_default_interval(int B, int T, int K) {
+    if (!shape_ok(B, T, 1, K)) return 0;
+    return fill_delta(B, T, K);
 }
 
 int semicrf_prefix(const float* em, const int32_t* lengths, int B, int T, int C,

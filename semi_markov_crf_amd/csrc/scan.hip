@@ -60,48 +60,49 @@ __global__ __launch_bounds__(256) void k_em_tile_sums(const float* __restrict__ 
     }
 }
 
-// grid (B), block 256.  Exclusive prefix (or suffix) over the n tiles, per column.
+// grid (C, B), block 256: one workgroup per (label, sequence).  Exclusive prefix (or
+// suffix) over the n tiles of one column: thread i sums the tiles at ordinal positions
+// [i*per, (i+1)*per) of the scan order (ascending tile index, or descending when reverse)
+// in order; a fixed-order scan of those 256 sums (Hillis-Steele within each wavefront,
+// then the four wavefront totals) gives each thread its offset, and it writes the
+// offsets of its tiles in order.  Every addition happens in the same order on every
+// call, so results are reproducible bit for bit.
 __global__ __launch_bounds__(256) void k_tile_scan(const double* __restrict__ tile_sums, int n,
-                                                   int C, int reverse,
-                                                   double* __restrict__ offsets,
-                                                   double* __restrict__ totals) {
-    __shared__ double part[257];
-    const int b = blockIdx.x, tid = threadIdx.x;
+                                                  int C, int reverse,
+                                                  double* __restrict__ offsets,
+                                                  double* __restrict__ totals) {
+    __shared__ double wsum[4];
+    const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
     const int per = (n + 255) / 256;
     const double* in = tile_sums + (size_t)b * n * C;
-    for (int c = 0; c < C; ++c) {
-        // thread tid owns the tiles at ordinal positions [tid*per, (tid+1)*per) of the
-        // scan order (ascending tile index, or descending when reverse)
-        double s = 0.0;
+    auto idx = [&](int o) { return (size_t)(reverse ? n - 1 - o : o) * C + c; };
+    double s = 0.0;
+    for (int i = 0; i < per; ++i) {
+        const int o = tid * per + i;
+        if (o < n) s += in[idx(o)];
+    }
+    double v = s;   // inclusive scan within the wavefront
+    for (int d = 1; d < 64; d <<= 1) {
+        const double u = __shfl_up(v, d, 64);
+        if (lane >= d) v += u;
+    }
+    if (lane == 63) wsum[w] = v;
+    double excl = __shfl_up(v, 1, 64);
+    if (lane == 0) excl = 0.0;
+    __syncthreads();
+    double base = 0.0;
+    for (int i = 0; i < w; ++i) base += wsum[i];
+    double run = base + excl;
+    if (offsets)
         for (int i = 0; i < per; ++i) {
             const int o = tid * per + i;
-            if (o < n) s += in[(size_t)(reverse ? n - 1 - o : o) * C + c];
-        }
-        part[tid] = s;
-        __syncthreads();
-        if (tid == 0) {
-            double run = 0.0;
-            for (int i = 0; i < 256; ++i) {
-                const double v = part[i];
-                part[i] = run;
-                run += v;
+            if (o < n) {
+                offsets[(size_t)b * n * C + idx(o)] = run;
+                run += in[idx(o)];
             }
-            part[256] = run;
         }
-        __syncthreads();
-        double run = part[tid];
-        if (offsets)
-            for (int i = 0; i < per; ++i) {
-                const int o = tid * per + i;
-                if (o < n) {
-                    const size_t idx = (size_t)(reverse ? n - 1 - o : o) * C + c;
-                    offsets[(size_t)b * n * C + idx] = run;
-                    run += in[idx];
-                }
-            }
-        if (totals && tid == 0) totals[(size_t)b * C + c] = part[256];
-        __syncthreads();
-    }
+    if (totals && tid == 255) totals[(size_t)b * C + c] = base + v;
 }
 
 // grid (ntiles, B), block 256, dynamic LDS = TS*C*4 + TS*C*8 + 256*8 bytes.
@@ -316,7 +317,8 @@ hipError_t launch_em_tile_sums(const float* em, const int32_t* lengths, int B, i
 
 hipError_t launch_tile_scan(const double* tile_sums, int B, int n, int C, bool reverse,
                             double* offsets, double* totals, hipStream_t stream) {
-    hipLaunchKernelGGL(k_tile_scan, dim3(B), dim3(256), 0, stream, tile_sums, n, C,
+    if (B < 1 || C < 1) return hipSuccess;
+    hipLaunchKernelGGL(k_tile_scan, dim3(C, B), dim3(256), 0, stream, tile_sums, n, C,
                        reverse ? 1 : 0, offsets, totals);
     return hipGetLastError();
 }

@@ -121,6 +121,19 @@ def test_checkpoint_interval(native):
     assert f(0, 5, 0) == 0 and f(10, 0, 0) == 0 and f(10, 5, -1) == 0
 
 
+def test_default_interval(native):
+    lib = native.load()
+    f = lib.semicrf_default_interval
+    assert f(4, 100_000, 200) == 1786          # 56 spans a sequence: 224 spans
+    assert f(1, 1_000_000, 200) == 4465        # 224 spans
+    assert f(8, 10_000, 64) == 384             # two burn-ins (384): 27 spans a sequence
+    assert f(32, 800, 30) == 155               # two burn-ins (180) exceed ceil(sqrt(TK))
+    assert f(64, 100_000, 200) == 4473         # 1472 spans: the batch fills the device
+    assert f(1, 1000, 200) == 448              # two burn-ins exceed ceil(sqrt(TK))
+    assert f(4, 100_000, 1) == 317             # 1264 spans of ceil(sqrt(TK))
+    assert f(0, 100, 5) == 0 and f(1, 0, 5) == 0 and f(1, 10, 0) == 0
+
+
 def test_viterbi_interval(native):
     lib = native.load()
     f = lib.semicrf_viterbi_interval
