@@ -243,8 +243,236 @@ __global__ __launch_bounds__(256) void k_trans_step(const TransStepArgs a) {
     }
 }
 
+// Label counts above 16: the two sums over labels of k_trans_step are small dense
+// products per tile, [C x TM] x [TM x C] for the transition posteriors and
+// [TM x C] x [C x C] per direction for the transition step, so they run register-blocked
+// (4 x 4 outputs a thread, float4 operands from LDS, labels padded to C4 = ceil(C/4)*4
+// with zeros) on the row exponentials E = 2^(X - row max):
+//   partial[c', c] = 2^tr2[c', c] * sum_r 2^(m1[r] + m2[r] - log2 Z) E1[r, c'] E2[r, c]
+// The row scale 2^(m1 + m2 - log2 Z) is at most about 2^(-min tr2) in exact arithmetic (a
+// transition posterior is at most 1); a tile in which it, or 2^(max tr2), would leave the
+// fp32 range (above 2^60) sums the exact per-term exponentials instead.  The transition
+// step and its log-space replay are those of k_trans_step.
+__host__ __device__ static inline int c4_of(int C) { return (C + 3) / 4 * 4; }
+static size_t step_lds_wide(int C, int TM) {
+    const int C4 = c4_of(C);
+    return (size_t)8 * (2 * TM * C + 2 * TM) + (size_t)4 * TM + (size_t)8 * TM * C4 +
+           (size_t)4 * C4 * C4 + 32;
+}
+
+__global__ __launch_bounds__(256) void k_trans_step_wide(const TransStepArgs a) {
+    extern __shared__ double lds[];
+    const int C = a.C, T = a.T, TM = a.tile, C4 = c4_of(C);
+    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int L = abs(a.Leff[b]);
+    const size_t rowC = (size_t)(T + 1) * C;
+    double* X1 = lds;                                // [TM][C] forward messages (base 2)
+    double* X2 = X1 + (size_t)TM * C;                // [TM][C] backward messages
+    double* m1 = X2 + (size_t)TM * C;                // [TM] row maxima
+    double* m2 = m1 + TM;
+    float* sc = (float*)(m2 + TM);                   // [TM] 2^(m1 + m2 - log2 Z)
+    float* E1 = sc + TM;                             // [TM][C4] 2^(X1 - m1), pad 0
+    float* E2 = E1 + (size_t)TM * C4;                // [TM][C4]
+    float* trw = E2 + (size_t)TM * C4;               // [C4][C4] 2^(tr2 - tmax), pad 0
+    float* red = trw + (size_t)C4 * C4;              // [4] wavefront maxima
+    int& exact_flag = *reinterpret_cast<int*>(red + 4);   // exact partials for this tile
+
+    auto tr2_at = [&](int q) { return fmaxf((float)((double)a.trans[q] * LOG2E), NEG); };
+    // tmax: block maximum of tr2
+    float tm_loc = NEG;
+    for (int q = tid; q < C * C; q += 256) tm_loc = fmaxf(tm_loc, tr2_at(q));
+    for (int off = 32; off >= 1; off >>= 1) tm_loc = fmaxf(tm_loc, __shfl_xor(tm_loc, off, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = tm_loc;
+    __syncthreads();
+    const float tmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    for (int q = tid; q < C4 * C4; q += 256) {
+        const int i = q / C4, j = q - i * C4;
+        trw[q] = (i < C && j < C) ? fast_exp2(tr2_at(i * C + j) - tmax) : 0.0f;
+    }
+
+    double* XF = a.XF + (size_t)b * rowC;
+    double* XB = a.XB + (size_t)b * rowC;
+    const double* Sb = a.S + (size_t)b * rowC;
+    const float* Ps = a.proj_start ? a.proj_start + (size_t)b * T * C : nullptr;
+    const float* Pe = a.proj_end ? a.proj_end + (size_t)b * T * C : nullptr;
+    const double logZ = a.logz[b];
+    const double lz2 = logZ * LOG2E;
+    const double* offF = a.off ? a.off + (size_t)b * a.nspans : nullptr;
+    const double* offB = a.off ? a.off + ((size_t)a.B + b) * a.nspans : nullptr;
+    auto oXF = [&](int s) { return offF ? offF[(s - 1) / a.delta] : 0.0; };
+    auto oXB = [&](int s) { return offB ? offB[(L - s - 1) / a.delta] : 0.0; };
+    double* part_trans = a.part_trans + ((size_t)b * a.ngroups + g) * C * C;
+    const int NB4 = C4 / 4;
+
+    const int tile_end = min(a.ntiles, (g + 1) * a.tpg);
+    for (int tile = g * a.tpg; tile < tile_end; ++tile) {
+        const int p0 = tile * TM;
+        const bool first = tile == g * a.tpg;
+        __syncthreads();   // the previous tile's LDS is read no more
+        if (tid == 0) exact_flag = tmax > 60.0f;
+        for (int q = tid; q < TM * C; q += 256) {
+            const int r = q / C, c = q - r * C;
+            const int s = p0 + r;
+            const bool in = s >= 1 && s <= L - 1;
+            X1[q] = in ? (XF[(size_t)s * C + c] + oXF(s)) * LOG2E : DNEG;
+            X2[q] = in ? (XB[(size_t)s * C + c] + oXB(s)) * LOG2E : DNEG;
+        }
+        __syncthreads();
+        for (int r = tid; r < 2 * TM; r += 256) {
+            const double* x = (r < TM ? X1 : X2) + (size_t)(r % TM) * C;
+            double m = DNEG;
+            for (int c = 0; c < C; ++c) m = fmax(m, x[c]);
+            (r < TM ? m1 : m2)[r % TM] = m;
+        }
+        __syncthreads();
+        for (int r = tid; r < TM; r += 256) {
+            const double e = m1[r] + m2[r] - lz2;
+            if (e > 60.0) exact_flag = 1;
+            sc[r] = fast_exp2((float)e);
+        }
+        for (int q = tid; q < 2 * TM * C4; q += 256) {
+            const bool fw = q < TM * C4;
+            const int qq = fw ? q : q - TM * C4;
+            const int r = qq / C4, c = qq - r * C4;
+            float e = 0.0f;
+            if (c < C) e = fast_exp2((float)((fw ? X1 : X2)[(size_t)r * C + c] - (fw ? m1 : m2)[r]));
+            (fw ? E1 : E2)[qq] = e;
+        }
+        __syncthreads();
+        // transition partials, 4 x 4 blocks of (c', c)
+        const bool exact = exact_flag;
+        for (int q = tid; q < NB4 * NB4; q += 256) {
+            const int i0 = (q / NB4) * 4, l0 = (q % NB4) * 4;
+            float acc[4][4] = {};
+            if (!exact) {
+                for (int r = 0; r < TM; ++r) {
+                    const float sr = sc[r];
+                    const float4 x = *reinterpret_cast<const float4*>(E1 + (size_t)r * C4 + i0);
+                    const float4 y = *reinterpret_cast<const float4*>(E2 + (size_t)r * C4 + l0);
+                    const float xa[4] = {x.x * sr, x.y * sr, x.z * sr, x.w * sr};
+                    const float ya[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int l = 0; l < 4; ++l) acc[i][l] = fmaf(xa[i], ya[l], acc[i][l]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int l = 0; l < 4; ++l) {
+                    const int cp = i0 + i, c = l0 + l;
+                    if (cp >= C || c >= C) continue;
+                    const float tv = tr2_at(cp * C + c);
+                    float v;
+                    if (!exact) {
+                        v = acc[i][l] * fast_exp2(tv);
+                    } else {
+                        v = 0.0f;
+                        for (int r = 0; r < TM; ++r)
+                            v += fast_exp2((float)(X1[(size_t)r * C + cp] + X2[(size_t)r * C + c] - lz2) + tv);
+                    }
+                    double* pt = part_trans + (size_t)cp * C + c;
+                    *pt = first ? (double)v : *pt + (double)v;
+                }
+        }
+        // the transition step, 4 rows x 4 labels a block per direction
+        const int RB = TM / 4;
+        for (int q = tid; q < 2 * RB * NB4; q += 256) {
+            const bool fw = q < RB * NB4;
+            const int qq = fw ? q : q - RB * NB4;
+            const int r0 = (qq / NB4) * 4, l0 = (qq % NB4) * 4;
+            const float* E = fw ? E1 : E2;
+            float acc[4][4] = {};
+            for (int j = 0; j < C4; j += 4) {
+                float e[4][4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 v = *reinterpret_cast<const float4*>(E + (size_t)(r0 + i) * C4 + j);
+                    e[i][0] = v.x; e[i][1] = v.y; e[i][2] = v.z; e[i][3] = v.w;
+                }
+                float w[4][4];   // w[jj][l]: weight of label j + jj into label l0 + l
+                if (fw) {
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const float4 v = *reinterpret_cast<const float4*>(trw + (size_t)(j + jj) * C4 + l0);
+                        w[jj][0] = v.x; w[jj][1] = v.y; w[jj][2] = v.z; w[jj][3] = v.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int l = 0; l < 4; ++l) {
+                        const float4 v = *reinterpret_cast<const float4*>(trw + (size_t)(l0 + l) * C4 + j);
+                        w[0][l] = v.x; w[1][l] = v.y; w[2][l] = v.z; w[3][l] = v.w;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                        for (int l = 0; l < 4; ++l) acc[i][l] = fmaf(e[i][jj], w[jj][l], acc[i][l]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int l = 0; l < 4; ++l) {
+                    const int r = r0 + i, c = l0 + l;
+                    const int s = p0 + r;
+                    if (c >= C || s > T) continue;
+                    const float sum = acc[i][l];
+                    double out;
+                    if (fw) {
+                        if (s == 0) out = ((Ps ? (double)Ps[c] : 0.0) + (offF ? offF[0] : 0.0) +
+                                           Sb[(size_t)L * C + c] - logZ) * LOG2E;
+                        else if (s > L - 1) out = DNEG;
+                        else {
+                            float lv = fast_log2(sum) + tmax;
+                            if (!(sum >= 0x1p-100f)) {
+                                const double* x = X1 + (size_t)r * C;
+                                float m = NEG;
+                                for (int jx = 0; jx < C; ++jx) m = fmaxf(m, (float)(x[jx] - m1[r]) + tr2_at(jx * C + c));
+                                float z = 0.0f;
+                                for (int jx = 0; jx < C; ++jx) z += fast_exp2((float)(x[jx] - m1[r]) + tr2_at(jx * C + c) - m);
+                                lv = m + fast_log2(z);
+                            }
+                            out = m1[r] + (double)lv +
+                                  ((Ps ? (double)Ps[(size_t)s * C + c] : 0.0) - Sb[(size_t)s * C + c] +
+                                   Sb[(size_t)L * C + c] - logZ) * LOG2E;
+                        }
+                        XF[(size_t)s * C + c] = out;
+                    } else {
+                        if (s == L) out = ((Pe ? (double)Pe[(size_t)(L - 1) * C + c] : 0.0) +
+                                           (offB ? offB[0] : 0.0)) * LOG2E;
+                        else if (s < 1 || s > L) out = DNEG;
+                        else {
+                            float lv = fast_log2(sum) + tmax;
+                            if (!(sum >= 0x1p-100f)) {
+                                const double* x = X2 + (size_t)r * C;
+                                float m = NEG;
+                                for (int jx = 0; jx < C; ++jx) m = fmaxf(m, (float)(x[jx] - m2[r]) + tr2_at(c * C + jx));
+                                float z = 0.0f;
+                                for (int jx = 0; jx < C; ++jx) z += fast_exp2((float)(x[jx] - m2[r]) + tr2_at(c * C + jx) - m);
+                                lv = m + fast_log2(z);
+                            }
+                            out = m2[r] + (double)lv +
+                                  ((Pe ? (double)Pe[(size_t)(s - 1) * C + c] : 0.0) + Sb[(size_t)s * C + c] -
+                                   Sb[(size_t)L * C + c]) * LOG2E;
+                        }
+                        XB[(size_t)s * C + c] = out;
+                    }
+                }
+        }
+    }
+}
+
 hipError_t launch_trans_step(const TransStepArgs& a, hipStream_t stream) {
     if (a.tpg < 1 || a.ngroups != (a.ntiles + a.tpg - 1) / a.tpg) return hipErrorInvalidValue;
+    if (a.C > 16) {
+        if (a.tile % 4 != 0) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(k_trans_step_wide, dim3(a.ngroups, a.B), dim3(256),
+                           step_lds_wide(a.C, a.tile), stream, a);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_trans_step, dim3(a.ngroups, a.B), dim3(256), step_lds(a.C, a.tile), stream,
                        a);
     return hipGetLastError();

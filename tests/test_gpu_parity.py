@@ -158,6 +158,34 @@ def test_forbidden_transitions_and_durations(crf):
     check_viterbi(w, np_(score), np_(labels), np_(seg), ref)
 
 
+@pytest.mark.parametrize("big", [False, True], ids=["forbidden", "large_transition"])
+def test_wide_label_transitions(crf, big):
+    """More than 16 labels (the register-blocked transition step): self-transitions
+    forbidden, and with `big` one transition weight of 70 (2^101 in base 2), which makes
+    the blocked transition posteriors leave the fp32 range, so the exact per-term sum
+    serves those tiles.  The raw node mass is held to 1e-4 without the large weight; with
+    it (log Z about 3,000, one transition dominating every path) the streamed fp32 sums
+    drift up to 1.6e-4 from 1, the same with the per-term transition step, so it is held to
+    5e-4 there; the normalised marginals stay within 1e-11 of the oracle."""
+    w = workloads.make_custom(33, 2, 90, 24, 12, ragged=True)
+    w.trans[np.arange(24), np.arange(24)] = -np.inf
+    if big:
+        w.trans[0, 1] = 70.0
+    print(f"\n[wide labels: C={w.C} K={w.K} big={big}]", flush=True)
+    em, lengths, trans, dur = dev(w)
+    ref = oracle.batch(w.em, w.lengths, w.trans, w.dur, w.K)
+    assert_scalar_close(np_(crf.logz(em, lengths, trans, dur)), ref["logZ"], LOGZ_RTOL, "logz")
+    out = crf.backward(em, lengths, trans, dur, want_node_mass=True, check_status=True)
+    nm = np_(out["node_mass"])[w.lengths[:, None] > np.arange(w.T)]
+    assert np.abs(nm - 1.0).max() <= (5e-4 if big else 1e-4)
+    assert_abs_close(np_(out["marginals"]), ref["mu"], MARG_ATOL, "marginals")
+    assert_abs_close(np_(out["grad_em"]), ref["grad_em"], MARG_ATOL, "grad_em")
+    assert_scalar_close(np_(out["grad_trans"]), ref["grad_trans"], GRAD_RTOL, "grad_trans")
+    assert_scalar_close(np_(out["grad_dur"]), ref["grad_dur"], GRAD_RTOL, "grad_dur")
+    score, labels, seg = crf.viterbi(em, lengths, trans, dur)
+    check_viterbi(w, np_(score), np_(labels), np_(seg), ref)
+
+
 def test_invalid_length_is_flagged(crf):
     import torch
     w = workloads.make_custom(41, 3, 20, 3, 4, ragged=False)
