@@ -203,25 +203,30 @@ def config_timings(crf, d):
     return out
 
 
-def only_config(crf, d, name, reps):
+def only_config(crf, d, name, reps, delta=0):
     """One other configuration alone: backward, Viterbi and log Z, each timed over reps
-    calls after one untimed call."""
+    calls after one untimed call (delta: the checkpoint interval of log Z and the backward,
+    0 for the library default)."""
     import torch
 
     import workloads
     w = workloads.long_duration() if name == "long_duration" else \
         workloads.make({"speech": 1, "long": 3, "large_c": 4}[name])
     em, lengths, trans, dur = (torch.from_numpy(a).to(d) for a in (w.em, w.lengths, w.trans, w.dur))
-    ws = {op: torch.empty(crf.workspace_bytes(op, w.B, w.T, w.C, w.K), dtype=torch.uint8, device=d)
+    ws = {op: torch.empty(crf.workspace_bytes(op, w.B, w.T, w.C, w.K, delta), dtype=torch.uint8,
+                          device=d)
           for op in (crf.OP_BACKWARD, crf.OP_VITERBI, crf.OP_LOGZ)}
-    mb = _time_ms(lambda: crf.backward(em, lengths, trans, dur, workspace=ws[crf.OP_BACKWARD]), d,
-                  reps)
+    mb = _time_ms(lambda: crf.backward(em, lengths, trans, dur, delta=delta,
+                                       workspace=ws[crf.OP_BACKWARD]), d, reps)
     mv = _time_ms(lambda: crf.viterbi(em, lengths, trans, dur, workspace=ws[crf.OP_VITERBI]), d,
                   reps)
-    ml = _time_ms(lambda: crf.logz(em, lengths, trans, dur, workspace=ws[crf.OP_LOGZ]), d, reps)
+    ml = _time_ms(lambda: crf.logz(em, lengths, trans, dur, delta=delta,
+                                   workspace=ws[crf.OP_LOGZ]), d, reps)
     pos = w.positions()
     return {"config": name, "B": w.B, "T": w.T, "K": w.K, "C": w.C, "positions": pos,
-            "reps": reps, "backward_ms": mb, "viterbi_ms": mv, "logz_ms": ml,
+            "reps": reps,
+            "delta": delta or crf.default_interval(crf.OP_BACKWARD, w.B, w.T, w.C, w.K),
+            "backward_ms": mb, "viterbi_ms": mv, "logz_ms": ml,
             "fwd_bwd_positions_per_s": pos / (mb * 1e-3)}
 
 
@@ -321,7 +326,7 @@ def main():
     lib = _native.load()
     if args.only_config:
         print(json.dumps(only_config(crf, torch.device("cuda:0"), args.only_config,
-                                     max(1, args.steps))), flush=True)
+                                     max(1, args.steps), args.delta)), flush=True)
         return
     hip = hip_runtime()
     w = workloads.make(CONFIG)
@@ -331,7 +336,8 @@ def main():
     trans = torch.from_numpy(w.trans).to(d)
     dur = torch.from_numpy(w.dur).to(d)
     B, T, C, K = w.B, w.T, w.C, w.K
-    delta = crf.checkpoint_interval(T, K, args.delta) if args.delta else crf.default_interval(B, T, K)
+    delta = (crf.checkpoint_interval(T, K, args.delta) if args.delta
+             else crf.default_interval(crf.OP_BACKWARD, B, T, C, K))
     vdelta = crf.viterbi_interval(B, T, K)
     nb = crf.workspace_bytes(crf.OP_BACKWARD, B, T, C, K, args.delta)
     nv = crf.workspace_bytes(crf.OP_VITERBI, B, T, C, K)

@@ -86,11 +86,15 @@ int semicrf_checkpoint_interval(int T, int K, int delta);
  * long, so that the spans swept at once occupy more compute units.  0 on bad input. */
 int semicrf_viterbi_interval(int B, int T, int K);
 
-/* The checkpoint interval semicrf_logz and semicrf_backward use for delta = 0:
- * semicrf_checkpoint_interval(T, K, 0) while the batch has at least 224 spans of that
- * length (7/8 of the MI355X's 256 compute units), else shortened until it has about 224,
- * but not below two burn-ins (6 K) nor above ceil(sqrt(T*K)).  0 on bad input. */
-int semicrf_default_interval(int B, int T, int K);
+/* The checkpoint interval `op` uses for delta = 0 (SEMICRF_OP_VITERBI: the decode's,
+ * semicrf_viterbi_interval).  For log Z and the backward every span is swept at once, so
+ * the interval is the one, over every span count n (interval ceil(T/n)), that minimises
+ * (interval + burn-in 3K) * ceil(workgroups / share): workgroups = B * spans for log Z
+ * and for a backward whose two directions share a workgroup (small label counts), else
+ * twice that; share = 224 workgroups (7/8 of the MI355X's 256 compute units, leaving room
+ * for a concurrent call) where the round kernels run (C <= 16, K <= 1025), else 256.
+ * Ties go to the longer interval.  0 on bad or unsupported input. */
+int semicrf_default_interval(semicrf_op op, int B, int T, int C, int K);
 
 /* Bytes of workspace that `op` needs for these shapes (delta as the call takes it: > 0 an
  * explicit interval, 0 the default above).  0 if the arguments are invalid or
@@ -112,7 +116,8 @@ int semicrf_prefix(const float* emissions, const int32_t* lengths, int B, int T,
 
 /* log Z for every sequence: the log-sum-exp of the scores of all segmentations
  * (EN explainer, "2. Methodology", "Streaming Forward-Backward with Ring Buffers",
- * forward pass).  delta: checkpoint interval (0 = semicrf_default_interval(B, T, K)), the
+ * forward pass).  delta: checkpoint interval (0 = semicrf_default_interval(SEMICRF_OP_LOGZ,
+ * B, T, C, K)), the
  * same value as given to semicrf_workspace_bytes.  Output: log_z [B] float32. */
 int semicrf_logz(const float* emissions, const int32_t* lengths, const float* trans,
                  const float* dur, int B, int T, int C, int K, int delta, hipStream_t stream,
@@ -129,7 +134,8 @@ int semicrf_logz(const float* emissions, const int32_t* lengths, const float* tr
  *   marginals      [B, T, C] float32  or NULL: posterior probability that position t
  *                                     lies in a segment of label c (sums to 1 over c)
  *   log_z          [B]       float32  or NULL
- * delta: checkpoint interval (0 = semicrf_default_interval(B, T, K)); results do not
+ * delta: checkpoint interval (0 = semicrf_default_interval(SEMICRF_OP_BACKWARD, B, T, C,
+ * K)); results do not
  * depend on it beyond rounding. */
 int semicrf_backward(const float* emissions, const int32_t* lengths, const float* trans,
                      const float* dur, int B, int T, int C, int K, int delta,

@@ -38,9 +38,9 @@ def viterbi_interval(B: int, T: int, K: int) -> int:
     return int(_native.load().semicrf_viterbi_interval(B, T, K))
 
 
-def default_interval(B: int, T: int, K: int) -> int:
-    """Checkpoint interval log Z and the backward use for delta = 0."""
-    return int(_native.load().semicrf_default_interval(B, T, K))
+def default_interval(op: int, B: int, T: int, C: int, K: int) -> int:
+    """Checkpoint interval `op` uses for delta = 0."""
+    return int(_native.load().semicrf_default_interval(op, B, T, C, K))
 
 
 def workspace_bytes(op: int, B: int, T: int, C: int, K: int, delta: int = 0) -> int:

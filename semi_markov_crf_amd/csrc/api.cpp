@@ -68,23 +68,52 @@ int default_delta(int B, int T, int K) {
     return d;
 }
 
-// The default interval of log Z and the backward (delta = 0).  A span's sweep takes time
-// in proportion to its length plus its burn-in while every span has a compute unit of its
-// own, and a second round of workgroups doubles it.  So when ceil(sqrt(T*K)) gives fewer
-// spans than 7/8 of the MI355X's 256 compute units hold (the rest is left to a concurrent
-// call, such as a decode on another stream), the interval shrinks until the batch's spans
-// reach that count, but not below two burn-ins.  At B = 4, T = 10^5, K = 200 (224 spans of
-// 1,786 instead of 180 of 2,237) a backward pass beside a decode drops from 1.96 to
-// 1.74 ms per pair of calls.
-int fill_delta(int B, int T, int K) {
-    constexpr long long TARGET = 256 * 7 / 8;
+// Workgroups that one checkpoint span of `op` takes in the span launch: one for log Z;
+// for the backward one when the round kernel holds both directions of a span in one
+// workgroup (as its launcher decides, without projections), else two.
+static int span_workgroups(const SweepCfg& cfg, int op, int C) {
+    if (op != SEMICRF_OP_BACKWARD) return 1;
+    if (cfg.split && !cfg.xk) {
+        const bool lin = (cfg.lse.layout & SWEEP_LINEAR) != 0;
+        if (64 + 2 * cfg.NTv <= 512 &&
+            2 * lse_round_region_bytes(C, cfg.CPr, cfg.lse.P, cfg.lse.CH, lin, false) <= 150 * 1024)
+            return 1;
+    }
+    return 2;
+}
+
+// The default interval of log Z and the backward (delta = 0).  Every span is swept at
+// once; a workgroup's sweep takes time in proportion to its span plus its burn-in, and
+// once the spans' workgroups outnumber what the compute units run side by side, a CU
+// holds two and each takes about twice as long (measured: the sweeps are issue-bound on
+// their CU).  So the interval is the one, over every span count n (interval ceil(T/n)),
+// that minimises (interval + burn-in) * ceil(workgroups / share), the longer on ties.
+// share: 224 workgroups (7/8 of the MI355X's 256 CUs, the rest left to a concurrent call
+// such as a decode on another stream) for the round kernels, 256 for the others.
+// Measured at B = 4, T = 10^5, K = 200 (round kernel, one workgroup per span): a backward
+// beside a decode takes 1.74 ms a pair at 1,786 against 1.96 at ceil(sqrt(TK))/2; 32 speech
+// sequences (K = 30, C = 39, two workgroups a span) take 0.50 ms at 200 against 0.68 at 155.
+int fill_delta(int B, int T, int K, int op, const SweepCfg& cfg, int C) {
     const int d0 = resolve_delta(T, K, 0);
     if (d0 < 1) return 0;
-    if ((long long)B * ((T + d0 - 1) / d0) >= TARGET) return d0;
-    const long long per = std::max<long long>(1, TARGET / B);   // spans per sequence
-    long long d = (T + per - 1) / per;
-    d = std::max<long long>(d, 2LL * spec_warm(K));
-    return (int)std::min<long long>(d, d0);
+    const long long wps = span_workgroups(cfg, op, C);
+    const long long share = (cfg.split && !cfg.xk) ? 256 * 7 / 8 : 256;
+    const long long warm = spec_warm(K);
+    const long long nmax = std::max<long long>(1, std::min<long long>(T, 8192 / B));
+    long long best_d = d0;
+    double best = 1e300;
+    for (long long n = 1; n <= nmax; ++n) {
+        const long long d = (T + n - 1) / n;
+        if (n > 1 && d == (T + n - 2) / (n - 1)) continue;   // same interval as n - 1
+        const long long spans = (T + d - 1) / d;
+        const long long rounds = (wps * B * spans + share - 1) / share;
+        const double f = (double)(d + (spans > 1 ? warm : 0)) * (double)rounds;
+        if (f < best || (f == best && d > best_d)) {
+            best = f;
+            best_d = d;
+        }
+    }
+    return (int)best_d;
 }
 
 bool shape_ok(int B, int T, int C, int K) {
@@ -110,7 +139,7 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         // decode runs forward only, with the default interval)
         // delta = 0 (and always for the decode): the batch-aware default interval
         lo.delta = op == SEMICRF_OP_VITERBI ? default_delta(B, T, K)
-                   : delta == 0             ? fill_delta(B, T, K)
+                   : delta == 0             ? fill_delta(B, T, K, op, cfg, C)
                                             : resolve_delta(T, K, delta);
         if (lo.delta < 1) return false;
         lo.nspans = (T + lo.delta - 1) / lo.delta;
@@ -322,9 +351,13 @@ int semicrf_viterbi_interval(int B, int T, int K) {
     return default_delta(B, T, K);
 }
 
-int semicrf_default_interval(int B, int T, int K) {
-    if (!shape_ok(B, T, 1, K)) return 0;
-    return fill_delta(B, T, K);
+int semicrf_default_interval(semicrf_op op, int B, int T, int C, int K) {
+    if (!shape_ok(B, T, C, K)) return 0;
+    if (op == SEMICRF_OP_VITERBI) return default_delta(B, T, K);
+    if (op != SEMICRF_OP_LOGZ && op != SEMICRF_OP_BACKWARD) return 0;
+    const SweepCfg cfg = choose_sweep(C, K);
+    if (!cfg.ok) return 0;
+    return fill_delta(B, T, K, op, cfg, C);
 }
 
 int semicrf_prefix(const float* em, const int32_t* lengths, int B, int T, int C,

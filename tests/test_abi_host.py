@@ -124,14 +124,27 @@ def test_checkpoint_interval(native):
 def test_default_interval(native):
     lib = native.load()
     f = lib.semicrf_default_interval
-    assert f(4, 100_000, 200) == 1786          # 56 spans a sequence: 224 spans
-    assert f(1, 1_000_000, 200) == 4465        # 224 spans
-    assert f(8, 10_000, 64) == 384             # two burn-ins (384): 27 spans a sequence
-    assert f(32, 800, 30) == 155               # two burn-ins (180) exceed ceil(sqrt(TK))
-    assert f(64, 100_000, 200) == 4473         # 1472 spans: the batch fills the device
-    assert f(1, 1000, 200) == 448              # two burn-ins exceed ceil(sqrt(TK))
-    assert f(4, 100_000, 1) == 317             # 1264 spans of ceil(sqrt(TK))
-    assert f(0, 100, 5) == 0 and f(1, 0, 5) == 0 and f(1, 10, 0) == 0
+    LZ, BW, VI = native.OP_LOGZ, native.OP_BACKWARD, native.OP_VITERBI
+    # round kernels, both directions of a span in one workgroup: 224 workgroups
+    assert f(BW, 4, 100_000, 6, 200) == 1786   # 56 spans a sequence
+    assert f(LZ, 4, 100_000, 6, 200) == 1786
+    assert f(BW, 1, 1_000_000, 6, 200) == 4465
+    # 16 labels: two workgroups a span
+    assert f(BW, 4, 100_000, 16, 200) == 3572  # 28 spans a sequence
+    # other kernels: 256 workgroups, two a span for the backward
+    assert f(BW, 32, 800, 39, 30) == 200       # 4 spans a sequence
+    assert f(LZ, 32, 800, 39, 30) == 100       # 8
+    assert f(BW, 8, 10_000, 64, 64) == 625     # 16
+    assert f(LZ, 8, 10_000, 64, 64) == 313     # 32
+    assert f(BW, 1, 1_000_000, 6, 2000) == 7813
+    # a batch that fills the device: fewer, longer spans
+    assert f(BW, 64, 100_000, 6, 200) == 14286
+    # short sequences: one span (no burn-in) beats any split
+    assert f(BW, 2, 64, 4, 8) == 64
+    # the decode keeps its own interval
+    assert f(VI, 4, 100_000, 6, 200) == lib.semicrf_viterbi_interval(4, 100_000, 200)
+    assert f(BW, 0, 100, 4, 5) == 0 and f(BW, 1, 0, 4, 5) == 0 and f(BW, 1, 10, 4, 0) == 0
+    assert f(BW, 1, 100, 200, 5) == 0          # unsupported label count
 
 
 def test_viterbi_interval(native):
