@@ -19,12 +19,12 @@ constexpr size_t ALIGN = 256;
 constexpr int MAX_T = 1 << 29;   // keeps position arithmetic (t + delta) inside int
 
 struct Layout {
-    int nts = 0, ntm = 0, tm = 0, tpg = 0, ngm = 0, delta = 0, nspans = 0, ndir = 0;
+    int nts = 0, ntm = 0, tm = 0, tpg = 0, ngm = 0, delta = 0, nspans = 0, ndir = 0, npb = 1;
     size_t status = 0, Leff = 0, tsum = 0, toff = 0, ttot = 0, S = 0;
     size_t logz = 0, logzb = 0;
     size_t head = 0, tail = 0, lzloc = 0, soff = 0, fbad = 0, diag = 0, sstat = 0;
     size_t ckR = 0, ckB = 0, ckM = 0, ckH = 0, XF = 0, XB = 0;
-    size_t dnt = 0, dno = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0, rps = 0;
+    size_t dnt = 0, dno = 0, mut = 0, mutot = 0, zt = 0, pd = 0, pt = 0, rps = 0, pbp = 0;
     size_t gcnt = 0, gpart = 0;
     size_t bp = 0, vfin = 0, vend = 0, btr = 0, bent = 0, btg = 0;
     size_t xkr = 0;                 // long-duration sweeps: the global ring scratch
@@ -188,6 +188,9 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         lo.tpg = marg_tiles_per_group(B, lo.ntm, C, K);
         lo.ngm = (lo.ntm + lo.tpg - 1) / lo.tpg;
         lo.pd = m.take(sizeof(double) * B * lo.ngm * K * C);
+        // label groups' shares of the raw boundary sums (more than one group only)
+        lo.npb = (C + marg_labels(C) - 1) / marg_labels(C);
+        if (lo.npb > 1) lo.pbp = m.take(sizeof(float) * (size_t)lo.npb * B * T);
         lo.pt = m.take(sizeof(double) * B * lo.ngm * C * C);
         lo.rps = m.take(sizeof(double) * reduce_scratch_doubles(C, K));
         // gold-segmentation loss (semicrf_nll): counters and block sums
@@ -462,6 +465,8 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
     m.pstart = br.grad_start;
     m.pend = br.grad_end;
     m.pbsum = br.prob;
+    m.cg = marg_labels(C);
+    m.pb_part = lo.npb > 1 ? at<float>(workspace, lo.pbp) : nullptr;
     // mu lives in the caller's marginals, else in grad_emissions (k_grad_em then works in
     // place); k_marginals leaves the in-tile prefix there first
     float* mu = marginals ? marginals : grad_em;
@@ -476,6 +481,8 @@ static int run_backward(const float* em, const int32_t* lengths, const float* tr
     bo.grad_proj_end = br.grad_end;
     bo.boundary = br.prob;
     bo.node_mass = br.node_mass;
+    bo.pb_part = (lo.npb > 1 && br.prob) ? m.pb_part : nullptr;
+    bo.npb = lo.npb;
     LAUNCH(launch_node_marginals(m.Dloc, at<double>(workspace, lo.dno), a.Leff, B, T, C, lo.tm,
                                  lo.ntm, mu, at<double>(workspace, lo.mut),
                                  at<double>(workspace, lo.zt), bo, stream));

@@ -17,6 +17,7 @@ int scan_tile(int C);
 // Positions per tile of the marginal and node-marginal kernels, and durations per chunk
 // of the marginal kernel.
 int marg_tile(int C, int K);
+int marg_labels(int C);   // labels a k_marginals workgroup takes (a label group)
 int marg_kchunk(int C, int K);
 
 // ------------------------------------------------------------------ sweep configuration
@@ -292,6 +293,10 @@ struct MargArgs {
     float* pstart;          // [B][T][C] or NULL: raw start mass of segments at each position
     float* pend;            // [B][T][C] or NULL: raw mass of segments whose last position it is
     float* pbsum;           // [B][T] or NULL: raw start mass summed over labels
+    int cg;                 // labels per label group (marg_labels(C))
+    // [groups][B][T]: each label group's share of pbsum when there are several (NULL
+    // otherwise); k_node_marginals adds them up in group order
+    float* pb_part;
 };
 hipError_t launch_marginals(const MargArgs& a, hipStream_t stream);
 // tiles per group of the posterior partials: enough groups to fill the device, the
@@ -309,6 +314,8 @@ struct BoundaryOut {
     float* grad_proj_end;
     float* boundary;
     float* node_mass;           // [B][T] or NULL: the per-position normaliser itself
+    const float* pb_part;       // [npb][B][T] label groups' raw boundary sums, or NULL
+    int npb;                    // (then boundary holds nothing yet)
 };
 hipError_t launch_node_marginals(const float* Dloc, const double* dn_off, const int* Leff,
                                  int B, int T, int C, int tile, int ntiles, float* mu,

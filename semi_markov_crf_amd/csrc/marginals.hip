@@ -39,11 +39,22 @@
 
 namespace semicrf {
 
-// LDS of k_marginals for tile TM and duration chunk KC: the tile's own start / end values,
-// the two shifted windows of a chunk, start / end mass accumulators (fp64), the prefix
-// scratch (256 doubles) and the chunk's durations (fp32).
-static size_t marg_lds(int C, int TM, int KC) {
-    return (size_t)8 * C * (6 * TM + 2 * KC) + (size_t)8 * 256 + (size_t)4 * KC * C;
+// LDS of k_marginals for CL labels, tile TM and duration chunk KC: the tile's own start /
+// end values, the two shifted windows of a chunk, start / end mass accumulators (fp64), the
+// prefix scratch (256 doubles) and the chunk's durations (fp32).
+static size_t marg_lds(int CL, int TM, int KC) {
+    return (size_t)8 * CL * (6 * TM + 2 * KC) + (size_t)8 * 256 + (size_t)4 * KC * CL;
+}
+
+// Labels a k_marginals workgroup takes: all of them up to 16, else groups of 16.
+int marg_labels(int C) { return C <= 16 ? C : 16; }
+
+__host__ __device__ static inline int c4_of(int C) { return (C + 3) / 4 * 4; }
+// LDS of k_trans_step_wide (more than 16 labels) for tile TM
+static size_t step_lds_wide(int C, int TM) {
+    const int C4 = c4_of(C);
+    return (size_t)8 * (2 * TM * C + 2 * TM) + (size_t)4 * TM + (size_t)8 * TM * C4 +
+           (size_t)4 * C4 * C4 + 32;
 }
 
 // Tile and duration chunk.  First choice: the largest tile of at least max(32, K/4)
@@ -53,15 +64,19 @@ static size_t marg_lds(int C, int TM, int KC) {
 // the fp64 sums).  Otherwise the largest tile that fits one workgroup per CU with such a
 // chunk; the smallest tile takes any chunk.
 static void marg_shape(int C, int K, int* tm, int* kc) {
+    const int CL = marg_labels(C);
     auto chunks = [&](int t, int min_kc, size_t budget) {
-        if (K <= 512 && marg_lds(C, t, K) <= budget) return K;
+        if (K <= 512 && marg_lds(CL, t, K) <= budget) return K;
         for (int k = 512; k >= min_kc; k >>= 1)
-            if (k < K && marg_lds(C, t, k) <= budget) return k;
+            if (k < K && marg_lds(CL, t, k) <= budget) return k;
         return 0;
     };
+    // above 16 labels the transition step shares the tile: keep its LDS within 150 KB
+    int tmax = 512;
+    while (C > 16 && tmax > 8 && step_lds_wide(C, tmax) > 150 * 1024) tmax >>= 1;
     int tmin = 32;
     while (tmin < 512 && 4 * tmin < K) tmin *= 2;
-    for (int t = 512; t >= tmin; t >>= 1) {
+    for (int t = tmax; t >= tmin; t >>= 1) {
         const int k = chunks(t, std::min(K, 64), 52 * 1024);
         if (k > 0) {
             *tm = t;
@@ -69,7 +84,7 @@ static void marg_shape(int C, int K, int* tm, int* kc) {
             return;
         }
     }
-    for (int t = 512; t >= 8; t >>= 1) {
+    for (int t = tmax; t >= 8; t >>= 1) {
         const int k = chunks(t, t > 8 ? std::min(K, 64) : 1, 150 * 1024);
         if (k > 0) {
             *tm = t;
@@ -253,12 +268,6 @@ __global__ __launch_bounds__(256) void k_trans_step(const TransStepArgs a) {
 // transition posterior is at most 1); a tile in which it, or 2^(max tr2), would leave the
 // fp32 range (above 2^60) sums the exact per-term exponentials instead.  The transition
 // step and its log-space replay are those of k_trans_step.
-__host__ __device__ static inline int c4_of(int C) { return (C + 3) / 4 * 4; }
-static size_t step_lds_wide(int C, int TM) {
-    const int C4 = c4_of(C);
-    return (size_t)8 * (2 * TM * C + 2 * TM) + (size_t)4 * TM + (size_t)8 * TM * C4 +
-           (size_t)4 * C4 * C4 + 32;
-}
 
 __global__ __launch_bounds__(256) void k_trans_step_wide(const TransStepArgs a) {
     extern __shared__ double lds[];
@@ -478,8 +487,10 @@ hipError_t launch_trans_step(const TransStepArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// grid (ngroups, B), block 256: the tiles g*tpg .. (g+1)*tpg - 1 of sequence b in order.
-// Durations are taken in chunks [kc0, kc1] of at most KC: per chunk the starts
+// grid (ngroups, B, label groups), block 256: the tiles g*tpg .. (g+1)*tpg - 1 of sequence
+// b in order, for the labels c0 .. c0+CL-1 of one label group (c0 = z * cg; the labels are
+// independent here, and a group of at most 16 keeps the staged windows small enough for
+// several workgroups a CU at large label counts).  Durations are taken in chunks [kc0, kc1] of at most KC: per chunk the starts
 // [p0 - kc1, p0 + TM - 1 - kc0] and the ends [p0 + kc0, p0 + TM - 1 + kc1] are staged
 // beside the tile's own starts and ends.  The duration partials of the group's tiles are
 // summed in tile order (each lane owns the same entries in every tile).
@@ -487,45 +498,53 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
     extern __shared__ double lds[];
     const int C = a.C, K = a.K, T = a.T, TM = a.tile, KC = a.kchunk;
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int c0 = blockIdx.z * a.cg, CL = min(a.cg, C - c0);   // this workgroup's labels
     const int L = abs(a.Leff[b]);
     const size_t rowC = (size_t)(T + 1) * C;
 
-    double* AFt = lds;                               // [TM][C]: starts p0 .. p0+TM-1
-    double* ABt = AFt + (size_t)TM * C;              // [TM][C]: ends p0 .. p0+TM-1
-    double* AFw = ABt + (size_t)TM * C;              // [TM+KC][C]: starts of the chunk's ends
-    double* ABw = AFw + (size_t)(TM + KC) * C;       // [TM+KC][C]: ends of the chunk's starts
-    double* Dst = ABw + (size_t)(TM + KC) * C;       // [TM][C] start mass
-    double* Den = Dst + (size_t)TM * C;              // [TM][C] end mass
-    double* csum = Den + (size_t)TM * C;             // [256] prefix scratch
-    float* dur2 = (float*)(csum + 256);              // [KC][C]
+    // LDS rows hold the group's CL labels
+    double* AFt = lds;                               // [TM][CL]: starts p0 .. p0+TM-1
+    double* ABt = AFt + (size_t)TM * CL;             // [TM][CL]: ends p0 .. p0+TM-1
+    double* AFw = ABt + (size_t)TM * CL;             // [TM+KC][CL]: starts of the chunk's ends
+    double* ABw = AFw + (size_t)(TM + KC) * CL;      // [TM+KC][CL]: ends of the chunk's starts
+    double* Dst = ABw + (size_t)(TM + KC) * CL;      // [TM][CL] start mass
+    double* Den = Dst + (size_t)TM * CL;             // [TM][CL] end mass
+    double* csum = Den + (size_t)TM * CL;            // [256] prefix scratch
+    float* dur2 = (float*)(csum + 256);              // [KC][CL]
 
     double* part_dur = a.part_dur + ((size_t)b * a.ngroups + g) * K * C;
     float* Dloc = a.Dloc + (size_t)b * T * C;
     const double* AF = a.AF + (size_t)b * rowC;
     const double* AB = a.AB + (size_t)b * rowC;
     const int tile_end = min(a.ntiles, (g + 1) * a.tpg);
+    // q over [rows][CL]: row q / CL, global label c0 + q % CL
     for (int tile = g * a.tpg; tile < tile_end; ++tile) {
         const int p0 = tile * TM;
         const bool first = tile == g * a.tpg;    // stores the group's partials, later tiles add
         double* dn_tile = a.dn_tile + ((size_t)b * a.ntiles + tile) * C;
         if (p0 > L) {   // nothing of this sequence here
-            for (int q = tid; q < C; q += 256) dn_tile[q] = 0.0;
-            for (int q = tid; q < TM * C; q += 256)
-                if (p0 + q / C < T) Dloc[(size_t)p0 * C + q] = 0.0f;
+            for (int q = tid; q < CL; q += 256) dn_tile[c0 + q] = 0.0;
+            for (int q = tid; q < TM * CL; q += 256) {
+                const int r = q / CL;
+                if (p0 + r < T) Dloc[(size_t)(p0 + r) * C + c0 + (q - r * CL)] = 0.0f;
+            }
             if (first)
-                for (int q = tid; q < K * C; q += 256) part_dur[q] = 0.0;
+                for (int q = tid; q < K * CL; q += 256) {
+                    const int k = q / CL;
+                    part_dur[(size_t)k * C + c0 + (q - k * CL)] = 0.0;
+                }
             continue;
         }
         // base 2; invalid starts / ends get DNEG so that their exponentials vanish
         auto af = [&](int s, int c) -> double {
-            return (s >= 0 && s <= L - 1) ? AF[(size_t)s * C + c] : DNEG;
+            return (s >= 0 && s <= L - 1) ? AF[(size_t)s * C + c0 + c] : DNEG;
         };
         auto ab = [&](int u, int c) -> double {
-            return (u >= 1 && u <= L) ? AB[(size_t)u * C + c] : DNEG;
+            return (u >= 1 && u <= L) ? AB[(size_t)u * C + c0 + c] : DNEG;
         };
 
-        for (int q = tid; q < TM * C; q += 256) {
-            const int r = q / C, c = q - r * C;
+        for (int q = tid; q < TM * CL; q += 256) {
+            const int r = q / CL, c = q - r * CL;
             const int s = p0 + r;
             AFt[q] = af(s, c);
             ABt[q] = ab(s, c);
@@ -539,27 +558,29 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
             const int kc1 = min(K, kc0 + KC - 1);
             const int nk = kc1 - kc0 + 1;
             __syncthreads();   // the previous chunk's windows are no longer read
-            for (int q = tid; q < (TM + nk - 1) * C; q += 256) {
-                const int r = q / C, c = q - r * C;
+            for (int q = tid; q < (TM + nk - 1) * CL; q += 256) {
+                const int r = q / CL, c = q - r * CL;
                 AFw[q] = af(p0 - kc1 + r, c);
                 ABw[q] = ab(p0 + kc0 + r, c);
             }
-            for (int q = tid; q < nk * C; q += 256)
-                dur2[q] = fmaxf((float)((double)a.dur[(size_t)(kc0 - 1) * C + q] * LOG2E), NEG);
+            for (int q = tid; q < nk * CL; q += 256) {
+                const int k = q / CL, c = q - k * CL;
+                dur2[q] = fmaxf((float)((double)a.dur[(size_t)(kc0 - 1 + k) * C + c0 + c] * LOG2E), NEG);
+            }
             __syncthreads();
 
             // ---- phase 1: per position, start and end mass of the chunk's segments (fp64
             // sums of the same per-segment values: they cancel exactly in mu's prefix)
-            for (int q = tid; q < TM * C; q += 256) {
-                const int r = q / C, c = q - r * C;
+            for (int q = tid; q < TM * CL; q += 256) {
+                const int r = q / CL, c = q - r * CL;
                 if (p0 + r > L) continue;
                 double st = Dst[q], en = Den[q];
                 const double a0 = AFt[q], b0 = ABt[q];
 #pragma unroll 4
                 for (int k = kc0; k <= kc1; ++k) {
-                    const float d = dur2[(k - kc0) * C + c];
-                    st += (double)seg(a0 + ABw[(size_t)(r + k - kc0) * C + c], d);   // [t, t+k)
-                    en += (double)seg(AFw[(size_t)(r + kc1 - k) * C + c] + b0, d);   // [t-k, t)
+                    const float d = dur2[(k - kc0) * CL + c];
+                    st += (double)seg(a0 + ABw[(size_t)(r + k - kc0) * CL + c], d);   // [t, t+k)
+                    en += (double)seg(AFw[(size_t)(r + kc1 - k) * CL + c] + b0, d);   // [t-k, t)
                 }
                 Dst[q] = st;
                 Den[q] = en;
@@ -567,14 +588,14 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
 
             // ---- phase 2: duration partials, lanes over (k, c), segments starting in the
             // tile (an fp32 sum over the tile's rows, then fp64 across tiles)
-            for (int q = tid; q < nk * C; q += 256) {
-                const int kk = q / C, c = q - kk * C;
+            for (int q = tid; q < nk * CL; q += 256) {
+                const int kk = q / CL, c = q - kk * CL;
                 const float d = dur2[q];
                 float acc = 0.0f;
 #pragma unroll 4
                 for (int r = 0; r < TM; ++r)
-                    acc += seg(AFt[(size_t)r * C + c] + ABw[(size_t)(r + kk) * C + c], d);
-                double* pd = part_dur + (size_t)(kc0 - 1) * C + q;
+                    acc += seg(AFt[(size_t)r * CL + c] + ABw[(size_t)(r + kk) * CL + c], d);
+                double* pd = part_dur + (size_t)(kc0 - 1 + kk) * C + c0 + c;
                 *pd = first ? (double)acc : *pd + (double)acc;
             }
         }
@@ -582,43 +603,47 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
 
         // ---- raw boundary masses, then start mass - end mass per position
         if (a.pstart || a.pend)
-            for (int q = tid; q < TM * C; q += 256) {
-                const int r = q / C, c = q - r * C;
+            for (int q = tid; q < TM * CL; q += 256) {
+                const int r = q / CL, c = c0 + (q - r * CL);
                 const int t = p0 + r;
                 if (a.pstart && t < L) a.pstart[((size_t)b * T + t) * C + c] = (float)Dst[q];
                 if (a.pend && t >= 1 && t <= L) a.pend[((size_t)b * T + t - 1) * C + c] = (float)Den[q];
             }
-        if (a.pbsum)
+        if (a.pbsum) {
+            // one label group: the sum itself; several: this group's share, which
+            // k_node_marginals adds up in group order
+            float* out = a.cg < C ? a.pb_part + (size_t)blockIdx.z * a.B * T : a.pbsum;
             for (int r = tid; r < TM; r += 256) {
                 const int t = p0 + r;
                 if (t >= L) continue;
                 double s = 0.0;
-                for (int c = 0; c < C; ++c) s += Dst[(size_t)r * C + c];
-                a.pbsum[(size_t)b * T + t] = (float)s;
+                for (int c = 0; c < CL; ++c) s += Dst[(size_t)r * CL + c];
+                out[(size_t)b * T + t] = (float)s;
             }
+        }
         __syncthreads();
-        for (int q = tid; q < TM * C; q += 256) Dst[q] -= Den[q];
+        for (int q = tid; q < TM * CL; q += 256) Dst[q] -= Den[q];
         __syncthreads();
         // in-tile inclusive prefix per label: lanes over (label, row chunk), fixed order;
         // the last row's value is the tile total
-        for (int c0 = 0; c0 < C; c0 += 256) {
-            const int CW = min(256, C - c0);
+        for (int cb = 0; cb < CL; cb += 256) {
+            const int CW = min(256, CL - cb);
             const int R = 256 / CW;
             const int chunk = (TM + R - 1) / R;
-            const int cw = tid % CW, r = tid / CW, c = c0 + cw;
+            const int cw = tid % CW, r = tid / CW, c = cb + cw;
             const bool act = r < R;
             double acc = 0.0;
             if (act)
-                for (int i = r * chunk; i < min(TM, (r + 1) * chunk); ++i) acc += Dst[(size_t)i * C + c];
+                for (int i = r * chunk; i < min(TM, (r + 1) * chunk); ++i) acc += Dst[(size_t)i * CL + c];
             csum[tid] = acc;
             __syncthreads();
             if (act) {
                 double run = 0.0;
                 for (int qq = 0; qq < r; ++qq) run += csum[qq * CW + cw];
                 for (int i = r * chunk; i < min(TM, (r + 1) * chunk); ++i) {
-                    run += Dst[(size_t)i * C + c];
-                    if (p0 + i < T) Dloc[(size_t)(p0 + i) * C + c] = (float)run;
-                    if (i == TM - 1) dn_tile[c] = run;
+                    run += Dst[(size_t)i * CL + c];
+                    if (p0 + i < T) Dloc[(size_t)(p0 + i) * C + c0 + c] = (float)run;
+                    if (i == TM - 1) dn_tile[c0 + c] = run;
                 }
             }
             __syncthreads();
@@ -627,9 +652,12 @@ __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
 }
 
 hipError_t launch_marginals(const MargArgs& a, hipStream_t stream) {
-    const size_t lds = marg_lds(a.C, a.tile, a.kchunk);
+    if (a.cg < 1 || a.cg > a.C) return hipErrorInvalidValue;
+    const int nlg = (a.C + a.cg - 1) / a.cg;
+    if (nlg > 1 && a.pbsum && !a.pb_part) return hipErrorInvalidValue;
+    const size_t lds = marg_lds(a.cg, a.tile, a.kchunk);
     if (a.tpg < 1 || a.ngroups != (a.ntiles + a.tpg - 1) / a.tpg) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_marginals, dim3(a.ngroups, a.B), dim3(256), lds, stream, a);
+    hipLaunchKernelGGL(k_marginals, dim3(a.ngroups, a.B, nlg), dim3(256), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -688,7 +716,14 @@ __global__ __launch_bounds__(256) void k_node_marginals(const float* Dloc,
                 const int t = p0 + r;
                 if (t >= T) continue;
                 float* o = bo.boundary + (size_t)b * T + t;
-                *o = r < rows ? (float)((double)*o / zrow[r]) : 0.0f;
+                double raw = 0.0;
+                if (r < rows) {
+                    if (bo.pb_part)
+                        for (int gq = 0; gq < bo.npb; ++gq) raw += (double)bo.pb_part[((size_t)gq * gridDim.y + b) * T + t];
+                    else
+                        raw = (double)*o;
+                }
+                *o = r < rows ? (float)(raw / zrow[r]) : 0.0f;
             }
         if (bo.grad_proj_start || bo.grad_proj_end)
             for (int q = tid; q < TM * C; q += 256) {
