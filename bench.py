@@ -51,7 +51,7 @@ SWEEP_SRCS = [os.path.join(ROOT, "semi_markov_crf_amd", "csrc", f)
                         "internal.h")]
 SWEEP_COUNTERS = {"sha256": "c485464895e7d4c03e61808a986c6e850909d23a6616992084d42a93ca24044e",
                   "delta": 1786, "valu": 191_963_364, "trans": 5_562_640,
-                  "hbm_bytes": (24_209 * 2.0 + 47_886 * 1.0) * 1024}
+                  "hbm_bytes": (24_121 * 2.0 + 47_889 * 1.0) * 1024}
 
 
 def sources_sha(paths):
