@@ -49,7 +49,7 @@ N_CU = 256
 SWEEP_SRCS = [os.path.join(ROOT, "semi_markov_crf_amd", "csrc", f)
               for f in ("sweep_lse_round.h", "sweep_lse_kernel.h", "ring.h", "common.h",
                         "internal.h")]
-SWEEP_COUNTERS = {"sha256": "c485464895e7d4c03e61808a986c6e850909d23a6616992084d42a93ca24044e",
+SWEEP_COUNTERS = {"sha256": "06bb9190e989629a48563fed5c0fa43ad8f600250343af60d592f68810b67cb0",
                   "delta": 1786, "valu": 191_963_364, "trans": 5_562_640,
                   "hbm_bytes": (24_121 * 2.0 + 47_889 * 1.0) * 1024}
 

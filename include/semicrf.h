@@ -93,7 +93,8 @@ int semicrf_viterbi_interval(int B, int T, int K);
  * and for a backward whose two directions share a workgroup (small label counts), else
  * twice that; share = 224 workgroups (7/8 of the MI355X's 256 compute units, leaving room
  * for a concurrent call) where the round kernels run (C <= 16, K <= 1025), else 256.
- * Ties go to the longer interval.  0 on bad or unsupported input. */
+ * Intervals shorter than the burn-in are not taken (unless T is); ties go to the longer
+ * interval.  0 on bad or unsupported input. */
 int semicrf_default_interval(semicrf_op op, int B, int T, int C, int K);
 
 /* Bytes of workspace that `op` needs for these shapes (delta as the call takes it: > 0 an

@@ -87,7 +87,10 @@ static int span_workgroups(const SweepCfg& cfg, int op, int C) {
 // once the spans' workgroups outnumber what the compute units run side by side, a CU
 // holds two and each takes about twice as long (measured: the sweeps are issue-bound on
 // their CU).  So the interval is the one, over every span count n (interval ceil(T/n)),
-// that minimises (interval + burn-in) * ceil(workgroups / share), the longer on ties.
+// that minimises (interval + burn-in) * ceil(workgroups / share), the longer on ties, among
+// intervals at least one burn-in long (shorter spans would spend most of their sweep
+// burning in, and their seam windows and checkpoints grow with the span count: at
+// K = 8000 that kept the backward's workspace at T = 10^6 from doubling).
 // share: 224 workgroups (7/8 of the MI355X's 256 CUs, the rest left to a concurrent call
 // such as a decode on another stream) for the round kernels, 256 for the others.
 // Measured at B = 4, T = 10^5, K = 200 (round kernel, one workgroup per span): a backward
@@ -105,6 +108,7 @@ int fill_delta(int B, int T, int K, int op, const SweepCfg& cfg, int C) {
     for (long long n = 1; n <= nmax; ++n) {
         const long long d = (T + n - 1) / n;
         if (n > 1 && d == (T + n - 2) / (n - 1)) continue;   // same interval as n - 1
+        if (n > 1 && d < warm) break;   // spans no shorter than their burn-in (and smaller)
         const long long spans = (T + d - 1) / d;
         const long long rounds = (wps * B * spans + share - 1) / share;
         const double f = (double)(d + (spans > 1 ? warm : 0)) * (double)rounds;
