@@ -65,10 +65,15 @@ static size_t step_lds_wide(int C, int TM) {
 // chunk; the smallest tile takes any chunk.
 static void marg_shape(int C, int K, int* tm, int* kc) {
     const int CL = marg_labels(C);
+    // chunks of equal size (ceil(K / n) for the fewest chunks n that fit): no short last
+    // chunk that stages a whole window for a few durations and leaves most lanes of the
+    // duration partials idle
     auto chunks = [&](int t, int min_kc, size_t budget) {
-        if (K <= 512 && marg_lds(CL, t, K) <= budget) return K;
-        for (int k = 512; k >= min_kc; k >>= 1)
-            if (k < K && marg_lds(CL, t, k) <= budget) return k;
+        for (int n = 1; n <= K; ++n) {
+            const int k = (K + n - 1) / n;
+            if (k < min_kc) break;
+            if (k <= 512 && marg_lds(CL, t, k) <= budget) return k;
+        }
         return 0;
     };
     // above 16 labels the transition step shares the tile: keep its LDS within 150 KB
