@@ -221,7 +221,7 @@ __global__ __launch_bounds__(BT_THREADS) void k_bt_fill(const uint32_t* __restri
 
 int backtrace_chunk(int C, int K) {
     // W > K (a segment never skips a chunk); the LDS form needs (W + K) C + 3 W words
-    return max(K + 1, min(max(1024, 2 * K), 20480 / max(C, 1) - K));
+    return max(K + 1, min(max(512, 2 * K), 20480 / max(C, 1) - K));
 }
 
 int backtrace_chunks(int T, int C, int K) {
