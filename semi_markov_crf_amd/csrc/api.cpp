@@ -547,7 +547,7 @@ static int run_viterbi(const float* em, const int32_t* lengths, const float* tra
     STAGE(2);
     LAUNCH(launch_backtrace(a.bp, vend, B, T, C, K, at<int32_t>(workspace, lo.btr),
                             at<int32_t>(workspace, lo.bent),
-                            backtrace_global(C, K) ? at<int>(workspace, lo.btg) : nullptr, labels,
+                            backtrace_global(T, C, K) ? at<int>(workspace, lo.btg) : nullptr, labels,
                             seg_start, stream));
     STAGE(3);
     return SEMICRF_OK;

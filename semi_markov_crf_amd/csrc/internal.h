@@ -361,10 +361,10 @@ hipError_t launch_gold(const GoldArgs& g, hipStream_t stream);
 
 // ------------------------------------------------------------------ Viterbi
 // chunk length and chunk count of the parallel backtrace
-int backtrace_chunk(int C, int K);
+int backtrace_chunk(int T, int C, int K);
 int backtrace_chunks(int T, int C, int K);
 // the backtrace's chunk tables live in global memory (the chunks' LDS would not hold them)
-bool backtrace_global(int C, int K);
+bool backtrace_global(int T, int C, int K);
 // int32 words of that global scratch (0 when the tables fit LDS)
 size_t backtrace_scratch_ints(int B, int T, int C, int K);
 // vend[b] = {L, c*}: c* the lowest label maximising vfin[b][c] (the values V(L, c) of the

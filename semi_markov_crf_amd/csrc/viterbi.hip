@@ -219,35 +219,39 @@ __global__ __launch_bounds__(BT_THREADS) void k_bt_fill(const uint32_t* __restri
     }
 }
 
-int backtrace_chunk(int C, int K) {
-    // W > K (a segment never skips a chunk); the LDS form needs (W + K) C + 3 W words
-    return max(K + 1, min(max(512, 2 * K), 20480 / max(C, 1) - K));
+int backtrace_chunk(int T, int C, int K) {
+    // The fill walks a chunk's chain one segment at a time (up to W steps, short decoded
+    // segments make it that long) and the compose walks the chunks one after another
+    // ((T + 1) / W steps of about 1.4x a walk step): W ~ 1.2 sqrt(T) balances them.  W > K
+    // (a segment never skips a chunk); the LDS form needs (W + K) C + 3 W words.
+    const int w = max(64, (int)ceil(1.2 * sqrt((double)T + 1.0)));
+    return max(K + 1, min(w, 20480 / max(C, 1) - K));
 }
 
 int backtrace_chunks(int T, int C, int K) {
-    const int W = backtrace_chunk(C, K);
+    const int W = backtrace_chunk(T, C, K);
     return (T + 1 + W - 1) / W;
 }
 
-bool backtrace_global(int C, int K) {
-    const size_t W = (size_t)backtrace_chunk(C, K);
+bool backtrace_global(int T, int C, int K) {
+    const size_t W = (size_t)backtrace_chunk(T, C, K);
     const size_t lds_t = W * C * sizeof(int);
     const size_t lds_f = (W + K) * C * sizeof(uint32_t) + 3 * W * sizeof(int);
     return lds_t > BT_LDS_MAX || lds_f > BT_LDS_MAX;
 }
 
 size_t backtrace_scratch_ints(int B, int T, int C, int K) {
-    if (!backtrace_global(C, K)) return 0;
-    const size_t W = (size_t)backtrace_chunk(C, K);
+    if (!backtrace_global(T, C, K)) return 0;
+    const size_t W = (size_t)backtrace_chunk(T, C, K);
     return (size_t)B * backtrace_chunks(T, C, K) * (W * C + 3 * W);
 }
 
 hipError_t launch_backtrace(const uint32_t* bp, const int* vend, int B, int T, int C, int K,
                             int32_t* tr, int32_t* ent, int* gscratch, int32_t* labels,
                             uint8_t* seg_start, hipStream_t stream) {
-    const int W = backtrace_chunk(C, K);
+    const int W = backtrace_chunk(T, C, K);
     const int nch = backtrace_chunks(T, C, K);
-    if (backtrace_global(C, K)) {
+    if (backtrace_global(T, C, K)) {
         if (!gscratch) return hipErrorInvalidValue;
         int* gnxt = gscratch;
         int* gseg = gscratch + (size_t)B * nch * W * C;
