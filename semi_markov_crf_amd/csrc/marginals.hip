@@ -834,21 +834,23 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const double* __restric
     const bool isd = e < nd;
     const int ee = isd ? e : e - nd;
     const int stride = isd ? nd : C * C;
+    // the (sequence, group) pairs slice, slice + RP_SLICES, ... in order; the iterations
+    // are independent until the sum, so their loads overlap
     double total = 0.0;
-    for (int b = 0; b < B; ++b) {
+    const int npairs = B * ngroups;
+#pragma unroll 4
+    for (int q = slice; q < npairs; q += RP_SLICES) {
+        const int b = q / ngroups, j = q - b * ngroups;
         const int L = abs(Leff[b]);
-        double s = 0.0;
-        for (int j = slice; j < ngroups; j += RP_SLICES) {
-            double zs = 0.0, ns = 0.0;
-            for (int tl = j * tpg; tl < min(ntiles, (j + 1) * tpg); ++tl) {
-                const int rows = max(0, min(TM, L - tl * TM));
-                zs += (double)rows * z_tile[(size_t)b * ntiles + tl];
-                ns += (double)rows;
-            }
-            const size_t at = ((size_t)b * ngroups + j) * stride + ee;
-            s += (isd ? (double)part_dur[at] : part_trans[at]) / (ns > 0.0 ? zs / ns : 1.0);
+        double zs = 0.0, ns = 0.0;
+        for (int tl = j * tpg; tl < min(ntiles, (j + 1) * tpg); ++tl) {
+            const int rows = max(0, min(TM, L - tl * TM));
+            zs += (double)rows * z_tile[(size_t)b * ntiles + tl];
+            ns += (double)rows;
         }
-        total += (grad_log_z ? (double)grad_log_z[b] : 1.0) * s;
+        const size_t at = ((size_t)b * ngroups + j) * stride + ee;
+        const double x = (isd ? (double)part_dur[at] : part_trans[at]) / (ns > 0.0 ? zs / ns : 1.0);
+        total += (grad_log_z ? (double)grad_log_z[b] : 1.0) * x;
     }
     scratch[(size_t)slice * n + e] = total;
 }
