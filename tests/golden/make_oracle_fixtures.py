@@ -9,12 +9,14 @@ touches the HIP path.  Output: ``tests/golden/oracle_cfg{i}.npz`` with
   (``path_segs`` rows (start, length, label), ``path_gaps``, offsets ``path_off``,
   ``final_gap``), so a decode can be compared decision by decision;
 * mu and grad_em (float32) on contiguous windows of positions: [j*D - K, j*D + K]
-  around every multiple j*D of the checkpoint interval D = ceil(sqrt(T*K)) counted
-  from either end of the sequence (where the streamed sweeps of the two directions
-  restart), plus the first and last 2K positions (``win_pos`` per sequence with
-  offsets ``win_off``); instead, every position for the tiny and speech
-  configurations and for sequence 0 of the genomic one (``mu_full`` /
-  ``grad_em_full`` with ``full_seqs``).
+  around every multiple j*D of the checkpoint interval D counted from either end of the
+  sequence (where the span sweeps of the two directions join), plus the first and last
+  2K positions (``win_pos`` per sequence with offsets ``win_off``); instead, every
+  position for the tiny and speech configurations and for sequence 0 of the genomic one
+  (``mu_full`` / ``grad_em_full`` with ``full_seqs``).  D is the interval the library's
+  backward takes by default at each shape (``SEAM_INTERVAL``, stored as
+  ``seam_interval``; the header ``include/semicrf.h`` states the rule, and the parity
+  test checks that the library still picks it).
 
 Usage:  python tests/golden/make_oracle_fixtures.py [cfg ...] [--workers N]
 """
@@ -22,7 +24,6 @@ Usage:  python tests/golden/make_oracle_fixtures.py [cfg ...] [--workers N]
 from __future__ import annotations
 
 import argparse
-import math
 import os
 import sys
 import time
@@ -37,13 +38,14 @@ import oracle      # noqa: E402
 import workloads   # noqa: E402
 
 FULL_SEQS = {0: "all", 1: "all", 2: [0], 3: [], 4: []}
+# the backward's default checkpoint interval at the windowed shapes: genomic (56 spans a
+# sequence), long genomic (224 spans), large label set (16 spans a sequence)
+SEAM_INTERVAL = {2: 1786, 3: 4465, 4: 625}
 
 
-def window_positions(L: int, T: int, K: int) -> np.ndarray:
+def window_positions(L: int, T: int, K: int, D: int) -> np.ndarray:
     """Sorted positions in [0, L): windows of half-width K around every multiple of the
-    checkpoint interval from either end, and the first and last 2K positions."""
-    D = math.isqrt(T * K - 1) + 1 if T * K > 1 else 1
-    D = min(D, T)
+    checkpoint interval D from either end, and the first and last 2K positions."""
     keep = np.zeros(L, dtype=bool)
     keep[: min(L, 2 * K)] = True
     keep[max(0, L - 2 * K):] = True
@@ -75,7 +77,9 @@ def make_fixture(index: int, workers: int) -> str:
     out["final_gap"] = np.array([p["final_gap"] for p in res["paths"]])
     # mu / grad_em windows (none where every position is stored)
     full = list(range(w.B)) if FULL_SEQS[index] == "all" else FULL_SEQS[index]
-    pos = [np.zeros(0, dtype=np.int32) if b in full else window_positions(int(L), w.T, w.K)
+    D = SEAM_INTERVAL.get(index, w.T)
+    out["seam_interval"] = np.array(D, dtype=np.int32)
+    pos = [np.zeros(0, dtype=np.int32) if b in full else window_positions(int(L), w.T, w.K, D)
            for b, L in enumerate(w.lengths)]
     out["win_off"] = np.cumsum([0] + [len(p) for p in pos]).astype(np.int64)
     out["win_pos"] = np.concatenate(pos)

@@ -244,7 +244,11 @@ def test_config_against_oracle_fixture(crf, cfg):
         assert_abs_close(mu[b], ref["mu_full"][i], MARG_ATOL, f"marginals of sequence {b}")
         assert_abs_close(ge[b], ref["grad_em_full"][i], MARG_ATOL, f"grad_em of sequence {b}")
     # contiguous windows around every checkpoint seam of both sweep directions and the
-    # first and last 2K positions of the other sequences
+    # first and last 2K positions of the other sequences (the seams of the interval the
+    # backward above took by default)
+    if "seam_interval" in ref:
+        assert crf.default_interval(crf.OP_BACKWARD, w.B, w.T, w.C, w.K) == \
+            int(ref["seam_interval"]), "the fixture's windows are not on the backward's seams"
     off, pos = ref["win_off"], ref["win_pos"]
     for b in range(w.B):
         p = pos[off[b]:off[b + 1]]
