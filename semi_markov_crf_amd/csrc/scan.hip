@@ -246,6 +246,7 @@ __global__ __launch_bounds__(256) void k_prefix_rows(const float* __restrict__ e
                                                      double* __restrict__ S,
                                                      int* __restrict__ status) {
     __shared__ double wsum[4][CC];
+    extern __shared__ double stage[];   // [256][SCAN_ROWS * CC + 1]
     const int tile = blockIdx.x, b = blockIdx.y, ntiles = gridDim.x, tid = threadIdx.x;
     const int w = tid >> 6;
     const int L = abs(Leff[b]);
@@ -283,14 +284,24 @@ __global__ __launch_bounds__(256) void k_prefix_rows(const float* __restrict__ e
         for (int q = 0; q < w; ++q) run += wsum[q][c];
         excl[c] += run;
     }
+    // the tile's rows t0+1 .. t0+1024 go out through LDS, so that each store instruction
+    // writes 64 consecutive doubles instead of one double every 4*CC: lane blocks of
+    // 4*CC values one double apart (odd stride: no bank conflicts on the writes)
+    constexpr int LB = SCAN_ROWS * CC + 1;
+    double* st = stage + (size_t)tid * LB;
 #pragma unroll
-    for (int i = 0; i < SCAN_ROWS; ++i) {
-        if (tr + i >= T) break;
+    for (int i = 0; i < SCAN_ROWS; ++i)
 #pragma unroll
         for (int c = 0; c < CC; ++c) {
             excl[c] += x[i][c];
-            Sb[(size_t)(tr + i + 1) * CC + c] = excl[c];
+            st[i * CC + c] = excl[c];
         }
+    __syncthreads();
+    const int nout = min(1024, T - t0) * CC;   // rows t0+1 .. min(t0+1024, T)
+    double* dst = Sb + (size_t)(t0 + 1) * CC;
+    for (int e = tid; e < nout; e += 256) {
+        const int lane = e / (SCAN_ROWS * CC);
+        dst[e] = stage[(size_t)lane * LB + (e - lane * SCAN_ROWS * CC)];
     }
     if (tile == 0 && tid < CC) Sb[tid] = 0.0;
 }
@@ -330,7 +341,8 @@ hipError_t launch_prefix(const float* em, const int* Leff, int B, int T, int C,
     const int nt = (T + TS - 1) / TS;
 #define SEMICRF_ROWS_CASE(CC)                                                                  \
     case CC:                                                                                   \
-        hipLaunchKernelGGL(k_prefix_rows<CC>, dim3(nt, B), dim3(256), 0, stream, em, Leff, B,  \
+        hipLaunchKernelGGL(k_prefix_rows<CC>, dim3(nt, B), dim3(256),                        \
+                           (size_t)256 * (4 * (CC) + 1) * 8, stream, em, Leff, B,            \
                            T, tile_offsets, totals, S, status);                                \
         return hipGetLastError();
     if (TS == 1024) switch (C) {
