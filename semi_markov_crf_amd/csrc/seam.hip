@@ -90,34 +90,57 @@ __global__ __launch_bounds__(256) void k_seam_stats(const SeamArgs s) {
 // the spans' states are the same up to c_j = (max d + min d) / 2; the frame offsets chain
 // the c_j; the first seam that fails stops the chain.
 __global__ __launch_bounds__(64) void k_seam(const SeamArgs s) {
-    const int b = blockIdx.x, dir = blockIdx.y, tid = threadIdx.x;
-    if (tid != 0) return;
+    const int b = blockIdx.x, dir = blockIdx.y, lane = threadIdx.x;
     const int Lr = s.Leff[b];
     const bool bad = Lr < 0;
     const int L = bad ? -Lr : Lr;
     const int n = (L + s.delta - 1) / s.delta;                    // spans that hold positions
     const size_t row = (size_t)dir * s.B + b;
     double* off = s.off + row * s.nspans;
-    double cur = 0.0, sum = 0.0, mx = 0.0;
+    // the seams 1 .. n-1, 64 at a time, one a lane: the first one not accepted stops the
+    // chain; the frame offsets are the prefix sums of the accepted constants (a fixed-order
+    // wavefront scan), the bound the sum and maximum of their tau
+    double cur = 0.0, sum = 0.0, mx = 0.0;                         // the same in every lane
     int fb = s.nspans;
-    off[0] = 0.0;
-    for (int j = 1; j < n; ++j) {
-        const double* st = s.stats + (row * s.nspans + j) * 3;
-        const double gmax = st[0], gmin = st[1];
-        const bool any = gmax >= gmin;                             // some finite entry
-        const double tau = any ? 0.5 * (gmax - gmin) : 0.0;
-        const bool ok = st[2] == 0.0 && tau <= s.tol;
-        if (!ok) {
-            fb = j;
+    if (lane == 0) off[0] = 0.0;
+    for (int j0 = 1; j0 < n; j0 += 64) {
+        const int j = j0 + lane;
+        const bool in = j < n;
+        double c = 0.0, tau = 0.0;
+        bool ok = true;
+        if (in) {
+            const double* st = s.stats + (row * s.nspans + j) * 3;
+            const double gmax = st[0], gmin = st[1];
+            const bool any = gmax >= gmin;                         // some finite entry
+            tau = any ? 0.5 * (gmax - gmin) : 0.0;
+            ok = st[2] == 0.0 && tau <= s.tol;
+            c = any ? 0.5 * (gmax + gmin) : 0.0;
+        }
+        const unsigned long long badm = __ballot(in && !ok);
+        const int first = badm ? __builtin_ctzll(badm) : 64;     // first seam not accepted
+        const bool acc = in && lane < first;
+        double v = acc ? c : 0.0;                                  // inclusive scan
+        for (int d = 1; d < 64; d <<= 1) {
+            const double u = __shfl_up(v, d, 64);
+            if (lane >= d) v += u;
+        }
+        if (acc) off[j] = cur + v;
+        double ts = acc ? tau : 0.0, tm = ts;
+        for (int d = 32; d >= 1; d >>= 1) {
+            ts += __shfl_xor(ts, d, 64);
+            tm = fmax(tm, __shfl_xor(tm, d, 64));
+        }
+        cur += __shfl(v, 63, 64);
+        sum += ts;
+        mx = fmax(mx, tm);
+        if (badm) {
+            fb = j0 + first;
             break;
         }
-        cur += any ? 0.5 * (gmax + gmin) : 0.0;
-        sum += tau;
-        mx = fmax(mx, tau);
-        off[j] = cur;
     }
     // a repaired sweep continues in the frame of span fb-1
-    for (int j = fb; j < n; ++j) off[j] = cur;
+    for (int j = fb + lane; j < n; j += 64) off[j] = cur;
+    if (lane != 0) return;
     s.first_bad[row] = fb;
     if (fb >= s.nspans) {
         const double lz = bad ? __longlong_as_double(0x7ff8000000000000LL) : s.lzloc[row] + cur;
