@@ -338,7 +338,7 @@ def main():
     B, T, C, K = w.B, w.T, w.C, w.K
     delta = (crf.checkpoint_interval(T, K, args.delta) if args.delta
              else crf.default_interval(crf.OP_BACKWARD, B, T, C, K))
-    vdelta = crf.viterbi_interval(B, T, K)
+    vdelta = crf.default_interval(crf.OP_VITERBI, B, T, C, K)
     nb = crf.workspace_bytes(crf.OP_BACKWARD, B, T, C, K, args.delta)
     nv = crf.workspace_bytes(crf.OP_VITERBI, B, T, C, K)
     ws_b = torch.empty(nb, dtype=torch.uint8, device=d)

@@ -80,21 +80,19 @@ const char* semicrf_status_string(int status);
  * about sqrt(TK)); clamped to [1, T].  0 on bad input. */
 int semicrf_checkpoint_interval(int T, int K, int delta);
 
-/* The decode's checkpoint interval for a batch of B sequences of padded length T
- * (semicrf_viterbi takes none): semicrf_checkpoint_interval(T, K, 0), halved when the
- * batch holds at most 128 spans of that length and each is at least four burn-ins (12 K)
- * long, so that the spans swept at once occupy more compute units.  0 on bad input. */
-int semicrf_viterbi_interval(int B, int T, int K);
 
-/* The checkpoint interval `op` uses for delta = 0 (SEMICRF_OP_VITERBI: the decode's,
- * semicrf_viterbi_interval).  For log Z and the backward every span is swept at once, so
- * the interval is the one, over every span count n (interval ceil(T/n)), that minimises
- * (interval + burn-in 3K) * ceil(workgroups / share): workgroups = B * spans for log Z
- * and for a backward whose two directions share a workgroup (small label counts), else
+/* The checkpoint interval `op` uses for delta = 0 (semicrf_viterbi takes none and always
+ * uses it).  Every span is swept at once, so where the round kernels run (C <= 16,
+ * K <= 1025) and for log Z and the backward everywhere, the interval is the one, over
+ * every span count n (interval ceil(T/n)), that minimises
+ * (interval + burn-in 3K) * ceil(workgroups / share): workgroups = B * spans for log Z, the
+ * decode and a backward whose two directions share a workgroup (small label counts), else
  * twice that; share = 224 workgroups (7/8 of the MI355X's 256 compute units, leaving room
- * for a concurrent call) where the round kernels run (C <= 16, K <= 1025), else 256.
- * Intervals shorter than the burn-in are not taken (unless T is); ties go to the longer
- * interval.  0 on bad or unsupported input. */
+ * for a concurrent call) where the round kernels run, else 256.  Intervals shorter than
+ * the burn-in are not taken (unless T is); ties go to the longer interval.  The decode
+ * outside the round kernels takes ceil(sqrt(T*K)), halved when the batch holds at most
+ * 128 spans of that length and each is at least four burn-ins (12 K) long.  0 on bad or
+ * unsupported input. */
 int semicrf_default_interval(semicrf_op op, int B, int T, int C, int K);
 
 /* Bytes of workspace that `op` needs for these shapes (delta as the call takes it: > 0 an

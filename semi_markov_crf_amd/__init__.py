@@ -25,17 +25,12 @@ from . import _native
 from ._native import OP_BACKWARD, OP_LOGZ, OP_PREFIX, OP_VITERBI, SemiCRFError
 
 __all__ = ["prefix", "logz", "backward", "viterbi", "nll", "log_partition", "workspace_bytes",
-           "checkpoint_interval", "viterbi_interval", "default_interval", "read_status", "SemiCRFError",
+           "checkpoint_interval", "default_interval", "read_status", "SemiCRFError",
            "OP_LOGZ", "OP_BACKWARD", "OP_VITERBI", "OP_PREFIX"]
 
 
 def checkpoint_interval(T: int, K: int, delta: int = 0) -> int:
     return int(_native.load().semicrf_checkpoint_interval(T, K, delta))
-
-
-def viterbi_interval(B: int, T: int, K: int) -> int:
-    """Checkpoint interval the decode uses for a batch of B sequences of padded length T."""
-    return int(_native.load().semicrf_viterbi_interval(B, T, K))
 
 
 def default_interval(op: int, B: int, T: int, C: int, K: int) -> int:

@@ -42,7 +42,6 @@ _VITERBI = [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _c_siz
 SIGNATURES = {
     "semicrf_status_string": (ctypes.c_char_p, [_c_int]),
     "semicrf_checkpoint_interval": (_c_int, [_c_int, _c_int, _c_int]),
-    "semicrf_viterbi_interval": (_c_int, [_c_int, _c_int, _c_int]),
     "semicrf_default_interval": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "semicrf_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "semicrf_prefix": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp, _vp, _c_size, _vp]),

@@ -55,11 +55,11 @@ int resolve_delta(int T, int K, int delta) {
     return (int)d;
 }
 
-// The decode's checkpoint interval (it takes none).  It starts from ceil(sqrt(T*K)) and
-// halves it when the batch's spans (one workgroup each) would leave most compute units
-// idle and a span stays long next to its burn-in: at B = 4, T = 10^5, K = 200 the decode
-// drops from 1.78 to 1.18 ms; with 32 speech-length sequences the halving costs more
-// burn-in than it gains (0.53 -> 0.61 ms), so it is not taken there.
+// The decode's checkpoint interval outside the round kernels (more than 16 labels, or
+// K > 1025).  It starts from ceil(sqrt(T*K)) and halves it when the batch's spans (one
+// workgroup each) would leave most compute units idle and a span stays long next to its
+// burn-in: with 32 speech-length sequences the halving costs more burn-in than it gains
+// (0.53 -> 0.61 ms), so it is not taken there.
 int default_delta(int B, int T, int K) {
     const int d = resolve_delta(T, K, 0);
     if (d < 1) return 0;
@@ -120,6 +120,15 @@ int fill_delta(int B, int T, int K, int op, const SweepCfg& cfg, int C) {
     return (int)best_d;
 }
 
+// The decode's checkpoint interval (it takes none): the span launch's cost model of
+// fill_delta where the round kernel runs (one workgroup a span; at B = 4, T = 10^5, K = 200
+// beside a backward pass: 1.68 against 1.71 ms a pair with ceil(sqrt(TK))/2, three runs
+// each), default_delta otherwise.
+int decode_delta(int B, int T, int K, const SweepCfg& cfg, int C) {
+    if (cfg.split && !cfg.xk) return fill_delta(B, T, K, SEMICRF_OP_VITERBI, cfg, C);
+    return default_delta(B, T, K);
+}
+
 bool shape_ok(int B, int T, int C, int K) {
     return B >= 1 && T >= 1 && C >= 1 && K >= 1 && T <= MAX_T && K <= 65535;
 }
@@ -142,7 +151,7 @@ bool make_layout(int op, int B, int T, int C, int K, int delta, Layout& lo) {
         // checkpoint spans: checkpoints, seam windows and frame offsets per direction (the
         // decode runs forward only, with the default interval)
         // delta = 0 (and always for the decode): the batch-aware default interval
-        lo.delta = op == SEMICRF_OP_VITERBI ? default_delta(B, T, K)
+        lo.delta = op == SEMICRF_OP_VITERBI ? decode_delta(B, T, K, cfg, C)
                    : delta == 0             ? fill_delta(B, T, K, op, cfg, C)
                                             : resolve_delta(T, K, delta);
         if (lo.delta < 1) return false;
@@ -353,17 +362,12 @@ const char* semicrf_status_string(int status) {
 
 int semicrf_checkpoint_interval(int T, int K, int delta) { return resolve_delta(T, K, delta); }
 
-int semicrf_viterbi_interval(int B, int T, int K) {
-    if (!shape_ok(B, T, 1, K)) return 0;
-    return default_delta(B, T, K);
-}
-
 int semicrf_default_interval(semicrf_op op, int B, int T, int C, int K) {
     if (!shape_ok(B, T, C, K)) return 0;
-    if (op == SEMICRF_OP_VITERBI) return default_delta(B, T, K);
-    if (op != SEMICRF_OP_LOGZ && op != SEMICRF_OP_BACKWARD) return 0;
+    if (op != SEMICRF_OP_LOGZ && op != SEMICRF_OP_BACKWARD && op != SEMICRF_OP_VITERBI) return 0;
     const SweepCfg cfg = choose_sweep(C, K);
     if (!cfg.ok) return 0;
+    if (op == SEMICRF_OP_VITERBI) return decode_delta(B, T, K, cfg, C);
     return fill_delta(B, T, K, op, cfg, C);
 }
 

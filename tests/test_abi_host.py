@@ -141,22 +141,24 @@ def test_default_interval(native):
     assert f(BW, 64, 100_000, 6, 200) == 14286
     # short sequences: one span (no burn-in) beats any split
     assert f(BW, 2, 64, 4, 8) == 64
-    # the decode keeps its own interval
-    assert f(VI, 4, 100_000, 6, 200) == lib.semicrf_viterbi_interval(4, 100_000, 200)
     assert f(BW, 0, 100, 4, 5) == 0 and f(BW, 1, 0, 4, 5) == 0 and f(BW, 1, 10, 4, 0) == 0
     assert f(BW, 1, 100, 200, 5) == 0          # unsupported label count
 
 
-def test_viterbi_interval(native):
+def test_decode_interval(native):
     lib = native.load()
-    f = lib.semicrf_viterbi_interval
-    assert f(4, 100_000, 200) == 2237          # 92 spans of 4473 >= 12 K: halved
-    assert f(1, 1_000_000, 200) == 7072        # 71 spans of 14143: halved
-    assert f(8, 10_000, 64) == 400             # 104 spans of 800 >= 768: halved
-    assert f(32, 800, 30) == 155               # 192 spans: the batch fills the device
-    assert f(64, 100_000, 200) == 4473         # 1472 spans
-    assert f(1, 1000, 200) == 448              # a span shorter than 12 K: kept
-    assert f(0, 100, 5) == 0 and f(1, 0, 5) == 0 and f(1, 10, 0) == 0
+    f = lib.semicrf_default_interval
+    VI = native.OP_VITERBI
+    # round kernels: the span launch's model, one workgroup a span, 224 workgroups
+    assert f(VI, 4, 100_000, 6, 200) == 1786
+    assert f(VI, 1, 1_000_000, 6, 200) == 4465
+    assert f(VI, 2, 2000, 16, 20) == 65        # 31 spans a sequence, one burn-in long
+    assert f(VI, 1, 1000, 6, 200) == 1000      # one span: no burn-in
+    # other kernels: ceil(sqrt(TK)), halved for few long spans
+    assert f(VI, 8, 10_000, 64, 64) == 400     # 104 spans of 800 >= 768: halved
+    assert f(VI, 32, 800, 39, 30) == 155       # 192 spans: the batch fills the device
+    assert f(VI, 1, 5000, 3, 1030) == 2270     # long durations: spans shorter than 12 K kept
+    assert f(VI, 0, 100, 4, 5) == 0 and f(VI, 1, 0, 4, 5) == 0 and f(VI, 1, 10, 4, 0) == 0
 
 
 def test_workspace_bytes(native):

@@ -151,7 +151,7 @@ def test_decode_over_spans_matches_oracle_decisions(crf, case):
                                                  check_status=True)
     s2, l2, g2, _, rep2 = crf.viterbi(em, lengths, trans, dur, seam_tolerance=-1.0,
                                       want_seams=True, check_status=True)
-    D = crf.viterbi_interval(B, T, K)
+    D = crf.default_interval(crf.OP_VITERBI, B, T, C, K)
     assert np.all(np_(rep) == 0)
     np.testing.assert_array_equal(np_(rep2), (np.asarray(w.lengths) > D).astype(np.int32))
     print(f"seam bound {np_(bound)}", flush=True)
