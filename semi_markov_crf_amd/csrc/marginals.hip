@@ -499,11 +499,16 @@ hipError_t launch_trans_step(const TransStepArgs& a, hipStream_t stream) {
 // [p0 - kc1, p0 + TM - 1 - kc0] and the ends [p0 + kc0, p0 + TM - 1 + kc1] are staged
 // beside the tile's own starts and ends.  The duration partials of the group's tiles are
 // summed in tile order (each lane owns the same entries in every tile).
+// CLT > 0: the workgroup takes all CLT = C labels, known at compile time (the LDS strides
+// and the row / label splits of the lane indexes fold into constants); CLT = 0: label
+// groups of a.cg, the last one possibly shorter.
+template <int CLT>
 __global__ __launch_bounds__(256) void k_marginals(const MargArgs a) {
     extern __shared__ double lds[];
     const int C = a.C, K = a.K, T = a.T, TM = a.tile, KC = a.kchunk;
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int c0 = blockIdx.z * a.cg, CL = min(a.cg, C - c0);   // this workgroup's labels
+    const int c0 = CLT ? 0 : blockIdx.z * a.cg;
+    const int CL = CLT ? CLT : min(a.cg, C - c0);   // this workgroup's labels
     const int L = abs(a.Leff[b]);
     const size_t rowC = (size_t)(T + 1) * C;
 
@@ -662,7 +667,16 @@ hipError_t launch_marginals(const MargArgs& a, hipStream_t stream) {
     if (nlg > 1 && a.pbsum && !a.pb_part) return hipErrorInvalidValue;
     const size_t lds = marg_lds(a.cg, a.tile, a.kchunk);
     if (a.tpg < 1 || a.ngroups != (a.ntiles + a.tpg - 1) / a.tpg) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_marginals, dim3(a.ngroups, a.B, nlg), dim3(256), lds, stream, a);
+    const dim3 grid(a.ngroups, a.B, nlg);
+#define MARG_CASE(n) \
+    case n: hipLaunchKernelGGL(k_marginals<n>, grid, dim3(256), lds, stream, a); break;
+    switch (nlg == 1 ? a.C : 0) {
+        MARG_CASE(1) MARG_CASE(2) MARG_CASE(3) MARG_CASE(4) MARG_CASE(5) MARG_CASE(6)
+        MARG_CASE(7) MARG_CASE(8) MARG_CASE(9) MARG_CASE(10) MARG_CASE(11) MARG_CASE(12)
+        MARG_CASE(13) MARG_CASE(14) MARG_CASE(15) MARG_CASE(16)
+        default: hipLaunchKernelGGL(k_marginals<0>, grid, dim3(256), lds, stream, a); break;
+    }
+#undef MARG_CASE
     return hipGetLastError();
 }
 
