@@ -296,8 +296,8 @@ def span_positions(lengths, delta, warm):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--delta", type=int, default=0,
                     help="checkpoint interval of the backward (0: the library default)")
     ap.add_argument("--cpu-sample", type=int, default=12_000,
