@@ -840,33 +840,58 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const double* __restric
                                                          int B, int C, int K, int TM, int ntiles,
                                                          int tpg, int ngroups,
                                                          double* __restrict__ scratch) {
+    // weights g_b / z_j of the (sequence, group) pairs of this workgroup's four slices,
+    // RP_W of them a pass, computed once and shared by the workgroup's 64 elements
+    constexpr int RP_W = 256;
+    __shared__ double wq[RP_W];
     const int n = K * C + C * C;
     const int e = blockIdx.x * 64 + (threadIdx.x & 63);
-    const int slice = blockIdx.y * 4 + (threadIdx.x >> 6);
-    if (e >= n) return;
+    const int sl4 = threadIdx.x >> 6;
+    const int slice = blockIdx.y * 4 + sl4;
     const int nd = K * C;
     const bool isd = e < nd;
     const int ee = isd ? e : e - nd;
     const int stride = isd ? nd : C * C;
-    // the (sequence, group) pairs slice, slice + RP_SLICES, ... in order; the iterations
-    // are independent until the sum, so their loads overlap
-    double total = 0.0;
     const int npairs = B * ngroups;
-#pragma unroll 4
-    for (int q = slice; q < npairs; q += RP_SLICES) {
-        const int b = q / ngroups, j = q - b * ngroups;
-        const int L = abs(Leff[b]);
-        double zs = 0.0, ns = 0.0;
-        for (int tl = j * tpg; tl < min(ntiles, (j + 1) * tpg); ++tl) {
-            const int rows = max(0, min(TM, L - tl * TM));
-            zs += (double)rows * z_tile[(size_t)b * ntiles + tl];
-            ns += (double)rows;
+    // pass m covers the pairs blockIdx.y * 4 + s + RP_SLICES * i, s < 4, i in
+    // [m * RP_W / 4, (m + 1) * RP_W / 4): wq[s * RP_W / 4 + i - m * RP_W / 4]
+    double total = 0.0;
+    const int iters = (npairs + RP_SLICES - 1) / RP_SLICES;
+    for (int i0 = 0; i0 < iters; i0 += RP_W / 4) {
+        __syncthreads();   // the previous pass's weights are no longer read
+        {
+            const int s = threadIdx.x / (RP_W / 4), i = i0 + threadIdx.x % (RP_W / 4);
+            const int q = blockIdx.y * 4 + s + RP_SLICES * i;
+            double w = 0.0;
+            if (q < npairs) {
+                const int b = q / ngroups, j = q - b * ngroups;
+                const int L = abs(Leff[b]);
+                double zs = 0.0, ns = 0.0;
+                for (int tl = j * tpg; tl < min(ntiles, (j + 1) * tpg); ++tl) {
+                    const int rows = max(0, min(TM, L - tl * TM));
+                    zs += (double)rows * z_tile[(size_t)b * ntiles + tl];
+                    ns += (double)rows;
+                }
+                w = (grad_log_z ? (double)grad_log_z[b] : 1.0) / (ns > 0.0 ? zs / ns : 1.0);
+            }
+            wq[threadIdx.x] = w;
         }
-        const size_t at = ((size_t)b * ngroups + j) * stride + ee;
-        const double x = (isd ? (double)part_dur[at] : part_trans[at]) / (ns > 0.0 ? zs / ns : 1.0);
-        total += (grad_log_z ? (double)grad_log_z[b] : 1.0) * x;
+        __syncthreads();
+        if (e < n) {
+            const int i1 = min(iters, i0 + RP_W / 4);
+            // the pairs in order; the iterations are independent until the sum, so their
+            // loads overlap
+#pragma unroll 4
+            for (int i = i0; i < i1; ++i) {
+                const int q = slice + RP_SLICES * i;
+                if (q >= npairs) break;
+                const size_t at = (size_t)q * stride + ee;   // q = b * ngroups + j
+                const double x = isd ? (double)part_dur[at] : part_trans[at];
+                total += wq[sl4 * (RP_W / 4) + (i - i0)] * x;
+            }
+        }
     }
-    scratch[(size_t)slice * n + e] = total;
+    if (e < n) scratch[(size_t)slice * n + e] = total;
 }
 
 __global__ __launch_bounds__(256) void k_reduce_slices(const double* __restrict__ scratch, int C,
