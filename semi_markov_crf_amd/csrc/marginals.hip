@@ -828,8 +828,8 @@ hipError_t launch_grad_em(const float* mu, const double* mu_tot, const int* Leff
 // part[b][j] / z_j, z_j the mean per-position normaliser over the group's valid positions
 // (it drifts by far less than 1e-6 across a group).  Pass 1: grid (ceil(n / 64),
 // RP_SLICES / 4), block 256; lane (e, slice) sums the groups j = slice, slice + RP_SLICES,
-// ... of every sequence into scratch[slice][e].  Pass 2: one lane per output adds the
-// slices in order.  Fixed order throughout: bitwise reproducible.
+// ... of every sequence into scratch[slice][e].  Pass 2: four wavefronts per 64 outputs
+// add every fourth slice, then the four partials are added in order.  Fixed order throughout: bitwise reproducible.
 constexpr int RP_SLICES = 128;
 
 __global__ __launch_bounds__(256) void k_reduce_partials(const double* __restrict__ part_dur,
@@ -894,16 +894,26 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const double* __restric
     if (e < n) scratch[(size_t)slice * n + e] = total;
 }
 
+// block 256 over 64 consecutive outputs: wavefront w adds the slices w, w + 4, ... of its
+// lane's output, then lane 0..63 of wavefront 0 adds the four partials in order.
 __global__ __launch_bounds__(256) void k_reduce_slices(const double* __restrict__ scratch, int C,
                                                        int K, float* __restrict__ grad_dur,
                                                        float* __restrict__ grad_trans) {
+    __shared__ double part[4][64];
     const int n = K * C + C * C;
-    const int e = blockIdx.x * 256 + threadIdx.x;
-    if (e >= n) return;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int e = blockIdx.x * 64 + lane;
     double total = 0.0;
-    for (int sl = 0; sl < RP_SLICES; ++sl) total += scratch[(size_t)sl * n + e];
-    if (e < K * C) grad_dur[e] = (float)total;
-    else grad_trans[e - K * C] = (float)total;
+    if (e < n)
+#pragma unroll 8
+        for (int sl = w; sl < RP_SLICES; sl += 4) total += scratch[(size_t)sl * n + e];
+    part[w][lane] = total;
+    __syncthreads();
+    if (w == 0 && e < n) {
+        const double t = ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+        if (e < K * C) grad_dur[e] = (float)t;
+        else grad_trans[e - K * C] = (float)t;
+    }
 }
 
 size_t reduce_scratch_doubles(int C, int K) { return (size_t)RP_SLICES * (K * C + C * C); }
@@ -918,7 +928,7 @@ hipError_t launch_reduce_partials(const double* part_dur, const double* part_tra
     hipLaunchKernelGGL(k_reduce_partials, dim3((n + 63) / 64, RP_SLICES / 4), dim3(256), 0, stream,
                        part_dur, part_trans, z_tile, Leff, grad_log_z, B, C, K, tile, ntiles,
                        tpg, ngroups, scratch);
-    hipLaunchKernelGGL(k_reduce_slices, dim3((n + 255) / 256), dim3(256), 0, stream, scratch, C, K,
+    hipLaunchKernelGGL(k_reduce_slices, dim3((n + 63) / 64), dim3(256), 0, stream, scratch, C, K,
                        grad_dur, grad_trans);
     return hipGetLastError();
 }
