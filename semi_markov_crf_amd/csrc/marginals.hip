@@ -695,21 +695,25 @@ int marg_tiles_per_group(int B, int ntiles, int C, int K) {
 }
 
 // grid (ntiles, B), block 256: mu over positions [p0, p0+TM) = the tile's offset (fp64
-// prefix of the tile totals) + the in-tile prefix, normalised per position; tile sums of
-// mu and the tile's mean normaliser; the boundary outputs rescaled in place.
+// prefix of the tile totals) + the in-tile prefix, normalised per position (one reciprocal
+// of the raw sum per position); tile sums of mu and the tile's mean normaliser; the
+// boundary outputs rescaled in place.  CT > 0: C = CT known at compile time.
+template <int CT>
 __global__ __launch_bounds__(256) void k_node_marginals(const float* Dloc,
                                                         const double* __restrict__ dn_off,
-                                                        const int* __restrict__ Leff, int T, int C,
+                                                        const int* __restrict__ Leff, int T, int Cr,
                                                         int TM, float* mu,
                                                         double* __restrict__ mu_tile,
                                                         double* __restrict__ z_tile,
                                                         const BoundaryOut bo) {
     extern __shared__ double lds[];
+    const int C = CT ? CT : Cr;
     const int tile = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, ntiles = gridDim.x;
     const int L = abs(Leff[b]);
     const int p0 = tile * TM;
     double* v = lds;                       // [TM][C]
     double* zrow = v + (size_t)TM * C;     // [TM]
+    double* rz = zrow + TM;                // [TM]: 1 / zrow
     const float* D = Dloc + (size_t)b * T * C;
     const int rows = max(0, min(TM, L - p0));   // positions p0 .. p0+rows-1 are < L
     const double* off = dn_off + ((size_t)b * ntiles + tile) * C;
@@ -719,6 +723,7 @@ __global__ __launch_bounds__(256) void k_node_marginals(const float* Dloc,
         double z = 0.0;
         for (int c = 0; c < C; ++c) z += v[(size_t)r * C + c];
         zrow[r] = z;
+        rz[r] = 1.0 / z;
     }
     __syncthreads();
     if (bo.node_mass)
@@ -742,7 +747,7 @@ __global__ __launch_bounds__(256) void k_node_marginals(const float* Dloc,
                     else
                         raw = (double)*o;
                 }
-                *o = r < rows ? (float)(raw / zrow[r]) : 0.0f;
+                *o = r < rows ? (float)(raw * rz[r]) : 0.0f;
             }
         if (bo.grad_proj_start || bo.grad_proj_end)
             for (int q = tid; q < TM * C; q += 256) {
@@ -753,10 +758,10 @@ __global__ __launch_bounds__(256) void k_node_marginals(const float* Dloc,
                 const bool in = r < rows;
                 if (bo.grad_proj_start)
                     bo.grad_proj_start[idx] =
-                        in ? (float)(g * (double)bo.grad_proj_start[idx] / zrow[r]) : 0.0f;
+                        in ? (float)(g * (double)bo.grad_proj_start[idx] * rz[r]) : 0.0f;
                 if (bo.grad_proj_end)
                     bo.grad_proj_end[idx] =
-                        in ? (float)(g * (double)bo.grad_proj_end[idx] / zrow[r]) : 0.0f;
+                        in ? (float)(g * (double)bo.grad_proj_end[idx] * rz[r]) : 0.0f;
             }
     }
     float* mub = mu + (size_t)b * T * C;
@@ -766,7 +771,7 @@ __global__ __launch_bounds__(256) void k_node_marginals(const float* Dloc,
         if (t >= T) continue;
         float val = 0.0f;
         if (r < rows) {
-            const double w = v[q] / zrow[r];
+            const double w = v[q] * rz[r];
             v[q] = w;
             val = (float)w;
         }
@@ -788,9 +793,23 @@ __global__ __launch_bounds__(256) void k_node_marginals(const float* Dloc,
 hipError_t launch_node_marginals(const float* Dloc, const double* dn_off, const int* Leff, int B,
                                  int T, int C, int tile, int ntiles, float* mu, double* mu_tile,
                                  double* z_tile, const BoundaryOut& bo, hipStream_t stream) {
-    const size_t lds = (size_t)8 * ((size_t)tile * C + tile);
-    hipLaunchKernelGGL(k_node_marginals, dim3(ntiles, B), dim3(256), lds, stream, Dloc, dn_off, Leff,
-                       T, C, tile, mu, mu_tile, z_tile, bo);
+    const size_t lds = (size_t)8 * ((size_t)tile * C + 2 * tile);
+    const dim3 grid(ntiles, B);
+#define NODE_CASE(n)                                                                          \
+    case n:                                                                                   \
+        hipLaunchKernelGGL(k_node_marginals<n>, grid, dim3(256), lds, stream, Dloc, dn_off, Leff, \
+                           T, C, tile, mu, mu_tile, z_tile, bo);                               \
+        break;
+    switch (C <= 16 ? C : 0) {
+        NODE_CASE(1) NODE_CASE(2) NODE_CASE(3) NODE_CASE(4) NODE_CASE(5) NODE_CASE(6)
+        NODE_CASE(7) NODE_CASE(8) NODE_CASE(9) NODE_CASE(10) NODE_CASE(11) NODE_CASE(12)
+        NODE_CASE(13) NODE_CASE(14) NODE_CASE(15) NODE_CASE(16)
+        default:
+            hipLaunchKernelGGL(k_node_marginals<0>, grid, dim3(256), lds, stream, Dloc, dn_off,
+                               Leff, T, C, tile, mu, mu_tile, z_tile, bo);
+            break;
+    }
+#undef NODE_CASE
     return hipGetLastError();
 }
 
