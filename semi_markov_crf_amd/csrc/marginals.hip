@@ -128,10 +128,12 @@ static size_t step_lds(int C, int TM) {
 // across the group's tiles); then the transition step of every row and direction, lanes
 // over (row, label), as a linear sum of the row's exponentials (relative to the row
 // maximum) against 2^(trans - max trans), redone exactly in log space where that sum
-// leaves [2^-100, inf); written back over the messages.
+// leaves [2^-100, inf); written back over the messages.  CT > 0: C = CT known at compile
+// time.
+template <int CT>
 __global__ __launch_bounds__(256) void k_trans_step(const TransStepArgs a) {
     extern __shared__ double lds[];
-    const int C = a.C, T = a.T, TM = a.tile;
+    const int C = CT ? CT : a.C, T = a.T, TM = a.tile;
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int L = abs(a.Leff[b]);
     const size_t rowC = (size_t)(T + 1) * C;
@@ -487,8 +489,17 @@ hipError_t launch_trans_step(const TransStepArgs& a, hipStream_t stream) {
                            step_lds_wide(a.C, a.tile), stream, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_trans_step, dim3(a.ngroups, a.B), dim3(256), step_lds(a.C, a.tile), stream,
-                       a);
+    const dim3 grid(a.ngroups, a.B);
+    const size_t lds = step_lds(a.C, a.tile);
+#define STEP_CASE(n) \
+    case n: hipLaunchKernelGGL(k_trans_step<n>, grid, dim3(256), lds, stream, a); break;
+    switch (a.C) {
+        STEP_CASE(1) STEP_CASE(2) STEP_CASE(3) STEP_CASE(4) STEP_CASE(5) STEP_CASE(6)
+        STEP_CASE(7) STEP_CASE(8) STEP_CASE(9) STEP_CASE(10) STEP_CASE(11) STEP_CASE(12)
+        STEP_CASE(13) STEP_CASE(14) STEP_CASE(15) STEP_CASE(16)
+        default: hipLaunchKernelGGL(k_trans_step<0>, grid, dim3(256), lds, stream, a); break;
+    }
+#undef STEP_CASE
     return hipGetLastError();
 }
 
