@@ -824,12 +824,15 @@ hipError_t launch_node_marginals(const float* Dloc, const double* dn_off, const 
     return hipGetLastError();
 }
 
-// grid (ceil(T*C/256), B): grad_em = g * (mu - mean over the valid positions of mu)
+// grid (ceil(T*C/256), B): grad_em = g * (mu - mean over the valid positions of mu).
+// CT > 0: C = CT known at compile time.
+template <int CT>
 __global__ __launch_bounds__(256) void k_grad_em(const float* mu,
                                                  const double* __restrict__ mu_tot,
                                                  const int* __restrict__ Leff,
                                                  const float* __restrict__ grad_log_z, int T,
-                                                 int C, float* grad_em) {
+                                                 int Cr, float* grad_em) {
+    const int C = CT ? CT : Cr;
     const int b = blockIdx.y;
     const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (q >= (size_t)T * C) return;
@@ -848,8 +851,22 @@ hipError_t launch_grad_em(const float* mu, const double* mu_tot, const int* Leff
                           const float* grad_log_z, int B, int T, int C, float* grad_em,
                           hipStream_t stream) {
     const size_t n = (size_t)T * C;
-    hipLaunchKernelGGL(k_grad_em, dim3((unsigned)((n + 255) / 256), B), dim3(256), 0, stream, mu,
-                       mu_tot, Leff, grad_log_z, T, C, grad_em);
+    const dim3 grid((unsigned)((n + 255) / 256), B);
+#define GEM_CASE(n)                                                                            \
+    case n:                                                                                    \
+        hipLaunchKernelGGL(k_grad_em<n>, grid, dim3(256), 0, stream, mu, mu_tot, Leff, grad_log_z, \
+                           T, C, grad_em);                                                      \
+        break;
+    switch (C <= 16 ? C : 0) {
+        GEM_CASE(1) GEM_CASE(2) GEM_CASE(3) GEM_CASE(4) GEM_CASE(5) GEM_CASE(6)
+        GEM_CASE(7) GEM_CASE(8) GEM_CASE(9) GEM_CASE(10) GEM_CASE(11) GEM_CASE(12)
+        GEM_CASE(13) GEM_CASE(14) GEM_CASE(15) GEM_CASE(16)
+        default:
+            hipLaunchKernelGGL(k_grad_em<0>, grid, dim3(256), 0, stream, mu, mu_tot, Leff,
+                               grad_log_z, T, C, grad_em);
+            break;
+    }
+#undef GEM_CASE
     return hipGetLastError();
 }
 
